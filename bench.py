@@ -1,0 +1,220 @@
+#!/usr/bin/env python3
+"""KDA prefill + decode throughput on one MI355X.
+
+A step is one ``kda_chunk_fwd`` over the 8K-token workload (B=1, H=32,
+T=8192, K=V=128, bf16 inputs, fp32 state, zero initial state, final state
+returned), with all inputs resident in HBM.  ``value`` is prefill tokens/s
+(B*T / step time).  The same line carries the decode workload (256
+sequences x 32 heads, 512 MiB fp32 state, 64 successive one-token steps), the
+roofline of the dominant launch, and the fp64 CPU oracle timed on a bounded
+sample of the prefill workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--extra] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
+
+METRIC = "KDA prefill tokens/s (MFMA % peak) + decode tokens/s (HBM GB/s %)"
+
+
+def prefill_bytes(B, T, H, K, V, in_bytes=2, s0=False, final=True):
+    """Algorithmic HBM bytes of one prefill call: q, k, g (K each), v, beta
+    and o per head-token, plus the initial / final state per (b, h)."""
+    per_ht = in_bytes * (3 * K + V + 1) + in_bytes * V
+    return B * T * H * per_ht + B * H * K * V * 4 * (int(s0) + int(final))
+
+
+def prefill_flops(B, T, H, K, V, C=64):
+    """Algorithmic flops per head-token of the chunk form at C = 64 with the
+    triangular products counted as half: C (3K + 2V) + 6 K V."""
+    return B * T * H * (C * (3 * K + 2 * V) + 6 * K * V)
+
+
+def decode_bytes(N, H, K, V, in_bytes=2):
+    """Per step: state read + write (8 K V) and the token vectors."""
+    return N * H * (8 * K * V + in_bytes * (3 * K + V + 1) + in_bytes * V)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-passes", type=int, default=3)
+    ap.add_argument("--extra", action="store_true", help="also time the 32K x 256-chain and 1M-token workloads")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=4, help="heads of the 8K workload the oracle runs")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run only a plain device copy of this size (counter calibration) and exit")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only; --gpus %d is not supported "
+              "(heads and batch shard without communication; see DESIGN.md)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_delta_rule_66_amd as kda
+    from gated_delta_rule_66_amd.inputs import CONFIGS, make_decode_config, make_prefill_config
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4, "launches": 5}))
+        return
+
+    kda.load_library()   # fails loudly if the HIP library is missing
+    stream = torch.cuda.current_stream(dev)
+
+    def time_calls(fn, warmup, steps):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for _ in range(steps):
+            fn()
+        end.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / steps   # ms per call
+
+    # ------------------------------------------------------------ prefill, 8K workload
+    cfg = CONFIGS["c1"]
+    x = make_prefill_config(cfg, dev)
+    B, T, H, K, V = cfg.B, cfg.T, cfg.H, cfg.K, cfg.V
+    plan = kda.chunk_plan(B, T, H, K, V, cfg.dtype)
+    o = torch.empty((B, T, H, V), dtype=cfg.dtype, device=dev)
+    sT = torch.empty((B, H, K, V), dtype=torch.float32, device=dev)
+    ws_n = kda.chunk_workspace_size(B, T, H, K, V, cfg.dtype)
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
+
+    def prefill_step():
+        kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], True, None,
+                      out=o, final_state=sT, workspace=ws)
+
+    ms = time_calls(prefill_step, args.warmup, args.steps)
+    tok_s = B * T / (ms * 1e-3)
+    nbytes = prefill_bytes(B, T, H, K, V, 2, s0=False, final=True)
+    nflops = prefill_flops(B, T, H, K, V)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    tflops = nflops / (ms * 1e-3) / 1e12
+    del x, o, sT, ws
+    torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------ decode workload
+    dcfg = CONFIGS["c4"]
+    d = make_decode_config(dcfg, dev)
+    pristine = d["state"]
+    state = pristine.clone()
+    od = torch.empty((dcfg.N, dcfg.H, dcfg.V), dtype=dcfg.dtype, device=dev)
+
+    def decode_pass():
+        for t in range(dcfg.steps):
+            kda.recurrent_step(d["q"][t], d["k"][t], d["v"][t], d["g"][t], d["beta"][t], state, out=od)
+
+    state.copy_(pristine)
+    ms_pass = time_calls(decode_pass, 1, args.decode_passes)
+    ms_step = ms_pass / dcfg.steps
+    dec_tok_s = dcfg.N / (ms_step * 1e-3)
+    dec_bytes = decode_bytes(dcfg.N, dcfg.H, dcfg.K, dcfg.V)
+    dec_gbs = dec_bytes / (ms_step * 1e-3) / 1e9
+    del d, pristine, state, od
+    torch.cuda.empty_cache()
+
+    extra = {}
+    if args.extra:
+        for name in ("c2", "c3"):
+            c = CONFIGS[name]
+            xe = make_prefill_config(c, dev)
+            oe = torch.empty((c.B, c.T, c.H, c.V), dtype=c.dtype, device=dev)
+            se = torch.empty((c.B, c.H, c.K, c.V), dtype=torch.float32, device=dev)
+            n_ws = kda.chunk_workspace_size(c.B, c.T, c.H, c.K, c.V, c.dtype)
+            wse = torch.empty(max(n_ws, 1), dtype=torch.uint8, device=dev)
+            fn = lambda: kda.chunk_fwd(xe["q"], xe["k"], xe["v"], xe["g"], xe["beta"], xe["s0"], True,
+                                       None, out=oe, final_state=se, workspace=wse)
+            mse = time_calls(fn, 2, 5)
+            nb = prefill_bytes(c.B, c.T, c.H, c.K, c.V, 2, s0=c.s0_std is not None, final=True)
+            nf = prefill_flops(c.B, c.T, c.H, c.K, c.V)
+            extra[name] = {
+                "workload": "B=%d T=%d H=%d K=V=%d bf16%s" % (c.B, c.T, c.H, c.K,
+                                                             ", S0~N(0,0.02), 20%% channels at g=-5"
+                                                             if c.pinned_frac else ""),
+                "plan": list(kda.chunk_plan(c.B, c.T, c.H, c.K, c.V, c.dtype)),
+                "ms": round(mse, 4),
+                "tokens_per_s": c.B * c.T / (mse * 1e-3),
+                "hbm_frac": nb / (mse * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                "mfma_frac": nf / (mse * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            }
+            del xe, oe, se, wse
+            torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------ CPU oracle baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        xs = make_prefill_config(cfg, dev, H=args.cpu_heads)   # same recipe, fewer heads
+        q, k, v, g, be = (xs[n].cpu() for n in ("q", "k", "v", "g", "beta"))
+        nthreads = oracle.oracle_max_threads()
+        t0 = time.perf_counter()
+        oracle.oracle_fwd(q, k, v, g, be, None, nthreads=nthreads)
+        dt = time.perf_counter() - t0
+        head_tokens = cfg.B * cfg.T * args.cpu_heads
+        cpu = {
+            "value": head_tokens / dt / cfg.H,       # tokens/s of all 32 heads
+            "unit": "tokens/s",
+            "cores": nthreads,
+            "kind": "oracle",
+            "sample": "fp64 token-by-token oracle on %d of %d heads of the 8K workload (T=%d), "
+                      "%.1f s; scaled to all heads" % (args.cpu_heads, cfg.H, cfg.T, dt),
+        }
+
+    line = {
+        "metric": METRIC,
+        "value": tok_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "KDA prefill B=1 T=8192 H=32 K=V=128 bf16 in, fp32 state, S0=0, final state out",
+                   "global_batch": B, "seq_len": T, "heads": H, "plan": {"n_seg": plan[0], "v_block": plan[1]},
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "kda_chunk_fwd call (all launches of the plan)",
+                     "algorithmic_bytes_per_call": nbytes},
+        "mfma": {"achieved_tflops": tflops, "peak_tflops": BF16_PEAK_TFLOPS, "frac": tflops / BF16_PEAK_TFLOPS,
+                 "algorithmic_flops_per_call": nflops},
+        "decode": {"workload": "256 seq x 32 heads, K=V=128, fp32 state 512 MiB, 64 steps, bf16 tokens",
+                   "tokens_per_s": dec_tok_s, "ms_per_step": ms_step, "achieved_gbs": dec_gbs,
+                   "hbm_frac": dec_gbs / HBM_PEAK_GBS, "bytes_per_step": dec_bytes},
+        "cpu_baseline": cpu,
+    }
+    if extra:
+        line["extra"] = extra
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,21 @@
+"""MI355X (gfx950) KDA: chunked prefill and recurrent decode in HIP.
+
+``chunk_fwd`` and ``recurrent_step`` call the C ABI of ``libkda.so``
+(include/kda.h) through ctypes.  The library is loaded on first use and is
+required: there is no CPU or PyTorch fallback.
+"""
+from .kda import (  # noqa: F401
+    KDAError,
+    Plan,
+    chunk_fwd,
+    chunk_plan,
+    chunk_workspace_size,
+    load_library,
+    recurrent_step,
+    status_string,
+    version,
+)
+from .build import LIB_PATH, build_library  # noqa: F401
+
+__all__ = ["chunk_fwd", "recurrent_step", "chunk_plan", "chunk_workspace_size",
+           "load_library", "build_library", "version", "status_string", "KDAError", "Plan"]

@@ -1,0 +1,253 @@
+// C ABI of libkda.so: argument validation, plan selection and launches.
+// The declarations and their contracts are in include/kda.h.
+#include "kda.h"
+#include "kda_internal.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+using namespace kda;
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t elem_size(kda_dtype dt) { return dt == KDA_BF16 ? 2 : 4; }
+
+kda_status check_dtype(kda_dtype dt) {
+    return (dt == KDA_F32 || dt == KDA_BF16) ? KDA_OK : KDA_ERR_INVALID_ARG;
+}
+
+// Sizes the chunk kernels implement.
+kda_status check_prefill_sizes(int B, int T, int H, int K, int V, kda_dtype dt) {
+    if (B < 0 || T < 0 || H < 0 || K <= 0 || V <= 0) return KDA_ERR_INVALID_ARG;
+    if (check_dtype(dt) != KDA_OK) return KDA_ERR_INVALID_ARG;
+    if (!(K == 64 || K == 128) || !(V == 64 || V == 128)) return KDA_ERR_UNSUPPORTED;
+    if (dt == KDA_F32 && !(K == 64 && V == 64)) return KDA_ERR_UNSUPPORTED;
+    // every index stays within size_t and every grid within int
+    const double rows = (double)B * (double)T * (double)H;
+    if (rows * (double)(K > V ? K : V) > 9.0e18) return KDA_ERR_UNSUPPORTED;
+    if ((double)B * H * 2.0 * 1024 > 2.0e9) return KDA_ERR_UNSUPPORTED;
+    return KDA_OK;
+}
+
+bool ranges_partially_overlap(const void* a, const void* b, size_t n) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    if (x == y) return false;
+    return (x < y) ? (y < x + n) : (x < y + n);
+}
+
+kda_status device_cus(int* cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return KDA_ERR_HIP;
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+        return KDA_ERR_HIP;
+    *cus = n;
+    return KDA_OK;
+}
+
+// Resolve a (possibly partial) requested plan.  Needs the device CU count
+// only when something is left for the library to choose.
+kda_status resolve_plan(int B, int T, int H, int K, int V, kda_dtype dt, const kda_plan* req,
+                        kda_plan* out, int* cps_out) {
+    const int n_chunks = (T + kChunk - 1) / kChunk;
+    const long bh = (long)B * H;
+    int vb = req ? req->v_block : 0;
+    int ns = req ? req->n_seg : 0;
+    if (vb < 0 || ns < 0) return KDA_ERR_INVALID_ARG;
+    int cus = 0;
+    if (vb == 0 || ns == 0) {
+        kda_status s = device_cus(&cus);
+        if (s != KDA_OK) return s;
+    }
+    if (vb != 0) {
+        if (vb != 64 && vb != 128) return KDA_ERR_INVALID_ARG;
+        if (vb > K || vb > V || !chunk_variant_exists((int)dt, K, vb)) return KDA_ERR_UNSUPPORTED;
+    } else {
+        // the widest block that still gives every CU a workgroup, else 64
+        vb = 64;
+        if (V >= 128 && K >= 128 && chunk_variant_exists((int)dt, K, 128) && bh * (V / 128) >= cus)
+            vb = 128;
+        if (!chunk_variant_exists((int)dt, K, vb)) return KDA_ERR_UNSUPPORTED;
+    }
+    if (ns == 0) {
+        // split long sequences into segments when (b, h, column block)
+        // workgroups alone leave compute units idle; each segment keeps at
+        // least 8 chunks so the extra summary pass stays amortised
+        const long wgs = bh * (V / vb);
+        ns = 1;
+        if (wgs > 0 && wgs < cus) {
+            const long want = (cus + wgs - 1) / wgs;
+            const long cap = n_chunks / 8;
+            ns = (int)(want < cap ? want : cap);
+            if (ns < 1) ns = 1;
+        }
+    }
+    if (n_chunks > 0 && ns > n_chunks) ns = n_chunks;
+    if (ns < 1) ns = 1;
+    int cps = n_chunks > 0 ? (n_chunks + ns - 1) / ns : 1;
+    if (n_chunks > 0) ns = (n_chunks + cps - 1) / cps;   // no empty segments
+    out->n_seg = ns;
+    out->v_block = vb;
+    if (cps_out) *cps_out = cps;
+    return KDA_OK;
+}
+
+size_t workspace_bytes_for(int B, int H, int K, int V, const kda_plan& pl) {
+    if (pl.n_seg <= 1) return 0;
+    const size_t bh = (size_t)B * H;
+    // transitions P (K x K) and local states L (K x V) of all but the last
+    // segment, plus one K x V slot per (b, h) for a redirected final state
+    return ((size_t)(pl.n_seg - 1) * bh * K * (size_t)(K + V) + bh * K * V) * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_version(void) { return "kda-mi355x 0.1.0 gfx950"; }
+
+const char* kda_status_string(kda_status s) {
+    switch (s) {
+        case KDA_OK: return "ok";
+        case KDA_ERR_INVALID_ARG: return "invalid argument";
+        case KDA_ERR_UNSUPPORTED: return "unsupported sizes or dtype";
+        case KDA_ERR_WORKSPACE: return "workspace missing or too small";
+        case KDA_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+kda_status kda_chunk_fwd_plan(int B, int T, int H, int K, int V, kda_dtype dt, kda_plan* plan) {
+    if (!plan) return KDA_ERR_INVALID_ARG;
+    kda_status s = check_prefill_sizes(B, T, H, K, V, dt);
+    if (s != KDA_OK) return s;
+    return resolve_plan(B, T, H, K, V, dt, nullptr, plan, nullptr);
+}
+
+size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int K, int V, kda_dtype dt,
+                                    const kda_plan* plan) {
+    if (check_prefill_sizes(B, T, H, K, V, dt) != KDA_OK) return (size_t)-1;
+    kda_plan pl;
+    if (resolve_plan(B, T, H, K, V, dt, plan, &pl, nullptr) != KDA_OK) return (size_t)-1;
+    return workspace_bytes_for(B, H, K, V, pl);
+}
+
+kda_status kda_chunk_fwd(int B, int T, int H, int K, int V, kda_dtype dt,
+                         const void* q, const void* k, const void* v,
+                         const void* g, const void* beta,
+                         const float* initial_state,
+                         void* o, float* final_state,
+                         const kda_plan* plan,
+                         void* workspace, size_t workspace_bytes,
+                         void* stream) {
+    kda_status s = check_prefill_sizes(B, T, H, K, V, dt);
+    if (s != KDA_OK) return s;
+    const long bh = (long)B * H;
+    if (bh > 0 && T > 0) {
+        if (!q || !k || !v || !g || !beta || !o) return KDA_ERR_INVALID_ARG;
+        if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(beta) ||
+            !aligned16(o))
+            return KDA_ERR_INVALID_ARG;
+    }
+    if ((initial_state && !aligned16(initial_state)) || (final_state && !aligned16(final_state)) ||
+        (workspace && !aligned16(workspace)))
+        return KDA_ERR_INVALID_ARG;
+    const size_t state_bytes = (size_t)bh * K * V * sizeof(float);
+    if (initial_state && final_state && ranges_partially_overlap(initial_state, final_state, state_bytes))
+        return KDA_ERR_INVALID_ARG;
+    if (bh == 0) return KDA_OK;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+
+    if (T == 0) {
+        if (!final_state || final_state == initial_state) return KDA_OK;
+        return launch_copy_state(initial_state, final_state, (size_t)bh * K * V, st) == hipSuccess
+                   ? KDA_OK : KDA_ERR_HIP;
+    }
+
+    kda_plan pl;
+    int cps = 1;
+    s = resolve_plan(B, T, H, K, V, dt, plan, &pl, &cps);
+    if (s != KDA_OK) return s;
+    const size_t need = workspace_bytes_for(B, H, K, V, pl);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
+
+    ChunkParams p{};
+    p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta;
+    p.B = B; p.T = T; p.H = H; p.V = V;
+    p.n_seg = pl.n_seg;
+    p.cps = cps;
+    const int vb = pl.v_block;
+
+    if (pl.n_seg == 1) {
+        p.s0 = initial_state;
+        p.o = o;
+        p.sT = final_state;
+        p.n_vb = V / vb;
+        p.summary = 0;
+        return launch_chunk((int)dt, K, vb, p, (int)(bh * (V / vb)), st) == hipSuccess ? KDA_OK
+                                                                                     : KDA_ERR_HIP;
+    }
+
+    float* ws = reinterpret_cast<float*>(workspace);
+    float* wsP = ws;
+    float* wsL = wsP + (size_t)(pl.n_seg - 1) * bh * K * K;
+    float* wsFinal = wsL + (size_t)(pl.n_seg - 1) * bh * K * V;
+
+    // pass 1: per segment (but the last), transition P and local state L
+    ChunkParams p1 = p;
+    p1.summary = 1;
+    p1.n_vb = (K + V) / vb;
+    p1.wsP = wsP;
+    p1.wsL = wsL;
+    if (launch_chunk((int)dt, K, vb, p1, (int)(bh * (pl.n_seg - 1) * p1.n_vb), st) != hipSuccess)
+        return KDA_ERR_HIP;
+    // pass 2: serial combine per (b, h): segment start states, over L
+    ScanParams sp{};
+    sp.s0 = initial_state;
+    sp.wsP = wsP;
+    sp.wsL = wsL;
+    sp.BH = (int)bh;
+    sp.V = V;
+    sp.n_seg = pl.n_seg;
+    if (launch_scan(K, sp, st) != hipSuccess) return KDA_ERR_HIP;
+    // pass 3: every segment from its true start state, with output
+    const bool aliased = final_state && final_state == initial_state;
+    ChunkParams p3 = p;
+    p3.summary = 0;
+    p3.n_vb = V / vb;
+    p3.s0 = initial_state;
+    p3.seg_init = wsL;
+    p3.o = o;
+    p3.sT = aliased ? wsFinal : final_state;
+    if (launch_chunk((int)dt, K, vb, p3, (int)(bh * pl.n_seg * p3.n_vb), st) != hipSuccess)
+        return KDA_ERR_HIP;
+    if (aliased && launch_copy_state(wsFinal, final_state, (size_t)bh * K * V, st) != hipSuccess)
+        return KDA_ERR_HIP;
+    return KDA_OK;
+}
+
+kda_status kda_recurrent_step(int N, int H, int K, int V, kda_dtype dt,
+                              const void* q, const void* k, const void* v,
+                              const void* g, const void* beta,
+                              float* state, void* o, void* stream) {
+    if (N < 0 || H < 0 || K <= 0 || V <= 0) return KDA_ERR_INVALID_ARG;
+    if (check_dtype(dt) != KDA_OK) return KDA_ERR_INVALID_ARG;
+    if (!(K == 64 || K == 128) || !(V == 64 || V == 128)) return KDA_ERR_UNSUPPORTED;
+    if ((double)N * H > 2.0e9) return KDA_ERR_UNSUPPORTED;
+    const long nh = (long)N * H;
+    if (nh == 0) return KDA_OK;
+    if (!q || !k || !v || !g || !beta || !state || !o) return KDA_ERR_INVALID_ARG;
+    if (!aligned16(state)) return KDA_ERR_INVALID_ARG;
+    (void)elem_size;
+    DecodeParams p{};
+    p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta;
+    p.state = state;
+    p.o = o;
+    p.NH = (int)nh;
+    return launch_decode((int)dt, K, V, p, reinterpret_cast<hipStream_t>(stream)) == hipSuccess
+               ? KDA_OK : KDA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,121 @@
+// KDA recurrent decode step for gfx950: one read and one write of the fp32
+// state per (sequence, head) and token.
+//
+// Page: "Kimi K3 — открытая модель, которая обошла закрытых лидеров рынка"
+// (aiblin.ru), section "Как хранить миллион токенов в памяти": a fixed-size
+// state S replaces the KV cache and each token rewrites it (decay by the
+// clamped forget gate alpha in [e^-5, 1], then the delta-rule erase/write
+// with strength beta).  Per (n, h):
+//   S' = Diag(alpha) S ;  y = S'^T k ;  z = S'^T q ;  u = beta (v - y)
+//   S  = S' + k u^T    ;  o = S^T q = z + (q . k) u
+// The value columns are independent, so a workgroup of 256 threads tiles
+// the K x V state as (row group) x (4-column group); partial dot products
+// over rows are combined through LDS, and each thread rewrites exactly the
+// 4-column slices it read (coalesced 16-byte accesses along V).  The kernel
+// is HBM-bound: 8 K V bytes of state traffic against 7 K V flops.
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+template <typename T, int K, int V>
+__global__ __launch_bounds__(256) void kda_decode_kernel(DecodeParams p) {
+    constexpr int CG = V / 4;            // 4-column groups
+    constexpr int RG = 256 / CG;         // row groups
+    constexpr int RPT = K / RG;          // state rows per thread
+    static_assert(CG * RG == 256 && RPT * RG == K, "decode tiling");
+    __shared__ float red[RG][CG][9];
+    __shared__ float qk_part[RG];
+
+    const int nh = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int cg = tid % CG, rg = tid / CG;
+    const T* qp = reinterpret_cast<const T*>(p.q) + (size_t)nh * K;
+    const T* kp = reinterpret_cast<const T*>(p.k) + (size_t)nh * K;
+    const T* gp = reinterpret_cast<const T*>(p.g) + (size_t)nh * K;
+    const T* vp = reinterpret_cast<const T*>(p.v) + (size_t)nh * V;
+    float* S = p.state + (size_t)nh * K * V;
+
+    float s[RPT][4], kk[RPT], qq[RPT];
+    float y[4] = {0.f, 0.f, 0.f, 0.f}, z[4] = {0.f, 0.f, 0.f, 0.f};
+    float qk = 0.f;
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+        const int row = rg * RPT + r;
+        const float4 x = *reinterpret_cast<const float4*>(S + (size_t)row * V + 4 * cg);
+        kk[r] = ld_scalar(kp + row);
+        qq[r] = ld_scalar(qp + row);
+        const float a = fast_exp2(clamp_gate_log2(ld_scalar(gp + row)));
+        s[r][0] = x.x * a;
+        s[r][1] = x.y * a;
+        s[r][2] = x.z * a;
+        s[r][3] = x.w * a;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            y[i] += s[r][i] * kk[r];
+            z[i] += s[r][i] * qq[r];
+        }
+        qk += qq[r] * kk[r];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        red[rg][cg][i] = y[i];
+        red[rg][cg][4 + i] = z[i];
+    }
+    if (cg == 0) qk_part[rg] = qk;
+    __syncthreads();
+    float yf[4] = {0.f, 0.f, 0.f, 0.f}, zf[4] = {0.f, 0.f, 0.f, 0.f};
+    float qkf = 0.f;
+#pragma unroll
+    for (int r = 0; r < RG; ++r) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            yf[i] += red[r][cg][i];
+            zf[i] += red[r][cg][4 + i];
+        }
+        qkf += qk_part[r];
+    }
+    const float beta = ld_scalar(reinterpret_cast<const T*>(p.beta) + nh);
+    float u[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u[i] = beta * (ld_scalar(vp + 4 * cg + i) - yf[i]);
+    if (rg == 0) {
+        T* op = reinterpret_cast<T*>(p.o) + (size_t)nh * V + 4 * cg;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) op[i] = from_f32<T>(zf[i] + qkf * u[i]);
+    }
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+        const int row = rg * RPT + r;
+        float4 x;
+        x.x = s[r][0] + kk[r] * u[0];
+        x.y = s[r][1] + kk[r] * u[1];
+        x.z = s[r][2] + kk[r] * u[2];
+        x.w = s[r][3] + kk[r] * u[3];
+        *reinterpret_cast<float4*>(S + (size_t)row * V + 4 * cg) = x;
+    }
+}
+
+template <typename T, int K, int V>
+static hipError_t launch_decode_t(const DecodeParams& p, hipStream_t stream) {
+    hipLaunchKernelGGL((kda_decode_kernel<T, K, V>), dim3(p.NH), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_decode_kv(int K, int V, const DecodeParams& p, hipStream_t stream) {
+    if (K == 128 && V == 128) return launch_decode_t<T, 128, 128>(p, stream);
+    if (K == 128 && V == 64) return launch_decode_t<T, 128, 64>(p, stream);
+    if (K == 64 && V == 128) return launch_decode_t<T, 64, 128>(p, stream);
+    if (K == 64 && V == 64) return launch_decode_t<T, 64, 64>(p, stream);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode(int dtype, int K, int V, const DecodeParams& p, hipStream_t stream) {
+    if (p.NH <= 0) return hipSuccess;
+    if (dtype == 1) return launch_decode_kv<bf16>(K, V, p, stream);
+    if (dtype == 0) return launch_decode_kv<float>(K, V, p, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace kda

@@ -1,0 +1,172 @@
+// Device-side helpers for the gfx950 KDA kernels: element types, MFMA
+// fragments and their LDS loads.
+//
+// MFMA conventions (v_mfma_f32_16x16x32_bf16 and v_mfma_f32_16x16x4_f32,
+// wave64): for a 16x16 output tile D = A (16 x Kred) * B (Kred x 16),
+//   * accumulator / result: lane l holds D[4*(l/16) + e][l % 16], e = 0..3;
+//   * an operand "fragment" covers a 32-deep slab of the reduction: lane l
+//     holds 8 reduction slots for row (A) or column (B) l % 16, slots owned by
+//     lane group l/16.  Any assignment of reduction indices to slots works
+//     as long as A and B use the same one, so two assignments are used:
+//       natural : slot (g, i) -> 8*g + i            (one 16-byte LDS read)
+//       permuted: slot (g, i) -> 16*(i/4) + 4*g + i%4
+//     The permuted one makes two vertically stacked result tiles, as they sit
+//     in the accumulator registers, a B fragment directly (and a transposed A
+//     fragment), so a state or error tile never leaves registers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+template <typename T> struct FragOf;
+template <> struct FragOf<bf16> { typedef bf16x8 type; };
+template <> struct FragOf<float> { typedef f32x8 type; };
+
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+__device__ __forceinline__ float to_f32(float x) { return x; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }  // RNE
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+
+// ---- MFMA: acc += A * B over one 32-deep slab --------------------------------
+__device__ __forceinline__ f32x4 mma(f32x4 acc, bf16x8 a, bf16x8 b) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma(f32x4 acc, f32x8 a, f32x8 b) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[i], acc, 0, 0, 0);
+    return acc;
+}
+// single 16x16x4 fp32 step (used by the triangular solve)
+__device__ __forceinline__ f32x4 mma4(f32x4 acc, float a, float b) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+}
+
+// ---- fragment construction ----------------------------------------------------
+template <typename T> __device__ __forceinline__ typename FragOf<T>::type frag_from(const float* x);
+template <> __device__ __forceinline__ bf16x8 frag_from<bf16>(const float* x) {
+    bf16x8 r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = (bf16)x[i];
+    return r;
+}
+template <> __device__ __forceinline__ f32x8 frag_from<float>(const float* x) {
+    f32x8 r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = x[i];
+    return r;
+}
+
+// two stacked accumulator tiles -> one permuted-slot fragment
+template <typename T>
+__device__ __forceinline__ typename FragOf<T>::type frag_from_tiles(f32x4 top, f32x4 bot) {
+    float x[8] = {top[0], top[1], top[2], top[3], bot[0], bot[1], bot[2], bot[3]};
+    return frag_from<T>(x);
+}
+
+// natural slots: 8 consecutive elements (16-byte aligned for bf16, 32 for f32)
+template <typename T> __device__ __forceinline__ typename FragOf<T>::type ld_frag(const T* p);
+template <> __device__ __forceinline__ bf16x8 ld_frag<bf16>(const bf16* p) {
+    return *reinterpret_cast<const bf16x8*>(p);
+}
+template <> __device__ __forceinline__ f32x8 ld_frag<float>(const float* p) {
+    f32x4 a = *reinterpret_cast<const f32x4*>(p);
+    f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+    f32x8 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { r[i] = a[i]; r[4 + i] = b[i]; }
+    return r;
+}
+
+// permuted slots: elements p[0..3] and p[16..19]
+template <typename T> __device__ __forceinline__ typename FragOf<T>::type ld_frag_perm(const T* p);
+template <> __device__ __forceinline__ bf16x8 ld_frag_perm<bf16>(const bf16* p) {
+    bf16x4 a = *reinterpret_cast<const bf16x4*>(p);
+    bf16x4 b = *reinterpret_cast<const bf16x4*>(p + 16);
+    bf16x8 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { r[i] = a[i]; r[4 + i] = b[i]; }
+    return r;
+}
+template <> __device__ __forceinline__ f32x8 ld_frag_perm<float>(const float* p) {
+    f32x4 a = *reinterpret_cast<const f32x4*>(p);
+    f32x4 b = *reinterpret_cast<const f32x4*>(p + 16);
+    f32x8 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { r[i] = a[i]; r[4 + i] = b[i]; }
+    return r;
+}
+
+// 8 consecutive fp32 values from LDS (16-byte aligned)
+__device__ __forceinline__ void ld8f(const float* p, float* x) {
+    f32x4 a = *reinterpret_cast<const f32x4*>(p);
+    f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { x[i] = a[i]; x[4 + i] = b[i]; }
+}
+
+// ---- 8-element global I/O in the input dtype ---------------------------------
+// A "pack" is 8 consecutive input elements: 16 bytes of bf16 or 32 of fp32.
+template <typename T> struct Pack8;
+template <> struct Pack8<bf16> {
+    uint4 d;
+    __device__ __forceinline__ void load(const bf16* p) { d = *reinterpret_cast<const uint4*>(p); }
+    __device__ __forceinline__ void zero() { d = make_uint4(0, 0, 0, 0); }
+    __device__ __forceinline__ void to_f32(float* x) const {
+        const uint32_t w[4] = {d.x, d.y, d.z, d.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[2 * i] = __uint_as_float(w[i] << 16);
+            x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+        }
+    }
+};
+template <> struct Pack8<float> {
+    float4 a, b;
+    __device__ __forceinline__ void load(const float* p) {
+        a = *reinterpret_cast<const float4*>(p);
+        b = *reinterpret_cast<const float4*>(p + 4);
+    }
+    __device__ __forceinline__ void zero() { a = make_float4(0, 0, 0, 0); b = a; }
+    __device__ __forceinline__ void to_f32(float* x) const {
+        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    }
+};
+
+// store 8 fp32 values as 8 elements of T (16-byte aligned for bf16)
+__device__ __forceinline__ void st8(bf16* p, const float* x) {
+    bf16x8 r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = (bf16)x[i];
+    *reinterpret_cast<bf16x8*>(p) = r;
+}
+__device__ __forceinline__ void st8(float* p, const float* x) {
+    *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+    *reinterpret_cast<float4*>(p + 4) = make_float4(x[4], x[5], x[6], x[7]);
+}
+
+// ---- scalar math ---------------------------------------------------------------
+constexpr float kLog2e = 1.4426950408889634f;
+
+// exp2 on the hardware transcendental unit (v_exp_f32)
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// forget-gate clamp in log space: log alpha in [-5, 0]; returned in log2 units
+__device__ __forceinline__ float clamp_gate_log2(float g) {
+    return fminf(fmaxf(g, -5.0f), 0.0f) * kLog2e;
+}
+
+__device__ __forceinline__ float ld_scalar(const bf16* p) { return (float)*p; }
+__device__ __forceinline__ float ld_scalar(const float* p) { return *p; }
+
+}  // namespace kda

@@ -1,0 +1,202 @@
+"""ctypes binding of libkda.so (declared in include/kda.h).
+
+Argument marshalling only: every step of KDA runs in the HIP kernels.  torch
+supplies device memory (outputs, workspace) and the current HIP stream.  If
+the library is not built this module raises; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+from .build import LIB_PATH
+
+KDA_OK = 0
+KDA_ERR_INVALID_ARG = 1
+KDA_ERR_UNSUPPORTED = 2
+KDA_ERR_WORKSPACE = 3
+KDA_ERR_HIP = 4
+KDA_F32 = 0
+KDA_BF16 = 1
+
+EXPORTED_SYMBOLS = (
+    "kda_chunk_fwd_plan",
+    "kda_chunk_fwd_workspace_size",
+    "kda_chunk_fwd",
+    "kda_recurrent_step",
+    "kda_status_string",
+    "kda_version",
+)
+
+
+class KDAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s failed: %s (status %d)" % (where, status_string(status), status))
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("n_seg", ctypes.c_int), ("v_block", ctypes.c_int)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libkda.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError("libkda.so is not built (%s); run __graft_entry__.build()" % path)
+    lib = ctypes.CDLL(path)
+    i, p, sz = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+    lib.kda_chunk_fwd_plan.argtypes = [i, i, i, i, i, i, ctypes.POINTER(Plan)]
+    lib.kda_chunk_fwd_plan.restype = i
+    lib.kda_chunk_fwd_workspace_size.argtypes = [i, i, i, i, i, i, ctypes.POINTER(Plan)]
+    lib.kda_chunk_fwd_workspace_size.restype = sz
+    lib.kda_chunk_fwd.argtypes = [i, i, i, i, i, i, p, p, p, p, p, p, p, p,
+                                  ctypes.POINTER(Plan), p, sz, p]
+    lib.kda_chunk_fwd.restype = i
+    lib.kda_recurrent_step.argtypes = [i, i, i, i, i, p, p, p, p, p, p, p, p]
+    lib.kda_recurrent_step.restype = i
+    lib.kda_status_string.argtypes = [i]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_version.argtypes = []
+    lib.kda_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().kda_status_string(int(status)).decode()
+
+
+def version() -> str:
+    return load_library().kda_version().decode()
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return KDA_BF16
+    if dt == torch.float32:
+        return KDA_F32
+    raise TypeError("KDA inputs must be bfloat16 or float32, got %s" % dt)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_ptr(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _plan_arg(plan) -> Optional[Plan]:
+    if plan is None:
+        return None
+    if isinstance(plan, Plan):
+        return plan
+    n_seg, v_block = plan
+    return Plan(int(n_seg), int(v_block))
+
+
+def _check(t: torch.Tensor, name: str, shape, dtype, device):
+    if t.device != device:
+        raise ValueError("%s must be on %s" % (name, device))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if t.dtype != dtype:
+        raise ValueError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def chunk_plan(B: int, T: int, H: int, K: int, V: int, dtype: torch.dtype) -> Tuple[int, int]:
+    """(n_seg, v_block) the library picks for these sizes on the current device."""
+    pl = Plan()
+    st = load_library().kda_chunk_fwd_plan(B, T, H, K, V, _dtype_code(dtype), ctypes.byref(pl))
+    if st != KDA_OK:
+        raise KDAError(st, "kda_chunk_fwd_plan")
+    return pl.n_seg, pl.v_block
+
+
+def chunk_workspace_size(B: int, T: int, H: int, K: int, V: int, dtype: torch.dtype, plan=None) -> int:
+    pl = _plan_arg(plan)
+    n = load_library().kda_chunk_fwd_workspace_size(B, T, H, K, V, _dtype_code(dtype),
+                                                    None if pl is None else ctypes.byref(pl))
+    if n == ctypes.c_size_t(-1).value:
+        raise KDAError(KDA_ERR_INVALID_ARG, "kda_chunk_fwd_workspace_size")
+    return int(n)
+
+
+def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+              beta: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
+              output_final_state: bool = True, plan=None, *,
+              out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
+              workspace: Optional[torch.Tensor] = None):
+    """KDA chunked prefill through ``kda_chunk_fwd``.
+
+    q, k, g: [B, T, H, K]; v: [B, T, H, V]; beta: [B, T, H] (one dtype, bf16
+    or fp32, on one GPU); initial_state: [B, H, K, V] fp32 or None.
+    Returns (o [B, T, H, V], final_state [B, H, K, V] fp32 or None).
+    ``final_state`` may be passed to write in place (it may be
+    ``initial_state`` itself); ``plan`` = (n_seg, v_block), 0 = auto.
+    """
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    dev = q.device
+    dt = q.dtype
+    for name, t, shp in (("q", q, (B, T, H, K)), ("k", k, (B, T, H, K)), ("g", g, (B, T, H, K)),
+                         ("v", v, (B, T, H, V)), ("beta", beta, (B, T, H))):
+        _check(t, name, shp, dt, dev)
+    if initial_state is not None:
+        _check(initial_state, "initial_state", (B, H, K, V), torch.float32, dev)
+    if out is None:
+        out = torch.empty((B, T, H, V), dtype=dt, device=dev)
+    else:
+        _check(out, "out", (B, T, H, V), dt, dev)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((B, H, K, V), dtype=torch.float32, device=dev)
+    elif final_state is not None:
+        _check(final_state, "final_state", (B, H, K, V), torch.float32, dev)
+    pl = _plan_arg(plan)
+    ws_bytes = chunk_workspace_size(B, T, H, K, V, dt, pl)
+    if ws_bytes > 0 and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load_library().kda_chunk_fwd(
+        B, T, H, K, V, _dtype_code(dt), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+        _ptr(initial_state), _ptr(out), _ptr(final_state),
+        None if pl is None else ctypes.byref(pl), _ptr(workspace), ws_len, _stream_ptr(dev))
+    if st != KDA_OK:
+        raise KDAError(st, "kda_chunk_fwd")
+    return out, final_state
+
+
+def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                   beta: torch.Tensor, state: torch.Tensor, *, out: Optional[torch.Tensor] = None):
+    """One KDA decode step through ``kda_recurrent_step``; ``state`` is
+    updated in place.  q, k, g: [N, H, K]; v: [N, H, V]; beta: [N, H];
+    state: [N, H, K, V] fp32.  Returns o [N, H, V]."""
+    N, H, K = q.shape
+    V = v.shape[-1]
+    dev = q.device
+    dt = q.dtype
+    for name, t, shp in (("q", q, (N, H, K)), ("k", k, (N, H, K)), ("g", g, (N, H, K)),
+                         ("v", v, (N, H, V)), ("beta", beta, (N, H))):
+        _check(t, name, shp, dt, dev)
+    _check(state, "state", (N, H, K, V), torch.float32, dev)
+    if out is None:
+        out = torch.empty((N, H, V), dtype=dt, device=dev)
+    else:
+        _check(out, "out", (N, H, V), dt, dev)
+    st = load_library().kda_recurrent_step(N, H, K, V, _dtype_code(dt), _ptr(q), _ptr(k), _ptr(v),
+                                           _ptr(g), _ptr(beta), _ptr(state), _ptr(out),
+                                           _stream_ptr(dev))
+    if st != KDA_OK:
+        raise KDAError(st, "kda_recurrent_step")
+    return out

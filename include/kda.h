@@ -1,0 +1,149 @@
+/*
+ * kda.h — C ABI of the MI355X (gfx950) KDA library, libkda.so.
+ *
+ * KDA (Kimi Delta Attention) is a gated delta-rule linear attention: each
+ * head keeps a fixed-size state S (K x V, fp32) instead of a KV cache, and
+ * every token applies, per batch row b and head h,
+ *
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = S_t^T q_t
+ *
+ * with a per-key-channel forget gate alpha_t = exp(g_t), g clamped to
+ * [-5, 0] (alpha in [e^-5, 1]) inside the library.
+ *
+ * Page: "Kimi K3 — открытая модель, которая обошла закрытых лидеров рынка"
+ * (aiblin.ru).  Section "Как хранить миллион токенов в памяти": the state
+ * matrix S of fixed size, the delta rule (partly erase, then write), beta as
+ * write strength in [0, 1], alpha as forgetting coefficient and its clamp to
+ * [e^-5, 1].  Section "Как распараллелили последовательное обновление":
+ * chunk-parallel evaluation (all tokens of a chunk at once, then the state
+ * passed on, in parallel over heads) and the one-card segment planner for
+ * long prefill (per segment a local state and a transition matrix,
+ * recombined exactly).  The update formula itself is lost on the page; the
+ * equation above is the reading used throughout.
+ *
+ * Conventions for every call:
+ *   - All tensor pointers are DEVICE pointers (HIP), row-major, contiguous,
+ *     16-byte aligned.  The caller owns every buffer, the workspace included;
+ *     the library allocates no memory and keeps no state between calls.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is
+ *     the default stream) of the current HIP device.  Nothing is synchronised.
+ *   - Arguments are validated on the host before anything is launched; on an
+ *     error nothing is launched.  KDA_ERR_INVALID_ARG: a null pointer, a
+ *     negative size, a misaligned pointer, a partially overlapping state
+ *     pair.  KDA_ERR_UNSUPPORTED: sizes or a dtype the kernels do not
+ *     implement.  KDA_ERR_WORKSPACE: workspace missing or too small.
+ *     KDA_ERR_HIP: a HIP launch or query failed.
+ *   - Token tensors (q, k, v, g, beta, o) share one dtype `dt`; states are
+ *     always fp32.  o is rounded to `dt` (round to nearest even).
+ *   - Results are deterministic: no floating-point atomics.
+ *   - Non-finite inputs propagate; they are not detected.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kda_status {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARG = 1,
+    KDA_ERR_UNSUPPORTED = 2,
+    KDA_ERR_WORKSPACE = 3,
+    KDA_ERR_HIP = 4
+} kda_status;
+
+typedef enum kda_dtype {
+    KDA_F32 = 0,
+    KDA_BF16 = 1
+} kda_dtype;
+
+/*
+ * Execution plan of a prefill call.  n_seg: number of sequence segments
+ * evaluated side by side on one card (1 = plain chunk pass; > 1 adds the
+ * segment summary and segment scan passes).  v_block: value columns per
+ * workgroup (64 or 128).  Either field 0 means "let the library choose".
+ * Any valid plan gives the same result up to fp32/bf16 rounding.
+ */
+typedef struct kda_plan {
+    int n_seg;
+    int v_block;
+} kda_plan;
+
+/* Sizes supported by the kernels: K, V in {64, 128}; bf16 or fp32 inputs
+ * (fp32 only with K = 64).  T >= 0 is arbitrary (the tail chunk is masked);
+ * B, H >= 0. */
+
+/*
+ * The plan kda_chunk_fwd would use for these sizes on the current device.
+ * Fills *plan.  Returns KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED or
+ * KDA_ERR_HIP (device query failed).
+ */
+kda_status kda_chunk_fwd_plan(int B, int T, int H, int K, int V, kda_dtype dt,
+                              kda_plan* plan);
+
+/*
+ * Bytes of device workspace kda_chunk_fwd needs for these sizes and plan
+ * (plan NULL or fields 0: the library's choice on the current device).
+ * 0 when no workspace is needed (n_seg = 1); (size_t)-1 for invalid or
+ * unsupported arguments.
+ */
+size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int K, int V, kda_dtype dt,
+                                    const kda_plan* plan);
+
+/*
+ * Chunked prefill (the page's chunk-parallel form, section "Как
+ * распараллелили последовательное обновление"), optionally resuming from an
+ * initial state and returning the final state (the prefix-cache mechanism).
+ *
+ *   q, k, g : [B, T, H, K]  dtype dt   (g = log alpha before the clamp)
+ *   v       : [B, T, H, V]  dtype dt
+ *   beta    : [B, T, H]     dtype dt   (write strength; not clamped)
+ *   initial_state : [B, H, K, V] fp32, or NULL for zeros
+ *   o       : [B, T, H, V]  dtype dt   (written; may be NULL only if T == 0)
+ *   final_state   : [B, H, K, V] fp32, or NULL (not written).  It may alias
+ *                   initial_state exactly (in-place resume); a partial
+ *                   overlap is KDA_ERR_INVALID_ARG.
+ *   plan    : NULL or a kda_plan (fields 0 = library's choice).
+ *   workspace / workspace_bytes : device scratch of at least
+ *             kda_chunk_fwd_workspace_size(...) bytes for the same plan
+ *             (may be NULL when that size is 0).
+ * T == 0 writes final_state = initial_state (or zeros) and nothing else.
+ */
+kda_status kda_chunk_fwd(int B, int T, int H, int K, int V, kda_dtype dt,
+                         const void* q, const void* k, const void* v,
+                         const void* g, const void* beta,
+                         const float* initial_state,
+                         void* o, float* final_state,
+                         const kda_plan* plan,
+                         void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/*
+ * One decode step for N independent sequences (page section "Как хранить
+ * миллион токенов в памяти": the fixed-size state replaces the KV cache).
+ * Reads and writes the state once.
+ *
+ *   q, k, g : [N, H, K] dtype dt;  v : [N, H, V] dtype dt;  beta : [N, H] dtype dt
+ *   state   : [N, H, K, V] fp32, updated IN PLACE to S_t
+ *   o       : [N, H, V] dtype dt (written), o = S_t^T q
+ */
+kda_status kda_recurrent_step(int N, int H, int K, int V, kda_dtype dt,
+                              const void* q, const void* k, const void* v,
+                              const void* g, const void* beta,
+                              float* state, void* o, void* stream);
+
+/* Static description of a status code. */
+const char* kda_status_string(kda_status s);
+
+/* Library version string. */
+const char* kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */

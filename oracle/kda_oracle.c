@@ -48,7 +48,7 @@
 #include <omp.h>
 #endif
 
-#define ORACLE_MAX_COLS 32   /* value columns handled by one work item */
+#define ORACLE_MAX_COLS 16   /* value columns handled by one work item */
 
 static double clamp_log_alpha(double g)
 {

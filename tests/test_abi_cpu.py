@@ -1,0 +1,137 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/kda.h declares, and rejects bad arguments on the host before any HIP
+call (no compute is launched here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_66_amd as kda_pkg
+from gated_delta_rule_66_amd import kda as K_
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+F32, BF16 = 0, 1
+FAKE = 1 << 20          # an aligned, never-dereferenced address
+
+
+def _lib():
+    if not os.path.exists(kda_pkg.LIB_PATH):
+        kda_pkg.build_library()
+    return K_.load_library()
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(kda_[a-z_0-9]+)\s*\(",
+                                 src, flags=re.M)))
+
+
+def test_header_declares_the_expected_calls():
+    decl = _declared_functions()
+    assert decl == sorted(K_.EXPORTED_SYMBOLS), decl
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib()
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    out = os.popen("nm -D --defined-only %s" % kda_pkg.LIB_PATH).read()
+    for name in _declared_functions():
+        assert re.search(r"\bT %s\b" % name, out), name
+
+
+def test_version_and_status_strings():
+    _lib()
+    assert "gfx950" in kda_pkg.version()
+    for s in range(5):
+        assert kda_pkg.status_string(s) and kda_pkg.status_string(s) != "unknown status"
+    assert kda_pkg.status_string(99) == "unknown status"
+
+
+def _fwd(lib, B=1, T=64, H=1, K=128, V=128, dt=BF16, q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE,
+         s0=None, o=FAKE, sT=None, plan=None, ws=None, ws_bytes=0):
+    p = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.kda_chunk_fwd(B, T, H, K, V, dt, p(q), p(k), p(v), p(g), p(beta), p(s0), p(o), p(sT),
+                             None if plan is None else ctypes.byref(plan), p(ws), ws_bytes, None)
+
+
+def test_prefill_rejects_bad_sizes_before_any_launch():
+    lib = _lib()
+    assert _fwd(lib, B=-1) == INVALID
+    assert _fwd(lib, T=-5) == INVALID
+    assert _fwd(lib, H=-1) == INVALID
+    assert _fwd(lib, K=0) == INVALID
+    assert _fwd(lib, dt=7) == INVALID
+    assert _fwd(lib, K=96) == UNSUPPORTED
+    assert _fwd(lib, V=256) == UNSUPPORTED
+    assert _fwd(lib, dt=F32, K=128, V=128) == UNSUPPORTED
+
+
+def test_prefill_rejects_null_and_misaligned_pointers():
+    lib = _lib()
+    for name in ("q", "k", "v", "g", "beta", "o"):
+        assert _fwd(lib, **{name: None}) == INVALID, name
+        assert _fwd(lib, **{name: FAKE + 2}) == INVALID, name
+    assert _fwd(lib, s0=FAKE + 4) == INVALID
+    assert _fwd(lib, sT=FAKE + 8) == INVALID
+
+
+def test_prefill_rejects_partially_overlapping_states():
+    lib = _lib()
+    # B*H*K*V*4 bytes per state; offset by 16 bytes: partial overlap
+    assert _fwd(lib, s0=FAKE, sT=FAKE + 16) == INVALID
+
+
+def test_prefill_workspace_check_with_explicit_plan():
+    lib = _lib()
+    plan = K_.Plan(4, 64)
+    need = lib.kda_chunk_fwd_workspace_size(1, 64 * 40, 2, 128, 128, BF16, ctypes.byref(plan))
+    # (n_seg - 1) * B*H * K*(K+V) + B*H*K*V fp32 words
+    assert need == (3 * 2 * 128 * 256 + 2 * 128 * 128) * 4
+    assert _fwd(lib, T=64 * 40, H=2, plan=plan, ws=None) == WORKSPACE
+    assert _fwd(lib, T=64 * 40, H=2, plan=plan, ws=FAKE, ws_bytes=need - 1) == WORKSPACE
+    one = K_.Plan(1, 128)
+    assert lib.kda_chunk_fwd_workspace_size(1, 64 * 40, 2, 128, 128, BF16, ctypes.byref(one)) == 0
+
+
+def test_prefill_rejects_bad_plans():
+    lib = _lib()
+    assert _fwd(lib, plan=K_.Plan(1, 96)) == INVALID
+    assert _fwd(lib, plan=K_.Plan(-1, 64)) == INVALID
+    assert _fwd(lib, K=64, V=64, plan=K_.Plan(1, 128)) == UNSUPPORTED
+    bad = K_.Plan(1, 96)
+    assert lib.kda_chunk_fwd_workspace_size(1, 64, 1, 128, 128, BF16, ctypes.byref(bad)) == ctypes.c_size_t(-1).value
+
+
+def test_prefill_empty_batch_is_a_no_op():
+    lib = _lib()
+    assert _fwd(lib, B=0, q=None, k=None, v=None, g=None, beta=None, o=None) == OK
+    assert _fwd(lib, H=0, q=None, k=None, v=None, g=None, beta=None, o=None) == OK
+
+
+def test_decode_rejects_bad_arguments():
+    lib = _lib()
+    p = ctypes.c_void_p
+    args = lambda **kw: [kw.get(n, p(FAKE)) for n in ("q", "k", "v", "g", "beta", "state", "o")]
+    assert lib.kda_recurrent_step(-1, 1, 128, 128, BF16, *args(), None) == INVALID
+    assert lib.kda_recurrent_step(1, 1, 100, 128, BF16, *args(), None) == UNSUPPORTED
+    assert lib.kda_recurrent_step(1, 1, 128, 128, 5, *args(), None) == INVALID
+    for name in ("q", "k", "v", "g", "beta", "state", "o"):
+        assert lib.kda_recurrent_step(2, 2, 128, 128, BF16, *args(**{name: None}), None) == INVALID, name
+    assert lib.kda_recurrent_step(2, 2, 128, 128, BF16, *args(state=p(FAKE + 4)), None) == INVALID
+    assert lib.kda_recurrent_step(0, 2, 128, 128, BF16, *args(), None) == OK
+
+
+def test_package_raises_without_library(tmp_path):
+    saved = K_._lib
+    K_._lib = None
+    try:
+        with pytest.raises(RuntimeError):
+            K_.load_library(str(tmp_path / "missing.so"))
+    finally:
+        K_._lib = saved

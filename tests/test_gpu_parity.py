@@ -1,0 +1,342 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 oracle.
+
+Every case prints its name before it touches the GPU.  Inputs are the
+seeded recipes of ``gated_delta_rule_66_amd.inputs``; the oracle always sees
+the exact values the GPU saw (bf16 values upcast, no re-rounding).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gated_delta_rule_66_amd import chunk_fwd, recurrent_step, chunk_plan
+from gated_delta_rule_66_amd.inputs import (CONFIGS, make_decode, make_decode_config, make_prefill,
+                                            make_prefill_config)
+from tests.kda_bruteforce import dense_f64_chain
+from tests.parity import TOL, o_err, s_err
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def say(msg):
+    print("[case] " + msg, flush=True)
+
+
+def to_dev(d):
+    return {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+
+
+def run_oracle(d):
+    return oracle.oracle_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"])
+
+
+def gpu_fwd(x, plan=None, s0="use", **kw):
+    init = x["s0"] if s0 == "use" else s0
+    return chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], init, True, plan, **kw)
+
+
+# ------------------------------------------------------------------ small cases
+def test_config0_full_parity():
+    cfg = CONFIGS["c0"]
+    say("c0 full: B=1 H=2 T=256 K=V=64 fp32")
+    d = make_prefill_config(cfg, "cpu")
+    x = to_dev(d)
+    o, sT = gpu_fwd(x)
+    torch.cuda.synchronize()
+    o_ref, s_ref = run_oracle(d)
+    assert o_err(o, o_ref) < TOL[torch.float32]
+    assert s_err(sT, s_ref) < TOL[torch.float32]
+
+
+SHAPES = [
+    # (K, V, T, B, H, with_s0, plan)
+    (128, 128, 1, 2, 3, True, None),
+    (128, 128, 15, 2, 3, True, None),
+    (128, 128, 16, 1, 2, False, None),
+    (128, 128, 17, 2, 3, True, None),
+    (128, 128, 63, 1, 2, True, None),
+    (128, 128, 64, 2, 3, True, None),
+    (128, 128, 65, 1, 2, True, None),
+    (128, 128, 130, 2, 3, True, (1, 128)),
+    (128, 128, 1000, 1, 3, True, (1, 64)),
+    (128, 128, 1000, 1, 3, True, (1, 128)),
+    (64, 64, 1, 1, 2, True, None),
+    (64, 64, 100, 2, 2, True, None),
+    (64, 64, 640, 1, 2, False, (1, 64)),
+    (128, 64, 300, 1, 2, True, None),
+    (64, 128, 300, 1, 2, True, (1, 128)),
+    (64, 128, 300, 1, 2, True, (1, 64)),
+]
+
+
+@pytest.mark.parametrize("K,V,T,B,H,with_s0,plan", SHAPES)
+def test_prefill_bf16_shapes(K, V, T, B, H, with_s0, plan):
+    say("bf16 prefill K=%d V=%d T=%d B=%d H=%d s0=%s plan=%s" % (K, V, T, B, H, with_s0, plan))
+    d = make_prefill(B, T, H, K, V, torch.bfloat16, seed=100 + T, s0_std=0.02 if with_s0 else None)
+    x = to_dev(d)
+    o, sT = gpu_fwd(x, plan)
+    torch.cuda.synchronize()
+    o_ref, s_ref = run_oracle(d)
+    assert o_err(o, o_ref) < TOL[torch.bfloat16]
+    assert s_err(sT, s_ref) < TOL[torch.bfloat16]
+
+
+@pytest.mark.parametrize("dtype,K,V", [(torch.bfloat16, 128, 128), (torch.bfloat16, 64, 64),
+                                       (torch.float32, 64, 64)])
+@pytest.mark.parametrize("n_seg", [2, 3, 7])
+def test_segment_planner_matches_oracle(dtype, K, V, n_seg):
+    """Segment transitions computed side by side and recombined: the result
+    must not depend on the number of segments (page section on the one-card
+    segment planner)."""
+    T = 64 * 37 + 5
+    say("segments dtype=%s K=%d V=%d n_seg=%d T=%d" % (dtype, K, V, n_seg, T))
+    d = make_prefill(1, T, 2, K, V, dtype, seed=7, s0_std=0.02)
+    x = to_dev(d)
+    o_ref, s_ref = run_oracle(d)
+    for vb in sorted({64, min(128, K, V)}):
+        o, sT = gpu_fwd(x, (n_seg, vb))
+        torch.cuda.synchronize()
+        assert o_err(o, o_ref) < TOL[dtype], vb
+        assert s_err(sT, s_ref) < TOL[dtype], vb
+
+
+# ------------------------------------------------------------------ pins on the GPU
+@pytest.mark.parametrize("plan", [(1, 64), (1, 128), (3, 64)])
+def test_p1_no_forget_no_write(plan):
+    say("P1 alpha=1 beta=0 plan=%s" % (plan,))
+    d = make_prefill(1, 300, 2, 128, 128, torch.bfloat16, seed=11, s0_std=1.0)
+    d["g"].zero_()
+    d["beta"].zero_()
+    x = to_dev(d)
+    o, sT = gpu_fwd(x, plan)
+    torch.cuda.synchronize()
+    assert torch.equal(sT, x["s0"]), "state must be unchanged bit for bit"
+    o_ref, _ = run_oracle(d)
+    assert o_err(o, o_ref) < TOL[torch.bfloat16]
+
+
+@pytest.mark.parametrize("dtype,K", [(torch.bfloat16, 128), (torch.float32, 64)])
+def test_p2_full_write_unit_key(dtype, K):
+    say("P2 alpha=1 beta=1 basis keys dtype=%s" % dtype)
+    T, H = 200, 2
+    gen = torch.Generator().manual_seed(12)
+    idx = torch.randint(0, K, (1, T, H), generator=gen)
+    k = torch.nn.functional.one_hot(idx, K).to(dtype)
+    v = torch.randn(1, T, H, K, generator=gen).to(dtype)
+    d = dict(q=k.clone(), k=k, v=v, g=torch.zeros_like(k), beta=torch.ones(1, T, H, dtype=dtype),
+             s0=torch.randn(1, H, K, K, generator=gen))
+    x = to_dev(d)
+    o, _ = gpu_fwd(x)
+    torch.cuda.synchronize()
+    assert o_err(o, v) < TOL[dtype]
+
+
+def test_p3_clamp_bitwise():
+    say("P3 clamp: g=-50 == g=-5, g=+3 == g=0, bitwise")
+    d = make_prefill(2, 257, 2, 128, 128, torch.bfloat16, seed=13, s0_std=0.02)
+    x = to_dev(d)
+    outs = []
+    for val in (-5.0, -50.0, 0.0, 3.0):
+        x["g"].fill_(val)
+        outs.append(gpu_fwd(x))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    assert torch.equal(outs[2][0], outs[3][0]) and torch.equal(outs[2][1], outs[3][1])
+    # mixed out-of-range channels against the oracle (the all-floor stress run)
+    g = d["g"].float()
+    g[..., ::2] = -9.0
+    g[..., 1::2] = -5.0
+    d["g"] = g.to(torch.bfloat16)
+    x = to_dev(d)
+    o, sT = gpu_fwd(x)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(sT).all()
+    o_ref, s_ref = run_oracle(d)
+    assert o_err(o, o_ref) < TOL[torch.bfloat16]
+    assert s_err(sT, s_ref) < TOL[torch.bfloat16]
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 5, 8])
+def test_p5_dense_expansion_short(T):
+    say("P5 dense transition expansion T=%d" % T)
+    d = make_prefill(1, T, 1, 64, 64, torch.float32, seed=20 + T, s0_std=0.5)
+    x = to_dev(d)
+    o, sT = gpu_fwd(x)
+    torch.cuda.synchronize()
+    od, sd = dense_f64_chain(d["q"][0, :, 0].numpy(), d["k"][0, :, 0].numpy(), d["v"][0, :, 0].numpy(),
+                             d["g"][0, :, 0].numpy(), d["beta"][0, :, 0].numpy(), d["s0"][0, 0].numpy())
+    assert o_err(o, od[None, :, None, :]) < TOL[torch.float32]
+    assert s_err(sT, sd[None, None]) < TOL[torch.float32]
+
+
+@pytest.mark.parametrize("plan", [None, (2, 64)])
+def test_p6_split_and_resume(plan):
+    say("P6 split/resume plan=%s" % (plan,))
+    T1, T2 = 700, 555
+    d = make_prefill(1, T1 + T2, 3, 128, 128, torch.bfloat16, seed=14, s0_std=0.02)
+    x = to_dev(d)
+    o_full, s_full = gpu_fwd(x, plan)
+    a = {k: (v[:, :T1].contiguous() if k != "s0" else v) for k, v in x.items()}
+    o1, s1 = gpu_fwd(a, plan)
+    b = {k: (v[:, T1:].contiguous() if k != "s0" else v) for k, v in x.items()}
+    o2, s2 = gpu_fwd(b, plan, s0=s1)
+    torch.cuda.synchronize()
+    o_ref, s_ref = run_oracle(d)
+    assert o_err(torch.cat([o1, o2], 1), o_ref) < TOL[torch.bfloat16]
+    assert s_err(s2, s_ref) < TOL[torch.bfloat16]
+    assert o_err(o_full, o_ref) < TOL[torch.bfloat16]
+    assert s_err(s_full, s_ref) < TOL[torch.bfloat16]
+
+
+def test_p7_linearity():
+    say("P7 linear in (S0, V)")
+    d = make_prefill(1, 333, 2, 128, 128, torch.bfloat16, seed=15, s0_std=0.05)
+    x = to_dev(d)
+    o, s = gpu_fwd(x)
+    xa = dict(x)
+    xa["v"] = torch.zeros_like(x["v"])
+    oa, sa = gpu_fwd(xa)
+    ob, sb = gpu_fwd(x, s0=None)
+    torch.cuda.synchronize()
+    assert o_err(oa.float() + ob.float(), o.float()) < TOL[torch.bfloat16]
+    assert s_err(sa + sb, s) < TOL[torch.bfloat16]
+
+
+def test_p8_prefill_then_decode_equals_longer_prefill():
+    say("P8 prefill(T1) + decode x n == prefill(T1 + n); T=1 prefill == one decode step")
+    T1, n = 190, 6
+    d = make_prefill(2, T1 + n, 3, 128, 128, torch.bfloat16, seed=16, s0_std=0.02)
+    x = to_dev(d)
+    a = {k: (v[:, :T1].contiguous() if k != "s0" else v) for k, v in x.items()}
+    o1, s = gpu_fwd(a)
+    state = s.clone()
+    outs = []
+    for t in range(T1, T1 + n):
+        outs.append(recurrent_step(x["q"][:, t].contiguous(), x["k"][:, t].contiguous(),
+                                   x["v"][:, t].contiguous(), x["g"][:, t].contiguous(),
+                                   x["beta"][:, t].contiguous(), state))
+    torch.cuda.synchronize()
+    o_ref, s_ref = run_oracle(d)
+    o_dec = torch.stack(outs, 1)
+    assert o_err(torch.cat([o1, o_dec], 1), o_ref) < TOL[torch.bfloat16]
+    assert s_err(state, s_ref) < TOL[torch.bfloat16]
+    # one token: prefill and the decode kernel agree
+    one = {k: (v[:, :1].contiguous() if k != "s0" else v) for k, v in x.items()}
+    o_p, s_p = gpu_fwd(one)
+    st = x["s0"].clone()
+    o_d = recurrent_step(x["q"][:, 0].contiguous(), x["k"][:, 0].contiguous(), x["v"][:, 0].contiguous(),
+                         x["g"][:, 0].contiguous(), x["beta"][:, 0].contiguous(), st)
+    torch.cuda.synchronize()
+    assert o_err(o_p, o_d[:, None]) < TOL[torch.bfloat16]
+    assert s_err(s_p, st) < 1e-3
+
+
+@pytest.mark.parametrize("plan", [(1, 64), (4, 64)])
+def test_in_place_state_resume(plan):
+    say("final_state aliasing initial_state plan=%s" % (plan,))
+    d = make_prefill(1, 64 * 20 + 9, 2, 128, 128, torch.bfloat16, seed=17, s0_std=0.02)
+    x = to_dev(d)
+    state = x["s0"].clone()
+    o, s = chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], state, True, plan, final_state=state)
+    torch.cuda.synchronize()
+    assert s.data_ptr() == state.data_ptr()
+    o_ref, s_ref = run_oracle(d)
+    assert o_err(o, o_ref) < TOL[torch.bfloat16]
+    assert s_err(state, s_ref) < TOL[torch.bfloat16]
+
+
+def test_empty_sequence_copies_state():
+    say("T=0")
+    d = make_prefill(2, 0, 3, 128, 128, torch.bfloat16, seed=18, s0_std=0.02)
+    x = to_dev(d)
+    o, s = gpu_fwd(x)
+    torch.cuda.synchronize()
+    assert o.shape == (2, 0, 3, 128)
+    assert torch.equal(s, x["s0"])
+    _, s0 = gpu_fwd(x, s0=None)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(s0) == 0
+
+
+def test_deterministic_repeat():
+    say("bitwise repeatability")
+    d = make_prefill(1, 64 * 30, 4, 128, 128, torch.bfloat16, seed=19, s0_std=0.02)
+    x = to_dev(d)
+    for plan in ((1, 64), (3, 128)):
+        a = gpu_fwd(x, plan)
+        b = gpu_fwd(x, plan)
+        torch.cuda.synchronize()
+        assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+# ------------------------------------------------------------------ decode
+@pytest.mark.parametrize("dtype,K,V", [(torch.bfloat16, 128, 128), (torch.bfloat16, 64, 128),
+                                       (torch.bfloat16, 128, 64), (torch.float32, 64, 64),
+                                       (torch.float32, 128, 128)])
+def test_decode_steps_match_oracle(dtype, K, V):
+    say("decode dtype=%s K=%d V=%d" % (dtype, K, V))
+    N, H, steps = 5, 3, 16
+    d = make_decode(N, H, K, V, steps, dtype, seed=21)
+    x = to_dev(d)
+    state = x["state"].clone()
+    ref_state = d["state"].double().numpy().copy()
+    for t in range(steps):
+        o = recurrent_step(x["q"][t], x["k"][t], x["v"][t], x["g"][t], x["beta"][t], state)
+        o_ref = oracle.oracle_step(d["q"][t], d["k"][t], d["v"][t], d["g"][t], d["beta"][t], ref_state)
+        torch.cuda.synchronize()
+        assert max_rel(o, o_ref) < TOL[dtype], t
+    assert s_err(state, ref_state) < TOL[dtype]
+
+
+def max_rel(o, o_ref):
+    # decode output [N, H, V]: chains (n, h)
+    from tests.parity import max_rel_l2
+    return max_rel_l2(o, o_ref, (0, 1))
+
+
+# ------------------------------------------------------------------ full-size workloads
+def _sampled_oracle(x, chains):
+    """Oracle on selected (b, h) chains of device inputs; returns lists."""
+    outs = []
+    for b, h in chains:
+        sl = lambda t: t[b:b + 1, :, h:h + 1].contiguous().cpu()
+        s0 = None if x["s0"] is None else x["s0"][b:b + 1, h:h + 1].cpu()
+        o_ref, s_ref = oracle.oracle_fwd(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["g"]), sl(x["beta"]), s0)
+        outs.append((o_ref, s_ref))
+    return outs
+
+
+@pytest.mark.parametrize("name,chains", [("c1", [(0, 0), (0, 7), (0, 19), (0, 31)]),
+                                         ("c2", [(0, 3), (5, 17), (7, 31)]),
+                                         ("c3", [(0, 11)])])
+def test_full_size_prefill_sampled(name, chains):
+    cfg = CONFIGS[name]
+    plan = chunk_plan(cfg.B, cfg.T, cfg.H, cfg.K, cfg.V, cfg.dtype)
+    say("full %s B=%d T=%d H=%d plan=%s, oracle on chains %s" % (name, cfg.B, cfg.T, cfg.H, plan, chains))
+    x = make_prefill_config(cfg, DEV)
+    o, sT = chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], True, None)
+    torch.cuda.synchronize()
+    assert torch.isfinite(sT).all()
+    refs = _sampled_oracle(x, chains)
+    for (b, h), (o_ref, s_ref) in zip(chains, refs):
+        assert o_err(o[b:b + 1, :, h:h + 1], o_ref) < TOL[cfg.dtype], (b, h)
+        assert s_err(sT[b:b + 1, h:h + 1], s_ref) < TOL[cfg.dtype], (b, h)
+    del x, o, sT
+    torch.cuda.empty_cache()
+
+
+def test_full_size_decode_sampled():
+    cfg = CONFIGS["c4"]
+    say("full c4 decode N=%d H=%d steps=%d, oracle on 8 sequences" % (cfg.N, cfg.H, cfg.steps))
+    x = make_decode_config(cfg, DEV)
+    sel = torch.arange(0, cfg.N, cfg.N // 8)
+    ref_state = x["state"][sel].double().cpu().numpy().copy()
+    state = x["state"].clone()
+    for t in range(cfg.steps):
+        o = recurrent_step(x["q"][t], x["k"][t], x["v"][t], x["g"][t], x["beta"][t], state)
+        o_ref = oracle.oracle_step(x["q"][t][sel].cpu(), x["k"][t][sel].cpu(), x["v"][t][sel].cpu(),
+                                   x["g"][t][sel].cpu(), x["beta"][t][sel].cpu(), ref_state)
+        assert max_rel(o[sel], o_ref) < TOL[cfg.dtype], t
+    torch.cuda.synchronize()
+    assert s_err(state[sel], ref_state) < TOL[cfg.dtype]
