@@ -61,9 +61,10 @@ kda_status resolve_plan(int B, int T, int H, int K, int V, kda_dtype dt, const k
         kda_status s = device_cus(&cus);
         if (s != KDA_OK) return s;
     }
-    if (vb != 0) {
+    const bool vb_fixed = vb != 0;
+    if (vb_fixed) {
         if (vb != 64 && vb != 128) return KDA_ERR_INVALID_ARG;
-        if (vb > K || vb > V || !chunk_variant_exists((int)dt, K, vb)) return KDA_ERR_UNSUPPORTED;
+        if (vb > V || !chunk_variant_exists((int)dt, K, vb)) return KDA_ERR_UNSUPPORTED;
     } else {
         // the widest block that still gives every CU a workgroup, else 64
         vb = 64;
@@ -88,6 +89,11 @@ kda_status resolve_plan(int B, int T, int H, int K, int V, kda_dtype dt, const k
     if (ns < 1) ns = 1;
     int cps = n_chunks > 0 ? (n_chunks + ns - 1) / ns : 1;
     if (n_chunks > 0) ns = (n_chunks + cps - 1) / cps;   // no empty segments
+    // the summary pass carries the K transition columns in whole blocks
+    if (ns > 1 && K % vb != 0) {
+        if (vb_fixed) return KDA_ERR_UNSUPPORTED;
+        vb = 64;
+    }
     out->n_seg = ns;
     out->v_block = vb;
     if (cps_out) *cps_out = cps;
@@ -147,8 +153,8 @@ kda_status kda_chunk_fwd(int B, int T, int H, int K, int V, kda_dtype dt,
     const long bh = (long)B * H;
     if (bh > 0 && T > 0) {
         if (!q || !k || !v || !g || !beta || !o) return KDA_ERR_INVALID_ARG;
-        if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(beta) ||
-            !aligned16(o))
+        if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(o) ||
+            (reinterpret_cast<uintptr_t>(beta) % elem_size(dt)) != 0)
             return KDA_ERR_INVALID_ARG;
     }
     if ((initial_state && !aligned16(initial_state)) || (final_state && !aligned16(final_state)) ||
@@ -240,7 +246,9 @@ kda_status kda_recurrent_step(int N, int H, int K, int V, kda_dtype dt,
     if (nh == 0) return KDA_OK;
     if (!q || !k || !v || !g || !beta || !state || !o) return KDA_ERR_INVALID_ARG;
     if (!aligned16(state)) return KDA_ERR_INVALID_ARG;
-    (void)elem_size;
+    const uintptr_t es = elem_size(dt);
+    for (const void* t : {q, k, v, g, beta, (const void*)o})
+        if (reinterpret_cast<uintptr_t>(t) % es != 0) return KDA_ERR_INVALID_ARG;
     DecodeParams p{};
     p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta;
     p.state = state;

@@ -40,40 +40,45 @@ namespace {
 
 constexpr int C = kChunk;
 
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
 template <typename T, int K, int NW>
 struct ChunkLayout {
     static constexpr int VB = 16 * NW;           // value columns per workgroup
     static constexpr int NT = 64 * NW;           // threads
     static constexpr int SZ = (int)sizeof(T);
-    static constexpr int PAD = 16 / SZ;          // 16 bytes of padding per row
-    static constexpr int LDK = K + PAD;          // [token][channel] rows
+    static constexpr int PAD = 16 / SZ;          // 16 bytes of row padding
+    static constexpr int LDK1 = K + PAD;         // Kd, Qd, Kinv: [token][channel], 16-byte reads
+    static constexpr int LDK2 = K + 4;           // W, Q e^G: [token][channel], 8/16-byte reads
     static constexpr int LDT = C + PAD;          // [channel][token] rows
-    static constexpr int LDA = C + 4;            // fp32 A / Tm rows
+    static constexpr int LDL = C + 4;            // solve blocks / Mqk: [token][token]
+    static constexpr int LDD = 16;               // fp32 diagonal blocks of A
     static constexpr int LDO = VB + PAD;         // output staging rows
-    static constexpr int NAT = C * LDK * SZ;     // one [C][LDK] buffer
-    // region KQ: phase A = Kd | Qd | Kinv ; phase B = W | X (solve scratch) | O
-    static constexpr int X_BYTES = 3 * 16 * 16 * 4;
-    static constexpr int KQ_A = 3 * NAT;
-    static constexpr int KQ_B = NAT + X_BYTES + C * LDO * SZ;
-    static constexpr int KQ = KQ_A > KQ_B ? KQ_A : KQ_B;
-    // region G: phase A = G (fp32 cumsum) ; phase B = A/Tm (fp32) | Mqk
-    static constexpr int G_A = C * K * 4;
-    static constexpr int G_B = C * LDA * 4 + C * LDT * SZ;
-    static constexpr int GR = G_A > G_B ? G_A : G_B;
+    // prep mappings: a thread owns 2 adjacent channels and a run of tokens
+    static constexpr int CPK = K / 2, PK = NT / CPK, TPK = C / PK;
+    static constexpr int CPV = VB / 2, PV = NT / CPV, TPV = C / PV;
+    // region KQ: Kd | Qd | Kinv (prep -> A/Mqk), then W | O (solve -> store)
+    static constexpr int NAT1 = C * LDK1 * SZ;
+    static constexpr int W_BYTES = C * LDK2 * SZ;
+    static constexpr int KQ = cmax(3 * NAT1, W_BYTES + C * LDO * SZ);
+    // region R: prep partial sums, then the solve blocks (L) and fp32 diagonals
+    static constexpr int PART_BYTES = 2 * PK * K * 4;
+    static constexpr int L_BYTES = C * LDL * SZ;
+    static constexpr int R = cmax(PART_BYTES, L_BYTES + 4 * 16 * LDD * 4);
     static constexpr int oKQ = 0;
-    static constexpr int oG = oKQ + KQ;
-    static constexpr int oKhbT = oG + GR;               // [K][LDT] beta K e^{G}, transposed
-    static constexpr int oQh = oKhbT + K * LDT * SZ;    // [C][LDK] Q e^{G}
-    static constexpr int oKbT = oQh + NAT;              // [K][LDT] K e^{G_C-G}, transposed
-    static constexpr int oVbT = oKbT + K * LDT * SZ;    // [VB][LDT] beta V, transposed
-    static constexpr int oF = oVbT + VB * LDT * SZ;     // fp32 [6][K] block-pair gate factors
-    static constexpr int oEGC = oF + 6 * K * 4;         // fp32 [K] e^{G_C}
-    static constexpr int oBeta = oEGC + K * 4;          // fp32 [C]
-    static constexpr int oPart = oBeta + C * 4;         // fp32 [NT] cumsum partial sums
-    static constexpr int TOTAL = oPart + NT * 4;
+    static constexpr int oR = oKQ + KQ;
+    static constexpr int oMqk = oR + R;                  // [C][LDL]
+    static constexpr int oQh = oMqk + C * LDL * SZ;      // [C][LDK2] Q e^{G}
+    static constexpr int oKhbT = oQh + C * LDK2 * SZ;    // [K][LDT] beta K e^{G}, channel-major
+    static constexpr int oKbT = oKhbT + K * LDT * SZ;    // [K][LDT] K e^{G_C-G}, channel-major
+    static constexpr int oVbT = oKbT + K * LDT * SZ;     // [VB][LDT] beta V, channel-major
+    static constexpr int oF = oVbT + VB * LDT * SZ;      // fp32 [6][K] e^{G_b(i) - G_b(j)}
+    static constexpr int oEGC = oF + 6 * K * 4;          // fp32 [K] e^{G_C}
+    static constexpr int oBeta = oEGC + K * 4;           // fp32 [C]
+    static constexpr int TOTAL = oBeta + C * 4;
     static_assert(TOTAL <= 160 * 1024, "LDS budget exceeded");
-    static_assert(NW >= 3, "the triangular solve needs three waves");
-    static_assert(NT % K == 0 && C % (NT / K) == 0, "cumsum mapping");
+    static_assert(CPK * PK == NT && TPK * PK == C && (TPK == 4 || TPK == 8 || TPK == 16), "key prep mapping");
+    static_assert(CPV * PV == NT && TPV == 8, "value prep mapping");
 };
 
 // lower block pairs (i >= j) of the 4 x 4 sub-chunk grid
@@ -94,40 +99,54 @@ __device__ __forceinline__ void ld8_as_f32(const T* p, float* x) {
     for (int i = 0; i < 8; ++i) x[i] = to_f32(f[i]);
 }
 
+// G (log2 units) at the first token of 16-token block `blk`, for channels
+// c and c+1, from the per-part sums and first values.
+template <int PK, int TPK, int K>
+__device__ __forceinline__ float2 block_ref(const float* sPart, const float* sFirst, int blk, int c) {
+    const int pb = 16 * blk / TPK;
+    float2 r = *reinterpret_cast<const float2*>(&sFirst[pb * K + c]);
+    for (int pp = 0; pp < pb; ++pp) {
+        const float2 s = *reinterpret_cast<const float2*>(&sPart[pp * K + c]);
+        r.x += s.x;
+        r.y += s.y;
+    }
+    return r;
+}
+
 }  // namespace
 
 template <typename T, int K, int NW>
 __global__ __launch_bounds__(64 * NW) void kda_chunk_kernel(ChunkParams p) {
     using L = ChunkLayout<T, K, NW>;
     using Frag = typename FragOf<T>::type;
-    constexpr int VB = L::VB, NT = L::NT;
-    constexpr int LDK = L::LDK, LDT = L::LDT, LDA = L::LDA, LDO = L::LDO;
-    constexpr int NK8 = K / 8;                // 8-element packs per key row
-    constexpr int NV8 = VB / 8;               // 8-element packs per value row
-    constexpr int REPK = C * NK8 / NT;
-    constexpr int REPV = C * NV8 / NT;
-    constexpr int KS = K / 32;                // reduction slabs over key channels
-    constexpr int CT = K / 16;                // 16-row tiles of the state
-    static_assert(REPK * NT == C * NK8 && REPV * NT == C * NV8, "load mapping");
+    using Frag4 = typename Frag4Of<T>::type;
+    constexpr int VB = L::VB;
+    constexpr int LDK1 = L::LDK1, LDK2 = L::LDK2, LDT = L::LDT, LDL = L::LDL, LDD = L::LDD, LDO = L::LDO;
+    constexpr int CPK = L::CPK, PK = L::PK, TPK = L::TPK;
+    constexpr int CPV = L::CPV, TPV = L::TPV;
+    constexpr int NV8 = VB / 8;
+    constexpr int REPO = C * NV8 / L::NT;      // output store packs per thread
+    constexpr int KS = K / 32;                 // 32-deep slabs over key channels
+    constexpr int CT = K / 16;                 // 16-row tiles of the state
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
     T* sKd = reinterpret_cast<T*>(smem + L::oKQ);
-    T* sQd = sKd + C * LDK;
-    T* sKinv = sQd + C * LDK;
+    T* sQd = sKd + C * LDK1;
+    T* sKinv = sQd + C * LDK1;
     T* sW = reinterpret_cast<T*>(smem + L::oKQ);
-    float* sX = reinterpret_cast<float*>(smem + L::oKQ + L::NAT);
-    T* sO = reinterpret_cast<T*>(smem + L::oKQ + L::NAT + L::X_BYTES);
-    float* sG = reinterpret_cast<float*>(smem + L::oG);
-    float* sA = reinterpret_cast<float*>(smem + L::oG);
-    T* sMqk = reinterpret_cast<T*>(smem + L::oG + C * LDA * 4);
-    T* sKhbT = reinterpret_cast<T*>(smem + L::oKhbT);
+    T* sO = reinterpret_cast<T*>(smem + L::oKQ + L::W_BYTES);
+    float* sPart = reinterpret_cast<float*>(smem + L::oR);
+    float* sFirst = sPart + PK * K;
+    T* sL = reinterpret_cast<T*>(smem + L::oR);
+    float* sAd = reinterpret_cast<float*>(smem + L::oR + L::L_BYTES);
+    T* sMqk = reinterpret_cast<T*>(smem + L::oMqk);
     T* sQh = reinterpret_cast<T*>(smem + L::oQh);
+    T* sKhbT = reinterpret_cast<T*>(smem + L::oKhbT);
     T* sKbT = reinterpret_cast<T*>(smem + L::oKbT);
     T* sVbT = reinterpret_cast<T*>(smem + L::oVbT);
     float* sF = reinterpret_cast<float*>(smem + L::oF);
     float* sEGC = reinterpret_cast<float*>(smem + L::oEGC);
     float* sBeta = reinterpret_cast<float*>(smem + L::oBeta);
-    float* sPart = reinterpret_cast<float*>(smem + L::oPart);
 
     const int tid = threadIdx.x;
     const int w = tid >> 6, l = tid & 63, lg = l >> 4, lr = l & 15;
@@ -153,16 +172,20 @@ __global__ __launch_bounds__(64 * NW) void kda_chunk_kernel(ChunkParams p) {
 
     // summary pass columns: [0, K) carry the transition P (start I, values 0),
     // [K, K+V) the local state L (start 0, the real values)
-    const int col0 = vb * VB;                           // first column of the block
+    const int col0 = vb * VB;
     const bool pmode = p.summary && col0 < K;
-    const int vcol0 = p.summary ? (pmode ? 0 : col0 - K) : col0;   // first value column
-    const int my_col = col0 + 16 * w + lr;              // this lane's column (block space)
+    const int vcol0 = p.summary ? (pmode ? 0 : col0 - K) : col0;
+    const int my_col = col0 + 16 * w + lr;
 
     const T* __restrict__ qg = reinterpret_cast<const T*>(p.q);
     const T* __restrict__ kg = reinterpret_cast<const T*>(p.k);
     const T* __restrict__ vg = reinterpret_cast<const T*>(p.v);
     const T* __restrict__ gg = reinterpret_cast<const T*>(p.g);
     const T* __restrict__ bg = reinterpret_cast<const T*>(p.beta);
+
+    // prep mapping: key side (channels 2cp, 2cp+1; tokens pk*TPK ..), value side
+    const int cp = tid % CPK, pk = tid / CPK;
+    const int vp = tid % CPV, pv = tid / CPV;
 
     // ---- initial state: S[ct] = rows 16ct + 4lg + e, column my_col --------
     f32x4 S[CT];
@@ -185,244 +208,247 @@ __global__ __launch_bounds__(64 * NW) void kda_chunk_kernel(ChunkParams p) {
         }
     }
 
+    // ---- raw chunk registers (loaded one chunk ahead) ------------------------
+    // (kept raw: converting at load time would make every load wait)
+    Pack2<T> kr[TPK], qr[TPK], gr[TPK], vr[TPV];
+    T br[TPK];
+    // global addressing: a buffer resource at the chunk's first row (scalar
+    // registers), a 32-bit lane byte offset and a scalar per-token offset;
+    // one chunk of one head spans far less than 2^32 bytes
+    constexpr unsigned SZ = sizeof(T);
+    const unsigned rowK = (unsigned)p.H * K * SZ, rowV = (unsigned)p.H * V * SZ, rowB = (unsigned)p.H * SZ;
+    const unsigned vK = (unsigned)pk * TPK * rowK + 2u * cp * SZ;   // lane offsets
+    const unsigned vB = (unsigned)pk * TPK * rowB;
+    const unsigned vV = (unsigned)pv * TPV * rowV + 2u * vp * SZ;
+    auto load_chunk = [&](int ci) {
+        const int t0 = ci * C;
+        const int nt = min(C, p.T - t0);
+        const size_t head_row = (size_t)(b * (size_t)p.T + t0) * p.H + h;   // token t0 of (b, h)
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + head_row * K);
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(qg + head_row * K);
+        const __amdgpu_buffer_rsrc_t rg = make_rsrc(gg + head_row * K);
+        const __amdgpu_buffer_rsrc_t rb = make_rsrc(bg + head_row);
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + head_row * V + vcol0);
+#pragma unroll
+        for (int i = 0; i < TPK; ++i) {
+            const int t = pk * TPK + i;
+            if (t < nt) {
+                buf_load2<T>(kr[i], rk, vK, i * rowK);
+                buf_load2<T>(gr[i], rg, vK, i * rowK);
+                if (!p.summary) buf_load2<T>(qr[i], rq, vK, i * rowK); else qr[i].zero();
+                buf_load1(br[i], rb, vB, i * rowB);
+            } else {
+                kr[i].zero();
+                gr[i].zero();
+                qr[i].zero();
+                br[i] = from_f32<T>(0.f);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < TPV; ++i) {
+            const int t = pv * TPV + i;
+            if (t < nt && !pmode) buf_load2<T>(vr[i], rv, vV, i * rowV);
+            else vr[i].zero();
+        }
+    };
+    if (c_begin < c_end) load_chunk(c_begin);
+
     for (int ci = c_begin; ci < c_end; ++ci) {
         const int t0 = ci * C;
         const int nt = min(C, p.T - t0);
 
-        // ---- P0: stream the chunk in ----------------------------------------
-        Pack8<T> kr[REPK], qr[REPK], vr[REPV];
-#pragma unroll
-        for (int r = 0; r < REPK; ++r) {
-            const int it = tid + r * NT;
-            const int t = it / NK8, c8 = it % NK8;
-            float gx[8];
-            if (t < nt) {
-                const size_t off = ((size_t)(b * (size_t)p.T + t0 + t) * p.H + h) * K + 8 * c8;
-                kr[r].load(kg + off);
-                if (!p.summary) qr[r].load(qg + off); else qr[r].zero();
-                Pack8<T> gp;
-                gp.load(gg + off);
-                gp.to_f32(gx);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) gx[e] = clamp_gate_log2(gx[e]);
-            } else {
-                kr[r].zero();
-                qr[r].zero();
-#pragma unroll
-                for (int e = 0; e < 8; ++e) gx[e] = 0.f;
-            }
-            st8(&sG[t * K + 8 * c8], gx);
-        }
-#pragma unroll
-        for (int r = 0; r < REPV; ++r) {
-            const int it = tid + r * NT;
-            const int t = it / NV8, n8 = it % NV8;
-            if (t < nt && !pmode) {
-                const size_t off = ((size_t)(b * (size_t)p.T + t0 + t) * p.H + h) * V + vcol0 + 8 * n8;
-                vr[r].load(vg + off);
-            } else {
-                vr[r].zero();
-            }
-        }
-        if (tid < C)
-            sBeta[tid] = (tid < nt) ? ld_scalar(bg + (size_t)(b * (size_t)p.T + t0 + tid) * p.H + h) : 0.f;
-        __syncthreads();
-
-        // ---- P1: beta V (transposed) and the in-chunk gate cumsum ------------
-#pragma unroll
-        for (int r = 0; r < REPV; ++r) {
-            const int it = tid + r * NT;
-            const int t = it / NV8, n8 = it % NV8;
-            float x8[8];
-            vr[r].to_f32(x8);
-            const float bt = sBeta[t];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) sVbT[(8 * n8 + e) * LDT + t] = from_f32<T>(bt * x8[e]);
-        }
+        // ---- P1: in-chunk gate cumsum, part totals ----------------------------
+        float gl0[TPK], gl1[TPK];
         {
-            constexpr int P = NT / K, R = C / P;
-            const int c = tid % K, part = tid / K;
-            float s = 0.f;
+            float s0 = 0.f, s1 = 0.f;
 #pragma unroll
-            for (int i = 0; i < R; ++i) s += sG[(part * R + i) * K + c];
-            sPart[part * K + c] = s;
-            __syncthreads();
-            float run = 0.f;
-            for (int pp = 0; pp < part; ++pp) run += sPart[pp * K + c];
+            for (int i = 0; i < TPK; ++i) {
+                s0 += clamp_gate_log2(gr[i].lo());
+                s1 += clamp_gate_log2(gr[i].hi());
+                gl0[i] = s0;
+                gl1[i] = s1;
+            }
+            *reinterpret_cast<float2*>(&sPart[pk * K + 2 * cp]) = make_float2(s0, s1);
+            *reinterpret_cast<float2*>(&sFirst[pk * K + 2 * cp]) = make_float2(gl0[0], gl1[0]);
+            if (cp == 0) {
 #pragma unroll
-            for (int i = 0; i < R; ++i) {
-                run += sG[(part * R + i) * K + c];
-                sG[(part * R + i) * K + c] = run;
+                for (int i = 0; i < TPK; ++i) sBeta[pk * TPK + i] = to_f32(br[i]);
             }
         }
         __syncthreads();
 
-        // ---- P2: key/query-side operands -------------------------------------
-        for (int idx = tid; idx < K; idx += NT) sEGC[idx] = fast_exp2(sG[(C - 1) * K + idx]);
-        for (int idx = tid; idx < 6 * K; idx += NT) {
-            int i, j;
-            offdiag_pair(idx / K, i, j);
-            const int c = idx % K;
-            sF[idx] = fast_exp2(sG[16 * i * K + c] - sG[16 * j * K + c]);
+        // ---- P2: key/query-side operands (one pass, registers -> LDS) ---------
+        {
+            float off0 = 0.f, off1 = 0.f, tot0 = 0.f, tot1 = 0.f;
+            for (int pp = 0; pp < PK; ++pp) {
+                const float2 sp = *reinterpret_cast<const float2*>(&sPart[pp * K + 2 * cp]);
+                if (pp < pk) { off0 += sp.x; off1 += sp.y; }
+                tot0 += sp.x;
+                tot1 += sp.y;
+            }
+            const float2 gb = block_ref<PK, TPK, K>(sPart, sFirst, (pk * TPK) / 16, 2 * cp);
+            const float egb0 = fast_exp2(gb.x), egb1 = fast_exp2(gb.y);            // e^{G_b}      <= 1
+            const float ecb0 = fast_exp2(tot0 - gb.x), ecb1 = fast_exp2(tot1 - gb.y);  // e^{G_C-G_b} <= 1
+            float kh0[TPK], kh1[TPK], kb0[TPK], kb1[TPK];
+#pragma unroll
+            for (int i = 0; i < TPK; ++i) {
+                const int t = pk * TPK + i;
+                const float d0 = off0 + gl0[i] - gb.x, d1 = off1 + gl1[i] - gb.y;  // G_t - G_b <= 0
+                const float e10 = fast_exp2(d0), e11 = fast_exp2(d1);     // e^{G_t-G_b}
+                const float e20 = fast_exp2(-d0), e21 = fast_exp2(-d1);   // e^{G_b-G_t} <= e^75
+                const float k0 = kr[i].lo(), k1 = kr[i].hi();
+                const float q0 = qr[i].lo(), q1 = qr[i].hi();
+                const float bt = to_f32(br[i]);
+                st2(&sKd[t * LDK1 + 2 * cp], k0 * e10, k1 * e11);
+                st2(&sKinv[t * LDK1 + 2 * cp], k0 * e20, k1 * e21);
+                if (!p.summary) {
+                    st2(&sQd[t * LDK1 + 2 * cp], q0 * e10, q1 * e11);
+                    st2(&sQh[t * LDK2 + 2 * cp], q0 * e10 * egb0, q1 * e11 * egb1);
+                }
+                kh0[i] = bt * k0 * e10 * egb0;     // beta e^{G_t}
+                kh1[i] = bt * k1 * e11 * egb1;
+                kb0[i] = k0 * e20 * ecb0;          // e^{G_C-G_t}
+                kb1[i] = k1 * e21 * ecb1;
+            }
+            st_run<TPK>(&sKhbT[(2 * cp) * LDT + pk * TPK], kh0);
+            st_run<TPK>(&sKhbT[(2 * cp + 1) * LDT + pk * TPK], kh1);
+            st_run<TPK>(&sKbT[(2 * cp) * LDT + pk * TPK], kb0);
+            st_run<TPK>(&sKbT[(2 * cp + 1) * LDT + pk * TPK], kb1);
+            if (pk == 0) *reinterpret_cast<float2*>(&sEGC[2 * cp]) = make_float2(fast_exp2(tot0), fast_exp2(tot1));
+            for (int pr = pk; pr < 6; pr += PK) {
+                int i, j;
+                offdiag_pair(pr, i, j);
+                const float2 gi = block_ref<PK, TPK, K>(sPart, sFirst, i, 2 * cp);
+                const float2 gj = block_ref<PK, TPK, K>(sPart, sFirst, j, 2 * cp);
+                *reinterpret_cast<float2*>(&sF[pr * K + 2 * cp]) =
+                    make_float2(fast_exp2(gi.x - gj.x), fast_exp2(gi.y - gj.y));
+            }
+            // beta V, channel-major
+            float bv0[TPV], bv1[TPV];
+#pragma unroll
+            for (int i = 0; i < TPV; ++i) {
+                const float bt = sBeta[pv * TPV + i];
+                bv0[i] = bt * vr[i].lo();
+                bv1[i] = bt * vr[i].hi();
+            }
+            st_run<TPV>(&sVbT[(2 * vp) * LDT + pv * TPV], bv0);
+            st_run<TPV>(&sVbT[(2 * vp + 1) * LDT + pv * TPV], bv1);
         }
-#pragma unroll
-        for (int r = 0; r < REPK; ++r) {
-            const int it = tid + r * NT;
-            const int t = it / NK8, c8 = it % NK8;
-            float g8[8], gb8[8], gc8[8], kx[8], qx[8];
-            ld8f(&sG[t * K + 8 * c8], g8);
-            ld8f(&sG[(t & ~15) * K + 8 * c8], gb8);
-            ld8f(&sG[(C - 1) * K + 8 * c8], gc8);
-            kr[r].to_f32(kx);
-            qr[r].to_f32(qx);
-            const float bt = sBeta[t];
-            float kd[8], ki[8], kh[8], kb[8], qd[8], qh[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float e0 = fast_exp2(g8[e]);              // e^{G_t}         <= 1
-                const float e1 = fast_exp2(g8[e] - gb8[e]);     // e^{G_t - G_b}   <= 1
-                const float e2 = fast_exp2(gb8[e] - g8[e]);     // e^{G_b - G_t}   <= e^75
-                const float e3 = fast_exp2(gc8[e] - g8[e]);     // e^{G_C - G_t}   <= 1
-                kd[e] = kx[e] * e1;
-                ki[e] = kx[e] * e2;
-                kh[e] = bt * kx[e] * e0;
-                kb[e] = kx[e] * e3;
-                qd[e] = qx[e] * e1;
-                qh[e] = qx[e] * e0;
-            }
-            st8(&sKd[t * LDK + 8 * c8], kd);
-            st8(&sKinv[t * LDK + 8 * c8], ki);
-            if (!p.summary) {
-                st8(&sQd[t * LDK + 8 * c8], qd);
-                st8(&sQh[t * LDK + 8 * c8], qh);
-            }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                sKhbT[(8 * c8 + e) * LDT + t] = from_f32<T>(kh[e]);
-                sKbT[(8 * c8 + e) * LDT + t] = from_f32<T>(kb[e]);
-            }
-        }
+        // the raw registers are consumed: fetch the next chunk behind the compute
+        // (the scheduling fence keeps the loads from being hoisted above the
+        // last uses, which would hold two chunks in registers)
+        __builtin_amdgcn_sched_barrier(0);
+        if (ci + 1 < c_end) load_chunk(ci + 1);
         __syncthreads();
 
         // ---- P3: A and Mqk, one 16 x 16 block pair per wave at a time ---------
-        // (writes region G, whose gate cumsum is no longer needed)
-        for (int pi = w; pi < 10; pi += NW) {
-            int i, j;
-            lower_pair(pi, i, j);
-            f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accM = {0.f, 0.f, 0.f, 0.f};
+        // A's diagonal blocks go to fp32 (for the block inverses), its
+        // off-diagonal blocks to the solve buffer negated; Mqk blocks (0,1)
+        // and (2,3) are zero (read by the 32-deep slabs of the output).
+        for (int task = w; task < 12; task += NW) {
+            if (task < 10) {
+                int i, j;
+                lower_pair(task, i, j);
+                f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accM = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const int c0 = 32 * ks + 8 * lg;
-                const Frag ak = ld_frag<T>(&sKd[(16 * i + lr) * LDK + c0]);
-                float kv[8];
-                ld8_as_f32<T>(&sKinv[(16 * j + lr) * LDK + c0], kv);
-                if (i != j) {
-                    float f[8];
-                    ld8f(&sF[(i * (i - 1) / 2 + j) * K + c0], f);
+                for (int ks = 0; ks < KS; ++ks) {
+                    const int c0 = 32 * ks + 8 * lg;
+                    const Frag ak = ld_frag<T>(&sKd[(16 * i + lr) * LDK1 + c0]);
+                    float kv[8];
+                    ld8_as_f32<T>(&sKinv[(16 * j + lr) * LDK1 + c0], kv);
+                    if (i != j) {
+                        float f[8];
+                        ld8f(&sF[(i * (i - 1) / 2 + j) * K + c0], f);
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) kv[e] *= f[e];
+                        for (int e = 0; e < 8; ++e) kv[e] *= f[e];
+                    }
+                    const Frag bk = frag_from<T>(kv);
+                    accA = mma(accA, ak, bk);
+                    if (!p.summary) accM = mma(accM, ld_frag<T>(&sQd[(16 * i + lr) * LDK1 + c0]), bk);
                 }
-                const Frag bk = frag_from<T>(kv);
-                accA = mma(accA, ak, bk);
-                if (!p.summary) accM = mma(accM, ld_frag<T>(&sQd[(16 * i + lr) * LDK + c0]), bk);
-            }
-            const int r = 16 * j + lr;
+                const int r = 16 * j + lr;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int s = 16 * i + 4 * lg + e;
-                sA[s * LDA + r] = (i > j || r < s) ? sBeta[s] * accA[e] : 0.f;
-                if (!p.summary) sMqk[s * LDT + r] = from_f32<T>((i > j || r <= s) ? accM[e] : 0.f);
-            }
-        }
-        for (int idx = tid; idx < C * C; idx += NT) {
-            const int s = idx / C, r = idx % C;
-            if ((r >> 4) > (s >> 4)) {
-                sA[s * LDA + r] = 0.f;
-                if (!p.summary) sMqk[s * LDT + r] = from_f32<T>(0.f);
+                for (int e = 0; e < 4; ++e) {
+                    const int s = 16 * i + 4 * lg + e;
+                    const float a = sBeta[s] * accA[e];
+                    if (i == j) sAd[(i * 16 + 4 * lg + e) * LDD + lr] = (r < s) ? a : 0.f;
+                    else sL[s * LDL + r] = from_f32<T>(-a);
+                    if (!p.summary) sMqk[s * LDL + r] = from_f32<T>((i > j || r <= s) ? accM[e] : 0.f);
+                }
+            } else if (!p.summary) {
+                const int i = (task == 10) ? 0 : 2, j = i + 1;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sMqk[(16 * i + 4 * lg + e) * LDL + 16 * j + lr] = from_f32<T>(0.f);
             }
         }
         __syncthreads();
 
-        // ---- P4: Tm = (I + A)^{-1} in place, fp32 ------------------------------
-        // diagonal 16 x 16 blocks by forward substitution, one lane per column
+        // ---- P4: inverses D_i = (I + A_ii)^{-1} of the diagonal blocks --------
+        // forward substitution in fp32, one lane per (block, column)
         if (w == 0) {
             const int i = lg, j = lr;
             float xv[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
+                float row[16];
+#pragma unroll
+                for (int m4 = 0; m4 < 4; ++m4) {
+                    const f32x4 a4 = *reinterpret_cast<const f32x4*>(&sAd[(i * 16 + r) * LDD + 4 * m4]);
+                    row[4 * m4] = a4[0];
+                    row[4 * m4 + 1] = a4[1];
+                    row[4 * m4 + 2] = a4[2];
+                    row[4 * m4 + 3] = a4[3];
+                }
                 float acc = (r == j) ? 1.f : 0.f;
 #pragma unroll
-                for (int m = 0; m < r; ++m) acc -= sA[(16 * i + r) * LDA + 16 * i + m] * xv[m];
+                for (int m = 0; m < r; ++m) acc -= row[m] * xv[m];
                 xv[r] = acc;
             }
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sA[(16 * i + r) * LDA + 16 * i + j] = xv[r];
+            for (int r = 0; r < 16; ++r) sL[(16 * i + r) * LDL + 16 * i + j] = from_f32<T>(xv[r]);
         }
         __syncthreads();
-        // row blocks below: Tm_ij = -D_i sum_{k=j}^{i-1} A_ik Tm_kj (fp32 MFMA)
-#pragma unroll
-        for (int i = 1; i < 4; ++i) {
-            if (w < i) {
-                const int j = w;
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-                for (int kk = 16 * j; kk < 16 * i; kk += 4)
-                    acc = mma4(acc, sA[(16 * i + lr) * LDA + kk + lg], sA[(kk + lg) * LDA + 16 * j + lr]);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) sX[j * 256 + (4 * lg + e) * 16 + lr] = acc[e];
-            }
-            __syncthreads();
-            if (w < i) {
-                const int j = w;
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int mm = 0; mm < 16; mm += 4)
-                    acc = mma4(acc, sA[(16 * i + lr) * LDA + 16 * i + mm + lg], sX[j * 256 + (mm + lg) * 16 + lr]);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) sA[(16 * i + 4 * lg + e) * LDA + 16 * j + lr] = -acc[e];
-            }
-            __syncthreads();
-        }
 
-        // ---- P5: W = Tm (beta K e^G) (shared), U~ = Tm (beta V) (per wave) ---
-        Frag Tf[4][2];
+        // ---- P5: W = (I+A)^{-1} beta K e^G and U~ = (I+A)^{-1} beta V ---------
+        // block forward substitution per 16-column tile, tiles in registers:
+        //   X_i = D_i (R_i - sum_{k<i} A_ik X_k)
+        Frag4 Ld[4], Lo[6];
 #pragma unroll
-        for (int ti = 0; ti < 4; ++ti) {
+        for (int i = 0; i < 4; ++i) Ld[i] = ld_frag4<T>(&sL[(16 * i + lr) * LDL + 16 * i + 4 * lg]);
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                if (ks <= (ti >> 1)) {
-                    float xv[8];
-                    ld8f(&sA[(16 * ti + lr) * LDA + 32 * ks + 8 * lg], xv);
-                    Tf[ti][ks] = frag_from<T>(xv);
-                }
-            }
+        for (int q6 = 0; q6 < 6; ++q6) {
+            const int i = (q6 >= 3) ? 3 : (q6 >= 1) ? 2 : 1;
+            const int k = q6 - i * (i - 1) / 2;
+            Lo[q6] = ld_frag4<T>(&sL[(16 * i + lr) * LDL + 16 * k + 4 * lg]);
         }
+        auto solve_tile = [&](const T* rhs, f32x4* X) {
+            // rhs: channel-major row of this tile's first column; R_i read as
+            // an accumulator tile (rows 16i + 4lg + e, column lr)
+            Frag4 Xb[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                f32x4 acc = ld4_as_f32<T>(rhs + lr * LDT + 16 * i + 4 * lg);
+#pragma unroll
+                for (int k = 0; k < i; ++k) acc = mma16(acc, Lo[i * (i - 1) / 2 + k], Xb[k]);
+                X[i] = mma16(f32x4{0.f, 0.f, 0.f, 0.f}, Ld[i], frag4_from<T>(acc));
+                Xb[i] = frag4_from<T>(X[i]);
+            }
+        };
         for (int ct = w; ct < CT; ct += NW) {
-            Frag bk[2];
+            f32x4 X[4];
+            solve_tile(&sKhbT[16 * ct * LDT], X);
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) bk[ks] = ld_frag<T>(&sKhbT[(16 * ct + lr) * LDT + 32 * ks + 8 * lg]);
-#pragma unroll
-            for (int ti = 0; ti < 4; ++ti) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-                    if (ks <= (ti >> 1)) acc = mma(acc, Tf[ti][ks], bk[ks]);
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    sW[(16 * ti + 4 * lg + e) * LDK + 16 * ct + lr] = from_f32<T>(acc[e]);
-            }
+                    sW[(16 * i + 4 * lg + e) * LDK2 + 16 * ct + lr] = from_f32<T>(X[i][e]);
         }
         f32x4 Ut[4];
-#pragma unroll
-        for (int ti = 0; ti < 4; ++ti) Ut[ti] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (!pmode) {
-            Frag bv[2];
+            solve_tile(&sVbT[16 * w * LDT], Ut);
+        } else {
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) bv[ks] = ld_frag<T>(&sVbT[(16 * w + lr) * LDT + 32 * ks + 8 * lg]);
-#pragma unroll
-            for (int ti = 0; ti < 4; ++ti)
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-                    if (ks <= (ti >> 1)) Ut[ti] = mma(Ut[ti], Tf[ti][ks], bv[ks]);
+            for (int i = 0; i < 4; ++i) Ut[i] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
         __syncthreads();
 
@@ -436,7 +462,7 @@ __global__ __launch_bounds__(64 * NW) void kda_chunk_kernel(ChunkParams p) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
-                acc = mma(acc, ld_frag_perm<T>(&sW[(16 * ti + lr) * LDK + 32 * ks + 4 * lg]), Sb[ks]);
+                acc = mma(acc, ld_frag_perm<T>(&sW[(16 * ti + lr) * LDK2 + 32 * ks + 4 * lg]), Sb[ks]);
             U[ti] = Ut[ti] - acc;
         }
         Frag Ub[2];
@@ -448,11 +474,11 @@ __global__ __launch_bounds__(64 * NW) void kda_chunk_kernel(ChunkParams p) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks)
-                    acc = mma(acc, ld_frag_perm<T>(&sQh[(16 * ti + lr) * LDK + 32 * ks + 4 * lg]), Sb[ks]);
+                    acc = mma(acc, ld_frag_perm<T>(&sQh[(16 * ti + lr) * LDK2 + 32 * ks + 4 * lg]), Sb[ks]);
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks)
                     if (ks <= (ti >> 1))
-                        acc = mma(acc, ld_frag_perm<T>(&sMqk[(16 * ti + lr) * LDT + 32 * ks + 4 * lg]), Ub[ks]);
+                        acc = mma(acc, ld_frag_perm<T>(&sMqk[(16 * ti + lr) * LDL + 32 * ks + 4 * lg]), Ub[ks]);
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     sO[(16 * ti + 4 * lg + e) * LDO + 16 * w + lr] = from_f32<T>(acc[e]);
@@ -470,16 +496,16 @@ __global__ __launch_bounds__(64 * NW) void kda_chunk_kernel(ChunkParams p) {
 
         // ---- P7: stream the chunk's output out ---------------------------------
         if (!p.summary) {
-            T* og = reinterpret_cast<T*>(p.o);
+            const __amdgpu_buffer_rsrc_t ro =
+                make_rsrc(reinterpret_cast<T*>(p.o) + ((size_t)(b * (size_t)p.T + t0) * p.H + h) * V + vcol0);
 #pragma unroll
-            for (int r = 0; r < REPV; ++r) {
-                const int it = tid + r * NT;
+            for (int r = 0; r < REPO; ++r) {
+                const int it = tid + r * L::NT;
                 const int t = it / NV8, n8 = it % NV8;
                 if (t < nt) {
-                    const size_t off = ((size_t)(b * (size_t)p.T + t0 + t) * p.H + h) * V + vcol0 + 8 * n8;
-                    *reinterpret_cast<uint4*>(og + off) = *reinterpret_cast<const uint4*>(&sO[t * LDO + 8 * n8]);
-                    if (sizeof(T) == 4)
-                        *reinterpret_cast<uint4*>(og + off + 4) = *reinterpret_cast<const uint4*>(&sO[t * LDO + 8 * n8 + 4]);
+                    const unsigned off = (unsigned)t * rowV + 8u * n8 * SZ;
+                    buf_store16(ro, off, 0, *reinterpret_cast<const uint4*>(&sO[t * LDO + 8 * n8]));
+                    if (SZ == 4) buf_store16(ro, off + 16, 0, *reinterpret_cast<const uint4*>(&sO[t * LDO + 8 * n8 + 4]));
                 }
             }
         }

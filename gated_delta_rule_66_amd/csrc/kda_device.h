@@ -46,9 +46,39 @@ __device__ __forceinline__ f32x4 mma(f32x4 acc, f32x8 a, f32x8 b) {
     for (int i = 0; i < 8; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[i], acc, 0, 0, 0);
     return acc;
 }
-// single 16x16x4 fp32 step (used by the triangular solve)
-__device__ __forceinline__ f32x4 mma4(f32x4 acc, float a, float b) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+// ---- MFMA over a 16-deep slab (16x16x16 bf16 / four 16x16x4 fp32) --------------
+// Slot (g, i) of lane l holds reduction index 4*g + i (g = l/16): a result tile
+// in accumulator layout is a B operand of this shape as it stands.
+template <typename T> struct Frag4Of;
+template <> struct Frag4Of<bf16> { typedef bf16x4 type; };
+template <> struct Frag4Of<float> { typedef f32x4 type; };
+
+__device__ __forceinline__ f32x4 mma16(f32x4 acc, bf16x4 a, bf16x4 b) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, acc, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma16(f32x4 acc, f32x4 a, f32x4 b) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[i], acc, 0, 0, 0);
+    return acc;
+}
+template <typename T> __device__ __forceinline__ typename Frag4Of<T>::type frag4_from(f32x4 x);
+template <> __device__ __forceinline__ bf16x4 frag4_from<bf16>(f32x4 x) {
+    bf16x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = (bf16)x[i];
+    return r;
+}
+template <> __device__ __forceinline__ f32x4 frag4_from<float>(f32x4 x) { return x; }
+// 4 consecutive elements (8-byte aligned for bf16, 16 for fp32)
+template <typename T> __device__ __forceinline__ typename Frag4Of<T>::type ld_frag4(const T* p) {
+    return *reinterpret_cast<const typename Frag4Of<T>::type*>(p);
+}
+template <typename T> __device__ __forceinline__ f32x4 ld4_as_f32(const T* p) {
+    typename Frag4Of<T>::type f = ld_frag4<T>(p);
+    f32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = to_f32(f[i]);
+    return r;
 }
 
 // ---- fragment construction ----------------------------------------------------
@@ -112,6 +142,92 @@ __device__ __forceinline__ void ld8f(const float* p, float* x) {
     f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
 #pragma unroll
     for (int i = 0; i < 4; ++i) { x[i] = a[i]; x[4 + i] = b[i]; }
+}
+
+// ---- 2-element (channel pair) global / LDS I/O in the input dtype ------------
+template <typename T> struct Pack2;
+template <> struct Pack2<bf16> {
+    uint32_t d;
+    __device__ __forceinline__ void load(const bf16* p) { d = *reinterpret_cast<const uint32_t*>(p); }
+    __device__ __forceinline__ void zero() { d = 0u; }
+    __device__ __forceinline__ float lo() const { return __uint_as_float(d << 16); }
+    __device__ __forceinline__ float hi() const { return __uint_as_float(d & 0xffff0000u); }
+};
+template <> struct Pack2<float> {
+    float2 d;
+    __device__ __forceinline__ void load(const float* p) { d = *reinterpret_cast<const float2*>(p); }
+    __device__ __forceinline__ void zero() { d = make_float2(0.f, 0.f); }
+    __device__ __forceinline__ float lo() const { return d.x; }
+    __device__ __forceinline__ float hi() const { return d.y; }
+};
+__device__ __forceinline__ void st2(bf16* p, float a, float b) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    bf16x2 r;
+    r[0] = (bf16)a;
+    r[1] = (bf16)b;
+    *reinterpret_cast<bf16x2*>(p) = r;
+}
+__device__ __forceinline__ void st2(float* p, float a, float b) {
+    *reinterpret_cast<float2*>(p) = make_float2(a, b);
+}
+// N consecutive values stored as N elements of T (N * sizeof(T) >= 8 bytes,
+// aligned to min(16, N * sizeof(T)))
+template <int N> __device__ __forceinline__ void st_run(bf16* p, const float* x) {
+    static_assert(N % 4 == 0, "run length");
+    if constexpr (N % 8 == 0) {
+#pragma unroll
+        for (int j = 0; j < N; j += 8) {
+            bf16x8 r;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) r[i] = (bf16)x[j + i];
+            *reinterpret_cast<bf16x8*>(p + j) = r;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < N; j += 4) {
+            bf16x4 r;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) r[i] = (bf16)x[j + i];
+            *reinterpret_cast<bf16x4*>(p + j) = r;
+        }
+    }
+}
+template <int N> __device__ __forceinline__ void st_run(float* p, const float* x) {
+    static_assert(N % 4 == 0, "run length");
+#pragma unroll
+    for (int j = 0; j < N; j += 4)
+        *reinterpret_cast<float4*>(p + j) = make_float4(x[j], x[j + 1], x[j + 2], x[j + 3]);
+}
+
+// ---- buffer (descriptor-based) global access -------------------------------------
+// A raw buffer resource over a chunk's base address: the base lives in scalar
+// registers and every lane adds only a 32-bit byte offset, plus a wave-uniform
+// scalar offset per load.  No range clamping (records = 0xffffffff); callers
+// mask out-of-range rows themselves.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)0xffffffff, 0x00020000);
+}
+template <typename T> __device__ __forceinline__ void buf_load2(Pack2<T>& x, __amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff);
+template <> __device__ __forceinline__ void buf_load2<bf16>(Pack2<bf16>& x, __amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
+    x.d = __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
+}
+template <> __device__ __forceinline__ void buf_load2<float>(Pack2<float>& x, __amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
+    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0);
+    x.d = make_float2(__uint_as_float(v[0]), __uint_as_float(v[1]));
+}
+// one element, kept raw (converted when used)
+__device__ __forceinline__ void buf_load1(bf16& x, __amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
+    const unsigned short u = __builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, (int)soff, 0);
+    x = __builtin_bit_cast(bf16, u);
+}
+__device__ __forceinline__ void buf_load1(float& x, __amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
+    x = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0));
+}
+__device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff, uint4 v) {
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    u32x4 x = {v.x, v.y, v.z, v.w};
+    __builtin_amdgcn_raw_buffer_store_b128(x, r, (int)voff, (int)soff, 0);
 }
 
 // ---- 8-element global I/O in the input dtype ---------------------------------

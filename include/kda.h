@@ -23,9 +23,12 @@
  * equation above is the reading used throughout.
  *
  * Conventions for every call:
- *   - All tensor pointers are DEVICE pointers (HIP), row-major, contiguous,
- *     16-byte aligned.  The caller owns every buffer, the workspace included;
- *     the library allocates no memory and keeps no state between calls.
+ *   - All tensor pointers are DEVICE pointers (HIP), row-major, contiguous.
+ *     Alignment: states and the workspace 16 bytes; for prefill q, k, v, g
+ *     and o 16 bytes and beta its element size; for decode every token
+ *     tensor its element size.  The caller owns every buffer, the workspace
+ *     included; the library allocates no memory and keeps no state between
+ *     calls.
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is
  *     the default stream) of the current HIP device.  Nothing is synchronised.
  *   - Arguments are validated on the host before anything is launched; on an
@@ -65,7 +68,8 @@ typedef enum kda_dtype {
  * Execution plan of a prefill call.  n_seg: number of sequence segments
  * evaluated side by side on one card (1 = plain chunk pass; > 1 adds the
  * segment summary and segment scan passes).  v_block: value columns per
- * workgroup (64 or 128).  Either field 0 means "let the library choose".
+ * workgroup (64 or 128; at most V, and with n_seg > 1 it must divide K).
+ * Either field 0 means "let the library choose".
  * Any valid plan gives the same result up to fp32/bf16 rounding.
  */
 typedef struct kda_plan {

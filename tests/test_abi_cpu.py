@@ -76,7 +76,10 @@ def test_prefill_rejects_null_and_misaligned_pointers():
     lib = _lib()
     for name in ("q", "k", "v", "g", "beta", "o"):
         assert _fwd(lib, **{name: None}) == INVALID, name
+    for name in ("q", "k", "v", "g", "o"):
         assert _fwd(lib, **{name: FAKE + 2}) == INVALID, name
+    assert _fwd(lib, beta=FAKE + 1) == INVALID
+    assert _fwd(lib, dt=F32, K=64, V=64, beta=FAKE + 2) == INVALID
     assert _fwd(lib, s0=FAKE + 4) == INVALID
     assert _fwd(lib, sT=FAKE + 8) == INVALID
 
@@ -104,6 +107,8 @@ def test_prefill_rejects_bad_plans():
     assert _fwd(lib, plan=K_.Plan(1, 96)) == INVALID
     assert _fwd(lib, plan=K_.Plan(-1, 64)) == INVALID
     assert _fwd(lib, K=64, V=64, plan=K_.Plan(1, 128)) == UNSUPPORTED
+    # a segmented plan needs value blocks that tile the K transition columns
+    assert _fwd(lib, T=64 * 40, K=64, V=128, plan=K_.Plan(2, 128), ws=FAKE, ws_bytes=1 << 30) == UNSUPPORTED
     bad = K_.Plan(1, 96)
     assert lib.kda_chunk_fwd_workspace_size(1, 64, 1, 128, 128, BF16, ctypes.byref(bad)) == ctypes.c_size_t(-1).value
 
