@@ -42,43 +42,47 @@ constexpr int C = kChunk;
 
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
 
-template <typename T, int K, int NW>
+template <typename T, int K, int NTW>
 struct ChunkLayout {
-    static constexpr int VB = 16 * NW;           // value columns per workgroup
+    static constexpr int NW = 4;                 // waves (one per SIMD)
+    static constexpr int VB = 16 * NW * NTW;     // value columns per workgroup (NTW 16-col tiles per wave)
     static constexpr int NT = 64 * NW;           // threads
     static constexpr int SZ = (int)sizeof(T);
     static constexpr int PAD = 16 / SZ;          // 16 bytes of row padding
     static constexpr int LDK1 = K + PAD;         // Kd, Qd, Kinv: [token][channel], 16-byte reads
-    static constexpr int LDK2 = K + 4;           // W, Q e^G: [token][channel], 8/16-byte reads
+    static constexpr int LDK2 = K + PAD;         // W, Q e^G: [token][channel], 16-byte rows
     static constexpr int LDT = C + PAD;          // [channel][token] rows
     static constexpr int LDL = C + 4;            // solve blocks / Mqk: [token][token]
     static constexpr int LDD = 16;               // fp32 diagonal blocks of A
-    static constexpr int LDO = VB + PAD;         // output staging rows
-    // prep mappings: a thread owns 2 adjacent channels and a run of tokens
-    static constexpr int CPK = K / 2, PK = NT / CPK, TPK = C / PK;
-    static constexpr int CPV = VB / 2, PV = NT / CPV, TPV = C / PV;
-    // region KQ: Kd | Qd | Kinv (prep -> A/Mqk), then W | O (solve -> store)
+    // prep: wave w owns CPW groups of 8 key channels for all 64 tokens; lane
+    // = (group, part of TPL consecutive tokens); likewise CPWV groups of 8
+    // value columns with TPLV tokens per lane
+    static constexpr int CPW = K / (8 * NW);
+    static constexpr int TPL = CPW;
+    static constexpr int NPART = 64 / CPW;
+    static constexpr int CPWV = VB / (8 * NW);
+    static constexpr int TPLV = CPWV;
+    // region KQ: Kd | Qd | Kinv (prep -> A/Mqk), then W (solve -> state pass)
     static constexpr int NAT1 = C * LDK1 * SZ;
-    static constexpr int W_BYTES = C * LDK2 * SZ;
-    static constexpr int KQ = cmax(3 * NAT1, W_BYTES + C * LDO * SZ);
-    // region R: prep partial sums, then the solve blocks (L) and fp32 diagonals
-    static constexpr int PART_BYTES = 2 * PK * K * 4;
+    static constexpr int KQ = cmax(3 * NAT1, C * LDK2 * SZ);
     static constexpr int L_BYTES = C * LDL * SZ;
-    static constexpr int R = cmax(PART_BYTES, L_BYTES + 4 * 16 * LDD * 4);
+    static constexpr int R = L_BYTES + 4 * 16 * LDD * 4;
     static constexpr int oKQ = 0;
-    static constexpr int oR = oKQ + KQ;
+    static constexpr int oR = oKQ + KQ;                  // solve blocks | fp32 diagonals of A
     static constexpr int oMqk = oR + R;                  // [C][LDL]
     static constexpr int oQh = oMqk + C * LDL * SZ;      // [C][LDK2] Q e^{G}
     static constexpr int oKhbT = oQh + C * LDK2 * SZ;    // [K][LDT] beta K e^{G}, channel-major
     static constexpr int oKbT = oKhbT + K * LDT * SZ;    // [K][LDT] K e^{G_C-G}, channel-major
-    static constexpr int oVbT = oKbT + K * LDT * SZ;     // [VB][LDT] beta V, channel-major
+    static constexpr int oVbT = oKbT + K * LDT * SZ;     // [VB][LDT] beta V, channel-major;
+                                                          // in the state pass: per-wave output staging
     static constexpr int oF = oVbT + VB * LDT * SZ;      // fp32 [6][K] e^{G_b(i) - G_b(j)}
     static constexpr int oEGC = oF + 6 * K * 4;          // fp32 [K] e^{G_C}
     static constexpr int oBeta = oEGC + K * 4;           // fp32 [C]
     static constexpr int TOTAL = oBeta + C * 4;
     static_assert(TOTAL <= 160 * 1024, "LDS budget exceeded");
-    static_assert(CPK * PK == NT && TPK * PK == C && (TPK == 4 || TPK == 8 || TPK == 16), "key prep mapping");
-    static_assert(CPV * PV == NT && TPV == 8, "value prep mapping");
+    static_assert(NW * C * 16 * NTW <= VB * LDT, "output staging must fit the beta-V buffer");
+    static_assert(CPW * 8 * NW == K && (CPW == 2 || CPW == 4), "key prep mapping");
+    static_assert(CPWV * 8 * NW == VB && (CPWV == 2 || CPWV == 4), "value prep mapping");
 };
 
 // lower block pairs (i >= j) of the 4 x 4 sub-chunk grid
@@ -99,44 +103,43 @@ __device__ __forceinline__ void ld8_as_f32(const T* p, float* x) {
     for (int i = 0; i < 8; ++i) x[i] = to_f32(f[i]);
 }
 
-// G (log2 units) at the first token of 16-token block `blk`, for channels
-// c and c+1, from the per-part sums and first values.
-template <int PK, int TPK, int K>
-__device__ __forceinline__ float2 block_ref(const float* sPart, const float* sFirst, int blk, int c) {
-    const int pb = 16 * blk / TPK;
-    float2 r = *reinterpret_cast<const float2*>(&sFirst[pb * K + c]);
-    for (int pp = 0; pp < pb; ++pp) {
-        const float2 s = *reinterpret_cast<const float2*>(&sPart[pp * K + c]);
-        r.x += s.x;
-        r.y += s.y;
-    }
-    return r;
+// B fragment of the column side of block pair (i, j) for the 32-deep slab at
+// channel c0: rows of block j of K e^{G_b(j) - G}, times e^{G_b(i) - G_b(j)}
+// per channel when i > j.
+template <typename T, int K>
+__device__ __forceinline__ typename FragOf<T>::type col_frag(const T* sKinv, const float* sF, int i, int j,
+                                                            int lr, int c0) {
+    constexpr int LDK1 = K + 16 / (int)sizeof(T);
+    if (i == j) return ld_frag<T>(&sKinv[(16 * j + lr) * LDK1 + c0]);
+    float kv[8], f[8];
+    ld8_as_f32<T>(&sKinv[(16 * j + lr) * LDK1 + c0], kv);
+    ld8f(&sF[(i * (i - 1) / 2 + j) * K + c0], f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) kv[e] *= f[e];
+    return frag_from<T>(kv);
 }
 
 }  // namespace
 
-template <typename T, int K, int NW>
-__global__ __launch_bounds__(64 * NW) void kda_chunk_kernel(ChunkParams p) {
-    using L = ChunkLayout<T, K, NW>;
+template <typename T, int K, int NTW, bool SUMMARY>
+__global__ __launch_bounds__(256) void kda_chunk_kernel(ChunkParams p) {
+    using L = ChunkLayout<T, K, NTW>;
+    constexpr int NW = L::NW;
     using Frag = typename FragOf<T>::type;
     using Frag4 = typename Frag4Of<T>::type;
     constexpr int VB = L::VB;
-    constexpr int LDK1 = L::LDK1, LDK2 = L::LDK2, LDT = L::LDT, LDL = L::LDL, LDD = L::LDD, LDO = L::LDO;
-    constexpr int CPK = L::CPK, PK = L::PK, TPK = L::TPK;
-    constexpr int CPV = L::CPV, TPV = L::TPV;
-    constexpr int NV8 = VB / 8;
-    constexpr int REPO = C * NV8 / L::NT;      // output store packs per thread
+    constexpr int LDK1 = L::LDK1, LDK2 = L::LDK2, LDT = L::LDT, LDL = L::LDL, LDD = L::LDD;
+    constexpr int CPW = L::CPW, TPL = L::TPL, NPART = L::NPART;
+    constexpr int CPWV = L::CPWV, TPLV = L::TPLV;
     constexpr int KS = K / 32;                 // 32-deep slabs over key channels
     constexpr int CT = K / 16;                 // 16-row tiles of the state
+    constexpr unsigned SZ = sizeof(T);
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
     T* sKd = reinterpret_cast<T*>(smem + L::oKQ);
     T* sQd = sKd + C * LDK1;
     T* sKinv = sQd + C * LDK1;
     T* sW = reinterpret_cast<T*>(smem + L::oKQ);
-    T* sO = reinterpret_cast<T*>(smem + L::oKQ + L::W_BYTES);
-    float* sPart = reinterpret_cast<float*>(smem + L::oR);
-    float* sFirst = sPart + PK * K;
     T* sL = reinterpret_cast<T*>(smem + L::oR);
     float* sAd = reinterpret_cast<float*>(smem + L::oR + L::L_BYTES);
     T* sMqk = reinterpret_cast<T*>(smem + L::oMqk);
@@ -160,7 +163,7 @@ __global__ __launch_bounds__(64 * NW) void kda_chunk_kernel(ChunkParams p) {
     const int lid = ((G & 7) == 0) ? (x & 7) * (G >> 3) + (x >> 3) : x;
     const int vb = lid % p.n_vb;
     const int rest = lid / p.n_vb;
-    const int nseg_here = p.summary ? p.n_seg - 1 : p.n_seg;
+    const int nseg_here = SUMMARY ? p.n_seg - 1 : p.n_seg;
     const int seg = rest % nseg_here;
     const int bh = rest / nseg_here;
     const int b = bh / p.H, h = bh % p.H;
@@ -173,9 +176,10 @@ __global__ __launch_bounds__(64 * NW) void kda_chunk_kernel(ChunkParams p) {
     // summary pass columns: [0, K) carry the transition P (start I, values 0),
     // [K, K+V) the local state L (start 0, the real values)
     const int col0 = vb * VB;
-    const bool pmode = p.summary && col0 < K;
-    const int vcol0 = p.summary ? (pmode ? 0 : col0 - K) : col0;
-    const int my_col = col0 + 16 * w + lr;
+    const bool pmode = SUMMARY && col0 < K;
+    const int vcol0 = SUMMARY ? (pmode ? 0 : col0 - K) : col0;
+    // this lane's state columns: tile j covers block columns 16 (NTW w + j) + [0, 16)
+    const int tile0 = NTW * w;
 
     const T* __restrict__ qg = reinterpret_cast<const T*>(p.q);
     const T* __restrict__ kg = reinterpret_cast<const T*>(p.k);
@@ -183,43 +187,48 @@ __global__ __launch_bounds__(64 * NW) void kda_chunk_kernel(ChunkParams p) {
     const T* __restrict__ gg = reinterpret_cast<const T*>(p.g);
     const T* __restrict__ bg = reinterpret_cast<const T*>(p.beta);
 
-    // prep mapping: key side (channels 2cp, 2cp+1; tokens pk*TPK ..), value side
-    const int cp = tid % CPK, pk = tid / CPK;
-    const int vp = tid % CPV, pv = tid / CPV;
+    // prep lane roles
+    const int c8l = l % CPW, part = l / CPW;
+    const int c0 = 8 * (CPW * w + c8l);        // first of this lane's 8 key channels
+    const int n8l = l % CPWV, pv = l / CPWV;
+    const int n0 = 8 * (CPWV * w + n8l);       // first of this lane's 8 value columns
 
-    // ---- initial state: S[ct] = rows 16ct + 4lg + e, column my_col --------
-    f32x4 S[CT];
+    // ---- initial state: S[j][ct] = rows 16ct + 4lg + e of tile j, column lr --
+    f32x4 S[NTW][CT];
     {
         const float* src = nullptr;
-        if (!p.summary) {
+        if (!SUMMARY) {
             if (seg == 0) src = p.s0 ? p.s0 + (size_t)bh * K * V : nullptr;
             else src = p.seg_init + ((size_t)(seg - 1) * BH + bh) * K * V;
         }
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
+        for (int j = 0; j < NTW; ++j) {
+            const int col = col0 + 16 * (tile0 + j) + lr;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int row = 16 * ct + 4 * lg + e;
-                float s = 0.f;
-                if (src) s = src[(size_t)row * V + my_col];
-                else if (pmode) s = (row == my_col) ? 1.f : 0.f;
-                S[ct][e] = s;
+            for (int ct = 0; ct < CT; ++ct) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int row = 16 * ct + 4 * lg + e;
+                    float v0 = 0.f;
+                    if (src) v0 = src[(size_t)row * V + col];
+                    else if (pmode) v0 = (row == col) ? 1.f : 0.f;
+                    S[j][ct][e] = v0;
+                }
             }
         }
     }
 
-    // ---- raw chunk registers (loaded one chunk ahead) ------------------------
-    // (kept raw: converting at load time would make every load wait)
-    Pack2<T> kr[TPK], qr[TPK], gr[TPK], vr[TPV];
-    T br[TPK];
-    // global addressing: a buffer resource at the chunk's first row (scalar
-    // registers), a 32-bit lane byte offset and a scalar per-token offset;
-    // one chunk of one head spans far less than 2^32 bytes
-    constexpr unsigned SZ = sizeof(T);
+    // ---- raw chunk registers, loaded one chunk ahead ---------------------
+    // (kept raw: converting at load time would make every load wait).
+    // Global addressing: a buffer resource at the chunk's first row (scalar
+    // registers), a 32-bit lane byte offset and a scalar per-token offset.
+    Pack8<T> kr[TPL], qr[TPL], gr[TPL], vr[TPLV];
+    T br[TPL], bvr[TPLV];
     const unsigned rowK = (unsigned)p.H * K * SZ, rowV = (unsigned)p.H * V * SZ, rowB = (unsigned)p.H * SZ;
-    const unsigned vK = (unsigned)pk * TPK * rowK + 2u * cp * SZ;   // lane offsets
-    const unsigned vB = (unsigned)pk * TPK * rowB;
-    const unsigned vV = (unsigned)pv * TPV * rowV + 2u * vp * SZ;
+    const unsigned vK = (unsigned)part * TPL * rowK + (unsigned)c0 * SZ;
+    const unsigned vB = (unsigned)part * TPL * rowB;
+    const unsigned vV = (unsigned)pv * TPLV * rowV + (unsigned)n0 * SZ;
+    const unsigned vBV = (unsigned)pv * TPLV * rowB;
     auto load_chunk = [&](int ci) {
         const int t0 = ci * C;
         const int nt = min(C, p.T - t0);
@@ -230,12 +239,11 @@ __global__ __launch_bounds__(64 * NW) void kda_chunk_kernel(ChunkParams p) {
         const __amdgpu_buffer_rsrc_t rb = make_rsrc(bg + head_row);
         const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + head_row * V + vcol0);
 #pragma unroll
-        for (int i = 0; i < TPK; ++i) {
-            const int t = pk * TPK + i;
-            if (t < nt) {
-                buf_load2<T>(kr[i], rk, vK, i * rowK);
-                buf_load2<T>(gr[i], rg, vK, i * rowK);
-                if (!p.summary) buf_load2<T>(qr[i], rq, vK, i * rowK); else qr[i].zero();
+        for (int i = 0; i < TPL; ++i) {
+            if (part * TPL + i < nt) {
+                buf_load8<T>(kr[i], rk, vK, i * rowK);
+                buf_load8<T>(gr[i], rg, vK, i * rowK);
+                if (!SUMMARY) buf_load8<T>(qr[i], rq, vK, i * rowK); else qr[i].zero();
                 buf_load1(br[i], rb, vB, i * rowB);
             } else {
                 kr[i].zero();
@@ -245,10 +253,14 @@ __global__ __launch_bounds__(64 * NW) void kda_chunk_kernel(ChunkParams p) {
             }
         }
 #pragma unroll
-        for (int i = 0; i < TPV; ++i) {
-            const int t = pv * TPV + i;
-            if (t < nt && !pmode) buf_load2<T>(vr[i], rv, vV, i * rowV);
-            else vr[i].zero();
+        for (int i = 0; i < TPLV; ++i) {
+            if (pv * TPLV + i < nt && !pmode) {
+                buf_load8<T>(vr[i], rv, vV, i * rowV);
+                buf_load1(bvr[i], rb, vBV, i * rowB);
+            } else {
+                vr[i].zero();
+                bvr[i] = from_f32<T>(0.f);
+            }
         }
     };
     if (c_begin < c_end) load_chunk(c_begin);
@@ -257,135 +269,149 @@ __global__ __launch_bounds__(64 * NW) void kda_chunk_kernel(ChunkParams p) {
         const int t0 = ci * C;
         const int nt = min(C, p.T - t0);
 
-        // ---- P1: in-chunk gate cumsum, part totals ----------------------------
-        float gl0[TPK], gl1[TPK];
+        // ---- P1: gate cumsum and key/query-side operands (registers -> LDS) ---
         {
-            float s0 = 0.f, s1 = 0.f;
+            // in-lane inclusive sums over this lane's tokens, then a scan over
+            // the lanes holding the same channels (parts in token order)
+            float G[TPL][8];
 #pragma unroll
-            for (int i = 0; i < TPK; ++i) {
-                s0 += clamp_gate_log2(gr[i].lo());
-                s1 += clamp_gate_log2(gr[i].hi());
-                gl0[i] = s0;
-                gl1[i] = s1;
-            }
-            *reinterpret_cast<float2*>(&sPart[pk * K + 2 * cp]) = make_float2(s0, s1);
-            *reinterpret_cast<float2*>(&sFirst[pk * K + 2 * cp]) = make_float2(gl0[0], gl1[0]);
-            if (cp == 0) {
+            for (int i = 0; i < TPL; ++i) {
+                float g8[8];
+                gr[i].to_f32(g8);
 #pragma unroll
-                for (int i = 0; i < TPK; ++i) sBeta[pk * TPK + i] = to_f32(br[i]);
+                for (int e = 0; e < 8; ++e) G[i][e] = (i ? G[i - 1][e] : 0.f) + clamp_gate_log2(g8[e]);
             }
-        }
-        __syncthreads();
-
-        // ---- P2: key/query-side operands (one pass, registers -> LDS) ---------
-        {
-            float off0 = 0.f, off1 = 0.f, tot0 = 0.f, tot1 = 0.f;
-            for (int pp = 0; pp < PK; ++pp) {
-                const float2 sp = *reinterpret_cast<const float2*>(&sPart[pp * K + 2 * cp]);
-                if (pp < pk) { off0 += sp.x; off1 += sp.y; }
-                tot0 += sp.x;
-                tot1 += sp.y;
-            }
-            const float2 gb = block_ref<PK, TPK, K>(sPart, sFirst, (pk * TPK) / 16, 2 * cp);
-            const float egb0 = fast_exp2(gb.x), egb1 = fast_exp2(gb.y);            // e^{G_b}      <= 1
-            const float ecb0 = fast_exp2(tot0 - gb.x), ecb1 = fast_exp2(tot1 - gb.y);  // e^{G_C-G_b} <= 1
-            float kh0[TPK], kh1[TPK], kb0[TPK], kb1[TPK];
+            float incl[8], gfirst[8], gb[8], gcum[8];
 #pragma unroll
-            for (int i = 0; i < TPK; ++i) {
-                const int t = pk * TPK + i;
-                const float d0 = off0 + gl0[i] - gb.x, d1 = off1 + gl1[i] - gb.y;  // G_t - G_b <= 0
-                const float e10 = fast_exp2(d0), e11 = fast_exp2(d1);     // e^{G_t-G_b}
-                const float e20 = fast_exp2(-d0), e21 = fast_exp2(-d1);   // e^{G_b-G_t} <= e^75
-                const float k0 = kr[i].lo(), k1 = kr[i].hi();
-                const float q0 = qr[i].lo(), q1 = qr[i].hi();
-                const float bt = to_f32(br[i]);
-                st2(&sKd[t * LDK1 + 2 * cp], k0 * e10, k1 * e11);
-                st2(&sKinv[t * LDK1 + 2 * cp], k0 * e20, k1 * e21);
-                if (!p.summary) {
-                    st2(&sQd[t * LDK1 + 2 * cp], q0 * e10, q1 * e11);
-                    st2(&sQh[t * LDK2 + 2 * cp], q0 * e10 * egb0, q1 * e11 * egb1);
+            for (int e = 0; e < 8; ++e) incl[e] = G[TPL - 1][e];
+#pragma unroll
+            for (int d = CPW; d < 64; d <<= 1) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float y = __shfl_up(incl[e], d);
+                    if (l >= d) incl[e] += y;
                 }
-                kh0[i] = bt * k0 * e10 * egb0;     // beta e^{G_t}
-                kh1[i] = bt * k1 * e11 * egb1;
-                kb0[i] = k0 * e20 * ecb0;          // e^{G_C-G_t}
-                kb1[i] = k1 * e21 * ecb1;
             }
-            st_run<TPK>(&sKhbT[(2 * cp) * LDT + pk * TPK], kh0);
-            st_run<TPK>(&sKhbT[(2 * cp + 1) * LDT + pk * TPK], kh1);
-            st_run<TPK>(&sKbT[(2 * cp) * LDT + pk * TPK], kb0);
-            st_run<TPK>(&sKbT[(2 * cp + 1) * LDT + pk * TPK], kb1);
-            if (pk == 0) *reinterpret_cast<float2*>(&sEGC[2 * cp]) = make_float2(fast_exp2(tot0), fast_exp2(tot1));
-            for (int pr = pk; pr < 6; pr += PK) {
-                int i, j;
-                offdiag_pair(pr, i, j);
-                const float2 gi = block_ref<PK, TPK, K>(sPart, sFirst, i, 2 * cp);
-                const float2 gj = block_ref<PK, TPK, K>(sPart, sFirst, j, 2 * cp);
-                *reinterpret_cast<float2*>(&sF[pr * K + 2 * cp]) =
-                    make_float2(fast_exp2(gi.x - gj.x), fast_exp2(gi.y - gj.y));
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float excl = incl[e] - G[TPL - 1][e];
+#pragma unroll
+                for (int i = 0; i < TPL; ++i) G[i][e] += excl;
+                gfirst[e] = G[0][e];
+                gcum[e] = __shfl(incl[e], (NPART - 1) * CPW + c8l);    // G at the chunk's last token
+            }
+            // G at the first token of a 16-token block (same channels): this
+            // lane's block, and the two blocks of pair `part` of the table of
+            // e^{G_b(i) - G_b(j)} (all lanes shuffle; parts >= 6 discard)
+            const int myblk = (part * TPL) >> 4;
+            int pi_ = 1, pj_ = 0;
+            if (part < 6) offdiag_pair(part, pi_, pj_);
+            const int src_b = (16 * myblk / TPL) * CPW + c8l;
+            const int src_i = (16 * pi_ / TPL) * CPW + c8l;
+            const int src_j = (16 * pj_ / TPL) * CPW + c8l;
+            float f[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                gb[e] = __shfl(gfirst[e], src_b);
+                f[e] = fast_exp2(__shfl(gfirst[e], src_i) - __shfl(gfirst[e], src_j));
+            }
+            if (part < 6) st8(&sF[part * K + c0], f);
+            if (part == 0) {
+                float f[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) f[e] = fast_exp2(gcum[e]);
+                st8(&sEGC[c0], f);
+            }
+            if (w == 0 && c8l == 0) {
+#pragma unroll
+                for (int i = 0; i < TPL; ++i) sBeta[part * TPL + i] = to_f32(br[i]);
+            }
+            float egb[8], ecb[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                egb[e] = fast_exp2(gb[e]);             // e^{G_b}       <= 1
+                ecb[e] = fast_exp2(gcum[e] - gb[e]);   // e^{G_C - G_b} <= 1
+            }
+            float kh[8][TPL], kb[8][TPL];
+#pragma unroll
+            for (int i = 0; i < TPL; ++i) {
+                const int t = part * TPL + i;
+                float kx[8], kd[8], ki[8];
+                kr[i].to_f32(kx);
+                const float bt = to_f32(br[i]);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float d = G[i][e] - gb[e];       // G_t - G_b in [-108, 0] (log2)
+                    const float e1 = fast_exp2(d);         // e^{G_t - G_b} <= 1
+                    const float e2 = fast_exp2(-d);        // e^{G_b - G_t} <= e^75
+                    kd[e] = kx[e] * e1;
+                    ki[e] = kx[e] * e2;
+                    kh[e][i] = bt * kd[e] * egb[e];        // beta k e^{G_t}
+                    kb[e][i] = ki[e] * ecb[e];             // k e^{G_C - G_t}
+                }
+                st8(&sKd[t * LDK1 + c0], kd);
+                st8(&sKinv[t * LDK1 + c0], ki);
+            }
+            // (fence: the query side below reuses the registers of the key side)
+            __builtin_amdgcn_sched_barrier(0);
+            if (!SUMMARY) {
+#pragma unroll
+                for (int i = 0; i < TPL; ++i) {
+                    const int t = part * TPL + i;
+                    float qx[8], qd[8], qh[8];
+                    qr[i].to_f32(qx);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        qd[e] = qx[e] * fast_exp2(G[i][e] - gb[e]);   // q e^{G_t - G_b}
+                        qh[e] = qd[e] * egb[e];                        // q e^{G_t}
+                    }
+                    st8(&sQd[t * LDK1 + c0], qd);
+                    st8(&sQh[t * LDK2 + c0], qh);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                st_small<TPL>(&sKhbT[(c0 + e) * LDT + part * TPL], kh[e]);
+                st_small<TPL>(&sKbT[(c0 + e) * LDT + part * TPL], kb[e]);
             }
             // beta V, channel-major
-            float bv0[TPV], bv1[TPV];
+            float bv[8][TPLV];
 #pragma unroll
-            for (int i = 0; i < TPV; ++i) {
-                const float bt = sBeta[pv * TPV + i];
-                bv0[i] = bt * vr[i].lo();
-                bv1[i] = bt * vr[i].hi();
+            for (int i = 0; i < TPLV; ++i) {
+                float vx[8];
+                vr[i].to_f32(vx);
+                const float bt = to_f32(bvr[i]);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) bv[e][i] = bt * vx[e];
             }
-            st_run<TPV>(&sVbT[(2 * vp) * LDT + pv * TPV], bv0);
-            st_run<TPV>(&sVbT[(2 * vp + 1) * LDT + pv * TPV], bv1);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) st_small<TPLV>(&sVbT[(n0 + e) * LDT + pv * TPLV], bv[e]);
         }
-        // the raw registers are consumed: fetch the next chunk behind the compute
-        // (the scheduling fence keeps the loads from being hoisted above the
-        // last uses, which would hold two chunks in registers)
-        __builtin_amdgcn_sched_barrier(0);
-        if (ci + 1 < c_end) load_chunk(ci + 1);
         __syncthreads();
 
-        // ---- P3: A and Mqk, one 16 x 16 block pair per wave at a time ---------
-        // A's diagonal blocks go to fp32 (for the block inverses), its
-        // off-diagonal blocks to the solve buffer negated; Mqk blocks (0,1)
-        // and (2,3) are zero (read by the 32-deep slabs of the output).
-        for (int task = w; task < 12; task += NW) {
-            if (task < 10) {
-                int i, j;
-                lower_pair(task, i, j);
-                f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accM = {0.f, 0.f, 0.f, 0.f};
+        // ---- P2: A, D_i = (I + A_ii)^{-1} and Mqk --------------------------------
+        if (w == 0) {
+            // diagonal blocks of A (fp32), then their inverses by forward
+            // substitution, one lane per (block, column); the LDS round trip
+            // stays inside this wave
+            f32x4 acc[4];
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const int c0 = 32 * ks + 8 * lg;
-                    const Frag ak = ld_frag<T>(&sKd[(16 * i + lr) * LDK1 + c0]);
-                    float kv[8];
-                    ld8_as_f32<T>(&sKinv[(16 * j + lr) * LDK1 + c0], kv);
-                    if (i != j) {
-                        float f[8];
-                        ld8f(&sF[(i * (i - 1) / 2 + j) * K + c0], f);
+            for (int i = 0; i < 4; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) kv[e] *= f[e];
-                    }
-                    const Frag bk = frag_from<T>(kv);
-                    accA = mma(accA, ak, bk);
-                    if (!p.summary) accM = mma(accM, ld_frag<T>(&sQd[(16 * i + lr) * LDK1 + c0]), bk);
-                }
-                const int r = 16 * j + lr;
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    acc[i] = mma(acc[i], ld_frag<T>(&sKd[(16 * i + lr) * LDK1 + 32 * ks + 8 * lg]),
+                                 ld_frag<T>(&sKinv[(16 * i + lr) * LDK1 + 32 * ks + 8 * lg]));
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int s = 16 * i + 4 * lg + e;
-                    const float a = sBeta[s] * accA[e];
-                    if (i == j) sAd[(i * 16 + 4 * lg + e) * LDD + lr] = (r < s) ? a : 0.f;
-                    else sL[s * LDL + r] = from_f32<T>(-a);
-                    if (!p.summary) sMqk[s * LDL + r] = from_f32<T>((i > j || r <= s) ? accM[e] : 0.f);
+                    const int s_ = 16 * i + 4 * lg + e, r = 16 * i + lr;
+                    sAd[(16 * i + 4 * lg + e) * LDD + lr] = (r < s_) ? sBeta[s_] * acc[i][e] : 0.f;
                 }
-            } else if (!p.summary) {
-                const int i = (task == 10) ? 0 : 2, j = i + 1;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) sMqk[(16 * i + 4 * lg + e) * LDL + 16 * j + lr] = from_f32<T>(0.f);
-            }
-        }
-        __syncthreads();
-
-        // ---- P4: inverses D_i = (I + A_ii)^{-1} of the diagonal blocks --------
-        // forward substitution in fp32, one lane per (block, column)
-        if (w == 0) {
+            wave_lds_sync();
             const int i = lg, j = lr;
             float xv[16];
 #pragma unroll
@@ -399,17 +425,49 @@ __global__ __launch_bounds__(64 * NW) void kda_chunk_kernel(ChunkParams p) {
                     row[4 * m4 + 2] = a4[2];
                     row[4 * m4 + 3] = a4[3];
                 }
-                float acc = (r == j) ? 1.f : 0.f;
+                float a = (r == j) ? 1.f : 0.f;
 #pragma unroll
-                for (int m = 0; m < r; ++m) acc -= row[m] * xv[m];
-                xv[r] = acc;
+                for (int m = 0; m < r; ++m) a -= row[m] * xv[m];
+                xv[r] = a;
             }
 #pragma unroll
             for (int r = 0; r < 16; ++r) sL[(16 * i + r) * LDL + 16 * i + j] = from_f32<T>(xv[r]);
+        } else {
+            // off-diagonal blocks of A (negated, into the solve buffer), then
+            // the blocks of Mqk; its blocks (0,1) and (2,3) are zero (they are
+            // read by the 32-deep slabs of the output product)
+            constexpr int NTASK = SUMMARY ? 6 : 18;
+            for (int task = w - 1; task < NTASK; task += NW - 1) {
+                if (task < 16) {
+                    int i, j;
+                    if (task < 6) offdiag_pair(task, i, j);
+                    else lower_pair(task - 6, i, j);
+                    const T* rowsrc = (task < 6) ? sKd : sQd;
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) {
+                        const int cc = 32 * ks + 8 * lg;
+                        acc = mma(acc, ld_frag<T>(&rowsrc[(16 * i + lr) * LDK1 + cc]),
+                                  col_frag<T, K>(sKinv, sF, i, j, lr, cc));
+                    }
+                    const int r = 16 * j + lr;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int s_ = 16 * i + 4 * lg + e;
+                        if (task < 6) sL[s_ * LDL + r] = from_f32<T>(-sBeta[s_] * acc[e]);
+                        else sMqk[s_ * LDL + r] = from_f32<T>((i > j || r <= s_) ? acc[e] : 0.f);
+                    }
+                } else {
+                    const int i = (task == 16) ? 0 : 2, j = i + 1;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        sMqk[(16 * i + 4 * lg + e) * LDL + 16 * j + lr] = from_f32<T>(0.f);
+                }
+            }
         }
         __syncthreads();
 
-        // ---- P5: W = (I+A)^{-1} beta K e^G and U~ = (I+A)^{-1} beta V ---------
+        // ---- P3: W = (I+A)^{-1} beta K e^G and U~ = (I+A)^{-1} beta V ---------
         // block forward substitution per 16-column tile, tiles in registers:
         //   X_i = D_i (R_i - sum_{k<i} A_ik X_k)
         Frag4 Ld[4], Lo[6];
@@ -443,78 +501,113 @@ __global__ __launch_bounds__(64 * NW) void kda_chunk_kernel(ChunkParams p) {
                 for (int e = 0; e < 4; ++e)
                     sW[(16 * i + 4 * lg + e) * LDK2 + 16 * ct + lr] = from_f32<T>(X[i][e]);
         }
-        f32x4 Ut[4];
-        if (!pmode) {
-            solve_tile(&sVbT[16 * w * LDT], Ut);
-        } else {
+        f32x4 Ut[NTW][4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) Ut[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < NTW; ++j) {
+            if (!pmode) {
+                solve_tile(&sVbT[16 * (tile0 + j) * LDT], Ut[j]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) Ut[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
         }
         __syncthreads();
 
-        // ---- P6: the state pass (per wave, registers) --------------------------
-        Frag Sb[KS];
+        // fetch the next chunk behind the state pass (the scheduling fences keep
+        // the loads in place, so the raw registers live only across this phase)
+        __builtin_amdgcn_sched_barrier(0);
+        if (ci + 1 < c_end) load_chunk(ci + 1);
+        __builtin_amdgcn_sched_barrier(0);
+
+        // ---- P4: the state pass (per wave, registers); output straight out ---
+        // each key-side fragment read from LDS serves the wave's NTW tiles
+        Frag Sb[NTW][KS];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) Sb[ks] = frag_from_tiles<T>(S[2 * ks], S[2 * ks + 1]);
-        f32x4 U[4];
+        for (int j = 0; j < NTW; ++j)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) Sb[j][ks] = frag_from_tiles<T>(S[j][2 * ks], S[j][2 * ks + 1]);
+        f32x4 U[NTW][4];
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            f32x4 acc[NTW];
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                acc = mma(acc, ld_frag_perm<T>(&sW[(16 * ti + lr) * LDK2 + 32 * ks + 4 * lg]), Sb[ks]);
-            U[ti] = Ut[ti] - acc;
+            for (int j = 0; j < NTW; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const Frag a = ld_frag_perm<T>(&sW[(16 * ti + lr) * LDK2 + 32 * ks + 4 * lg]);
+#pragma unroll
+                for (int j = 0; j < NTW; ++j) acc[j] = mma(acc[j], a, Sb[j][ks]);
+            }
+#pragma unroll
+            for (int j = 0; j < NTW; ++j) U[j][ti] = Ut[j][ti] - acc[j];
         }
-        Frag Ub[2];
-        Ub[0] = frag_from_tiles<T>(U[0], U[1]);
-        Ub[1] = frag_from_tiles<T>(U[2], U[3]);
-        if (!p.summary) {
+        Frag Ub[NTW][2];
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) {
+            Ub[j][0] = frag_from_tiles<T>(U[j][0], U[j][1]);
+            Ub[j][1] = frag_from_tiles<T>(U[j][2], U[j][3]);
+        }
+        if (!SUMMARY) {
+            // this wave's 64 x 16NTW output block is staged row-major in the
+            // beta-V buffer (free after the solve), then written out in
+            // 16-byte pieces
+            constexpr int OW = 16 * NTW;                 // staged row length
+            T* sO = sVbT + w * (C * OW);
 #pragma unroll
             for (int ti = 0; ti < 4; ++ti) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                f32x4 acc[NTW];
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
-                    acc = mma(acc, ld_frag_perm<T>(&sQh[(16 * ti + lr) * LDK2 + 32 * ks + 4 * lg]), Sb[ks]);
+                for (int j = 0; j < NTW; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks)
-                    if (ks <= (ti >> 1))
-                        acc = mma(acc, ld_frag_perm<T>(&sMqk[(16 * ti + lr) * LDL + 32 * ks + 4 * lg]), Ub[ks]);
+                for (int ks = 0; ks < KS; ++ks) {
+                    const Frag a = ld_frag_perm<T>(&sQh[(16 * ti + lr) * LDK2 + 32 * ks + 4 * lg]);
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    sO[(16 * ti + 4 * lg + e) * LDO + 16 * w + lr] = from_f32<T>(acc[e]);
+                    for (int j = 0; j < NTW; ++j) acc[j] = mma(acc[j], a, Sb[j][ks]);
+                }
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    if (ks <= (ti >> 1)) {
+                        const Frag a = ld_frag_perm<T>(&sMqk[(16 * ti + lr) * LDL + 32 * ks + 4 * lg]);
+#pragma unroll
+                        for (int j = 0; j < NTW; ++j) acc[j] = mma(acc[j], a, Ub[j][ks]);
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < NTW; ++j)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) sO[(16 * ti + 4 * lg + e) * OW + 16 * j + lr] = from_f32<T>(acc[j][e]);
+            }
+            wave_lds_sync();
+            constexpr int PPR = OW * (int)SZ / 16;       // 16-byte pieces per row
+            const __amdgpu_buffer_rsrc_t ro = make_rsrc(
+                reinterpret_cast<T*>(p.o) + ((size_t)(b * (size_t)p.T + t0) * p.H + h) * V + vcol0 + OW * w);
+#pragma unroll
+            for (int pc = l; pc < C * PPR; pc += 64) {
+                const int row = pc / PPR, seg = pc % PPR;
+                if (row < nt)
+                    buf_store16(ro, (unsigned)row * rowV + (unsigned)seg * 16u, 0u,
+                                *reinterpret_cast<const uint4*>(&sO[row * OW + seg * (16 / (int)SZ)]));
             }
         }
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
             const f32x4 eg = *reinterpret_cast<const f32x4*>(&sEGC[16 * ct + 4 * lg]);
-            S[ct] = S[ct] * eg;
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-                S[ct] = mma(S[ct], ld_frag_perm<T>(&sKbT[(16 * ct + lr) * LDT + 32 * ks + 4 * lg]), Ub[ks]);
-        }
-        __syncthreads();
-
-        // ---- P7: stream the chunk's output out ---------------------------------
-        if (!p.summary) {
-            const __amdgpu_buffer_rsrc_t ro =
-                make_rsrc(reinterpret_cast<T*>(p.o) + ((size_t)(b * (size_t)p.T + t0) * p.H + h) * V + vcol0);
+            for (int j = 0; j < NTW; ++j) S[j][ct] = S[j][ct] * eg;
 #pragma unroll
-            for (int r = 0; r < REPO; ++r) {
-                const int it = tid + r * L::NT;
-                const int t = it / NV8, n8 = it % NV8;
-                if (t < nt) {
-                    const unsigned off = (unsigned)t * rowV + 8u * n8 * SZ;
-                    buf_store16(ro, off, 0, *reinterpret_cast<const uint4*>(&sO[t * LDO + 8 * n8]));
-                    if (SZ == 4) buf_store16(ro, off + 16, 0, *reinterpret_cast<const uint4*>(&sO[t * LDO + 8 * n8 + 4]));
-                }
+            for (int ks = 0; ks < 2; ++ks) {
+                const Frag a = ld_frag_perm<T>(&sKbT[(16 * ct + lr) * LDT + 32 * ks + 4 * lg]);
+#pragma unroll
+                for (int j = 0; j < NTW; ++j) S[j][ct] = mma(S[j][ct], a, Ub[j][ks]);
             }
         }
+        __syncthreads();
     }
 
     // ---- final state of this segment / column block ----------------------------
     float* dst = nullptr;
     size_t ld = V;
-    if (!p.summary) {
+    if (!SUMMARY) {
         if (seg == p.n_seg - 1 && p.sT) dst = p.sT + (size_t)bh * K * V;
     } else if (pmode) {
         dst = p.wsP + ((size_t)seg * BH + bh) * K * K;
@@ -523,11 +616,15 @@ __global__ __launch_bounds__(64 * NW) void kda_chunk_kernel(ChunkParams p) {
         dst = p.wsL + ((size_t)seg * BH + bh) * K * V;
     }
     if (dst) {
-        const int col = p.summary ? (pmode ? my_col : my_col - K) : my_col;
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
+        for (int j = 0; j < NTW; ++j) {
+            const int my_col = col0 + 16 * (tile0 + j) + lr;
+            const int col = SUMMARY ? (pmode ? my_col : my_col - K) : my_col;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) dst[(size_t)(16 * ct + 4 * lg + e) * ld + col] = S[ct][e];
+            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dst[(size_t)(16 * ct + 4 * lg + e) * ld + col] = S[j][ct][e];
+        }
     }
 }
 
@@ -586,21 +683,24 @@ bool chunk_variant_exists(int dtype, int K, int VB) {
     return false;
 }
 
-template <typename T, int K, int NW>
+template <typename T, int K, int NTW>
 static hipError_t launch_chunk_t(const ChunkParams& p, int grid, hipStream_t stream) {
-    hipLaunchKernelGGL((kda_chunk_kernel<T, K, NW>), dim3(grid), dim3(64 * NW), 0, stream, p);
+    if (p.summary)
+        hipLaunchKernelGGL((kda_chunk_kernel<T, K, NTW, true>), dim3(grid), dim3(256), 0, stream, p);
+    else
+        hipLaunchKernelGGL((kda_chunk_kernel<T, K, NTW, false>), dim3(grid), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
 hipError_t launch_chunk(int dtype, int K, int VB, const ChunkParams& p, int grid, hipStream_t stream) {
     if (grid <= 0) return hipSuccess;
     if (dtype == 1) {
-        if (K == 128 && VB == 128) return launch_chunk_t<bf16, 128, 8>(p, grid, stream);
-        if (K == 128 && VB == 64) return launch_chunk_t<bf16, 128, 4>(p, grid, stream);
-        if (K == 64 && VB == 128) return launch_chunk_t<bf16, 64, 8>(p, grid, stream);
-        if (K == 64 && VB == 64) return launch_chunk_t<bf16, 64, 4>(p, grid, stream);
+        if (K == 128 && VB == 128) return launch_chunk_t<bf16, 128, 2>(p, grid, stream);
+        if (K == 128 && VB == 64) return launch_chunk_t<bf16, 128, 1>(p, grid, stream);
+        if (K == 64 && VB == 128) return launch_chunk_t<bf16, 64, 2>(p, grid, stream);
+        if (K == 64 && VB == 64) return launch_chunk_t<bf16, 64, 1>(p, grid, stream);
     } else if (dtype == 0) {
-        if (K == 64 && VB == 64) return launch_chunk_t<float, 64, 4>(p, grid, stream);
+        if (K == 64 && VB == 64) return launch_chunk_t<float, 64, 1>(p, grid, stream);
     }
     return hipErrorInvalidValue;
 }

@@ -224,6 +224,14 @@ __device__ __forceinline__ void buf_load1(bf16& x, __amdgpu_buffer_rsrc_t r, uns
 __device__ __forceinline__ void buf_load1(float& x, __amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
     x = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0));
 }
+template <typename T> struct Pack8;
+template <typename T> __device__ __forceinline__ void buf_load8(Pack8<T>& x, __amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff);
+__device__ __forceinline__ void buf_store1(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff, bf16 x) {
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, x), r, (int)voff, (int)soff, 0);
+}
+__device__ __forceinline__ void buf_store1(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff, float x) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, (int)voff, (int)soff, 0);
+}
 __device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff, uint4 v) {
     typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
     u32x4 x = {v.x, v.y, v.z, v.w};
@@ -259,6 +267,43 @@ template <> struct Pack8<float> {
     }
 };
 
+template <> __device__ __forceinline__ void buf_load8<bf16>(Pack8<bf16>& x, __amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+    x.d = make_uint4(v[0], v[1], v[2], v[3]);
+}
+template <> __device__ __forceinline__ void buf_load8<float>(Pack8<float>& x, __amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+    const u32x4 b = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff + 16, (int)soff, 0);
+    x.a = make_float4(__uint_as_float(a[0]), __uint_as_float(a[1]), __uint_as_float(a[2]), __uint_as_float(a[3]));
+    x.b = make_float4(__uint_as_float(b[0]), __uint_as_float(b[1]), __uint_as_float(b[2]), __uint_as_float(b[3]));
+}
+
+// N (1, 2, 4 or a multiple of 4) consecutive values stored as elements of T
+template <int N> __device__ __forceinline__ void st_small(bf16* p, const float* x) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    if constexpr (N == 1) {
+        *p = (bf16)x[0];
+    } else if constexpr (N == 2) {
+        bf16x2 r;
+        r[0] = (bf16)x[0];
+        r[1] = (bf16)x[1];
+        *reinterpret_cast<bf16x2*>(p) = r;
+    } else {
+        st_run<N>(p, x);
+    }
+}
+template <int N> __device__ __forceinline__ void st_small(float* p, const float* x) {
+    if constexpr (N == 1) {
+        *p = x[0];
+    } else if constexpr (N == 2) {
+        *reinterpret_cast<float2*>(p) = make_float2(x[0], x[1]);
+    } else {
+        st_run<N>(p, x);
+    }
+}
+
 // store 8 fp32 values as 8 elements of T (16-byte aligned for bf16)
 __device__ __forceinline__ void st8(bf16* p, const float* x) {
     bf16x8 r;
@@ -269,6 +314,16 @@ __device__ __forceinline__ void st8(bf16* p, const float* x) {
 __device__ __forceinline__ void st8(float* p, const float* x) {
     *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
     *reinterpret_cast<float4*>(p + 4) = make_float4(x[4], x[5], x[6], x[7]);
+}
+
+// ---- wave-level LDS exchange ------------------------------------------------------
+// Lanes of one wave that hand data to each other through LDS: the wave's LDS
+// operations execute in order, so a compiler fence (no hardware wait) between
+// the writes and the reads is enough.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // ---- scalar math ---------------------------------------------------------------
