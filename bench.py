@@ -9,7 +9,17 @@ sequences x 32 heads, 512 MiB fp32 state, 64 successive one-token steps), the
 roofline of the dominant launch, and the fp64 CPU oracle timed on a bounded
 sample of the prefill workload.
 
+The roofline object describes the dominant kernel of the prefill step: its
+algorithmic bytes per launch (1,282 B per head-token it processes plus the
+states it must read or write) over its average duration, measured with HIP
+events that the library records on the launch stream (kda_profile_start).
+``traffic`` is the HBM traffic per launch from rocprofv3 FETCH_SIZE and
+WRITE_SIZE counters, scaled by a plain-copy calibration; it is read from
+profiles/chunk_kernel_c1_traffic.json and reported only while the kernel
+source still has the hash recorded there.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--extra] [--no-cpu-baseline]
+       [--no-decode] [--cpu-seconds S]
 """
 from __future__ import annotations
 
@@ -18,6 +28,9 @@ import json
 import os
 import sys
 import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chunk_kernel_c1_traffic.json")
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
@@ -43,6 +56,25 @@ def decode_bytes(N, H, K, V, in_bytes=2):
     return N * H * (8 * K * V + in_bytes * (3 * K + V + 1) + in_bytes * V)
 
 
+def recorded_traffic(kernel, plan):
+    """Counter-derived HBM bytes per launch of `kernel`, if the committed
+    measurement was taken on the current kernel sources and plan."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None, "no counter record"
+    from gated_delta_rule_66_amd.traffic import kernel_source_hash
+    if rec.get("source_sha256") != kernel_source_hash():
+        return None, "kernel changed since the counters were taken"
+    if list(rec.get("plan", [])) != list(plan):
+        return None, "plan differs from the one profiled"
+    k = rec.get("kernels", {}).get(kernel)
+    if not k:
+        return None, "kernel not in the counter record"
+    return k["hbm_bytes_per_launch"], rec.get("note", "")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -51,7 +83,9 @@ def main():
     ap.add_argument("--decode-passes", type=int, default=3)
     ap.add_argument("--extra", action="store_true", help="also time the 32K x 256-chain and 1M-token workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=4, help="heads of the 8K workload the oracle runs")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target duration of the oracle sample (heads of the 8K workload)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run only a plain device copy of this size (counter calibration) and exit")
     args = ap.parse_args()
@@ -94,6 +128,19 @@ def main():
         torch.cuda.synchronize()
         return start.elapsed_time(end) / steps   # ms per call
 
+    def time_launches(fn, steps):
+        """Per-kernel average duration (ms) and launch count per call, from
+        the events the library records around each launch."""
+        torch.cuda.synchronize()
+        kda.profile_start(64 * steps + 64)
+        for _ in range(steps):
+            fn()
+        rec = kda.profile_stop(64 * steps + 64)
+        per = {}
+        for name, ms in rec:
+            per.setdefault(name, []).append(ms)
+        return {n: {"avg_ms": sum(v) / len(v), "launches_per_call": len(v) / steps} for n, v in per.items()}
+
     # ------------------------------------------------------------ prefill, 8K workload
     cfg = CONFIGS["c1"]
     x = make_prefill_config(cfg, dev)
@@ -109,33 +156,60 @@ def main():
                       out=o, final_state=sT, workspace=ws)
 
     ms = time_calls(prefill_step, args.warmup, args.steps)
+    kernels = time_launches(prefill_step, args.steps)
     tok_s = B * T / (ms * 1e-3)
     nbytes = prefill_bytes(B, T, H, K, V, 2, s0=False, final=True)
     nflops = prefill_flops(B, T, H, K, V)
     gbs = nbytes / (ms * 1e-3) / 1e9
     tflops = nflops / (ms * 1e-3) / 1e12
+
+    # algorithmic bytes per launch of each kernel: 1,282 B per head-token it
+    # processes (q, k, g, v, beta in; o out) plus the states it must move
+    n_seg = plan[0]
+    seg_tokens = min(T, ((T + 63) // 64 + n_seg - 1) // n_seg * 64)
+    summary_tokens = max(T - seg_tokens, 0) if n_seg > 1 else 0
+    per_kernel_bytes = {
+        "chunk_output": nbytes,
+        # k, g, v, beta of the tokens before the last segment; P and L out
+        "chunk_summary": B * H * summary_tokens * 2 * (2 * K + V + 1)
+                         + (n_seg - 1) * B * H * K * (K + V) * 4,
+        # P and L read, start states written over L
+        "segment_scan": (n_seg - 1) * B * H * K * (K + 2 * V) * 4,
+    }
+    dom = max(kernels, key=lambda n: kernels[n]["avg_ms"] * kernels[n]["launches_per_call"])
+    dom_ms = kernels[dom]["avg_ms"]
+    dom_bytes = per_kernel_bytes.get(dom, 0)
+    dom_gbs = dom_bytes / (dom_ms * 1e-3) / 1e9
+    traffic, traffic_note = recorded_traffic(dom, plan)
     del x, o, sT, ws
     torch.cuda.empty_cache()
 
     # ------------------------------------------------------------ decode workload
-    dcfg = CONFIGS["c4"]
-    d = make_decode_config(dcfg, dev)
-    pristine = d["state"]
-    state = pristine.clone()
-    od = torch.empty((dcfg.N, dcfg.H, dcfg.V), dtype=dcfg.dtype, device=dev)
+    dec = None
+    if not args.no_decode:
+        dcfg = CONFIGS["c4"]
+        d = make_decode_config(dcfg, dev)
+        pristine = d["state"]
+        state = pristine.clone()
+        od = torch.empty((dcfg.N, dcfg.H, dcfg.V), dtype=dcfg.dtype, device=dev)
 
-    def decode_pass():
-        for t in range(dcfg.steps):
-            kda.recurrent_step(d["q"][t], d["k"][t], d["v"][t], d["g"][t], d["beta"][t], state, out=od)
+        def decode_pass():
+            for t in range(dcfg.steps):
+                kda.recurrent_step(d["q"][t], d["k"][t], d["v"][t], d["g"][t], d["beta"][t], state, out=od)
 
-    state.copy_(pristine)
-    ms_pass = time_calls(decode_pass, 1, args.decode_passes)
-    ms_step = ms_pass / dcfg.steps
-    dec_tok_s = dcfg.N / (ms_step * 1e-3)
-    dec_bytes = decode_bytes(dcfg.N, dcfg.H, dcfg.K, dcfg.V)
-    dec_gbs = dec_bytes / (ms_step * 1e-3) / 1e9
-    del d, pristine, state, od
-    torch.cuda.empty_cache()
+        state.copy_(pristine)
+        ms_pass = time_calls(decode_pass, 1, args.decode_passes)
+        dk = time_launches(decode_pass, 1)["decode_step"]
+        ms_step = ms_pass / dcfg.steps
+        dec_bytes = decode_bytes(dcfg.N, dcfg.H, dcfg.K, dcfg.V)
+        dec_gbs = dec_bytes / (ms_step * 1e-3) / 1e9
+        dec = {"workload": "256 seq x 32 heads, K=V=128, fp32 state 512 MiB, 64 steps, bf16 tokens",
+               "tokens_per_s": dcfg.N / (ms_step * 1e-3), "ms_per_step": ms_step, "achieved_gbs": dec_gbs,
+               "hbm_frac": dec_gbs / HBM_PEAK_GBS, "bytes_per_step": dec_bytes,
+               "kernel_avg_ms": dk["avg_ms"],
+               "kernel_gbs": dec_bytes / (dk["avg_ms"] * 1e-3) / 1e9}
+        del d, pristine, state, od
+        torch.cuda.empty_cache()
 
     extra = {}
     if args.extra:
@@ -168,20 +242,39 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
-        xs = make_prefill_config(cfg, dev, H=args.cpu_heads)   # same recipe, fewer heads
-        q, k, v, g, be = (xs[n].cpu() for n in ("q", "k", "v", "g", "beta"))
         nthreads = oracle.oracle_max_threads()
-        t0 = time.perf_counter()
-        oracle.oracle_fwd(q, k, v, g, be, None, nthreads=nthreads)
-        dt = time.perf_counter() - t0
-        head_tokens = cfg.B * cfg.T * args.cpu_heads
+
+        def oracle_inputs(nh):
+            xs = make_prefill_config(cfg, dev, H=nh)   # same recipe, first nh heads' draws
+            return [xs[n].cpu() for n in ("q", "k", "v", "g", "beta")]
+
+        def run_oracle(inp, reps):
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                oracle.oracle_fwd(*inp, None, nthreads=nthreads)
+            return time.perf_counter() - t0
+
+        # the oracle parallelises over (b, h, 16-column block) chains: size the
+        # sample (heads, then repetitions of the whole workload) so that every
+        # thread has chains and the run lasts about cpu_seconds
+        chains1 = V // 16
+        t1 = run_oracle(oracle_inputs(1), 1)
+        per_chain = t1 / -(-chains1 // nthreads)
+        rounds = max(1, int(args.cpu_seconds / max(per_chain, 1e-9)))
+        nh = max(1, min(H, rounds * nthreads // chains1))
+        inp = oracle_inputs(nh)
+        t_one = run_oracle(inp, 1)
+        reps = max(1, int(round(args.cpu_seconds / max(t_one, 1e-9)))) if nh == H else 1
+        dt = run_oracle(inp, reps) if reps > 1 else t_one
+        chains = nh * chains1
         cpu = {
-            "value": head_tokens / dt / cfg.H,       # tokens/s of all 32 heads
+            "value": B * T * nh * reps / dt / H,       # tokens/s of all H heads
             "unit": "tokens/s",
-            "cores": nthreads,
+            "cores": min(nthreads, chains),
             "kind": "oracle",
-            "sample": "fp64 token-by-token oracle on %d of %d heads of the 8K workload (T=%d), "
-                      "%.1f s; scaled to all heads" % (args.cpu_heads, cfg.H, cfg.T, dt),
+            "sample": "fp64 token-by-token oracle (C, OpenMP, %d threads) on %d of %d heads of the 8K "
+                      "workload (B=1, T=%d, K=V=128), run %d time(s): %.1f s wall; tokens/s scaled to "
+                      "all %d heads" % (min(nthreads, chains), nh, H, T, reps, dt, H),
         }
 
     line = {
@@ -200,15 +293,18 @@ def main():
         "config": {"workload": "KDA prefill B=1 T=8192 H=32 K=V=128 bf16 in, fp32 state, S0=0, final state out",
                    "global_batch": B, "seq_len": T, "heads": H, "plan": {"n_seg": plan[0], "v_block": plan[1]},
                    "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": gbs / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "kda_chunk_fwd call (all launches of the plan)",
-                     "algorithmic_bytes_per_call": nbytes},
+        "roofline": {"bound": "hbm", "achieved": dom_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": dom_gbs / HBM_PEAK_GBS,
+                     "traffic": traffic,
+                     "kernel": dom, "kernel_avg_ms": dom_ms,
+                     "algorithmic_bytes_per_launch": dom_bytes,
+                     "traffic_note": traffic_note},
+        "roofline_call": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_call": nbytes},
         "mfma": {"achieved_tflops": tflops, "peak_tflops": BF16_PEAK_TFLOPS, "frac": tflops / BF16_PEAK_TFLOPS,
                  "algorithmic_flops_per_call": nflops},
-        "decode": {"workload": "256 seq x 32 heads, K=V=128, fp32 state 512 MiB, 64 steps, bf16 tokens",
-                   "tokens_per_s": dec_tok_s, "ms_per_step": ms_step, "achieved_gbs": dec_gbs,
-                   "hbm_frac": dec_gbs / HBM_PEAK_GBS, "bytes_per_step": dec_bytes},
+        "kernels": kernels,
+        "decode": dec,
         "cpu_baseline": cpu,
     }
     if extra:

@@ -11,11 +11,13 @@ from .kda import (  # noqa: F401
     chunk_plan,
     chunk_workspace_size,
     load_library,
+    profile_start,
+    profile_stop,
     recurrent_step,
     status_string,
     version,
 )
 from .build import LIB_PATH, build_library  # noqa: F401
 
-__all__ = ["chunk_fwd", "recurrent_step", "chunk_plan", "chunk_workspace_size",
+__all__ = ["chunk_fwd", "recurrent_step", "chunk_plan", "chunk_workspace_size", "profile_start", "profile_stop",
            "load_library", "build_library", "version", "status_string", "KDAError", "Plan"]

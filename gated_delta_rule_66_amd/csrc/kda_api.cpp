@@ -5,10 +5,41 @@
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <string.h>
 
 using namespace kda;
 
 namespace {
+
+// ---- optional per-launch timing (kda_profile_start / kda_profile_stop) ------
+// While active, every kernel launch is bracketed by two HIP events recorded on
+// the launch stream.  Process-wide, not thread-safe; off unless started.
+struct LaunchProfiler {
+    bool on = false;
+    int cap = 0, n = 0;
+    hipEvent_t* ev = nullptr;          // 2 * cap events
+    const char** names = nullptr;      // cap launch names
+};
+LaunchProfiler g_prof;
+
+template <class F>
+hipError_t launch_timed(const char* name, hipStream_t st, F&& launch) {
+    if (!g_prof.on || g_prof.n >= g_prof.cap) return launch();
+    const int i = g_prof.n++;
+    (void)hipEventRecord(g_prof.ev[2 * i], st);
+    const hipError_t e = launch();
+    (void)hipEventRecord(g_prof.ev[2 * i + 1], st);
+    g_prof.names[i] = name;
+    return e;
+}
+
+void profiler_release() {
+    if (g_prof.ev)
+        for (int i = 0; i < 2 * g_prof.cap; ++i) (void)hipEventDestroy(g_prof.ev[i]);
+    delete[] g_prof.ev;
+    delete[] g_prof.names;
+    g_prof = LaunchProfiler{};
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -168,8 +199,9 @@ kda_status kda_chunk_fwd(int B, int T, int H, int K, int V, kda_dtype dt,
 
     if (T == 0) {
         if (!final_state || final_state == initial_state) return KDA_OK;
-        return launch_copy_state(initial_state, final_state, (size_t)bh * K * V, st) == hipSuccess
-                   ? KDA_OK : KDA_ERR_HIP;
+        return launch_timed("copy_state", st, [&] {
+                   return launch_copy_state(initial_state, final_state, (size_t)bh * K * V, st);
+               }) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
     }
 
     kda_plan pl;
@@ -192,8 +224,9 @@ kda_status kda_chunk_fwd(int B, int T, int H, int K, int V, kda_dtype dt,
         p.sT = final_state;
         p.n_vb = V / vb;
         p.summary = 0;
-        return launch_chunk((int)dt, K, vb, p, (int)(bh * (V / vb)), st) == hipSuccess ? KDA_OK
-                                                                                     : KDA_ERR_HIP;
+        return launch_timed("chunk_output", st, [&] {
+                   return launch_chunk((int)dt, K, vb, p, (int)(bh * (V / vb)), st);
+               }) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
     }
 
     float* ws = reinterpret_cast<float*>(workspace);
@@ -207,7 +240,9 @@ kda_status kda_chunk_fwd(int B, int T, int H, int K, int V, kda_dtype dt,
     p1.n_vb = (K + V) / vb;
     p1.wsP = wsP;
     p1.wsL = wsL;
-    if (launch_chunk((int)dt, K, vb, p1, (int)(bh * (pl.n_seg - 1) * p1.n_vb), st) != hipSuccess)
+    if (launch_timed("chunk_summary", st, [&] {
+            return launch_chunk((int)dt, K, vb, p1, (int)(bh * (pl.n_seg - 1) * p1.n_vb), st);
+        }) != hipSuccess)
         return KDA_ERR_HIP;
     // pass 2: serial combine per (b, h): segment start states, over L
     ScanParams sp{};
@@ -217,7 +252,8 @@ kda_status kda_chunk_fwd(int B, int T, int H, int K, int V, kda_dtype dt,
     sp.BH = (int)bh;
     sp.V = V;
     sp.n_seg = pl.n_seg;
-    if (launch_scan(K, sp, st) != hipSuccess) return KDA_ERR_HIP;
+    if (launch_timed("segment_scan", st, [&] { return launch_scan(K, sp, st); }) != hipSuccess)
+        return KDA_ERR_HIP;
     // pass 3: every segment from its true start state, with output
     const bool aliased = final_state && final_state == initial_state;
     ChunkParams p3 = p;
@@ -227,9 +263,13 @@ kda_status kda_chunk_fwd(int B, int T, int H, int K, int V, kda_dtype dt,
     p3.seg_init = wsL;
     p3.o = o;
     p3.sT = aliased ? wsFinal : final_state;
-    if (launch_chunk((int)dt, K, vb, p3, (int)(bh * pl.n_seg * p3.n_vb), st) != hipSuccess)
+    if (launch_timed("chunk_output", st, [&] {
+            return launch_chunk((int)dt, K, vb, p3, (int)(bh * pl.n_seg * p3.n_vb), st);
+        }) != hipSuccess)
         return KDA_ERR_HIP;
-    if (aliased && launch_copy_state(wsFinal, final_state, (size_t)bh * K * V, st) != hipSuccess)
+    if (aliased && launch_timed("copy_state", st, [&] {
+            return launch_copy_state(wsFinal, final_state, (size_t)bh * K * V, st);
+        }) != hipSuccess)
         return KDA_ERR_HIP;
     return KDA_OK;
 }
@@ -254,8 +294,48 @@ kda_status kda_recurrent_step(int N, int H, int K, int V, kda_dtype dt,
     p.state = state;
     p.o = o;
     p.NH = (int)nh;
-    return launch_decode((int)dt, K, V, p, reinterpret_cast<hipStream_t>(stream)) == hipSuccess
-               ? KDA_OK : KDA_ERR_HIP;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    return launch_timed("decode_step", st, [&] { return launch_decode((int)dt, K, V, p, st); }) ==
+                   hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_profile_start(int max_launches) {
+    if (max_launches <= 0 || max_launches > (1 << 20)) return KDA_ERR_INVALID_ARG;
+    profiler_release();
+    g_prof.ev = new hipEvent_t[2 * (size_t)max_launches]();
+    g_prof.names = new const char*[max_launches]();
+    for (int i = 0; i < 2 * max_launches; ++i) {
+        if (hipEventCreate(&g_prof.ev[i]) != hipSuccess) {
+            for (int j = 0; j < i; ++j) (void)hipEventDestroy(g_prof.ev[j]);
+            delete[] g_prof.ev;
+            delete[] g_prof.names;
+            g_prof = LaunchProfiler{};
+            return KDA_ERR_HIP;
+        }
+    }
+    g_prof.cap = max_launches;
+    g_prof.on = true;
+    return KDA_OK;
+}
+
+int kda_profile_stop(const char** names, float* ms, int cap) {
+    if (!g_prof.ev) return -1;
+    const int n = g_prof.n;
+    int ret = n;
+    for (int i = 0; i < n; ++i) {
+        float t = 0.f;
+        if (hipEventSynchronize(g_prof.ev[2 * i + 1]) != hipSuccess ||
+            hipEventElapsedTime(&t, g_prof.ev[2 * i], g_prof.ev[2 * i + 1]) != hipSuccess) {
+            ret = -1;
+            break;
+        }
+        if (i < cap) {
+            if (names) names[i] = g_prof.names[i];
+            if (ms) ms[i] = t;
+        }
+    }
+    profiler_release();
+    return ret;
 }
 
 }  // extern "C"

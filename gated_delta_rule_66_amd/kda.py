@@ -29,6 +29,8 @@ EXPORTED_SYMBOLS = (
     "kda_recurrent_step",
     "kda_status_string",
     "kda_version",
+    "kda_profile_start",
+    "kda_profile_stop",
 )
 
 
@@ -67,6 +69,10 @@ def load_library(path: str = LIB_PATH):
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_version.argtypes = []
     lib.kda_version.restype = ctypes.c_char_p
+    lib.kda_profile_start.argtypes = [i]
+    lib.kda_profile_start.restype = i
+    lib.kda_profile_stop.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_float), i]
+    lib.kda_profile_stop.restype = i
     _lib = lib
     return lib
 
@@ -77,6 +83,23 @@ def status_string(status: int) -> str:
 
 def version() -> str:
     return load_library().kda_version().decode()
+
+
+def profile_start(max_launches: int = 4096) -> None:
+    """Start per-launch event timing of the library's kernels (``kda_profile_start``)."""
+    st = load_library().kda_profile_start(int(max_launches))
+    if st != KDA_OK:
+        raise KDAError(st, "kda_profile_start")
+
+
+def profile_stop(cap: int = 4096):
+    """Stop timing; returns [(launch name, milliseconds)] in launch order."""
+    names = (ctypes.c_char_p * cap)()
+    ms = (ctypes.c_float * cap)()
+    n = load_library().kda_profile_stop(names, ms, int(cap))
+    if n < 0:
+        raise RuntimeError("kda_profile_stop failed (profiling not started or event query failed)")
+    return [(names[i].decode(), float(ms[i])) for i in range(min(n, cap))]
 
 
 def _dtype_code(dt: torch.dtype) -> int:

@@ -27,8 +27,7 @@
  *     Alignment: states and the workspace 16 bytes; for prefill q, k, v, g
  *     and o 16 bytes and beta its element size; for decode every token
  *     tensor its element size.  The caller owns every buffer, the workspace
- *     included; the library allocates no memory and keeps no state between
- *     calls.
+ *     included; the library allocates no device memory.
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is
  *     the default stream) of the current HIP device.  Nothing is synchronised.
  *   - Arguments are validated on the host before anything is launched; on an
@@ -40,6 +39,8 @@
  *   - Token tensors (q, k, v, g, beta, o) share one dtype `dt`; states are
  *     always fp32.  o is rounded to `dt` (round to nearest even).
  *   - Results are deterministic: no floating-point atomics.
+ *   - The library keeps no state between calls, except the opt-in launch
+ *     timing of kda_profile_start / kda_profile_stop below.
  *   - Non-finite inputs propagate; they are not detected.
  */
 #ifndef KDA_H
@@ -139,6 +140,23 @@ kda_status kda_recurrent_step(int N, int H, int K, int V, kda_dtype dt,
                               const void* q, const void* k, const void* v,
                               const void* g, const void* beta,
                               float* state, void* o, void* stream);
+
+/*
+ * Optional per-launch timing, for benchmarks and tracing.  After
+ * kda_profile_start(max_launches), each kernel launched by kda_chunk_fwd or
+ * kda_recurrent_step (up to max_launches of them) is bracketed by two HIP
+ * events recorded on its own stream; launches beyond that are not timed.
+ * kda_profile_stop waits for the recorded events, writes up to `cap` launch
+ * names (static strings: "chunk_output", "chunk_summary", "segment_scan",
+ * "copy_state", "decode_step") and durations in milliseconds, releases the
+ * events, and returns the number of timed launches (-1: profiling was not
+ * started or a HIP event query failed).  The recording state is process-wide
+ * and not thread-safe; profiling is off unless started.
+ * kda_profile_start returns KDA_ERR_INVALID_ARG for max_launches outside
+ * [1, 2^20] and KDA_ERR_HIP if an event cannot be created.
+ */
+kda_status kda_profile_start(int max_launches);
+int kda_profile_stop(const char** names, float* ms, int cap);
 
 /* Static description of a status code. */
 const char* kda_status_string(kda_status s);

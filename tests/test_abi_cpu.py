@@ -132,6 +132,16 @@ def test_decode_rejects_bad_arguments():
     assert lib.kda_recurrent_step(0, 2, 128, 128, BF16, *args(), None) == OK
 
 
+def test_profile_calls_validate_without_a_gpu():
+    lib = _lib()
+    lib.kda_profile_stop.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+    lib.kda_profile_stop.restype = ctypes.c_int
+    assert lib.kda_profile_stop(None, None, 0) == -1          # never started
+    assert lib.kda_profile_start(0) == INVALID
+    assert lib.kda_profile_start(-3) == INVALID
+    assert lib.kda_profile_start((1 << 20) + 1) == INVALID
+
+
 def test_package_raises_without_library(tmp_path):
     saved = K_._lib
     K_._lib = None

@@ -270,6 +270,24 @@ def test_deterministic_repeat():
         assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
+def test_launch_profiling_names_every_launch():
+    say("per-launch event timing: plain and segmented plans")
+    import gated_delta_rule_66_amd as kda
+    d = make_prefill(1, 64 * 12, 2, 128, 128, torch.bfloat16, seed=23)
+    x = to_dev(d)
+    ws = torch.empty(kda.chunk_workspace_size(1, 64 * 12, 2, 128, 128, torch.bfloat16, (3, 64)),
+                     dtype=torch.uint8, device=DEV)
+    kda.profile_start(16)
+    gpu_fwd(x, (1, 64))
+    gpu_fwd(x, (3, 64), workspace=ws)
+    rec = kda.profile_stop(16)
+    assert [n for n, _ in rec] == ["chunk_output", "chunk_summary", "segment_scan", "chunk_output"]
+    assert all(ms > 0 for _, ms in rec)
+    o, _ = gpu_fwd(x, (1, 64))                 # timing is off again: results unchanged
+    ref, _ = run_oracle(d)
+    assert o_err(o, ref) < TOL[torch.bfloat16]
+
+
 # ------------------------------------------------------------------ decode
 @pytest.mark.parametrize("dtype,K,V", [(torch.bfloat16, 128, 128), (torch.bfloat16, 64, 128),
                                        (torch.bfloat16, 128, 64), (torch.float32, 64, 64),
