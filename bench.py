@@ -163,18 +163,15 @@ def main():
     gbs = nbytes / (ms * 1e-3) / 1e9
     tflops = nflops / (ms * 1e-3) / 1e12
 
-    # algorithmic bytes per launch of each kernel: 1,282 B per head-token it
-    # processes (q, k, g, v, beta in; o out) plus the states it must move
-    n_seg = plan[0]
-    seg_tokens = min(T, ((T + 63) // 64 + n_seg - 1) // n_seg * 64)
-    summary_tokens = max(T - seg_tokens, 0) if n_seg > 1 else 0
+    # algorithmic bytes per launch of each kernel: the path's 1,282 B per
+    # head-token (q, k, g, v, beta in; o out) plus the states, attributed to
+    # the kernel that moves them; workspace traffic (segment summaries, the
+    # per-chunk records of the two-pass plan) is overhead and counts zero
+    in_bytes = B * T * H * 2 * (3 * K + V + 1)
+    out_bytes = B * T * H * 2 * V + B * H * K * V * 4
     per_kernel_bytes = {
-        "chunk_output": nbytes,
-        # k, g, v, beta of the tokens before the last segment; P and L out
-        "chunk_summary": B * H * summary_tokens * 2 * (2 * K + V + 1)
-                         + (n_seg - 1) * B * H * K * (K + V) * 4,
-        # P and L read, start states written over L
-        "segment_scan": (n_seg - 1) * B * H * K * (K + 2 * V) * 4,
+        "chunk_output": nbytes, "chunk_summary": 0, "segment_scan": 0, "copy_state": 0,
+        "intra_chunk": in_bytes, "state_output": out_bytes, "state_summary": 0,
     }
     dom = max(kernels, key=lambda n: kernels[n]["avg_ms"] * kernels[n]["launches_per_call"])
     dom_ms = kernels[dom]["avg_ms"]
@@ -291,7 +288,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "KDA prefill B=1 T=8192 H=32 K=V=128 bf16 in, fp32 state, S0=0, final state out",
-                   "global_batch": B, "seq_len": T, "heads": H, "plan": {"n_seg": plan[0], "v_block": plan[1]},
+                   "global_batch": B, "seq_len": T, "heads": H,
+                   "plan": {"n_seg": plan[0], "v_block": plan[1], "split": plan[2]},
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": dom_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": dom_gbs / HBM_PEAK_GBS,

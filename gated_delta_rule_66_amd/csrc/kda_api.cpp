@@ -86,34 +86,55 @@ kda_status resolve_plan(int B, int T, int H, int K, int V, kda_dtype dt, const k
     const long bh = (long)B * H;
     int vb = req ? req->v_block : 0;
     int ns = req ? req->n_seg : 0;
-    if (vb < 0 || ns < 0) return KDA_ERR_INVALID_ARG;
+    int split = req ? req->split : 0;
+    if (vb < 0 || ns < 0 || split < 0 || split > 2) return KDA_ERR_INVALID_ARG;
+    if (vb != 0 && vb != 64 && vb != 128) return KDA_ERR_INVALID_ARG;
+    if (split == 0) split = split_variant_exists((int)dt, K, V, 64) ? 2 : 1;
     int cus = 0;
     if (vb == 0 || ns == 0) {
         kda_status s = device_cus(&cus);
         if (s != KDA_OK) return s;
     }
     const bool vb_fixed = vb != 0;
-    if (vb_fixed) {
-        if (vb != 64 && vb != 128) return KDA_ERR_INVALID_ARG;
-        if (vb > V || !chunk_variant_exists((int)dt, K, vb)) return KDA_ERR_UNSUPPORTED;
+    if (split == 2) {
+        // state pass: two workgroups fit a CU; 64 value columns per workgroup
+        // unless asked otherwise
+        if (!vb_fixed) vb = 64;
+        if (vb > V || !split_variant_exists((int)dt, K, V, vb)) return KDA_ERR_UNSUPPORTED;
+        if (ns == 0) {
+            // segments until the state pass has about two workgroups per CU,
+            // each segment keeping at least 4 chunks
+            const long wgs = bh * (V / vb);
+            ns = 1;
+            if (wgs > 0 && wgs < 2L * cus) {
+                const long want = (2L * cus + wgs - 1) / wgs;
+                const long cap = n_chunks / 4;
+                ns = (int)(want < cap ? want : cap);
+                if (ns < 1) ns = 1;
+            }
+        }
     } else {
-        // the widest block that still gives every CU a workgroup, else 64
-        vb = 64;
-        if (V >= 128 && K >= 128 && chunk_variant_exists((int)dt, K, 128) && bh * (V / 128) >= cus)
-            vb = 128;
-        if (!chunk_variant_exists((int)dt, K, vb)) return KDA_ERR_UNSUPPORTED;
-    }
-    if (ns == 0) {
-        // split long sequences into segments when (b, h, column block)
-        // workgroups alone leave compute units idle; each segment keeps at
-        // least 8 chunks so the extra summary pass stays amortised
-        const long wgs = bh * (V / vb);
-        ns = 1;
-        if (wgs > 0 && wgs < cus) {
-            const long want = (cus + wgs - 1) / wgs;
-            const long cap = n_chunks / 8;
-            ns = (int)(want < cap ? want : cap);
-            if (ns < 1) ns = 1;
+        if (vb_fixed) {
+            if (vb > V || !chunk_variant_exists((int)dt, K, vb)) return KDA_ERR_UNSUPPORTED;
+        } else {
+            // the widest block that still gives every CU a workgroup, else 64
+            vb = 64;
+            if (V >= 128 && K >= 128 && chunk_variant_exists((int)dt, K, 128) && bh * (V / 128) >= cus)
+                vb = 128;
+            if (!chunk_variant_exists((int)dt, K, vb)) return KDA_ERR_UNSUPPORTED;
+        }
+        if (ns == 0) {
+            // split long sequences into segments when (b, h, column block)
+            // workgroups alone leave compute units idle; each segment keeps at
+            // least 8 chunks so the extra summary pass stays amortised
+            const long wgs = bh * (V / vb);
+            ns = 1;
+            if (wgs > 0 && wgs < cus) {
+                const long want = (cus + wgs - 1) / wgs;
+                const long cap = n_chunks / 8;
+                ns = (int)(want < cap ? want : cap);
+                if (ns < 1) ns = 1;
+            }
         }
     }
     if (n_chunks > 0 && ns > n_chunks) ns = n_chunks;
@@ -127,16 +148,31 @@ kda_status resolve_plan(int B, int T, int H, int K, int V, kda_dtype dt, const k
     }
     out->n_seg = ns;
     out->v_block = vb;
+    out->split = split;
     if (cps_out) *cps_out = cps;
     return KDA_OK;
 }
 
-size_t workspace_bytes_for(int B, int H, int K, int V, const kda_plan& pl) {
+size_t record_bytes(int K, int V, kda_dtype dt) {
+    return rec_layout(K, V, (int)elem_size(dt)).bytes;
+}
+
+size_t segment_bytes(int B, int H, int K, int V, const kda_plan& pl) {
     if (pl.n_seg <= 1) return 0;
     const size_t bh = (size_t)B * H;
     // transitions P (K x K) and local states L (K x V) of all but the last
     // segment, plus one K x V slot per (b, h) for a redirected final state
     return ((size_t)(pl.n_seg - 1) * bh * K * (size_t)(K + V) + bh * K * V) * sizeof(float);
+}
+
+size_t workspace_bytes_for(int B, int T, int H, int K, int V, kda_dtype dt, const kda_plan& pl) {
+    size_t n = segment_bytes(B, H, K, V, pl);
+    if (pl.split == 2) {
+        const size_t nc = (size_t)(T + kChunk - 1) / kChunk;
+        n = (n + 255) & ~(size_t)255;
+        n += (size_t)B * H * nc * record_bytes(K, V, dt);
+    }
+    return n;
 }
 
 }  // namespace
@@ -168,7 +204,7 @@ size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int K, int V, kda_dtype
     if (check_prefill_sizes(B, T, H, K, V, dt) != KDA_OK) return (size_t)-1;
     kda_plan pl;
     if (resolve_plan(B, T, H, K, V, dt, plan, &pl, nullptr) != KDA_OK) return (size_t)-1;
-    return workspace_bytes_for(B, H, K, V, pl);
+    return workspace_bytes_for(B, T, H, K, V, dt, pl);
 }
 
 kda_status kda_chunk_fwd(int B, int T, int H, int K, int V, kda_dtype dt,
@@ -208,8 +244,84 @@ kda_status kda_chunk_fwd(int B, int T, int H, int K, int V, kda_dtype dt,
     int cps = 1;
     s = resolve_plan(B, T, H, K, V, dt, plan, &pl, &cps);
     if (s != KDA_OK) return s;
-    const size_t need = workspace_bytes_for(B, H, K, V, pl);
+    const size_t need = workspace_bytes_for(B, T, H, K, V, dt, pl);
     if (need > 0 && (!workspace || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
+
+    if (pl.split == 2) {
+        // ---- intra-chunk pass: every (b, h, chunk) record at once ----------
+        const int NC = (T + kChunk - 1) / kChunk;
+        const size_t seg_b = (segment_bytes(B, H, K, V, pl) + 255) & ~(size_t)255;
+        unsigned char* recs = reinterpret_cast<unsigned char*>(workspace) + seg_b;
+        IntraParams ip{};
+        ip.q = q; ip.k = k; ip.v = v; ip.g = g; ip.beta = beta;
+        ip.rec = recs;
+        ip.B = B; ip.T = T; ip.H = H; ip.NC = NC;
+        const long items = bh * NC;
+        if (items > 2000000000L) return KDA_ERR_UNSUPPORTED;
+        ip.n_items = (int)items;
+        int cus = 0;
+        if (device_cus(&cus) != KDA_OK) return KDA_ERR_HIP;
+        const int igrid = (int)(items < cus ? items : cus);
+        if (launch_timed("intra_chunk", st, [&] { return launch_intra((int)dt, K, V, ip, igrid, st); }) !=
+            hipSuccess)
+            return KDA_ERR_HIP;
+        // ---- state pass ---------------------------------------------------------
+        const int vb = pl.v_block;
+        StateParams sp{};
+        sp.rec = recs;
+        sp.B = B; sp.T = T; sp.H = H; sp.V = V; sp.NC = NC;
+        sp.n_seg = pl.n_seg;
+        sp.cps = cps;
+        if (pl.n_seg == 1) {
+            sp.s0 = initial_state;
+            sp.o = o;
+            sp.sT = final_state;
+            sp.n_vb = V / vb;
+            sp.summary = 0;
+            return launch_timed("state_output", st, [&] {
+                       return launch_state((int)dt, K, vb, sp, (int)(bh * (V / vb)), st);
+                   }) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+        }
+        float* ws = reinterpret_cast<float*>(workspace);
+        float* wsP = ws;
+        float* wsL = wsP + (size_t)(pl.n_seg - 1) * bh * K * K;
+        float* wsFinal = wsL + (size_t)(pl.n_seg - 1) * bh * K * V;
+        StateParams s1 = sp;
+        s1.summary = 1;
+        s1.n_vb = (K + V) / vb;
+        s1.wsP = wsP;
+        s1.wsL = wsL;
+        if (launch_timed("state_summary", st, [&] {
+                return launch_state((int)dt, K, vb, s1, (int)(bh * (pl.n_seg - 1) * s1.n_vb), st);
+            }) != hipSuccess)
+            return KDA_ERR_HIP;
+        ScanParams scp{};
+        scp.s0 = initial_state;
+        scp.wsP = wsP;
+        scp.wsL = wsL;
+        scp.BH = (int)bh;
+        scp.V = V;
+        scp.n_seg = pl.n_seg;
+        if (launch_timed("segment_scan", st, [&] { return launch_scan(K, scp, st); }) != hipSuccess)
+            return KDA_ERR_HIP;
+        const bool aliased = final_state && final_state == initial_state;
+        StateParams s3 = sp;
+        s3.summary = 0;
+        s3.n_vb = V / vb;
+        s3.s0 = initial_state;
+        s3.seg_init = wsL;
+        s3.o = o;
+        s3.sT = aliased ? wsFinal : final_state;
+        if (launch_timed("state_output", st, [&] {
+                return launch_state((int)dt, K, vb, s3, (int)(bh * pl.n_seg * s3.n_vb), st);
+            }) != hipSuccess)
+            return KDA_ERR_HIP;
+        if (aliased && launch_timed("copy_state", st, [&] {
+                return launch_copy_state(wsFinal, final_state, (size_t)bh * K * V, st);
+            }) != hipSuccess)
+            return KDA_ERR_HIP;
+        return KDA_OK;
+    }
 
     ChunkParams p{};
     p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta;

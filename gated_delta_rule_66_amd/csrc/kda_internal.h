@@ -48,6 +48,60 @@ struct DecodeParams {
     int NH;                 // N * H
 };
 
+// ---- split path: intra-chunk pass, then state pass ----------------------------
+// Per (b, h, chunk) the intra-chunk pass writes one record of the operands the
+// state pass needs; all arrays row-major without padding, in the input dtype
+// except egc:
+//   W   [C][K]   (I + A)^{-1} diag(beta) K e^{G}
+//   Qh  [C][K]   Q e^{G}
+//   Mqk [C][C]   masked similarities, lower triangle incl. diagonal
+//   KbT [K][C]   (K e^{G_C - G})^T
+//   UtT [V][C]   ((I + A)^{-1} diag(beta) V)^T
+//   egc [K]      fp32 e^{G_C}
+// Records are 256-byte aligned; record (b*H + h)*NC + chunk.
+struct RecLayout {
+    size_t oW, oQh, oMqk, oKbT, oUtT, oEgc, bytes;
+};
+constexpr RecLayout rec_layout(int K, int V, int elem) {
+    RecLayout r{};
+    size_t o = 0;
+    r.oW = o;   o += (size_t)kChunk * K * elem;
+    r.oQh = o;  o += (size_t)kChunk * K * elem;
+    r.oMqk = o; o += (size_t)kChunk * kChunk * elem;
+    r.oKbT = o; o += (size_t)K * kChunk * elem;
+    r.oUtT = o; o += (size_t)V * kChunk * elem;
+    r.oEgc = o; o += (size_t)K * 4;
+    r.bytes = (o + 255) & ~(size_t)255;
+    return r;
+}
+
+struct IntraParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* g;
+    const void* beta;
+    unsigned char* rec;     // [B*H*NC] records
+    int B, T, H, NC;        // NC = chunks per sequence
+    int n_items;            // B * H * NC
+};
+
+struct StateParams {
+    const unsigned char* rec;
+    const float* s0;        // [B,H,K,V] initial state of segment 0, or null (zeros)
+    const float* seg_init;  // [n_seg-1][B*H][K][V]: start state of segment s >= 1 at slot s-1
+    void* o;                // [B,T,H,V] (output pass only)
+    float* sT;              // [B,H,K,V] final state or null (output pass only)
+    float* wsP;             // summary pass: [n_seg-1][B*H][K][K]
+    float* wsL;             // summary pass: [n_seg-1][B*H][K][V]
+    int B, T, H, V, NC;
+    int n_seg, cps, n_vb, summary;
+};
+
+bool split_variant_exists(int dtype, int K, int V, int VB);
+hipError_t launch_intra(int dtype, int K, int V, const IntraParams& p, int grid, hipStream_t stream);
+hipError_t launch_state(int dtype, int K, int VB, const StateParams& p, int grid, hipStream_t stream);
+
 // Kernel-variant selection: returns false if (dtype, K, VB) has no kernel.
 bool chunk_variant_exists(int dtype, int K, int VB);
 

@@ -1,0 +1,802 @@
+// Split chunked KDA prefill for gfx950.
+//
+// Intra-chunk pass: every (batch, head, chunk) at once, independent of the
+// state: gate cumsum, intra-chunk similarities, the UT solve, and the chunk's
+// operands of the state pass written to a workspace record.
+// State pass: per (batch, head, segment, value-column block), the chunks in
+// order: U = U~ - W S, O = (Q e^G) S + Mqk U, S <- Diag(e^{G_C}) S + (K e^{G_C-G})^T U.
+//
+// Page: "Kimi K3 — открытая модель, которая обошла закрытых лидеров рынка"
+// (aiblin.ru), section "Как распараллелили последовательное обновление": the
+// tokens of a chunk are handled together and only the state is passed from
+// chunk to chunk; here the chunk-local part runs for all chunks side by side,
+// so only the state pass is sequential.  The chunk-form algebra and the
+// sub-chunk split of the gate exponents are those of the single-pass kernel.
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+namespace {
+
+constexpr int C = kChunk;
+
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
+__device__ __forceinline__ void offdiag_pair(int p, int& i, int& j) {
+    i = (p >= 3) ? 3 : (p >= 1) ? 2 : 1;
+    j = p - i * (i - 1) / 2;
+}
+__device__ __forceinline__ void lower_pair(int p, int& i, int& j) {
+    i = (p >= 6) ? 3 : (p >= 3) ? 2 : (p >= 1) ? 1 : 0;
+    j = p - i * (i + 1) / 2;
+}
+
+template <typename T>
+__device__ __forceinline__ void ld8_as_f32(const T* p, float* x) {
+    typename FragOf<T>::type f = ld_frag<T>(p);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = to_f32(f[i]);
+}
+
+// column side of block pair (i, j) for the 32-deep slab at channel c0
+template <typename T, int LDK1, int K>
+__device__ __forceinline__ typename FragOf<T>::type col_frag(const T* sKinv, const float* sF, int i, int j,
+                                                            int lr, int c0) {
+    if (i == j) return ld_frag<T>(&sKinv[(16 * j + lr) * LDK1 + c0]);
+    float kv[8], f[8];
+    ld8_as_f32<T>(&sKinv[(16 * j + lr) * LDK1 + c0], kv);
+    ld8f(&sF[(i * (i - 1) / 2 + j) * K + c0], f);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) kv[e] *= f[e];
+    return frag_from<T>(kv);
+}
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, unsigned voff) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// 4 values of T as one 8- (bf16) or 16-byte (fp32) global store
+__device__ __forceinline__ void st4(bf16* p, const float* x) {
+    bf16x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = (bf16)x[i];
+    *reinterpret_cast<bf16x4*>(p) = r;
+}
+__device__ __forceinline__ void st4(float* p, const float* x) {
+    *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+}
+
+}  // namespace
+
+// ============================================================================
+// Intra-chunk pass
+// ============================================================================
+template <typename T, int K, int V>
+struct IntraLayout {
+    static constexpr int NW = 8;                 // waves
+    static constexpr int NT = 64 * NW;
+    static constexpr int SZ = (int)sizeof(T);
+    static constexpr int PAD = 16 / SZ;
+    static constexpr int LDK1 = K + PAD;         // Kd, Qd, Kinv, W: [token][channel]
+    static constexpr int LDT = C + PAD;          // [channel][token]
+    static constexpr int LDL = C + 4;            // solve blocks / Mqk
+    static constexpr int LDD = 16;
+    // prep: wave w owns CPW groups of 8 key channels (TPL tokens per lane) and
+    // CPWV groups of 8 value columns (TPLV tokens per lane)
+    static constexpr int CPW = K / (8 * NW);
+    static constexpr int TPL = CPW;
+    static constexpr int NPART = 64 / CPW;
+    static constexpr int CPWV = V / (8 * NW);
+    static constexpr int TPLV = CPWV;
+    static constexpr int CT = K / 16, NVT = V / 16;
+    static constexpr int KQ = 3 * C * LDK1 * SZ;         // Kd | Qd | Kinv, then W staging
+    static constexpr int L_BYTES = C * LDL * SZ;
+    static constexpr int R = L_BYTES + 4 * 16 * LDD * 4;
+    static constexpr int oKQ = 0;
+    static constexpr int oR = oKQ + KQ;                  // solve blocks | fp32 diagonal blocks of A
+    static constexpr int oMqk = oR + R;
+    static constexpr int oKhbT = oMqk + C * LDL * SZ;    // [K][LDT] beta K e^{G}
+    static constexpr int oVbT = oKhbT + K * LDT * SZ;    // [V][LDT] beta V
+    static constexpr int oF = oVbT + V * LDT * SZ;       // fp32 [6][K]
+    static constexpr int oBeta = oF + 6 * K * 4;         // fp32 [C]
+    static constexpr int TOTAL = oBeta + C * 4;
+    static_assert(TOTAL <= 160 * 1024, "LDS budget exceeded");
+    static_assert(CPW * 8 * NW == K && (CPW == 1 || CPW == 2 || CPW == 4), "key prep mapping");
+    static_assert(CPWV * 8 * NW == V && (CPWV == 1 || CPWV == 2 || CPWV == 4), "value prep mapping");
+};
+
+template <typename T, int K, int V>
+__global__ __launch_bounds__(512) void kda_intra_kernel(IntraParams p) {
+    using L = IntraLayout<T, K, V>;
+    constexpr int NW = L::NW, NT = L::NT;
+    using Frag4 = typename Frag4Of<T>::type;
+    constexpr int LDK1 = L::LDK1, LDT = L::LDT, LDL = L::LDL, LDD = L::LDD;
+    constexpr int CPW = L::CPW, TPL = L::TPL, NPART = L::NPART;
+    constexpr int CPWV = L::CPWV, TPLV = L::TPLV;
+    constexpr int CT = L::CT, NVT = L::NVT;
+    constexpr int KS = K / 32;
+    constexpr unsigned SZ = sizeof(T);
+    constexpr RecLayout RL = rec_layout(K, V, (int)sizeof(T));
+
+    __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
+    T* sKd = reinterpret_cast<T*>(smem + L::oKQ);
+    T* sQd = sKd + C * LDK1;
+    T* sKinv = sQd + C * LDK1;
+    T* sW = reinterpret_cast<T*>(smem + L::oKQ);
+    T* sL = reinterpret_cast<T*>(smem + L::oR);
+    float* sAd = reinterpret_cast<float*>(smem + L::oR + L::L_BYTES);
+    T* sMqk = reinterpret_cast<T*>(smem + L::oMqk);
+    T* sKhbT = reinterpret_cast<T*>(smem + L::oKhbT);
+    T* sVbT = reinterpret_cast<T*>(smem + L::oVbT);
+    float* sF = reinterpret_cast<float*>(smem + L::oF);
+    float* sBeta = reinterpret_cast<float*>(smem + L::oBeta);
+
+    const int tid = threadIdx.x;
+    const int w = tid >> 6, l = tid & 63, lg = l >> 4, lr = l & 15;
+
+    const T* __restrict__ qg = reinterpret_cast<const T*>(p.q);
+    const T* __restrict__ kg = reinterpret_cast<const T*>(p.k);
+    const T* __restrict__ vg = reinterpret_cast<const T*>(p.v);
+    const T* __restrict__ gg = reinterpret_cast<const T*>(p.g);
+    const T* __restrict__ bg = reinterpret_cast<const T*>(p.beta);
+
+    const int c8l = l % CPW, part = l / CPW;
+    const int c0 = 8 * (CPW * w + c8l);
+    const int n8l = l % CPWV, pv = l / CPWV;
+    const int n0 = 8 * (CPWV * w + n8l);
+
+    Pack8<T> kr[TPL], qr[TPL], gr[TPL], vr[TPLV];
+    T br[TPL], bvr[TPLV];
+    const unsigned rowK = (unsigned)p.H * K * SZ, rowV = (unsigned)p.H * V * SZ, rowB = (unsigned)p.H * SZ;
+    const unsigned vK = (unsigned)part * TPL * rowK + (unsigned)c0 * SZ;
+    const unsigned vB = (unsigned)part * TPL * rowB;
+    const unsigned vV = (unsigned)pv * TPLV * rowV + (unsigned)n0 * SZ;
+    const unsigned vBV = (unsigned)pv * TPLV * rowB;
+    auto load_item = [&](int item) {
+        const int bh = item / p.NC, ci = item - bh * p.NC;
+        const int b = bh / p.H, h = bh - b * p.H;
+        const int t0 = ci * C;
+        const int nt = min(C, p.T - t0);
+        const size_t head_row = (size_t)(b * (size_t)p.T + t0) * p.H + h;
+        const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + head_row * K);
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(qg + head_row * K);
+        const __amdgpu_buffer_rsrc_t rg = make_rsrc(gg + head_row * K);
+        const __amdgpu_buffer_rsrc_t rb = make_rsrc(bg + head_row);
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + head_row * V);
+#pragma unroll
+        for (int i = 0; i < TPL; ++i) {
+            if (part * TPL + i < nt) {
+                buf_load8<T>(kr[i], rk, vK, i * rowK);
+                buf_load8<T>(gr[i], rg, vK, i * rowK);
+                buf_load8<T>(qr[i], rq, vK, i * rowK);
+                buf_load1(br[i], rb, vB, i * rowB);
+            } else {
+                kr[i].zero();
+                gr[i].zero();
+                qr[i].zero();
+                br[i] = from_f32<T>(0.f);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < TPLV; ++i) {
+            if (pv * TPLV + i < nt) {
+                buf_load8<T>(vr[i], rv, vV, i * rowV);
+                buf_load1(bvr[i], rb, vBV, i * rowB);
+            } else {
+                vr[i].zero();
+                bvr[i] = from_f32<T>(0.f);
+            }
+        }
+    };
+
+    const int G = gridDim.x;
+    if ((int)blockIdx.x < p.n_items) load_item(blockIdx.x);
+
+    for (int item = blockIdx.x; item < p.n_items; item += G) {
+        unsigned char* rec = p.rec + (size_t)item * RL.bytes;
+        T* gW = reinterpret_cast<T*>(rec + RL.oW);
+        T* gQh = reinterpret_cast<T*>(rec + RL.oQh);
+        T* gMqk = reinterpret_cast<T*>(rec + RL.oMqk);
+        T* gKbT = reinterpret_cast<T*>(rec + RL.oKbT);
+        T* gUtT = reinterpret_cast<T*>(rec + RL.oUtT);
+        float* gEgc = reinterpret_cast<float*>(rec + RL.oEgc);
+
+        // ---- P1: gate cumsum; key / query side to LDS, Qh, KbT, e^{G_C} out ----
+        {
+            float G[TPL][8];
+#pragma unroll
+            for (int i = 0; i < TPL; ++i) {
+                float g8[8];
+                gr[i].to_f32(g8);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) G[i][e] = (i ? G[i - 1][e] : 0.f) + clamp_gate_log2(g8[e]);
+            }
+            float incl[8], gfirst[8], gb[8], gcum[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) incl[e] = G[TPL - 1][e];
+#pragma unroll
+            for (int d = CPW; d < 64; d <<= 1) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float y = __shfl_up(incl[e], d);
+                    if (l >= d) incl[e] += y;
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float excl = incl[e] - G[TPL - 1][e];
+#pragma unroll
+                for (int i = 0; i < TPL; ++i) G[i][e] += excl;
+                gfirst[e] = G[0][e];
+                gcum[e] = __shfl(incl[e], (NPART - 1) * CPW + c8l);
+            }
+            const int myblk = (part * TPL) >> 4;
+            int pi_ = 1, pj_ = 0;
+            if (part < 6) offdiag_pair(part, pi_, pj_);
+            const int src_b = (16 * myblk / TPL) * CPW + c8l;
+            const int src_i = (16 * pi_ / TPL) * CPW + c8l;
+            const int src_j = (16 * pj_ / TPL) * CPW + c8l;
+            float f[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                gb[e] = __shfl(gfirst[e], src_b);
+                f[e] = fast_exp2(__shfl(gfirst[e], src_i) - __shfl(gfirst[e], src_j));
+            }
+            if (part < 6) st8(&sF[part * K + c0], f);
+            if (part == 0) {
+                float ec[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ec[e] = fast_exp2(gcum[e]);
+                st8(&gEgc[c0], ec);
+            }
+            if (w == 0 && c8l == 0) {
+#pragma unroll
+                for (int i = 0; i < TPL; ++i) sBeta[part * TPL + i] = to_f32(br[i]);
+            }
+            float egb[8], ecb[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                egb[e] = fast_exp2(gb[e]);
+                ecb[e] = fast_exp2(gcum[e] - gb[e]);
+            }
+            float kh[8][TPL], kb[8][TPL];
+#pragma unroll
+            for (int i = 0; i < TPL; ++i) {
+                const int t = part * TPL + i;
+                float kx[8], kd[8], ki[8];
+                kr[i].to_f32(kx);
+                const float bt = to_f32(br[i]);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float d = G[i][e] - gb[e];
+                    const float e1 = fast_exp2(d);
+                    const float e2 = fast_exp2(-d);
+                    kd[e] = kx[e] * e1;
+                    ki[e] = kx[e] * e2;
+                    kh[e][i] = bt * kd[e] * egb[e];
+                    kb[e][i] = ki[e] * ecb[e];
+                }
+                st8(&sKd[t * LDK1 + c0], kd);
+                st8(&sKinv[t * LDK1 + c0], ki);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < TPL; ++i) {
+                const int t = part * TPL + i;
+                float qx[8], qd[8], qh[8];
+                qr[i].to_f32(qx);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    qd[e] = qx[e] * fast_exp2(G[i][e] - gb[e]);
+                    qh[e] = qd[e] * egb[e];
+                }
+                st8(&sQd[t * LDK1 + c0], qd);
+                st8(&gQh[t * K + c0], qh);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                st_small<TPL>(&sKhbT[(c0 + e) * LDT + part * TPL], kh[e]);
+                st_small<TPL>(&gKbT[(c0 + e) * C + part * TPL], kb[e]);
+            }
+            float bv[8][TPLV];
+#pragma unroll
+            for (int i = 0; i < TPLV; ++i) {
+                float vx[8];
+                vr[i].to_f32(vx);
+                const float bt = to_f32(bvr[i]);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) bv[e][i] = bt * vx[e];
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) st_small<TPLV>(&sVbT[(n0 + e) * LDT + pv * TPLV], bv[e]);
+        }
+        __syncthreads();
+
+        // the raw registers are free: fetch the next item behind P2 / P3
+        __builtin_amdgcn_sched_barrier(0);
+        if (item + G < p.n_items) load_item(item + G);
+        __builtin_amdgcn_sched_barrier(0);
+
+        // ---- P2: diagonal blocks of A and their inverses; off-diagonal A; Mqk ----
+        // waves 0-3: diagonal block w, then task w; waves 4-7: tasks w, w+4, ...
+        // tasks 0-5: off-diagonal blocks of -A (into the solve buffer); 6-15:
+        // blocks of Mqk; 16, 17: the zero blocks (0,1), (2,3) of Mqk
+        if (w < 4) {
+            const int i = w;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                acc = mma(acc, ld_frag<T>(&sKd[(16 * i + lr) * LDK1 + 32 * ks + 8 * lg]),
+                          ld_frag<T>(&sKinv[(16 * i + lr) * LDK1 + 32 * ks + 8 * lg]));
+            float* Ad = sAd + i * 16 * LDD;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int s_ = 4 * lg + e;
+                Ad[s_ * LDD + lr] = (lr < s_) ? sBeta[16 * i + s_] * acc[e] : 0.f;
+            }
+            wave_lds_sync();
+            if (lg == 0) {
+                // column lr of (I + A_ii)^{-1} by forward substitution
+                const int j = lr;
+                float xv[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float row[16];
+#pragma unroll
+                    for (int m4 = 0; m4 < 4; ++m4) {
+                        const f32x4 a4 = *reinterpret_cast<const f32x4*>(&Ad[r * LDD + 4 * m4]);
+                        row[4 * m4] = a4[0];
+                        row[4 * m4 + 1] = a4[1];
+                        row[4 * m4 + 2] = a4[2];
+                        row[4 * m4 + 3] = a4[3];
+                    }
+                    float a = (r == j) ? 1.f : 0.f;
+#pragma unroll
+                    for (int m = 0; m < r; ++m) a -= row[m] * xv[m];
+                    xv[r] = a;
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) sL[(16 * i + r) * LDL + 16 * i + j] = from_f32<T>(xv[r]);
+            }
+        }
+        {
+            constexpr int NTASK = 18;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int task = (w < 4) ? (m == 0 ? w : NTASK) : w + 4 * m;
+                if (task < NTASK) {
+                    if (task < 16) {
+                        int i, j;
+                        if (task < 6) offdiag_pair(task, i, j);
+                        else lower_pair(task - 6, i, j);
+                        const T* rowsrc = (task < 6) ? sKd : sQd;
+                        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int ks = 0; ks < KS; ++ks) {
+                            const int cc = 32 * ks + 8 * lg;
+                            acc = mma(acc, ld_frag<T>(&rowsrc[(16 * i + lr) * LDK1 + cc]),
+                                      col_frag<T, LDK1, K>(sKinv, sF, i, j, lr, cc));
+                        }
+                        const int r = 16 * j + lr;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int s_ = 16 * i + 4 * lg + e;
+                            if (task < 6) sL[s_ * LDL + r] = from_f32<T>(-sBeta[s_] * acc[e]);
+                            else sMqk[s_ * LDL + r] = from_f32<T>((i > j || r <= s_) ? acc[e] : 0.f);
+                        }
+                    } else {
+                        const int i = (task == 16) ? 0 : 2, j = i + 1;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            sMqk[(16 * i + 4 * lg + e) * LDL + 16 * j + lr] = from_f32<T>(0.f);
+                    }
+                }
+            }
+        }
+        __syncthreads();
+
+        // ---- P3: W and U~ tiles by block forward substitution; Mqk out ----------
+        {
+            // Mqk rows, 16 bytes at a time
+            constexpr int PPR = C * (int)SZ / 16;
+#pragma unroll
+            for (int pc = tid; pc < C * PPR; pc += NT) {
+                const int row = pc / PPR, seg = pc % PPR;
+                *reinterpret_cast<uint4*>(&gMqk[row * C + seg * (16 / (int)SZ)]) =
+                    *reinterpret_cast<const uint4*>(&sMqk[row * LDL + seg * (16 / (int)SZ)]);
+            }
+        }
+        {
+            Frag4 Ld[4], Lo[6];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Ld[i] = ld_frag4<T>(&sL[(16 * i + lr) * LDL + 16 * i + 4 * lg]);
+#pragma unroll
+            for (int q6 = 0; q6 < 6; ++q6) {
+                const int i = (q6 >= 3) ? 3 : (q6 >= 1) ? 2 : 1;
+                const int k = q6 - i * (i - 1) / 2;
+                Lo[q6] = ld_frag4<T>(&sL[(16 * i + lr) * LDL + 16 * k + 4 * lg]);
+            }
+            auto solve_tile = [&](const T* rhs, f32x4* X) {
+                Frag4 Xb[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    f32x4 acc = ld4_as_f32<T>(rhs + lr * LDT + 16 * i + 4 * lg);
+#pragma unroll
+                    for (int k = 0; k < i; ++k) acc = mma16(acc, Lo[i * (i - 1) / 2 + k], Xb[k]);
+                    X[i] = mma16(f32x4{0.f, 0.f, 0.f, 0.f}, Ld[i], frag4_from<T>(acc));
+                    Xb[i] = frag4_from<T>(X[i]);
+                }
+            };
+#pragma unroll
+            for (int m = 0; m < (CT + NVT + NW - 1) / NW; ++m) {
+                const int u = w + NW * m;
+                if (u < CT) {
+                    f32x4 X[4];
+                    solve_tile(&sKhbT[16 * u * LDT], X);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            sW[(16 * i + 4 * lg + e) * LDK1 + 16 * u + lr] = from_f32<T>(X[i][e]);
+                } else if (u < CT + NVT) {
+                    const int vt = u - CT;
+                    f32x4 X[4];
+                    solve_tile(&sVbT[16 * vt * LDT], X);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        float x4[4] = {X[i][0], X[i][1], X[i][2], X[i][3]};
+                        st4(&gUtT[(16 * vt + lr) * C + 16 * i + 4 * lg], x4);
+                    }
+                }
+            }
+        }
+        __syncthreads();
+
+        // ---- W out, 16 bytes at a time --------------------------------------------
+        {
+            constexpr int PPR = K * (int)SZ / 16;
+#pragma unroll
+            for (int pc = tid; pc < C * PPR; pc += NT) {
+                const int row = pc / PPR, seg = pc % PPR;
+                *reinterpret_cast<uint4*>(&gW[row * K + seg * (16 / (int)SZ)]) =
+                    *reinterpret_cast<const uint4*>(&sW[row * LDK1 + seg * (16 / (int)SZ)]);
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// ============================================================================
+// State pass
+// ============================================================================
+template <typename T, int K, int NTW>
+struct StateLayout {
+    static constexpr int NW = 4;
+    static constexpr int VB = 16 * NW * NTW;
+    static constexpr int SZ = (int)sizeof(T);
+    static constexpr int PAD = 16 / SZ;
+    static constexpr int LDK2 = K + PAD;     // W, Qh rows
+    static constexpr int LDL = C + 4;        // Mqk rows
+    static constexpr int LDT = C + PAD;      // KbT, UtT rows
+    static constexpr int oW = 0;
+    static constexpr int oQh = oW + C * LDK2 * SZ;
+    static constexpr int oMqk = oQh + C * LDK2 * SZ;
+    static constexpr int oKbT = oMqk + C * LDL * SZ;
+    static constexpr int oUtT = oKbT + K * LDT * SZ;     // then: per-wave output staging
+    static constexpr int oEGC = oUtT + VB * LDT * SZ;
+    static constexpr int TOTAL = oEGC + K * 4;
+    static_assert(TOTAL <= 160 * 1024, "LDS budget exceeded");
+    static_assert(C * 16 * NTW <= 16 * NTW * LDT, "output staging must fit the wave's U~ rows");
+    // 16-byte pieces of one record the workgroup loads
+    static constexpr int PW = C * K * SZ / 16;           // W (and Qh)
+    static constexpr int PM = C * C * SZ / 16;           // Mqk
+    static constexpr int PK = K * C * SZ / 16;           // KbT
+    static constexpr int PU = VB * C * SZ / 16;          // U~ rows of the block
+    static constexpr int PE = K * 4 / 16;                // e^{G_C}
+    static constexpr int PTOT = 2 * PW + PM + PK + PU + PE;
+    static constexpr int NPT = (PTOT + 255) / 256;       // pieces per thread
+};
+
+template <typename T, int K, int NTW, bool SUMMARY>
+__global__ __launch_bounds__(256, (NTW == 1 && sizeof(T) == 2 ? 2 : 1)) void kda_state_kernel(StateParams p) {
+    using L = StateLayout<T, K, NTW>;
+    constexpr int NW = L::NW;
+    using Frag = typename FragOf<T>::type;
+    constexpr int VB = L::VB;
+    constexpr int LDK2 = L::LDK2, LDL = L::LDL, LDT = L::LDT;
+    constexpr int KS = K / 32, CT = K / 16;
+    constexpr unsigned SZ = sizeof(T);
+    constexpr int NPT = L::NPT;
+
+    __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
+    T* sW = reinterpret_cast<T*>(smem + L::oW);
+    T* sQh = reinterpret_cast<T*>(smem + L::oQh);
+    T* sMqk = reinterpret_cast<T*>(smem + L::oMqk);
+    T* sKbT = reinterpret_cast<T*>(smem + L::oKbT);
+    T* sUtT = reinterpret_cast<T*>(smem + L::oUtT);
+    float* sEGC = reinterpret_cast<float*>(smem + L::oEGC);
+
+    const int tid = threadIdx.x;
+    const int w = tid >> 6, l = tid & 63, lg = l >> 4, lr = l & 15;
+
+    const int G = gridDim.x;
+    const int x = blockIdx.x;
+    const int lid = ((G & 7) == 0) ? (x & 7) * (G >> 3) + (x >> 3) : x;
+    const int vb = lid % p.n_vb;
+    const int rest = lid / p.n_vb;
+    const int nseg_here = SUMMARY ? p.n_seg - 1 : p.n_seg;
+    const int seg = rest % nseg_here;
+    const int bh = rest / nseg_here;
+    const int b = bh / p.H, h = bh % p.H;
+    const int BH = p.B * p.H;
+    const int V = p.V;
+    const int c_begin = seg * p.cps;
+    const int c_end = min(c_begin + p.cps, p.NC);
+
+    const int col0 = vb * VB;
+    const bool pmode = SUMMARY && col0 < K;
+    const int vcol0 = SUMMARY ? (pmode ? 0 : col0 - K) : col0;
+    const int tile0 = NTW * w;
+
+    const RecLayout RL = rec_layout(K, V, (int)sizeof(T));
+    const unsigned char* rec0 = p.rec + (size_t)bh * p.NC * RL.bytes;
+
+    // ---- initial state --------------------------------------------------------
+    f32x4 S[NTW][CT];
+    {
+        const float* src = nullptr;
+        if (!SUMMARY) {
+            if (seg == 0) src = p.s0 ? p.s0 + (size_t)bh * K * V : nullptr;
+            else src = p.seg_init + ((size_t)(seg - 1) * BH + bh) * K * V;
+        }
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) {
+            const int col = col0 + 16 * (tile0 + j) + lr;
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int row = 16 * ct + 4 * lg + e;
+                    float v0 = 0.f;
+                    if (src) v0 = src[(size_t)row * V + col];
+                    else if (pmode) v0 = (row == col) ? 1.f : 0.f;
+                    S[j][ct][e] = v0;
+                }
+        }
+    }
+
+    // ---- record loads: 16-byte pieces into registers, one chunk ahead ------------
+    // piece index pc = tid + 256 m over [W | Qh | Mqk | KbT | U~ rows | e^{G_C}]
+    uint4 pre[NPT];
+    auto load_rec = [&](int ci) {
+        const unsigned char* rec = rec0 + (size_t)ci * RL.bytes;
+        const __amdgpu_buffer_rsrc_t rr = make_rsrc(rec);
+#pragma unroll
+        for (int m = 0; m < NPT; ++m) {
+            const int pc = tid + 256 * m;
+            unsigned off = 0;
+            bool ok = true;
+            if (pc < 2 * L::PW) {
+                off = (unsigned)RL.oW + (unsigned)pc * 16u;          // W and Qh are adjacent
+            } else if (pc < 2 * L::PW + L::PM) {
+                off = (unsigned)RL.oMqk + (unsigned)(pc - 2 * L::PW) * 16u;
+            } else if (pc < 2 * L::PW + L::PM + L::PK) {
+                off = (unsigned)RL.oKbT + (unsigned)(pc - 2 * L::PW - L::PM) * 16u;
+            } else if (pc < 2 * L::PW + L::PM + L::PK + L::PU) {
+                ok = !pmode;
+                off = (unsigned)RL.oUtT + (unsigned)vcol0 * C * SZ +
+                      (unsigned)(pc - 2 * L::PW - L::PM - L::PK) * 16u;
+            } else if (pc < L::PTOT) {
+                off = (unsigned)RL.oEgc + (unsigned)(pc - 2 * L::PW - L::PM - L::PK - L::PU) * 16u;
+            } else {
+                ok = false;
+            }
+            pre[m] = ok ? buf_load16(rr, off) : make_uint4(0, 0, 0, 0);
+        }
+    };
+    auto store_rec = [&]() {
+#pragma unroll
+        for (int m = 0; m < NPT; ++m) {
+            const int pc = tid + 256 * m;
+            unsigned char* dst = nullptr;
+            if (pc < 2 * L::PW) {
+                constexpr int PR = K * (int)SZ / 16;                    // pieces per row
+                const int q = pc % L::PW, row = q / PR, cs = q % PR;
+                dst = smem + (pc < L::PW ? L::oW : L::oQh) + row * LDK2 * SZ + cs * 16;
+            } else if (pc < 2 * L::PW + L::PM) {
+                constexpr int PR = C * (int)SZ / 16;
+                const int q = pc - 2 * L::PW, row = q / PR, cs = q % PR;
+                dst = smem + L::oMqk + row * LDL * SZ + cs * 16;
+            } else if (pc < 2 * L::PW + L::PM + L::PK) {
+                constexpr int PR = C * (int)SZ / 16;
+                const int q = pc - 2 * L::PW - L::PM, row = q / PR, cs = q % PR;
+                dst = smem + L::oKbT + row * LDT * SZ + cs * 16;
+            } else if (pc < 2 * L::PW + L::PM + L::PK + L::PU) {
+                constexpr int PR = C * (int)SZ / 16;
+                const int q = pc - 2 * L::PW - L::PM - L::PK, row = q / PR, cs = q % PR;
+                dst = smem + L::oUtT + row * LDT * SZ + cs * 16;
+            } else if (pc < L::PTOT) {
+                const int q = pc - 2 * L::PW - L::PM - L::PK - L::PU;
+                dst = smem + L::oEGC + q * 16;
+            }
+            if (dst) *reinterpret_cast<uint4*>(dst) = pre[m];
+        }
+    };
+    if (c_begin < c_end) load_rec(c_begin);
+
+    const unsigned rowV = (unsigned)p.H * V * SZ;
+    for (int ci = c_begin; ci < c_end; ++ci) {
+        const int t0 = ci * C;
+        const int nt = min(C, p.T - t0);
+        store_rec();
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+        if (ci + 1 < c_end) load_rec(ci + 1);
+        __builtin_amdgcn_sched_barrier(0);
+
+        Frag Sb[NTW][KS];
+#pragma unroll
+        for (int j = 0; j < NTW; ++j)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) Sb[j][ks] = frag_from_tiles<T>(S[j][2 * ks], S[j][2 * ks + 1]);
+        // U = U~ - W S
+        f32x4 U[NTW][4];
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti) {
+            f32x4 acc[NTW];
+#pragma unroll
+            for (int j = 0; j < NTW; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const Frag a = ld_frag_perm<T>(&sW[(16 * ti + lr) * LDK2 + 32 * ks + 4 * lg]);
+#pragma unroll
+                for (int j = 0; j < NTW; ++j) acc[j] = mma(acc[j], a, Sb[j][ks]);
+            }
+#pragma unroll
+            for (int j = 0; j < NTW; ++j) {
+                const f32x4 ut = pmode ? f32x4{0.f, 0.f, 0.f, 0.f}
+                                       : ld4_as_f32<T>(&sUtT[(16 * (tile0 + j) + lr) * LDT + 16 * ti + 4 * lg]);
+                U[j][ti] = ut - acc[j];
+            }
+        }
+        Frag Ub[NTW][2];
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) {
+            Ub[j][0] = frag_from_tiles<T>(U[j][0], U[j][1]);
+            Ub[j][1] = frag_from_tiles<T>(U[j][2], U[j][3]);
+        }
+        if (!SUMMARY) {
+            // output block of this wave staged in its own (consumed) U~ rows
+            constexpr int OW = 16 * NTW;
+            T* sO = sUtT + 16 * tile0 * LDT;
+            wave_lds_sync();
+#pragma unroll
+            for (int ti = 0; ti < 4; ++ti) {
+                f32x4 acc[NTW];
+#pragma unroll
+                for (int j = 0; j < NTW; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const Frag a = ld_frag_perm<T>(&sQh[(16 * ti + lr) * LDK2 + 32 * ks + 4 * lg]);
+#pragma unroll
+                    for (int j = 0; j < NTW; ++j) acc[j] = mma(acc[j], a, Sb[j][ks]);
+                }
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    if (ks <= (ti >> 1)) {
+                        const Frag a = ld_frag_perm<T>(&sMqk[(16 * ti + lr) * LDL + 32 * ks + 4 * lg]);
+#pragma unroll
+                        for (int j = 0; j < NTW; ++j) acc[j] = mma(acc[j], a, Ub[j][ks]);
+                    }
+                }
+#pragma unroll
+                for (int j = 0; j < NTW; ++j)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) sO[(16 * ti + 4 * lg + e) * OW + 16 * j + lr] = from_f32<T>(acc[j][e]);
+            }
+            wave_lds_sync();
+            constexpr int PPR = OW * (int)SZ / 16;
+            const __amdgpu_buffer_rsrc_t ro = make_rsrc(
+                reinterpret_cast<T*>(p.o) + ((size_t)(b * (size_t)p.T + t0) * p.H + h) * V + vcol0 + OW * w);
+#pragma unroll
+            for (int pc = l; pc < C * PPR; pc += 64) {
+                const int row = pc / PPR, sg = pc % PPR;
+                if (row < nt)
+                    buf_store16(ro, (unsigned)row * rowV + (unsigned)sg * 16u, 0u,
+                                *reinterpret_cast<const uint4*>(&sO[row * OW + sg * (16 / (int)SZ)]));
+            }
+        }
+        // S <- Diag(e^{G_C}) S + (K e^{G_C - G})^T U
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+            const f32x4 eg = *reinterpret_cast<const f32x4*>(&sEGC[16 * ct + 4 * lg]);
+#pragma unroll
+            for (int j = 0; j < NTW; ++j) S[j][ct] = S[j][ct] * eg;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const Frag a = ld_frag_perm<T>(&sKbT[(16 * ct + lr) * LDT + 32 * ks + 4 * lg]);
+#pragma unroll
+                for (int j = 0; j < NTW; ++j) S[j][ct] = mma(S[j][ct], a, Ub[j][ks]);
+            }
+        }
+        __syncthreads();
+    }
+
+    float* dst = nullptr;
+    size_t ld = V;
+    if (!SUMMARY) {
+        if (seg == p.n_seg - 1 && p.sT) dst = p.sT + (size_t)bh * K * V;
+    } else if (pmode) {
+        dst = p.wsP + ((size_t)seg * BH + bh) * K * K;
+        ld = K;
+    } else {
+        dst = p.wsL + ((size_t)seg * BH + bh) * K * V;
+    }
+    if (dst) {
+#pragma unroll
+        for (int j = 0; j < NTW; ++j) {
+            const int my_col = col0 + 16 * (tile0 + j) + lr;
+            const int col = SUMMARY ? (pmode ? my_col : my_col - K) : my_col;
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dst[(size_t)(16 * ct + 4 * lg + e) * ld + col] = S[j][ct][e];
+        }
+    }
+}
+
+// ---- launchers ---------------------------------------------------------------------
+bool split_variant_exists(int dtype, int K, int V, int VB) {
+    const bool kv = (K == 64 || K == 128) && (V == 64 || V == 128);
+    if (dtype == 1) return kv && (VB == 64 || VB == 128) && VB <= V;
+    if (dtype == 0) return K == 64 && V == 64 && VB == 64;
+    return false;
+}
+
+template <typename T, int K, int V>
+static hipError_t launch_intra_t(const IntraParams& p, int grid, hipStream_t stream) {
+    hipLaunchKernelGGL((kda_intra_kernel<T, K, V>), dim3(grid), dim3(512), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_intra(int dtype, int K, int V, const IntraParams& p, int grid, hipStream_t stream) {
+    if (grid <= 0) return hipSuccess;
+    if (dtype == 1) {
+        if (K == 128 && V == 128) return launch_intra_t<bf16, 128, 128>(p, grid, stream);
+        if (K == 128 && V == 64) return launch_intra_t<bf16, 128, 64>(p, grid, stream);
+        if (K == 64 && V == 128) return launch_intra_t<bf16, 64, 128>(p, grid, stream);
+        if (K == 64 && V == 64) return launch_intra_t<bf16, 64, 64>(p, grid, stream);
+    } else if (dtype == 0) {
+        if (K == 64 && V == 64) return launch_intra_t<float, 64, 64>(p, grid, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <typename T, int K, int NTW>
+static hipError_t launch_state_t(const StateParams& p, int grid, hipStream_t stream) {
+    if (p.summary)
+        hipLaunchKernelGGL((kda_state_kernel<T, K, NTW, true>), dim3(grid), dim3(256), 0, stream, p);
+    else
+        hipLaunchKernelGGL((kda_state_kernel<T, K, NTW, false>), dim3(grid), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_state(int dtype, int K, int VB, const StateParams& p, int grid, hipStream_t stream) {
+    if (grid <= 0) return hipSuccess;
+    if (dtype == 1) {
+        if (K == 128 && VB == 128) return launch_state_t<bf16, 128, 2>(p, grid, stream);
+        if (K == 128 && VB == 64) return launch_state_t<bf16, 128, 1>(p, grid, stream);
+        if (K == 64 && VB == 128) return launch_state_t<bf16, 64, 2>(p, grid, stream);
+        if (K == 64 && VB == 64) return launch_state_t<bf16, 64, 1>(p, grid, stream);
+    } else if (dtype == 0) {
+        if (K == 64 && VB == 64) return launch_state_t<float, 64, 1>(p, grid, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace kda

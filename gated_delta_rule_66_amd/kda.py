@@ -41,7 +41,7 @@ class KDAError(RuntimeError):
 
 
 class Plan(ctypes.Structure):
-    _fields_ = [("n_seg", ctypes.c_int), ("v_block", ctypes.c_int)]
+    _fields_ = [("n_seg", ctypes.c_int), ("v_block", ctypes.c_int), ("split", ctypes.c_int)]
 
 
 _lib = None
@@ -119,12 +119,15 @@ def _stream_ptr(device: torch.device):
 
 
 def _plan_arg(plan) -> Optional[Plan]:
+    """None, a Plan, or a tuple (n_seg, v_block[, split]); 0 = library's choice."""
     if plan is None:
         return None
     if isinstance(plan, Plan):
         return plan
-    n_seg, v_block = plan
-    return Plan(int(n_seg), int(v_block))
+    vals = [int(x) for x in plan]
+    if len(vals) not in (2, 3):
+        raise ValueError("plan is (n_seg, v_block[, split])")
+    return Plan(vals[0], vals[1], vals[2] if len(vals) == 3 else 0)
 
 
 def _check(t: torch.Tensor, name: str, shape, dtype, device):
@@ -138,13 +141,13 @@ def _check(t: torch.Tensor, name: str, shape, dtype, device):
         raise ValueError("%s must be contiguous" % name)
 
 
-def chunk_plan(B: int, T: int, H: int, K: int, V: int, dtype: torch.dtype) -> Tuple[int, int]:
-    """(n_seg, v_block) the library picks for these sizes on the current device."""
+def chunk_plan(B: int, T: int, H: int, K: int, V: int, dtype: torch.dtype) -> Tuple[int, int, int]:
+    """(n_seg, v_block, split) the library picks for these sizes on the current device."""
     pl = Plan()
     st = load_library().kda_chunk_fwd_plan(B, T, H, K, V, _dtype_code(dtype), ctypes.byref(pl))
     if st != KDA_OK:
         raise KDAError(st, "kda_chunk_fwd_plan")
-    return pl.n_seg, pl.v_block
+    return pl.n_seg, pl.v_block, pl.split
 
 
 def chunk_workspace_size(B: int, T: int, H: int, K: int, V: int, dtype: torch.dtype, plan=None) -> int:

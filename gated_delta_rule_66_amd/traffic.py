@@ -42,6 +42,10 @@ def launch_name(kernel_name: str):
     if "kda_chunk_kernel" in n:
         # template flag SUMMARY is the last template argument
         return "chunk_summary" if ("true>" in n or "Lb1E" in n) else "chunk_output"
+    if "kda_intra_kernel" in n:
+        return "intra_chunk"
+    if "kda_state_kernel" in n:
+        return "state_summary" if ("true>" in n or "Lb1E" in n) else "state_output"
     if "kda_scan_kernel" in n:
         return "segment_scan"
     if "kda_decode_kernel" in n:

@@ -66,16 +66,23 @@ typedef enum kda_dtype {
 } kda_dtype;
 
 /*
- * Execution plan of a prefill call.  n_seg: number of sequence segments
- * evaluated side by side on one card (1 = plain chunk pass; > 1 adds the
- * segment summary and segment scan passes).  v_block: value columns per
- * workgroup (64 or 128; at most V, and with n_seg > 1 it must divide K).
- * Either field 0 means "let the library choose".
- * Any valid plan gives the same result up to fp32/bf16 rounding.
+ * Execution plan of a prefill call.
+ *   split:   1 = single pass: one kernel per (b, h, segment, column block)
+ *            walks the chunks and does all chunk work in order;
+ *            2 = two passes: an intra-chunk pass over every (b, h, chunk) at
+ *            once writes per-chunk operands to the workspace, then a state
+ *            pass walks the chunks (the workspace holds those records).
+ *   n_seg:   number of sequence segments evaluated side by side on one card
+ *            (1 = none; > 1 adds the segment summary and segment scan passes).
+ *   v_block: value columns per workgroup of the state-carrying pass (64 or
+ *            128; at most V, and with n_seg > 1 it must divide K).
+ * Any field 0 means "let the library choose".  Any valid plan gives the same
+ * result up to fp32/bf16 rounding.
  */
 typedef struct kda_plan {
     int n_seg;
     int v_block;
+    int split;
 } kda_plan;
 
 /* Sizes supported by the kernels: K, V in {64, 128}; bf16 or fp32 inputs
@@ -92,9 +99,11 @@ kda_status kda_chunk_fwd_plan(int B, int T, int H, int K, int V, kda_dtype dt,
 
 /*
  * Bytes of device workspace kda_chunk_fwd needs for these sizes and plan
- * (plan NULL or fields 0: the library's choice on the current device).
- * 0 when no workspace is needed (n_seg = 1); (size_t)-1 for invalid or
- * unsupported arguments.
+ * (plan NULL or fields 0: the library's choice on the current device):
+ * with split = 2 one record per (b, h, chunk) (for K = V = 128 bf16, 72.5 KiB),
+ * with n_seg > 1 the segment transitions and local states
+ * ((n_seg - 1) * B * H * K * (K + V) fp32) plus B * H * K * V fp32.
+ * 0 when none is needed; (size_t)-1 for invalid or unsupported arguments.
  */
 size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int K, int V, kda_dtype dt,
                                     const kda_plan* plan);
@@ -147,8 +156,9 @@ kda_status kda_recurrent_step(int N, int H, int K, int V, kda_dtype dt,
  * kda_recurrent_step (up to max_launches of them) is bracketed by two HIP
  * events recorded on its own stream; launches beyond that are not timed.
  * kda_profile_stop waits for the recorded events, writes up to `cap` launch
- * names (static strings: "chunk_output", "chunk_summary", "segment_scan",
- * "copy_state", "decode_step") and durations in milliseconds, releases the
+ * names (static strings: "intra_chunk", "state_output", "state_summary",
+ * "chunk_output", "chunk_summary", "segment_scan", "copy_state",
+ * "decode_step") and durations in milliseconds, releases the
  * events, and returns the number of timed launches (-1: profiling was not
  * started or a HIP event query failed).  The recording state is process-wide
  * and not thread-safe; profiling is off unless started.

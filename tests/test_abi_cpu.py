@@ -92,14 +92,18 @@ def test_prefill_rejects_partially_overlapping_states():
 
 def test_prefill_workspace_check_with_explicit_plan():
     lib = _lib()
-    plan = K_.Plan(4, 64)
-    need = lib.kda_chunk_fwd_workspace_size(1, 64 * 40, 2, 128, 128, BF16, ctypes.byref(plan))
-    # (n_seg - 1) * B*H * K*(K+V) + B*H*K*V fp32 words
-    assert need == (3 * 2 * 128 * 256 + 2 * 128 * 128) * 4
-    assert _fwd(lib, T=64 * 40, H=2, plan=plan, ws=None) == WORKSPACE
-    assert _fwd(lib, T=64 * 40, H=2, plan=plan, ws=FAKE, ws_bytes=need - 1) == WORKSPACE
-    one = K_.Plan(1, 128)
-    assert lib.kda_chunk_fwd_workspace_size(1, 64 * 40, 2, 128, 128, BF16, ctypes.byref(one)) == 0
+    T, H = 64 * 40, 2
+    seg = (3 * 2 * 128 * 256 + 2 * 128 * 128) * 4     # (n_seg-1) B H K (K+V) + B H K V fp32 words
+    # one record per (b, h, chunk): W, Qh [64 x 128], Mqk [64 x 64], KbT, UtT [128 x 64] bf16, e^{G_C} fp32
+    rec = 2 * (64 * 128 * 2 + 64 * 64 + 2 * 128 * 64) + 128 * 4
+    assert rec % 256 == 0
+    for plan, need_expected in ((K_.Plan(4, 64, 1), seg), (K_.Plan(4, 64, 2), seg + H * 40 * rec),
+                                (K_.Plan(1, 64, 2), H * 40 * rec), (K_.Plan(1, 128, 1), 0)):
+        need = lib.kda_chunk_fwd_workspace_size(1, T, H, 128, 128, BF16, ctypes.byref(plan))
+        assert need == need_expected, (plan.n_seg, plan.v_block, plan.split)
+        if need:
+            assert _fwd(lib, T=T, H=H, plan=plan, ws=None) == WORKSPACE
+            assert _fwd(lib, T=T, H=H, plan=plan, ws=FAKE, ws_bytes=need - 1) == WORKSPACE
 
 
 def test_prefill_rejects_bad_plans():
@@ -109,6 +113,8 @@ def test_prefill_rejects_bad_plans():
     assert _fwd(lib, K=64, V=64, plan=K_.Plan(1, 128)) == UNSUPPORTED
     # a segmented plan needs value blocks that tile the K transition columns
     assert _fwd(lib, T=64 * 40, K=64, V=128, plan=K_.Plan(2, 128), ws=FAKE, ws_bytes=1 << 30) == UNSUPPORTED
+    assert _fwd(lib, plan=K_.Plan(1, 64, 3)) == INVALID
+    assert _fwd(lib, plan=K_.Plan(1, 64, -1)) == INVALID
     bad = K_.Plan(1, 96)
     assert lib.kda_chunk_fwd_workspace_size(1, 64, 1, 128, 128, BF16, ctypes.byref(bad)) == ctypes.c_size_t(-1).value
 

@@ -31,18 +31,26 @@ def run_oracle(d):
     return oracle.oracle_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"])
 
 
-def gpu_fwd(x, plan=None, s0="use", **kw):
+def gpu_fwd(x, plan=None, s0="use", split=0, **kw):
+    """Prefill through the C ABI; split 1 = single-pass kernel, 2 = intra-chunk
+    pass + state pass, 0 = the library's choice."""
     init = x["s0"] if s0 == "use" else s0
+    if split:
+        plan = (0, 0, split) if plan is None else (plan[0], plan[1], split)
     return chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], init, True, plan, **kw)
 
 
+PATHS = [1, 2]
+
+
 # ------------------------------------------------------------------ small cases
-def test_config0_full_parity():
+@pytest.mark.parametrize("split", PATHS)
+def test_config0_full_parity(split):
     cfg = CONFIGS["c0"]
-    say("c0 full: B=1 H=2 T=256 K=V=64 fp32")
+    say("c0 full: B=1 H=2 T=256 K=V=64 fp32 split=%d" % split)
     d = make_prefill_config(cfg, "cpu")
     x = to_dev(d)
-    o, sT = gpu_fwd(x)
+    o, sT = gpu_fwd(x, split=split)
     torch.cuda.synchronize()
     o_ref, s_ref = run_oracle(d)
     assert o_err(o, o_ref) < TOL[torch.float32]
@@ -70,12 +78,13 @@ SHAPES = [
 ]
 
 
+@pytest.mark.parametrize("split", PATHS)
 @pytest.mark.parametrize("K,V,T,B,H,with_s0,plan", SHAPES)
-def test_prefill_bf16_shapes(K, V, T, B, H, with_s0, plan):
-    say("bf16 prefill K=%d V=%d T=%d B=%d H=%d s0=%s plan=%s" % (K, V, T, B, H, with_s0, plan))
+def test_prefill_bf16_shapes(K, V, T, B, H, with_s0, plan, split):
+    say("bf16 prefill K=%d V=%d T=%d B=%d H=%d s0=%s plan=%s split=%d" % (K, V, T, B, H, with_s0, plan, split))
     d = make_prefill(B, T, H, K, V, torch.bfloat16, seed=100 + T, s0_std=0.02 if with_s0 else None)
     x = to_dev(d)
-    o, sT = gpu_fwd(x, plan)
+    o, sT = gpu_fwd(x, plan, split=split)
     torch.cuda.synchronize()
     o_ref, s_ref = run_oracle(d)
     assert o_err(o, o_ref) < TOL[torch.bfloat16]
@@ -85,24 +94,25 @@ def test_prefill_bf16_shapes(K, V, T, B, H, with_s0, plan):
 @pytest.mark.parametrize("dtype,K,V", [(torch.bfloat16, 128, 128), (torch.bfloat16, 64, 64),
                                        (torch.float32, 64, 64)])
 @pytest.mark.parametrize("n_seg", [2, 3, 7])
-def test_segment_planner_matches_oracle(dtype, K, V, n_seg):
+@pytest.mark.parametrize("split", PATHS)
+def test_segment_planner_matches_oracle(dtype, K, V, n_seg, split):
     """Segment transitions computed side by side and recombined: the result
     must not depend on the number of segments (page section on the one-card
     segment planner)."""
     T = 64 * 37 + 5
-    say("segments dtype=%s K=%d V=%d n_seg=%d T=%d" % (dtype, K, V, n_seg, T))
+    say("segments dtype=%s K=%d V=%d n_seg=%d T=%d split=%d" % (dtype, K, V, n_seg, T, split))
     d = make_prefill(1, T, 2, K, V, dtype, seed=7, s0_std=0.02)
     x = to_dev(d)
     o_ref, s_ref = run_oracle(d)
     for vb in sorted({64, min(128, K, V)}):
-        o, sT = gpu_fwd(x, (n_seg, vb))
+        o, sT = gpu_fwd(x, (n_seg, vb), split=split)
         torch.cuda.synchronize()
         assert o_err(o, o_ref) < TOL[dtype], vb
         assert s_err(sT, s_ref) < TOL[dtype], vb
 
 
 # ------------------------------------------------------------------ pins on the GPU
-@pytest.mark.parametrize("plan", [(1, 64), (1, 128), (3, 64)])
+@pytest.mark.parametrize("plan", [(1, 64, 1), (1, 128, 1), (3, 64, 1), (1, 64, 2), (1, 128, 2), (3, 64, 2)])
 def test_p1_no_forget_no_write(plan):
     say("P1 alpha=1 beta=0 plan=%s" % (plan,))
     d = make_prefill(1, 300, 2, 128, 128, torch.bfloat16, seed=11, s0_std=1.0)
@@ -116,9 +126,10 @@ def test_p1_no_forget_no_write(plan):
     assert o_err(o, o_ref) < TOL[torch.bfloat16]
 
 
+@pytest.mark.parametrize("split", PATHS)
 @pytest.mark.parametrize("dtype,K", [(torch.bfloat16, 128), (torch.float32, 64)])
-def test_p2_full_write_unit_key(dtype, K):
-    say("P2 alpha=1 beta=1 basis keys dtype=%s" % dtype)
+def test_p2_full_write_unit_key(dtype, K, split):
+    say("P2 alpha=1 beta=1 basis keys dtype=%s split=%d" % (dtype, split))
     T, H = 200, 2
     gen = torch.Generator().manual_seed(12)
     idx = torch.randint(0, K, (1, T, H), generator=gen)
@@ -127,19 +138,20 @@ def test_p2_full_write_unit_key(dtype, K):
     d = dict(q=k.clone(), k=k, v=v, g=torch.zeros_like(k), beta=torch.ones(1, T, H, dtype=dtype),
              s0=torch.randn(1, H, K, K, generator=gen))
     x = to_dev(d)
-    o, _ = gpu_fwd(x)
+    o, _ = gpu_fwd(x, split=split)
     torch.cuda.synchronize()
     assert o_err(o, v) < TOL[dtype]
 
 
-def test_p3_clamp_bitwise():
-    say("P3 clamp: g=-50 == g=-5, g=+3 == g=0, bitwise")
+@pytest.mark.parametrize("split", PATHS)
+def test_p3_clamp_bitwise(split):
+    say("P3 clamp: g=-50 == g=-5, g=+3 == g=0, bitwise; split=%d" % split)
     d = make_prefill(2, 257, 2, 128, 128, torch.bfloat16, seed=13, s0_std=0.02)
     x = to_dev(d)
     outs = []
     for val in (-5.0, -50.0, 0.0, 3.0):
         x["g"].fill_(val)
-        outs.append(gpu_fwd(x))
+        outs.append(gpu_fwd(x, split=split))
     torch.cuda.synchronize()
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
     assert torch.equal(outs[2][0], outs[3][0]) and torch.equal(outs[2][1], outs[3][1])
@@ -149,7 +161,7 @@ def test_p3_clamp_bitwise():
     g[..., 1::2] = -5.0
     d["g"] = g.to(torch.bfloat16)
     x = to_dev(d)
-    o, sT = gpu_fwd(x)
+    o, sT = gpu_fwd(x, split=split)
     torch.cuda.synchronize()
     assert torch.isfinite(o.float()).all() and torch.isfinite(sT).all()
     o_ref, s_ref = run_oracle(d)
@@ -157,12 +169,13 @@ def test_p3_clamp_bitwise():
     assert s_err(sT, s_ref) < TOL[torch.bfloat16]
 
 
+@pytest.mark.parametrize("split", PATHS)
 @pytest.mark.parametrize("T", [1, 2, 3, 5, 8])
-def test_p5_dense_expansion_short(T):
-    say("P5 dense transition expansion T=%d" % T)
+def test_p5_dense_expansion_short(T, split):
+    say("P5 dense transition expansion T=%d split=%d" % (T, split))
     d = make_prefill(1, T, 1, 64, 64, torch.float32, seed=20 + T, s0_std=0.5)
     x = to_dev(d)
-    o, sT = gpu_fwd(x)
+    o, sT = gpu_fwd(x, split=split)
     torch.cuda.synchronize()
     od, sd = dense_f64_chain(d["q"][0, :, 0].numpy(), d["k"][0, :, 0].numpy(), d["v"][0, :, 0].numpy(),
                              d["g"][0, :, 0].numpy(), d["beta"][0, :, 0].numpy(), d["s0"][0, 0].numpy())
@@ -170,7 +183,7 @@ def test_p5_dense_expansion_short(T):
     assert s_err(sT, sd[None, None]) < TOL[torch.float32]
 
 
-@pytest.mark.parametrize("plan", [None, (2, 64)])
+@pytest.mark.parametrize("plan", [None, (2, 64), (0, 0, 1), (2, 64, 1)])
 def test_p6_split_and_resume(plan):
     say("P6 split/resume plan=%s" % (plan,))
     T1, T2 = 700, 555
@@ -189,15 +202,16 @@ def test_p6_split_and_resume(plan):
     assert s_err(s_full, s_ref) < TOL[torch.bfloat16]
 
 
-def test_p7_linearity():
-    say("P7 linear in (S0, V)")
+@pytest.mark.parametrize("split", PATHS)
+def test_p7_linearity(split):
+    say("P7 linear in (S0, V) split=%d" % split)
     d = make_prefill(1, 333, 2, 128, 128, torch.bfloat16, seed=15, s0_std=0.05)
     x = to_dev(d)
-    o, s = gpu_fwd(x)
+    o, s = gpu_fwd(x, split=split)
     xa = dict(x)
     xa["v"] = torch.zeros_like(x["v"])
-    oa, sa = gpu_fwd(xa)
-    ob, sb = gpu_fwd(x, s0=None)
+    oa, sa = gpu_fwd(xa, split=split)
+    ob, sb = gpu_fwd(x, s0=None, split=split)
     torch.cuda.synchronize()
     assert o_err(oa.float() + ob.float(), o.float()) < TOL[torch.bfloat16]
     assert s_err(sa + sb, s) < TOL[torch.bfloat16]
@@ -232,7 +246,7 @@ def test_p8_prefill_then_decode_equals_longer_prefill():
     assert s_err(s_p, st) < TOL[torch.bfloat16]
 
 
-@pytest.mark.parametrize("plan", [(1, 64), (4, 64)])
+@pytest.mark.parametrize("plan", [(1, 64, 1), (4, 64, 1), (1, 64, 2), (4, 64, 2)])
 def test_in_place_state_resume(plan):
     say("final_state aliasing initial_state plan=%s" % (plan,))
     d = make_prefill(1, 64 * 20 + 9, 2, 128, 128, torch.bfloat16, seed=17, s0_std=0.02)
@@ -263,7 +277,7 @@ def test_deterministic_repeat():
     say("bitwise repeatability")
     d = make_prefill(1, 64 * 30, 4, 128, 128, torch.bfloat16, seed=19, s0_std=0.02)
     x = to_dev(d)
-    for plan in ((1, 64), (3, 128)):
+    for plan in ((1, 64, 1), (3, 128, 1), (1, 64, 2), (3, 128, 2)):
         a = gpu_fwd(x, plan)
         b = gpu_fwd(x, plan)
         torch.cuda.synchronize()
@@ -275,13 +289,17 @@ def test_launch_profiling_names_every_launch():
     import gated_delta_rule_66_amd as kda
     d = make_prefill(1, 64 * 12, 2, 128, 128, torch.bfloat16, seed=23)
     x = to_dev(d)
-    ws = torch.empty(kda.chunk_workspace_size(1, 64 * 12, 2, 128, 128, torch.bfloat16, (3, 64)),
+    ws = torch.empty(kda.chunk_workspace_size(1, 64 * 12, 2, 128, 128, torch.bfloat16, (3, 64, 2)),
                      dtype=torch.uint8, device=DEV)
     kda.profile_start(16)
-    gpu_fwd(x, (1, 64))
-    gpu_fwd(x, (3, 64), workspace=ws)
+    gpu_fwd(x, (1, 64, 1))
+    gpu_fwd(x, (3, 64, 1), workspace=ws)
+    gpu_fwd(x, (1, 64, 2), workspace=ws)
+    gpu_fwd(x, (3, 64, 2), workspace=ws)
     rec = kda.profile_stop(16)
-    assert [n for n, _ in rec] == ["chunk_output", "chunk_summary", "segment_scan", "chunk_output"]
+    assert [n for n, _ in rec] == ["chunk_output", "chunk_summary", "segment_scan", "chunk_output",
+                                   "intra_chunk", "state_output",
+                                   "intra_chunk", "state_summary", "segment_scan", "state_output"]
     assert all(ms > 0 for _, ms in rec)
     o, _ = gpu_fwd(x, (1, 64))                 # timing is off again: results unchanged
     ref, _ = run_oracle(d)
@@ -325,15 +343,20 @@ def _sampled_oracle(x, chains):
     return outs
 
 
-@pytest.mark.parametrize("name,chains", [("c1", [(0, 0), (0, 7), (0, 19), (0, 31)]),
-                                         ("c2", [(0, 3), (5, 17), (7, 31)]),
-                                         ("c3", [(0, 11)])])
-def test_full_size_prefill_sampled(name, chains):
+@pytest.mark.parametrize("name,chains,split", [("c1", [(0, 0), (0, 7), (0, 19), (0, 31)], 0),
+                                               ("c1", [(0, 3), (0, 30)], 1),
+                                               ("c2", [(0, 3), (5, 17), (7, 31)], 0),
+                                               ("c3", [(0, 11)], 0)])
+def test_full_size_prefill_sampled(name, chains, split):
+    """Full-size workloads in the launch configuration bench.py times (the
+    library's plan), checked against the oracle on sampled (b, h) chains."""
     cfg = CONFIGS[name]
-    plan = chunk_plan(cfg.B, cfg.T, cfg.H, cfg.K, cfg.V, cfg.dtype)
-    say("full %s B=%d T=%d H=%d plan=%s, oracle on chains %s" % (name, cfg.B, cfg.T, cfg.H, plan, chains))
+    plan = (0, 0, split)
+    say("full %s B=%d T=%d H=%d plan=%s, oracle on chains %s" %
+        (name, cfg.B, cfg.T, cfg.H, chunk_plan(cfg.B, cfg.T, cfg.H, cfg.K, cfg.V, cfg.dtype) if not split
+         else plan, chains))
     x = make_prefill_config(cfg, DEV)
-    o, sT = chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], True, None)
+    o, sT = chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], True, plan)
     torch.cuda.synchronize()
     assert torch.isfinite(sT).all()
     refs = _sampled_oracle(x, chains)
