@@ -629,41 +629,72 @@ __global__ __launch_bounds__(256) void kda_chunk_kernel(ChunkParams p) {
 }
 
 // Segment scan: S_{j+1} = P_j S_j + L_j, written over L_j, per (b, h) and
-// 16-column block; fp32.
+// 16-column block, on fp32 MFMA (16x16x4).  Wave w owns row tiles
+// [TPW w, TPW w + TPW); MFMA step ks reduces over the state rows
+// {(K/4) g + ks : g = 0..3} (lane group g supplies one of them), so every lane
+// reads K/4 consecutive elements of its P row.  The next segment's P rows and
+// L tiles are loaded while the current one is applied.
 template <int K>
 __global__ __launch_bounds__(256) void kda_scan_kernel(ScanParams p) {
-    constexpr int TPR = 256 / K;        // threads per state row
-    constexpr int CPT = 16 / TPR;       // columns per thread
-    __shared__ float sS[K * 16];
+    constexpr int RT = K / 16;          // row tiles
+    constexpr int TPW = RT / 4;         // row tiles per wave
+    constexpr int KQ = K / 4;           // reduction steps
+    constexpr int LD = 17;
+    __shared__ float sS[K * LD];
     const int ncb = p.V / 16;
     const int bh = blockIdx.x / ncb, cb = blockIdx.x % ncb;
     const int tid = threadIdx.x;
-    const int row = tid / TPR, n0 = (tid % TPR) * CPT;
+    const int w = tid >> 6, l = tid & 63, lg = l >> 4, lr = l & 15;
     const int V = p.V;
-    const size_t col = (size_t)cb * 16 + n0;
+    const size_t col = (size_t)cb * 16 + lr;
+    for (int i = tid; i < K * 16; i += 256) {
+        const int row = i / 16, c = i % 16;
+        sS[row * LD + c] = p.s0 ? p.s0[((size_t)bh * K + row) * V + (size_t)cb * 16 + c] : 0.f;
+    }
+    float a[TPW][KQ];
+    f32x4 lt[TPW];
+    auto load_seg = [&](int j) {
+        const float* P = p.wsP + ((size_t)j * p.BH + bh) * K * K;
+        const float* Lj = p.wsL + ((size_t)j * p.BH + bh) * K * V;
 #pragma unroll
-    for (int i = 0; i < CPT; ++i)
-        sS[row * 16 + n0 + i] = p.s0 ? p.s0[((size_t)bh * K + row) * V + col + i] : 0.f;
+        for (int t = 0; t < TPW; ++t) {
+            const int rt = TPW * w + t;
+            const float* prow = P + (size_t)(16 * rt + lr) * K + KQ * lg;
+#pragma unroll
+            for (int q4 = 0; q4 < KQ / 4; ++q4) {
+                const float4 v4 = *reinterpret_cast<const float4*>(prow + 4 * q4);
+                a[t][4 * q4] = v4.x;
+                a[t][4 * q4 + 1] = v4.y;
+                a[t][4 * q4 + 2] = v4.z;
+                a[t][4 * q4 + 3] = v4.w;
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) lt[t][e] = Lj[(size_t)(16 * rt + 4 * lg + e) * V + col];
+        }
+    };
+    if (p.n_seg > 1) load_seg(0);
     __syncthreads();
     for (int j = 0; j + 1 < p.n_seg; ++j) {
-        const float* P = p.wsP + ((size_t)j * p.BH + bh) * K * K;
-        float* Lj = p.wsL + ((size_t)j * p.BH + bh) * K * V;
-        float acc[CPT];
+        f32x4 acc[TPW];
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) acc[i] = Lj[(size_t)row * V + col + i];
-        for (int m = 0; m < K; m += 4) {
-            const float4 pm = *reinterpret_cast<const float4*>(P + (size_t)row * K + m);
-            const float pv[4] = {pm.x, pm.y, pm.z, pm.w};
+        for (int t = 0; t < TPW; ++t) {
+            acc[t] = lt[t];
 #pragma unroll
-            for (int mm = 0; mm < 4; ++mm)
-#pragma unroll
-                for (int i = 0; i < CPT; ++i) acc[i] += pv[mm] * sS[(m + mm) * 16 + n0 + i];
+            for (int ks = 0; ks < KQ; ++ks)
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t][ks], sS[(KQ * lg + ks) * LD + lr], acc[t], 0, 0, 0);
         }
+        if (j + 2 < p.n_seg) load_seg(j + 1);
+        float* Lj = p.wsL + ((size_t)j * p.BH + bh) * K * V;
         __syncthreads();
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            sS[row * 16 + n0 + i] = acc[i];
-            Lj[(size_t)row * V + col + i] = acc[i];
+        for (int t = 0; t < TPW; ++t) {
+            const int rt = TPW * w + t;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int row = 16 * rt + 4 * lg + e;
+                sS[row * LD + lr] = acc[t][e];
+                Lj[(size_t)row * V + col] = acc[t][e];
+            }
         }
         __syncthreads();
     }

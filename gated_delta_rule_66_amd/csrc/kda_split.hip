@@ -474,9 +474,10 @@ __global__ __launch_bounds__(512) void kda_intra_kernel(IntraParams p) {
 // ============================================================================
 // State pass
 // ============================================================================
-template <typename T, int K, int NTW>
+template <typename T, int K, int NW_, int NTW, bool SUMMARY>
 struct StateLayout {
-    static constexpr int NW = 4;
+    static constexpr int NW = NW_;                       // waves; wave w owns NTW 16-column tiles
+    static constexpr int NT = 64 * NW;
     static constexpr int VB = 16 * NW * NTW;
     static constexpr int SZ = (int)sizeof(T);
     static constexpr int PAD = 16 / SZ;
@@ -492,20 +493,23 @@ struct StateLayout {
     static constexpr int TOTAL = oEGC + K * 4;
     static_assert(TOTAL <= 160 * 1024, "LDS budget exceeded");
     static_assert(C * 16 * NTW <= 16 * NTW * LDT, "output staging must fit the wave's U~ rows");
-    // 16-byte pieces of one record the workgroup loads
-    static constexpr int PW = C * K * SZ / 16;           // W (and Qh)
-    static constexpr int PM = C * C * SZ / 16;           // Mqk
+    // 16-byte pieces of one record the workgroup loads (the summary pass
+    // computes no output and skips Qh and Mqk)
+    static constexpr int PW = C * K * SZ / 16;           // W
+    static constexpr int PQ = SUMMARY ? 0 : C * K * SZ / 16;   // Qh
+    static constexpr int PM = SUMMARY ? 0 : C * C * SZ / 16;   // Mqk
     static constexpr int PK = K * C * SZ / 16;           // KbT
     static constexpr int PU = VB * C * SZ / 16;          // U~ rows of the block
     static constexpr int PE = K * 4 / 16;                // e^{G_C}
-    static constexpr int PTOT = 2 * PW + PM + PK + PU + PE;
-    static constexpr int NPT = (PTOT + 255) / 256;       // pieces per thread
+    static constexpr int E1 = PW, E2 = E1 + PQ, E3 = E2 + PM, E4 = E3 + PK, E5 = E4 + PU;
+    static constexpr int PTOT = E5 + PE;
+    static constexpr int NPT = (PTOT + NT - 1) / NT;     // pieces per thread
 };
 
-template <typename T, int K, int NTW, bool SUMMARY>
-__global__ __launch_bounds__(256, (NTW == 1 && sizeof(T) == 2 ? 2 : 1)) void kda_state_kernel(StateParams p) {
-    using L = StateLayout<T, K, NTW>;
-    constexpr int NW = L::NW;
+template <typename T, int K, int NW, int NTW, bool SUMMARY>
+__global__ __launch_bounds__(64 * NW, (NW == 4 && NTW == 1 && sizeof(T) == 2 ? 2 : 1))
+void kda_state_kernel(StateParams p) {
+    using L = StateLayout<T, K, NW, NTW, SUMMARY>;
     using Frag = typename FragOf<T>::type;
     constexpr int VB = L::VB;
     constexpr int LDK2 = L::LDK2, LDL = L::LDL, LDT = L::LDT;
@@ -571,28 +575,30 @@ __global__ __launch_bounds__(256, (NTW == 1 && sizeof(T) == 2 ? 2 : 1)) void kda
     }
 
     // ---- record loads: 16-byte pieces into registers, one chunk ahead ------------
-    // piece index pc = tid + 256 m over [W | Qh | Mqk | KbT | U~ rows | e^{G_C}]
+    // piece index pc = tid + NT m over [W | Qh | Mqk | KbT | U~ rows | e^{G_C}]
+    constexpr int NT = L::NT;
     uint4 pre[NPT];
     auto load_rec = [&](int ci) {
         const unsigned char* rec = rec0 + (size_t)ci * RL.bytes;
         const __amdgpu_buffer_rsrc_t rr = make_rsrc(rec);
 #pragma unroll
         for (int m = 0; m < NPT; ++m) {
-            const int pc = tid + 256 * m;
+            const int pc = tid + NT * m;
             unsigned off = 0;
             bool ok = true;
-            if (pc < 2 * L::PW) {
-                off = (unsigned)RL.oW + (unsigned)pc * 16u;          // W and Qh are adjacent
-            } else if (pc < 2 * L::PW + L::PM) {
-                off = (unsigned)RL.oMqk + (unsigned)(pc - 2 * L::PW) * 16u;
-            } else if (pc < 2 * L::PW + L::PM + L::PK) {
-                off = (unsigned)RL.oKbT + (unsigned)(pc - 2 * L::PW - L::PM) * 16u;
-            } else if (pc < 2 * L::PW + L::PM + L::PK + L::PU) {
+            if (pc < L::E1) {
+                off = (unsigned)RL.oW + (unsigned)pc * 16u;
+            } else if (pc < L::E2) {
+                off = (unsigned)RL.oQh + (unsigned)(pc - L::E1) * 16u;
+            } else if (pc < L::E3) {
+                off = (unsigned)RL.oMqk + (unsigned)(pc - L::E2) * 16u;
+            } else if (pc < L::E4) {
+                off = (unsigned)RL.oKbT + (unsigned)(pc - L::E3) * 16u;
+            } else if (pc < L::E5) {
                 ok = !pmode;
-                off = (unsigned)RL.oUtT + (unsigned)vcol0 * C * SZ +
-                      (unsigned)(pc - 2 * L::PW - L::PM - L::PK) * 16u;
+                off = (unsigned)RL.oUtT + (unsigned)vcol0 * C * SZ + (unsigned)(pc - L::E4) * 16u;
             } else if (pc < L::PTOT) {
-                off = (unsigned)RL.oEgc + (unsigned)(pc - 2 * L::PW - L::PM - L::PK - L::PU) * 16u;
+                off = (unsigned)RL.oEgc + (unsigned)(pc - L::E5) * 16u;
             } else {
                 ok = false;
             }
@@ -602,27 +608,26 @@ __global__ __launch_bounds__(256, (NTW == 1 && sizeof(T) == 2 ? 2 : 1)) void kda
     auto store_rec = [&]() {
 #pragma unroll
         for (int m = 0; m < NPT; ++m) {
-            const int pc = tid + 256 * m;
+            const int pc = tid + NT * m;
             unsigned char* dst = nullptr;
-            if (pc < 2 * L::PW) {
-                constexpr int PR = K * (int)SZ / 16;                    // pieces per row
-                const int q = pc % L::PW, row = q / PR, cs = q % PR;
-                dst = smem + (pc < L::PW ? L::oW : L::oQh) + row * LDK2 * SZ + cs * 16;
-            } else if (pc < 2 * L::PW + L::PM) {
-                constexpr int PR = C * (int)SZ / 16;
-                const int q = pc - 2 * L::PW, row = q / PR, cs = q % PR;
-                dst = smem + L::oMqk + row * LDL * SZ + cs * 16;
-            } else if (pc < 2 * L::PW + L::PM + L::PK) {
-                constexpr int PR = C * (int)SZ / 16;
-                const int q = pc - 2 * L::PW - L::PM, row = q / PR, cs = q % PR;
-                dst = smem + L::oKbT + row * LDT * SZ + cs * 16;
-            } else if (pc < 2 * L::PW + L::PM + L::PK + L::PU) {
-                constexpr int PR = C * (int)SZ / 16;
-                const int q = pc - 2 * L::PW - L::PM - L::PK, row = q / PR, cs = q % PR;
-                dst = smem + L::oUtT + row * LDT * SZ + cs * 16;
+            constexpr int PRK = K * (int)SZ / 16;        // pieces per K-long row
+            constexpr int PRC = C * (int)SZ / 16;        // pieces per C-long row
+            if (pc < L::E1) {
+                dst = smem + L::oW + (pc / PRK) * LDK2 * SZ + (pc % PRK) * 16;
+            } else if (pc < L::E2) {
+                const int q = pc - L::E1;
+                dst = smem + L::oQh + (q / PRK) * LDK2 * SZ + (q % PRK) * 16;
+            } else if (pc < L::E3) {
+                const int q = pc - L::E2;
+                dst = smem + L::oMqk + (q / PRC) * LDL * SZ + (q % PRC) * 16;
+            } else if (pc < L::E4) {
+                const int q = pc - L::E3;
+                dst = smem + L::oKbT + (q / PRC) * LDT * SZ + (q % PRC) * 16;
+            } else if (pc < L::E5) {
+                const int q = pc - L::E4;
+                dst = smem + L::oUtT + (q / PRC) * LDT * SZ + (q % PRC) * 16;
             } else if (pc < L::PTOT) {
-                const int q = pc - 2 * L::PW - L::PM - L::PK - L::PU;
-                dst = smem + L::oEGC + q * 16;
+                dst = smem + L::oEGC + (pc - L::E5) * 16;
             }
             if (dst) *reinterpret_cast<uint4*>(dst) = pre[m];
         }
@@ -777,24 +782,25 @@ hipError_t launch_intra(int dtype, int K, int V, const IntraParams& p, int grid,
     return hipErrorInvalidValue;
 }
 
-template <typename T, int K, int NTW>
+template <typename T, int K, int NW>
 static hipError_t launch_state_t(const StateParams& p, int grid, hipStream_t stream) {
     if (p.summary)
-        hipLaunchKernelGGL((kda_state_kernel<T, K, NTW, true>), dim3(grid), dim3(256), 0, stream, p);
+        hipLaunchKernelGGL((kda_state_kernel<T, K, NW, 1, true>), dim3(grid), dim3(64 * NW), 0, stream, p);
     else
-        hipLaunchKernelGGL((kda_state_kernel<T, K, NTW, false>), dim3(grid), dim3(256), 0, stream, p);
+        hipLaunchKernelGGL((kda_state_kernel<T, K, NW, 1, false>), dim3(grid), dim3(64 * NW), 0, stream, p);
     return hipGetLastError();
 }
 
+// VB = 16 * NW value columns per workgroup
 hipError_t launch_state(int dtype, int K, int VB, const StateParams& p, int grid, hipStream_t stream) {
     if (grid <= 0) return hipSuccess;
     if (dtype == 1) {
-        if (K == 128 && VB == 128) return launch_state_t<bf16, 128, 2>(p, grid, stream);
-        if (K == 128 && VB == 64) return launch_state_t<bf16, 128, 1>(p, grid, stream);
-        if (K == 64 && VB == 128) return launch_state_t<bf16, 64, 2>(p, grid, stream);
-        if (K == 64 && VB == 64) return launch_state_t<bf16, 64, 1>(p, grid, stream);
+        if (K == 128 && VB == 128) return launch_state_t<bf16, 128, 8>(p, grid, stream);
+        if (K == 128 && VB == 64) return launch_state_t<bf16, 128, 4>(p, grid, stream);
+        if (K == 64 && VB == 128) return launch_state_t<bf16, 64, 8>(p, grid, stream);
+        if (K == 64 && VB == 64) return launch_state_t<bf16, 64, 4>(p, grid, stream);
     } else if (dtype == 0) {
-        if (K == 64 && VB == 64) return launch_state_t<float, 64, 1>(p, grid, stream);
+        if (K == 64 && VB == 64) return launch_state_t<float, 64, 4>(p, grid, stream);
     }
     return hipErrorInvalidValue;
 }
