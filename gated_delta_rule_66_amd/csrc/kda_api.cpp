@@ -89,25 +89,31 @@ kda_status resolve_plan(int B, int T, int H, int K, int V, kda_dtype dt, const k
     int split = req ? req->split : 0;
     if (vb < 0 || ns < 0 || split < 0 || split > 2) return KDA_ERR_INVALID_ARG;
     if (vb != 0 && vb != 64 && vb != 128) return KDA_ERR_INVALID_ARG;
-    if (split == 0) split = split_variant_exists((int)dt, K, V, 64) ? 2 : 1;
     int cus = 0;
-    if (vb == 0 || ns == 0) {
+    if (vb == 0 || ns == 0 || split == 0) {
         kda_status s = device_cus(&cus);
         if (s != KDA_OK) return s;
     }
+    if (split == 0) {
+        // single pass when (b, h, 128-column) chains alone fill the device;
+        // otherwise the two-pass form, whose first pass is parallel over chunks
+        const bool wide = bh * (V >= 128 ? V / 128 : 1) >= cus && chunk_variant_exists((int)dt, K, V >= 128 ? 128 : 64);
+        split = (!wide && split_variant_exists((int)dt, K, V, 64)) ? 2 : 1;
+    }
     const bool vb_fixed = vb != 0;
     if (split == 2) {
-        // state pass: two workgroups fit a CU; 64 value columns per workgroup
-        // unless asked otherwise
-        if (!vb_fixed) vb = 64;
+        // state pass: 128 value columns per workgroup (each chunk record is
+        // read once per (b, h, segment)) where the sizes allow, else 64
+        if (!vb_fixed) vb = (V >= 128 && (K % 128 == 0) && split_variant_exists((int)dt, K, V, 128)) ? 128 : 64;
         if (vb > V || !split_variant_exists((int)dt, K, V, vb)) return KDA_ERR_UNSUPPORTED;
         if (ns == 0) {
-            // segments until the state pass has about two workgroups per CU,
-            // each segment keeping at least 4 chunks
+            // segments until the state pass has about one workgroup per CU
+            // (two for 64-column blocks), each segment keeping at least 4 chunks
             const long wgs = bh * (V / vb);
+            const long slots = (vb == 128 ? 1L : 2L) * cus;
             ns = 1;
-            if (wgs > 0 && wgs < 2L * cus) {
-                const long want = (2L * cus + wgs - 1) / wgs;
+            if (wgs > 0 && wgs < slots) {
+                const long want = (slots + wgs - 1) / wgs;
                 const long cap = n_chunks / 4;
                 ns = (int)(want < cap ? want : cap);
                 if (ns < 1) ns = 1;

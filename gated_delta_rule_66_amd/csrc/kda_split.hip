@@ -204,6 +204,7 @@ __global__ __launch_bounds__(512) void kda_intra_kernel(IntraParams p) {
         T* gKbT = reinterpret_cast<T*>(rec + RL.oKbT);
         T* gUtT = reinterpret_cast<T*>(rec + RL.oUtT);
         float* gEgc = reinterpret_cast<float*>(rec + RL.oEgc);
+        const __amdgpu_buffer_rsrc_t rrec = make_rsrc(rec);
 
         // ---- P1: gate cumsum; key / query side to LDS, Qh, KbT, e^{G_C} out ----
         {
@@ -251,7 +252,10 @@ __global__ __launch_bounds__(512) void kda_intra_kernel(IntraParams p) {
                 float ec[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) ec[e] = fast_exp2(gcum[e]);
-                st8(&gEgc[c0], ec);
+                const float4 a4 = make_float4(ec[0], ec[1], ec[2], ec[3]);
+                const float4 b4 = make_float4(ec[4], ec[5], ec[6], ec[7]);
+                buf_store16(rrec, (unsigned)RL.oEgc + (unsigned)c0 * 4u, 0u, *reinterpret_cast<const uint4*>(&a4));
+                buf_store16(rrec, (unsigned)RL.oEgc + (unsigned)c0 * 4u + 16u, 0u, *reinterpret_cast<const uint4*>(&b4));
             }
             if (w == 0 && c8l == 0) {
 #pragma unroll
@@ -295,13 +299,24 @@ __global__ __launch_bounds__(512) void kda_intra_kernel(IntraParams p) {
                     qh[e] = qd[e] * egb[e];
                 }
                 st8(&sQd[t * LDK1 + c0], qd);
-                st8(&gQh[t * K + c0], qh);
+                if constexpr (sizeof(T) == 2) {
+                    const auto qf = frag_from<T>(qh);
+                    buf_store16(rrec, (unsigned)RL.oQh + (unsigned)(t * K + c0) * SZ, 0u, *reinterpret_cast<const uint4*>(&qf));
+                } else {
+                    st8(&gQh[t * K + c0], qh);
+                }
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 st_small<TPL>(&sKhbT[(c0 + e) * LDT + part * TPL], kh[e]);
-                st_small<TPL>(&gKbT[(c0 + e) * C + part * TPL], kb[e]);
+                if constexpr (sizeof(T) == 2 && TPL == 2) {
+                    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+                    b2 r; r[0] = (bf16)kb[e][0]; r[1] = (bf16)kb[e][1];
+                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, r), rrec, (int)((unsigned)RL.oKbT + (unsigned)((c0 + e) * C + part * TPL) * SZ), 0, 0);
+                } else {
+                    st_small<TPL>(&gKbT[(c0 + e) * C + part * TPL], kb[e]);
+                }
             }
             float bv[8][TPLV];
 #pragma unroll
@@ -334,10 +349,11 @@ __global__ __launch_bounds__(512) void kda_intra_kernel(IntraParams p) {
                 acc = mma(acc, ld_frag<T>(&sKd[(16 * i + lr) * LDK1 + 32 * ks + 8 * lg]),
                           ld_frag<T>(&sKinv[(16 * i + lr) * LDK1 + 32 * ks + 8 * lg]));
             float* Ad = sAd + i * 16 * LDD;
+            const f32x4 bt = *reinterpret_cast<const f32x4*>(&sBeta[16 * i + 4 * lg]);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int s_ = 4 * lg + e;
-                Ad[s_ * LDD + lr] = (lr < s_) ? sBeta[16 * i + s_] * acc[e] : 0.f;
+                Ad[s_ * LDD + lr] = (lr < s_) ? bt[e] * acc[e] : 0.f;
             }
             wave_lds_sync();
             if (lg == 0) {
@@ -375,18 +391,22 @@ __global__ __launch_bounds__(512) void kda_intra_kernel(IntraParams p) {
                         if (task < 6) offdiag_pair(task, i, j);
                         else lower_pair(task - 6, i, j);
                         const T* rowsrc = (task < 6) ? sKd : sQd;
-                        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                        typename FragOf<T>::type fa[KS], fb[KS];
 #pragma unroll
                         for (int ks = 0; ks < KS; ++ks) {
                             const int cc = 32 * ks + 8 * lg;
-                            acc = mma(acc, ld_frag<T>(&rowsrc[(16 * i + lr) * LDK1 + cc]),
-                                      col_frag<T, LDK1, K>(sKinv, sF, i, j, lr, cc));
+                            fa[ks] = ld_frag<T>(&rowsrc[(16 * i + lr) * LDK1 + cc]);
+                            fb[ks] = col_frag<T, LDK1, K>(sKinv, sF, i, j, lr, cc);
                         }
+                        const f32x4 bt = *reinterpret_cast<const f32x4*>(&sBeta[16 * i + 4 * lg]);
+                        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int ks = 0; ks < KS; ++ks) acc = mma(acc, fa[ks], fb[ks]);
                         const int r = 16 * j + lr;
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const int s_ = 16 * i + 4 * lg + e;
-                            if (task < 6) sL[s_ * LDL + r] = from_f32<T>(-sBeta[s_] * acc[e]);
+                            if (task < 6) sL[s_ * LDL + r] = from_f32<T>(-bt[e] * acc[e]);
                             else sMqk[s_ * LDL + r] = from_f32<T>((i > j || r <= s_) ? acc[e] : 0.f);
                         }
                     } else {
@@ -577,8 +597,10 @@ void kda_state_kernel(StateParams p) {
     // ---- record loads: 16-byte pieces into registers, one chunk ahead ------------
     // piece index pc = tid + NT m over [W | Qh | Mqk | KbT | U~ rows | e^{G_C}]
     constexpr int NT = L::NT;
-    uint4 pre[NPT];
-    auto load_rec = [&](int ci) {
+    // (two register sets: the 8-wave variant keeps two records in flight)
+    constexpr int DEPTH = 1;
+    uint4 preA[NPT], preB[NPT];
+    auto load_rec = [&](int ci, uint4 (&pre)[NPT]) {
         const unsigned char* rec = rec0 + (size_t)ci * RL.bytes;
         const __amdgpu_buffer_rsrc_t rr = make_rsrc(rec);
 #pragma unroll
@@ -605,7 +627,7 @@ void kda_state_kernel(StateParams p) {
             pre[m] = ok ? buf_load16(rr, off) : make_uint4(0, 0, 0, 0);
         }
     };
-    auto store_rec = [&]() {
+    auto store_rec = [&](const uint4 (&pre)[NPT]) {
 #pragma unroll
         for (int m = 0; m < NPT; ++m) {
             const int pc = tid + NT * m;
@@ -632,18 +654,12 @@ void kda_state_kernel(StateParams p) {
             if (dst) *reinterpret_cast<uint4*>(dst) = pre[m];
         }
     };
-    if (c_begin < c_end) load_rec(c_begin);
-
     const unsigned rowV = (unsigned)p.H * V * SZ;
-    for (int ci = c_begin; ci < c_end; ++ci) {
+    // one chunk of the state pass, operands in LDS
+    auto step = [&](int ci) {
         const int t0 = ci * C;
         const int nt = min(C, p.T - t0);
-        store_rec();
-        __syncthreads();
-        __builtin_amdgcn_sched_barrier(0);
-        if (ci + 1 < c_end) load_rec(ci + 1);
-        __builtin_amdgcn_sched_barrier(0);
-
+        // every phase first reads all of its LDS operands, then runs its MFMAs
         Frag Sb[NTW][KS];
 #pragma unroll
         for (int j = 0; j < NTW; ++j)
@@ -651,23 +667,28 @@ void kda_state_kernel(StateParams p) {
             for (int ks = 0; ks < KS; ++ks) Sb[j][ks] = frag_from_tiles<T>(S[j][2 * ks], S[j][2 * ks + 1]);
         // U = U~ - W S
         f32x4 U[NTW][4];
+        {
+            Frag aw[4][KS];
+            f32x4 ut[NTW][4];
 #pragma unroll
-        for (int ti = 0; ti < 4; ++ti) {
-            f32x4 acc[NTW];
+            for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
-            for (int j = 0; j < NTW; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int ks = 0; ks < KS; ++ks) aw[ti][ks] = ld_frag_perm<T>(&sW[(16 * ti + lr) * LDK2 + 32 * ks + 4 * lg]);
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const Frag a = ld_frag_perm<T>(&sW[(16 * ti + lr) * LDK2 + 32 * ks + 4 * lg]);
+            for (int j = 0; j < NTW; ++j)
 #pragma unroll
-                for (int j = 0; j < NTW; ++j) acc[j] = mma(acc[j], a, Sb[j][ks]);
-            }
+                for (int ti = 0; ti < 4; ++ti)
+                    ut[j][ti] = pmode ? f32x4{0.f, 0.f, 0.f, 0.f}
+                                      : ld4_as_f32<T>(&sUtT[(16 * (tile0 + j) + lr) * LDT + 16 * ti + 4 * lg]);
 #pragma unroll
-            for (int j = 0; j < NTW; ++j) {
-                const f32x4 ut = pmode ? f32x4{0.f, 0.f, 0.f, 0.f}
-                                       : ld4_as_f32<T>(&sUtT[(16 * (tile0 + j) + lr) * LDT + 16 * ti + 4 * lg]);
-                U[j][ti] = ut - acc[j];
-            }
+            for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+                for (int j = 0; j < NTW; ++j) {
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) acc = mma(acc, aw[ti][ks], Sb[j][ks]);
+                    U[j][ti] = ut[j][ti] - acc;
+                }
         }
         Frag Ub[NTW][2];
 #pragma unroll
@@ -676,34 +697,38 @@ void kda_state_kernel(StateParams p) {
             Ub[j][1] = frag_from_tiles<T>(U[j][2], U[j][3]);
         }
         if (!SUMMARY) {
-            // output block of this wave staged in its own (consumed) U~ rows
+            // O = (Q e^G) S + Mqk U, staged in this wave's own (consumed) U~ rows
             constexpr int OW = 16 * NTW;
             T* sO = sUtT + 16 * tile0 * LDT;
-            wave_lds_sync();
+            Frag aq[4][KS], am[4][2];
 #pragma unroll
             for (int ti = 0; ti < 4; ++ti) {
-                f32x4 acc[NTW];
 #pragma unroll
-                for (int j = 0; j < NTW; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int ks = 0; ks < KS; ++ks) aq[ti][ks] = ld_frag_perm<T>(&sQh[(16 * ti + lr) * LDK2 + 32 * ks + 4 * lg]);
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const Frag a = ld_frag_perm<T>(&sQh[(16 * ti + lr) * LDK2 + 32 * ks + 4 * lg]);
+                for (int ks = 0; ks < 2; ++ks)
+                    if (ks <= (ti >> 1)) am[ti][ks] = ld_frag_perm<T>(&sMqk[(16 * ti + lr) * LDL + 32 * ks + 4 * lg]);
+            }
+            f32x4 acco[NTW][4];
 #pragma unroll
-                    for (int j = 0; j < NTW; ++j) acc[j] = mma(acc[j], a, Sb[j][ks]);
+            for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+                for (int j = 0; j < NTW; ++j) {
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) acc = mma(acc, aq[ti][ks], Sb[j][ks]);
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks)
+                        if (ks <= (ti >> 1)) acc = mma(acc, am[ti][ks], Ub[j][ks]);
+                    acco[j][ti] = acc;
                 }
+            wave_lds_sync();
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    if (ks <= (ti >> 1)) {
-                        const Frag a = ld_frag_perm<T>(&sMqk[(16 * ti + lr) * LDL + 32 * ks + 4 * lg]);
-#pragma unroll
-                        for (int j = 0; j < NTW; ++j) acc[j] = mma(acc[j], a, Ub[j][ks]);
-                    }
-                }
+            for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
                 for (int j = 0; j < NTW; ++j)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) sO[(16 * ti + 4 * lg + e) * OW + 16 * j + lr] = from_f32<T>(acc[j][e]);
-            }
+                    for (int e = 0; e < 4; ++e) sO[(16 * ti + 4 * lg + e) * OW + 16 * j + lr] = from_f32<T>(acco[j][ti][e]);
             wave_lds_sync();
             constexpr int PPR = OW * (int)SZ / 16;
             const __amdgpu_buffer_rsrc_t ro = make_rsrc(
@@ -717,19 +742,57 @@ void kda_state_kernel(StateParams p) {
             }
         }
         // S <- Diag(e^{G_C}) S + (K e^{G_C - G})^T U
+        {
+            Frag ak[CT][2];
+            f32x4 eg[CT];
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-            const f32x4 eg = *reinterpret_cast<const f32x4*>(&sEGC[16 * ct + 4 * lg]);
+            for (int ct = 0; ct < CT; ++ct) {
+                eg[ct] = *reinterpret_cast<const f32x4*>(&sEGC[16 * ct + 4 * lg]);
 #pragma unroll
-            for (int j = 0; j < NTW; ++j) S[j][ct] = S[j][ct] * eg;
+                for (int ks = 0; ks < 2; ++ks) ak[ct][ks] = ld_frag_perm<T>(&sKbT[(16 * ct + lr) * LDT + 32 * ks + 4 * lg]);
+            }
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const Frag a = ld_frag_perm<T>(&sKbT[(16 * ct + lr) * LDT + 32 * ks + 4 * lg]);
+            for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-                for (int j = 0; j < NTW; ++j) S[j][ct] = mma(S[j][ct], a, Ub[j][ks]);
+                for (int j = 0; j < NTW; ++j) {
+                    S[j][ct] = S[j][ct] * eg[ct];
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks) S[j][ct] = mma(S[j][ct], ak[ct][ks], Ub[j][ks]);
+                }
+        }
+    };
+
+    if (c_begin < c_end) load_rec(c_begin, preA);
+    if (DEPTH == 2 && c_begin + 1 < c_end) load_rec(c_begin + 1, preB);
+    if constexpr (DEPTH == 2) {
+        for (int ci = c_begin; ci < c_end; ci += 2) {
+            store_rec(preA);
+            __syncthreads();
+            __builtin_amdgcn_sched_barrier(0);
+            if (ci + 2 < c_end) load_rec(ci + 2, preA);
+            __builtin_amdgcn_sched_barrier(0);
+            step(ci);
+            __syncthreads();
+            if (ci + 1 < c_end) {
+                store_rec(preB);
+                __syncthreads();
+                __builtin_amdgcn_sched_barrier(0);
+                if (ci + 3 < c_end) load_rec(ci + 3, preB);
+                __builtin_amdgcn_sched_barrier(0);
+                step(ci + 1);
+                __syncthreads();
             }
         }
-        __syncthreads();
+    } else {
+        for (int ci = c_begin; ci < c_end; ++ci) {
+            store_rec(preA);
+            __syncthreads();
+            __builtin_amdgcn_sched_barrier(0);
+            if (ci + 1 < c_end) load_rec(ci + 1, preA);
+            __builtin_amdgcn_sched_barrier(0);
+            step(ci);
+            __syncthreads();
+        }
     }
 
     float* dst = nullptr;
