@@ -89,6 +89,14 @@ kda_status resolve_plan(int B, int T, int H, int K, int V, kda_dtype dt, const k
     int split = req ? req->split : 0;
     if (vb < 0 || ns < 0 || split < 0 || split > 2) return KDA_ERR_INVALID_ARG;
     if (vb != 0 && vb != 64 && vb != 128) return KDA_ERR_INVALID_ARG;
+    // requests no path can serve, rejected before any device query
+    if (vb != 0 && vb > V) return KDA_ERR_UNSUPPORTED;
+    if (vb != 0 && ns > 1 && K % vb != 0) {
+        // the summary pass carries the K transition columns in whole blocks;
+        // it runs whenever the request leaves more than one segment
+        const int cps_req = (n_chunks + ns - 1) / ns;
+        if (n_chunks > cps_req) return KDA_ERR_UNSUPPORTED;
+    }
     int cus = 0;
     if (vb == 0 || ns == 0 || split == 0) {
         kda_status s = device_cus(&cus);
