@@ -15,7 +15,7 @@ states it must read or write) over its average duration, measured with HIP
 events that the library records on the launch stream (kda_profile_start).
 ``traffic`` is the HBM traffic per launch from rocprofv3 FETCH_SIZE and
 WRITE_SIZE counters, scaled by a plain-copy calibration; it is read from
-profiles/chunk_kernel_c1_traffic.json and reported only while the kernel
+profiles/prefill_c1_traffic.json and reported only while the kernel
 source still has the hash recorded there.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--extra] [--no-cpu-baseline]
@@ -30,7 +30,7 @@ import sys
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "chunk_kernel_c1_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_c1_traffic.json")
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
