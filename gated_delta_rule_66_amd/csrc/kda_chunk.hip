@@ -641,8 +641,12 @@ __global__ __launch_bounds__(256) void kda_scan_kernel(ScanParams p) {
     constexpr int KQ = K / 4;           // reduction steps
     constexpr int LD = 17;
     __shared__ float sS[K * LD];
+    // the column blocks of one (b, h) read the same P rows: place them on one
+    // XCD (workgroups are dealt to the 8 XCDs round robin) so they share its L2
+    const int G = gridDim.x, x = blockIdx.x;
+    const int lid = ((G & 7) == 0) ? (x & 7) * (G >> 3) + (x >> 3) : x;
     const int ncb = p.V / 16;
-    const int bh = blockIdx.x / ncb, cb = blockIdx.x % ncb;
+    const int bh = lid / ncb, cb = lid % ncb;
     const int tid = threadIdx.x;
     const int w = tid >> 6, l = tid & 63, lg = l >> 4, lr = l & 15;
     const int V = p.V;

@@ -597,9 +597,7 @@ void kda_state_kernel(StateParams p) {
     // ---- record loads: 16-byte pieces into registers, one chunk ahead ------------
     // piece index pc = tid + NT m over [W | Qh | Mqk | KbT | U~ rows | e^{G_C}]
     constexpr int NT = L::NT;
-    // (two register sets: the 8-wave variant keeps two records in flight)
-    constexpr int DEPTH = 1;
-    uint4 preA[NPT], preB[NPT];
+    uint4 pre[NPT];
     auto load_rec = [&](int ci, uint4 (&pre)[NPT]) {
         const unsigned char* rec = rec0 + (size_t)ci * RL.bytes;
         const __amdgpu_buffer_rsrc_t rr = make_rsrc(rec);
@@ -762,37 +760,15 @@ void kda_state_kernel(StateParams p) {
         }
     };
 
-    if (c_begin < c_end) load_rec(c_begin, preA);
-    if (DEPTH == 2 && c_begin + 1 < c_end) load_rec(c_begin + 1, preB);
-    if constexpr (DEPTH == 2) {
-        for (int ci = c_begin; ci < c_end; ci += 2) {
-            store_rec(preA);
-            __syncthreads();
-            __builtin_amdgcn_sched_barrier(0);
-            if (ci + 2 < c_end) load_rec(ci + 2, preA);
-            __builtin_amdgcn_sched_barrier(0);
-            step(ci);
-            __syncthreads();
-            if (ci + 1 < c_end) {
-                store_rec(preB);
-                __syncthreads();
-                __builtin_amdgcn_sched_barrier(0);
-                if (ci + 3 < c_end) load_rec(ci + 3, preB);
-                __builtin_amdgcn_sched_barrier(0);
-                step(ci + 1);
-                __syncthreads();
-            }
-        }
-    } else {
-        for (int ci = c_begin; ci < c_end; ++ci) {
-            store_rec(preA);
-            __syncthreads();
-            __builtin_amdgcn_sched_barrier(0);
-            if (ci + 1 < c_end) load_rec(ci + 1, preA);
-            __builtin_amdgcn_sched_barrier(0);
-            step(ci);
-            __syncthreads();
-        }
+    if (c_begin < c_end) load_rec(c_begin, pre);
+    for (int ci = c_begin; ci < c_end; ++ci) {
+        store_rec(pre);
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+        if (ci + 1 < c_end) load_rec(ci + 1, pre);
+        __builtin_amdgcn_sched_barrier(0);
+        step(ci);
+        __syncthreads();
     }
 
     float* dst = nullptr;
@@ -845,25 +821,26 @@ hipError_t launch_intra(int dtype, int K, int V, const IntraParams& p, int grid,
     return hipErrorInvalidValue;
 }
 
-template <typename T, int K, int NW>
+template <typename T, int K, int NW, int NTW>
 static hipError_t launch_state_t(const StateParams& p, int grid, hipStream_t stream) {
     if (p.summary)
-        hipLaunchKernelGGL((kda_state_kernel<T, K, NW, 1, true>), dim3(grid), dim3(64 * NW), 0, stream, p);
+        hipLaunchKernelGGL((kda_state_kernel<T, K, NW, NTW, true>), dim3(grid), dim3(64 * NW), 0, stream, p);
     else
-        hipLaunchKernelGGL((kda_state_kernel<T, K, NW, 1, false>), dim3(grid), dim3(64 * NW), 0, stream, p);
+        hipLaunchKernelGGL((kda_state_kernel<T, K, NW, NTW, false>), dim3(grid), dim3(64 * NW), 0, stream, p);
     return hipGetLastError();
 }
 
-// VB = 16 * NW value columns per workgroup
+// VB = 16 * NW * NTW value columns per workgroup; 128 columns run as 4 waves of
+// two 16-column tiles (each LDS operand fragment serves two MFMAs)
 hipError_t launch_state(int dtype, int K, int VB, const StateParams& p, int grid, hipStream_t stream) {
     if (grid <= 0) return hipSuccess;
     if (dtype == 1) {
-        if (K == 128 && VB == 128) return launch_state_t<bf16, 128, 8>(p, grid, stream);
-        if (K == 128 && VB == 64) return launch_state_t<bf16, 128, 4>(p, grid, stream);
-        if (K == 64 && VB == 128) return launch_state_t<bf16, 64, 8>(p, grid, stream);
-        if (K == 64 && VB == 64) return launch_state_t<bf16, 64, 4>(p, grid, stream);
+        if (K == 128 && VB == 128) return launch_state_t<bf16, 128, 4, 2>(p, grid, stream);
+        if (K == 128 && VB == 64) return launch_state_t<bf16, 128, 4, 1>(p, grid, stream);
+        if (K == 64 && VB == 128) return launch_state_t<bf16, 64, 8, 1>(p, grid, stream);
+        if (K == 64 && VB == 64) return launch_state_t<bf16, 64, 4, 1>(p, grid, stream);
     } else if (dtype == 0) {
-        if (K == 64 && VB == 64) return launch_state_t<float, 64, 4>(p, grid, stream);
+        if (K == 64 && VB == 64) return launch_state_t<float, 64, 4, 1>(p, grid, stream);
     }
     return hipErrorInvalidValue;
 }
