@@ -8,6 +8,8 @@ from .kda import (  # noqa: F401
     KDAError,
     Plan,
     chunk_fwd,
+    chunk_fwd_varlen,
+    chunk_fwd_varlen_workspace_size,
     chunk_plan,
     chunk_workspace_size,
     load_library,
@@ -19,5 +21,5 @@ from .kda import (  # noqa: F401
 )
 from .build import LIB_PATH, build_library  # noqa: F401
 
-__all__ = ["chunk_fwd", "recurrent_step", "chunk_plan", "chunk_workspace_size", "profile_start", "profile_stop",
+__all__ = ["chunk_fwd", "chunk_fwd_varlen", "chunk_fwd_varlen_workspace_size", "recurrent_step", "chunk_plan", "chunk_workspace_size", "profile_start", "profile_stop",
            "load_library", "build_library", "version", "status_string", "KDAError", "Plan"]

@@ -400,6 +400,108 @@ kda_status kda_chunk_fwd(int B, int T, int H, int K, int V, kda_dtype dt,
     return KDA_OK;
 }
 
+// ---- packed variable-length batch --------------------------------------------------
+static size_t varlen_chunk_bound(int N, int T_total) {
+    // sum_i ceil(len_i / C) <= ceil(T_total / C) + N
+    return (size_t)(T_total + kChunk - 1) / kChunk + (size_t)N;
+}
+
+static kda_status check_varlen_sizes(int N, int T_total, int H, int K, int V, kda_dtype dt) {
+    if (N < 0) return KDA_ERR_INVALID_ARG;
+    kda_status s = check_prefill_sizes(1, T_total, H, K, V, dt);
+    if (s != KDA_OK) return s;
+    if (!split_variant_exists((int)dt, K, V, 64)) return KDA_ERR_UNSUPPORTED;
+    if ((double)H * (double)varlen_chunk_bound(N, T_total) > 2.0e9 || (double)N * H * 2.0 > 2.0e9)
+        return KDA_ERR_UNSUPPORTED;
+    return KDA_OK;
+}
+
+size_t kda_chunk_fwd_varlen_workspace_size(int N, int T_total, int H, int K, int V, kda_dtype dt) {
+    if (check_varlen_sizes(N, T_total, H, K, V, dt) != KDA_OK) return (size_t)-1;
+    const size_t offs = ((size_t)(N + 1) * sizeof(int) + 255) & ~(size_t)255;
+    return offs + (size_t)H * varlen_chunk_bound(N, T_total) * record_bytes(K, V, dt);
+}
+
+kda_status kda_chunk_fwd_varlen(int N, const int* cu_seqlens, int T_total, int H, int K, int V, kda_dtype dt,
+                                const void* q, const void* k, const void* v,
+                                const void* g, const void* beta,
+                                const float* initial_state,
+                                void* o, float* final_state,
+                                void* workspace, size_t workspace_bytes,
+                                void* stream) {
+    kda_status s = check_varlen_sizes(N, T_total, H, K, V, dt);
+    if (s != KDA_OK) return s;
+    const long nh = (long)N * H;
+    if (nh > 0 && !cu_seqlens) return KDA_ERR_INVALID_ARG;
+    if (H > 0 && T_total > 0) {
+        if (!q || !k || !v || !g || !beta || !o) return KDA_ERR_INVALID_ARG;
+        if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(o) ||
+            (reinterpret_cast<uintptr_t>(beta) % elem_size(dt)) != 0)
+            return KDA_ERR_INVALID_ARG;
+    }
+    if ((cu_seqlens && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u)) ||
+        (initial_state && !aligned16(initial_state)) || (final_state && !aligned16(final_state)) ||
+        (workspace && !aligned16(workspace)))
+        return KDA_ERR_INVALID_ARG;
+    const size_t state_bytes = (size_t)nh * K * V * sizeof(float);
+    if (initial_state && final_state && ranges_partially_overlap(initial_state, final_state, state_bytes))
+        return KDA_ERR_INVALID_ARG;
+    if (nh == 0) return KDA_OK;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (T_total == 0) {
+        if (!final_state || final_state == initial_state) return KDA_OK;
+        return launch_timed("copy_state", st, [&] {
+                   return launch_copy_state(initial_state, final_state, (size_t)nh * K * V, st);
+               }) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    }
+    const size_t need = kda_chunk_fwd_varlen_workspace_size(N, T_total, H, K, V, dt);
+    if (!workspace || workspace_bytes < need) return KDA_ERR_WORKSPACE;
+    int cus = 0;
+    if (device_cus(&cus) != KDA_OK) return KDA_ERR_HIP;
+
+    const size_t offs = ((size_t)(N + 1) * sizeof(int) + 255) & ~(size_t)255;
+    int* chunk_off = reinterpret_cast<int*>(workspace);
+    unsigned char* recs = reinterpret_cast<unsigned char*>(workspace) + offs;
+    const int ncb = (int)varlen_chunk_bound(N, T_total);
+    if (launch_timed("varlen_prep", st, [&] {
+            return launch_varlen_prep(cu_seqlens, N, T_total, ncb, chunk_off, st);
+        }) != hipSuccess)
+        return KDA_ERR_HIP;
+
+    IntraParams ip{};
+    ip.q = q; ip.k = k; ip.v = v; ip.g = g; ip.beta = beta;
+    ip.rec = recs;
+    ip.B = 1; ip.T = T_total; ip.H = H; ip.NC = ncb;
+    ip.n_items = H * ncb;
+    ip.cu_seqlens = cu_seqlens;
+    ip.chunk_off = chunk_off;
+    ip.N = N;
+    const int igrid = ip.n_items < cus ? ip.n_items : cus;
+    if (launch_timed("intra_chunk", st, [&] { return launch_intra((int)dt, K, V, ip, igrid, st); }) != hipSuccess)
+        return KDA_ERR_HIP;
+
+    // state pass: one workgroup per (sequence, head, column block); 128-column
+    // blocks when they still give every CU a workgroup
+    int vb = 64;
+    if (V >= 128 && split_variant_exists((int)dt, K, V, 128) && nh * (V / 128) >= cus) vb = 128;
+    StateParams sp{};
+    sp.rec = recs;
+    sp.s0 = initial_state;
+    sp.o = o;
+    sp.sT = final_state;
+    sp.B = N; sp.T = T_total; sp.H = H; sp.V = V; sp.NC = ncb;
+    sp.n_seg = 1;
+    sp.cps = ncb;
+    sp.n_vb = V / vb;
+    sp.summary = 0;
+    sp.cu_seqlens = cu_seqlens;
+    sp.chunk_off = chunk_off;
+    sp.N = N;
+    return launch_timed("state_output", st, [&] {
+               return launch_state((int)dt, K, vb, sp, (int)(nh * (V / vb)), st);
+           }) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 kda_status kda_recurrent_step(int N, int H, int K, int V, kda_dtype dt,
                               const void* q, const void* k, const void* v,
                               const void* g, const void* beta,

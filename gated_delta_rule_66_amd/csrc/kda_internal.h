@@ -84,6 +84,11 @@ struct IntraParams {
     unsigned char* rec;     // [B*H*NC] records
     int B, T, H, NC;        // NC = chunks per sequence
     int n_items;            // B * H * NC
+    // packed variable-length batch (B = 1, T = total tokens): null for a
+    // regular batch.  Record (h * NC + global chunk); NC = chunk bound.
+    const int* cu_seqlens;  // [N + 1] token offsets
+    const int* chunk_off;   // [N + 1] chunk offsets (kda_varlen_prep_kernel)
+    int N;
 };
 
 struct StateParams {
@@ -96,9 +101,18 @@ struct StateParams {
     float* wsL;             // summary pass: [n_seg-1][B*H][K][V]
     int B, T, H, V, NC;
     int n_seg, cps, n_vb, summary;
+    // packed variable-length batch (B = 1, T = total tokens; one segment):
+    // null for a regular batch; workgroup (sequence, head, column block)
+    const int* cu_seqlens;
+    const int* chunk_off;
+    int N;
 };
 
 bool split_variant_exists(int dtype, int K, int V, int VB);
+// chunk offsets of a packed batch: chunk_off[i] = sum_{j<i} ceil(len_j / C),
+// capped at max_chunks; lengths from cu_seqlens clamped to [0, T_total]
+hipError_t launch_varlen_prep(const int* cu_seqlens, int N, int T_total, int max_chunks, int* chunk_off,
+                              hipStream_t stream);
 hipError_t launch_intra(int dtype, int K, int V, const IntraParams& p, int grid, hipStream_t stream);
 hipError_t launch_state(int dtype, int K, int VB, const StateParams& p, int grid, hipStream_t stream);
 

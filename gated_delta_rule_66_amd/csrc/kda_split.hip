@@ -52,6 +52,13 @@ __device__ __forceinline__ typename FragOf<T>::type col_frag(const T* sKinv, con
     return frag_from<T>(kv);
 }
 
+// token range [s0, s1) of sequence i of a packed batch; out-of-range offsets
+// are clamped so that every access stays inside the T_total rows
+__device__ __forceinline__ void seq_range(const int* cu, int i, int T_total, int& s0, int& s1) {
+    s0 = min(max(cu[i], 0), T_total);
+    s1 = max(s0, min(max(cu[i + 1], 0), T_total));
+}
+
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, unsigned voff) {
@@ -157,11 +164,32 @@ __global__ __launch_bounds__(512) void kda_intra_kernel(IntraParams p) {
     const unsigned vV = (unsigned)pv * TPLV * rowV + (unsigned)n0 * SZ;
     const unsigned vBV = (unsigned)pv * TPLV * rowB;
     auto load_item = [&](int item) {
-        const int bh = item / p.NC, ci = item - bh * p.NC;
-        const int b = bh / p.H, h = bh - b * p.H;
-        const int t0 = ci * C;
-        const int nt = min(C, p.T - t0);
-        const size_t head_row = (size_t)(b * (size_t)p.T + t0) * p.H + h;
+        int t0, nt;
+        size_t head_row;
+        if (p.cu_seqlens) {
+            // packed batch: item = h * NC + global chunk; find its sequence
+            const int h = item / p.NC, gc = item - h * p.NC;
+            t0 = 0;
+            nt = 0;
+            if (gc < p.chunk_off[p.N]) {
+                int lo = 0, hi = p.N;              // chunk_off[lo] <= gc < chunk_off[hi]
+                while (hi - lo > 1) {
+                    const int mid = (lo + hi) >> 1;
+                    if (p.chunk_off[mid] <= gc) lo = mid; else hi = mid;
+                }
+                int s0, s1;
+                seq_range(p.cu_seqlens, lo, p.T, s0, s1);
+                t0 = s0 + (gc - p.chunk_off[lo]) * C;
+                nt = max(0, min(C, s1 - t0));
+            }
+            head_row = (size_t)t0 * p.H + h;
+        } else {
+            const int bh = item / p.NC, ci = item - bh * p.NC;
+            const int b = bh / p.H, h = bh - b * p.H;
+            t0 = ci * C;
+            nt = min(C, p.T - t0);
+            head_row = (size_t)(b * (size_t)p.T + t0) * p.H + h;
+        }
         const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + head_row * K);
         const __amdgpu_buffer_rsrc_t rq = make_rsrc(qg + head_row * K);
         const __amdgpu_buffer_rsrc_t rg = make_rsrc(gg + head_row * K);
@@ -559,8 +587,25 @@ void kda_state_kernel(StateParams p) {
     const int b = bh / p.H, h = bh % p.H;
     const int BH = p.B * p.H;
     const int V = p.V;
-    const int c_begin = seg * p.cps;
-    const int c_end = min(c_begin + p.cps, p.NC);
+    // token rows of this chain: [row0, row_end) in the [rows][H] layout, and
+    // its records from rec_first on
+    int c_begin, c_end;
+    size_t row0, row_end, rec_first;
+    if (p.cu_seqlens) {
+        int s0, s1;
+        seq_range(p.cu_seqlens, b, p.T, s0, s1);          // b = sequence index
+        row0 = (size_t)s0;
+        row_end = (size_t)s1;
+        c_begin = 0;
+        c_end = p.chunk_off[b + 1] - p.chunk_off[b];
+        rec_first = (size_t)h * p.NC + p.chunk_off[b];
+    } else {
+        row0 = (size_t)b * p.T;
+        row_end = row0 + p.T;
+        c_begin = seg * p.cps;
+        c_end = min(c_begin + p.cps, p.NC);
+        rec_first = (size_t)bh * p.NC;
+    }
 
     const int col0 = vb * VB;
     const bool pmode = SUMMARY && col0 < K;
@@ -568,7 +613,7 @@ void kda_state_kernel(StateParams p) {
     const int tile0 = NTW * w;
 
     const RecLayout RL = rec_layout(K, V, (int)sizeof(T));
-    const unsigned char* rec0 = p.rec + (size_t)bh * p.NC * RL.bytes;
+    const unsigned char* rec0 = p.rec + rec_first * RL.bytes;
 
     // ---- initial state --------------------------------------------------------
     f32x4 S[NTW][CT];
@@ -655,8 +700,8 @@ void kda_state_kernel(StateParams p) {
     const unsigned rowV = (unsigned)p.H * V * SZ;
     // one chunk of the state pass, operands in LDS
     auto step = [&](int ci) {
-        const int t0 = ci * C;
-        const int nt = min(C, p.T - t0);
+        const size_t trow = row0 + (size_t)ci * C;                 // first token row of the chunk
+        const int nt = (int)min((size_t)C, row_end - trow);
         // every phase first reads all of its LDS operands, then runs its MFMAs
         Frag Sb[NTW][KS];
 #pragma unroll
@@ -730,7 +775,7 @@ void kda_state_kernel(StateParams p) {
             wave_lds_sync();
             constexpr int PPR = OW * (int)SZ / 16;
             const __amdgpu_buffer_rsrc_t ro = make_rsrc(
-                reinterpret_cast<T*>(p.o) + ((size_t)(b * (size_t)p.T + t0) * p.H + h) * V + vcol0 + OW * w);
+                reinterpret_cast<T*>(p.o) + (trow * p.H + h) * V + vcol0 + OW * w);
 #pragma unroll
             for (int pc = l; pc < C * PPR; pc += 64) {
                 const int row = pc / PPR, sg = pc % PPR;
@@ -792,6 +837,48 @@ void kda_state_kernel(StateParams p) {
                 for (int e = 0; e < 4; ++e) dst[(size_t)(16 * ct + 4 * lg + e) * ld + col] = S[j][ct][e];
         }
     }
+}
+
+// Chunk offsets of a packed batch (one workgroup; block-wide scans of 256
+// sequence lengths at a time).
+__global__ __launch_bounds__(256) void kda_varlen_prep_kernel(const int* cu, int N, int T_total, int max_chunks,
+                                                              int* chunk_off) {
+    __shared__ int buf[256];
+    __shared__ int carry;
+    const int tid = threadIdx.x;
+    if (tid == 0) {
+        carry = 0;
+        chunk_off[0] = 0;
+    }
+    __syncthreads();
+    for (int base = 0; base < N; base += 256) {
+        const int i = base + tid;
+        int c = 0;
+        if (i < N) {
+            int s0, s1;
+            seq_range(cu, i, T_total, s0, s1);
+            c = (s1 - s0 + C - 1) / C;
+        }
+        buf[tid] = c;
+        __syncthreads();
+        for (int d = 1; d < 256; d <<= 1) {
+            const int add = (tid >= d) ? buf[tid - d] : 0;
+            __syncthreads();
+            buf[tid] += add;
+            __syncthreads();
+        }
+        if (i < N) chunk_off[i + 1] = min(carry + buf[tid], max_chunks);
+        __syncthreads();
+        if (tid == 255) carry = min(carry + buf[255], max_chunks);
+        __syncthreads();
+    }
+}
+
+hipError_t launch_varlen_prep(const int* cu_seqlens, int N, int T_total, int max_chunks, int* chunk_off,
+                              hipStream_t stream) {
+    hipLaunchKernelGGL(kda_varlen_prep_kernel, dim3(1), dim3(256), 0, stream, cu_seqlens, N, T_total, max_chunks,
+                       chunk_off);
+    return hipGetLastError();
 }
 
 // ---- launchers ---------------------------------------------------------------------

@@ -26,6 +26,8 @@ EXPORTED_SYMBOLS = (
     "kda_chunk_fwd_plan",
     "kda_chunk_fwd_workspace_size",
     "kda_chunk_fwd",
+    "kda_chunk_fwd_varlen_workspace_size",
+    "kda_chunk_fwd_varlen",
     "kda_recurrent_step",
     "kda_status_string",
     "kda_version",
@@ -63,6 +65,10 @@ def load_library(path: str = LIB_PATH):
     lib.kda_chunk_fwd.argtypes = [i, i, i, i, i, i, p, p, p, p, p, p, p, p,
                                   ctypes.POINTER(Plan), p, sz, p]
     lib.kda_chunk_fwd.restype = i
+    lib.kda_chunk_fwd_varlen_workspace_size.argtypes = [i, i, i, i, i, i]
+    lib.kda_chunk_fwd_varlen_workspace_size.restype = sz
+    lib.kda_chunk_fwd_varlen.argtypes = [i, p, i, i, i, i, i, p, p, p, p, p, p, p, p, p, sz, p]
+    lib.kda_chunk_fwd_varlen.restype = i
     lib.kda_recurrent_step.argtypes = [i, i, i, i, i, p, p, p, p, p, p, p, p]
     lib.kda_recurrent_step.restype = i
     lib.kda_status_string.argtypes = [i]
@@ -200,6 +206,58 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
         None if pl is None else ctypes.byref(pl), _ptr(workspace), ws_len, _stream_ptr(dev))
     if st != KDA_OK:
         raise KDAError(st, "kda_chunk_fwd")
+    return out, final_state
+
+
+def chunk_fwd_varlen_workspace_size(N: int, T_total: int, H: int, K: int, V: int, dtype: torch.dtype) -> int:
+    n = load_library().kda_chunk_fwd_varlen_workspace_size(N, T_total, H, K, V, _dtype_code(dtype))
+    if n == ctypes.c_size_t(-1).value:
+        raise KDAError(KDA_ERR_INVALID_ARG, "kda_chunk_fwd_varlen_workspace_size")
+    return int(n)
+
+
+def chunk_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                     beta: torch.Tensor, cu_seqlens: torch.Tensor,
+                     initial_state: Optional[torch.Tensor] = None, output_final_state: bool = True, *,
+                     out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None):
+    """Packed variable-length prefill through ``kda_chunk_fwd_varlen``.
+
+    q, k, g: [T_total, H, K]; v: [T_total, H, V]; beta: [T_total, H] (bf16 or
+    fp32); cu_seqlens: int32 [N + 1] on the same device; initial_state:
+    [N, H, K, V] fp32 or None.  Returns (o [T_total, H, V], final_state
+    [N, H, K, V] or None); ``final_state`` may be ``initial_state`` itself.
+    """
+    T_total, H, K = q.shape
+    V = v.shape[-1]
+    dev = q.device
+    dt = q.dtype
+    for name, t, shp in (("q", q, (T_total, H, K)), ("k", k, (T_total, H, K)), ("g", g, (T_total, H, K)),
+                         ("v", v, (T_total, H, V)), ("beta", beta, (T_total, H))):
+        _check(t, name, shp, dt, dev)
+    N = cu_seqlens.numel() - 1
+    if N < 0:
+        raise ValueError("cu_seqlens needs N + 1 >= 1 entries")
+    _check(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
+    if initial_state is not None:
+        _check(initial_state, "initial_state", (N, H, K, V), torch.float32, dev)
+    if out is None:
+        out = torch.empty((T_total, H, V), dtype=dt, device=dev)
+    else:
+        _check(out, "out", (T_total, H, V), dt, dev)
+    if final_state is None and output_final_state:
+        final_state = torch.empty((N, H, K, V), dtype=torch.float32, device=dev)
+    elif final_state is not None:
+        _check(final_state, "final_state", (N, H, K, V), torch.float32, dev)
+    ws_bytes = chunk_fwd_varlen_workspace_size(N, T_total, H, K, V, dt)
+    if ws_bytes > 0 and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load_library().kda_chunk_fwd_varlen(
+        N, _ptr(cu_seqlens), T_total, H, K, V, _dtype_code(dt), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+        _ptr(initial_state), _ptr(out), _ptr(final_state), _ptr(workspace), ws_len, _stream_ptr(dev))
+    if st != KDA_OK:
+        raise KDAError(st, "kda_chunk_fwd_varlen")
     return out, final_state
 
 

@@ -137,6 +137,41 @@ kda_status kda_chunk_fwd(int B, int T, int H, int K, int V, kda_dtype dt,
                          void* stream);
 
 /*
+ * Prefill of a packed batch of N variable-length sequences (the
+ * prefix-caching and multi-token-verification use: every sequence resumes
+ * from its own state and returns its own final state).  The habr.com
+ * article on the Kimi K3 technical report notes that KDA needs its own
+ * prefix-caching support in serving engines; this is that call.
+ *
+ *   cu_seqlens : DEVICE int32 [N + 1]: sequence i is tokens
+ *                [cu_seqlens[i], cu_seqlens[i+1]) of the packed axis;
+ *                cu_seqlens[0] = 0, non-decreasing, cu_seqlens[N] = T_total.
+ *                Read on the device (nothing is synchronised).  Offsets
+ *                outside that contract are clamped to [0, T_total] (results
+ *                for such sequences are then unspecified, but every access
+ *                stays inside the buffers).
+ *   q, k, g    : [T_total, H, K] dtype dt;  v, o : [T_total, H, V];
+ *   beta       : [T_total, H]
+ *   initial_state : [N, H, K, V] fp32 or NULL (zeros)
+ *   final_state   : [N, H, K, V] fp32 or NULL; may alias initial_state exactly
+ *   workspace  : device scratch of at least
+ *                kda_chunk_fwd_varlen_workspace_size(...) bytes
+ * Runs the two-pass plan (intra-chunk pass over every chunk of every
+ * sequence, then one state-carrying workgroup column block per (sequence,
+ * head)); sequences of length 0 copy their state.  Same conventions, dtypes
+ * and error codes as kda_chunk_fwd; sizes: K, V in {64, 128}, bf16 (fp32 with
+ * K = V = 64).
+ */
+size_t kda_chunk_fwd_varlen_workspace_size(int N, int T_total, int H, int K, int V, kda_dtype dt);
+kda_status kda_chunk_fwd_varlen(int N, const int* cu_seqlens, int T_total, int H, int K, int V, kda_dtype dt,
+                                const void* q, const void* k, const void* v,
+                                const void* g, const void* beta,
+                                const float* initial_state,
+                                void* o, float* final_state,
+                                void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/*
  * One decode step for N independent sequences (page section "Как хранить
  * миллион токенов в памяти": the fixed-size state replaces the KV cache).
  * Reads and writes the state once.
@@ -158,7 +193,7 @@ kda_status kda_recurrent_step(int N, int H, int K, int V, kda_dtype dt,
  * kda_profile_stop waits for the recorded events, writes up to `cap` launch
  * names (static strings: "intra_chunk", "state_output", "state_summary",
  * "chunk_output", "chunk_summary", "segment_scan", "copy_state",
- * "decode_step") and durations in milliseconds, releases the
+ * "varlen_prep", "decode_step") and durations in milliseconds, releases the
  * events, and returns the number of timed launches (-1: profiling was not
  * started or a HIP event query failed).  The recording state is process-wide
  * and not thread-safe; profiling is off unless started.

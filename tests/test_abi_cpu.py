@@ -148,6 +148,42 @@ def test_profile_calls_validate_without_a_gpu():
     assert lib.kda_profile_start((1 << 20) + 1) == INVALID
 
 
+def _varlen(lib, N=3, cu=FAKE, T=300, H=2, K=128, V=128, dt=BF16, s0=None, sT=None, ws=FAKE, ws_bytes=1 << 40,
+            **kw):
+    p = ctypes.c_void_p
+    t = {n: kw.get(n, FAKE) for n in ("q", "k", "v", "g", "beta", "o")}
+    return lib.kda_chunk_fwd_varlen(N, p(cu) if cu else None, T, H, K, V, dt, *(p(t[n]) if t[n] else None for n in
+                                    ("q", "k", "v", "g", "beta")), p(s0) if s0 else None,
+                                    p(t["o"]) if t["o"] else None, p(sT) if sT else None, p(ws) if ws else None,
+                                    ws_bytes, None)
+
+
+def test_varlen_validation_before_any_launch():
+    lib = _lib()
+    assert _varlen(lib, N=-1) == INVALID
+    assert _varlen(lib, cu=None) == INVALID
+    assert _varlen(lib, cu=FAKE + 2) == INVALID                  # int32 alignment
+    assert _varlen(lib, K=96) == UNSUPPORTED
+    assert _varlen(lib, K=128, V=128, dt=F32) == UNSUPPORTED    # fp32 only at K = V = 64
+    assert _varlen(lib, q=None) == INVALID
+    assert _varlen(lib, o=FAKE + 8) == INVALID
+    assert _varlen(lib, s0=FAKE, sT=FAKE + 16) == INVALID        # partial state overlap
+    assert _varlen(lib, ws=None) == WORKSPACE
+    assert _varlen(lib, N=0) == OK                               # nothing to do
+    assert _varlen(lib, H=0) == OK
+
+
+def test_varlen_workspace_formula():
+    lib = _lib()
+    N, T, H = 5, 1000, 3
+    rec = 2 * (64 * 128 * 2 + 64 * 64 + 2 * 128 * 64) + 128 * 4
+    bound = -(-T // 64) + N                  # sum_i ceil(len_i / 64) <= ceil(T / 64) + N
+    offs = -(-(N + 1) * 4 // 256) * 256
+    assert lib.kda_chunk_fwd_varlen_workspace_size(N, T, H, 128, 128, BF16) == offs + H * bound * rec
+    assert lib.kda_chunk_fwd_varlen_workspace_size(-1, T, H, 128, 128, BF16) == ctypes.c_size_t(-1).value
+    assert _varlen(lib, N=N, T=T, H=H, ws_bytes=offs + H * bound * rec - 1) == WORKSPACE
+
+
 def test_package_raises_without_library(tmp_path):
     saved = K_._lib
     K_._lib = None

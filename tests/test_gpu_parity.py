@@ -306,6 +306,86 @@ def test_launch_profiling_names_every_launch():
     assert o_err(o, ref) < TOL[torch.bfloat16]
 
 
+# ------------------------------------------------------------------ packed variable-length batches
+def _packed(lengths, H, K, V, dtype, seed, s0_std=0.02):
+    """Per-sequence inputs of the recipe, packed along the token axis."""
+    seqs = [make_prefill(1, n, H, K, V, dtype, seed=seed + i, s0_std=s0_std) for i, n in enumerate(lengths)]
+    cat = lambda name: torch.cat([d[name][0] for d in seqs], 0)
+    packed = {n: cat(n) for n in ("q", "k", "v", "g", "beta")}
+    packed["s0"] = torch.cat([d["s0"] for d in seqs], 0) if s0_std is not None else None
+    cu = torch.tensor([0] + list(np.cumsum(lengths)), dtype=torch.int32)
+    return seqs, packed, cu
+
+
+VARLEN = [([0, 1, 63, 64, 65, 200, 7, 129], 3, 128, 128, torch.bfloat16),
+          ([130, 0, 5, 64], 2, 64, 128, torch.bfloat16),
+          ([70, 300, 1], 2, 128, 64, torch.bfloat16),
+          ([17, 64, 100, 0, 3], 2, 64, 64, torch.float32)]
+
+
+@pytest.mark.parametrize("lengths,H,K,V,dtype", VARLEN)
+def test_varlen_matches_oracle_and_single_calls(lengths, H, K, V, dtype):
+    """A packed batch equals the oracle per sequence, and equals (bit for
+    bit) one prefill call per sequence on the same two-pass plan."""
+    from gated_delta_rule_66_amd import chunk_fwd_varlen
+    say("varlen lengths=%s H=%d K=%d V=%d %s" % (lengths, H, K, V, dtype))
+    seqs, x, cu = _packed(lengths, H, K, V, dtype, seed=40)
+    xd = to_dev(x)
+    o, sT = chunk_fwd_varlen(xd["q"], xd["k"], xd["v"], xd["g"], xd["beta"], cu.to(DEV), xd["s0"])
+    torch.cuda.synchronize()
+    vb = 64     # few (sequence, head) chains: the library uses 64-column blocks
+    for i, (d, n) in enumerate(zip(seqs, lengths)):
+        a, e = int(cu[i]), int(cu[i + 1])
+        o_ref, s_ref = run_oracle(d)
+        if n:
+            assert o_err(o[a:e][None], o_ref) < TOL[dtype], i
+        assert s_err(sT[i:i + 1], s_ref) < TOL[dtype], i
+        one = to_dev(d)
+        o1, s1 = gpu_fwd(one, (1, vb, 2))
+        torch.cuda.synchronize()
+        assert torch.equal(o[a:e], o1[0]) and torch.equal(sT[i:i + 1], s1), i
+
+
+def test_varlen_in_place_and_empty():
+    from gated_delta_rule_66_amd import chunk_fwd_varlen
+    say("varlen: final state in place; all sequences empty")
+    seqs, x, cu = _packed([100, 0, 65], 2, 128, 128, torch.bfloat16, seed=50)
+    xd = to_dev(x)
+    state = xd["s0"].clone()
+    o, s = chunk_fwd_varlen(xd["q"], xd["k"], xd["v"], xd["g"], xd["beta"], cu.to(DEV), state, final_state=state)
+    torch.cuda.synchronize()
+    assert s.data_ptr() == state.data_ptr()
+    for i, d in enumerate(seqs):
+        _, s_ref = run_oracle(d)
+        assert s_err(state[i:i + 1], s_ref) < TOL[torch.bfloat16], i
+    # T_total = 0: every final state is its initial state
+    z = {n: t[:0].contiguous() for n, t in xd.items() if n != "s0"}
+    cu0 = torch.zeros(4, dtype=torch.int32, device=DEV)
+    s0 = torch.randn(3, 2, 128, 128, device=DEV)
+    o0, s_out = chunk_fwd_varlen(z["q"], z["k"], z["v"], z["g"], z["beta"], cu0, s0)
+    torch.cuda.synchronize()
+    assert o0.shape == (0, 2, 128) and torch.equal(s_out, s0)
+
+
+def test_varlen_many_sequences_sampled():
+    """A serving-size packed batch (64 sequences of mixed length, 32 heads)
+    on the library's own plan, checked on sampled sequences."""
+    from gated_delta_rule_66_amd import chunk_fwd_varlen
+    gen = torch.Generator().manual_seed(60)
+    lengths = torch.randint(0, 900, (64,), generator=gen).tolist()
+    say("varlen 64 sequences, total %d tokens, H=32" % sum(lengths))
+    seqs, x, cu = _packed(lengths, 32, 128, 128, torch.bfloat16, seed=61)
+    xd = to_dev(x)
+    o, sT = chunk_fwd_varlen(xd["q"], xd["k"], xd["v"], xd["g"], xd["beta"], cu.to(DEV), xd["s0"])
+    torch.cuda.synchronize()
+    for i in (0, 17, 42, 63):
+        a, e = int(cu[i]), int(cu[i + 1])
+        o_ref, s_ref = run_oracle(seqs[i])
+        if e > a:
+            assert o_err(o[a:e][None], o_ref) < TOL[torch.bfloat16], i
+        assert s_err(sT[i:i + 1], s_ref) < TOL[torch.bfloat16], i
+
+
 # ------------------------------------------------------------------ decode
 @pytest.mark.parametrize("dtype,K,V", [(torch.bfloat16, 128, 128), (torch.bfloat16, 64, 128),
                                        (torch.bfloat16, 128, 64), (torch.float32, 64, 64),
