@@ -234,6 +234,35 @@ def main():
             }
             del xe, oe, se, wse
             torch.cuda.empty_cache()
+        # packed variable-length batch: 256 sequences of lengths drawn
+        # uniformly from [1, 2048], 32 heads, K = V = 128, per-sequence states
+        gen = torch.Generator().manual_seed(7)
+        lengths = torch.randint(1, 2049, (256,), generator=gen)
+        cu = torch.zeros(257, dtype=torch.int32)
+        cu[1:] = torch.cumsum(lengths, 0).to(torch.int32)
+        Tt, Hv = int(cu[-1]), 32
+        xv = make_prefill_config(CONFIGS["c1"], dev, T=Tt, B=1, H=Hv)
+        sq = lambda t: t[0]
+        s0v = torch.zeros((256, Hv, 128, 128), dtype=torch.float32, device=dev)
+        ov = torch.empty((Tt, Hv, 128), dtype=torch.bfloat16, device=dev)
+        sv = torch.empty_like(s0v)
+        wsv = torch.empty(kda.chunk_fwd_varlen_workspace_size(256, Tt, Hv, 128, 128, torch.bfloat16),
+                          dtype=torch.uint8, device=dev)
+        cud = cu.to(dev)
+        fnv = lambda: kda.chunk_fwd_varlen(sq(xv["q"]), sq(xv["k"]), sq(xv["v"]), sq(xv["g"]), sq(xv["beta"]),
+                                           cud, s0v, out=ov, final_state=sv, workspace=wsv)
+        msv = time_calls(fnv, 2, 5)
+        nbv = prefill_bytes(1, Tt, Hv, 128, 128, 2, s0=True, final=True) + 256 * Hv * 128 * 128 * 8 - \
+            Hv * 128 * 128 * 8
+        extra["varlen"] = {
+            "workload": "packed batch of 256 sequences, lengths U[1, 2048] (%d tokens), H=32, K=V=128 bf16, "
+                        "per-sequence initial and final states" % Tt,
+            "ms": round(msv, 4),
+            "tokens_per_s": Tt / (msv * 1e-3),
+            "hbm_frac": nbv / (msv * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        }
+        del xv, s0v, ov, sv, wsv
+        torch.cuda.empty_cache()
 
     # ------------------------------------------------------------ CPU oracle baseline
     cpu = None
