@@ -137,6 +137,14 @@ template <> __device__ __forceinline__ f32x8 ld_frag_perm<float>(const float* p)
 }
 
 // 8 consecutive fp32 values from LDS (16-byte aligned)
+// The value unchanged, hidden from the optimiser: index arithmetic derived
+// from it is redone where it is used instead of being hoisted out of a
+// persistent loop and kept live (or spilled) across the whole body.
+__device__ __forceinline__ int opaque(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
 __device__ __forceinline__ void ld8f(const float* p, float* x) {
     f32x4 a = *reinterpret_cast<const f32x4*>(p);
     f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);

@@ -82,38 +82,59 @@ __device__ __forceinline__ void st4(float* p, const float* x) {
 // ============================================================================
 // Intra-chunk pass
 // ============================================================================
+// Eight waves; wave w prepares tokens [8w, 8w + 8) of the chunk, so that each
+// load instruction reads whole rows (CG lanes x 16 bytes per token row) of
+// q, k, g and v.  The per-channel gate cumsum crosses waves through a small
+// LDS table of wave totals.  Outputs leave as whole rows too: Q e^{G} straight
+// from registers, everything else staged in LDS.
+// The channel-major [channel][token] LDS arrays of the intra-chunk pass keep
+// token t of channel row r at column t ^ (8 ((r >> 4) & 7)): 8-token units
+// are permuted per 16-row group, so that the column-wise writes of the
+// preparation phase (lanes on rows 8 apart) spread over all LDS banks while
+// 4- and 8-token runs stay contiguous.
+__device__ __forceinline__ int swz_t(int r, int t) { return t ^ (((r >> 4) & 7) << 3); }
+
 template <typename T, int K, int V>
 struct IntraLayout {
     static constexpr int NW = 8;                 // waves
     static constexpr int NT = 64 * NW;
+    static constexpr int TPW = C / NW;           // tokens per wave (8)
     static constexpr int SZ = (int)sizeof(T);
     static constexpr int PAD = 16 / SZ;
     static constexpr int LDK1 = K + PAD;         // Kd, Qd, Kinv, W: [token][channel]
     static constexpr int LDT = C + PAD;          // [channel][token]
     static constexpr int LDL = C + 4;            // solve blocks / Mqk
     static constexpr int LDD = 16;
-    // prep: wave w owns CPW groups of 8 key channels (TPL tokens per lane) and
-    // CPWV groups of 8 value columns (TPLV tokens per lane)
-    static constexpr int CPW = K / (8 * NW);
-    static constexpr int TPL = CPW;
-    static constexpr int NPART = 64 / CPW;
-    static constexpr int CPWV = V / (8 * NW);
-    static constexpr int TPLV = CPWV;
+    // key side: CG lanes of 8 channels per token row, RPI rows per
+    // instruction, TPL consecutive tokens per lane; value side likewise
+    static constexpr int CG = K / 8, RPI = 64 / CG, TPL = TPW / RPI;
+    static constexpr int CGV = V / 8, RPIV = 64 / CGV, TPLV = TPW / RPIV;
     static constexpr int CT = K / 16, NVT = V / 16;
     static constexpr int KQ = 3 * C * LDK1 * SZ;         // Kd | Qd | Kinv, then W staging
     static constexpr int L_BYTES = C * LDL * SZ;
     static constexpr int R = L_BYTES + 4 * 16 * LDD * 4;
     static constexpr int oKQ = 0;
-    static constexpr int oR = oKQ + KQ;                  // solve blocks | fp32 diagonal blocks of A
+    static constexpr int oR = oKQ + KQ;                  // solve blocks | fp32 diagonal blocks of A (transposed)
     static constexpr int oMqk = oR + R;
     static constexpr int oKhbT = oMqk + C * LDL * SZ;    // [K][LDT] beta K e^{G}
-    static constexpr int oVbT = oKhbT + K * LDT * SZ;    // [V][LDT] beta V
-    static constexpr int oF = oVbT + V * LDT * SZ;       // fp32 [6][K]
-    static constexpr int oBeta = oF + 6 * K * 4;         // fp32 [C]
+    static constexpr int oVbT = oKhbT + K * LDT * SZ;    // [V][LDT] beta V, then U~^T
+    static constexpr int oKbT = oVbT + V * LDT * SZ;     // [K][LDT] (K e^{G_C-G})^T
+    static constexpr int oF = oKbT + K * LDT * SZ;       // fp32 [7][K] e^{G_b(i) - G_b(j)}; row 6: ones
+    static constexpr int oWT = oF + 7 * K * 4;           // fp32 [NW][K] wave totals of clamped gates
+    static constexpr int oG0 = oWT + NW * K * 4;         // fp32 [NW][K] first token's clamped gate
+    static constexpr int oBeta = oG0 + NW * K * 4;       // fp32 [C]
     static constexpr int TOTAL = oBeta + C * 4;
+    // per-channel table of the preparation phase, over the solve blocks (free
+    // until P2): exclusive prefix before each wave [NW][K], then G_b, e^{G_b},
+    // e^{G_C - G_b} of each block [4][K] each
+    static constexpr int oTab = oR;
+    static constexpr int TAB = (NW + 12) * K * 4;
     static_assert(TOTAL <= 160 * 1024, "LDS budget exceeded");
-    static_assert(CPW * 8 * NW == K && (CPW == 1 || CPW == 2 || CPW == 4), "key prep mapping");
-    static_assert(CPWV * 8 * NW == V && (CPWV == 1 || CPWV == 2 || CPWV == 4), "value prep mapping");
+    static_assert(TAB <= R, "prefix table must fit the solve-block region");
+    static_assert(NT % K == 0, "whole threads per channel in the prefix table");
+    static_assert(CG * RPI == 64 && RPI * TPL == TPW && TPL >= 1, "key prep mapping");
+    static_assert(CGV * RPIV == 64 && RPIV * TPLV == TPW && TPLV >= 1, "value prep mapping");
+    static_assert(TPW * NW == C && TPW == 8, "two waves per 16-token block");
 };
 
 template <typename T, int K, int V>
@@ -122,8 +143,7 @@ __global__ __launch_bounds__(512) void kda_intra_kernel(IntraParams p) {
     constexpr int NW = L::NW, NT = L::NT;
     using Frag4 = typename Frag4Of<T>::type;
     constexpr int LDK1 = L::LDK1, LDT = L::LDT, LDL = L::LDL, LDD = L::LDD;
-    constexpr int CPW = L::CPW, TPL = L::TPL, NPART = L::NPART;
-    constexpr int CPWV = L::CPWV, TPLV = L::TPLV;
+    constexpr int CG = L::CG, TPL = L::TPL, CGV = L::CGV, TPLV = L::TPLV;
     constexpr int CT = L::CT, NVT = L::NVT;
     constexpr int KS = K / 32;
     constexpr unsigned SZ = sizeof(T);
@@ -139,11 +159,17 @@ __global__ __launch_bounds__(512) void kda_intra_kernel(IntraParams p) {
     T* sMqk = reinterpret_cast<T*>(smem + L::oMqk);
     T* sKhbT = reinterpret_cast<T*>(smem + L::oKhbT);
     T* sVbT = reinterpret_cast<T*>(smem + L::oVbT);
+    T* sKbT = reinterpret_cast<T*>(smem + L::oKbT);
     float* sF = reinterpret_cast<float*>(smem + L::oF);
+    float* sWT = reinterpret_cast<float*>(smem + L::oWT);
+    float* sG0 = reinterpret_cast<float*>(smem + L::oG0);
     float* sBeta = reinterpret_cast<float*>(smem + L::oBeta);
+    float* tPre = reinterpret_cast<float*>(smem + L::oTab);
+    float* tGb = tPre + NW * K;
+    float* tEgb = tGb + 4 * K;
+    float* tEcb = tEgb + 4 * K;
 
-    const int tid = threadIdx.x;
-    const int w = tid >> 6, l = tid & 63, lg = l >> 4, lr = l & 15;
+    const int w0 = threadIdx.x >> 6, l0 = threadIdx.x & 63;
 
     const T* __restrict__ qg = reinterpret_cast<const T*>(p.q);
     const T* __restrict__ kg = reinterpret_cast<const T*>(p.k);
@@ -151,25 +177,24 @@ __global__ __launch_bounds__(512) void kda_intra_kernel(IntraParams p) {
     const T* __restrict__ gg = reinterpret_cast<const T*>(p.g);
     const T* __restrict__ bg = reinterpret_cast<const T*>(p.beta);
 
-    const int c8l = l % CPW, part = l / CPW;
-    const int c0 = 8 * (CPW * w + c8l);
-    const int n8l = l % CPWV, pv = l / CPWV;
-    const int n0 = 8 * (CPWV * w + n8l);
+    // lane roles: key side channels [c0, c0 + 8) of tokens t1 .. t1 + TPL - 1;
+    // value side columns [n0, n0 + 8) of tokens tv .. tv + TPLV - 1
+    const int t1_ = L::TPW * w0 + TPL * (l0 / CG), tv_ = L::TPW * w0 + TPLV * (l0 / CGV);
 
+    // beta: lane l < 8 of wave w holds that of token 8 w + l
     Pack8<T> kr[TPL], qr[TPL], gr[TPL], vr[TPLV];
-    T br[TPL], bvr[TPLV];
+    T bw;
     const unsigned rowK = (unsigned)p.H * K * SZ, rowV = (unsigned)p.H * V * SZ, rowB = (unsigned)p.H * SZ;
-    const unsigned vK = (unsigned)part * TPL * rowK + (unsigned)c0 * SZ;
-    const unsigned vB = (unsigned)part * TPL * rowB;
-    const unsigned vV = (unsigned)pv * TPLV * rowV + (unsigned)n0 * SZ;
-    const unsigned vBV = (unsigned)pv * TPLV * rowB;
-    auto load_item = [&](int item) {
-        int t0, nt;
-        size_t head_row;
+    const unsigned vK = (unsigned)t1_ * rowK + (unsigned)(8 * (l0 % CG)) * SZ;
+    const unsigned vV = (unsigned)tv_ * rowV + (unsigned)(8 * (l0 % CGV)) * SZ;
+    const int tb_ = L::TPW * w0 + l0;
+    const unsigned vB = (unsigned)tb_ * rowB;
+    // where an item's tokens are: first [T][H] row of head h and the number of tokens
+    auto locate = [&](int item, size_t& head_row, int& nt) {
         if (p.cu_seqlens) {
             // packed batch: item = h * NC + global chunk; find its sequence
             const int h = item / p.NC, gc = item - h * p.NC;
-            t0 = 0;
+            int t0 = 0;
             nt = 0;
             if (gc < p.chunk_off[p.N]) {
                 int lo = 0, hi = p.N;              // chunk_off[lo] <= gc < chunk_off[hi]
@@ -186,69 +211,92 @@ __global__ __launch_bounds__(512) void kda_intra_kernel(IntraParams p) {
         } else {
             const int bh = item / p.NC, ci = item - bh * p.NC;
             const int b = bh / p.H, h = bh - b * p.H;
-            t0 = ci * C;
+            const int t0 = ci * C;
             nt = min(C, p.T - t0);
             head_row = (size_t)(b * (size_t)p.T + t0) * p.H + h;
         }
+    };
+    // the loads of an item: gates and keys, queries, values and beta
+    auto load_gk = [&](size_t head_row, int nt) {
         const __amdgpu_buffer_rsrc_t rk = make_rsrc(kg + head_row * K);
-        const __amdgpu_buffer_rsrc_t rq = make_rsrc(qg + head_row * K);
         const __amdgpu_buffer_rsrc_t rg = make_rsrc(gg + head_row * K);
-        const __amdgpu_buffer_rsrc_t rb = make_rsrc(bg + head_row);
-        const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + head_row * V);
 #pragma unroll
         for (int i = 0; i < TPL; ++i) {
-            if (part * TPL + i < nt) {
-                buf_load8<T>(kr[i], rk, vK, i * rowK);
+            if (t1_ + i < nt) {
                 buf_load8<T>(gr[i], rg, vK, i * rowK);
-                buf_load8<T>(qr[i], rq, vK, i * rowK);
-                buf_load1(br[i], rb, vB, i * rowB);
+                buf_load8<T>(kr[i], rk, vK, i * rowK);
             } else {
-                kr[i].zero();
                 gr[i].zero();
-                qr[i].zero();
-                br[i] = from_f32<T>(0.f);
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < TPLV; ++i) {
-            if (pv * TPLV + i < nt) {
-                buf_load8<T>(vr[i], rv, vV, i * rowV);
-                buf_load1(bvr[i], rb, vBV, i * rowB);
-            } else {
-                vr[i].zero();
-                bvr[i] = from_f32<T>(0.f);
+                kr[i].zero();
             }
         }
     };
+    auto load_q = [&](size_t head_row, int nt) {
+        const __amdgpu_buffer_rsrc_t rq = make_rsrc(qg + head_row * K);
+#pragma unroll
+        for (int i = 0; i < TPL; ++i) {
+            if (t1_ + i < nt) buf_load8<T>(qr[i], rq, vK, i * rowK);
+            else qr[i].zero();
+        }
+    };
+    auto load_vb = [&](size_t head_row, int nt) {
+        const __amdgpu_buffer_rsrc_t rv = make_rsrc(vg + head_row * V);
+        const __amdgpu_buffer_rsrc_t rb = make_rsrc(bg + head_row);
+#pragma unroll
+        for (int i = 0; i < TPLV; ++i) {
+            if (tv_ + i < nt) buf_load8<T>(vr[i], rv, vV, i * rowV);
+            else vr[i].zero();
+        }
+        if (l0 < L::TPW && tb_ < nt) buf_load1(bw, rb, vB, 0u);
+        else bw = from_f32<T>(0.f);
+    };
 
     const int G = gridDim.x;
-    if ((int)blockIdx.x < p.n_items) load_item(blockIdx.x);
+    // the row of ones of sF (scale of the diagonal block pairs)
+    for (int c = threadIdx.x; c < K; c += NT) sF[6 * K + c] = 1.f;
+    size_t nrow = 0;
+    int nnt = 0;
+    if ((int)blockIdx.x < p.n_items) {
+        locate(blockIdx.x, nrow, nnt);
+        load_gk(nrow, nnt);
+        load_q(nrow, nnt);
+        load_vb(nrow, nnt);
+    }
 
     for (int item = blockIdx.x; item < p.n_items; item += G) {
         unsigned char* rec = p.rec + (size_t)item * RL.bytes;
-        T* gW = reinterpret_cast<T*>(rec + RL.oW);
-        T* gQh = reinterpret_cast<T*>(rec + RL.oQh);
-        T* gMqk = reinterpret_cast<T*>(rec + RL.oMqk);
-        T* gKbT = reinterpret_cast<T*>(rec + RL.oKbT);
-        T* gUtT = reinterpret_cast<T*>(rec + RL.oUtT);
-        float* gEgc = reinterpret_cast<float*>(rec + RL.oEgc);
         const __amdgpu_buffer_rsrc_t rrec = make_rsrc(rec);
+        // lane indices redone per item (opaque() keeps the index arithmetic
+        // derived from them out of the loop preheader)
+        const int tid = opaque((int)threadIdx.x);
+        const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, lg = l >> 4, lr = l & 15;
+        const int c0 = 8 * (l % CG), t1 = L::TPW * w + TPL * (l / CG);
+        const int n0 = 8 * (l % CGV), tv = L::TPW * w + TPLV * (l / CGV);
 
-        // ---- P1: gate cumsum; key / query side to LDS, Qh, KbT, e^{G_C} out ----
+        // ---- P1a: clamped log gates, in-lane and in-wave inclusive sums ----------
+        float run[8], tot[8];
+        float c[TPL][8];                             // clamped log2 gates, reused in P1b
         {
-            float G[TPL][8];
 #pragma unroll
             for (int i = 0; i < TPL; ++i) {
                 float g8[8];
                 gr[i].to_f32(g8);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) G[i][e] = (i ? G[i - 1][e] : 0.f) + clamp_gate_log2(g8[e]);
+                for (int e = 0; e < 8; ++e) c[i][e] = clamp_gate_log2(g8[e]);
             }
-            float incl[8], gfirst[8], gb[8], gcum[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) incl[e] = G[TPL - 1][e];
+            for (int e = 0; e < 8; ++e) {
+                float s = 0.f;
 #pragma unroll
-            for (int d = CPW; d < 64; d <<= 1) {
+                for (int i = 0; i < TPL; ++i) s += c[i][e];
+                tot[e] = s;
+            }
+            // scan over the lanes holding the same channels (token order)
+            float incl[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) incl[e] = tot[e];
+#pragma unroll
+            for (int d = CG; d < 64; d <<= 1) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const float y = __shfl_up(incl[e], d);
@@ -256,209 +304,240 @@ __global__ __launch_bounds__(512) void kda_intra_kernel(IntraParams p) {
                 }
             }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float excl = incl[e] - G[TPL - 1][e];
-#pragma unroll
-                for (int i = 0; i < TPL; ++i) G[i][e] += excl;
-                gfirst[e] = G[0][e];
-                gcum[e] = __shfl(incl[e], (NPART - 1) * CPW + c8l);
+            for (int e = 0; e < 8; ++e) run[e] = incl[e] - tot[e];   // in-wave sum before this lane's tokens
+            // wave totals (last lanes) and the wave's first-token gates (first lanes)
+            if (l >= 64 - CG) {
+                st8(&sWT[w * K + c0], incl);
             }
-            const int myblk = (part * TPL) >> 4;
-            int pi_ = 1, pj_ = 0;
-            if (part < 6) offdiag_pair(part, pi_, pj_);
-            const int src_b = (16 * myblk / TPL) * CPW + c8l;
-            const int src_i = (16 * pi_ / TPL) * CPW + c8l;
-            const int src_j = (16 * pj_ / TPL) * CPW + c8l;
-            float f[8];
+            if (l < CG) {
+                float c0v[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                gb[e] = __shfl(gfirst[e], src_b);
-                f[e] = fast_exp2(__shfl(gfirst[e], src_i) - __shfl(gfirst[e], src_j));
+                for (int e = 0; e < 8; ++e) c0v[e] = c[0][e];
+                st8(&sG0[w * K + c0], c0v);
             }
-            if (part < 6) st8(&sF[part * K + c0], f);
-            if (part == 0) {
-                float ec[8];
+            if (l < L::TPW) sBeta[L::TPW * w + l] = to_f32(bw);
+        }
+        __syncthreads();
+
+        // ---- P1t: per-channel table (prefix over waves, block references, factors) --
+        {
+            constexpr int P = NT / K;                     // threads per channel
+            const int ch = tid % K, part = tid / K;
+            float pfx[NW + 1];                            // pfx[v]: sum of the totals of waves < v
+            pfx[0] = 0.f;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) ec[e] = fast_exp2(gcum[e]);
-                const float4 a4 = make_float4(ec[0], ec[1], ec[2], ec[3]);
-                const float4 b4 = make_float4(ec[4], ec[5], ec[6], ec[7]);
-                buf_store16(rrec, (unsigned)RL.oEgc + (unsigned)c0 * 4u, 0u, *reinterpret_cast<const uint4*>(&a4));
-                buf_store16(rrec, (unsigned)RL.oEgc + (unsigned)c0 * 4u + 16u, 0u, *reinterpret_cast<const uint4*>(&b4));
-            }
-            if (w == 0 && c8l == 0) {
+            for (int v = 0; v < NW; ++v) pfx[v + 1] = pfx[v] + sWT[v * K + ch];
 #pragma unroll
-                for (int i = 0; i < TPL; ++i) sBeta[part * TPL + i] = to_f32(br[i]);
-            }
-            float egb[8], ecb[8];
+            for (int v = 0; v < NW; ++v)
+                if (v % P == part) tPre[v * K + ch] = pfx[v];
+            // G_b: G at the first token of block b (the first token of wave 2 b)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                egb[e] = fast_exp2(gb[e]);
-                ecb[e] = fast_exp2(gcum[e] - gb[e]);
+            for (int b = 0; b < 4; ++b)
+                if (b % P == part) {
+                    const float gbv = pfx[2 * b] + sG0[2 * b * K + ch];
+                    tGb[b * K + ch] = gbv;
+                    tEgb[b * K + ch] = fast_exp2(gbv);                 // e^{G_b}       <= 1
+                    tEcb[b * K + ch] = fast_exp2(pfx[NW] - gbv);       // e^{G_C - G_b} <= 1
+                }
+            // e^{G_b(i) - G_b(j)} of the six off-diagonal block pairs
+#pragma unroll
+            for (int f = 0; f < 6; ++f)
+                if (f % P == part) {
+                    int bi, bj;
+                    offdiag_pair(f, bi, bj);
+                    const float gi = pfx[2 * bi] + sG0[2 * bi * K + ch];
+                    const float gj = pfx[2 * bj] + sG0[2 * bj * K + ch];
+                    sF[f * K + ch] = fast_exp2(gi - gj);
+                }
+            if (part == P - 1) buf_store1(rrec, (unsigned)RL.oEgc + (unsigned)ch * 4u, 0u, fast_exp2(pfx[NW]));
+        }
+        __syncthreads();
+
+        // ---- P1b: operands ---------------------------------------------------------------
+        {
+            // value side first, which frees its registers
+            {
+                float bv[8][TPLV];
+#pragma unroll
+                for (int i = 0; i < TPLV; ++i) {
+                    float vx[8];
+                    vr[i].to_f32(vx);
+                    const float bt = sBeta[tv + i];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) bv[e][i] = bt * vx[e];
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) st_small<TPLV>(&sVbT[(n0 + e) * LDT + swz_t(n0 + e, tv)], bv[e]);
             }
+            float pre[8], gb[8], egb[8], ecb[8];
+            const int myblk = w >> 1;
+            ld8f(&tPre[w * K + c0], pre);
+            ld8f(&tGb[myblk * K + c0], gb);
+            ld8f(&tEgb[myblk * K + c0], egb);
+            ld8f(&tEcb[myblk * K + c0], ecb);
             float kh[8][TPL], kb[8][TPL];
 #pragma unroll
             for (int i = 0; i < TPL; ++i) {
-                const int t = part * TPL + i;
-                float kx[8], kd[8], ki[8];
+                const int t = t1 + i;
+                float kx[8], qx[8], kd[8], ki[8], qd[8], qh[8];
                 kr[i].to_f32(kx);
-                const float bt = to_f32(br[i]);
+                qr[i].to_f32(qx);
+                const float bt = sBeta[t1 + i];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const float d = G[i][e] - gb[e];
-                    const float e1 = fast_exp2(d);
-                    const float e2 = fast_exp2(-d);
+                    run[e] += c[i][e];
+                    const float d = pre[e] + run[e] - gb[e];   // G_t - G_b in [-108, 0] (log2)
+                    const float e1 = fast_exp2(d);             // e^{G_t - G_b} <= 1
+                    const float e2 = fast_exp2(-d);            // e^{G_b - G_t} <= e^75
                     kd[e] = kx[e] * e1;
                     ki[e] = kx[e] * e2;
-                    kh[e][i] = bt * kd[e] * egb[e];
-                    kb[e][i] = ki[e] * ecb[e];
+                    kh[e][i] = bt * kd[e] * egb[e];            // beta k e^{G_t}
+                    kb[e][i] = ki[e] * ecb[e];                 // k e^{G_C - G_t}
+                    qd[e] = qx[e] * e1;                        // q e^{G_t - G_b}
+                    qh[e] = qd[e] * egb[e];                    // q e^{G_t}
                 }
                 st8(&sKd[t * LDK1 + c0], kd);
                 st8(&sKinv[t * LDK1 + c0], ki);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int i = 0; i < TPL; ++i) {
-                const int t = part * TPL + i;
-                float qx[8], qd[8], qh[8];
-                qr[i].to_f32(qx);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    qd[e] = qx[e] * fast_exp2(G[i][e] - gb[e]);
-                    qh[e] = qd[e] * egb[e];
-                }
                 st8(&sQd[t * LDK1 + c0], qd);
+                // Q e^{G}: CG lanes write one whole token row
                 if constexpr (sizeof(T) == 2) {
                     const auto qf = frag_from<T>(qh);
-                    buf_store16(rrec, (unsigned)RL.oQh + (unsigned)(t * K + c0) * SZ, 0u, *reinterpret_cast<const uint4*>(&qf));
+                    buf_store16(rrec, (unsigned)RL.oQh + (unsigned)(t * K + c0) * SZ, 0u,
+                                *reinterpret_cast<const uint4*>(&qf));
                 } else {
-                    st8(&gQh[t * K + c0], qh);
+                    buf_store16(rrec, (unsigned)RL.oQh + (unsigned)(t * K + c0) * SZ, 0u,
+                                *reinterpret_cast<const uint4*>(&qh[0]));
+                    buf_store16(rrec, (unsigned)RL.oQh + (unsigned)(t * K + c0) * SZ + 16u, 0u,
+                                *reinterpret_cast<const uint4*>(&qh[4]));
                 }
             }
-            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                st_small<TPL>(&sKhbT[(c0 + e) * LDT + part * TPL], kh[e]);
-                if constexpr (sizeof(T) == 2 && TPL == 2) {
-                    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
-                    b2 r; r[0] = (bf16)kb[e][0]; r[1] = (bf16)kb[e][1];
-                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, r), rrec, (int)((unsigned)RL.oKbT + (unsigned)((c0 + e) * C + part * TPL) * SZ), 0, 0);
-                } else {
-                    st_small<TPL>(&gKbT[(c0 + e) * C + part * TPL], kb[e]);
-                }
+                st_small<TPL>(&sKhbT[(c0 + e) * LDT + swz_t(c0 + e, t1)], kh[e]);
+                st_small<TPL>(&sKbT[(c0 + e) * LDT + swz_t(c0 + e, t1)], kb[e]);
             }
-            float bv[8][TPLV];
-#pragma unroll
-            for (int i = 0; i < TPLV; ++i) {
-                float vx[8];
-                vr[i].to_f32(vx);
-                const float bt = to_f32(bvr[i]);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) bv[e][i] = bt * vx[e];
-            }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) st_small<TPLV>(&sVbT[(n0 + e) * LDT + pv * TPLV], bv[e]);
         }
         __syncthreads();
 
         // the raw registers are free: fetch the next item behind P2 / P3
         __builtin_amdgcn_sched_barrier(0);
-        if (item + G < p.n_items) load_item(item + G);
+        if (item + G < p.n_items) {
+            locate(item + G, nrow, nnt);
+            load_gk(nrow, nnt);
+            load_q(nrow, nnt);
+            load_vb(nrow, nnt);
+        }
         __builtin_amdgcn_sched_barrier(0);
 
         // ---- P2: diagonal blocks of A and their inverses; off-diagonal A; Mqk ----
-        // waves 0-3: diagonal block w, then task w; waves 4-7: tasks w, w+4, ...
-        // tasks 0-5: off-diagonal blocks of -A (into the solve buffer); 6-15:
-        // blocks of Mqk; 16, 17: the zero blocks (0,1), (2,3) of Mqk
-        if (w < 4) {
-            const int i = w;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        // wave 0: the four diagonal blocks and their inverses, and the zero
+        // blocks of Mqk; waves 1-7: the off-diagonal blocks of A and the lower
+        // blocks of Mqk
+        if (w == 0) {
+            // A_ii, transposed into sAd: sAd[i][m][r] = A_ii[r][m]
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                acc = mma(acc, ld_frag<T>(&sKd[(16 * i + lr) * LDK1 + 32 * ks + 8 * lg]),
-                          ld_frag<T>(&sKinv[(16 * i + lr) * LDK1 + 32 * ks + 8 * lg]));
-            float* Ad = sAd + i * 16 * LDD;
-            const f32x4 bt = *reinterpret_cast<const f32x4*>(&sBeta[16 * i + 4 * lg]);
+            for (int i = 0; i < 4; ++i) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int s_ = 4 * lg + e;
-                Ad[s_ * LDD + lr] = (lr < s_) ? bt[e] * acc[e] : 0.f;
+                for (int ks = 0; ks < KS; ++ks)
+                    acc = mma(acc, ld_frag<T>(&sKd[(16 * i + lr) * LDK1 + 32 * ks + 8 * lg]),
+                              ld_frag<T>(&sKinv[(16 * i + lr) * LDK1 + 32 * ks + 8 * lg]));
+                const f32x4 bt = *reinterpret_cast<const f32x4*>(&sBeta[16 * i + 4 * lg]);
+                f32x4 a4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) a4[e] = (lr < 4 * lg + e) ? bt[e] * acc[e] : 0.f;
+                *reinterpret_cast<f32x4*>(&sAd[(i * 16 + lr) * LDD + 4 * lg]) = a4;
             }
             wave_lds_sync();
-            if (lg == 0) {
-                // column lr of (I + A_ii)^{-1} by forward substitution
-                const int j = lr;
-                float xv[16];
+            // lane (block lg, column lr) of (I + A_ii)^{-1} by right-looking
+            // forward substitution: when x[m] is final, remove its part from
+            // every later row
+            const float* At = sAd + lg * 16 * LDD;
+            float x[16];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float row[16];
+            for (int r = 0; r < 16; ++r) x[r] = (r == lr) ? 1.f : 0.f;
 #pragma unroll
-                    for (int m4 = 0; m4 < 4; ++m4) {
-                        const f32x4 a4 = *reinterpret_cast<const f32x4*>(&Ad[r * LDD + 4 * m4]);
-                        row[4 * m4] = a4[0];
-                        row[4 * m4 + 1] = a4[1];
-                        row[4 * m4 + 2] = a4[2];
-                        row[4 * m4 + 3] = a4[3];
-                    }
-                    float a = (r == j) ? 1.f : 0.f;
+            for (int m = 0; m < 15; ++m) {
+                float col[16];
 #pragma unroll
-                    for (int m = 0; m < r; ++m) a -= row[m] * xv[m];
-                    xv[r] = a;
+                for (int q4 = m / 4; q4 < 4; ++q4) {
+                    const f32x4 c4 = *reinterpret_cast<const f32x4*>(&At[m * LDD + 4 * q4]);
+                    col[4 * q4] = c4[0];
+                    col[4 * q4 + 1] = c4[1];
+                    col[4 * q4 + 2] = c4[2];
+                    col[4 * q4 + 3] = c4[3];
                 }
 #pragma unroll
-                for (int r = 0; r < 16; ++r) sL[(16 * i + r) * LDL + 16 * i + j] = from_f32<T>(xv[r]);
+                for (int r = m + 1; r < 16; ++r) x[r] -= col[r] * x[m];
             }
-        }
-        {
-            constexpr int NTASK = 18;
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const int task = (w < 4) ? (m == 0 ? w : NTASK) : w + 4 * m;
-                if (task < NTASK) {
-                    if (task < 16) {
-                        int i, j;
-                        if (task < 6) offdiag_pair(task, i, j);
-                        else lower_pair(task - 6, i, j);
-                        const T* rowsrc = (task < 6) ? sKd : sQd;
-                        typename FragOf<T>::type fa[KS], fb[KS];
+            for (int r = 0; r < 16; ++r) sL[(16 * lg + r) * LDL + 16 * lg + lr] = from_f32<T>(x[r]);
+            // the blocks of Mqk above the diagonal are zero
 #pragma unroll
-                        for (int ks = 0; ks < KS; ++ks) {
-                            const int cc = 32 * ks + 8 * lg;
-                            fa[ks] = ld_frag<T>(&rowsrc[(16 * i + lr) * LDK1 + cc]);
-                            fb[ks] = col_frag<T, LDK1, K>(sKinv, sF, i, j, lr, cc);
-                        }
-                        const f32x4 bt = *reinterpret_cast<const f32x4*>(&sBeta[16 * i + 4 * lg]);
-                        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int q = 0; q < 6; ++q) {
+                const int i = (q < 3) ? 0 : (q < 5) ? 1 : 2;
+                const int j = (q < 3) ? q + 1 : (q < 5) ? q - 1 : 3;
 #pragma unroll
-                        for (int ks = 0; ks < KS; ++ks) acc = mma(acc, fa[ks], fb[ks]);
-                        const int r = 16 * j + lr;
+                for (int e = 0; e < 4; ++e) sMqk[(16 * i + 4 * lg + e) * LDL + 16 * j + lr] = from_f32<T>(0.f);
+            }
+        } else {
+            // the sixteen blocks over waves 1-7, two or three each (tasks 0-5:
+            // off-diagonal blocks of -A, into the solve buffer; 6-15: blocks of
+            // Mqk); every task runs branch-free: a diagonal pair scales by the
+            // row of ones in sF, so that the scheduler can overlap a wave's tasks
+            auto task_ops = [&](int task, typename FragOf<T>::type (&fa)[KS], typename FragOf<T>::type (&fb)[KS]) {
+                int i, j;
+                if (task < 6) offdiag_pair(task, i, j);
+                else lower_pair(task - 6, i, j);
+                const T* rowsrc = (task < 6) ? sKd : sQd;
+                const int frow = (i == j) ? 6 : i * (i - 1) / 2 + j;
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            const int s_ = 16 * i + 4 * lg + e;
-                            if (task < 6) sL[s_ * LDL + r] = from_f32<T>(-bt[e] * acc[e]);
-                            else sMqk[s_ * LDL + r] = from_f32<T>((i > j || r <= s_) ? acc[e] : 0.f);
-                        }
-                    } else {
-                        const int i = (task == 16) ? 0 : 2, j = i + 1;
+                for (int ks = 0; ks < KS; ++ks) {
+                    const int cc = 32 * ks + 8 * lg;
+                    fa[ks] = ld_frag<T>(&rowsrc[(16 * i + lr) * LDK1 + cc]);
+                    float kv[8], f[8];
+                    ld8_as_f32<T>(&sKinv[(16 * j + lr) * LDK1 + cc], kv);
+                    ld8f(&sF[frow * K + cc], f);
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            sMqk[(16 * i + 4 * lg + e) * LDL + 16 * j + lr] = from_f32<T>(0.f);
-                    }
+                    for (int e = 0; e < 8; ++e) kv[e] *= f[e];
+                    fb[ks] = frag_from<T>(kv);
                 }
+            };
+            auto task_out = [&](int task, const typename FragOf<T>::type (&fa)[KS],
+                                const typename FragOf<T>::type (&fb)[KS]) {
+                int i, j;
+                if (task < 6) offdiag_pair(task, i, j);
+                else lower_pair(task - 6, i, j);
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) acc = mma(acc, fa[ks], fb[ks]);
+                const f32x4 bt = *reinterpret_cast<const f32x4*>(&sBeta[16 * i + 4 * lg]);
+                T* dst = (task < 6) ? sL : sMqk;
+                const int r = 16 * j + lr;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int s_ = 16 * i + 4 * lg + e;
+                    const float val = (task < 6) ? -bt[e] * acc[e] : ((i > j || r <= s_) ? acc[e] : 0.f);
+                    dst[s_ * LDL + r] = from_f32<T>(val);
+                }
+            };
+            // per wave 1..7: tasks (t0, t1[, t2])
+            const int t0 = (w <= 3) ? 2 * (w - 1) : (w == 4) ? 7 : (w == 5) ? 10 : (w == 6) ? 13 : 14;
+            const int t1 = (w <= 3) ? 2 * (w - 1) + 1 : (w == 4) ? 9 : (w == 5) ? 12 : (w == 6) ? 6 : 11;
+            typename FragOf<T>::type fa0[KS], fb0[KS], fa1[KS], fb1[KS];
+            task_ops(t0, fa0, fb0);
+            task_ops(t1, fa1, fb1);
+            task_out(t0, fa0, fb0);
+            task_out(t1, fa1, fb1);
+            if (w >= 6) {
+                const int t2 = (w == 6) ? 8 : 15;
+                task_ops(t2, fa0, fb0);
+                task_out(t2, fa0, fb0);
             }
         }
         __syncthreads();
 
-        // ---- P3: W and U~ tiles by block forward substitution; Mqk out ----------
-        {
-            // Mqk rows, 16 bytes at a time
-            constexpr int PPR = C * (int)SZ / 16;
-#pragma unroll
-            for (int pc = tid; pc < C * PPR; pc += NT) {
-                const int row = pc / PPR, seg = pc % PPR;
-                *reinterpret_cast<uint4*>(&gMqk[row * C + seg * (16 / (int)SZ)]) =
-                    *reinterpret_cast<const uint4*>(&sMqk[row * LDL + seg * (16 / (int)SZ)]);
-            }
-        }
+        // ---- P3: W and U~ tiles by block forward substitution -------------------------
         {
             Frag4 Ld[4], Lo[6];
 #pragma unroll
@@ -469,11 +548,16 @@ __global__ __launch_bounds__(512) void kda_intra_kernel(IntraParams p) {
                 const int k = q6 - i * (i - 1) / 2;
                 Lo[q6] = ld_frag4<T>(&sL[(16 * i + lr) * LDL + 16 * k + 4 * lg]);
             }
-            auto solve_tile = [&](const T* rhs, f32x4* X) {
+            // X = (I + A)^{-1} R for 16-column tile tl; R read from the
+            // channel-major rows rhs[lr][token] of that tile
+            auto solve_tile = [&](const T* rhs, int tl, f32x4* X) {
                 Frag4 Xb[4];
+                f32x4 R[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) R[i] = ld4_as_f32<T>(rhs + lr * LDT + swz_t(16 * tl, 16 * i + 4 * lg));
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    f32x4 acc = ld4_as_f32<T>(rhs + lr * LDT + 16 * i + 4 * lg);
+                    f32x4 acc = R[i];
 #pragma unroll
                     for (int k = 0; k < i; ++k) acc = mma16(acc, Lo[i * (i - 1) / 2 + k], Xb[k]);
                     X[i] = mma16(f32x4{0.f, 0.f, 0.f, 0.f}, Ld[i], frag4_from<T>(acc));
@@ -485,34 +569,58 @@ __global__ __launch_bounds__(512) void kda_intra_kernel(IntraParams p) {
                 const int u = w + NW * m;
                 if (u < CT) {
                     f32x4 X[4];
-                    solve_tile(&sKhbT[16 * u * LDT], X);
+                    solve_tile(&sKhbT[16 * u * LDT], u, X);
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
                             sW[(16 * i + 4 * lg + e) * LDK1 + 16 * u + lr] = from_f32<T>(X[i][e]);
                 } else if (u < CT + NVT) {
+                    // U~ written back over this tile's (consumed) beta V rows, transposed
                     const int vt = u - CT;
+                    T* rows = &sVbT[16 * vt * LDT];
                     f32x4 X[4];
-                    solve_tile(&sVbT[16 * vt * LDT], X);
+                    solve_tile(rows, vt, X);
+                    wave_lds_sync();
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         float x4[4] = {X[i][0], X[i][1], X[i][2], X[i][3]};
-                        st4(&gUtT[(16 * vt + lr) * C + 16 * i + 4 * lg], x4);
+                        st_small<4>(&rows[lr * LDT + swz_t(16 * vt, 16 * i + 4 * lg)], x4);
                     }
                 }
             }
         }
         __syncthreads();
 
-        // ---- W out, 16 bytes at a time --------------------------------------------
+        // ---- record rows out, 16 bytes at a time: W, Mqk, (K e^{G_C-G})^T, U~^T -----
         {
-            constexpr int PPR = K * (int)SZ / 16;
+            constexpr int E = 16 / (int)SZ;                  // elements per piece
+            constexpr int PW = K * (int)SZ / 16, PC = C * (int)SZ / 16;
+            static_assert((C * PW) % NT == 0 && (C * PC) % NT == 0 && (K * PC) % NT == 0 &&
+                              (V * PC) % NT == 0, "record rows split evenly over the workgroup");
 #pragma unroll
-            for (int pc = tid; pc < C * PPR; pc += NT) {
-                const int row = pc / PPR, seg = pc % PPR;
-                *reinterpret_cast<uint4*>(&gW[row * K + seg * (16 / (int)SZ)]) =
-                    *reinterpret_cast<const uint4*>(&sW[row * LDK1 + seg * (16 / (int)SZ)]);
+            for (int j = 0; j < C * PW / NT; ++j) {
+                const int pc = tid + NT * j;
+                buf_store16(rrec, (unsigned)RL.oW + (unsigned)pc * 16u, 0u,
+                            *reinterpret_cast<const uint4*>(&sW[(pc / PW) * LDK1 + (pc % PW) * E]));
+            }
+#pragma unroll
+            for (int j = 0; j < C * PC / NT; ++j) {
+                const int pc = tid + NT * j;
+                buf_store16(rrec, (unsigned)RL.oMqk + (unsigned)pc * 16u, 0u,
+                            *reinterpret_cast<const uint4*>(&sMqk[(pc / PC) * LDL + (pc % PC) * E]));
+            }
+#pragma unroll
+            for (int j = 0; j < K * PC / NT; ++j) {
+                const int pc = tid + NT * j;
+                buf_store16(rrec, (unsigned)RL.oKbT + (unsigned)pc * 16u, 0u,
+                            *reinterpret_cast<const uint4*>(&sKbT[(pc / PC) * LDT + swz_t(pc / PC, (pc % PC) * E)]));
+            }
+#pragma unroll
+            for (int j = 0; j < V * PC / NT; ++j) {
+                const int pc = tid + NT * j;
+                buf_store16(rrec, (unsigned)RL.oUtT + (unsigned)pc * 16u, 0u,
+                            *reinterpret_cast<const uint4*>(&sVbT[(pc / PC) * LDT + swz_t(pc / PC, (pc % PC) * E)]));
             }
         }
         __syncthreads();
