@@ -300,13 +300,16 @@ kda_status kda_chunk_fwd(int B, int T, int H, int K, int V, kda_dtype dt,
         float* wsP = ws;
         float* wsL = wsP + (size_t)(pl.n_seg - 1) * bh * K * K;
         float* wsFinal = wsL + (size_t)(pl.n_seg - 1) * bh * K * V;
+        // K = V = 128 (bf16): one 8-wave workgroup carries the transition and
+        // the load columns of a segment together and stages its records once
+        const int vbs = ((int)dt == 1 && K == 128 && V == 128) ? K + V : vb;
         StateParams s1 = sp;
         s1.summary = 1;
-        s1.n_vb = (K + V) / vb;
+        s1.n_vb = (K + V) / vbs;
         s1.wsP = wsP;
         s1.wsL = wsL;
         if (launch_timed("state_summary", st, [&] {
-                return launch_state((int)dt, K, vb, s1, (int)(bh * (pl.n_seg - 1) * s1.n_vb), st);
+                return launch_state((int)dt, K, vbs, s1, (int)(bh * (pl.n_seg - 1) * s1.n_vb), st);
             }) != hipSuccess)
             return KDA_ERR_HIP;
         ScanParams scp{};

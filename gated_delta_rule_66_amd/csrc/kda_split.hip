@@ -655,7 +655,7 @@ struct StateLayout {
     static constexpr int PQ = SUMMARY ? 0 : C * K * SZ / 16;   // Qh
     static constexpr int PM = SUMMARY ? 0 : C * C * SZ / 16;   // Mqk
     static constexpr int PK = K * C * SZ / 16;           // KbT
-    static constexpr int PU = VB * C * SZ / 16;          // U~ rows of the block
+    static constexpr int PU = (SUMMARY && VB > K ? VB - K : VB) * C * SZ / 16;   // U~ rows of the block
     static constexpr int PE = K * 4 / 16;                // e^{G_C}
     static constexpr int E1 = PW, E2 = E1 + PQ, E3 = E2 + PM, E4 = E3 + PK, E5 = E4 + PU;
     static constexpr int PTOT = E5 + PE;
@@ -672,6 +672,8 @@ void kda_state_kernel(StateParams p) {
     constexpr int KS = K / 32, CT = K / 16;
     constexpr unsigned SZ = sizeof(T);
     constexpr int NPT = L::NPT;
+    // 8-wave workgroups keep 256 registers per lane: operands are loaded per tile
+    constexpr bool NARROW_REGS = NW == 8 && NTW == 2;
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
     T* sW = reinterpret_cast<T*>(smem + L::oW);
@@ -716,9 +718,15 @@ void kda_state_kernel(StateParams p) {
     }
 
     const int col0 = vb * VB;
-    const bool pmode = SUMMARY && col0 < K;
-    const int vcol0 = SUMMARY ? (pmode ? 0 : col0 - K) : col0;
     const int tile0 = NTW * w;
+    // summary pass: columns below K carry the transition (identity start, no
+    // U~), the others the load; a workgroup may hold both kinds (a wave holds
+    // one).  The U~ rows staged are those of the value columns
+    // [vcol0, vcol0 + nvcol) of this workgroup.
+    const bool pmode = SUMMARY && col0 + 16 * tile0 < K;
+    const int vcol0 = SUMMARY ? max(col0 - K, 0) : col0;
+    const int nvcol = SUMMARY ? max(0, col0 + VB - max(col0, K)) : VB;
+    const int urow0 = SUMMARY ? col0 + 16 * tile0 - K - vcol0 : 16 * tile0;   // this wave's first U~ row
 
     const RecLayout RL = rec_layout(K, V, (int)sizeof(T));
     const unsigned char* rec0 = p.rec + rec_first * RL.bytes;
@@ -768,7 +776,7 @@ void kda_state_kernel(StateParams p) {
             } else if (pc < L::E4) {
                 off = (unsigned)RL.oKbT + (unsigned)(pc - L::E3) * 16u;
             } else if (pc < L::E5) {
-                ok = !pmode;
+                ok = pc - L::E4 < nvcol * (C * (int)SZ / 16);
                 off = (unsigned)RL.oUtT + (unsigned)vcol0 * C * SZ + (unsigned)(pc - L::E4) * 16u;
             } else if (pc < L::PTOT) {
                 off = (unsigned)RL.oEgc + (unsigned)(pc - L::E5) * 16u;
@@ -818,7 +826,24 @@ void kda_state_kernel(StateParams p) {
             for (int ks = 0; ks < KS; ++ks) Sb[j][ks] = frag_from_tiles<T>(S[j][2 * ks], S[j][2 * ks + 1]);
         // U = U~ - W S
         f32x4 U[NTW][4];
-        {
+        if constexpr (NARROW_REGS) {
+            // two waves per SIMD hide the LDS latency: operands per row tile
+#pragma unroll
+            for (int ti = 0; ti < 4; ++ti) {
+                Frag aw[KS];
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) aw[ks] = ld_frag_perm<T>(&sW[(16 * ti + lr) * LDK2 + 32 * ks + 4 * lg]);
+#pragma unroll
+                for (int j = 0; j < NTW; ++j) {
+                    const f32x4 ut = pmode ? f32x4{0.f, 0.f, 0.f, 0.f}
+                                           : ld4_as_f32<T>(&sUtT[(urow0 + 16 * j + lr) * LDT + 16 * ti + 4 * lg]);
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) acc = mma(acc, aw[ks], Sb[j][ks]);
+                    U[j][ti] = ut - acc;
+                }
+            }
+        } else {
             Frag aw[4][KS];
             f32x4 ut[NTW][4];
 #pragma unroll
@@ -830,7 +855,7 @@ void kda_state_kernel(StateParams p) {
 #pragma unroll
                 for (int ti = 0; ti < 4; ++ti)
                     ut[j][ti] = pmode ? f32x4{0.f, 0.f, 0.f, 0.f}
-                                      : ld4_as_f32<T>(&sUtT[(16 * (tile0 + j) + lr) * LDT + 16 * ti + 4 * lg]);
+                                      : ld4_as_f32<T>(&sUtT[(urow0 + 16 * j + lr) * LDT + 16 * ti + 4 * lg]);
 #pragma unroll
             for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
@@ -893,7 +918,21 @@ void kda_state_kernel(StateParams p) {
             }
         }
         // S <- Diag(e^{G_C}) S + (K e^{G_C - G})^T U
-        {
+        if constexpr (NARROW_REGS) {
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) {
+                const f32x4 eg = *reinterpret_cast<const f32x4*>(&sEGC[16 * ct + 4 * lg]);
+                Frag ak[2];
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) ak[ks] = ld_frag_perm<T>(&sKbT[(16 * ct + lr) * LDT + 32 * ks + 4 * lg]);
+#pragma unroll
+                for (int j = 0; j < NTW; ++j) {
+                    S[j][ct] = S[j][ct] * eg;
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks) S[j][ct] = mma(S[j][ct], ak[ks], Ub[j][ks]);
+                }
+            }
+        } else {
             Frag ak[CT][2];
             f32x4 eg[CT];
 #pragma unroll
@@ -1030,6 +1069,10 @@ static hipError_t launch_state_t(const StateParams& p, int grid, hipStream_t str
 hipError_t launch_state(int dtype, int K, int VB, const StateParams& p, int grid, hipStream_t stream) {
     if (grid <= 0) return hipSuccess;
     if (dtype == 1) {
+        if (K == 128 && VB == 256 && p.summary) {
+            hipLaunchKernelGGL((kda_state_kernel<bf16, 128, 8, 2, true>), dim3(grid), dim3(512), 0, stream, p);
+            return hipGetLastError();
+        }
         if (K == 128 && VB == 128) return launch_state_t<bf16, 128, 4, 2>(p, grid, stream);
         if (K == 128 && VB == 64) return launch_state_t<bf16, 128, 4, 1>(p, grid, stream);
         if (K == 64 && VB == 128) return launch_state_t<bf16, 64, 8, 1>(p, grid, stream);
