@@ -103,10 +103,10 @@ kda_status resolve_plan(int B, int T, int H, int K, int V, kda_dtype dt, const k
         if (s != KDA_OK) return s;
     }
     if (split == 0) {
-        // single pass when (b, h, 128-column) chains alone fill the device;
-        // otherwise the two-pass form, whose first pass is parallel over chunks
-        const bool wide = bh * (V >= 128 ? V / 128 : 1) >= cus && chunk_variant_exists((int)dt, K, V >= 128 ? 128 : 64);
-        split = (!wide && split_variant_exists((int)dt, K, V, 64)) ? 2 : 1;
+        // the two-pass form wherever it exists: its first pass is parallel over
+        // chunks, and it measured at least as fast as the single pass on every
+        // shape tried, including those whose (b, h) chains alone fill the device
+        split = split_variant_exists((int)dt, K, V, 64) ? 2 : 1;
     }
     const bool vb_fixed = vb != 0;
     if (split == 2) {

@@ -351,24 +351,24 @@ __global__ __launch_bounds__(512) void kda_intra_kernel(IntraParams p) {
                 }
             if (part == P - 1) buf_store1(rrec, (unsigned)RL.oEgc + (unsigned)ch * 4u, 0u, fast_exp2(pfx[NW]));
         }
+        // value side (needs only beta): beta V, channel-major
+        {
+            float bv[8][TPLV];
+#pragma unroll
+            for (int i = 0; i < TPLV; ++i) {
+                float vx[8];
+                vr[i].to_f32(vx);
+                const float bt = sBeta[tv + i];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) bv[e][i] = bt * vx[e];
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) st_small<TPLV>(&sVbT[(n0 + e) * LDT + swz_t(n0 + e, tv)], bv[e]);
+        }
         __syncthreads();
 
         // ---- P1b: operands ---------------------------------------------------------------
         {
-            // value side first, which frees its registers
-            {
-                float bv[8][TPLV];
-#pragma unroll
-                for (int i = 0; i < TPLV; ++i) {
-                    float vx[8];
-                    vr[i].to_f32(vx);
-                    const float bt = sBeta[tv + i];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) bv[e][i] = bt * vx[e];
-                }
-#pragma unroll
-                for (int e = 0; e < 8; ++e) st_small<TPLV>(&sVbT[(n0 + e) * LDT + swz_t(n0 + e, tv)], bv[e]);
-            }
             float pre[8], gb[8], egb[8], ecb[8];
             const int myblk = w >> 1;
             ld8f(&tPre[w * K + c0], pre);
@@ -419,10 +419,11 @@ __global__ __launch_bounds__(512) void kda_intra_kernel(IntraParams p) {
         }
         __syncthreads();
 
-        // the raw registers are free: fetch the next item behind P2 / P3
+        // the raw registers are free: fetch the next item, waves 0-3 here and
+        // waves 4-7 behind P2, so that half of the loads queue at a time
         __builtin_amdgcn_sched_barrier(0);
-        if (item + G < p.n_items) {
-            locate(item + G, nrow, nnt);
+        if (item + G < p.n_items) locate(item + G, nrow, nnt);
+        if (w < 4 && item + G < p.n_items) {
             load_gk(nrow, nnt);
             load_q(nrow, nnt);
             load_vb(nrow, nnt);
@@ -537,6 +538,13 @@ __global__ __launch_bounds__(512) void kda_intra_kernel(IntraParams p) {
         }
         __syncthreads();
 
+        __builtin_amdgcn_sched_barrier(0);
+        if (w >= 4 && item + G < p.n_items) {
+            load_gk(nrow, nnt);
+            load_q(nrow, nnt);
+            load_vb(nrow, nnt);
+        }
+        __builtin_amdgcn_sched_barrier(0);
         // ---- P3: W and U~ tiles by block forward substitution -------------------------
         {
             Frag4 Ld[4], Lo[6];
@@ -564,23 +572,45 @@ __global__ __launch_bounds__(512) void kda_intra_kernel(IntraParams p) {
                     Xb[i] = frag4_from<T>(X[i]);
                 }
             };
+            // two tiles, their dependency chains interleaved
+            auto solve_two = [&](const T* ra, int ta, const T* rb, int tb, f32x4* XA, f32x4* XB) {
+                Frag4 Xa[4], Xc[4];
+                f32x4 RA[4], RB[4];
 #pragma unroll
-            for (int m = 0; m < (CT + NVT + NW - 1) / NW; ++m) {
-                const int u = w + NW * m;
+                for (int i = 0; i < 4; ++i) {
+                    RA[i] = ld4_as_f32<T>(ra + lr * LDT + swz_t(16 * ta, 16 * i + 4 * lg));
+                    RB[i] = ld4_as_f32<T>(rb + lr * LDT + swz_t(16 * tb, 16 * i + 4 * lg));
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    f32x4 acca = RA[i], accb = RB[i];
+#pragma unroll
+                    for (int k = 0; k < i; ++k) {
+                        acca = mma16(acca, Lo[i * (i - 1) / 2 + k], Xa[k]);
+                        accb = mma16(accb, Lo[i * (i - 1) / 2 + k], Xc[k]);
+                    }
+                    XA[i] = mma16(f32x4{0.f, 0.f, 0.f, 0.f}, Ld[i], frag4_from<T>(acca));
+                    XB[i] = mma16(f32x4{0.f, 0.f, 0.f, 0.f}, Ld[i], frag4_from<T>(accb));
+                    Xa[i] = frag4_from<T>(XA[i]);
+                    Xc[i] = frag4_from<T>(XB[i]);
+                }
+            };
+            // tile u < CT: W columns [16 u, 16 u + 16) from beta K e^{G}; else
+            // U~ tile u - CT from beta V
+            auto tile_rhs = [&](int u) -> const T* {
+                return u < CT ? &sKhbT[16 * u * LDT] : &sVbT[16 * (u - CT) * LDT];
+            };
+            auto tile_out = [&](int u, const f32x4* X) {
                 if (u < CT) {
-                    f32x4 X[4];
-                    solve_tile(&sKhbT[16 * u * LDT], u, X);
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
 #pragma unroll
                         for (int e = 0; e < 4; ++e)
                             sW[(16 * i + 4 * lg + e) * LDK1 + 16 * u + lr] = from_f32<T>(X[i][e]);
-                } else if (u < CT + NVT) {
+                } else {
                     // U~ written back over this tile's (consumed) beta V rows, transposed
                     const int vt = u - CT;
                     T* rows = &sVbT[16 * vt * LDT];
-                    f32x4 X[4];
-                    solve_tile(rows, vt, X);
                     wave_lds_sync();
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
@@ -588,6 +618,18 @@ __global__ __launch_bounds__(512) void kda_intra_kernel(IntraParams p) {
                         st_small<4>(&rows[lr * LDT + swz_t(16 * vt, 16 * i + 4 * lg)], x4);
                     }
                 }
+            };
+            static_assert(CT + NVT <= 2 * NW, "at most two tiles per wave");
+            const int u0 = w, u1 = w + NW;
+            if (u1 < CT + NVT) {
+                f32x4 XA[4], XB[4];
+                solve_two(tile_rhs(u0), u0 < CT ? u0 : u0 - CT, tile_rhs(u1), u1 < CT ? u1 : u1 - CT, XA, XB);
+                tile_out(u0, XA);
+                tile_out(u1, XB);
+            } else if (u0 < CT + NVT) {
+                f32x4 X[4];
+                solve_tile(tile_rhs(u0), u0 < CT ? u0 : u0 - CT, X);
+                tile_out(u0, X);
             }
         }
         __syncthreads();
