@@ -10,6 +10,7 @@ from .kda import (  # noqa: F401
     chunk_fwd,
     chunk_fwd_varlen,
     chunk_fwd_varlen_workspace_size,
+    snapshot_count,
     chunk_plan,
     chunk_workspace_size,
     load_library,
@@ -21,5 +22,5 @@ from .kda import (  # noqa: F401
 )
 from .build import LIB_PATH, build_library  # noqa: F401
 
-__all__ = ["chunk_fwd", "chunk_fwd_varlen", "chunk_fwd_varlen_workspace_size", "recurrent_step", "chunk_plan", "chunk_workspace_size", "profile_start", "profile_stop",
+__all__ = ["chunk_fwd", "chunk_fwd_varlen", "chunk_fwd_varlen_workspace_size", "snapshot_count", "recurrent_step", "chunk_plan", "chunk_workspace_size", "profile_start", "profile_stop",
            "load_library", "build_library", "version", "status_string", "KDAError", "Plan"]

@@ -419,21 +419,27 @@ static kda_status check_varlen_sizes(int N, int T_total, int H, int K, int V, kd
     return KDA_OK;
 }
 
+// workspace of a packed batch: chunk offsets, snapshot offsets (each N + 1
+// ints, 256-byte aligned), then the chunk records
+static size_t varlen_offsets_bytes(int N) { return ((size_t)(N + 1) * sizeof(int) + 255) & ~(size_t)255; }
+
 size_t kda_chunk_fwd_varlen_workspace_size(int N, int T_total, int H, int K, int V, kda_dtype dt) {
     if (check_varlen_sizes(N, T_total, H, K, V, dt) != KDA_OK) return (size_t)-1;
-    const size_t offs = ((size_t)(N + 1) * sizeof(int) + 255) & ~(size_t)255;
-    return offs + (size_t)H * varlen_chunk_bound(N, T_total) * record_bytes(K, V, dt);
+    return 2 * varlen_offsets_bytes(N) + (size_t)H * varlen_chunk_bound(N, T_total) * record_bytes(K, V, dt);
 }
 
-kda_status kda_chunk_fwd_varlen(int N, const int* cu_seqlens, int T_total, int H, int K, int V, kda_dtype dt,
-                                const void* q, const void* k, const void* v,
-                                const void* g, const void* beta,
-                                const float* initial_state,
-                                void* o, float* final_state,
-                                void* workspace, size_t workspace_bytes,
-                                void* stream) {
+static kda_status varlen_impl(int N, const int* cu_seqlens, int T_total, int H, int K, int V, kda_dtype dt,
+                              const void* q, const void* k, const void* v, const void* g, const void* beta,
+                              const float* initial_state, void* o, float* final_state, int snap_interval,
+                              float* snapshots, int max_snapshots, void* workspace, size_t workspace_bytes,
+                              void* stream) {
     kda_status s = check_varlen_sizes(N, T_total, H, K, V, dt);
     if (s != KDA_OK) return s;
+    if (snap_interval < 0 || max_snapshots < 0 || snap_interval % kChunk != 0) return KDA_ERR_INVALID_ARG;
+    if (snap_interval > 0 && max_snapshots > 0) {
+        if (!snapshots || !aligned16(snapshots)) return KDA_ERR_INVALID_ARG;
+        if ((double)max_snapshots * H * K * V > 9.0e15) return KDA_ERR_INVALID_ARG;
+    }
     const long nh = (long)N * H;
     if (nh > 0 && !cu_seqlens) return KDA_ERR_INVALID_ARG;
     if (H > 0 && T_total > 0) {
@@ -462,12 +468,16 @@ kda_status kda_chunk_fwd_varlen(int N, const int* cu_seqlens, int T_total, int H
     int cus = 0;
     if (device_cus(&cus) != KDA_OK) return KDA_ERR_HIP;
 
-    const size_t offs = ((size_t)(N + 1) * sizeof(int) + 255) & ~(size_t)255;
+    const size_t offs = varlen_offsets_bytes(N);
     int* chunk_off = reinterpret_cast<int*>(workspace);
-    unsigned char* recs = reinterpret_cast<unsigned char*>(workspace) + offs;
+    int* snap_off = reinterpret_cast<int*>(reinterpret_cast<unsigned char*>(workspace) + offs);
+    unsigned char* recs = reinterpret_cast<unsigned char*>(workspace) + 2 * offs;
     const int ncb = (int)varlen_chunk_bound(N, T_total);
+    const bool snaps = snap_interval > 0 && max_snapshots > 0;
+    const int snap_every = snap_interval / kChunk;
     if (launch_timed("varlen_prep", st, [&] {
-            return launch_varlen_prep(cu_seqlens, N, T_total, ncb, chunk_off, st);
+            return launch_varlen_prep(cu_seqlens, N, T_total, ncb, chunk_off, snaps ? snap_every : 0,
+                                      snaps ? max_snapshots : 0, snaps ? snap_off : nullptr, st);
         }) != hipSuccess)
         return KDA_ERR_HIP;
 
@@ -500,9 +510,37 @@ kda_status kda_chunk_fwd_varlen(int N, const int* cu_seqlens, int T_total, int H
     sp.cu_seqlens = cu_seqlens;
     sp.chunk_off = chunk_off;
     sp.N = N;
+    if (snaps) {
+        sp.snaps = snapshots;
+        sp.snap_off = snap_off;
+        sp.snap_every = snap_every;
+        sp.max_snaps = max_snapshots;
+    }
     return launch_timed("state_output", st, [&] {
                return launch_state((int)dt, K, vb, sp, (int)(nh * (V / vb)), st);
            }) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
+kda_status kda_chunk_fwd_varlen(int N, const int* cu_seqlens, int T_total, int H, int K, int V, kda_dtype dt,
+                                const void* q, const void* k, const void* v,
+                                const void* g, const void* beta,
+                                const float* initial_state,
+                                void* o, float* final_state,
+                                void* workspace, size_t workspace_bytes,
+                                void* stream) {
+    return varlen_impl(N, cu_seqlens, T_total, H, K, V, dt, q, k, v, g, beta, initial_state, o, final_state, 0,
+                       nullptr, 0, workspace, workspace_bytes, stream);
+}
+
+kda_status kda_chunk_fwd_varlen_snapshots(int N, const int* cu_seqlens, int T_total, int H, int K, int V,
+                                          kda_dtype dt, const void* q, const void* k, const void* v,
+                                          const void* g, const void* beta, const float* initial_state,
+                                          void* o, float* final_state, int snapshot_interval,
+                                          float* snapshots, int max_snapshots,
+                                          void* workspace, size_t workspace_bytes, void* stream) {
+    if (snapshot_interval <= 0) return KDA_ERR_INVALID_ARG;
+    return varlen_impl(N, cu_seqlens, T_total, H, K, V, dt, q, k, v, g, beta, initial_state, o, final_state,
+                       snapshot_interval, snapshots, max_snapshots, workspace, workspace_bytes, stream);
 }
 
 kda_status kda_recurrent_step(int N, int H, int K, int V, kda_dtype dt,

@@ -106,13 +106,22 @@ struct StateParams {
     const int* cu_seqlens;
     const int* chunk_off;
     int N;
+    // state snapshots of a packed batch (output pass; null: none): after every
+    // snap_every chunks that lie wholly inside sequence i, the state goes to
+    // slot snap_off[i] + m of snaps [max_snaps][H][K][V] (slots past max_snaps
+    // are skipped)
+    float* snaps;
+    const int* snap_off;
+    int snap_every, max_snaps;
 };
 
 bool split_variant_exists(int dtype, int K, int V, int VB);
-// chunk offsets of a packed batch: chunk_off[i] = sum_{j<i} ceil(len_j / C),
-// capped at max_chunks; lengths from cu_seqlens clamped to [0, T_total]
+// offsets of a packed batch: chunk_off[i] = sum_{j<i} ceil(len_j / C), capped
+// at max_chunks, and (snap_off non-null) snap_off[i] = sum_{j<i}
+// floor(len_j / (snap_every C)), capped at max_snaps; lengths from cu_seqlens
+// clamped to [0, T_total]
 hipError_t launch_varlen_prep(const int* cu_seqlens, int N, int T_total, int max_chunks, int* chunk_off,
-                              hipStream_t stream);
+                              int snap_every, int max_snaps, int* snap_off, hipStream_t stream);
 hipError_t launch_intra(int dtype, int K, int V, const IntraParams& p, int grid, hipStream_t stream);
 hipError_t launch_state(int dtype, int K, int VB, const StateParams& p, int grid, hipStream_t stream);
 

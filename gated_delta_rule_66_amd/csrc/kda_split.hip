@@ -1002,6 +1002,23 @@ void kda_state_kernel(StateParams p) {
         if (ci + 1 < c_end) load_rec(ci + 1, pre);
         __builtin_amdgcn_sched_barrier(0);
         step(ci);
+        if constexpr (!SUMMARY) {
+            // state snapshot after every snap_every whole chunks of a sequence
+            if (p.snaps && (ci + 1) % p.snap_every == 0 && row0 + (size_t)(ci + 1) * C <= row_end) {
+                const int slot = p.snap_off[b] + (ci + 1) / p.snap_every - 1;
+                if (slot < p.max_snaps) {
+                    float* sd = p.snaps + ((size_t)slot * p.H + h) * K * V;
+#pragma unroll
+                    for (int j = 0; j < NTW; ++j) {
+                        const int col = col0 + 16 * (tile0 + j) + lr;
+#pragma unroll
+                        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) sd[(size_t)(16 * ct + 4 * lg + e) * V + col] = S[j][ct][e];
+                    }
+                }
+            }
+        }
         __syncthreads();
     }
 
@@ -1031,42 +1048,55 @@ void kda_state_kernel(StateParams p) {
 // Chunk offsets of a packed batch (one workgroup; block-wide scans of 256
 // sequence lengths at a time).
 __global__ __launch_bounds__(256) void kda_varlen_prep_kernel(const int* cu, int N, int T_total, int max_chunks,
-                                                              int* chunk_off) {
-    __shared__ int buf[256];
-    __shared__ int carry;
+                                                              int* chunk_off, int snap_len, int max_snaps,
+                                                              int* snap_off) {
+    __shared__ int buf[256], sbuf[256];
+    __shared__ int carry, scarry;
     const int tid = threadIdx.x;
     if (tid == 0) {
         carry = 0;
+        scarry = 0;
         chunk_off[0] = 0;
+        if (snap_off) snap_off[0] = 0;
     }
     __syncthreads();
     for (int base = 0; base < N; base += 256) {
         const int i = base + tid;
-        int c = 0;
+        int c = 0, sn = 0;
         if (i < N) {
             int s0, s1;
             seq_range(cu, i, T_total, s0, s1);
             c = (s1 - s0 + C - 1) / C;
+            if (snap_off) sn = (s1 - s0) / snap_len;
         }
         buf[tid] = c;
+        sbuf[tid] = sn;
         __syncthreads();
         for (int d = 1; d < 256; d <<= 1) {
             const int add = (tid >= d) ? buf[tid - d] : 0;
+            const int sadd = (tid >= d) ? sbuf[tid - d] : 0;
             __syncthreads();
             buf[tid] += add;
+            sbuf[tid] += sadd;
             __syncthreads();
         }
-        if (i < N) chunk_off[i + 1] = min(carry + buf[tid], max_chunks);
+        if (i < N) {
+            chunk_off[i + 1] = min(carry + buf[tid], max_chunks);
+            if (snap_off) snap_off[i + 1] = min(scarry + sbuf[tid], max_snaps);
+        }
         __syncthreads();
-        if (tid == 255) carry = min(carry + buf[255], max_chunks);
+        if (tid == 255) {
+            carry = min(carry + buf[255], max_chunks);
+            scarry = min(scarry + sbuf[255], max_snaps);
+        }
         __syncthreads();
     }
 }
 
 hipError_t launch_varlen_prep(const int* cu_seqlens, int N, int T_total, int max_chunks, int* chunk_off,
-                              hipStream_t stream) {
+                              int snap_every, int max_snaps, int* snap_off, hipStream_t stream) {
     hipLaunchKernelGGL(kda_varlen_prep_kernel, dim3(1), dim3(256), 0, stream, cu_seqlens, N, T_total, max_chunks,
-                       chunk_off);
+                       chunk_off, snap_every * C, max_snaps, snap_off);
     return hipGetLastError();
 }
 

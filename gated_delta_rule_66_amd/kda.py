@@ -28,6 +28,7 @@ EXPORTED_SYMBOLS = (
     "kda_chunk_fwd",
     "kda_chunk_fwd_varlen_workspace_size",
     "kda_chunk_fwd_varlen",
+    "kda_chunk_fwd_varlen_snapshots",
     "kda_recurrent_step",
     "kda_status_string",
     "kda_version",
@@ -69,6 +70,8 @@ def load_library(path: str = LIB_PATH):
     lib.kda_chunk_fwd_varlen_workspace_size.restype = sz
     lib.kda_chunk_fwd_varlen.argtypes = [i, p, i, i, i, i, i, p, p, p, p, p, p, p, p, p, sz, p]
     lib.kda_chunk_fwd_varlen.restype = i
+    lib.kda_chunk_fwd_varlen_snapshots.argtypes = [i, p, i, i, i, i, i, p, p, p, p, p, p, p, p, i, p, i, p, sz, p]
+    lib.kda_chunk_fwd_varlen_snapshots.restype = i
     lib.kda_recurrent_step.argtypes = [i, i, i, i, i, p, p, p, p, p, p, p, p]
     lib.kda_recurrent_step.restype = i
     lib.kda_status_string.argtypes = [i]
@@ -216,17 +219,31 @@ def chunk_fwd_varlen_workspace_size(N: int, T_total: int, H: int, K: int, V: int
     return int(n)
 
 
+def snapshot_count(cu_seqlens, snapshot_interval: int) -> int:
+    """Snapshots a packed batch yields: sum_i floor(len_i / snapshot_interval)
+    (cu_seqlens as a host sequence or tensor; a device tensor is copied)."""
+    cu = [int(x) for x in (cu_seqlens.tolist() if isinstance(cu_seqlens, torch.Tensor) else cu_seqlens)]
+    return sum(max(0, b - a) // snapshot_interval for a, b in zip(cu[:-1], cu[1:]))
+
+
 def chunk_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
                      beta: torch.Tensor, cu_seqlens: torch.Tensor,
                      initial_state: Optional[torch.Tensor] = None, output_final_state: bool = True, *,
                      out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
-                     workspace: Optional[torch.Tensor] = None):
-    """Packed variable-length prefill through ``kda_chunk_fwd_varlen``.
+                     workspace: Optional[torch.Tensor] = None, snapshot_interval: int = 0,
+                     snapshots: Optional[torch.Tensor] = None):
+    """Packed variable-length prefill through ``kda_chunk_fwd_varlen`` (or
+    ``kda_chunk_fwd_varlen_snapshots`` when ``snapshot_interval`` > 0).
 
     q, k, g: [T_total, H, K]; v: [T_total, H, V]; beta: [T_total, H] (bf16 or
     fp32); cu_seqlens: int32 [N + 1] on the same device; initial_state:
     [N, H, K, V] fp32 or None.  Returns (o [T_total, H, V], final_state
     [N, H, K, V] or None); ``final_state`` may be ``initial_state`` itself.
+    With ``snapshot_interval`` (a multiple of 64) it returns (o, final_state,
+    snapshots [S, H, K, V] fp32): snapshot m of sequence i, the state after
+    its first (m + 1) * snapshot_interval tokens, sits at
+    snapshot_count(cu_seqlens[:i + 1], snapshot_interval) + m.  ``snapshots``
+    may be passed preallocated (its first dimension is the capacity).
     """
     T_total, H, K = q.shape
     V = v.shape[-1]
@@ -253,6 +270,19 @@ def chunk_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch
     if ws_bytes > 0 and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if snapshot_interval:
+        if snapshots is None:
+            snapshots = torch.empty((snapshot_count(cu_seqlens, snapshot_interval), H, K, V),
+                                    dtype=torch.float32, device=dev)
+        else:
+            _check(snapshots, "snapshots", (snapshots.shape[0], H, K, V), torch.float32, dev)
+        st = load_library().kda_chunk_fwd_varlen_snapshots(
+            N, _ptr(cu_seqlens), T_total, H, K, V, _dtype_code(dt), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+            _ptr(beta), _ptr(initial_state), _ptr(out), _ptr(final_state), int(snapshot_interval),
+            _ptr(snapshots), snapshots.shape[0], _ptr(workspace), ws_len, _stream_ptr(dev))
+        if st != KDA_OK:
+            raise KDAError(st, "kda_chunk_fwd_varlen_snapshots")
+        return out, final_state, snapshots
     st = load_library().kda_chunk_fwd_varlen(
         N, _ptr(cu_seqlens), T_total, H, K, V, _dtype_code(dt), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
         _ptr(initial_state), _ptr(out), _ptr(final_state), _ptr(workspace), ws_len, _stream_ptr(dev))

@@ -172,6 +172,32 @@ kda_status kda_chunk_fwd_varlen(int N, const int* cu_seqlens, int T_total, int H
                                 void* stream);
 
 /*
+ * kda_chunk_fwd_varlen that also returns state snapshots at fixed block
+ * boundaries (prefix caching: a later request sharing the first m tokens of
+ * a sequence resumes from the snapshot at the largest boundary <= m).
+ *
+ *   snapshot_interval : tokens between snapshots; a positive multiple of 64
+ *                       (the chunk length), else KDA_ERR_INVALID_ARG.
+ *   snapshots         : DEVICE fp32 [max_snapshots, H, K, V], 16-byte aligned
+ *                       (may be NULL when max_snapshots == 0).
+ *   max_snapshots     : capacity in snapshots (>= 0); slots past it are not
+ *                       written.  With valid cu_seqlens the count needed is
+ *                       sum_i floor(len_i / snapshot_interval) <=
+ *                       floor(T_total / snapshot_interval).
+ * Snapshot m (m = 0, 1, ...) of sequence i, the state after its first
+ * (m + 1) * snapshot_interval tokens, is written to slot snap_off_i + m with
+ * snap_off_i = sum_{j < i} floor(len_j / snapshot_interval); nothing else in
+ * `snapshots` is touched.  o and final_state are exactly those of
+ * kda_chunk_fwd_varlen with the same arguments; the workspace is the same.
+ */
+kda_status kda_chunk_fwd_varlen_snapshots(int N, const int* cu_seqlens, int T_total, int H, int K, int V,
+                                          kda_dtype dt, const void* q, const void* k, const void* v,
+                                          const void* g, const void* beta, const float* initial_state,
+                                          void* o, float* final_state, int snapshot_interval,
+                                          float* snapshots, int max_snapshots,
+                                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * One decode step for N independent sequences (page section "Как хранить
  * миллион токенов в памяти": the fixed-size state replaces the KV cache).
  * Reads and writes the state once.

@@ -178,10 +178,42 @@ def test_varlen_workspace_formula():
     N, T, H = 5, 1000, 3
     rec = 2 * (64 * 128 * 2 + 64 * 64 + 2 * 128 * 64) + 128 * 4
     bound = -(-T // 64) + N                  # sum_i ceil(len_i / 64) <= ceil(T / 64) + N
-    offs = -(-(N + 1) * 4 // 256) * 256
-    assert lib.kda_chunk_fwd_varlen_workspace_size(N, T, H, 128, 128, BF16) == offs + H * bound * rec
+    offs = -(-(N + 1) * 4 // 256) * 256      # chunk offsets, then snapshot offsets
+    assert lib.kda_chunk_fwd_varlen_workspace_size(N, T, H, 128, 128, BF16) == 2 * offs + H * bound * rec
     assert lib.kda_chunk_fwd_varlen_workspace_size(-1, T, H, 128, 128, BF16) == ctypes.c_size_t(-1).value
-    assert _varlen(lib, N=N, T=T, H=H, ws_bytes=offs + H * bound * rec - 1) == WORKSPACE
+    assert _varlen(lib, N=N, T=T, H=H, ws_bytes=2 * offs + H * bound * rec - 1) == WORKSPACE
+
+
+def _snap(lib, interval=128, snaps=FAKE, cap=4, N=3, T=300, H=2, K=128, V=128, ws=FAKE, ws_bytes=1 << 40):
+    p = ctypes.c_void_p
+    lib.kda_chunk_fwd_varlen_snapshots.argtypes = [ctypes.c_int, p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                   ctypes.c_int, ctypes.c_int] + [p] * 8 + \
+        [ctypes.c_int, p, ctypes.c_int, p, ctypes.c_size_t, p]
+    lib.kda_chunk_fwd_varlen_snapshots.restype = ctypes.c_int
+    return lib.kda_chunk_fwd_varlen_snapshots(N, p(FAKE), T, H, K, V, BF16, *([p(FAKE)] * 5), None, p(FAKE), None,
+                                              interval, p(snaps) if snaps else None, cap, p(ws) if ws else None,
+                                              ws_bytes, None)
+
+
+def test_varlen_snapshot_validation_before_any_launch():
+    lib = _lib()
+    assert _snap(lib, interval=0) == INVALID                     # snapshots need an interval
+    assert _snap(lib, interval=-64) == INVALID
+    assert _snap(lib, interval=100) == INVALID                   # not a multiple of the chunk
+    assert _snap(lib, snaps=None) == INVALID                     # capacity without a buffer
+    assert _snap(lib, snaps=FAKE + 8) == INVALID                 # 16-byte alignment
+    assert _snap(lib, cap=-1) == INVALID
+    assert _snap(lib, K=96) == UNSUPPORTED
+    assert _snap(lib, ws=None) == WORKSPACE
+    assert _snap(lib, N=0) == OK                                 # nothing to do
+    assert _snap(lib, snaps=None, cap=0, N=0) == OK
+
+
+def test_snapshot_count_formula():
+    # sum_i floor(len_i / interval) over the packed lengths
+    assert K_.snapshot_count([0, 64, 64, 300, 1000], 128) == 0 + 0 + 1 + 5
+    assert K_.snapshot_count([0], 64) == 0
+    assert K_.snapshot_count([0, 640], 64) == 10
 
 
 def test_package_raises_without_library(tmp_path):

@@ -346,6 +346,49 @@ def test_varlen_matches_oracle_and_single_calls(lengths, H, K, V, dtype):
         assert torch.equal(o[a:e], o1[0]) and torch.equal(sT[i:i + 1], s1), i
 
 
+SNAPSHOTS = [([0, 64, 200, 513, 128, 320, 7], 2, 128, 128, torch.bfloat16, 128),
+             ([130, 256, 0, 64], 2, 64, 128, torch.bfloat16, 64),
+             ([100, 300, 384], 2, 128, 64, torch.bfloat16, 192),
+             ([128, 65, 256], 2, 64, 64, torch.float32, 64)]
+
+
+@pytest.mark.parametrize("lengths,H,K,V,dtype,interval", SNAPSHOTS)
+def test_varlen_snapshots_match_oracle_prefixes(lengths, H, K, V, dtype, interval):
+    """Snapshot m of sequence i is the state after the first (m + 1) *
+    interval tokens of that sequence (the oracle's final state on that
+    prefix); o and the final states are bitwise those of the call without
+    snapshots; a slot past the capacity is left untouched."""
+    from gated_delta_rule_66_amd import chunk_fwd_varlen, snapshot_count
+    say("varlen snapshots lengths=%s H=%d K=%d V=%d %s every %d" % (lengths, H, K, V, dtype, interval))
+    seqs, x, cu = _packed(lengths, H, K, V, dtype, seed=60)
+    xd = to_dev(x)
+    cud = cu.to(DEV)
+    o0, s0 = chunk_fwd_varlen(xd["q"], xd["k"], xd["v"], xd["g"], xd["beta"], cud, xd["s0"])
+    o, sT, snaps = chunk_fwd_varlen(xd["q"], xd["k"], xd["v"], xd["g"], xd["beta"], cud, xd["s0"],
+                                    snapshot_interval=interval)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o0) and torch.equal(sT, s0)
+    n_snap = snapshot_count(cu, interval)
+    assert snaps.shape == (n_snap, H, K, V)
+    base = 0
+    for i, (d, n) in enumerate(zip(seqs, lengths)):
+        for m in range(n // interval):
+            t_end = (m + 1) * interval
+            prefix = {name: (t if name == "s0" else t[:, :t_end].contiguous()) for name, t in d.items()}
+            _, s_ref = run_oracle(prefix)
+            assert s_err(snaps[base + m:base + m + 1], s_ref) < TOL[dtype], (i, m)
+        base += n // interval
+    assert base == n_snap
+    # one slot less capacity: every slot below it as before, the next one untouched
+    if n_snap > 1:
+        big = torch.full((n_snap, H, K, V), 7.0, device=DEV)
+        chunk_fwd_varlen(xd["q"], xd["k"], xd["v"], xd["g"], xd["beta"], cud, xd["s0"],
+                         snapshot_interval=interval, snapshots=big[:n_snap - 1])
+        torch.cuda.synchronize()
+        assert torch.equal(big[:n_snap - 1], snaps[:n_snap - 1])
+        assert bool((big[n_snap - 1] == 7.0).all())
+
+
 def test_varlen_in_place_and_empty():
     from gated_delta_rule_66_amd import chunk_fwd_varlen
     say("varlen: final state in place; all sequences empty")
