@@ -205,7 +205,22 @@ def main():
                "hbm_frac": dec_gbs / HBM_PEAK_GBS, "bytes_per_step": dec_bytes,
                "kernel_avg_ms": dk["avg_ms"],
                "kernel_gbs": dec_bytes / (dk["avg_ms"] * 1e-3) / 1e9}
-        del d, pristine, state, od
+        # multi-token verification: the first 4 tokens of every sequence in one
+        # call, state read and written once, against 4 single steps
+        TV = 4
+        tok = lambda t: t[:TV].transpose(0, 1).contiguous()
+        dv = {n: tok(d[n]) for n in ("q", "k", "v", "g", "beta")}
+        ov = torch.empty((dcfg.N, TV, dcfg.H, dcfg.V), dtype=dcfg.dtype, device=dev)
+        state.copy_(pristine)
+        ms_verify = time_calls(lambda: kda.recurrent_steps(dv["q"], dv["k"], dv["v"], dv["g"], dv["beta"], state,
+                                                           out=ov), 2, 10)
+        verify_bytes = decode_bytes(dcfg.N, dcfg.H, dcfg.K, dcfg.V) + \
+            (TV - 1) * (dec_bytes - 8 * dcfg.N * dcfg.H * dcfg.K * dcfg.V)
+        dec["verify"] = {"tokens_per_sequence": TV, "ms": ms_verify,
+                         "tokens_per_s": dcfg.N * TV / (ms_verify * 1e-3),
+                         "achieved_gbs": verify_bytes / (ms_verify * 1e-3) / 1e9,
+                         "speedup_vs_single_steps": TV * ms_step / ms_verify}
+        del d, pristine, state, od, dv, ov
         torch.cuda.empty_cache()
 
     extra = {}

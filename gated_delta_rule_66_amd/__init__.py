@@ -17,10 +17,11 @@ from .kda import (  # noqa: F401
     profile_start,
     profile_stop,
     recurrent_step,
+    recurrent_steps,
     status_string,
     version,
 )
 from .build import LIB_PATH, build_library  # noqa: F401
 
-__all__ = ["chunk_fwd", "chunk_fwd_varlen", "chunk_fwd_varlen_workspace_size", "snapshot_count", "recurrent_step", "chunk_plan", "chunk_workspace_size", "profile_start", "profile_stop",
+__all__ = ["chunk_fwd", "chunk_fwd_varlen", "chunk_fwd_varlen_workspace_size", "snapshot_count", "recurrent_step", "recurrent_steps", "chunk_plan", "chunk_workspace_size", "profile_start", "profile_stop",
            "load_library", "build_library", "version", "status_string", "KDAError", "Plan"]

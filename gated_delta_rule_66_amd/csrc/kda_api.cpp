@@ -543,6 +543,39 @@ kda_status kda_chunk_fwd_varlen_snapshots(int N, const int* cu_seqlens, int T_to
                        snapshot_interval, snapshots, max_snapshots, workspace, workspace_bytes, stream);
 }
 
+kda_status kda_recurrent_steps(int N, int T, int H, int K, int V, kda_dtype dt,
+                               const void* q, const void* k, const void* v,
+                               const void* g, const void* beta,
+                               float* state, void* o, float* step_states, void* stream) {
+    if (N < 0 || T < 0 || H < 0 || K <= 0 || V <= 0) return KDA_ERR_INVALID_ARG;
+    if (check_dtype(dt) != KDA_OK) return KDA_ERR_INVALID_ARG;
+    if (!(K == 64 || K == 128) || !(V == 64 || V == 128)) return KDA_ERR_UNSUPPORTED;
+    if ((double)N * H > 1.0e9 || (double)N * T * H * (K > V ? K : V) > 9.0e15) return KDA_ERR_UNSUPPORTED;
+    const long nh = (long)N * H;
+    if (nh == 0 || T == 0) return KDA_OK;
+    if (!q || !k || !v || !g || !beta || !state || !o) return KDA_ERR_INVALID_ARG;
+    if (!aligned16(state) || (step_states && !aligned16(step_states))) return KDA_ERR_INVALID_ARG;
+    const uintptr_t es = elem_size(dt);
+    for (const void* t : {q, k, v, g, beta, (const void*)o})
+        if (reinterpret_cast<uintptr_t>(t) % es != 0) return KDA_ERR_INVALID_ARG;
+    if (step_states) {
+        // the two buffers may not share a byte
+        const uintptr_t a0 = reinterpret_cast<uintptr_t>(state), a1 = a0 + (size_t)nh * K * V * sizeof(float);
+        const uintptr_t b0 = reinterpret_cast<uintptr_t>(step_states),
+                        b1 = b0 + (size_t)nh * T * K * V * sizeof(float);
+        if (a0 < b1 && b0 < a1) return KDA_ERR_INVALID_ARG;
+    }
+    MultiDecodeParams p{};
+    p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta;
+    p.state = state;
+    p.o = o;
+    p.step_states = step_states;
+    p.N = N; p.T = T; p.H = H;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    return launch_timed("decode_steps", st, [&] { return launch_decode_multi((int)dt, K, V, p, st); }) ==
+                   hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 kda_status kda_recurrent_step(int N, int H, int K, int V, kda_dtype dt,
                               const void* q, const void* k, const void* v,
                               const void* g, const void* beta,

@@ -108,6 +108,106 @@ __global__ __launch_bounds__(256) void kda_decode_kernel(DecodeParams p) {
     }
 }
 
+// T consecutive tokens of each sequence in one launch (multi-token
+// verification): the tiling of kda_decode_kernel, the state slice held in
+// registers across the tokens and written once; optionally the state after
+// every token (so that a caller can resume after any accepted prefix).
+template <typename T, int K, int V, int VW>
+__global__ __launch_bounds__(256) void kda_decode_multi_kernel(MultiDecodeParams p) {
+    constexpr int NB = V / VW;
+    constexpr int CG = VW / 4;
+    constexpr int RG = 256 / CG;
+    constexpr int RPT = K / RG;
+    static_assert(CG * RG == 256 && RPT * RG == K, "decode tiling");
+    __shared__ float red[RG][CG][9];
+    __shared__ float qk_part[RG];
+    __shared__ float sk[K], sq[K], sa[K];
+
+    const int nh = blockIdx.x / NB;
+    const int cb = blockIdx.x % NB;
+    const int n = nh / p.H, h = nh % p.H;
+    const int tid = threadIdx.x;
+    const int cg = tid % CG, rg = tid / CG;
+    const int col = cb * VW + 4 * cg;
+    float* S = p.state + (size_t)nh * K * V;
+
+    f32x4 x[RPT];
+#pragma unroll
+    for (int r = 0; r < RPT; ++r)
+        x[r] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + (size_t)(rg * RPT + r) * V + col));
+
+    for (int t = 0; t < p.T; ++t) {
+        const size_t tok = ((size_t)n * p.T + t) * p.H + h;
+        const T* qp = reinterpret_cast<const T*>(p.q) + tok * K;
+        const T* kp = reinterpret_cast<const T*>(p.k) + tok * K;
+        const T* gp = reinterpret_cast<const T*>(p.g) + tok * K;
+        const T* vp = reinterpret_cast<const T*>(p.v) + tok * V;
+        __syncthreads();                                   // the previous token's LDS reads are done
+        for (int r = tid; r < K; r += 256) {
+            sk[r] = ld_scalar(kp + r);
+            sq[r] = ld_scalar(qp + r);
+            sa[r] = fast_exp2(clamp_gate_log2(ld_scalar(gp + r)));
+        }
+        __syncthreads();
+        float kk[RPT];
+        float y[4] = {0.f, 0.f, 0.f, 0.f}, z[4] = {0.f, 0.f, 0.f, 0.f};
+        float qk = 0.f;
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) {
+            const int row = rg * RPT + r;
+            kk[r] = sk[row];
+            const float qq = sq[row], a = sa[row];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                x[r][i] *= a;                              // S' = Diag(alpha) S
+                y[i] += x[r][i] * kk[r];
+                z[i] += x[r][i] * qq;
+            }
+            qk += qq * kk[r];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            red[rg][cg][i] = y[i];
+            red[rg][cg][4 + i] = z[i];
+        }
+        if (cg == 0) qk_part[rg] = qk;
+        __syncthreads();
+        float yf[4] = {0.f, 0.f, 0.f, 0.f}, zf[4] = {0.f, 0.f, 0.f, 0.f};
+        float qkf = 0.f;
+#pragma unroll
+        for (int r = 0; r < RG; ++r) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                yf[i] += red[r][cg][i];
+                zf[i] += red[r][cg][4 + i];
+            }
+            qkf += qk_part[r];
+        }
+        const float beta = ld_scalar(reinterpret_cast<const T*>(p.beta) + tok);
+        float u[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) u[i] = beta * (ld_scalar(vp + col + i) - yf[i]);
+        if (rg == 0) {
+            T* op = reinterpret_cast<T*>(p.o) + tok * V + col;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) op[i] = from_f32<T>(zf[i] + qkf * u[i]);
+        }
+#pragma unroll
+        for (int r = 0; r < RPT; ++r)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[r][i] += kk[r] * u[i];   // S = S' + k u^T
+        if (p.step_states) {
+            float* D = p.step_states + tok * K * V;
+#pragma unroll
+            for (int r = 0; r < RPT; ++r)
+                __builtin_nontemporal_store(x[r], reinterpret_cast<f32x4*>(D + (size_t)(rg * RPT + r) * V + col));
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < RPT; ++r)
+        __builtin_nontemporal_store(x[r], reinterpret_cast<f32x4*>(S + (size_t)(rg * RPT + r) * V + col));
+}
+
 // 64 columns per workgroup: a 128-wide state is split over two workgroups
 // (more of them in flight for the same bytes per step; measured faster)
 template <typename T, int K, int V>
@@ -123,6 +223,30 @@ static hipError_t launch_decode_kv(int K, int V, const DecodeParams& p, hipStrea
     if (K == 128 && V == 64) return launch_decode_t<T, 128, 64>(p, stream);
     if (K == 64 && V == 128) return launch_decode_t<T, 64, 128>(p, stream);
     if (K == 64 && V == 64) return launch_decode_t<T, 64, 64>(p, stream);
+    return hipErrorInvalidValue;
+}
+
+template <typename T, int K, int V>
+static hipError_t launch_decode_multi_t(const MultiDecodeParams& p, hipStream_t stream) {
+    constexpr int VW = 64;
+    hipLaunchKernelGGL((kda_decode_multi_kernel<T, K, V, VW>), dim3(p.N * p.H * (V / VW)), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_decode_multi_kv(int K, int V, const MultiDecodeParams& p, hipStream_t stream) {
+    if (K == 128 && V == 128) return launch_decode_multi_t<T, 128, 128>(p, stream);
+    if (K == 128 && V == 64) return launch_decode_multi_t<T, 128, 64>(p, stream);
+    if (K == 64 && V == 128) return launch_decode_multi_t<T, 64, 128>(p, stream);
+    if (K == 64 && V == 64) return launch_decode_multi_t<T, 64, 64>(p, stream);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_multi(int dtype, int K, int V, const MultiDecodeParams& p, hipStream_t stream) {
+    if ((long)p.N * p.H <= 0 || p.T <= 0) return hipSuccess;
+    if ((long)p.N * p.H * 2 > 2000000000L) return hipErrorInvalidValue;
+    if (dtype == 1) return launch_decode_multi_kv<bf16>(K, V, p, stream);
+    if (dtype == 0) return launch_decode_multi_kv<float>(K, V, p, stream);
     return hipErrorInvalidValue;
 }
 

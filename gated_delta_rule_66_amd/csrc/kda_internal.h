@@ -48,6 +48,20 @@ struct DecodeParams {
     int NH;                 // N * H
 };
 
+// T tokens per sequence in one call: q, k, g [N][T][H][K], v, o [N][T][H][V],
+// beta [N][T][H]; the state is read once and written once
+struct MultiDecodeParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* g;
+    const void* beta;
+    float* state;           // [N][H][K][V], in place
+    void* o;
+    float* step_states;     // [N][T][H][K][V] state after each token, or null
+    int N, T, H;
+};
+
 // ---- split path: intra-chunk pass, then state pass ----------------------------
 // Per (b, h, chunk) the intra-chunk pass writes one record of the operands the
 // state pass needs; all arrays row-major without padding, in the input dtype
@@ -133,5 +147,6 @@ hipError_t launch_chunk(int dtype, int K, int VB, const ChunkParams& p, int grid
 hipError_t launch_scan(int K, const ScanParams& p, hipStream_t stream);
 hipError_t launch_copy_state(const float* src, float* dst, size_t n, hipStream_t stream);
 hipError_t launch_decode(int dtype, int K, int V, const DecodeParams& p, hipStream_t stream);
+hipError_t launch_decode_multi(int dtype, int K, int V, const MultiDecodeParams& p, hipStream_t stream);
 
 }  // namespace kda

@@ -30,6 +30,7 @@ EXPORTED_SYMBOLS = (
     "kda_chunk_fwd_varlen",
     "kda_chunk_fwd_varlen_snapshots",
     "kda_recurrent_step",
+    "kda_recurrent_steps",
     "kda_status_string",
     "kda_version",
     "kda_profile_start",
@@ -74,6 +75,8 @@ def load_library(path: str = LIB_PATH):
     lib.kda_chunk_fwd_varlen_snapshots.restype = i
     lib.kda_recurrent_step.argtypes = [i, i, i, i, i, p, p, p, p, p, p, p, p]
     lib.kda_recurrent_step.restype = i
+    lib.kda_recurrent_steps.argtypes = [i, i, i, i, i, i, p, p, p, p, p, p, p, p, p]
+    lib.kda_recurrent_steps.restype = i
     lib.kda_status_string.argtypes = [i]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_version.argtypes = []
@@ -289,6 +292,40 @@ def chunk_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch
     if st != KDA_OK:
         raise KDAError(st, "kda_chunk_fwd_varlen")
     return out, final_state
+
+
+def recurrent_steps(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                    beta: torch.Tensor, state: torch.Tensor, *, out: Optional[torch.Tensor] = None,
+                    step_states=None):
+    """T tokens per sequence through ``kda_recurrent_steps`` (multi-token
+    verification); ``state`` is updated in place to the state after the last
+    token.  q, k, g: [N, T, H, K]; v: [N, T, H, V]; beta: [N, T, H]; state:
+    [N, H, K, V] fp32.  ``step_states``: None, True (allocate) or a
+    [N, T, H, K, V] fp32 tensor that receives the state after every token.
+    Returns o [N, T, H, V], or (o, step_states) when step states are asked for."""
+    N, T, H, K = q.shape
+    V = v.shape[-1]
+    dev = q.device
+    dt = q.dtype
+    for name, t, shp in (("q", q, (N, T, H, K)), ("k", k, (N, T, H, K)), ("g", g, (N, T, H, K)),
+                         ("v", v, (N, T, H, V)), ("beta", beta, (N, T, H))):
+        _check(t, name, shp, dt, dev)
+    _check(state, "state", (N, H, K, V), torch.float32, dev)
+    if out is None:
+        out = torch.empty((N, T, H, V), dtype=dt, device=dev)
+    else:
+        _check(out, "out", (N, T, H, V), dt, dev)
+    want_steps = step_states is not None and step_states is not False
+    if step_states is True:
+        step_states = torch.empty((N, T, H, K, V), dtype=torch.float32, device=dev)
+    elif want_steps:
+        _check(step_states, "step_states", (N, T, H, K, V), torch.float32, dev)
+    st = load_library().kda_recurrent_steps(N, T, H, K, V, _dtype_code(dt), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                            _ptr(beta), _ptr(state), _ptr(out),
+                                            _ptr(step_states) if want_steps else None, _stream_ptr(dev))
+    if st != KDA_OK:
+        raise KDAError(st, "kda_recurrent_steps")
+    return (out, step_states) if want_steps else out
 
 
 def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,

@@ -212,6 +212,24 @@ kda_status kda_recurrent_step(int N, int H, int K, int V, kda_dtype dt,
                               float* state, void* o, void* stream);
 
 /*
+ * T consecutive tokens of each of N sequences in one call (multi-token
+ * verification of a draft, as in speculative decoding): the same update as T
+ * calls of kda_recurrent_step, with the state read once and written once.
+ *
+ *   q, k, g : [N, T, H, K] dtype dt;  v : [N, T, H, V];  beta : [N, T, H]
+ *   state   : [N, H, K, V] fp32, updated IN PLACE to the state after token T
+ *   o       : [N, T, H, V] dtype dt (written), o_t = S_t^T q_t
+ *   step_states : [N, T, H, K, V] fp32, the state after each token (so that a
+ *                 caller can resume after any accepted prefix), or NULL.  It
+ *                 must not overlap state.
+ * T == 0 or N * H == 0 does nothing.  Sizes and dtypes as kda_recurrent_step.
+ */
+kda_status kda_recurrent_steps(int N, int T, int H, int K, int V, kda_dtype dt,
+                               const void* q, const void* k, const void* v,
+                               const void* g, const void* beta,
+                               float* state, void* o, float* step_states, void* stream);
+
+/*
  * Optional per-launch timing, for benchmarks and tracing.  After
  * kda_profile_start(max_launches), each kernel launched by kda_chunk_fwd or
  * kda_recurrent_step (up to max_launches of them) is bracketed by two HIP
@@ -219,7 +237,7 @@ kda_status kda_recurrent_step(int N, int H, int K, int V, kda_dtype dt,
  * kda_profile_stop waits for the recorded events, writes up to `cap` launch
  * names (static strings: "intra_chunk", "state_output", "state_summary",
  * "chunk_output", "chunk_summary", "segment_scan", "copy_state",
- * "varlen_prep", "decode_step") and durations in milliseconds, releases the
+ * "varlen_prep", "decode_step", "decode_steps") and durations in milliseconds, releases the
  * events, and returns the number of timed launches (-1: profiling was not
  * started or a HIP event query failed).  The recording state is process-wide
  * and not thread-safe; profiling is off unless started.

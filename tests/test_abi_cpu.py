@@ -216,6 +216,35 @@ def test_snapshot_count_formula():
     assert K_.snapshot_count([0, 640], 64) == 10
 
 
+def _steps(lib, N=2, T=3, H=2, K=128, V=128, dt=BF16, state=FAKE, steps=None, **kw):
+    p = ctypes.c_void_p
+    lib.kda_recurrent_steps.argtypes = [ctypes.c_int] * 6 + [p] * 9
+    lib.kda_recurrent_steps.restype = ctypes.c_int
+    t = {n: kw.get(n, FAKE) for n in ("q", "k", "v", "g", "beta", "o")}
+    return lib.kda_recurrent_steps(N, T, H, K, V, dt, *(p(t[n]) if t[n] else None for n in ("q", "k", "v", "g", "beta")),
+                                   p(state) if state else None, p(t["o"]) if t["o"] else None,
+                                   p(steps) if steps else None, None)
+
+
+def test_recurrent_steps_validation_before_any_launch():
+    lib = _lib()
+    assert _steps(lib, T=-1) == INVALID
+    assert _steps(lib, N=-1) == INVALID
+    assert _steps(lib, K=96) == UNSUPPORTED
+    assert _steps(lib, dt=7) == INVALID
+    assert _steps(lib, state=None) == INVALID
+    assert _steps(lib, state=FAKE + 4) == INVALID                 # 16-byte alignment
+    assert _steps(lib, q=FAKE + 1) == INVALID                     # element alignment
+    assert _steps(lib, steps=FAKE + 8) == INVALID                 # 16-byte alignment
+    # step states may not share a byte with the state
+    nbytes = 2 * 2 * 128 * 128 * 4
+    assert _steps(lib, steps=FAKE) == INVALID
+    assert _steps(lib, steps=FAKE + nbytes - 16) == INVALID
+    assert _steps(lib, steps=FAKE - 3 * nbytes + 16) == INVALID
+    assert _steps(lib, T=0) == OK                                 # nothing to do
+    assert _steps(lib, N=0) == OK
+
+
 def test_package_raises_without_library(tmp_path):
     saved = K_._lib
     K_._lib = None

@@ -448,6 +448,49 @@ def test_decode_steps_match_oracle(dtype, K, V):
     assert s_err(state, ref_state) < TOL[dtype]
 
 
+MULTI = [(torch.bfloat16, 128, 128, 4), (torch.bfloat16, 64, 128, 9), (torch.bfloat16, 128, 64, 1),
+         (torch.float32, 64, 64, 5)]
+
+
+@pytest.mark.parametrize("dtype,K,V,T", MULTI)
+def test_multi_token_steps(dtype, K, V, T):
+    """T tokens per sequence in one call: o, the final state and every
+    per-token state match the oracle, and equal (bit for bit) T successive
+    single decode steps."""
+    from gated_delta_rule_66_amd import recurrent_steps
+    say("decode multi dtype=%s K=%d V=%d T=%d" % (dtype, K, V, T))
+    N, H = 5, 3
+    d = make_decode(N, H, K, V, T, dtype, seed=23)
+    tok = lambda t: t.transpose(0, 1).contiguous()          # [T, N, ...] -> [N, T, ...]
+    xm = {n: tok(d[n]).to(DEV) for n in ("q", "k", "v", "g", "beta")}
+    state = d["state"].to(DEV).clone()
+    o, steps = recurrent_steps(xm["q"], xm["k"], xm["v"], xm["g"], xm["beta"], state, step_states=True)
+    torch.cuda.synchronize()
+    # oracle: the T tokens as a prefill of B = N sequences from the given state
+    qo, ko, vo, go, bo = (tok(d[n]) for n in ("q", "k", "v", "g", "beta"))
+    o_ref, s_ref = oracle.oracle_fwd(qo, ko, vo, go, bo, d["state"])
+    assert o_err(o, o_ref) < TOL[dtype]
+    assert s_err(state, s_ref) < TOL[dtype]
+    for t in range(T):
+        _, st_ref = oracle.oracle_fwd(qo[:, :t + 1], ko[:, :t + 1], vo[:, :t + 1], go[:, :t + 1], bo[:, :t + 1],
+                                      d["state"])
+        assert s_err(steps[:, t], st_ref) < TOL[dtype], t
+    # the same tokens one decode step at a time
+    x = to_dev(d)
+    st1 = x["state"].clone()
+    for t in range(T):
+        o1 = recurrent_step(x["q"][t], x["k"][t], x["v"][t], x["g"][t], x["beta"][t], st1)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o[:, t]), t
+        assert torch.equal(st1, steps[:, t]), t
+    assert torch.equal(st1, state)
+    # without step states only o and the state are written
+    state2 = d["state"].to(DEV).clone()
+    o2 = recurrent_steps(xm["q"], xm["k"], xm["v"], xm["g"], xm["beta"], state2)
+    torch.cuda.synchronize()
+    assert torch.equal(o2, o) and torch.equal(state2, state)
+
+
 def max_rel(o, o_ref):
     # decode output [N, H, V]: chains (n, h)
     from tests.parity import max_rel_l2
