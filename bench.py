@@ -178,7 +178,26 @@ def main():
     dom_bytes = per_kernel_bytes.get(dom, 0)
     dom_gbs = dom_bytes / (dom_ms * 1e-3) / 1e9
     traffic, traffic_note = recorded_traffic(dom, plan)
-    del x, o, sT, ws
+
+    # the same call with the output gate fused into the store of o, beside the
+    # ungated call followed by a separate elementwise o * sigmoid(gate)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(11)
+    z = torch.randn((B, T, H, V), generator=gen, device=dev).to(cfg.dtype)
+
+    def gated_step():
+        kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], True, None,
+                      out=o, final_state=sT, workspace=ws, gate=z)
+
+    def unfused_step():
+        prefill_step()
+        o.mul_(torch.sigmoid(z))
+
+    ms_gated = time_calls(gated_step, 2, args.steps)
+    ms_unfused = time_calls(unfused_step, 2, args.steps)
+    gate = {"ms": ms_gated, "tokens_per_s": B * T / (ms_gated * 1e-3), "ms_ungated": ms,
+            "ms_unfused": ms_unfused}
+    del x, o, sT, ws, z
     torch.cuda.empty_cache()
 
     # ------------------------------------------------------------ decode workload
@@ -346,6 +365,7 @@ def main():
         "mfma": {"achieved_tflops": tflops, "peak_tflops": BF16_PEAK_TFLOPS, "frac": tflops / BF16_PEAK_TFLOPS,
                  "algorithmic_flops_per_call": nflops},
         "kernels": kernels,
+        "gate": gate,
         "decode": dec,
         "cpu_baseline": cpu,
     }

@@ -221,14 +221,14 @@ size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int K, int V, kda_dtype
     return workspace_bytes_for(B, T, H, K, V, dt, pl);
 }
 
-kda_status kda_chunk_fwd(int B, int T, int H, int K, int V, kda_dtype dt,
-                         const void* q, const void* k, const void* v,
-                         const void* g, const void* beta,
-                         const float* initial_state,
-                         void* o, float* final_state,
-                         const kda_plan* plan,
-                         void* workspace, size_t workspace_bytes,
-                         void* stream) {
+static kda_status chunk_impl(int B, int T, int H, int K, int V, kda_dtype dt,
+                             const void* q, const void* k, const void* v,
+                             const void* g, const void* beta, const void* gate,
+                             const float* initial_state,
+                             void* o, float* final_state,
+                             const kda_plan* plan,
+                             void* workspace, size_t workspace_bytes,
+                             void* stream) {
     kda_status s = check_prefill_sizes(B, T, H, K, V, dt);
     if (s != KDA_OK) return s;
     const long bh = (long)B * H;
@@ -237,6 +237,7 @@ kda_status kda_chunk_fwd(int B, int T, int H, int K, int V, kda_dtype dt,
         if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(o) ||
             (reinterpret_cast<uintptr_t>(beta) % elem_size(dt)) != 0)
             return KDA_ERR_INVALID_ARG;
+        if (gate && !aligned16(gate)) return KDA_ERR_INVALID_ARG;
     }
     if ((initial_state && !aligned16(initial_state)) || (final_state && !aligned16(final_state)) ||
         (workspace && !aligned16(workspace)))
@@ -289,6 +290,7 @@ kda_status kda_chunk_fwd(int B, int T, int H, int K, int V, kda_dtype dt,
         if (pl.n_seg == 1) {
             sp.s0 = initial_state;
             sp.o = o;
+            sp.gate = gate;
             sp.sT = final_state;
             sp.n_vb = V / vb;
             sp.summary = 0;
@@ -328,6 +330,7 @@ kda_status kda_chunk_fwd(int B, int T, int H, int K, int V, kda_dtype dt,
         s3.s0 = initial_state;
         s3.seg_init = wsL;
         s3.o = o;
+        s3.gate = gate;
         s3.sT = aliased ? wsFinal : final_state;
         if (launch_timed("state_output", st, [&] {
                 return launch_state((int)dt, K, vb, s3, (int)(bh * pl.n_seg * s3.n_vb), st);
@@ -350,6 +353,7 @@ kda_status kda_chunk_fwd(int B, int T, int H, int K, int V, kda_dtype dt,
     if (pl.n_seg == 1) {
         p.s0 = initial_state;
         p.o = o;
+        p.gate = gate;
         p.sT = final_state;
         p.n_vb = V / vb;
         p.summary = 0;
@@ -391,6 +395,7 @@ kda_status kda_chunk_fwd(int B, int T, int H, int K, int V, kda_dtype dt,
     p3.s0 = initial_state;
     p3.seg_init = wsL;
     p3.o = o;
+    p3.gate = gate;
     p3.sT = aliased ? wsFinal : final_state;
     if (launch_timed("chunk_output", st, [&] {
             return launch_chunk((int)dt, K, vb, p3, (int)(bh * pl.n_seg * p3.n_vb), st);
@@ -401,6 +406,31 @@ kda_status kda_chunk_fwd(int B, int T, int H, int K, int V, kda_dtype dt,
         }) != hipSuccess)
         return KDA_ERR_HIP;
     return KDA_OK;
+}
+
+kda_status kda_chunk_fwd(int B, int T, int H, int K, int V, kda_dtype dt,
+                         const void* q, const void* k, const void* v,
+                         const void* g, const void* beta,
+                         const float* initial_state,
+                         void* o, float* final_state,
+                         const kda_plan* plan,
+                         void* workspace, size_t workspace_bytes,
+                         void* stream) {
+    return chunk_impl(B, T, H, K, V, dt, q, k, v, g, beta, nullptr, initial_state, o, final_state, plan,
+                      workspace, workspace_bytes, stream);
+}
+
+kda_status kda_chunk_fwd_gated(int B, int T, int H, int K, int V, kda_dtype dt,
+                               const void* q, const void* k, const void* v,
+                               const void* g, const void* beta, const void* gate,
+                               const float* initial_state,
+                               void* o, float* final_state,
+                               const kda_plan* plan,
+                               void* workspace, size_t workspace_bytes,
+                               void* stream) {
+    if (!gate && (long)B * H > 0 && T > 0) return KDA_ERR_INVALID_ARG;
+    return chunk_impl(B, T, H, K, V, dt, q, k, v, g, beta, gate, initial_state, o, final_state, plan,
+                      workspace, workspace_bytes, stream);
 }
 
 // ---- packed variable-length batch --------------------------------------------------
@@ -430,6 +460,7 @@ size_t kda_chunk_fwd_varlen_workspace_size(int N, int T_total, int H, int K, int
 
 static kda_status varlen_impl(int N, const int* cu_seqlens, int T_total, int H, int K, int V, kda_dtype dt,
                               const void* q, const void* k, const void* v, const void* g, const void* beta,
+                              const void* gate,
                               const float* initial_state, void* o, float* final_state, int snap_interval,
                               float* snapshots, int max_snapshots, void* workspace, size_t workspace_bytes,
                               void* stream) {
@@ -447,6 +478,7 @@ static kda_status varlen_impl(int N, const int* cu_seqlens, int T_total, int H, 
         if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(g) || !aligned16(o) ||
             (reinterpret_cast<uintptr_t>(beta) % elem_size(dt)) != 0)
             return KDA_ERR_INVALID_ARG;
+        if (gate && !aligned16(gate)) return KDA_ERR_INVALID_ARG;
     }
     if ((cu_seqlens && (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u)) ||
         (initial_state && !aligned16(initial_state)) || (final_state && !aligned16(final_state)) ||
@@ -501,6 +533,7 @@ static kda_status varlen_impl(int N, const int* cu_seqlens, int T_total, int H, 
     sp.rec = recs;
     sp.s0 = initial_state;
     sp.o = o;
+    sp.gate = gate;
     sp.sT = final_state;
     sp.B = N; sp.T = T_total; sp.H = H; sp.V = V; sp.NC = ncb;
     sp.n_seg = 1;
@@ -528,8 +561,18 @@ kda_status kda_chunk_fwd_varlen(int N, const int* cu_seqlens, int T_total, int H
                                 void* o, float* final_state,
                                 void* workspace, size_t workspace_bytes,
                                 void* stream) {
-    return varlen_impl(N, cu_seqlens, T_total, H, K, V, dt, q, k, v, g, beta, initial_state, o, final_state, 0,
-                       nullptr, 0, workspace, workspace_bytes, stream);
+    return varlen_impl(N, cu_seqlens, T_total, H, K, V, dt, q, k, v, g, beta, nullptr, initial_state, o,
+                       final_state, 0, nullptr, 0, workspace, workspace_bytes, stream);
+}
+
+kda_status kda_chunk_fwd_varlen_gated(int N, const int* cu_seqlens, int T_total, int H, int K, int V,
+                                      kda_dtype dt, const void* q, const void* k, const void* v,
+                                      const void* g, const void* beta, const void* gate,
+                                      const float* initial_state, void* o, float* final_state,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+    if (!gate && (long)N * H > 0 && T_total > 0) return KDA_ERR_INVALID_ARG;
+    return varlen_impl(N, cu_seqlens, T_total, H, K, V, dt, q, k, v, g, beta, gate, initial_state, o,
+                       final_state, 0, nullptr, 0, workspace, workspace_bytes, stream);
 }
 
 kda_status kda_chunk_fwd_varlen_snapshots(int N, const int* cu_seqlens, int T_total, int H, int K, int V,
@@ -539,8 +582,9 @@ kda_status kda_chunk_fwd_varlen_snapshots(int N, const int* cu_seqlens, int T_to
                                           float* snapshots, int max_snapshots,
                                           void* workspace, size_t workspace_bytes, void* stream) {
     if (snapshot_interval <= 0) return KDA_ERR_INVALID_ARG;
-    return varlen_impl(N, cu_seqlens, T_total, H, K, V, dt, q, k, v, g, beta, initial_state, o, final_state,
-                       snapshot_interval, snapshots, max_snapshots, workspace, workspace_bytes, stream);
+    return varlen_impl(N, cu_seqlens, T_total, H, K, V, dt, q, k, v, g, beta, nullptr, initial_state, o,
+                       final_state, snapshot_interval, snapshots, max_snapshots, workspace, workspace_bytes,
+                       stream);
 }
 
 kda_status kda_recurrent_steps(int N, int T, int H, int K, int V, kda_dtype dt,

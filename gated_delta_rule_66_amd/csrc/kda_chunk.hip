@@ -581,12 +581,17 @@ __global__ __launch_bounds__(256) void kda_chunk_kernel(ChunkParams p) {
             constexpr int PPR = OW * (int)SZ / 16;       // 16-byte pieces per row
             const __amdgpu_buffer_rsrc_t ro = make_rsrc(
                 reinterpret_cast<T*>(p.o) + ((size_t)(b * (size_t)p.T + t0) * p.H + h) * V + vcol0 + OW * w);
+            const size_t obase = ((size_t)(b * (size_t)p.T + t0) * p.H + h) * V + vcol0 + OW * w;
+            const __amdgpu_buffer_rsrc_t rz = make_rsrc(p.gate ? reinterpret_cast<const T*>(p.gate) + obase : nullptr);
 #pragma unroll
             for (int pc = l; pc < C * PPR; pc += 64) {
                 const int row = pc / PPR, seg = pc % PPR;
-                if (row < nt)
-                    buf_store16(ro, (unsigned)row * rowV + (unsigned)seg * 16u, 0u,
-                                *reinterpret_cast<const uint4*>(&sO[row * OW + seg * (16 / (int)SZ)]));
+                if (row < nt) {
+                    const unsigned off = (unsigned)row * rowV + (unsigned)seg * 16u;
+                    uint4 ov = *reinterpret_cast<const uint4*>(&sO[row * OW + seg * (16 / (int)SZ)]);
+                    if (p.gate) ov = gate_piece(ov, buf_load16(rz, off), (const T*)nullptr);
+                    buf_store16(ro, off, 0u, ov);
+                }
             }
         }
 #pragma unroll

@@ -348,4 +348,33 @@ __device__ __forceinline__ float clamp_gate_log2(float g) {
 __device__ __forceinline__ float ld_scalar(const bf16* p) { return (float)*p; }
 __device__ __forceinline__ float ld_scalar(const float* p) { return *p; }
 
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, unsigned voff) {
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+// Output gate on one 16-byte piece of o (input dtype): o * sigmoid(z), z of
+// the same layout; both widened to fp32, the product rounded once.
+__device__ __forceinline__ float sigmoidf_fast(float z) {
+    return __builtin_amdgcn_rcpf(1.f + fast_exp2(-1.4426950408889634f * z));
+}
+__device__ __forceinline__ uint4 gate_piece(uint4 o, uint4 z, const bf16*) {
+    const uint32_t ow[4] = {o.x, o.y, o.z, o.w}, zw[4] = {z.x, z.y, z.z, z.w};
+    float r[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        r[2 * i] = __uint_as_float(ow[i] << 16) * sigmoidf_fast(__uint_as_float(zw[i] << 16));
+        r[2 * i + 1] = __uint_as_float(ow[i] & 0xffff0000u) * sigmoidf_fast(__uint_as_float(zw[i] & 0xffff0000u));
+    }
+    const bf16x8 b = frag_from<bf16>(r);
+    return *reinterpret_cast<const uint4*>(&b);
+}
+__device__ __forceinline__ uint4 gate_piece(uint4 o, uint4 z, const float*) {
+    return make_uint4(__float_as_uint(__uint_as_float(o.x) * sigmoidf_fast(__uint_as_float(z.x))),
+                      __float_as_uint(__uint_as_float(o.y) * sigmoidf_fast(__uint_as_float(z.y))),
+                      __float_as_uint(__uint_as_float(o.z) * sigmoidf_fast(__uint_as_float(z.z))),
+                      __float_as_uint(__uint_as_float(o.w) * sigmoidf_fast(__uint_as_float(z.w))));
+}
+
 }  // namespace kda

@@ -19,6 +19,7 @@ struct ChunkParams {
     const float* s0;        // [B,H,K,V] initial state of segment 0, or null (zeros)
     const float* seg_init;  // [n_seg-1][B*H][K][V]: start state of segment s >= 1 at slot s-1
     void* o;                // [B,T,H,V] (output pass only)
+    const void* gate;       // [B,T,H,V] output gate pre-activation z (o <- o sigmoid(z)), or null
     float* sT;              // [B,H,K,V] final state or null (output pass only)
     float* wsP;             // summary pass: [n_seg-1][B*H][K][K]
     float* wsL;             // summary pass: [n_seg-1][B*H][K][V]
@@ -110,6 +111,7 @@ struct StateParams {
     const float* s0;        // [B,H,K,V] initial state of segment 0, or null (zeros)
     const float* seg_init;  // [n_seg-1][B*H][K][V]: start state of segment s >= 1 at slot s-1
     void* o;                // [B,T,H,V] (output pass only)
+    const void* gate;       // [B,T,H,V] output gate pre-activation z (o <- o sigmoid(z)), or null
     float* sT;              // [B,H,K,V] final state or null (output pass only)
     float* wsP;             // summary pass: [n_seg-1][B*H][K][K]
     float* wsL;             // summary pass: [n_seg-1][B*H][K][V]

@@ -61,10 +61,6 @@ __device__ __forceinline__ void seq_range(const int* cu, int i, int T_total, int
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, unsigned voff) {
-    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0);
-    return make_uint4(v[0], v[1], v[2], v[3]);
-}
 
 // 4 values of T as one 8- (bf16) or 16-byte (fp32) global store
 __device__ __forceinline__ void st4(bf16* p, const float* x) {
@@ -951,12 +947,17 @@ void kda_state_kernel(StateParams p) {
             constexpr int PPR = OW * (int)SZ / 16;
             const __amdgpu_buffer_rsrc_t ro = make_rsrc(
                 reinterpret_cast<T*>(p.o) + (trow * p.H + h) * V + vcol0 + OW * w);
+            const size_t obase = (trow * p.H + h) * V + vcol0 + OW * w;
+            const __amdgpu_buffer_rsrc_t rz = make_rsrc(p.gate ? reinterpret_cast<const T*>(p.gate) + obase : nullptr);
 #pragma unroll
             for (int pc = l; pc < C * PPR; pc += 64) {
                 const int row = pc / PPR, sg = pc % PPR;
-                if (row < nt)
-                    buf_store16(ro, (unsigned)row * rowV + (unsigned)sg * 16u, 0u,
-                                *reinterpret_cast<const uint4*>(&sO[row * OW + sg * (16 / (int)SZ)]));
+                if (row < nt) {
+                    const unsigned off = (unsigned)row * rowV + (unsigned)sg * 16u;
+                    uint4 ov = *reinterpret_cast<const uint4*>(&sO[row * OW + sg * (16 / (int)SZ)]);
+                    if (p.gate) ov = gate_piece(ov, buf_load16(rz, off), (const T*)nullptr);
+                    buf_store16(ro, off, 0u, ov);
+                }
             }
         }
         // S <- Diag(e^{G_C}) S + (K e^{G_C - G})^T U

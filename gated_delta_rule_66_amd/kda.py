@@ -26,8 +26,10 @@ EXPORTED_SYMBOLS = (
     "kda_chunk_fwd_plan",
     "kda_chunk_fwd_workspace_size",
     "kda_chunk_fwd",
+    "kda_chunk_fwd_gated",
     "kda_chunk_fwd_varlen_workspace_size",
     "kda_chunk_fwd_varlen",
+    "kda_chunk_fwd_varlen_gated",
     "kda_chunk_fwd_varlen_snapshots",
     "kda_recurrent_step",
     "kda_recurrent_steps",
@@ -67,6 +69,11 @@ def load_library(path: str = LIB_PATH):
     lib.kda_chunk_fwd.argtypes = [i, i, i, i, i, i, p, p, p, p, p, p, p, p,
                                   ctypes.POINTER(Plan), p, sz, p]
     lib.kda_chunk_fwd.restype = i
+    lib.kda_chunk_fwd_gated.argtypes = [i, i, i, i, i, i, p, p, p, p, p, p, p, p, p,
+                                        ctypes.POINTER(Plan), p, sz, p]
+    lib.kda_chunk_fwd_gated.restype = i
+    lib.kda_chunk_fwd_varlen_gated.argtypes = [i, p, i, i, i, i, i, p, p, p, p, p, p, p, p, p, p, sz, p]
+    lib.kda_chunk_fwd_varlen_gated.restype = i
     lib.kda_chunk_fwd_varlen_workspace_size.argtypes = [i, i, i, i, i, i]
     lib.kda_chunk_fwd_varlen_workspace_size.restype = sz
     lib.kda_chunk_fwd_varlen.argtypes = [i, p, i, i, i, i, i, p, p, p, p, p, p, p, p, p, sz, p]
@@ -175,14 +182,17 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
               beta: torch.Tensor, initial_state: Optional[torch.Tensor] = None,
               output_final_state: bool = True, plan=None, *,
               out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
-              workspace: Optional[torch.Tensor] = None):
-    """KDA chunked prefill through ``kda_chunk_fwd``.
+              workspace: Optional[torch.Tensor] = None, gate: Optional[torch.Tensor] = None):
+    """KDA chunked prefill through ``kda_chunk_fwd`` (``kda_chunk_fwd_gated``
+    with ``gate``).
 
     q, k, g: [B, T, H, K]; v: [B, T, H, V]; beta: [B, T, H] (one dtype, bf16
     or fp32, on one GPU); initial_state: [B, H, K, V] fp32 or None.
     Returns (o [B, T, H, V], final_state [B, H, K, V] fp32 or None).
     ``final_state`` may be passed to write in place (it may be
-    ``initial_state`` itself); ``plan`` = (n_seg, v_block), 0 = auto.
+    ``initial_state`` itself); ``plan`` = (n_seg, v_block, split), 0 = auto.
+    ``gate``: [B, T, H, V] output gate pre-activation; o is returned as
+    o * sigmoid(gate).
     """
     B, T, H, K = q.shape
     V = v.shape[-1]
@@ -206,6 +216,15 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
     if ws_bytes > 0 and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if gate is not None:
+        _check(gate, "gate", (B, T, H, V), dt, dev)
+        st = load_library().kda_chunk_fwd_gated(
+            B, T, H, K, V, _dtype_code(dt), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(gate),
+            _ptr(initial_state), _ptr(out), _ptr(final_state),
+            None if pl is None else ctypes.byref(pl), _ptr(workspace), ws_len, _stream_ptr(dev))
+        if st != KDA_OK:
+            raise KDAError(st, "kda_chunk_fwd_gated")
+        return out, final_state
     st = load_library().kda_chunk_fwd(
         B, T, H, K, V, _dtype_code(dt), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
         _ptr(initial_state), _ptr(out), _ptr(final_state),
@@ -234,7 +253,7 @@ def chunk_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch
                      initial_state: Optional[torch.Tensor] = None, output_final_state: bool = True, *,
                      out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
                      workspace: Optional[torch.Tensor] = None, snapshot_interval: int = 0,
-                     snapshots: Optional[torch.Tensor] = None):
+                     snapshots: Optional[torch.Tensor] = None, gate: Optional[torch.Tensor] = None):
     """Packed variable-length prefill through ``kda_chunk_fwd_varlen`` (or
     ``kda_chunk_fwd_varlen_snapshots`` when ``snapshot_interval`` > 0).
 
@@ -247,6 +266,8 @@ def chunk_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch
     its first (m + 1) * snapshot_interval tokens, sits at
     snapshot_count(cu_seqlens[:i + 1], snapshot_interval) + m.  ``snapshots``
     may be passed preallocated (its first dimension is the capacity).
+    ``gate``: [T_total, H, V] output gate pre-activation (o * sigmoid(gate));
+    not together with snapshots.
     """
     T_total, H, K = q.shape
     V = v.shape[-1]
@@ -273,6 +294,17 @@ def chunk_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch
     if ws_bytes > 0 and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if gate is not None:
+        if snapshot_interval:
+            raise ValueError("gate and snapshots are separate calls")
+        _check(gate, "gate", (T_total, H, V), dt, dev)
+        st = load_library().kda_chunk_fwd_varlen_gated(
+            N, _ptr(cu_seqlens), T_total, H, K, V, _dtype_code(dt), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+            _ptr(beta), _ptr(gate), _ptr(initial_state), _ptr(out), _ptr(final_state), _ptr(workspace), ws_len,
+            _stream_ptr(dev))
+        if st != KDA_OK:
+            raise KDAError(st, "kda_chunk_fwd_varlen_gated")
+        return out, final_state
     if snapshot_interval:
         if snapshots is None:
             snapshots = torch.empty((snapshot_count(cu_seqlens, snapshot_interval), H, K, V),

@@ -137,6 +137,30 @@ kda_status kda_chunk_fwd(int B, int T, int H, int K, int V, kda_dtype dt,
                          void* stream);
 
 /*
+ * kda_chunk_fwd with the output gate of the KDA block fused into the store
+ * of o (habr.com article on the Kimi K3 technical report, the section on
+ * gating after attention: a gate decides what fraction of the attention
+ * output enters the residual stream, and KDA blocks use it too; the form is
+ * not given there, the plainest reading is taken):
+ *
+ *   o[b,t,h,:] = RNE_dt( RNE_dt(S_t^T q_t) * sigmoid(gate[b,t,h,:]) )
+ *
+ *   gate : [B, T, H, V] dtype dt, the gate pre-activation, 16-byte aligned;
+ *          NULL is KDA_ERR_INVALID_ARG when there is work.
+ * The same result as kda_chunk_fwd followed by an elementwise o * sigmoid(gate)
+ * in fp32 rounded to dt, up to the 1-ulp exp2 and reciprocal of the sigmoid;
+ * it saves that pass over o.  Every other argument as kda_chunk_fwd.
+ */
+kda_status kda_chunk_fwd_gated(int B, int T, int H, int K, int V, kda_dtype dt,
+                               const void* q, const void* k, const void* v,
+                               const void* g, const void* beta, const void* gate,
+                               const float* initial_state,
+                               void* o, float* final_state,
+                               const kda_plan* plan,
+                               void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/*
  * Prefill of a packed batch of N variable-length sequences (the
  * prefix-caching and multi-token-verification use: every sequence resumes
  * from its own state and returns its own final state).  The habr.com
@@ -170,6 +194,16 @@ kda_status kda_chunk_fwd_varlen(int N, const int* cu_seqlens, int T_total, int H
                                 void* o, float* final_state,
                                 void* workspace, size_t workspace_bytes,
                                 void* stream);
+
+/*
+ * kda_chunk_fwd_varlen with the output gate fused as in kda_chunk_fwd_gated;
+ * gate : [T_total, H, V] dtype dt.
+ */
+kda_status kda_chunk_fwd_varlen_gated(int N, const int* cu_seqlens, int T_total, int H, int K, int V,
+                                      kda_dtype dt, const void* q, const void* k, const void* v,
+                                      const void* g, const void* beta, const void* gate,
+                                      const float* initial_state, void* o, float* final_state,
+                                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * kda_chunk_fwd_varlen that also returns state snapshots at fixed block

@@ -245,6 +245,25 @@ def test_recurrent_steps_validation_before_any_launch():
     assert _steps(lib, N=0) == OK
 
 
+def test_gated_entry_points_validate_the_gate():
+    lib = _lib()
+    p = ctypes.c_void_p
+    lib.kda_chunk_fwd_gated.argtypes = [ctypes.c_int] * 6 + [p] * 9 + [p, p, ctypes.c_size_t, p]
+    lib.kda_chunk_fwd_gated.restype = ctypes.c_int
+    args = lambda gate: (1, 100, 2, 128, 128, BF16, *([p(FAKE)] * 5), p(gate) if gate else None, None,
+                         p(FAKE), None, None, p(FAKE), 1 << 40, None)
+    assert lib.kda_chunk_fwd_gated(*args(None)) == INVALID         # a gated call needs the gate
+    assert lib.kda_chunk_fwd_gated(*args(FAKE + 8)) == INVALID     # 16-byte alignment
+    lib.kda_chunk_fwd_varlen_gated.argtypes = [ctypes.c_int, p] + [ctypes.c_int] * 5 + [p] * 9 + \
+        [p, ctypes.c_size_t, p]
+    lib.kda_chunk_fwd_varlen_gated.restype = ctypes.c_int
+    vargs = lambda gate, N=3: (N, p(FAKE), 300, 2, 128, 128, BF16, *([p(FAKE)] * 5),
+                               p(gate) if gate else None, None, p(FAKE), None, p(FAKE), 1 << 40, None)
+    assert lib.kda_chunk_fwd_varlen_gated(*vargs(None)) == INVALID
+    assert lib.kda_chunk_fwd_varlen_gated(*vargs(FAKE + 4)) == INVALID
+    assert lib.kda_chunk_fwd_varlen_gated(*vargs(None, N=0)) == OK   # nothing to do
+
+
 def test_package_raises_without_library(tmp_path):
     saved = K_._lib
     K_._lib = None

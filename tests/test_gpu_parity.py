@@ -306,6 +306,59 @@ def test_launch_profiling_names_every_launch():
     assert o_err(o, ref) < TOL[torch.bfloat16]
 
 
+# ------------------------------------------------------------------ fused output gate
+def _gate(shape, dtype, seed):
+    gen = torch.Generator().manual_seed(seed)
+    return (torch.randn(shape, generator=gen) * 2.0).to(dtype)
+
+
+def _gate_close(fused, o_plain, z, dtype):
+    """fused = RNE(o * sigmoid(z)) up to the sigmoid's hardware exp2 and
+    reciprocal (about 1 ulp each): within one bf16 rounding step of the
+    product torch forms in fp32, or a few fp32 ulp for fp32."""
+    ref = (o_plain.float() * torch.sigmoid(z.float()))
+    ulp = 2.0 ** -7 if dtype == torch.bfloat16 else 2.0 ** -19
+    return bool(((fused.float() - ref).abs() <= ulp * ref.abs() + 1e-30).all())
+
+
+@pytest.mark.parametrize("split", PATHS)
+@pytest.mark.parametrize("T,K,V,dtype,plan", [(300, 128, 128, torch.bfloat16, None),
+                                              (1000, 128, 128, torch.bfloat16, (3, 128)),
+                                              (130, 64, 128, torch.bfloat16, None),
+                                              (200, 64, 64, torch.float32, None)])
+def test_output_gate_fused(split, T, K, V, dtype, plan):
+    """o * sigmoid(gate) fused into the store of o: against the oracle's
+    o * sigmoid(gate) and against the unfused composition on the GPU; the
+    final state is untouched by the gate."""
+    say("gate split=%d T=%d K=%d V=%d %s plan=%s" % (split, T, K, V, dtype, plan))
+    d = make_prefill(2, T, 2, K, V, dtype, seed=70, s0_std=0.02)
+    z = _gate((2, T, 2, V), dtype, seed=71)
+    x = to_dev(d)
+    zd = z.to(DEV)
+    o_plain, s_plain = gpu_fwd(x, plan, split=split)
+    o_gated, s_gated = gpu_fwd(x, plan, split=split, gate=zd)
+    torch.cuda.synchronize()
+    assert torch.equal(s_gated, s_plain)
+    assert _gate_close(o_gated, o_plain, zd, dtype)
+    o_ref, _ = run_oracle(d)
+    g_ref = np.asarray(o_ref, np.float64) / (1.0 + np.exp(-z.double().numpy()))
+    assert o_err(o_gated, g_ref) < TOL[dtype]
+
+
+def test_output_gate_fused_varlen():
+    from gated_delta_rule_66_amd import chunk_fwd_varlen
+    say("gate varlen")
+    seqs, x, cu = _packed([100, 0, 257, 64], 2, 128, 128, torch.bfloat16, seed=72)
+    xd = to_dev(x)
+    z = _gate((int(cu[-1]), 2, 128), torch.bfloat16, seed=73).to(DEV)
+    cud = cu.to(DEV)
+    o_plain, s_plain = chunk_fwd_varlen(xd["q"], xd["k"], xd["v"], xd["g"], xd["beta"], cud, xd["s0"])
+    o_gated, s_gated = chunk_fwd_varlen(xd["q"], xd["k"], xd["v"], xd["g"], xd["beta"], cud, xd["s0"], gate=z)
+    torch.cuda.synchronize()
+    assert torch.equal(s_gated, s_plain)
+    assert _gate_close(o_gated, o_plain, z, torch.bfloat16)
+
+
 # ------------------------------------------------------------------ packed variable-length batches
 def _packed(lengths, H, K, V, dtype, seed, s0_std=0.02):
     """Per-sequence inputs of the recipe, packed along the token axis."""
