@@ -10,6 +10,7 @@ this module only compiles it with gcc and marshals numpy arrays.
 from .oracle import (  # noqa: F401
     build_oracle,
     oracle_fwd,
+    oracle_bwd,
     oracle_step,
     oracle_max_threads,
     ORACLE_SO,

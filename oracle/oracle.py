@@ -44,6 +44,8 @@ def _load():
         lib.kda_oracle_fwd.restype = i
         lib.kda_oracle_step.argtypes = [i, i, i, i, p, p, p, p, p, p, p, i]
         lib.kda_oracle_step.restype = i
+        lib.kda_oracle_bwd.argtypes = [i, i, i, i, i, p, p, p, p, p, p, p, p, p, p, p, p, p, p, i]
+        lib.kda_oracle_bwd.restype = i
         lib.kda_oracle_max_threads.argtypes = []
         lib.kda_oracle_max_threads.restype = i
         _lib = lib
@@ -118,3 +120,35 @@ def oracle_step(q, k, v, g, beta, state, *, nthreads: int = 0):
     if rc != 0:
         raise ValueError("oracle rejected sizes")
     return o
+
+
+def oracle_bwd(q, k, v, g, beta, s0, d_o, dsT=None, *, nthreads: int = 0):
+    """Token-by-token fp64 KDA backward (reverse-mode chain rule of
+    ``oracle_fwd``).
+
+    q, k, g: [B, T, H, K]; v: [B, T, H, V]; beta: [B, T, H]; s0: [B, H, K, V]
+    or None; d_o: [B, T, H, V] (dL/do) or None (zeros); dsT: [B, H, K, V]
+    (dL/dS_T) or None (zeros).
+    Returns (dq, dk, dv, dg, dbeta, ds0), fp64 in the input layouts.
+    """
+    q, k, v, g, beta, d_o = (_f32(x) for x in (q, k, v, g, beta, d_o))
+    s0, dsT = _f64(s0), _f64(dsT)
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    assert k.shape == (B, T, H, K) and g.shape == (B, T, H, K)
+    assert v.shape == (B, T, H, V) and beta.shape == (B, T, H)
+    for name, t, shp in (("s0", s0, (B, H, K, V)), ("d_o", d_o, (B, T, H, V)), ("dsT", dsT, (B, H, K, V))):
+        if t is not None:
+            assert t.shape == shp, name
+    dq = np.zeros((B, T, H, K), np.float64)
+    dk = np.zeros((B, T, H, K), np.float64)
+    dv = np.zeros((B, T, H, V), np.float64)
+    dg = np.zeros((B, T, H, K), np.float64)
+    dbeta = np.zeros((B, T, H), np.float64)
+    ds0 = np.zeros((B, H, K, V), np.float64)
+    rc = _load().kda_oracle_bwd(B, T, H, K, V, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(s0),
+                                _ptr(d_o), _ptr(dsT), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta),
+                                _ptr(ds0), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle rejected sizes (%d)" % rc)
+    return dq, dk, dv, dg, dbeta, ds0
