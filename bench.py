@@ -19,7 +19,7 @@ profiles/prefill_c1_traffic.json and reported only while the kernel
 source still has the hash recorded there.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--extra] [--no-cpu-baseline]
-       [--no-decode] [--cpu-seconds S]
+       [--no-decode] [--no-backward] [--cpu-seconds S]
 """
 from __future__ import annotations
 
@@ -84,6 +84,7 @@ def main():
     ap.add_argument("--extra", action="store_true", help="also time the 32K x 256-chain and 1M-token workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target duration of the oracle sample (heads of the 8K workload)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -199,6 +200,30 @@ def main():
             "ms_unfused": ms_unfused}
     del x, o, sT, ws, z
     torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------ backward, 8K workload
+    bwd = None
+    if not args.no_backward:
+        x = make_prefill_config(cfg, dev)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(12)
+        d_o = torch.randn((B, T, H, V), generator=gen, device=dev).to(cfg.dtype)
+        ws_b = torch.empty(max(kda.chunk_bwd_workspace_size(B, T, H, K, V, cfg.dtype), 1), dtype=torch.uint8,
+                           device=dev)
+
+        def bwd_step():
+            kda.chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], d_o, None, workspace=ws_b)
+
+        ms_b = time_calls(bwd_step, 1, 3)
+        # algorithmic bytes: the forward's inputs and dL/do read, the five gradients written
+        b_bytes = B * T * H * 2 * (2 * (3 * K + V + 1) + V)
+        bwd = {"workload": "gradients of the 8K prefill (dq, dk, dv, dg, dbeta; zero S0, no dL/dS_T)",
+               "ms": ms_b, "tokens_per_s": B * T / (ms_b * 1e-3),
+               "achieved_gbs": b_bytes / (ms_b * 1e-3) / 1e9,
+               "hbm_frac": b_bytes / (ms_b * 1e-3) / 1e9 / HBM_PEAK_GBS,
+               "workspace_bytes": ws_b.numel()}
+        del x, d_o, ws_b
+        torch.cuda.empty_cache()
 
     # ------------------------------------------------------------ decode workload
     dec = None
@@ -366,6 +391,7 @@ def main():
                  "algorithmic_flops_per_call": nflops},
         "kernels": kernels,
         "gate": gate,
+        "backward": bwd,
         "decode": dec,
         "cpu_baseline": cpu,
     }

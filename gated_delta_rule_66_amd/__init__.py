@@ -7,6 +7,8 @@ required: there is no CPU or PyTorch fallback.
 from .kda import (  # noqa: F401
     KDAError,
     Plan,
+    chunk_bwd,
+    chunk_bwd_workspace_size,
     chunk_fwd,
     chunk_fwd_varlen,
     chunk_fwd_varlen_workspace_size,
@@ -23,5 +25,5 @@ from .kda import (  # noqa: F401
 )
 from .build import LIB_PATH, build_library  # noqa: F401
 
-__all__ = ["chunk_fwd", "chunk_fwd_varlen", "chunk_fwd_varlen_workspace_size", "snapshot_count", "recurrent_step", "recurrent_steps", "chunk_plan", "chunk_workspace_size", "profile_start", "profile_stop",
+__all__ = ["chunk_fwd", "chunk_bwd", "chunk_bwd_workspace_size", "chunk_fwd_varlen", "chunk_fwd_varlen_workspace_size", "snapshot_count", "recurrent_step", "recurrent_steps", "chunk_plan", "chunk_workspace_size", "profile_start", "profile_stop",
            "load_library", "build_library", "version", "status_string", "KDAError", "Plan"]

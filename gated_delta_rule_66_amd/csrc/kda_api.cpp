@@ -587,6 +587,72 @@ kda_status kda_chunk_fwd_varlen_snapshots(int N, const int* cu_seqlens, int T_to
                        stream);
 }
 
+// ---- backward -------------------------------------------------------------------------
+static kda_status check_bwd_sizes(int B, int T, int H, int K, int V, kda_dtype dt) {
+    if (B < 0 || T < 0 || H < 0 || K <= 0 || V <= 0) return KDA_ERR_INVALID_ARG;
+    if (check_dtype(dt) != KDA_OK) return KDA_ERR_INVALID_ARG;
+    if (!(K == 64 || K == 128) || !(V == 64 || V == 128)) return KDA_ERR_UNSUPPORTED;
+    if ((double)B * T * H * (K > V ? K : V) * 8.0 > 9.0e15 || (double)B * H * (V / 16) > 2.0e9)
+        return KDA_ERR_UNSUPPORTED;
+    return KDA_OK;
+}
+
+size_t kda_chunk_bwd_workspace_size(int B, int T, int H, int K, int V, kda_dtype dt) {
+    if (check_bwd_sizes(B, T, H, K, V, dt) != KDA_OK) return (size_t)-1;
+    if ((long)B * H == 0 || T == 0) return 0;
+    return bwd_workspace_bytes(B, T, H, K, V);
+}
+
+kda_status kda_chunk_bwd(int B, int T, int H, int K, int V, kda_dtype dt,
+                         const void* q, const void* k, const void* v, const void* g, const void* beta,
+                         const float* initial_state, const void* d_o, const float* d_final_state,
+                         void* dq, void* dk, void* dv, void* dg, void* dbeta, float* d_initial_state,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+    kda_status s = check_bwd_sizes(B, T, H, K, V, dt);
+    if (s != KDA_OK) return s;
+    const long bh = (long)B * H;
+    const uintptr_t es = elem_size(dt);
+    if (bh > 0 && T > 0) {
+        if (!q || !k || !v || !g || !beta || !dq || !dk || !dv || !dg || !dbeta) return KDA_ERR_INVALID_ARG;
+        for (const void* t : {q, k, v, g, beta, d_o, (const void*)dq, (const void*)dk, (const void*)dv,
+                              (const void*)dg, (const void*)dbeta})
+            if (reinterpret_cast<uintptr_t>(t) % es != 0) return KDA_ERR_INVALID_ARG;
+    }
+    if ((initial_state && !aligned16(initial_state)) || (d_final_state && !aligned16(d_final_state)) ||
+        (d_initial_state && !aligned16(d_initial_state)) || (workspace && !aligned16(workspace)))
+        return KDA_ERR_INVALID_ARG;
+    if (bh == 0) return KDA_OK;
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (T == 0) {
+        // no tokens: dL/dS_0 = dL/dS_T
+        if (!d_initial_state) return KDA_OK;
+        return launch_timed("copy_state", st, [&] {
+                   return launch_copy_state(d_final_state, d_initial_state, (size_t)bh * K * V, st);
+               }) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    }
+    const size_t need = bwd_workspace_bytes(B, T, H, K, V);
+    if (!workspace || workspace_bytes < need) return KDA_ERR_WORKSPACE;
+    const size_t NG = (size_t)((T + 7) / 8);
+    const size_t ck_bytes = ((size_t)bh * NG * K * V * sizeof(float) + 255) & ~(size_t)255;
+    const size_t BTH = (size_t)bh * T;
+    const size_t ncb = (size_t)(V / 16);
+    BwdParams p{};
+    p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta;
+    p.s0 = initial_state;
+    p.d_o = d_o;
+    p.dsT = d_final_state;
+    p.dq = dq; p.dk = dk; p.dv = dv; p.dg = dg; p.dbeta = dbeta;
+    p.ds0 = d_initial_state;
+    p.ckpt = reinterpret_cast<float*>(workspace);
+    p.pdq = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(workspace) + ck_bytes);
+    p.pdk = p.pdq + ncb * BTH * K;
+    p.pda = p.pdk + ncb * BTH * K;
+    p.pdb = p.pda + ncb * BTH * K;
+    p.B = B; p.T = T; p.H = H; p.V = V;
+    return launch_timed("backward", st, [&] { return launch_bwd((int)dt, K, p, st); }) == hipSuccess
+               ? KDA_OK : KDA_ERR_HIP;
+}
+
 kda_status kda_recurrent_steps(int N, int T, int H, int K, int V, kda_dtype dt,
                                const void* q, const void* k, const void* v,
                                const void* g, const void* beta,

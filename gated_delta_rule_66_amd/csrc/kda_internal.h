@@ -149,6 +149,32 @@ hipError_t launch_chunk(int dtype, int K, int VB, const ChunkParams& p, int grid
 hipError_t launch_scan(int K, const ScanParams& p, hipStream_t stream);
 hipError_t launch_copy_state(const float* src, float* dst, size_t n, hipStream_t stream);
 hipError_t launch_decode(int dtype, int K, int V, const DecodeParams& p, hipStream_t stream);
+
+// ---- backward ------------------------------------------------------------------
+struct BwdParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* g;
+    const void* beta;
+    const float* s0;        // [B,H,K,V] or null (zeros)
+    const void* d_o;        // [B,T,H,V] dL/do or null (zeros)
+    const float* dsT;       // [B,H,K,V] dL/dS_T or null (zeros)
+    void* dq;               // [B,T,H,K] dtype
+    void* dk;
+    void* dv;               // [B,T,H,V]
+    void* dg;               // [B,T,H,K]
+    void* dbeta;            // [B,T,H]
+    float* ds0;             // [B,H,K,V] or null
+    float* ckpt;            // workspace: [B*H][ceil(T/8)][K][V] state every 8 tokens
+    float* pdq;             // workspace: [V/16][B*T*H][K] partial sums per column block
+    float* pdk;
+    float* pda;
+    float* pdb;             // [V/16][B*T*H]
+    int B, T, H, V;
+};
+hipError_t launch_bwd(int dtype, int K, const BwdParams& p, hipStream_t stream);
+size_t bwd_workspace_bytes(int B, int T, int H, int K, int V);
 hipError_t launch_decode_multi(int dtype, int K, int V, const MultiDecodeParams& p, hipStream_t stream);
 
 }  // namespace kda

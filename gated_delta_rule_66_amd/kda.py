@@ -33,6 +33,8 @@ EXPORTED_SYMBOLS = (
     "kda_chunk_fwd_varlen_snapshots",
     "kda_recurrent_step",
     "kda_recurrent_steps",
+    "kda_chunk_bwd_workspace_size",
+    "kda_chunk_bwd",
     "kda_status_string",
     "kda_version",
     "kda_profile_start",
@@ -84,6 +86,10 @@ def load_library(path: str = LIB_PATH):
     lib.kda_recurrent_step.restype = i
     lib.kda_recurrent_steps.argtypes = [i, i, i, i, i, i, p, p, p, p, p, p, p, p, p]
     lib.kda_recurrent_steps.restype = i
+    lib.kda_chunk_bwd_workspace_size.argtypes = [i, i, i, i, i, i]
+    lib.kda_chunk_bwd_workspace_size.restype = sz
+    lib.kda_chunk_bwd.argtypes = [i, i, i, i, i, i] + [p] * 14 + [p, sz, p]
+    lib.kda_chunk_bwd.restype = i
     lib.kda_status_string.argtypes = [i]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_version.argtypes = []
@@ -324,6 +330,55 @@ def chunk_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch
     if st != KDA_OK:
         raise KDAError(st, "kda_chunk_fwd_varlen")
     return out, final_state
+
+
+def chunk_bwd_workspace_size(B: int, T: int, H: int, K: int, V: int, dtype: torch.dtype) -> int:
+    n = load_library().kda_chunk_bwd_workspace_size(B, T, H, K, V, _dtype_code(dtype))
+    if n == ctypes.c_size_t(-1).value:
+        raise KDAError(KDA_ERR_INVALID_ARG, "kda_chunk_bwd_workspace_size")
+    return int(n)
+
+
+def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor, beta: torch.Tensor,
+              initial_state: Optional[torch.Tensor], d_o: Optional[torch.Tensor],
+              d_final_state: Optional[torch.Tensor] = None, *, want_d_initial_state: bool = True,
+              workspace: Optional[torch.Tensor] = None):
+    """Gradients of the prefill through ``kda_chunk_bwd``.
+
+    Inputs as ``chunk_fwd``; d_o: [B, T, H, V] (dL/do) or None; d_final_state:
+    [B, H, K, V] fp32 (dL/dS_T) or None.  Returns (dq, dk, dv, dg, dbeta,
+    d_initial_state or None), gradients in the input dtype, the last fp32.
+    """
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    dev = q.device
+    dt = q.dtype
+    for name, t, shp in (("q", q, (B, T, H, K)), ("k", k, (B, T, H, K)), ("g", g, (B, T, H, K)),
+                         ("v", v, (B, T, H, V)), ("beta", beta, (B, T, H))):
+        _check(t, name, shp, dt, dev)
+    if initial_state is not None:
+        _check(initial_state, "initial_state", (B, H, K, V), torch.float32, dev)
+    if d_o is not None:
+        _check(d_o, "d_o", (B, T, H, V), dt, dev)
+    if d_final_state is not None:
+        _check(d_final_state, "d_final_state", (B, H, K, V), torch.float32, dev)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    dg = torch.empty_like(g)
+    dbeta = torch.empty_like(beta)
+    ds0 = torch.empty((B, H, K, V), dtype=torch.float32, device=dev) if want_d_initial_state else None
+    ws_bytes = chunk_bwd_workspace_size(B, T, H, K, V, dt)
+    if ws_bytes > 0 and (workspace is None or workspace.numel() * workspace.element_size() < ws_bytes):
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load_library().kda_chunk_bwd(
+        B, T, H, K, V, _dtype_code(dt), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+        _ptr(d_o), _ptr(d_final_state), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(ds0),
+        _ptr(workspace), ws_len, _stream_ptr(dev))
+    if st != KDA_OK:
+        raise KDAError(st, "kda_chunk_bwd")
+    return dq, dk, dv, dg, dbeta, ds0
 
 
 def recurrent_steps(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,

@@ -264,6 +264,34 @@ kda_status kda_recurrent_steps(int N, int T, int H, int K, int V, kda_dtype dt,
                                float* state, void* o, float* step_states, void* stream);
 
 /*
+ * Backward of kda_chunk_fwd: the gradients of a loss L with respect to q, k,
+ * v, g (log alpha before the clamp), beta and the initial state, given dL/do
+ * and dL/dS_T.  The pages give no backward; this is the chain rule applied
+ * to the recurrence (section "Как хранить миллион токенов в памяти"), token
+ * by token in reverse.  The clamp passes the gradient inside its closed
+ * range [-5, 0] and blocks it outside.
+ *
+ *   q, k, g, v, beta, initial_state : the forward's inputs (same layouts)
+ *   d_o           : [B, T, H, V] dtype dt, dL/do, or NULL (zeros)
+ *   d_final_state : [B, H, K, V] fp32, dL/dS_T, or NULL (zeros)
+ *   dq, dk, dg    : [B, T, H, K] dtype dt (written)
+ *   dv            : [B, T, H, V] dtype dt (written)
+ *   dbeta         : [B, T, H] dtype dt (written)
+ *   d_initial_state : [B, H, K, V] fp32 (written) or NULL
+ *   workspace     : at least kda_chunk_bwd_workspace_size(...) bytes: the
+ *                   state every 8 tokens (B*H*ceil(T/8)*K*V fp32) and the
+ *                   per-16-column partial sums (V/16 * B*T*H*(3K+1) fp32).
+ * Sizes: K, V in {64, 128}; bf16 or fp32.  The forward states are recomputed
+ * (no saved activations are needed).  Results are deterministic.
+ */
+size_t kda_chunk_bwd_workspace_size(int B, int T, int H, int K, int V, kda_dtype dt);
+kda_status kda_chunk_bwd(int B, int T, int H, int K, int V, kda_dtype dt,
+                         const void* q, const void* k, const void* v, const void* g, const void* beta,
+                         const float* initial_state, const void* d_o, const float* d_final_state,
+                         void* dq, void* dk, void* dv, void* dg, void* dbeta, float* d_initial_state,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Optional per-launch timing, for benchmarks and tracing.  After
  * kda_profile_start(max_launches), each kernel launched by kda_chunk_fwd or
  * kda_recurrent_step (up to max_launches of them) is bracketed by two HIP
@@ -271,7 +299,7 @@ kda_status kda_recurrent_steps(int N, int T, int H, int K, int V, kda_dtype dt,
  * kda_profile_stop waits for the recorded events, writes up to `cap` launch
  * names (static strings: "intra_chunk", "state_output", "state_summary",
  * "chunk_output", "chunk_summary", "segment_scan", "copy_state",
- * "varlen_prep", "decode_step", "decode_steps") and durations in milliseconds, releases the
+ * "varlen_prep", "decode_step", "decode_steps", "backward") and durations in milliseconds, releases the
  * events, and returns the number of timed launches (-1: profiling was not
  * started or a HIP event query failed).  The recording state is process-wide
  * and not thread-safe; profiling is off unless started.

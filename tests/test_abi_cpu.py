@@ -264,6 +264,36 @@ def test_gated_entry_points_validate_the_gate():
     assert lib.kda_chunk_fwd_varlen_gated(*vargs(None, N=0)) == OK   # nothing to do
 
 
+def _bwd(lib, B=1, T=100, H=2, K=128, V=128, dt=BF16, ws=FAKE, ws_bytes=1 << 40, ds0=None, **kw):
+    p = ctypes.c_void_p
+    lib.kda_chunk_bwd.argtypes = [ctypes.c_int] * 6 + [p] * 14 + [p, ctypes.c_size_t, p]
+    lib.kda_chunk_bwd.restype = ctypes.c_int
+    t = {n: kw.get(n, FAKE) for n in ("q", "k", "v", "g", "beta", "do", "dq", "dk", "dv", "dg", "dbeta")}
+    pt = lambda n: p(t[n]) if t[n] else None
+    return lib.kda_chunk_bwd(B, T, H, K, V, dt, pt("q"), pt("k"), pt("v"), pt("g"), pt("beta"), None, pt("do"), None,
+                             pt("dq"), pt("dk"), pt("dv"), pt("dg"), pt("dbeta"), p(ds0) if ds0 else None,
+                             p(ws) if ws else None, ws_bytes, None)
+
+
+def test_backward_validation_before_any_launch():
+    lib = _lib()
+    assert _bwd(lib, K=96) == UNSUPPORTED
+    assert _bwd(lib, T=-1) == INVALID
+    assert _bwd(lib, dt=5) == INVALID
+    assert _bwd(lib, dq=None) == INVALID
+    assert _bwd(lib, dbeta=None) == INVALID
+    assert _bwd(lib, dv=FAKE + 1) == INVALID                    # element alignment
+    assert _bwd(lib, ds0=FAKE + 8) == INVALID                   # 16-byte alignment
+    assert _bwd(lib, ws=None) == WORKSPACE
+    assert _bwd(lib, B=0) == OK
+    lib.kda_chunk_bwd_workspace_size.restype = ctypes.c_size_t
+    n = lib.kda_chunk_bwd_workspace_size(1, 100, 2, 128, 128, BF16)
+    ck = -(-(2 * 13 * 128 * 128 * 4) // 256) * 256              # the state every 8 tokens
+    assert n == ck + 8 * (100 * 2) * (3 * 128 + 1) * 4          # partial sums per 16-column block
+    assert _bwd(lib, ws_bytes=n - 1) == WORKSPACE
+    assert lib.kda_chunk_bwd_workspace_size(1, 0, 2, 128, 128, BF16) == 0
+
+
 def test_package_raises_without_library(tmp_path):
     saved = K_._lib
     K_._lib = None
