@@ -79,3 +79,24 @@ def test_backward_deterministic_and_t0():
     out = chunk_bwd(z["q"], z["k"], z["v"], z["g"], z["beta"], x["s0"], None, dsT_d)
     torch.cuda.synchronize()
     assert torch.equal(out[5], dsT_d)          # no tokens: dL/dS_0 = dL/dS_T
+
+
+def test_backward_full_8k_workload_sampled():
+    """The 8K workload (B=1, T=8192, H=32, K=V=128 bf16) as bench.py times
+    it: all gradients of sampled (b, h) chains against the oracle."""
+    from gated_delta_rule_66_amd.inputs import CONFIGS, make_prefill_config
+    say("bwd full 8K workload, sampled chains")
+    c = CONFIGS["c1"]
+    x = make_prefill_config(c, "cpu")
+    B, T, H, K, V = c.B, c.T, c.H, c.K, c.V
+    gen = torch.Generator().manual_seed(12)
+    d_o = torch.randn((B, T, H, V), generator=gen).to(c.dtype)
+    xd = {n: (t.to(DEV) if isinstance(t, torch.Tensor) else t) for n, t in x.items()}
+    out = chunk_bwd(xd["q"], xd["k"], xd["v"], xd["g"], xd["beta"], xd["s0"], d_o.to(DEV), None)
+    torch.cuda.synchronize()
+    heads = [0, 17, 31]
+    sl = lambda t: t[:, :, heads].contiguous()          # the sampled chains side by side (oracle threads)
+    s0 = None if x["s0"] is None else x["s0"][:, heads].contiguous()
+    ref = oracle.oracle_bwd(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["g"]), sl(x["beta"]), s0, sl(d_o), None)
+    got = [sl(t.cpu()) for t in out[:5]] + [out[5][:, heads].cpu()]
+    _check(*got, ref, c.dtype)
