@@ -660,9 +660,11 @@ __global__ __launch_bounds__(256) void kda_scan_kernel(ScanParams p) {
         const int row = i / 16, c = i % 16;
         sS[row * LD + c] = p.s0 ? p.s0[((size_t)bh * K + row) * V + (size_t)cb * 16 + c] : 0.f;
     }
-    float a[TPW][KQ];
-    f32x4 lt[TPW];
-    auto load_seg = [&](int j) {
+    // two register sets: segment j + 1's P rows and L tile are in flight
+    // during step j (loads are issued as soon as a set's MFMAs have read it)
+    float aA[TPW][KQ], aB[TPW][KQ];
+    f32x4 lA[TPW], lB[TPW];
+    auto load_seg = [&](int j, float (&a)[TPW][KQ], f32x4 (&lt)[TPW]) {
         const float* P = p.wsP + ((size_t)j * p.BH + bh) * K * K;
         const float* Lj = p.wsL + ((size_t)j * p.BH + bh) * K * V;
 #pragma unroll
@@ -681,18 +683,23 @@ __global__ __launch_bounds__(256) void kda_scan_kernel(ScanParams p) {
             for (int e = 0; e < 4; ++e) lt[t][e] = Lj[(size_t)(16 * rt + 4 * lg + e) * V + col];
         }
     };
-    if (p.n_seg > 1) load_seg(0);
-    __syncthreads();
-    for (int j = 0; j + 1 < p.n_seg; ++j) {
+    // S_{j+1} = P_j S_j + L_j with set (a, lt); then the set takes segment j + 2
+    auto step = [&](int j, float (&a)[TPW][KQ], f32x4 (&lt)[TPW]) {
+        // the B operands (S_j rows) are read from LDS together, ahead of the
+        // MFMA chains, so the chains do not wait on each read
+        float bS[KQ];
+#pragma unroll
+        for (int ks = 0; ks < KQ; ++ks) bS[ks] = sS[(KQ * lg + ks) * LD + lr];
+        __builtin_amdgcn_sched_barrier(0);
         f32x4 acc[TPW];
 #pragma unroll
-        for (int t = 0; t < TPW; ++t) {
-            acc[t] = lt[t];
+        for (int t = 0; t < TPW; ++t) acc[t] = lt[t];
 #pragma unroll
-            for (int ks = 0; ks < KQ; ++ks)
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t][ks], sS[(KQ * lg + ks) * LD + lr], acc[t], 0, 0, 0);
-        }
-        if (j + 2 < p.n_seg) load_seg(j + 1);
+        for (int ks = 0; ks < KQ; ++ks)
+#pragma unroll
+            for (int t = 0; t < TPW; ++t)
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t][ks], bS[ks], acc[t], 0, 0, 0);
+        if (j + 3 < p.n_seg) load_seg(j + 2, a, lt);
         float* Lj = p.wsL + ((size_t)j * p.BH + bh) * K * V;
         __syncthreads();
 #pragma unroll
@@ -706,6 +713,13 @@ __global__ __launch_bounds__(256) void kda_scan_kernel(ScanParams p) {
             }
         }
         __syncthreads();
+    };
+    if (p.n_seg > 1) load_seg(0, aA, lA);
+    if (p.n_seg > 2) load_seg(1, aB, lB);
+    __syncthreads();
+    for (int j = 0; j + 1 < p.n_seg; j += 2) {
+        step(j, aA, lA);
+        if (j + 2 < p.n_seg) step(j + 1, aB, lB);
     }
 }
 
