@@ -79,9 +79,10 @@ kda_status device_cus(int* cus) {
 }
 
 // Resolve a (possibly partial) requested plan.  Needs the device CU count
-// only when something is left for the library to choose.
+// only when something is left for the library to choose (cus_fixed > 0:
+// plan for that many CUs instead of querying the device).
 kda_status resolve_plan(int B, int T, int H, int K, int V, kda_dtype dt, const kda_plan* req,
-                        kda_plan* out, int* cps_out) {
+                        kda_plan* out, int* cps_out, int cus_fixed = 0) {
     const int n_chunks = (T + kChunk - 1) / kChunk;
     const long bh = (long)B * H;
     int vb = req ? req->v_block : 0;
@@ -97,8 +98,8 @@ kda_status resolve_plan(int B, int T, int H, int K, int V, kda_dtype dt, const k
         const int cps_req = (n_chunks + ns - 1) / ns;
         if (n_chunks > cps_req) return KDA_ERR_UNSUPPORTED;
     }
-    int cus = 0;
-    if (vb == 0 || ns == 0 || split == 0) {
+    int cus = cus_fixed;
+    if (cus <= 0 && (vb == 0 || ns == 0 || split == 0)) {
         kda_status s = device_cus(&cus);
         if (s != KDA_OK) return s;
     }
@@ -597,10 +598,53 @@ static kda_status check_bwd_sizes(int B, int T, int H, int K, int V, kda_dtype d
     return KDA_OK;
 }
 
+// Chunk-parallel backward (where the forward's two-pass plan exists): the
+// workspace holds, 256-byte aligned in this order, the forward plan's segment
+// arrays, its chunk records, the state after every chunk, dL/dS after every
+// chunk, then the token-level checkpoints and partial sums.
+struct BwdLayout {
+    bool chunked;
+    kda_plan plan;
+    int cps, NC;
+    size_t seg, rec, snaps, adj;    // byte offsets (chunk-parallel schedule)
+    size_t tok;                     // byte offset of the checkpoints and partial sums
+    size_t total;                   // bytes
+};
+static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+static kda_status bwd_layout(int B, int T, int H, int K, int V, kda_dtype dt, BwdLayout* L) {
+    *L = BwdLayout{};
+    L->NC = (T + kChunk - 1) / kChunk;
+    if (split_variant_exists((int)dt, K, V, 64) && V % 64 == 0) {
+        // the forward inside the backward is planned for the 256 CUs of an
+        // MI355X, so that the workspace size does not depend on the device
+        kda_status s = resolve_plan(B, T, H, K, V, dt, nullptr, &L->plan, &L->cps, 256);
+        if (s != KDA_OK) return s;
+        L->chunked = L->plan.split == 2;
+    }
+    if (!L->chunked) {
+        // whole-sequence schedule: checkpoints and partial sums only
+        L->tok = 0;
+        L->total = bwd_workspace_bytes(B, T, H, K, V);
+        return KDA_OK;
+    }
+    const size_t bh = (size_t)B * H, kv = (size_t)K * V * sizeof(float);
+    size_t o = 0;
+    L->seg = o;   o += align256(segment_bytes(B, H, K, V, L->plan));
+    L->rec = o;   o += align256(bh * L->NC * record_bytes(K, V, dt));
+    L->snaps = o; o += align256(bh * L->NC * kv);
+    L->adj = o;   o += align256(bh * L->NC * kv);
+    L->tok = o;   o += bwd_workspace_bytes(B, T, H, K, V);
+    L->total = o;
+    return KDA_OK;
+}
+
 size_t kda_chunk_bwd_workspace_size(int B, int T, int H, int K, int V, kda_dtype dt) {
     if (check_bwd_sizes(B, T, H, K, V, dt) != KDA_OK) return (size_t)-1;
     if ((long)B * H == 0 || T == 0) return 0;
-    return bwd_workspace_bytes(B, T, H, K, V);
+    BwdLayout L;
+    if (bwd_layout(B, T, H, K, V, dt, &L) != KDA_OK) return (size_t)-1;
+    return L.total;
 }
 
 kda_status kda_chunk_bwd(int B, int T, int H, int K, int V, kda_dtype dt,
@@ -630,8 +674,11 @@ kda_status kda_chunk_bwd(int B, int T, int H, int K, int V, kda_dtype dt,
                    return launch_copy_state(d_final_state, d_initial_state, (size_t)bh * K * V, st);
                }) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
     }
-    const size_t need = bwd_workspace_bytes(B, T, H, K, V);
-    if (!workspace || workspace_bytes < need) return KDA_ERR_WORKSPACE;
+    BwdLayout L;
+    s = bwd_layout(B, T, H, K, V, dt, &L);
+    if (s != KDA_OK) return s;
+    if (!workspace || workspace_bytes < L.total) return KDA_ERR_WORKSPACE;
+    unsigned char* ws = reinterpret_cast<unsigned char*>(workspace);
     const size_t NG = (size_t)((T + 7) / 8);
     const size_t ck_bytes = ((size_t)bh * NG * K * V * sizeof(float) + 255) & ~(size_t)255;
     const size_t BTH = (size_t)bh * T;
@@ -643,12 +690,81 @@ kda_status kda_chunk_bwd(int B, int T, int H, int K, int V, kda_dtype dt,
     p.dsT = d_final_state;
     p.dq = dq; p.dk = dk; p.dv = dv; p.dg = dg; p.dbeta = dbeta;
     p.ds0 = d_initial_state;
-    p.ckpt = reinterpret_cast<float*>(workspace);
-    p.pdq = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(workspace) + ck_bytes);
+    p.ckpt = reinterpret_cast<float*>(ws + L.tok);
+    p.pdq = reinterpret_cast<float*>(ws + L.tok + ck_bytes);
     p.pdk = p.pdq + ncb * BTH * K;
     p.pda = p.pdk + ncb * BTH * K;
     p.pdb = p.pda + ncb * BTH * K;
     p.B = B; p.T = T; p.H = H; p.V = V;
+    if (L.chunked) {
+        // the forward's records and the state after every chunk (no output)
+        const int NC = L.NC;
+        unsigned char* recs = ws + L.rec;
+        float* snaps = reinterpret_cast<float*>(ws + L.snaps);
+        IntraParams ip{};
+        ip.q = q; ip.k = k; ip.v = v; ip.g = g; ip.beta = beta;
+        ip.rec = recs;
+        ip.B = B; ip.T = T; ip.H = H; ip.NC = NC;
+        const long items = bh * NC;
+        if (items > 2000000000L) return KDA_ERR_UNSUPPORTED;
+        ip.n_items = (int)items;
+        int cus = 0;
+        if (device_cus(&cus) != KDA_OK) return KDA_ERR_HIP;
+        const int igrid = (int)(items < cus ? items : cus);
+        if (launch_timed("bwd_intra_chunk", st, [&] { return launch_intra((int)dt, K, V, ip, igrid, st); }) !=
+            hipSuccess)
+            return KDA_ERR_HIP;
+        const kda_plan& pl = L.plan;
+        const int vb = pl.v_block;
+        StateParams sp{};
+        sp.rec = recs;
+        sp.B = B; sp.T = T; sp.H = H; sp.V = V; sp.NC = NC;
+        sp.n_seg = pl.n_seg;
+        sp.cps = L.cps;
+        sp.s0 = initial_state;
+        float* wsP = reinterpret_cast<float*>(ws + L.seg);
+        float* wsL = wsP + (size_t)(pl.n_seg - 1) * bh * K * K;
+        if (pl.n_seg > 1) {
+            const int vbs = ((int)dt == 1 && K == 128 && V == 128) ? K + V : vb;
+            StateParams s1 = sp;
+            s1.summary = 1;
+            s1.n_vb = (K + V) / vbs;
+            s1.wsP = wsP;
+            s1.wsL = wsL;
+            if (launch_timed("bwd_state_summary", st, [&] {
+                    return launch_state((int)dt, K, vbs, s1, (int)(bh * (pl.n_seg - 1) * s1.n_vb), st);
+                }) != hipSuccess)
+                return KDA_ERR_HIP;
+            ScanParams scp{};
+            scp.s0 = initial_state;
+            scp.wsP = wsP;
+            scp.wsL = wsL;
+            scp.BH = (int)bh;
+            scp.V = V;
+            scp.n_seg = pl.n_seg;
+            if (launch_timed("bwd_segment_scan", st, [&] { return launch_scan(K, scp, st); }) != hipSuccess)
+                return KDA_ERR_HIP;
+            sp.seg_init = wsL;
+        }
+        sp.summary = 0;
+        sp.n_vb = V / vb;
+        sp.snaps = snaps;
+        sp.snap_every = 1;
+        sp.max_snaps = B * NC;
+        sp.snap_stride = NC;
+        if (launch_timed("bwd_states", st, [&] {
+                return launch_state((int)dt, K, vb, sp, (int)(bh * pl.n_seg * sp.n_vb), st);
+            }) != hipSuccess)
+            return KDA_ERR_HIP;
+        // dL/dS at every chunk boundary, then every chunk's tokens at once
+        p.NC = NC;
+        p.rec = recs;
+        p.snaps = snaps;
+        p.adj = reinterpret_cast<float*>(ws + L.adj);
+        if (launch_timed("bwd_state_reverse", st, [&] { return launch_bwd_state((int)dt, K, p, st); }) !=
+            hipSuccess)
+            return KDA_ERR_HIP;
+    }
     return launch_timed("backward", st, [&] { return launch_bwd((int)dt, K, p, st); }) == hipSuccess
                ? KDA_OK : KDA_ERR_HIP;
 }

@@ -14,13 +14,25 @@
 //
 // The recurrence acts on every value column separately, and so does the dS
 // recurrence; only the key-side gradients (dq, dk, da, dbeta) sum over the
-// columns.  A workgroup therefore owns one (b, h, 16-column block) and runs
-// the whole sequence: a forward sweep that stores its state slice every 8
-// tokens, then a reverse sweep that rebuilds each 8-token group's states in
+// columns.  A token-level workgroup owns one (b, h, 16-column block) and a
+// token range: a forward sweep that stores its state slice every 8 tokens,
+// then a reverse sweep that rebuilds each 8-token group's states in
 // registers from its checkpoint and applies the reverse steps.  Per token it
 // writes dv for its columns and its block's partial sums of dq, dk, da and
 // dbeta; a second kernel adds the blocks' partials in a fixed order
 // (deterministic) and applies the gate derivative.
+//
+// Chunk-parallel schedule (where the forward's two-pass plan exists): the
+// token range of a workgroup is one 64-token chunk, so every (b, h, chunk,
+// column block) runs at once.  It needs the state before its chunk and dL/dS
+// after it.  The states come from the forward's state pass (a snapshot after
+// every chunk).  The adjoints come from a reverse pass over the chunk
+// records: the forward state pass maps S to U = U~ - W S,
+// O = Qh S + Mqk U and S' = Diag(e^{G_C}) S + KbT U, so its transpose maps
+// (dS', dO) to
+//   dU = Mqk^T dO + KbT^T dS'
+//   dS = Diag(e^{G_C}) dS' + Qh^T dO - W^T dU
+// chunk by chunk from the end of the sequence.
 //
 // 256 threads: thread (cg = tid & 3, rg = tid >> 2) holds rows
 // [RPT rg, RPT rg + RPT) x columns [4 cg, 4 cg + 4) of the K x 16 slice.
@@ -57,7 +69,10 @@ __global__ __launch_bounds__(256) void kda_bwd_kernel(BwdParams p) {
     __shared__ float red[2][4][2 * BW_VB];      // row-reduction exchange, double-buffered
 
     const int ncb = p.V / BW_VB;
-    const int bh = blockIdx.x / ncb, cb = blockIdx.x % ncb;
+    // whole sequence: workgroup (bh, cb); chunk-parallel: (bh, chunk, cb)
+    const int cb = blockIdx.x % ncb;
+    const int chunk = p.NC > 0 ? (blockIdx.x / ncb) % p.NC : 0;
+    const int bh = p.NC > 0 ? blockIdx.x / ncb / p.NC : blockIdx.x / ncb;
     const int b = bh / p.H, h = bh % p.H;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
     const int cg = tid & 3, rg = tid >> 2;
@@ -67,6 +82,11 @@ __global__ __launch_bounds__(256) void kda_bwd_kernel(BwdParams p) {
     const size_t KV = (size_t)K * V;
     const int NG = (T_ + GS - 1) / GS;
     float* ck = p.ckpt + (size_t)bh * NG * KV;  // [NG][K][V] fp32
+    // this workgroup's token range [t_begin, t_end) as groups [g_begin, g_end)
+    const int t_begin = p.NC > 0 ? chunk * kChunk : 0;
+    const int t_end = p.NC > 0 ? min(T_, t_begin + kChunk) : T_;
+    const int g_begin = t_begin / GS, g_end = (t_end + GS - 1) / GS;
+    const bool first = chunk == 0, last = p.NC == 0 || chunk == p.NC - 1;
     int rbuf = 0;
 
     // sum over all K rows of x[c] (this thread's 4 columns; NV = 4 or 8 values)
@@ -159,38 +179,46 @@ __global__ __launch_bounds__(256) void kda_bwd_kernel(BwdParams p) {
     };
 
     // ---- forward sweep: the state before every group's first token ----------------
+    // start: S0 (first chunk), else the forward's state after the previous
+    // chunk, snapshot slot b NC + chunk - 1 of [B NC][H][K][V]
+    const float* sinit = first ? (p.s0 ? p.s0 + (size_t)bh * KV : nullptr)
+                               : p.snaps + (((size_t)b * p.NC + chunk - 1) * H + h) * KV;
     float S[RPT][4];
 #pragma unroll
     for (int j = 0; j < RPT; ++j)
 #pragma unroll
         for (int c = 0; c < 4; ++c)
-            S[j][c] = p.s0 ? p.s0[(size_t)bh * KV + (size_t)(row0 + j) * V + col0 + c] : 0.f;
-    if (NG > 1) fetch_group(0, false);
-    for (int gi = 0; gi < NG; ++gi) {
+            S[j][c] = sinit ? sinit[(size_t)(row0 + j) * V + col0 + c] : 0.f;
+    if (g_end - g_begin > 1) fetch_group(g_begin, false);
+    for (int gi = g_begin; gi < g_end; ++gi) {
 #pragma unroll
         for (int j = 0; j < RPT; ++j)
             *reinterpret_cast<f32x4*>(ck + (size_t)gi * KV + (size_t)(row0 + j) * V + col0) =
                 f32x4{S[j][0], S[j][1], S[j][2], S[j][3]};
-        if (gi + 1 == NG) break;                 // the last group's end state is not needed
+        if (gi + 1 == g_end) break;              // the last group's end state is not needed
         stage_group();
-        if (gi + 2 < NG) fetch_group(gi + 1, false);
+        if (gi + 2 < g_end) fetch_group(gi + 1, false);
         for (int r = 0; r < GS; ++r) fwd_token(S, r);
     }
 
     // ---- reverse sweep ---------------------------------------------------------------
+    // start: dL/dS_T (last chunk), else the reverse state pass's adjoint of
+    // the state after this chunk, [B H][NC][K][V]
+    const float* dinit = last ? (p.dsT ? p.dsT + (size_t)bh * KV : nullptr)
+                              : p.adj + ((size_t)bh * p.NC + chunk) * KV;
     float dS[RPT][4];
 #pragma unroll
     for (int j = 0; j < RPT; ++j)
 #pragma unroll
         for (int c = 0; c < 4; ++c)
-            dS[j][c] = p.dsT ? p.dsT[(size_t)bh * KV + (size_t)(row0 + j) * V + col0 + c] : 0.f;
+            dS[j][c] = dinit ? dinit[(size_t)(row0 + j) * V + col0 + c] : 0.f;
     const size_t BTH = (size_t)p.B * T_ * H;
-    if (NG > 0) fetch_group(NG - 1, true);
-    for (int gi = NG - 1; gi >= 0; --gi) {
+    if (g_end > g_begin) fetch_group(g_end - 1, true);
+    for (int gi = g_end - 1; gi >= g_begin; --gi) {
         const int t0 = gi * GS;
         const int n = min(GS, T_ - t0);
         stage_group();
-        if (gi > 0) fetch_group(gi - 1, true);
+        if (gi > g_begin) fetch_group(gi - 1, true);
         // St[r] = state before token t0 + r, r = 0..n
         float St[GS + 1][RPT][4];
 #pragma unroll
@@ -296,11 +324,196 @@ __global__ __launch_bounds__(256) void kda_bwd_kernel(BwdParams p) {
             }
         }
     }
-    if (p.ds0) {
+    if (p.ds0 && first) {
 #pragma unroll
         for (int j = 0; j < RPT; ++j)
             *reinterpret_cast<f32x4*>(p.ds0 + (size_t)bh * KV + (size_t)(row0 + j) * V + col0) =
                 f32x4{dS[j][0], dS[j][1], dS[j][2], dS[j][3]};
+    }
+}
+
+// ---- reverse state pass ------------------------------------------------------------
+// Workgroup (b, h, block of VB = 16 NW value columns); wave w owns the block's
+// 16-column tile w.  Per chunk, from the last to the second: the chunk's W,
+// Qh, Mqk, KbT and e^{G_C} are staged in LDS as the record holds them
+// (row-major), and dO^T of the block's columns; the transposed operands
+// (Mqk^T, KbT^T, Qh^T, W^T) are gathered column-wise from those rows.  The
+// result dS is the adjoint of the state after the previous chunk.
+template <typename T, int K, int NW>
+struct BwdStateLayout {
+    static constexpr int SZ = (int)sizeof(T);
+    static constexpr int PAD = 16 / SZ;
+    static constexpr int VB = 16 * NW;
+    static constexpr int NT = 64 * NW;
+    static constexpr int LDK = K + PAD;          // W, Qh: [C][LDK]
+    static constexpr int LDC = kChunk + PAD;     // Mqk [C][LDC], KbT [K][LDC], dO^T [VB][LDC]
+    static constexpr int oW = 0;
+    static constexpr int oQh = oW + kChunk * LDK * SZ;
+    static constexpr int oM = oQh + kChunk * LDK * SZ;
+    static constexpr int oKbT = oM + kChunk * LDC * SZ;
+    static constexpr int oDoT = oKbT + K * LDC * SZ;
+    static constexpr int oEgc = oDoT + VB * LDC * SZ;
+    static constexpr int TOTAL = oEgc + K * 4;
+    static_assert(TOTAL <= 160 * 1024, "LDS budget exceeded");
+    // 16-byte pieces staged from a record: W | Qh | Mqk | KbT (contiguous in
+    // the record) | e^{G_C}
+    static constexpr int PRK = K * SZ / 16, PRC = kChunk * SZ / 16;
+    static constexpr int E1 = kChunk * PRK, E2 = E1 + kChunk * PRK, E3 = E2 + kChunk * PRC, E4 = E3 + K * PRC;
+    static constexpr int PTOT = E4 + K * 4 / 16;
+    static constexpr int NPT = (PTOT + NT - 1) / NT;
+    // dO: VB columns of C token rows
+    static constexpr int PDR = VB * SZ / 16;     // pieces per token row
+    static constexpr int NPD = (kChunk * PDR + NT - 1) / NT;
+};
+
+template <typename T, int K, int NW>
+__global__ __launch_bounds__(64 * NW) void kda_bwd_state_kernel(BwdParams p) {
+    using L = BwdStateLayout<T, K, NW>;
+    using Frag = typename FragOf<T>::type;
+    constexpr int C = kChunk, VB = L::VB, NT = L::NT, NPT = L::NPT, NPD = L::NPD;
+    constexpr int LDK = L::LDK, LDC = L::LDC, CT = K / 16, KS = K / 32;
+    constexpr int SZ = L::SZ, EPP = 16 / SZ;
+
+    __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
+    const T* sW = reinterpret_cast<const T*>(smem + L::oW);
+    const T* sQh = reinterpret_cast<const T*>(smem + L::oQh);
+    const T* sM = reinterpret_cast<const T*>(smem + L::oM);
+    const T* sKbT = reinterpret_cast<const T*>(smem + L::oKbT);
+    T* sDoT = reinterpret_cast<T*>(smem + L::oDoT);
+    const float* sEgc = reinterpret_cast<const float*>(smem + L::oEgc);
+
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lg = l >> 4, lr = l & 15;
+    const int nvb = p.V / VB;
+    // the column blocks of one (b, h) read the same records: one XCD (L2)
+    const int G = gridDim.x, x = blockIdx.x;
+    const int lid = ((G & 7) == 0) ? (x & 7) * (G >> 3) + (x >> 3) : x;
+    const int vb = lid % nvb, bh = lid / nvb;
+    const int b = bh / p.H, h = bh % p.H;
+    const int V = p.V, NC = p.NC, T_ = p.T, H = p.H;
+    const size_t KV = (size_t)K * V;
+    const int col = vb * VB + 16 * w + lr;
+    const RecLayout RL = rec_layout(K, V, SZ);
+    const unsigned char* rec0 = p.rec + (size_t)bh * NC * RL.bytes;
+
+    // dS' of the last chunk: dL/dS_T; accumulator layout (rows 16 ct + 4 lg + e, column lr)
+    f32x4 dS[CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            dS[ct][e] = p.dsT ? p.dsT[(size_t)bh * KV + (size_t)(16 * ct + 4 * lg + e) * V + col] : 0.f;
+
+    uint4 pre[NPT], dpre[NPD];
+    auto load_chunk = [&](int ci) {
+        const __amdgpu_buffer_rsrc_t rr = make_rsrc(rec0 + (size_t)ci * RL.bytes);
+#pragma unroll
+        for (int m = 0; m < NPT; ++m) {
+            const int pc = tid + NT * m;
+            const unsigned off = pc < L::E4 ? (unsigned)RL.oW + (unsigned)pc * 16u
+                                            : (unsigned)RL.oEgc + (unsigned)(pc - L::E4) * 16u;
+            pre[m] = pc < L::PTOT ? buf_load16(rr, off) : make_uint4(0, 0, 0, 0);
+        }
+        const int t0 = ci * C, nt = min(C, T_ - t0);
+        const T* dob = p.d_o ? reinterpret_cast<const T*>(p.d_o) + (((size_t)b * T_ + t0) * H + h) * V + vb * VB
+                             : nullptr;
+        const __amdgpu_buffer_rsrc_t rd = make_rsrc(dob);
+        const unsigned rowV = (unsigned)H * V * SZ;
+#pragma unroll
+        for (int m = 0; m < NPD; ++m) {
+            const int pc = tid + NT * m, t = pc / L::PDR, sg = pc % L::PDR;
+            dpre[m] = (dob && pc < C * L::PDR && t < nt) ? buf_load16(rd, (unsigned)t * rowV + (unsigned)sg * 16u)
+                                                         : make_uint4(0, 0, 0, 0);
+        }
+    };
+    auto store_chunk = [&]() {
+#pragma unroll
+        for (int m = 0; m < NPT; ++m) {
+            const int pc = tid + NT * m;
+            unsigned char* dst = nullptr;
+            if (pc < L::E1) {
+                dst = smem + L::oW + (pc / L::PRK) * LDK * SZ + (pc % L::PRK) * 16;
+            } else if (pc < L::E2) {
+                const int q = pc - L::E1;
+                dst = smem + L::oQh + (q / L::PRK) * LDK * SZ + (q % L::PRK) * 16;
+            } else if (pc < L::E3) {
+                const int q = pc - L::E2;
+                dst = smem + L::oM + (q / L::PRC) * LDC * SZ + (q % L::PRC) * 16;
+            } else if (pc < L::E4) {
+                const int q = pc - L::E3;
+                dst = smem + L::oKbT + (q / L::PRC) * LDC * SZ + (q % L::PRC) * 16;
+            } else if (pc < L::PTOT) {
+                dst = smem + L::oEgc + (pc - L::E4) * 16;
+            }
+            if (dst) *reinterpret_cast<uint4*>(dst) = pre[m];
+        }
+        // dO^T: element e of piece (t, sg) is column EPP sg + e of token t
+#pragma unroll
+        for (int m = 0; m < NPD; ++m) {
+            const int pc = tid + NT * m;
+            if (pc < C * L::PDR) {
+                const int t = pc / L::PDR, sg = pc % L::PDR;
+                T v[EPP];
+                __builtin_memcpy(v, &dpre[m], 16);
+#pragma unroll
+                for (int e = 0; e < EPP; ++e) sDoT[(EPP * sg + e) * LDC + t] = v[e];
+            }
+        }
+    };
+    // A fragment of X^T for X row-major [reduction][row] in LDS: slot s of
+    // lane (lr, lg) holds X[32 ks + 4 lg + s][r0 + lr] (s < 4) and
+    // X[32 ks + 16 + 4 lg + s - 4][r0 + lr], the slot order of the B fragments
+    auto gather = [&](const T* X, int ld, int ks, int r0) {
+        Frag f;
+        const T* q0 = X + (32 * ks + 4 * lg) * ld + r0 + lr;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f[i] = q0[i * ld];
+            f[4 + i] = q0[(16 + i) * ld];
+        }
+        return f;
+    };
+
+    if (NC > 1) load_chunk(NC - 1);
+    for (int ci = NC - 1; ci >= 1; --ci) {
+        store_chunk();
+        __syncthreads();
+        if (ci > 1) load_chunk(ci - 1);
+        Frag bdo[2], bds[KS];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) bdo[ks] = ld_frag_perm<T>(&sDoT[(16 * w + lr) * LDC + 32 * ks + 4 * lg]);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) bds[ks] = frag_from_tiles<T>(dS[2 * ks], dS[2 * ks + 1]);
+        // -dU = -(Mqk^T dO + KbT^T dS'), 4 token tiles
+        f32x4 ndU[4];
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) acc = mma(acc, gather(sM, LDC, ks, 16 * ti), bdo[ks]);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) acc = mma(acc, gather(sKbT, LDC, ks, 16 * ti), bds[ks]);
+            ndU[ti] = -acc;
+        }
+        Frag bdu[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) bdu[ks] = frag_from_tiles<T>(ndU[2 * ks], ndU[2 * ks + 1]);
+        // dS = Diag(e^{G_C}) dS' + Qh^T dO - W^T dU
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+            const f32x4 eg = *reinterpret_cast<const f32x4*>(&sEgc[16 * ct + 4 * lg]);
+            f32x4 acc = dS[ct] * eg;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) acc = mma(acc, gather(sQh, LDK, ks, 16 * ct), bdo[ks]);
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) acc = mma(acc, gather(sW, LDK, ks, 16 * ct), bdu[ks]);
+            dS[ct] = acc;
+        }
+        float* dst = p.adj + ((size_t)bh * NC + ci - 1) * KV;
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dst[(size_t)(16 * ct + 4 * lg + e) * V + col] = dS[ct][e];
+        __syncthreads();
     }
 }
 
@@ -336,7 +549,8 @@ __global__ __launch_bounds__(256) void kda_bwd_reduce_kernel(BwdParams p) {
 
 template <typename T, int K>
 static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
-    const long wgs = (long)p.B * p.H * (p.V / BW_VB);
+    const long wgs = (long)p.B * p.H * (p.NC > 0 ? p.NC : 1) * (p.V / BW_VB);
+    if (wgs > 2000000000L) return hipErrorInvalidValue;
     hipLaunchKernelGGL((kda_bwd_kernel<T, K>), dim3((unsigned)wgs), dim3(256), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -352,6 +566,27 @@ hipError_t launch_bwd(int dtype, int K, const BwdParams& p, hipStream_t stream) 
     } else if (dtype == 0) {
         if (K == 128) return launch_bwd_t<float, 128>(p, stream);
         if (K == 64) return launch_bwd_t<float, 64>(p, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <typename T, int K>
+static hipError_t launch_bwd_state_t(const BwdParams& p, hipStream_t stream) {
+    constexpr int NW = 4;                        // 64 value columns per workgroup
+    const long wgs = (long)p.B * p.H * (p.V / (16 * NW));
+    if (wgs > 2000000000L) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((kda_bwd_state_kernel<T, K, NW>), dim3((unsigned)wgs), dim3(64 * NW), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_state(int dtype, int K, const BwdParams& p, hipStream_t stream) {
+    if (p.NC <= 1 || (long)p.B * p.H == 0) return hipSuccess;
+    if (p.V % 64 != 0) return hipErrorInvalidValue;
+    if (dtype == 1) {
+        if (K == 128) return launch_bwd_state_t<bf16, 128>(p, stream);
+        if (K == 64) return launch_bwd_state_t<bf16, 64>(p, stream);
+    } else if (dtype == 0) {
+        if (K == 64) return launch_bwd_state_t<float, 64>(p, stream);
     }
     return hipErrorInvalidValue;
 }

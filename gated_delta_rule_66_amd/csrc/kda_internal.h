@@ -18,7 +18,7 @@ struct ChunkParams {
     const void* beta;
     const float* s0;        // [B,H,K,V] initial state of segment 0, or null (zeros)
     const float* seg_init;  // [n_seg-1][B*H][K][V]: start state of segment s >= 1 at slot s-1
-    void* o;                // [B,T,H,V] (output pass only)
+    void* o;                // [B,T,H,V] (output pass only; null: states only, no output)
     const void* gate;       // [B,T,H,V] output gate pre-activation z (o <- o sigmoid(z)), or null
     float* sT;              // [B,H,K,V] final state or null (output pass only)
     float* wsP;             // summary pass: [n_seg-1][B*H][K][K]
@@ -110,7 +110,7 @@ struct StateParams {
     const unsigned char* rec;
     const float* s0;        // [B,H,K,V] initial state of segment 0, or null (zeros)
     const float* seg_init;  // [n_seg-1][B*H][K][V]: start state of segment s >= 1 at slot s-1
-    void* o;                // [B,T,H,V] (output pass only)
+    void* o;                // [B,T,H,V] (output pass only; null: states only, no output)
     const void* gate;       // [B,T,H,V] output gate pre-activation z (o <- o sigmoid(z)), or null
     float* sT;              // [B,H,K,V] final state or null (output pass only)
     float* wsP;             // summary pass: [n_seg-1][B*H][K][K]
@@ -122,13 +122,14 @@ struct StateParams {
     const int* cu_seqlens;
     const int* chunk_off;
     int N;
-    // state snapshots of a packed batch (output pass; null: none): after every
-    // snap_every chunks that lie wholly inside sequence i, the state goes to
-    // slot snap_off[i] + m of snaps [max_snaps][H][K][V] (slots past max_snaps
-    // are skipped)
+    // state snapshots (output pass; null: none): after every snap_every chunks
+    // that lie wholly inside sequence i, the state goes to slot
+    // snap_off[i] + m of snaps [max_snaps][H][K][V] (packed batch), or to slot
+    // i * snap_stride + m when snap_off is null (regular batch); slots past
+    // max_snaps are skipped
     float* snaps;
     const int* snap_off;
-    int snap_every, max_snaps;
+    int snap_every, max_snaps, snap_stride;
 };
 
 bool split_variant_exists(int dtype, int K, int V, int VB);
@@ -172,8 +173,16 @@ struct BwdParams {
     float* pda;
     float* pdb;             // [V/16][B*T*H]
     int B, T, H, V;
+    // chunk-parallel schedule (NC = chunks per sequence; 0: one workgroup per
+    // (b, h, column block) over the whole sequence)
+    int NC;
+    const unsigned char* rec;   // [B*H*NC] records of the forward's intra-chunk pass
+    const float* snaps;     // [B*NC][H][K][V]: slot b NC + c = state after chunk c
+    float* adj;             // [B*H][NC][K][V]: dL/dS after chunk c (c < NC - 1)
 };
 hipError_t launch_bwd(int dtype, int K, const BwdParams& p, hipStream_t stream);
+// the reverse state pass: p.adj for every chunk boundary (NC > 1)
+hipError_t launch_bwd_state(int dtype, int K, const BwdParams& p, hipStream_t stream);
 size_t bwd_workspace_bytes(int B, int T, int H, int K, int V);
 hipError_t launch_decode_multi(int dtype, int K, int V, const MultiDecodeParams& p, hipStream_t stream);
 

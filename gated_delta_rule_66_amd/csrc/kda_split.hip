@@ -910,7 +910,7 @@ void kda_state_kernel(StateParams p) {
             Ub[j][0] = frag_from_tiles<T>(U[j][0], U[j][1]);
             Ub[j][1] = frag_from_tiles<T>(U[j][2], U[j][3]);
         }
-        if (!SUMMARY) {
+        if (!SUMMARY && p.o) {
             // O = (Q e^G) S + Mqk U, staged in this wave's own (consumed) U~ rows
             constexpr int OW = 16 * NTW;
             T* sO = sUtT + 16 * tile0 * LDT;
@@ -1006,7 +1006,7 @@ void kda_state_kernel(StateParams p) {
         if constexpr (!SUMMARY) {
             // state snapshot after every snap_every whole chunks of a sequence
             if (p.snaps && (ci + 1) % p.snap_every == 0 && row0 + (size_t)(ci + 1) * C <= row_end) {
-                const int slot = p.snap_off[b] + (ci + 1) / p.snap_every - 1;
+                const int slot = (p.snap_off ? p.snap_off[b] : b * p.snap_stride) + (ci + 1) / p.snap_every - 1;
                 if (slot < p.max_snaps) {
                     float* sd = p.snaps + ((size_t)slot * p.H + h) * K * V;
 #pragma unroll

@@ -287,9 +287,16 @@ def test_backward_validation_before_any_launch():
     assert _bwd(lib, ws=None) == WORKSPACE
     assert _bwd(lib, B=0) == OK
     lib.kda_chunk_bwd_workspace_size.restype = ctypes.c_size_t
-    n = lib.kda_chunk_bwd_workspace_size(1, 100, 2, 128, 128, BF16)
     ck = -(-(2 * 13 * 128 * 128 * 4) // 256) * 256              # the state every 8 tokens
-    assert n == ck + 8 * (100 * 2) * (3 * 128 + 1) * 4          # partial sums per 16-column block
+    tok = ck + 8 * (100 * 2) * (3 * 128 + 1) * 4                # partial sums per 16-column block
+    # whole-sequence schedule (fp32 at K = V = 128): checkpoints and partial sums
+    assert lib.kda_chunk_bwd_workspace_size(1, 100, 2, 128, 128, F32) == tok
+    # chunk-parallel schedule: 2 chunks of 2 (b, h) chains, one segment: the
+    # chunk records (W, Qh, Mqk, KbT, U~^T bf16; e^{G_C} fp32), the state
+    # after every chunk and dL/dS after every chunk (fp32), then as above
+    n = lib.kda_chunk_bwd_workspace_size(1, 100, 2, 128, 128, BF16)
+    rec = (64 * 128 * 2 * 4 + 64 * 64 * 2 + 128 * 4 + 255) // 256 * 256
+    assert n == 4 * rec + 2 * (4 * 128 * 128 * 4) + tok
     assert _bwd(lib, ws_bytes=n - 1) == WORKSPACE
     assert lib.kda_chunk_bwd_workspace_size(1, 0, 2, 128, 128, BF16) == 0
 
