@@ -10,7 +10,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libkda.so")
-SOURCES = ["kda_api.cpp", "kda_chunk.hip", "kda_split.hip", "kda_decode.hip", "kda_bwd.hip"]
+SOURCES = ["kda_api.cpp", "kda_chunk.hip", "kda_split.hip", "kda_decode.hip", "kda_bwd.hip", "kda_bwd_chunk.hip"]
 ARCH = "gfx950"
 
 

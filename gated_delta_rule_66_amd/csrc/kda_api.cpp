@@ -598,24 +598,31 @@ static kda_status check_bwd_sizes(int B, int T, int H, int K, int V, kda_dtype d
     return KDA_OK;
 }
 
-// Chunk-parallel backward (where the forward's two-pass plan exists): the
+// Chunk-form backward (where the forward's two-pass plan exists): the
 // workspace holds, 256-byte aligned in this order, the forward plan's segment
 // arrays, its chunk records, the state after every chunk, dL/dS after every
-// chunk, then the token-level checkpoints and partial sums.
+// chunk, then the fp32 per-chunk intermediates of the gradient kernels.
+// Elsewhere the token-level schedule: checkpoints and partial sums only.
 struct BwdLayout {
     bool chunked;
     kda_plan plan;
     int cps, NC;
-    size_t seg, rec, snaps, adj;    // byte offsets (chunk-parallel schedule)
-    size_t tok;                     // byte offset of the checkpoints and partial sums
-    size_t total;                   // bytes
+    size_t seg, rec, snaps, adj, inter;   // byte offsets (chunk form)
+    size_t tok;                           // byte offset of the checkpoints and partial sums (token level)
+    size_t total;                         // bytes
 };
+// fp32 values per chunk of the chunk-form intermediates: dU, D, dQh, dKb,
+// dW, rs, dKh, Et
+static size_t bwd_inter_floats(int K, int V) {
+    const size_t c = kChunk;
+    return c * V + c * c + 4 * c * K + K + c * c;
+}
 static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 static kda_status bwd_layout(int B, int T, int H, int K, int V, kda_dtype dt, BwdLayout* L) {
     *L = BwdLayout{};
     L->NC = (T + kChunk - 1) / kChunk;
-    if (split_variant_exists((int)dt, K, V, 64) && V % 64 == 0) {
+    if (split_variant_exists((int)dt, K, V, 64) && bwd_chunk_variant_exists((int)dt, K, V) && V % 64 == 0) {
         // the forward inside the backward is planned for the 256 CUs of an
         // MI355X, so that the workspace size does not depend on the device
         kda_status s = resolve_plan(B, T, H, K, V, dt, nullptr, &L->plan, &L->cps, 256);
@@ -634,7 +641,7 @@ static kda_status bwd_layout(int B, int T, int H, int K, int V, kda_dtype dt, Bw
     L->rec = o;   o += align256(bh * L->NC * record_bytes(K, V, dt));
     L->snaps = o; o += align256(bh * L->NC * kv);
     L->adj = o;   o += align256(bh * L->NC * kv);
-    L->tok = o;   o += bwd_workspace_bytes(B, T, H, K, V);
+    L->inter = o; o += align256(bh * L->NC * bwd_inter_floats(K, V) * sizeof(float));
     L->total = o;
     return KDA_OK;
 }
@@ -679,10 +686,6 @@ kda_status kda_chunk_bwd(int B, int T, int H, int K, int V, kda_dtype dt,
     if (s != KDA_OK) return s;
     if (!workspace || workspace_bytes < L.total) return KDA_ERR_WORKSPACE;
     unsigned char* ws = reinterpret_cast<unsigned char*>(workspace);
-    const size_t NG = (size_t)((T + 7) / 8);
-    const size_t ck_bytes = ((size_t)bh * NG * K * V * sizeof(float) + 255) & ~(size_t)255;
-    const size_t BTH = (size_t)bh * T;
-    const size_t ncb = (size_t)(V / 16);
     BwdParams p{};
     p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta;
     p.s0 = initial_state;
@@ -690,11 +693,6 @@ kda_status kda_chunk_bwd(int B, int T, int H, int K, int V, kda_dtype dt,
     p.dsT = d_final_state;
     p.dq = dq; p.dk = dk; p.dv = dv; p.dg = dg; p.dbeta = dbeta;
     p.ds0 = d_initial_state;
-    p.ckpt = reinterpret_cast<float*>(ws + L.tok);
-    p.pdq = reinterpret_cast<float*>(ws + L.tok + ck_bytes);
-    p.pdk = p.pdq + ncb * BTH * K;
-    p.pda = p.pdk + ncb * BTH * K;
-    p.pdb = p.pda + ncb * BTH * K;
     p.B = B; p.T = T; p.H = H; p.V = V;
     if (L.chunked) {
         // the forward's records and the state after every chunk (no output)
@@ -756,15 +754,38 @@ kda_status kda_chunk_bwd(int B, int T, int H, int K, int V, kda_dtype dt,
                 return launch_state((int)dt, K, vb, sp, (int)(bh * pl.n_seg * sp.n_vb), st);
             }) != hipSuccess)
             return KDA_ERR_HIP;
-        // dL/dS at every chunk boundary, then every chunk's tokens at once
+        // dL/dS at every chunk boundary (and dU of every chunk), then the
+        // gradients of every chunk at once
         p.NC = NC;
         p.rec = recs;
         p.snaps = snaps;
         p.adj = reinterpret_cast<float*>(ws + L.adj);
+        const size_t nch = (size_t)bh * NC, c = kChunk;
+        float* f = reinterpret_cast<float*>(ws + L.inter);
+        p.cdU = f;  f += nch * c * V;
+        p.cD = f;   f += nch * c * c;
+        p.cdQh = f; f += nch * c * K;
+        p.cdKb = f; f += nch * c * K;
+        p.cdW = f;  f += nch * c * K;
+        p.crs = f;  f += nch * K;
+        p.cdKh = f; f += nch * c * K;
+        p.cEt = f;
         if (launch_timed("bwd_state_reverse", st, [&] { return launch_bwd_state((int)dt, K, p, st); }) !=
             hipSuccess)
             return KDA_ERR_HIP;
+        return launch_timed("bwd_chunks", st, [&] { return launch_bwd_chunk((int)dt, K, V, p, st); }) ==
+                       hipSuccess ? KDA_OK : KDA_ERR_HIP;
     }
+    // token-level schedule over the whole sequence
+    const size_t NG = (size_t)((T + 7) / 8);
+    const size_t ck_bytes = ((size_t)bh * NG * K * V * sizeof(float) + 255) & ~(size_t)255;
+    const size_t BTH = (size_t)bh * T;
+    const size_t ncb = (size_t)(V / 16);
+    p.ckpt = reinterpret_cast<float*>(ws + L.tok);
+    p.pdq = reinterpret_cast<float*>(ws + L.tok + ck_bytes);
+    p.pdk = p.pdq + ncb * BTH * K;
+    p.pda = p.pdk + ncb * BTH * K;
+    p.pdb = p.pda + ncb * BTH * K;
     return launch_timed("backward", st, [&] { return launch_bwd((int)dt, K, p, st); }) == hipSuccess
                ? KDA_OK : KDA_ERR_HIP;
 }

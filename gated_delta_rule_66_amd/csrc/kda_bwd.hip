@@ -473,11 +473,13 @@ __global__ __launch_bounds__(64 * NW) void kda_bwd_state_kernel(BwdParams p) {
         return f;
     };
 
-    if (NC > 1) load_chunk(NC - 1);
-    for (int ci = NC - 1; ci >= 1; --ci) {
+    // every chunk's dU goes to p.cdU (chunk-form gradients); the adjoint
+    // before chunk ci (ci >= 1) to p.adj
+    load_chunk(NC - 1);
+    for (int ci = NC - 1; ci >= 0; --ci) {
         store_chunk();
         __syncthreads();
-        if (ci > 1) load_chunk(ci - 1);
+        if (ci > 0) load_chunk(ci - 1);
         Frag bdo[2], bds[KS];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) bdo[ks] = ld_frag_perm<T>(&sDoT[(16 * w + lr) * LDC + 32 * ks + 4 * lg]);
@@ -494,6 +496,14 @@ __global__ __launch_bounds__(64 * NW) void kda_bwd_state_kernel(BwdParams p) {
             for (int ks = 0; ks < KS; ++ks) acc = mma(acc, gather(sKbT, LDC, ks, 16 * ti), bds[ks]);
             ndU[ti] = -acc;
         }
+        {
+            float* du = p.cdU + ((size_t)bh * NC + ci) * kChunk * V;
+#pragma unroll
+            for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) du[(size_t)(16 * ti + 4 * lg + e) * V + col] = -ndU[ti][e];
+        }
+        if (ci == 0 && !p.ds0) break;
         Frag bdu[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) bdu[ks] = frag_from_tiles<T>(ndU[2 * ks], ndU[2 * ks + 1]);
@@ -508,7 +518,8 @@ __global__ __launch_bounds__(64 * NW) void kda_bwd_state_kernel(BwdParams p) {
             for (int ks = 0; ks < 2; ++ks) acc = mma(acc, gather(sW, LDK, ks, 16 * ct), bdu[ks]);
             dS[ct] = acc;
         }
-        float* dst = p.adj + ((size_t)bh * NC + ci - 1) * KV;
+        // the adjoint before chunk ci: after chunk ci - 1, or dL/dS_0
+        float* dst = ci > 0 ? p.adj + ((size_t)bh * NC + ci - 1) * KV : p.ds0 + (size_t)bh * KV;
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
@@ -580,7 +591,7 @@ static hipError_t launch_bwd_state_t(const BwdParams& p, hipStream_t stream) {
 }
 
 hipError_t launch_bwd_state(int dtype, int K, const BwdParams& p, hipStream_t stream) {
-    if (p.NC <= 1 || (long)p.B * p.H == 0) return hipSuccess;
+    if (p.NC <= 0 || (long)p.B * p.H == 0) return hipSuccess;
     if (p.V % 64 != 0) return hipErrorInvalidValue;
     if (dtype == 1) {
         if (K == 128) return launch_bwd_state_t<bf16, 128>(p, stream);

@@ -1,0 +1,652 @@
+// Chunk-form backward of the KDA prefill for gfx950: the gradients of one
+// 64-token chunk with respect to q, k, v, g and beta, all chunks at once.
+//
+// The pages give no backward.  This is the chain rule applied to the chunk
+// form of the forward (page "Kimi K3 — открытая модель, которая обошла
+// закрытых лидеров рынка" (aiblin.ru), section "Как распараллелили
+// последовательное обновление": the tokens of a chunk are handled together
+// and only the state passes from chunk to chunk).  Per chunk, with S the
+// state before it, G the in-chunk inclusive cumsum of the clamped log-gates
+// and e^{G_C} the chunk total, the forward computes
+//   Ak[s,r] = sum_c k_s k_r e^{G_s - G_r}  (r < s),  A = diag(beta) Ak
+//   M[t,s]  = sum_c q_t k_s e^{G_t - G_s}  (s <= t)
+//   W = (I + A)^{-1} diag(beta) (K e^{G}),  U~ = (I + A)^{-1} diag(beta) V
+//   U = U~ - W S,  O = (Q e^{G}) S + M U,  S' = Diag(e^{G_C}) S + (K e^{G_C - G})^T U.
+// Given dO, dL/dS' (from the reverse state pass, which also hands over
+// dU = M^T dO + (K e^{G_C - G}) dL/dS'):
+//   D    = tril(dO U^T)                    dQh = dO S^T
+//   dKb  = U dS'^T                         dW  = -dU S^T
+//   (I + A)^T [dBv | dBk] = [dU | dW]      (back substitution)
+//   dv   = diag(beta) dBv                  dKh = diag(beta) dBk
+//   E    = -tril_strict(dBv U~^T + dBk W^T),  Et = diag(beta) E
+//   dbeta_s = dBv_s . v_s + dBk_s . (k_s e^{G_s}) + sum_r E[s,r] Ak[s,r]
+//   X1[s] = sum_{r<s} Et[s,r] k_r e^{G_s - G_r}    X2[r] = sum_{s>r} Et[s,r] k_s e^{G_s - G_r}
+//   Y1[t] = sum_{s<=t} D[t,s] k_s e^{G_t - G_s}    Y2[s] = sum_{t>=s} D[t,s] q_t e^{G_t - G_s}
+//   dq   = dQh e^{G} + Y1
+//   dk   = dKh e^{G} + X1 + X2 + Y2 + dKb e^{G_C - G}
+//   dG   = dQh q e^{G} + dKh k e^{G} - dKb k e^{G_C - G} + k (X1 - X2 - Y2) + q Y1
+//   dG_C += e^{G_C} rowsum(S * dS') + sum_s dKb_s k_s e^{G_C - G_s}
+//   dg_t = [-5 <= g_t <= 0] sum_{t' >= t} dG_{t'}
+// Every gated product runs per 16-token sub-chunk pair with sub-chunk
+// reference gates R_j (the cumsum before sub-chunk j), so that every
+// exponent is either <= 0 or within a sub-chunk (at most 80 at the clamp
+// floor), as in the forward.
+//
+// Three kernels, one workgroup (4 waves) per (b, h, chunk):
+//   vside  : U, D, dQh, dKb, dW and the e^{G_C} rowsum term (value-side products)
+//   ksolve : Ak, the back substitution, dv, dKh, Et, dbeta
+//   kgrad  : the gated products and dq, dk, dg (fp32 throughout)
+// Intermediates live in an fp32 workspace, one slot per chunk.
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+namespace {
+
+constexpr int C = kChunk;
+constexpr float kLog2e = 1.4426950408889634f;
+
+constexpr int cmax2(int a, int b) { return a > b ? a : b; }
+
+// 4 fp32 values stored as 4 elements of T
+template <typename T>
+__device__ __forceinline__ void st4(T* dst, f32x4 x) {
+    typename Frag4Of<T>::type f = frag4_from<T>(x);
+    *reinterpret_cast<typename Frag4Of<T>::type*>(dst) = f;
+}
+
+// the chunk's in-chunk cumsum of the clamped log-gates (log2 units) for
+// channel c, and the sub-chunk references R_j (j = 0..4; R_4 = G_C)
+template <typename T, int LDG, int K>
+__device__ __forceinline__ void gate_cumsum(const BwdParams& p, int b, int h, int t0, int nt, int c,
+                                            float* sG, float* sR, unsigned long long* pass_mask) {
+    const T* gp = reinterpret_cast<const T*>(p.g);
+    float acc = 0.f;
+    unsigned long long m = 0;
+    sR[c] = 0.f;
+    for (int t = 0; t < C; ++t) {
+        float gv = 0.f;
+        if (t < nt) {
+            const size_t e = (((size_t)b * p.T + t0 + t) * p.H + h) * K + c;
+            gv = to_f32(gp[e]);
+            if (gv >= -5.f && gv <= 0.f) m |= 1ull << t;
+        }
+        acc += fminf(fmaxf(gv, -5.f), 0.f) * kLog2e;
+        sG[t * LDG + c] = acc;
+        if ((t & 15) == 15) sR[((t >> 4) + 1) * K + c] = acc;
+    }
+    if (pass_mask) *pass_mask = m;
+}
+
+// copy rows [0, nt) of a token-major [*, H, N] tensor slice (head h, token t0)
+// into LDS [C][ld]; rows from nt on are zero
+template <typename T, int N>
+__device__ __forceinline__ void stage_rows(const void* src, const BwdParams& p, int b, int h, int t0, int nt,
+                                           T* dst, int ld, int tid) {
+    constexpr int PR = N * (int)sizeof(T) / 16;     // 16-byte pieces per row
+    const T* base = src ? reinterpret_cast<const T*>(src) + (((size_t)b * p.T + t0) * p.H + h) * N : nullptr;
+    for (int i = tid; i < C * PR; i += 256) {
+        const int t = i / PR, sg = i % PR;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (base && t < nt) v = *reinterpret_cast<const uint4*>(base + (size_t)t * p.H * N + sg * (16 / (int)sizeof(T)));
+        *reinterpret_cast<uint4*>(dst + t * ld + sg * (16 / (int)sizeof(T))) = v;
+    }
+}
+
+}  // namespace
+
+// ============================================================================
+// vside: U = U~ - W S;  D = tril(dO U^T);  dQh = dO S^T;  dKb = U dS'^T;
+//        dW = -dU S^T;  rs = e^{G_C} rowsum(S * dS')
+// ============================================================================
+template <typename T, int K, int V>
+struct VsideLayout {
+    static constexpr int SZ = (int)sizeof(T), PAD = 16 / SZ;
+    static constexpr int LDK = K + PAD, LDV = V + PAD;
+    static constexpr int oR1 = 0;                                        // S^T [V][LDK], then S [K][LDV]
+    static constexpr int oR2 = oR1 + cmax2(V * LDK, K * LDV) * SZ;       // W [C][LDK], then dO [C][LDV]
+    static constexpr int oU = oR2 + cmax2(C * LDK, C * LDV) * SZ;        // U [C][LDV]
+    static constexpr int oDS = oU + C * LDV * SZ;                        // dS' [K][LDV]
+    static constexpr int oDU = oDS + K * LDV * SZ;                       // dU [C][LDV]
+    static constexpr int TOTAL = oDU + C * LDV * SZ;
+    static_assert(TOTAL <= 160 * 1024, "LDS budget exceeded");
+};
+
+template <typename T, int K, int V>
+__global__ __launch_bounds__(256) void kda_bwd_vside_kernel(BwdParams p) {
+    using L = VsideLayout<T, K, V>;
+    using Frag = typename FragOf<T>::type;
+    constexpr int LDK = L::LDK, LDV = L::LDV, SZ = L::SZ;
+    constexpr int KS = K / 32, VS = V / 32, NVT = V / 16, NKT = K / 16;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
+    T* sR1 = reinterpret_cast<T*>(smem + L::oR1);
+    T* sR2 = reinterpret_cast<T*>(smem + L::oR2);
+    T* sU = reinterpret_cast<T*>(smem + L::oU);
+    T* sDS = reinterpret_cast<T*>(smem + L::oDS);
+    T* sDU = reinterpret_cast<T*>(smem + L::oDU);
+
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lg = l >> 4, lr = l & 15;
+    const int NC = p.NC;
+    const int ci = blockIdx.x % NC, bh = blockIdx.x / NC;
+    const int b = bh / p.H, h = bh % p.H;
+    const int t0 = ci * C, nt = min(C, p.T - t0);
+    const size_t KV = (size_t)K * V, cs = (size_t)bh * NC + ci;
+    const RecLayout RL = rec_layout(K, V, SZ);
+    const unsigned char* rec = p.rec + cs * RL.bytes;
+    const float* S0 = ci == 0 ? (p.s0 ? p.s0 + (size_t)bh * KV : nullptr)
+                              : p.snaps + (((size_t)b * NC + ci - 1) * p.H + h) * KV;
+    const float* dSp = ci == NC - 1 ? (p.dsT ? p.dsT + (size_t)bh * KV : nullptr) : p.adj + cs * KV;
+
+    // ---- phase 1: S^T and W; U = U~ - W S ----------------------------------------
+    for (int i = tid; i < K * V / 4; i += 256) {
+        const int r = i / (V / 4), c4 = 4 * (i % (V / 4));
+        const f32x4 x = S0 ? *reinterpret_cast<const f32x4*>(S0 + (size_t)r * V + c4) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sR1[(c4 + e) * LDK + r] = from_f32<T>(x[e]);
+    }
+    for (int i = tid; i < C * K * SZ / 16; i += 256) {
+        const int r = i / (K * SZ / 16), sg = i % (K * SZ / 16);
+        *reinterpret_cast<uint4*>(reinterpret_cast<unsigned char*>(sR2) + r * LDK * SZ + sg * 16) =
+            *reinterpret_cast<const uint4*>(rec + RL.oW + (size_t)i * 16);
+    }
+    __syncthreads();
+    for (int vt = w; vt < NVT; vt += 4) {
+        Frag bs[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) bs[ks] = ld_frag_perm<T>(&sR1[(16 * vt + lr) * LDK + 32 * ks + 4 * lg]);
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti) {
+            // U~[t][v] for t = 16 ti + 4 lg + e (the record holds U~^T [V][C])
+            const T* ut = reinterpret_cast<const T*>(rec + RL.oUtT) + (size_t)(16 * vt + lr) * C + 16 * ti + 4 * lg;
+            f32x4 acc = ld4_as_f32<T>(ut);
+            f32x4 m = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) m = mma(m, ld_frag_perm<T>(&sR2[(16 * ti + lr) * LDK + 32 * ks + 4 * lg]), bs[ks]);
+            acc = acc - m;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sU[(16 * ti + 4 * lg + e) * LDV + 16 * vt + lr] = from_f32<T>(acc[e]);
+        }
+    }
+    __syncthreads();
+
+    // ---- phase 2: S, dS', dO, dU ---------------------------------------------------
+    for (int i = tid; i < K * V / 4; i += 256) {
+        const int r = i / (V / 4), c4 = 4 * (i % (V / 4));
+        const f32x4 x = S0 ? *reinterpret_cast<const f32x4*>(S0 + (size_t)r * V + c4) : f32x4{0.f, 0.f, 0.f, 0.f};
+        const f32x4 y = dSp ? *reinterpret_cast<const f32x4*>(dSp + (size_t)r * V + c4) : f32x4{0.f, 0.f, 0.f, 0.f};
+        st4<T>(&sR1[r * LDV + c4], x);
+        st4<T>(&sDS[r * LDV + c4], y);
+    }
+    stage_rows<T, V>(p.d_o, p, b, h, t0, nt, sR2, LDV, tid);
+    {
+        const float* du = p.cdU + cs * C * V;
+        for (int i = tid; i < C * V / 4; i += 256) {
+            const int t = i / (V / 4), c4 = 4 * (i % (V / 4));
+            st4<T>(&sDU[t * LDV + c4], *reinterpret_cast<const f32x4*>(du + (size_t)t * V + c4));
+        }
+    }
+    __syncthreads();
+
+    // D = tril(dO U^T): 16 tiles (zeros above the diagonal blocks)
+    float* Dg = p.cD + cs * C * C;
+    for (int d = w; d < 16; d += 4) {
+        const int i = d >> 2, j = d & 3;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        if (j <= i) {
+#pragma unroll
+            for (int ks = 0; ks < VS; ++ks)
+                acc = mma(acc, ld_frag_perm<T>(&sR2[(16 * i + lr) * LDV + 32 * ks + 4 * lg]),
+                          ld_frag_perm<T>(&sU[(16 * j + lr) * LDV + 32 * ks + 4 * lg]));
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int t = 16 * i + 4 * lg + e, s = 16 * j + lr;
+            Dg[t * C + s] = (s <= t) ? acc[e] : 0.f;
+        }
+    }
+    // dQh = dO S^T, dW = -dU S^T, dKb = U dS'^T: 4 x NKT tiles each
+    float* dQh = p.cdQh + cs * C * K;
+    float* dKb = p.cdKb + cs * C * K;
+    float* dW = p.cdW + cs * C * K;
+    for (int q = w; q < 4 * NKT; q += 4) {
+        const int i = q / NKT, ct = q % NKT;
+        f32x4 aq = {0.f, 0.f, 0.f, 0.f}, aw = aq, ak = aq;
+#pragma unroll
+        for (int ks = 0; ks < VS; ++ks) {
+            const Frag bS = ld_frag_perm<T>(&sR1[(16 * ct + lr) * LDV + 32 * ks + 4 * lg]);
+            const Frag bD = ld_frag_perm<T>(&sDS[(16 * ct + lr) * LDV + 32 * ks + 4 * lg]);
+            aq = mma(aq, ld_frag_perm<T>(&sR2[(16 * i + lr) * LDV + 32 * ks + 4 * lg]), bS);
+            aw = mma(aw, ld_frag_perm<T>(&sDU[(16 * i + lr) * LDV + 32 * ks + 4 * lg]), bS);
+            ak = mma(ak, ld_frag_perm<T>(&sU[(16 * i + lr) * LDV + 32 * ks + 4 * lg]), bD);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const size_t o = (size_t)(16 * i + 4 * lg + e) * K + 16 * ct + lr;
+            dQh[o] = aq[e];
+            dW[o] = -aw[e];
+            dKb[o] = ak[e];
+        }
+    }
+    // rs[c] = e^{G_C}[c] sum_v S[c][v] dS'[c][v] (fp32 sources)
+    if (tid < K) {
+        float acc = 0.f;
+        if (S0 && dSp) {
+            const float* a = S0 + (size_t)tid * V;
+            const float* d = dSp + (size_t)tid * V;
+            for (int v = 0; v < V; v += 4) {
+                const f32x4 x = *reinterpret_cast<const f32x4*>(a + v), y = *reinterpret_cast<const f32x4*>(d + v);
+                acc += x[0] * y[0] + x[1] * y[1] + x[2] * y[2] + x[3] * y[3];
+            }
+        }
+        const float egc = reinterpret_cast<const float*>(rec + RL.oEgc)[tid];
+        p.crs[cs * K + tid] = egc * acc;
+    }
+}
+
+// ============================================================================
+// ksolve: Ak; (I + A)^T [dBv | dBk] = [dU | dW]; dv, dKh, Et, dbeta
+// ============================================================================
+template <typename T, int K, int V>
+struct KsolveLayout {
+    static constexpr int SZ = (int)sizeof(T), PAD = 16 / SZ;
+    static constexpr int LDK = K + PAD, LDV = V + PAD, LDC = C + PAD;
+    static constexpr int LDG = K + 4, LDA = C + 4;
+    static constexpr int oG = 0;                                // fp32 [C][LDG] cumsum (log2 units)
+    static constexpr int oR = oG + C * LDG * 4;                 // fp32 [5][K] sub-chunk references
+    static constexpr int oB = oR + 5 * K * 4;                   // fp32 [C] beta
+    static constexpr int oK = oB + C * 4;                       // T [C][LDK] k
+    static constexpr int oAkT = oK + C * LDK * SZ;              // fp32 [C][LDA] Ak^T
+    static constexpr int oBV = oAkT + C * LDA * 4;              // T [C][LDV] dBv
+    static constexpr int oBK = oBV + C * LDV * SZ;              // T [C][LDK] dBk
+    static constexpr int oW = oBK + C * LDK * SZ;               // T [C][LDK] W      } then E fp32 [C][LDA]
+    static constexpr int oUt = oW + C * LDK * SZ;               // T [V][LDC] U~^T   }
+    static constexpr int TOTAL = oUt + V * LDC * SZ;
+    static_assert(C * LDA * 4 <= C * LDK * SZ + V * LDC * SZ, "E must fit over W and U~^T");
+    static_assert(TOTAL <= 160 * 1024, "LDS budget exceeded");
+};
+
+template <typename T, int K, int V>
+__global__ __launch_bounds__(256) void kda_bwd_ksolve_kernel(BwdParams p) {
+    using L = KsolveLayout<T, K, V>;
+    using Frag = typename FragOf<T>::type;
+    constexpr int LDK = L::LDK, LDV = L::LDV, LDC = L::LDC, LDG = L::LDG, LDA = L::LDA, SZ = L::SZ;
+    constexpr int KS = K / 32, VS = V / 32;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
+    float* sG = reinterpret_cast<float*>(smem + L::oG);
+    float* sR = reinterpret_cast<float*>(smem + L::oR);
+    float* sB = reinterpret_cast<float*>(smem + L::oB);
+    T* sK = reinterpret_cast<T*>(smem + L::oK);
+    float* sAkT = reinterpret_cast<float*>(smem + L::oAkT);
+    T* sBV = reinterpret_cast<T*>(smem + L::oBV);
+    T* sBK = reinterpret_cast<T*>(smem + L::oBK);
+    T* sW = reinterpret_cast<T*>(smem + L::oW);
+    T* sUt = reinterpret_cast<T*>(smem + L::oUt);
+    float* sE = reinterpret_cast<float*>(smem + L::oW);
+
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lg = l >> 4, lr = l & 15;
+    const int NC = p.NC;
+    const int ci = blockIdx.x % NC, bh = blockIdx.x / NC;
+    const int b = bh / p.H, h = bh % p.H;
+    const int t0 = ci * C, nt = min(C, p.T - t0);
+    const size_t cs = (size_t)bh * NC + ci;
+    const RecLayout RL = rec_layout(K, V, SZ);
+    const unsigned char* rec = p.rec + cs * RL.bytes;
+
+    // ---- staging ------------------------------------------------------------------
+    if (tid < K) gate_cumsum<T, LDG, K>(p, b, h, t0, nt, tid, sG, sR, nullptr);
+    if (tid < C)
+        sB[tid] = tid < nt ? to_f32(reinterpret_cast<const T*>(p.beta)[((size_t)b * p.T + t0 + tid) * p.H + h]) : 0.f;
+    stage_rows<T, K>(p.k, p, b, h, t0, nt, sK, LDK, tid);
+    for (int i = tid; i < C * K * SZ / 16; i += 256) {
+        const int r = i / (K * SZ / 16), sg = i % (K * SZ / 16);
+        *reinterpret_cast<uint4*>(reinterpret_cast<unsigned char*>(sW) + r * LDK * SZ + sg * 16) =
+            *reinterpret_cast<const uint4*>(rec + RL.oW + (size_t)i * 16);
+    }
+    for (int i = tid; i < V * C * SZ / 16; i += 256) {
+        const int r = i / (C * SZ / 16), sg = i % (C * SZ / 16);
+        *reinterpret_cast<uint4*>(reinterpret_cast<unsigned char*>(sUt) + r * LDC * SZ + sg * 16) =
+            *reinterpret_cast<const uint4*>(rec + RL.oUtT + (size_t)i * 16);
+    }
+    for (int i = tid; i < C * LDA; i += 256) sAkT[i] = 0.f;
+    __syncthreads();
+
+    // ---- Ak = sum_c k_s k_r e^{G_s - G_r} (r < s), per sub-chunk block pair (i >= j) ----
+    // operands: k_s e^{G_s - R_i} (<= 1) and k_r e^{R_i - G_r} (<= 1 off the diagonal,
+    // <= e^80 on it)
+    for (int pr = w; pr < 10; pr += 4) {
+        int i = 0, j = pr;
+        while (j > i) { j -= i + 1; ++i; }
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            Frag fa, fb;
+            const int s = 16 * i + lr, r = 16 * j + lr;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int c = 32 * ks + 4 * lg + (u & 3) + (u >> 2) * 16;
+                const float ri = sR[i * K + c];
+                fa[u] = from_f32<T>(to_f32(sK[s * LDK + c]) * fast_exp2(sG[s * LDG + c] - ri));
+                fb[u] = from_f32<T>(to_f32(sK[r * LDK + c]) * fast_exp2(ri - sG[r * LDG + c]));
+            }
+            acc = mma(acc, fa, fb);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int s = 16 * i + 4 * lg + e, r = 16 * j + lr;
+            if (r < s) sAkT[r * LDA + s] = acc[e];
+        }
+    }
+    __syncthreads();
+
+    // ---- back substitution, one column of [dU | dW] per thread ---------------------
+    // x_s = rhs_s - sum_{r > s} A[r][s] x_r,  A[r][s] = beta_r Ak[r][s]
+    if (tid < V + K) {
+        const bool vcol = tid < V;
+        const float* rhs = vcol ? p.cdU + cs * C * V + tid : p.cdW + cs * C * K + (tid - V);
+        const int ld = vcol ? V : K;
+        float x[C], y[C];
+#pragma unroll
+        for (int s = 0; s < C; ++s) x[s] = rhs[(size_t)s * ld];
+#pragma unroll
+        for (int s = C - 1; s >= 0; --s) {
+            float acc = x[s];
+#pragma unroll
+            for (int r = s + 1; r < C; ++r) acc -= sAkT[s * LDA + r] * y[r];
+            x[s] = acc;
+            y[s] = sB[s] * acc;
+        }
+        if (vcol) {
+            T* dvp = reinterpret_cast<T*>(p.dv) + (((size_t)b * p.T + t0) * p.H + h) * V + tid;
+#pragma unroll
+            for (int s = 0; s < C; ++s) {
+                sBV[s * LDV + tid] = from_f32<T>(x[s]);
+                if (s < nt) dvp[(size_t)s * p.H * V] = from_f32<T>(y[s]);
+            }
+        } else {
+            const int c = tid - V;
+            float* dkh = p.cdKh + cs * C * K + c;
+#pragma unroll
+            for (int s = 0; s < C; ++s) {
+                sBK[s * LDK + c] = from_f32<T>(x[s]);
+                dkh[(size_t)s * K] = y[s];
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- E = -(dBv U~^T + dBk W^T), strictly lower; Et = diag(beta) E ---------------
+    f32x4 eacc[3];
+    int npr = 0;
+    for (int pr = w; pr < 10; pr += 4, ++npr) {
+        int i = 0, j = pr;
+        while (j > i) { j -= i + 1; ++i; }
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < VS; ++ks) {
+            // B operand (column r, reduction v) gathered from U~^T [v][r]
+            Frag fb;
+            const T* u0 = sUt + (32 * ks + 4 * lg) * LDC + 16 * j + lr;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                fb[u] = u0[u * LDC];
+                fb[4 + u] = u0[(16 + u) * LDC];
+            }
+            acc = mma(acc, ld_frag_perm<T>(&sBV[(16 * i + lr) * LDV + 32 * ks + 4 * lg]), fb);
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            acc = mma(acc, ld_frag_perm<T>(&sBK[(16 * i + lr) * LDK + 32 * ks + 4 * lg]),
+                      ld_frag_perm<T>(&sW[(16 * j + lr) * LDK + 32 * ks + 4 * lg]));
+        eacc[npr] = -acc;
+    }
+    __syncthreads();                                // W, U~^T no longer read: E goes over them
+    float* Et = p.cEt + cs * C * C;
+    npr = 0;
+    for (int pr = w; pr < 10; pr += 4, ++npr) {
+        int i = 0, j = pr;
+        while (j > i) { j -= i + 1; ++i; }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int s = 16 * i + 4 * lg + e, r = 16 * j + lr;
+            const float ev = r < s ? eacc[npr][e] : 0.f;
+            sE[s * LDA + r] = ev;
+            Et[s * C + r] = sB[s] * ev;
+        }
+    }
+    // the six blocks above the diagonal of Et are zero
+    for (int pr = w; pr < 6; pr += 4) {
+        const int i = pr < 3 ? 0 : (pr < 5 ? 1 : 2);
+        const int j = pr < 3 ? pr + 1 : (pr < 5 ? pr - 1 : 3);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Et[(16 * i + 4 * lg + e) * C + 16 * j + lr] = 0.f;
+    }
+    __syncthreads();
+
+    // ---- dbeta: four threads per token --------------------------------------------
+    {
+        const int s = tid >> 2, part = tid & 3;
+        float acc = 0.f;
+        if (s < nt) {
+            const T* vp = reinterpret_cast<const T*>(p.v) + (((size_t)b * p.T + t0 + s) * p.H + h) * V;
+            for (int v = part; v < V; v += 4) acc += to_f32(sBV[s * LDV + v]) * to_f32(vp[v]);
+            for (int c = part; c < K; c += 4)
+                acc += to_f32(sBK[s * LDK + c]) * to_f32(sK[s * LDK + c]) * fast_exp2(sG[s * LDG + c]);
+            for (int r = part; r < s; r += 4) acc += sE[s * LDA + r] * sAkT[r * LDA + s];
+        }
+        acc += __shfl_xor(acc, 1);
+        acc += __shfl_xor(acc, 2);
+        if (part == 0 && s < nt)
+            reinterpret_cast<T*>(p.dbeta)[((size_t)b * p.T + t0 + s) * p.H + h] = from_f32<T>(acc);
+    }
+}
+
+// ============================================================================
+// kgrad: X1, X2, Y1, Y2 and dq, dk, dg
+// ============================================================================
+// All in fp32 (operands and MFMA), whatever the input dtype: the terms of dG
+// are each far larger than their sum (they cancel), so bf16 operands here
+// would cost dg most of its precision.
+template <int K>
+struct KgradLayout {
+    static constexpr int LDK = K + 4, LDC = C + 4, LDG = K + 4;
+    static constexpr int oG = 0;                                // [C][LDG] cumsum (log2 units)
+    static constexpr int oR = oG + C * LDG * 4;                 // [5][K]
+    static constexpr int oK = oR + 5 * K * 4;                   // [C][LDK] k
+    static constexpr int oQ = oK + C * LDK * 4;                 // [C][LDK] q
+    static constexpr int oD = oQ + C * LDK * 4;                 // [C][LDC] D      } then dG [C][LDG]
+    static constexpr int oE = oD + C * LDC * 4;                 // [C][LDC] Et     }
+    static constexpr int oCS = oE + C * LDC * 4;                // [4][K] column sums
+    static constexpr int TOTAL = oCS + 4 * K * 4;
+    static_assert(C * LDG <= 2 * C * LDC, "dG must fit over D and Et");
+    static_assert(TOTAL <= 160 * 1024, "LDS budget exceeded");
+};
+
+template <typename T, int K>
+__global__ __launch_bounds__(256) void kda_bwd_kgrad_kernel(BwdParams p) {
+    using L = KgradLayout<K>;
+    constexpr int LDK = L::LDK, LDC = L::LDC, LDG = L::LDG;
+    constexpr int NKT = K / 16;                  // channel tiles; each wave takes NKT of the 4 NKT tiles
+    __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
+    float* sG = reinterpret_cast<float*>(smem + L::oG);
+    float* sR = reinterpret_cast<float*>(smem + L::oR);
+    float* sK = reinterpret_cast<float*>(smem + L::oK);
+    float* sQ = reinterpret_cast<float*>(smem + L::oQ);
+    float* sD = reinterpret_cast<float*>(smem + L::oD);
+    float* sE = reinterpret_cast<float*>(smem + L::oE);
+    float* sDG = reinterpret_cast<float*>(smem + L::oD);
+    float* sCS = reinterpret_cast<float*>(smem + L::oCS);
+
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lg = l >> 4, lr = l & 15;
+    const int NC = p.NC;
+    const int ci = blockIdx.x % NC, bh = blockIdx.x / NC;
+    const int b = bh / p.H, h = bh % p.H;
+    const int t0 = ci * C, nt = min(C, p.T - t0);
+    const size_t cs = (size_t)bh * NC + ci;
+    const size_t rowK = (size_t)p.H * K;
+
+    unsigned long long pass = 0;
+    if (tid < K) gate_cumsum<T, LDG, K>(p, b, h, t0, nt, tid, sG, sR, &pass);
+    {
+        const T* kp = reinterpret_cast<const T*>(p.k) + (((size_t)b * p.T + t0) * p.H + h) * K;
+        const T* qp = reinterpret_cast<const T*>(p.q) + (((size_t)b * p.T + t0) * p.H + h) * K;
+        for (int i = tid; i < C * K / 4; i += 256) {
+            const int t = i / (K / 4), c4 = 4 * (i % (K / 4));
+            f32x4 kv = {0.f, 0.f, 0.f, 0.f}, qv = kv;
+            if (t < nt) {
+                kv = ld4_as_f32<T>(kp + (size_t)t * rowK + c4);
+                qv = ld4_as_f32<T>(qp + (size_t)t * rowK + c4);
+            }
+            *reinterpret_cast<f32x4*>(&sK[t * LDK + c4]) = kv;
+            *reinterpret_cast<f32x4*>(&sQ[t * LDK + c4]) = qv;
+        }
+        const float* Dg = p.cD + cs * C * C;
+        const float* Eg = p.cEt + cs * C * C;
+        for (int i = tid; i < C * C / 4; i += 256) {
+            const int t = i / (C / 4), c4 = 4 * (i % (C / 4));
+            *reinterpret_cast<f32x4*>(&sD[t * LDC + c4]) = *reinterpret_cast<const f32x4*>(Dg + (size_t)t * C + c4);
+            *reinterpret_cast<f32x4*>(&sE[t * LDC + c4]) = *reinterpret_cast<const f32x4*>(Eg + (size_t)t * C + c4);
+        }
+    }
+    __syncthreads();
+
+    const float* dQhg = p.cdQh + cs * C * K;
+    const float* dKbg = p.cdKb + cs * C * K;
+    const float* dKhg = p.cdKh + cs * C * K;
+    T* dqo = reinterpret_cast<T*>(p.dq) + (((size_t)b * p.T + t0) * p.H + h) * K;
+    T* dko = reinterpret_cast<T*>(p.dk) + (((size_t)b * p.T + t0) * p.H + h) * K;
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    f32x4 dgr[NKT];                              // dG of this wave's tiles until D, Et are done
+#pragma unroll
+    for (int it = 0; it < NKT; ++it) {
+        const int q = w + 4 * it;
+        const int i = q / NKT, ct = q % NKT;
+        const int c = 16 * ct + lr;
+        const float Ri = sR[i * K + c];
+        // forward type on token block i: Y1 = D (k gated), X1 = Et (k gated)
+        f32x4 y1 = z, x1 = z;
+        for (int j = 0; j <= i; ++j) {
+            const float ref = j == i ? Ri : sR[(j + 1) * K + c];
+            f32x4 bk;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int s = 16 * j + 4 * lg + u;
+                bk[u] = sK[s * LDK + c] * fast_exp2(ref - sG[s * LDG + c]);
+            }
+            const f32x4 tD = mma16(z, *reinterpret_cast<const f32x4*>(&sD[(16 * i + lr) * LDC + 16 * j + 4 * lg]), bk);
+            const f32x4 tE = mma16(z, *reinterpret_cast<const f32x4*>(&sE[(16 * i + lr) * LDC + 16 * j + 4 * lg]), bk);
+            const float f = j == i ? 1.f : fast_exp2(Ri - ref);
+            y1 += f * tD;
+            x1 += f * tE;
+        }
+        // transposed type on token block i: Y2 = D^T (q gated), X2 = Et^T (k gated)
+        f32x4 y2d = z, x2d = z, y2o = z, x2o = z;
+        const float Rn = sR[(i + 1) * K + c];
+        for (int i2 = i; i2 < 4; ++i2) {
+            const float R2 = sR[i2 * K + c];
+            f32x4 bq, bk, aD, aE;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int t = 16 * i2 + 4 * lg + u;
+                const float gf = fast_exp2(sG[t * LDG + c] - R2);
+                bq[u] = sQ[t * LDK + c] * gf;
+                bk[u] = sK[t * LDK + c] * gf;
+                aD[u] = sD[t * LDC + 16 * i + lr];
+                aE[u] = sE[t * LDC + 16 * i + lr];
+            }
+            const f32x4 tY = mma16(z, aD, bq);
+            const f32x4 tX = mma16(z, aE, bk);
+            if (i2 == i) {
+                y2d = tY;
+                x2d = tX;
+            } else {
+                const float f = fast_exp2(R2 - Rn);
+                y2o += f * tY;
+                x2o += f * tX;
+            }
+        }
+        // epilogue on rows t = 16 i + 4 lg + e, channel c
+        const float RC = sR[4 * K + c];
+        float colpart = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int t = 16 * i + 4 * lg + e;
+            const float gl = sG[t * LDG + c];
+            const float eg = fast_exp2(gl), egc = fast_exp2(RC - gl);
+            const float fwd = fast_exp2(gl - Ri);
+            const float Y1 = fwd * y1[e], X1 = fwd * x1[e];
+            const float Y2 = fast_exp2(Ri - gl) * y2d[e] + fast_exp2(Rn - gl) * y2o[e];
+            const float X2 = fast_exp2(Ri - gl) * x2d[e] + fast_exp2(Rn - gl) * x2o[e];
+            const float kk = sK[t * LDK + c], qq = sQ[t * LDK + c];
+            const size_t o = (size_t)t * K + c;
+            const float dQh = dQhg[o], dKb = dKbg[o], dKh = dKhg[o];
+            const float kb = kk * egc;
+            dgr[it][e] = dQh * qq * eg + dKh * kk * eg - dKb * kb + kk * (X1 - X2 - Y2) + qq * Y1;
+            colpart += dKb * kb;
+            if (t < nt) {
+                dqo[(size_t)t * rowK + c] = from_f32<T>(dQh * eg + Y1);
+                dko[(size_t)t * rowK + c] = from_f32<T>(dKh * eg + X1 + X2 + Y2 + dKb * egc);
+            }
+        }
+        colpart += __shfl_xor(colpart, 16);
+        colpart += __shfl_xor(colpart, 32);
+        if (lg == 0) sCS[i * K + c] = colpart;
+    }
+    __syncthreads();                             // D and Et are no longer read: dG goes over them
+#pragma unroll
+    for (int it = 0; it < NKT; ++it) {
+        const int q = w + 4 * it;
+        const int i = q / NKT, ct = q % NKT;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sDG[(16 * i + 4 * lg + e) * LDG + 16 * ct + lr] = dgr[it][e];
+    }
+    __syncthreads();
+
+    // dg: reverse cumsum over the chunk plus the G_C terms, gate-derivative mask
+    if (tid < K) {
+        const int c = tid;
+        float tot = p.crs[cs * K + c] + sCS[c] + sCS[K + c] + sCS[2 * K + c] + sCS[3 * K + c];
+        T* dgo = reinterpret_cast<T*>(p.dg) + (((size_t)b * p.T + t0) * p.H + h) * K + c;
+        for (int t = C - 1; t >= 0; --t) {
+            tot += sDG[t * LDG + c];
+            if (t < nt) dgo[(size_t)t * rowK] = from_f32<T>(((pass >> t) & 1ull) ? tot : 0.f);
+        }
+    }
+}
+
+// ---- launchers ---------------------------------------------------------------------
+template <typename T, int K, int V>
+static hipError_t launch_bwd_chunk_t(const BwdParams& p, hipStream_t stream) {
+    const long n = (long)p.B * p.H * p.NC;
+    if (n <= 0) return hipSuccess;
+    if (n > 2000000000L) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((kda_bwd_vside_kernel<T, K, V>), dim3((unsigned)n), dim3(256), 0, stream, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((kda_bwd_ksolve_kernel<T, K, V>), dim3((unsigned)n), dim3(256), 0, stream, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((kda_bwd_kgrad_kernel<T, K>), dim3((unsigned)n), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+bool bwd_chunk_variant_exists(int dtype, int K, int V) {
+    const bool kv = (K == 64 || K == 128) && (V == 64 || V == 128);
+    if (dtype == 1) return kv;
+    if (dtype == 0) return K == 64 && V == 64;
+    return false;
+}
+
+hipError_t launch_bwd_chunk(int dtype, int K, int V, const BwdParams& p, hipStream_t stream) {
+    if (dtype == 1) {
+        if (K == 128 && V == 128) return launch_bwd_chunk_t<bf16, 128, 128>(p, stream);
+        if (K == 128 && V == 64) return launch_bwd_chunk_t<bf16, 128, 64>(p, stream);
+        if (K == 64 && V == 128) return launch_bwd_chunk_t<bf16, 64, 128>(p, stream);
+        if (K == 64 && V == 64) return launch_bwd_chunk_t<bf16, 64, 64>(p, stream);
+    } else if (dtype == 0) {
+        if (K == 64 && V == 64) return launch_bwd_chunk_t<float, 64, 64>(p, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace kda

@@ -179,10 +179,23 @@ struct BwdParams {
     const unsigned char* rec;   // [B*H*NC] records of the forward's intra-chunk pass
     const float* snaps;     // [B*NC][H][K][V]: slot b NC + c = state after chunk c
     float* adj;             // [B*H][NC][K][V]: dL/dS after chunk c (c < NC - 1)
+    // chunk-form gradients: fp32 intermediates, one slot per (b*H + h)*NC + chunk
+    float* cdU;             // [C][V] dU (reverse state pass)
+    float* cD;              // [C][C] tril(dO U^T)
+    float* cdQh;            // [C][K] dO S^T
+    float* cdKb;            // [C][K] U dS'^T
+    float* cdW;             // [C][K] -dU S^T
+    float* crs;             // [K] e^{G_C} rowsum(S * dS')
+    float* cdKh;            // [C][K] diag(beta) dBk
+    float* cEt;             // [C][C] diag(beta) E
 };
 hipError_t launch_bwd(int dtype, int K, const BwdParams& p, hipStream_t stream);
-// the reverse state pass: p.adj for every chunk boundary (NC > 1)
+// the reverse state pass: p.adj for every chunk boundary, p.cdU for every
+// chunk and p.ds0 (if set)
 hipError_t launch_bwd_state(int dtype, int K, const BwdParams& p, hipStream_t stream);
+// chunk-form gradients of every chunk (needs p.rec, p.snaps, p.adj, p.cdU)
+bool bwd_chunk_variant_exists(int dtype, int K, int V);
+hipError_t launch_bwd_chunk(int dtype, int K, int V, const BwdParams& p, hipStream_t stream);
 size_t bwd_workspace_bytes(int B, int T, int H, int K, int V);
 hipError_t launch_decode_multi(int dtype, int K, int V, const MultiDecodeParams& p, hipStream_t stream);
 

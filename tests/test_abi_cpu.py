@@ -291,12 +291,14 @@ def test_backward_validation_before_any_launch():
     tok = ck + 8 * (100 * 2) * (3 * 128 + 1) * 4                # partial sums per 16-column block
     # whole-sequence schedule (fp32 at K = V = 128): checkpoints and partial sums
     assert lib.kda_chunk_bwd_workspace_size(1, 100, 2, 128, 128, F32) == tok
-    # chunk-parallel schedule: 2 chunks of 2 (b, h) chains, one segment: the
-    # chunk records (W, Qh, Mqk, KbT, U~^T bf16; e^{G_C} fp32), the state
-    # after every chunk and dL/dS after every chunk (fp32), then as above
+    # chunk form: 2 chunks of 2 (b, h) chains, one segment: the chunk records
+    # (W, Qh, Mqk, KbT, U~^T bf16; e^{G_C} fp32), the state after every chunk
+    # and dL/dS after every chunk, then per chunk the fp32 intermediates dU,
+    # D, dQh, dKb, dW, rs, dKh, Et
     n = lib.kda_chunk_bwd_workspace_size(1, 100, 2, 128, 128, BF16)
     rec = (64 * 128 * 2 * 4 + 64 * 64 * 2 + 128 * 4 + 255) // 256 * 256
-    assert n == 4 * rec + 2 * (4 * 128 * 128 * 4) + tok
+    inter = 64 * 128 + 64 * 64 + 4 * 64 * 128 + 128 + 64 * 64
+    assert n == 4 * rec + 2 * (4 * 128 * 128 * 4) + 4 * inter * 4
     assert _bwd(lib, ws_bytes=n - 1) == WORKSPACE
     assert lib.kda_chunk_bwd_workspace_size(1, 0, 2, 128, 128, BF16) == 0
 
