@@ -770,11 +770,35 @@ kda_status kda_chunk_bwd(int B, int T, int H, int K, int V, kda_dtype dt,
         p.crs = f;  f += nch * K;
         p.cdKh = f; f += nch * c * K;
         p.cEt = f;
-        if (launch_timed("bwd_state_reverse", st, [&] { return launch_bwd_state((int)dt, K, p, st); }) !=
+        // reverse state pass over the forward plan's segments: summaries,
+        // scan (reusing the forward's segment arrays), then every segment
+        p.n_seg = pl.n_seg;
+        p.cps = L.cps;
+        p.wsP = wsP;
+        p.wsL = wsL;
+        if (pl.n_seg > 1) {
+            if (launch_timed("bwd_reverse_summary", st,
+                             [&] { return launch_bwd_state(true, (int)dt, K, p, st); }) != hipSuccess)
+                return KDA_ERR_HIP;
+            ScanParams scp{};
+            scp.s0 = d_final_state;
+            scp.wsP = wsP;
+            scp.wsL = wsL;
+            scp.BH = (int)bh;
+            scp.V = V;
+            scp.n_seg = pl.n_seg;
+            if (launch_timed("bwd_reverse_scan", st, [&] { return launch_scan(K, scp, st); }) != hipSuccess)
+                return KDA_ERR_HIP;
+        }
+        if (launch_timed("bwd_state_reverse", st, [&] { return launch_bwd_state(false, (int)dt, K, p, st); }) !=
             hipSuccess)
             return KDA_ERR_HIP;
-        return launch_timed("bwd_chunks", st, [&] { return launch_bwd_chunk((int)dt, K, V, p, st); }) ==
-                       hipSuccess ? KDA_OK : KDA_ERR_HIP;
+        static const char* const stage_names[3] = {"bwd_value_side", "bwd_solve", "bwd_gated"};
+        for (int stage = 0; stage < 3; ++stage)
+            if (launch_timed(stage_names[stage], st, [&] { return launch_bwd_chunk(stage, (int)dt, K, V, p, st); }) !=
+                hipSuccess)
+                return KDA_ERR_HIP;
+        return KDA_OK;
     }
     // token-level schedule over the whole sequence
     const size_t NG = (size_t)((T + 7) / 8);

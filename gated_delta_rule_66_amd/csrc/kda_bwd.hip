@@ -366,7 +366,7 @@ struct BwdStateLayout {
     static constexpr int NPD = (kChunk * PDR + NT - 1) / NT;
 };
 
-template <typename T, int K, int NW>
+template <typename T, int K, int NW, bool SUMMARY>
 __global__ __launch_bounds__(64 * NW) void kda_bwd_state_kernel(BwdParams p) {
     using L = BwdStateLayout<T, K, NW>;
     using Frag = typename FragOf<T>::type;
@@ -383,28 +383,45 @@ __global__ __launch_bounds__(64 * NW) void kda_bwd_state_kernel(BwdParams p) {
     const float* sEgc = reinterpret_cast<const float*>(smem + L::oEgc);
 
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lg = l >> 4, lr = l & 15;
-    const int nvb = p.V / VB;
-    // the column blocks of one (b, h) read the same records: one XCD (L2)
+    const int V = p.V, NC = p.NC, T_ = p.T, H = p.H;
+    // workgroup (b, h, segment, column block).  Summary: segments 1 .. n_seg - 1,
+    // columns [0, K + V): the first K carry the segment's transposed transition
+    // (identity start, dO taken as zero), the others its load (zero start).
+    const int nvb = (SUMMARY ? K + V : V) / VB;
+    const int nseg_here = SUMMARY ? p.n_seg - 1 : p.n_seg;
+    // the workgroups of one (b, h) read the same records: one XCD (L2)
     const int G = gridDim.x, x = blockIdx.x;
     const int lid = ((G & 7) == 0) ? (x & 7) * (G >> 3) + (x >> 3) : x;
-    const int vb = lid % nvb, bh = lid / nvb;
+    const int vb = lid % nvb, rest = lid / nvb;
+    const int seg = (rest % nseg_here) + (SUMMARY ? 1 : 0), bh = rest / nseg_here;
     const int b = bh / p.H, h = bh % p.H;
-    const int V = p.V, NC = p.NC, T_ = p.T, H = p.H;
-    const size_t KV = (size_t)K * V;
-    const int col = vb * VB + 16 * w + lr;
+    const int c_begin = seg * p.cps, c_end = min(c_begin + p.cps, NC);
+    const size_t KV = (size_t)K * V, BH = (size_t)p.B * p.H;
+    const bool pmode = SUMMARY && vb * VB < K;
+    const int vcol0 = SUMMARY ? (pmode ? 0 : vb * VB - K) : vb * VB;   // first value column of the block
+    const int col = (pmode ? vb * VB : vcol0) + 16 * w + lr;            // this lane's column
     const RecLayout RL = rec_layout(K, V, SZ);
     const unsigned char* rec0 = p.rec + (size_t)bh * NC * RL.bytes;
 
-    // dS' of the last chunk: dL/dS_T; accumulator layout (rows 16 ct + 4 lg + e, column lr)
+    // dS' after the segment's last chunk, accumulator layout (rows 16 ct + 4 lg + e,
+    // column lr): identity / zero (summary), dL/dS_T (last segment) or the segment
+    // scan's result for this segment (slot n_seg - 2 - seg)
+    const float* dinit = nullptr;
+    if (!SUMMARY)
+        dinit = seg == p.n_seg - 1 ? (p.dsT ? p.dsT + (size_t)bh * KV : nullptr)
+                                   : p.wsL + ((size_t)(p.n_seg - 2 - seg) * BH + bh) * KV;
     f32x4 dS[CT];
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            dS[ct][e] = p.dsT ? p.dsT[(size_t)bh * KV + (size_t)(16 * ct + 4 * lg + e) * V + col] : 0.f;
+        for (int e = 0; e < 4; ++e) {
+            const int row = 16 * ct + 4 * lg + e;
+            dS[ct][e] = dinit ? dinit[(size_t)row * V + col] : (pmode && row == col ? 1.f : 0.f);
+        }
 
+    // the loads of chunk ci - 1 are in flight during chunk ci
     uint4 pre[NPT], dpre[NPD];
-    auto load_chunk = [&](int ci) {
+    auto load_chunk = [&](int ci, uint4 (&pre)[NPT], uint4 (&dpre)[NPD]) {
         const __amdgpu_buffer_rsrc_t rr = make_rsrc(rec0 + (size_t)ci * RL.bytes);
 #pragma unroll
         for (int m = 0; m < NPT; ++m) {
@@ -414,8 +431,8 @@ __global__ __launch_bounds__(64 * NW) void kda_bwd_state_kernel(BwdParams p) {
             pre[m] = pc < L::PTOT ? buf_load16(rr, off) : make_uint4(0, 0, 0, 0);
         }
         const int t0 = ci * C, nt = min(C, T_ - t0);
-        const T* dob = p.d_o ? reinterpret_cast<const T*>(p.d_o) + (((size_t)b * T_ + t0) * H + h) * V + vb * VB
-                             : nullptr;
+        const T* dob = (p.d_o && !pmode) ? reinterpret_cast<const T*>(p.d_o) + (((size_t)b * T_ + t0) * H + h) * V + vcol0
+                                         : nullptr;
         const __amdgpu_buffer_rsrc_t rd = make_rsrc(dob);
         const unsigned rowV = (unsigned)H * V * SZ;
 #pragma unroll
@@ -425,7 +442,7 @@ __global__ __launch_bounds__(64 * NW) void kda_bwd_state_kernel(BwdParams p) {
                                                          : make_uint4(0, 0, 0, 0);
         }
     };
-    auto store_chunk = [&]() {
+    auto store_chunk = [&](const uint4 (&pre)[NPT], const uint4 (&dpre)[NPD]) {
 #pragma unroll
         for (int m = 0; m < NPT; ++m) {
             const int pc = tid + NT * m;
@@ -474,12 +491,11 @@ __global__ __launch_bounds__(64 * NW) void kda_bwd_state_kernel(BwdParams p) {
     };
 
     // every chunk's dU goes to p.cdU (chunk-form gradients); the adjoint
-    // before chunk ci (ci >= 1) to p.adj
-    load_chunk(NC - 1);
-    for (int ci = NC - 1; ci >= 0; --ci) {
-        store_chunk();
+    // before chunk ci to p.adj (ci >= 1) or p.ds0; false: nothing left to do
+    auto step = [&](int ci) -> bool {
+        store_chunk(pre, dpre);
         __syncthreads();
-        if (ci > 0) load_chunk(ci - 1);
+        if (ci - 1 >= c_begin) load_chunk(ci - 1, pre, dpre);
         Frag bdo[2], bds[KS];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) bdo[ks] = ld_frag_perm<T>(&sDoT[(16 * w + lr) * LDC + 32 * ks + 4 * lg]);
@@ -496,14 +512,14 @@ __global__ __launch_bounds__(64 * NW) void kda_bwd_state_kernel(BwdParams p) {
             for (int ks = 0; ks < KS; ++ks) acc = mma(acc, gather(sKbT, LDC, ks, 16 * ti), bds[ks]);
             ndU[ti] = -acc;
         }
-        {
+        if (!SUMMARY) {
             float* du = p.cdU + ((size_t)bh * NC + ci) * kChunk * V;
 #pragma unroll
             for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) du[(size_t)(16 * ti + 4 * lg + e) * V + col] = -ndU[ti][e];
+            if (ci == 0 && !p.ds0) return false;
         }
-        if (ci == 0 && !p.ds0) break;
         Frag bdu[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) bdu[ks] = frag_from_tiles<T>(ndU[2 * ks], ndU[2 * ks + 1]);
@@ -518,13 +534,29 @@ __global__ __launch_bounds__(64 * NW) void kda_bwd_state_kernel(BwdParams p) {
             for (int ks = 0; ks < 2; ++ks) acc = mma(acc, gather(sW, LDK, ks, 16 * ct), bdu[ks]);
             dS[ct] = acc;
         }
-        // the adjoint before chunk ci: after chunk ci - 1, or dL/dS_0
-        float* dst = ci > 0 ? p.adj + ((size_t)bh * NC + ci - 1) * KV : p.ds0 + (size_t)bh * KV;
+        if (!SUMMARY) {
+            // the adjoint before chunk ci: after chunk ci - 1, or dL/dS_0
+            float* dst = ci > 0 ? p.adj + ((size_t)bh * NC + ci - 1) * KV : p.ds0 + (size_t)bh * KV;
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) dst[(size_t)(16 * ct + 4 * lg + e) * V + col] = dS[ct][e];
+        }
+        __syncthreads();
+        return true;
+    };
+    if (c_end > c_begin) load_chunk(c_end - 1, pre, dpre);
+    for (int ci = c_end - 1; ci >= c_begin; --ci)
+        if (!step(ci)) break;
+    if (SUMMARY) {
+        // the segment's map, at scan slot n_seg - 1 - seg: transition [K][K] or load [K][V]
+        const int slot = p.n_seg - 1 - seg;
+        float* dst = pmode ? p.wsP + ((size_t)slot * BH + bh) * K * K : p.wsL + ((size_t)slot * BH + bh) * KV;
+        const int ld = pmode ? K : V;
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) dst[(size_t)(16 * ct + 4 * lg + e) * V + col] = dS[ct][e];
-        __syncthreads();
+            for (int e = 0; e < 4; ++e) dst[(size_t)(16 * ct + 4 * lg + e) * ld + col] = dS[ct][e];
     }
 }
 
@@ -581,23 +613,31 @@ hipError_t launch_bwd(int dtype, int K, const BwdParams& p, hipStream_t stream) 
     return hipErrorInvalidValue;
 }
 
-template <typename T, int K>
-static hipError_t launch_bwd_state_t(const BwdParams& p, hipStream_t stream) {
-    constexpr int NW = 4;                        // 64 value columns per workgroup
-    const long wgs = (long)p.B * p.H * (p.V / (16 * NW));
+// 64 columns per workgroup (4 waves), or 128 (8 waves: each record staged
+// once per (b, h, segment) where K = V = 128)
+template <typename T, int K, int NW>
+static hipError_t launch_bwd_state_t(bool summary, const BwdParams& p, hipStream_t stream) {
+    const long segs = summary ? p.n_seg - 1 : p.n_seg;
+    const long wgs = (long)p.B * p.H * segs * ((summary ? K + p.V : p.V) / (16 * NW));
+    if (wgs <= 0) return hipSuccess;
     if (wgs > 2000000000L) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((kda_bwd_state_kernel<T, K, NW>), dim3((unsigned)wgs), dim3(64 * NW), 0, stream, p);
+    if (summary)
+        hipLaunchKernelGGL((kda_bwd_state_kernel<T, K, NW, true>), dim3((unsigned)wgs), dim3(64 * NW), 0, stream, p);
+    else
+        hipLaunchKernelGGL((kda_bwd_state_kernel<T, K, NW, false>), dim3((unsigned)wgs), dim3(64 * NW), 0, stream, p);
     return hipGetLastError();
 }
 
-hipError_t launch_bwd_state(int dtype, int K, const BwdParams& p, hipStream_t stream) {
+hipError_t launch_bwd_state(bool summary, int dtype, int K, const BwdParams& p, hipStream_t stream) {
     if (p.NC <= 0 || (long)p.B * p.H == 0) return hipSuccess;
-    if (p.V % 64 != 0) return hipErrorInvalidValue;
+    if (p.V % 64 != 0 || K % 64 != 0 || p.n_seg < 1 || p.cps < 1) return hipErrorInvalidValue;
+    // the 8-wave variant's blocks: (K + V) / 128 in the summary, V / 128 otherwise
     if (dtype == 1) {
-        if (K == 128) return launch_bwd_state_t<bf16, 128>(p, stream);
-        if (K == 64) return launch_bwd_state_t<bf16, 64>(p, stream);
+        if (K == 128 && p.V == 128) return launch_bwd_state_t<bf16, 128, 8>(summary, p, stream);
+        if (K == 128) return launch_bwd_state_t<bf16, 128, 4>(summary, p, stream);
+        if (K == 64) return launch_bwd_state_t<bf16, 64, 4>(summary, p, stream);
     } else if (dtype == 0) {
-        if (K == 64) return launch_bwd_state_t<float, 64>(p, stream);
+        if (K == 64) return launch_bwd_state_t<float, 64, 4>(summary, p, stream);
     }
     return hipErrorInvalidValue;
 }

@@ -56,42 +56,61 @@ __device__ __forceinline__ void st4(T* dst, f32x4 x) {
     *reinterpret_cast<typename Frag4Of<T>::type*>(dst) = f;
 }
 
-// the chunk's in-chunk cumsum of the clamped log-gates (log2 units) for
-// channel c, and the sub-chunk references R_j (j = 0..4; R_4 = G_C)
+// 16-byte pieces: every global load of a staging phase is issued before any
+// of them is waited on, then the pieces go to LDS
+// pieces of the [C][N] token tile (head h, tokens t0 ..) of a [B, T, H, N]
+// tensor; rows from nt on (and a null source) are zero
+template <typename T, int N, int NP>
+__device__ __forceinline__ void load_tok_pieces(const void* src, const BwdParams& p, int b, int h, int t0, int nt,
+                                                uint4 (&r)[NP], int tid) {
+    constexpr int PR = N * (int)sizeof(T) / 16;
+    const T* base = src ? reinterpret_cast<const T*>(src) + (((size_t)b * p.T + t0) * p.H + h) * N : nullptr;
+#pragma unroll
+    for (int m = 0; m < NP; ++m) {
+        const int i = tid + 256 * m, t = i / PR, sg = i % PR;
+        r[m] = (base && i < C * PR && t < nt)
+                   ? *reinterpret_cast<const uint4*>(base + (size_t)t * p.H * N + sg * (16 / (int)sizeof(T)))
+                   : make_uint4(0, 0, 0, 0);
+    }
+}
+// pieces [0, n) of a contiguous array
+template <int NP>
+__device__ __forceinline__ void load_flat_pieces(const void* src, int n, uint4 (&r)[NP], int tid) {
+#pragma unroll
+    for (int m = 0; m < NP; ++m) {
+        const int i = tid + 256 * m;
+        r[m] = i < n ? reinterpret_cast<const uint4*>(src)[i] : make_uint4(0, 0, 0, 0);
+    }
+}
+// piece i to row i / PR, byte (i % PR) 16 of an LDS array with row stride ld_bytes
+template <int NP>
+__device__ __forceinline__ void store_pieces(void* dst, int ld_bytes, int PR, int n, const uint4 (&r)[NP], int tid) {
+#pragma unroll
+    for (int m = 0; m < NP; ++m) {
+        const int i = tid + 256 * m;
+        if (i < n) *reinterpret_cast<uint4*>(reinterpret_cast<unsigned char*>(dst) + (i / PR) * ld_bytes + (i % PR) * 16) = r[m];
+    }
+}
+
+// the in-chunk cumsum of the clamped log-gates (log2 units) for channel c
+// from the raw gates in LDS ([C][K], zero rows past nt), the sub-chunk
+// references R_j (j = 0..4; R_4 = G_C), and the tokens whose gate lies in
+// [-5, 0] (the clamp passes the gradient there)
 template <typename T, int LDG, int K>
-__device__ __forceinline__ void gate_cumsum(const BwdParams& p, int b, int h, int t0, int nt, int c,
-                                            float* sG, float* sR, unsigned long long* pass_mask) {
-    const T* gp = reinterpret_cast<const T*>(p.g);
+__device__ __forceinline__ void gate_cumsum_lds(const T* sgraw, int nt, int c, float* sG, float* sR,
+                                                unsigned long long* pass_mask) {
     float acc = 0.f;
     unsigned long long m = 0;
     sR[c] = 0.f;
+#pragma unroll 8
     for (int t = 0; t < C; ++t) {
-        float gv = 0.f;
-        if (t < nt) {
-            const size_t e = (((size_t)b * p.T + t0 + t) * p.H + h) * K + c;
-            gv = to_f32(gp[e]);
-            if (gv >= -5.f && gv <= 0.f) m |= 1ull << t;
-        }
+        const float gv = to_f32(sgraw[t * K + c]);
+        if (t < nt && gv >= -5.f && gv <= 0.f) m |= 1ull << t;
         acc += fminf(fmaxf(gv, -5.f), 0.f) * kLog2e;
         sG[t * LDG + c] = acc;
         if ((t & 15) == 15) sR[((t >> 4) + 1) * K + c] = acc;
     }
     if (pass_mask) *pass_mask = m;
-}
-
-// copy rows [0, nt) of a token-major [*, H, N] tensor slice (head h, token t0)
-// into LDS [C][ld]; rows from nt on are zero
-template <typename T, int N>
-__device__ __forceinline__ void stage_rows(const void* src, const BwdParams& p, int b, int h, int t0, int nt,
-                                           T* dst, int ld, int tid) {
-    constexpr int PR = N * (int)sizeof(T) / 16;     // 16-byte pieces per row
-    const T* base = src ? reinterpret_cast<const T*>(src) + (((size_t)b * p.T + t0) * p.H + h) * N : nullptr;
-    for (int i = tid; i < C * PR; i += 256) {
-        const int t = i / PR, sg = i % PR;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (base && t < nt) v = *reinterpret_cast<const uint4*>(base + (size_t)t * p.H * N + sg * (16 / (int)sizeof(T)));
-        *reinterpret_cast<uint4*>(dst + t * ld + sg * (16 / (int)sizeof(T))) = v;
-    }
 }
 
 }  // namespace
@@ -138,17 +157,49 @@ __global__ __launch_bounds__(256) void kda_bwd_vside_kernel(BwdParams p) {
                               : p.snaps + (((size_t)b * NC + ci - 1) * p.H + h) * KV;
     const float* dSp = ci == NC - 1 ? (p.dsT ? p.dsT + (size_t)bh * KV : nullptr) : p.adj + cs * KV;
 
-    // ---- phase 1: S^T and W; U = U~ - W S ----------------------------------------
-    for (int i = tid; i < K * V / 4; i += 256) {
-        const int r = i / (V / 4), c4 = 4 * (i % (V / 4));
-        const f32x4 x = S0 ? *reinterpret_cast<const f32x4*>(S0 + (size_t)r * V + c4) : f32x4{0.f, 0.f, 0.f, 0.f};
+    // ---- every global load first: S, dS' (fp32, 4 columns per piece), W, dO, dU ------
+    constexpr int NS = K * V / 4 / 256;              // S / dS' pieces per thread
+    constexpr int RQ = V / 4;                        // pieces per state row
+    static_assert(NS * 256 * 4 == K * V && 256 % RQ == 0, "state tiling");
+    constexpr int PRK = K * SZ / 16, PRV = V * SZ / 16;
+    constexpr int NPW = (C * PRK + 255) / 256, NPO = (C * PRV + 255) / 256;
+    constexpr int NDU = (C * V / 4 + 255) / 256;
+    f32x4 rS[NS], rD[NS], rU[NDU];
+    uint4 rw[NPW], ro[NPO];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) sR1[(c4 + e) * LDK + r] = from_f32<T>(x[e]);
+    for (int m = 0; m < NS; ++m) {
+        const int i = tid + 256 * m, r = i / RQ, c4 = 4 * (i % RQ);
+        rS[m] = S0 ? *reinterpret_cast<const f32x4*>(S0 + (size_t)r * V + c4) : f32x4{0.f, 0.f, 0.f, 0.f};
+        rD[m] = dSp ? *reinterpret_cast<const f32x4*>(dSp + (size_t)r * V + c4) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    for (int i = tid; i < C * K * SZ / 16; i += 256) {
-        const int r = i / (K * SZ / 16), sg = i % (K * SZ / 16);
-        *reinterpret_cast<uint4*>(reinterpret_cast<unsigned char*>(sR2) + r * LDK * SZ + sg * 16) =
-            *reinterpret_cast<const uint4*>(rec + RL.oW + (size_t)i * 16);
+    load_flat_pieces(rec + RL.oW, C * PRK, rw, tid);
+    load_tok_pieces<T, V>(p.d_o, p, b, h, t0, nt, ro, tid);
+    {
+        const f32x4* du = reinterpret_cast<const f32x4*>(p.cdU + cs * C * V);
+#pragma unroll
+        for (int m = 0; m < NDU; ++m) {
+            const int i = tid + 256 * m;
+            rU[m] = i < C * V / 4 ? du[i] : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    }
+
+    // ---- phase 1: S^T and W; U = U~ - W S ----------------------------------------
+#pragma unroll
+    for (int m = 0; m < NS; ++m) {
+        const int i = tid + 256 * m, r = i / RQ, c4 = 4 * (i % RQ);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sR1[(c4 + e) * LDK + r] = from_f32<T>(rS[m][e]);
+    }
+    store_pieces(sR2, LDK * SZ, PRK, C * PRK, rw, tid);
+    // rs[r] = e^{G_C}[r] sum_v S[r][v] dS'[r][v] (fp32): the RQ consecutive
+    // threads of a row add their pieces
+#pragma unroll
+    for (int m = 0; m < NS; ++m) {
+        const int i = tid + 256 * m, r = i / RQ;
+        float d = rS[m][0] * rD[m][0] + rS[m][1] * rD[m][1] + rS[m][2] * rD[m][2] + rS[m][3] * rD[m][3];
+#pragma unroll
+        for (int x = 1; x < RQ; x <<= 1) d += __shfl_xor(d, x);
+        if (i % RQ == 0) p.crs[cs * K + r] = reinterpret_cast<const float*>(rec + RL.oEgc)[r] * d;
     }
     __syncthreads();
     for (int vt = w; vt < NVT; vt += 4) {
@@ -170,21 +221,18 @@ __global__ __launch_bounds__(256) void kda_bwd_vside_kernel(BwdParams p) {
     }
     __syncthreads();
 
-    // ---- phase 2: S, dS', dO, dU ---------------------------------------------------
-    for (int i = tid; i < K * V / 4; i += 256) {
-        const int r = i / (V / 4), c4 = 4 * (i % (V / 4));
-        const f32x4 x = S0 ? *reinterpret_cast<const f32x4*>(S0 + (size_t)r * V + c4) : f32x4{0.f, 0.f, 0.f, 0.f};
-        const f32x4 y = dSp ? *reinterpret_cast<const f32x4*>(dSp + (size_t)r * V + c4) : f32x4{0.f, 0.f, 0.f, 0.f};
-        st4<T>(&sR1[r * LDV + c4], x);
-        st4<T>(&sDS[r * LDV + c4], y);
+    // ---- phase 2: S, dS', dO, dU from the registers ---------------------------------
+#pragma unroll
+    for (int m = 0; m < NS; ++m) {
+        const int i = tid + 256 * m, r = i / RQ, c4 = 4 * (i % RQ);
+        st4<T>(&sR1[r * LDV + c4], rS[m]);
+        st4<T>(&sDS[r * LDV + c4], rD[m]);
     }
-    stage_rows<T, V>(p.d_o, p, b, h, t0, nt, sR2, LDV, tid);
-    {
-        const float* du = p.cdU + cs * C * V;
-        for (int i = tid; i < C * V / 4; i += 256) {
-            const int t = i / (V / 4), c4 = 4 * (i % (V / 4));
-            st4<T>(&sDU[t * LDV + c4], *reinterpret_cast<const f32x4*>(du + (size_t)t * V + c4));
-        }
+    store_pieces(sR2, LDV * SZ, PRV, C * PRV, ro, tid);
+#pragma unroll
+    for (int m = 0; m < NDU; ++m) {
+        const int i = tid + 256 * m, t = i / RQ, c4 = 4 * (i % RQ);
+        if (i < C * V / 4) st4<T>(&sDU[t * LDV + c4], rU[m]);
     }
     __syncthreads();
 
@@ -228,20 +276,6 @@ __global__ __launch_bounds__(256) void kda_bwd_vside_kernel(BwdParams p) {
             dKb[o] = ak[e];
         }
     }
-    // rs[c] = e^{G_C}[c] sum_v S[c][v] dS'[c][v] (fp32 sources)
-    if (tid < K) {
-        float acc = 0.f;
-        if (S0 && dSp) {
-            const float* a = S0 + (size_t)tid * V;
-            const float* d = dSp + (size_t)tid * V;
-            for (int v = 0; v < V; v += 4) {
-                const f32x4 x = *reinterpret_cast<const f32x4*>(a + v), y = *reinterpret_cast<const f32x4*>(d + v);
-                acc += x[0] * y[0] + x[1] * y[1] + x[2] * y[2] + x[3] * y[3];
-            }
-        }
-        const float egc = reinterpret_cast<const float*>(rec + RL.oEgc)[tid];
-        p.crs[cs * K + tid] = egc * acc;
-    }
 }
 
 // ============================================================================
@@ -263,6 +297,7 @@ struct KsolveLayout {
     static constexpr int oUt = oW + C * LDK * SZ;               // T [V][LDC] U~^T   }
     static constexpr int TOTAL = oUt + V * LDC * SZ;
     static_assert(C * LDA * 4 <= C * LDK * SZ + V * LDC * SZ, "E must fit over W and U~^T");
+    static_assert(C * K * SZ <= C * LDA * 4, "the raw gates must fit over Ak^T");
     static_assert(TOTAL <= 160 * 1024, "LDS budget exceeded");
 };
 
@@ -293,23 +328,27 @@ __global__ __launch_bounds__(256) void kda_bwd_ksolve_kernel(BwdParams p) {
     const RecLayout RL = rec_layout(K, V, SZ);
     const unsigned char* rec = p.rec + cs * RL.bytes;
 
-    // ---- staging ------------------------------------------------------------------
-    if (tid < K) gate_cumsum<T, LDG, K>(p, b, h, t0, nt, tid, sG, sR, nullptr);
-    if (tid < C)
-        sB[tid] = tid < nt ? to_f32(reinterpret_cast<const T*>(p.beta)[((size_t)b * p.T + t0 + tid) * p.H + h]) : 0.f;
-    stage_rows<T, K>(p.k, p, b, h, t0, nt, sK, LDK, tid);
-    for (int i = tid; i < C * K * SZ / 16; i += 256) {
-        const int r = i / (K * SZ / 16), sg = i % (K * SZ / 16);
-        *reinterpret_cast<uint4*>(reinterpret_cast<unsigned char*>(sW) + r * LDK * SZ + sg * 16) =
-            *reinterpret_cast<const uint4*>(rec + RL.oW + (size_t)i * 16);
+    // ---- staging (the raw gates pass through the Ak^T area) -------------------------
+    {
+        constexpr int PRK = K * SZ / 16, PRC = C * SZ / 16;
+        constexpr int NPK = (C * PRK + 255) / 256, NPU = (V * PRC + 255) / 256;
+        uint4 rk[NPK], rg[NPK], rw[NPK], ru[NPU];
+        load_tok_pieces<T, K>(p.k, p, b, h, t0, nt, rk, tid);
+        load_tok_pieces<T, K>(p.g, p, b, h, t0, nt, rg, tid);
+        load_flat_pieces(rec + RL.oW, C * PRK, rw, tid);
+        load_flat_pieces(rec + RL.oUtT, V * PRC, ru, tid);
+        const float bt = tid < nt ? to_f32(reinterpret_cast<const T*>(p.beta)[((size_t)b * p.T + t0 + tid) * p.H + h])
+                                  : 0.f;
+        if (tid < C) sB[tid] = bt;
+        store_pieces(sK, LDK * SZ, PRK, C * PRK, rk, tid);
+        store_pieces(sAkT, K * SZ, PRK, C * PRK, rg, tid);
+        store_pieces(sW, LDK * SZ, PRK, C * PRK, rw, tid);
+        store_pieces(sUt, LDC * SZ, PRC, V * PRC, ru, tid);
     }
-    for (int i = tid; i < V * C * SZ / 16; i += 256) {
-        const int r = i / (C * SZ / 16), sg = i % (C * SZ / 16);
-        *reinterpret_cast<uint4*>(reinterpret_cast<unsigned char*>(sUt) + r * LDC * SZ + sg * 16) =
-            *reinterpret_cast<const uint4*>(rec + RL.oUtT + (size_t)i * 16);
-    }
-    for (int i = tid; i < C * LDA; i += 256) sAkT[i] = 0.f;
     __syncthreads();
+    if (tid < K) gate_cumsum_lds<T, LDG, K>(reinterpret_cast<const T*>(sAkT), nt, tid, sG, sR, nullptr);
+    __syncthreads();
+    // (Ak^T needs no clearing: every entry read below is written by the Gram)
 
     // ---- Ak = sum_c k_s k_r e^{G_s - G_r} (r < s), per sub-chunk block pair (i >= j) ----
     // operands: k_s e^{G_s - R_i} (<= 1) and k_r e^{R_i - G_r} (<= 1 off the diagonal,
@@ -447,35 +486,38 @@ __global__ __launch_bounds__(256) void kda_bwd_ksolve_kernel(BwdParams p) {
 // All in fp32 (operands and MFMA), whatever the input dtype: the terms of dG
 // are each far larger than their sum (they cancel), so bf16 operands here
 // would cost dg most of its precision.
-template <int K>
+template <typename T, int K>
 struct KgradLayout {
-    static constexpr int LDK = K + 4, LDC = C + 4, LDG = K + 4;
-    static constexpr int oG = 0;                                // [C][LDG] cumsum (log2 units)
-    static constexpr int oR = oG + C * LDG * 4;                 // [5][K]
-    static constexpr int oK = oR + 5 * K * 4;                   // [C][LDK] k
-    static constexpr int oQ = oK + C * LDK * 4;                 // [C][LDK] q
-    static constexpr int oD = oQ + C * LDK * 4;                 // [C][LDC] D      } then dG [C][LDG]
-    static constexpr int oE = oD + C * LDC * 4;                 // [C][LDC] Et     }
-    static constexpr int oCS = oE + C * LDC * 4;                // [4][K] column sums
-    static constexpr int TOTAL = oCS + 4 * K * 4;
+    static constexpr int SZ = (int)sizeof(T), PAD = 16 / SZ;
+    static constexpr int LDK = K + PAD, LDC = C + 4, LDG = K + 4;
+    static constexpr int oG = 0;                                // fp32 [C][LDG] cumsum (log2 units)
+    static constexpr int oR = oG + C * LDG * 4;                 // fp32 [5][K]
+    static constexpr int oK = oR + 5 * K * 4;                   // T [C][LDK] k (exact in fp32)
+    static constexpr int oQ = oK + C * LDK * SZ;                // T [C][LDK] q
+    static constexpr int oD = oQ + C * LDK * SZ;                // fp32 [C][LDC] D      } then dG [C][LDG]
+    static constexpr int oE = oD + C * LDC * 4;                 // fp32 [C][LDC] Et     }
+    static constexpr int oCS = oE + C * LDC * 4;                // fp32 [4][K] column sums
+    static constexpr int oGR = oCS + 4 * K * 4;                 // T [C][K] raw gates
+    static constexpr int TOTAL = oGR + C * K * SZ;
     static_assert(C * LDG <= 2 * C * LDC, "dG must fit over D and Et");
     static_assert(TOTAL <= 160 * 1024, "LDS budget exceeded");
 };
 
 template <typename T, int K>
 __global__ __launch_bounds__(256) void kda_bwd_kgrad_kernel(BwdParams p) {
-    using L = KgradLayout<K>;
-    constexpr int LDK = L::LDK, LDC = L::LDC, LDG = L::LDG;
+    using L = KgradLayout<T, K>;
+    constexpr int LDK = L::LDK, LDC = L::LDC, LDG = L::LDG, SZ = L::SZ;
     constexpr int NKT = K / 16;                  // channel tiles; each wave takes NKT of the 4 NKT tiles
     __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
     float* sG = reinterpret_cast<float*>(smem + L::oG);
     float* sR = reinterpret_cast<float*>(smem + L::oR);
-    float* sK = reinterpret_cast<float*>(smem + L::oK);
-    float* sQ = reinterpret_cast<float*>(smem + L::oQ);
+    T* sK = reinterpret_cast<T*>(smem + L::oK);
+    T* sQ = reinterpret_cast<T*>(smem + L::oQ);
     float* sD = reinterpret_cast<float*>(smem + L::oD);
     float* sE = reinterpret_cast<float*>(smem + L::oE);
     float* sDG = reinterpret_cast<float*>(smem + L::oD);
     float* sCS = reinterpret_cast<float*>(smem + L::oCS);
+    T* sGR = reinterpret_cast<T*>(smem + L::oGR);
 
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lg = l >> 4, lr = l & 15;
     const int NC = p.NC;
@@ -485,29 +527,24 @@ __global__ __launch_bounds__(256) void kda_bwd_kgrad_kernel(BwdParams p) {
     const size_t cs = (size_t)bh * NC + ci;
     const size_t rowK = (size_t)p.H * K;
 
-    unsigned long long pass = 0;
-    if (tid < K) gate_cumsum<T, LDG, K>(p, b, h, t0, nt, tid, sG, sR, &pass);
     {
-        const T* kp = reinterpret_cast<const T*>(p.k) + (((size_t)b * p.T + t0) * p.H + h) * K;
-        const T* qp = reinterpret_cast<const T*>(p.q) + (((size_t)b * p.T + t0) * p.H + h) * K;
-        for (int i = tid; i < C * K / 4; i += 256) {
-            const int t = i / (K / 4), c4 = 4 * (i % (K / 4));
-            f32x4 kv = {0.f, 0.f, 0.f, 0.f}, qv = kv;
-            if (t < nt) {
-                kv = ld4_as_f32<T>(kp + (size_t)t * rowK + c4);
-                qv = ld4_as_f32<T>(qp + (size_t)t * rowK + c4);
-            }
-            *reinterpret_cast<f32x4*>(&sK[t * LDK + c4]) = kv;
-            *reinterpret_cast<f32x4*>(&sQ[t * LDK + c4]) = qv;
-        }
-        const float* Dg = p.cD + cs * C * C;
-        const float* Eg = p.cEt + cs * C * C;
-        for (int i = tid; i < C * C / 4; i += 256) {
-            const int t = i / (C / 4), c4 = 4 * (i % (C / 4));
-            *reinterpret_cast<f32x4*>(&sD[t * LDC + c4]) = *reinterpret_cast<const f32x4*>(Dg + (size_t)t * C + c4);
-            *reinterpret_cast<f32x4*>(&sE[t * LDC + c4]) = *reinterpret_cast<const f32x4*>(Eg + (size_t)t * C + c4);
-        }
+        constexpr int PRK = K * SZ / 16, PRC = C * 4 / 16;
+        constexpr int NPK = (C * PRK + 255) / 256, NPC = (C * PRC + 255) / 256;
+        uint4 rk[NPK], rq[NPK], rg[NPK], rd[NPC], re[NPC];
+        load_tok_pieces<T, K>(p.k, p, b, h, t0, nt, rk, tid);
+        load_tok_pieces<T, K>(p.q, p, b, h, t0, nt, rq, tid);
+        load_tok_pieces<T, K>(p.g, p, b, h, t0, nt, rg, tid);
+        load_flat_pieces(p.cD + cs * C * C, C * PRC, rd, tid);
+        load_flat_pieces(p.cEt + cs * C * C, C * PRC, re, tid);
+        store_pieces(sK, LDK * SZ, PRK, C * PRK, rk, tid);
+        store_pieces(sQ, LDK * SZ, PRK, C * PRK, rq, tid);
+        store_pieces(sGR, K * SZ, PRK, C * PRK, rg, tid);
+        store_pieces(sD, LDC * 4, PRC, C * PRC, rd, tid);
+        store_pieces(sE, LDC * 4, PRC, C * PRC, re, tid);
     }
+    __syncthreads();
+    unsigned long long pass = 0;
+    if (tid < K) gate_cumsum_lds<T, LDG, K>(sGR, nt, tid, sG, sR, &pass);
     __syncthreads();
 
     const float* dQhg = p.cdQh + cs * C * K;
@@ -523,6 +560,15 @@ __global__ __launch_bounds__(256) void kda_bwd_kgrad_kernel(BwdParams p) {
         const int i = q / NKT, ct = q % NKT;
         const int c = 16 * ct + lr;
         const float Ri = sR[i * K + c];
+        // the epilogue's fp32 operands, loaded ahead of the tile's products
+        float eQh[4], eKb[4], eKh[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const size_t o = (size_t)(16 * i + 4 * lg + e) * K + c;
+            eQh[e] = dQhg[o];
+            eKb[e] = dKbg[o];
+            eKh[e] = dKhg[o];
+        }
         // forward type on token block i: Y1 = D (k gated), X1 = Et (k gated)
         f32x4 y1 = z, x1 = z;
         for (int j = 0; j <= i; ++j) {
@@ -531,7 +577,7 @@ __global__ __launch_bounds__(256) void kda_bwd_kgrad_kernel(BwdParams p) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int s = 16 * j + 4 * lg + u;
-                bk[u] = sK[s * LDK + c] * fast_exp2(ref - sG[s * LDG + c]);
+                bk[u] = to_f32(sK[s * LDK + c]) * fast_exp2(ref - sG[s * LDG + c]);
             }
             const f32x4 tD = mma16(z, *reinterpret_cast<const f32x4*>(&sD[(16 * i + lr) * LDC + 16 * j + 4 * lg]), bk);
             const f32x4 tE = mma16(z, *reinterpret_cast<const f32x4*>(&sE[(16 * i + lr) * LDC + 16 * j + 4 * lg]), bk);
@@ -549,8 +595,8 @@ __global__ __launch_bounds__(256) void kda_bwd_kgrad_kernel(BwdParams p) {
             for (int u = 0; u < 4; ++u) {
                 const int t = 16 * i2 + 4 * lg + u;
                 const float gf = fast_exp2(sG[t * LDG + c] - R2);
-                bq[u] = sQ[t * LDK + c] * gf;
-                bk[u] = sK[t * LDK + c] * gf;
+                bq[u] = to_f32(sQ[t * LDK + c]) * gf;
+                bk[u] = to_f32(sK[t * LDK + c]) * gf;
                 aD[u] = sD[t * LDC + 16 * i + lr];
                 aE[u] = sE[t * LDC + 16 * i + lr];
             }
@@ -577,9 +623,8 @@ __global__ __launch_bounds__(256) void kda_bwd_kgrad_kernel(BwdParams p) {
             const float Y1 = fwd * y1[e], X1 = fwd * x1[e];
             const float Y2 = fast_exp2(Ri - gl) * y2d[e] + fast_exp2(Rn - gl) * y2o[e];
             const float X2 = fast_exp2(Ri - gl) * x2d[e] + fast_exp2(Rn - gl) * x2o[e];
-            const float kk = sK[t * LDK + c], qq = sQ[t * LDK + c];
-            const size_t o = (size_t)t * K + c;
-            const float dQh = dQhg[o], dKb = dKbg[o], dKh = dKhg[o];
+            const float kk = to_f32(sK[t * LDK + c]), qq = to_f32(sQ[t * LDK + c]);
+            const float dQh = eQh[e], dKb = eKb[e], dKh = eKh[e];
             const float kb = kk * egc;
             dgr[it][e] = dQh * qq * eg + dKh * kk * eg - dKb * kb + kk * (X1 - X2 - Y2) + qq * Y1;
             colpart += dKb * kb;
@@ -616,17 +661,16 @@ __global__ __launch_bounds__(256) void kda_bwd_kgrad_kernel(BwdParams p) {
 
 // ---- launchers ---------------------------------------------------------------------
 template <typename T, int K, int V>
-static hipError_t launch_bwd_chunk_t(const BwdParams& p, hipStream_t stream) {
+static hipError_t launch_bwd_chunk_t(int stage, const BwdParams& p, hipStream_t stream) {
     const long n = (long)p.B * p.H * p.NC;
     if (n <= 0) return hipSuccess;
     if (n > 2000000000L) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((kda_bwd_vside_kernel<T, K, V>), dim3((unsigned)n), dim3(256), 0, stream, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((kda_bwd_ksolve_kernel<T, K, V>), dim3((unsigned)n), dim3(256), 0, stream, p);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((kda_bwd_kgrad_kernel<T, K>), dim3((unsigned)n), dim3(256), 0, stream, p);
+    if (stage == 0)
+        hipLaunchKernelGGL((kda_bwd_vside_kernel<T, K, V>), dim3((unsigned)n), dim3(256), 0, stream, p);
+    else if (stage == 1)
+        hipLaunchKernelGGL((kda_bwd_ksolve_kernel<T, K, V>), dim3((unsigned)n), dim3(256), 0, stream, p);
+    else
+        hipLaunchKernelGGL((kda_bwd_kgrad_kernel<T, K>), dim3((unsigned)n), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -637,14 +681,15 @@ bool bwd_chunk_variant_exists(int dtype, int K, int V) {
     return false;
 }
 
-hipError_t launch_bwd_chunk(int dtype, int K, int V, const BwdParams& p, hipStream_t stream) {
+hipError_t launch_bwd_chunk(int stage, int dtype, int K, int V, const BwdParams& p, hipStream_t stream) {
+    if (stage < 0 || stage > 2) return hipErrorInvalidValue;
     if (dtype == 1) {
-        if (K == 128 && V == 128) return launch_bwd_chunk_t<bf16, 128, 128>(p, stream);
-        if (K == 128 && V == 64) return launch_bwd_chunk_t<bf16, 128, 64>(p, stream);
-        if (K == 64 && V == 128) return launch_bwd_chunk_t<bf16, 64, 128>(p, stream);
-        if (K == 64 && V == 64) return launch_bwd_chunk_t<bf16, 64, 64>(p, stream);
+        if (K == 128 && V == 128) return launch_bwd_chunk_t<bf16, 128, 128>(stage, p, stream);
+        if (K == 128 && V == 64) return launch_bwd_chunk_t<bf16, 128, 64>(stage, p, stream);
+        if (K == 64 && V == 128) return launch_bwd_chunk_t<bf16, 64, 128>(stage, p, stream);
+        if (K == 64 && V == 64) return launch_bwd_chunk_t<bf16, 64, 64>(stage, p, stream);
     } else if (dtype == 0) {
-        if (K == 64 && V == 64) return launch_bwd_chunk_t<float, 64, 64>(p, stream);
+        if (K == 64 && V == 64) return launch_bwd_chunk_t<float, 64, 64>(stage, p, stream);
     }
     return hipErrorInvalidValue;
 }

@@ -188,14 +188,24 @@ struct BwdParams {
     float* crs;             // [K] e^{G_C} rowsum(S * dS')
     float* cdKh;            // [C][K] diag(beta) dBk
     float* cEt;             // [C][C] diag(beta) E
+    // reverse state pass over segments of cps chunks: the summary pass writes
+    // each segment's transposed transition (wsP [K][K]) and load (wsL [K][V])
+    // at scan slot n_seg - 1 - segment; the segment scan (from dL/dS_T) leaves
+    // dL/dS after segment j at wsL slot n_seg - 2 - j
+    int n_seg, cps;
+    float* wsP;
+    float* wsL;
 };
 hipError_t launch_bwd(int dtype, int K, const BwdParams& p, hipStream_t stream);
-// the reverse state pass: p.adj for every chunk boundary, p.cdU for every
-// chunk and p.ds0 (if set)
-hipError_t launch_bwd_state(int dtype, int K, const BwdParams& p, hipStream_t stream);
-// chunk-form gradients of every chunk (needs p.rec, p.snaps, p.adj, p.cdU)
+// the reverse state pass.  summary: every segment's map (segments >= 1);
+// otherwise p.adj for every chunk boundary, p.cdU for every chunk and p.ds0
+// (if set), each segment from its incoming adjoint
+hipError_t launch_bwd_state(bool summary, int dtype, int K, const BwdParams& p, hipStream_t stream);
+// chunk-form gradients of every chunk (needs p.rec, p.snaps, p.adj, p.cdU),
+// in three stages run in order: 0 value-side products, 1 Gram and back
+// substitution (dv, dbeta), 2 gated products (dq, dk, dg)
 bool bwd_chunk_variant_exists(int dtype, int K, int V);
-hipError_t launch_bwd_chunk(int dtype, int K, int V, const BwdParams& p, hipStream_t stream);
+hipError_t launch_bwd_chunk(int stage, int dtype, int K, int V, const BwdParams& p, hipStream_t stream);
 size_t bwd_workspace_bytes(int B, int T, int H, int K, int V);
 hipError_t launch_decode_multi(int dtype, int K, int V, const MultiDecodeParams& p, hipStream_t stream);
 
