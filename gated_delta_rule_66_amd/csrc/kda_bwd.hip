@@ -12,27 +12,29 @@
 //   dS'  = dS + k_t dy^T           da_t    = rowsum(dS' * S_{t-1})
 //   dS   = Diag(a_t) dS'           dg_t    = da_t a_t [-5 <= g_t <= 0]
 //
-// The recurrence acts on every value column separately, and so does the dS
-// recurrence; only the key-side gradients (dq, dk, da, dbeta) sum over the
-// columns.  A token-level workgroup owns one (b, h, 16-column block) and a
-// token range: a forward sweep that stores its state slice every 8 tokens,
-// then a reverse sweep that rebuilds each 8-token group's states in
-// registers from its checkpoint and applies the reverse steps.  Per token it
-// writes dv for its columns and its block's partial sums of dq, dk, da and
-// dbeta; a second kernel adds the blocks' partials in a fixed order
-// (deterministic) and applies the gate derivative.
+// This file holds two parts of the backward.
 //
-// Chunk-parallel schedule (where the forward's two-pass plan exists): the
-// token range of a workgroup is one 64-token chunk, so every (b, h, chunk,
-// column block) runs at once.  It needs the state before its chunk and dL/dS
-// after it.  The states come from the forward's state pass (a snapshot after
-// every chunk).  The adjoints come from a reverse pass over the chunk
-// records: the forward state pass maps S to U = U~ - W S,
-// O = Qh S + Mqk U and S' = Diag(e^{G_C}) S + KbT U, so its transpose maps
-// (dS', dO) to
+// Token-level gradients (the schedule for shapes without the two-pass
+// forward, fp32 with K or V = 128).  The recurrence acts on every value
+// column separately, and so does the dS recurrence; only the key-side
+// gradients (dq, dk, da, dbeta) sum over the columns.  A workgroup owns one
+// (b, h, 16-column block) and the whole sequence: a forward sweep that
+// stores its state slice every 8 tokens, then a reverse sweep that rebuilds
+// each 8-token group's states in registers from its checkpoint and applies
+// the reverse steps.  Per token it writes dv for its columns and its block's
+// partial sums of dq, dk, da and dbeta; a second kernel adds the blocks'
+// partials in a fixed order (deterministic) and applies the gate derivative.
+//
+// The reverse state pass of the chunk-form backward (kda_bwd_chunk.hip).
+// The forward state pass maps S to U = U~ - W S, O = Qh S + Mqk U and
+// S' = Diag(e^{G_C}) S + KbT U, so its transpose maps (dS', dO) to
 //   dU = Mqk^T dO + KbT^T dS'
 //   dS = Diag(e^{G_C}) dS' + Qh^T dO - W^T dU
-// chunk by chunk from the end of the sequence.
+// chunk by chunk from the end of the sequence.  It runs over the forward
+// plan's segments like the forward: per-segment summaries of this affine map
+// (a K x K transition and a K x V load), the segment scan from dL/dS_T, then
+// every segment from its incoming adjoint, writing dL/dS at each chunk
+// boundary and every chunk's dU.
 //
 // 256 threads: thread (cg = tid & 3, rg = tid >> 2) holds rows
 // [RPT rg, RPT rg + RPT) x columns [4 cg, 4 cg + 4) of the K x 16 slice.
@@ -69,10 +71,7 @@ __global__ __launch_bounds__(256) void kda_bwd_kernel(BwdParams p) {
     __shared__ float red[2][4][2 * BW_VB];      // row-reduction exchange, double-buffered
 
     const int ncb = p.V / BW_VB;
-    // whole sequence: workgroup (bh, cb); chunk-parallel: (bh, chunk, cb)
-    const int cb = blockIdx.x % ncb;
-    const int chunk = p.NC > 0 ? (blockIdx.x / ncb) % p.NC : 0;
-    const int bh = p.NC > 0 ? blockIdx.x / ncb / p.NC : blockIdx.x / ncb;
+    const int bh = blockIdx.x / ncb, cb = blockIdx.x % ncb;
     const int b = bh / p.H, h = bh % p.H;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
     const int cg = tid & 3, rg = tid >> 2;
@@ -82,11 +81,6 @@ __global__ __launch_bounds__(256) void kda_bwd_kernel(BwdParams p) {
     const size_t KV = (size_t)K * V;
     const int NG = (T_ + GS - 1) / GS;
     float* ck = p.ckpt + (size_t)bh * NG * KV;  // [NG][K][V] fp32
-    // this workgroup's token range [t_begin, t_end) as groups [g_begin, g_end)
-    const int t_begin = p.NC > 0 ? chunk * kChunk : 0;
-    const int t_end = p.NC > 0 ? min(T_, t_begin + kChunk) : T_;
-    const int g_begin = t_begin / GS, g_end = (t_end + GS - 1) / GS;
-    const bool first = chunk == 0, last = p.NC == 0 || chunk == p.NC - 1;
     int rbuf = 0;
 
     // sum over all K rows of x[c] (this thread's 4 columns; NV = 4 or 8 values)
@@ -179,46 +173,38 @@ __global__ __launch_bounds__(256) void kda_bwd_kernel(BwdParams p) {
     };
 
     // ---- forward sweep: the state before every group's first token ----------------
-    // start: S0 (first chunk), else the forward's state after the previous
-    // chunk, snapshot slot b NC + chunk - 1 of [B NC][H][K][V]
-    const float* sinit = first ? (p.s0 ? p.s0 + (size_t)bh * KV : nullptr)
-                               : p.snaps + (((size_t)b * p.NC + chunk - 1) * H + h) * KV;
     float S[RPT][4];
 #pragma unroll
     for (int j = 0; j < RPT; ++j)
 #pragma unroll
         for (int c = 0; c < 4; ++c)
-            S[j][c] = sinit ? sinit[(size_t)(row0 + j) * V + col0 + c] : 0.f;
-    if (g_end - g_begin > 1) fetch_group(g_begin, false);
-    for (int gi = g_begin; gi < g_end; ++gi) {
+            S[j][c] = p.s0 ? p.s0[(size_t)bh * KV + (size_t)(row0 + j) * V + col0 + c] : 0.f;
+    if (NG > 1) fetch_group(0, false);
+    for (int gi = 0; gi < NG; ++gi) {
 #pragma unroll
         for (int j = 0; j < RPT; ++j)
             *reinterpret_cast<f32x4*>(ck + (size_t)gi * KV + (size_t)(row0 + j) * V + col0) =
                 f32x4{S[j][0], S[j][1], S[j][2], S[j][3]};
-        if (gi + 1 == g_end) break;              // the last group's end state is not needed
+        if (gi + 1 == NG) break;                 // the last group's end state is not needed
         stage_group();
-        if (gi + 2 < g_end) fetch_group(gi + 1, false);
+        if (gi + 2 < NG) fetch_group(gi + 1, false);
         for (int r = 0; r < GS; ++r) fwd_token(S, r);
     }
 
     // ---- reverse sweep ---------------------------------------------------------------
-    // start: dL/dS_T (last chunk), else the reverse state pass's adjoint of
-    // the state after this chunk, [B H][NC][K][V]
-    const float* dinit = last ? (p.dsT ? p.dsT + (size_t)bh * KV : nullptr)
-                              : p.adj + ((size_t)bh * p.NC + chunk) * KV;
     float dS[RPT][4];
 #pragma unroll
     for (int j = 0; j < RPT; ++j)
 #pragma unroll
         for (int c = 0; c < 4; ++c)
-            dS[j][c] = dinit ? dinit[(size_t)(row0 + j) * V + col0 + c] : 0.f;
+            dS[j][c] = p.dsT ? p.dsT[(size_t)bh * KV + (size_t)(row0 + j) * V + col0 + c] : 0.f;
     const size_t BTH = (size_t)p.B * T_ * H;
-    if (g_end > g_begin) fetch_group(g_end - 1, true);
-    for (int gi = g_end - 1; gi >= g_begin; --gi) {
+    if (NG > 0) fetch_group(NG - 1, true);
+    for (int gi = NG - 1; gi >= 0; --gi) {
         const int t0 = gi * GS;
         const int n = min(GS, T_ - t0);
         stage_group();
-        if (gi > g_begin) fetch_group(gi - 1, true);
+        if (gi > 0) fetch_group(gi - 1, true);
         // St[r] = state before token t0 + r, r = 0..n
         float St[GS + 1][RPT][4];
 #pragma unroll
@@ -324,7 +310,7 @@ __global__ __launch_bounds__(256) void kda_bwd_kernel(BwdParams p) {
             }
         }
     }
-    if (p.ds0 && first) {
+    if (p.ds0) {
 #pragma unroll
         for (int j = 0; j < RPT; ++j)
             *reinterpret_cast<f32x4*>(p.ds0 + (size_t)bh * KV + (size_t)(row0 + j) * V + col0) =
@@ -592,7 +578,7 @@ __global__ __launch_bounds__(256) void kda_bwd_reduce_kernel(BwdParams p) {
 
 template <typename T, int K>
 static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
-    const long wgs = (long)p.B * p.H * (p.NC > 0 ? p.NC : 1) * (p.V / BW_VB);
+    const long wgs = (long)p.B * p.H * (p.V / BW_VB);
     if (wgs > 2000000000L) return hipErrorInvalidValue;
     hipLaunchKernelGGL((kda_bwd_kernel<T, K>), dim3((unsigned)wgs), dim3(256), 0, stream, p);
     hipError_t e = hipGetLastError();

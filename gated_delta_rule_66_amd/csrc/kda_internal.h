@@ -173,8 +173,7 @@ struct BwdParams {
     float* pda;
     float* pdb;             // [V/16][B*T*H]
     int B, T, H, V;
-    // chunk-parallel schedule (NC = chunks per sequence; 0: one workgroup per
-    // (b, h, column block) over the whole sequence)
+    // chunk-form backward (NC = chunks per sequence)
     int NC;
     const unsigned char* rec;   // [B*H*NC] records of the forward's intra-chunk pass
     const float* snaps;     // [B*NC][H][K][V]: slot b NC + c = state after chunk c

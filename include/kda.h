@@ -267,9 +267,12 @@ kda_status kda_recurrent_steps(int N, int T, int H, int K, int V, kda_dtype dt,
  * Backward of kda_chunk_fwd: the gradients of a loss L with respect to q, k,
  * v, g (log alpha before the clamp), beta and the initial state, given dL/do
  * and dL/dS_T.  The pages give no backward; this is the chain rule applied
- * to the recurrence (section "Как хранить миллион токенов в памяти"), token
- * by token in reverse.  The clamp passes the gradient inside its closed
- * range [-5, 0] and blocks it outside.
+ * to the recurrence (section "Как хранить миллион токенов в памяти") in its
+ * chunk form (section "Как распараллелили последовательное обновление"): the
+ * forward's state after every chunk, a reverse state pass for dL/dS at every
+ * chunk boundary, then every chunk's gradients at once.  fp32 with K or V =
+ * 128 (no two-pass forward) runs a token-level form instead.  The clamp
+ * passes the gradient inside its closed range [-5, 0] and blocks it outside.
  *
  *   q, k, g, v, beta, initial_state : the forward's inputs (same layouts)
  *   d_o           : [B, T, H, V] dtype dt, dL/do, or NULL (zeros)
@@ -278,9 +281,14 @@ kda_status kda_recurrent_steps(int N, int T, int H, int K, int V, kda_dtype dt,
  *   dv            : [B, T, H, V] dtype dt (written)
  *   dbeta         : [B, T, H] dtype dt (written)
  *   d_initial_state : [B, H, K, V] fp32 (written) or NULL
- *   workspace     : at least kda_chunk_bwd_workspace_size(...) bytes: the
- *                   state every 8 tokens (B*H*ceil(T/8)*K*V fp32) and the
- *                   per-16-column partial sums (V/16 * B*T*H*(3K+1) fp32).
+ *   workspace     : at least kda_chunk_bwd_workspace_size(...) bytes (the
+ *                   size does not depend on the device).  Chunk form: the
+ *                   forward plan's segment arrays, its chunk records, the
+ *                   state and dL/dS after every chunk (2 B*H*ceil(T/64)*K*V
+ *                   fp32) and per-chunk fp32 intermediates.  Token-level
+ *                   form: the state every 8 tokens (B*H*ceil(T/8)*K*V fp32)
+ *                   and the per-16-column partial sums
+ *                   (V/16 * B*T*H*(3K+1) fp32).
  * Sizes: K, V in {64, 128}; bf16 or fp32.  The forward states are recomputed
  * (no saved activations are needed).  Results are deterministic.
  */
@@ -293,13 +301,16 @@ kda_status kda_chunk_bwd(int B, int T, int H, int K, int V, kda_dtype dt,
 
 /*
  * Optional per-launch timing, for benchmarks and tracing.  After
- * kda_profile_start(max_launches), each kernel launched by kda_chunk_fwd or
- * kda_recurrent_step (up to max_launches of them) is bracketed by two HIP
+ * kda_profile_start(max_launches), each kernel launched by the library
+ * (up to max_launches of them) is bracketed by two HIP
  * events recorded on its own stream; launches beyond that are not timed.
  * kda_profile_stop waits for the recorded events, writes up to `cap` launch
  * names (static strings: "intra_chunk", "state_output", "state_summary",
  * "chunk_output", "chunk_summary", "segment_scan", "copy_state",
- * "varlen_prep", "decode_step", "decode_steps", "backward") and durations in milliseconds, releases the
+ * "varlen_prep", "decode_step", "decode_steps", "backward"; the chunk-form
+ * backward's "bwd_intra_chunk", "bwd_state_summary", "bwd_segment_scan",
+ * "bwd_states", "bwd_reverse_summary", "bwd_reverse_scan", "bwd_state_reverse",
+ * "bwd_value_side", "bwd_solve", "bwd_gated") and durations in milliseconds, releases the
  * events, and returns the number of timed launches (-1: profiling was not
  * started or a HIP event query failed).  The recording state is process-wide
  * and not thread-safe; profiling is off unless started.
