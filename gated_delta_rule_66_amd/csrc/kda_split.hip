@@ -700,7 +700,8 @@ struct StateLayout {
     static constexpr int NPT = (PTOT + NT - 1) / NT;     // pieces per thread
 };
 
-template <typename T, int K, int NW, int NTW, bool SUMMARY>
+// OUT: the output pass computes and stores O (false: states and snapshots only)
+template <typename T, int K, int NW, int NTW, bool SUMMARY, bool OUT = !SUMMARY>
 __global__ __launch_bounds__(64 * NW, (NW == 4 && NTW == 1 && sizeof(T) == 2 ? 2 : 1))
 void kda_state_kernel(StateParams p) {
     using L = StateLayout<T, K, NW, NTW, SUMMARY>;
@@ -910,7 +911,7 @@ void kda_state_kernel(StateParams p) {
             Ub[j][0] = frag_from_tiles<T>(U[j][0], U[j][1]);
             Ub[j][1] = frag_from_tiles<T>(U[j][2], U[j][3]);
         }
-        if (!SUMMARY && p.o) {
+        if constexpr (OUT) {
             // O = (Q e^G) S + Mqk U, staged in this wave's own (consumed) U~ rows
             constexpr int OW = 16 * NTW;
             T* sO = sUtT + 16 * tile0 * LDT;
@@ -1132,8 +1133,10 @@ template <typename T, int K, int NW, int NTW>
 static hipError_t launch_state_t(const StateParams& p, int grid, hipStream_t stream) {
     if (p.summary)
         hipLaunchKernelGGL((kda_state_kernel<T, K, NW, NTW, true>), dim3(grid), dim3(64 * NW), 0, stream, p);
+    else if (p.o)
+        hipLaunchKernelGGL((kda_state_kernel<T, K, NW, NTW, false, true>), dim3(grid), dim3(64 * NW), 0, stream, p);
     else
-        hipLaunchKernelGGL((kda_state_kernel<T, K, NW, NTW, false>), dim3(grid), dim3(64 * NW), 0, stream, p);
+        hipLaunchKernelGGL((kda_state_kernel<T, K, NW, NTW, false, false>), dim3(grid), dim3(64 * NW), 0, stream, p);
     return hipGetLastError();
 }
 
