@@ -60,34 +60,34 @@ __device__ __forceinline__ void st4(T* dst, f32x4 x) {
 // of them is waited on, then the pieces go to LDS
 // pieces of the [C][N] token tile (head h, tokens t0 ..) of a [B, T, H, N]
 // tensor; rows from nt on (and a null source) are zero
-template <typename T, int N, int NP>
+template <typename T, int N, int NP, int NT = 256>
 __device__ __forceinline__ void load_tok_pieces(const void* src, const BwdParams& p, int b, int h, int t0, int nt,
                                                 uint4 (&r)[NP], int tid) {
     constexpr int PR = N * (int)sizeof(T) / 16;
     const T* base = src ? reinterpret_cast<const T*>(src) + (((size_t)b * p.T + t0) * p.H + h) * N : nullptr;
 #pragma unroll
     for (int m = 0; m < NP; ++m) {
-        const int i = tid + 256 * m, t = i / PR, sg = i % PR;
+        const int i = tid + NT * m, t = i / PR, sg = i % PR;
         r[m] = (base && i < C * PR && t < nt)
                    ? *reinterpret_cast<const uint4*>(base + (size_t)t * p.H * N + sg * (16 / (int)sizeof(T)))
                    : make_uint4(0, 0, 0, 0);
     }
 }
 // pieces [0, n) of a contiguous array
-template <int NP>
+template <int NP, int NT = 256>
 __device__ __forceinline__ void load_flat_pieces(const void* src, int n, uint4 (&r)[NP], int tid) {
 #pragma unroll
     for (int m = 0; m < NP; ++m) {
-        const int i = tid + 256 * m;
+        const int i = tid + NT * m;
         r[m] = i < n ? reinterpret_cast<const uint4*>(src)[i] : make_uint4(0, 0, 0, 0);
     }
 }
 // piece i to row i / PR, byte (i % PR) 16 of an LDS array with row stride ld_bytes
-template <int NP>
+template <int NP, int NT = 256>
 __device__ __forceinline__ void store_pieces(void* dst, int ld_bytes, int PR, int n, const uint4 (&r)[NP], int tid) {
 #pragma unroll
     for (int m = 0; m < NP; ++m) {
-        const int i = tid + 256 * m;
+        const int i = tid + NT * m;
         if (i < n) *reinterpret_cast<uint4*>(reinterpret_cast<unsigned char*>(dst) + (i / PR) * ld_bytes + (i % PR) * 16) = r[m];
     }
 }
@@ -133,10 +133,11 @@ struct VsideLayout {
 };
 
 template <typename T, int K, int V>
-__global__ __launch_bounds__(256) void kda_bwd_vside_kernel(BwdParams p) {
+__global__ __launch_bounds__(512) void kda_bwd_vside_kernel(BwdParams p) {
     using L = VsideLayout<T, K, V>;
     using Frag = typename FragOf<T>::type;
     constexpr int LDK = L::LDK, LDV = L::LDV, SZ = L::SZ;
+    constexpr int NT = 512, NW = 8;
     constexpr int KS = K / 32, VS = V / 32, NVT = V / 16, NKT = K / 16;
     __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
     T* sR1 = reinterpret_cast<T*>(smem + L::oR1);
@@ -158,27 +159,27 @@ __global__ __launch_bounds__(256) void kda_bwd_vside_kernel(BwdParams p) {
     const float* dSp = ci == NC - 1 ? (p.dsT ? p.dsT + (size_t)bh * KV : nullptr) : p.adj + cs * KV;
 
     // ---- every global load first: S, dS' (fp32, 4 columns per piece), W, dO, dU ------
-    constexpr int NS = K * V / 4 / 256;              // S / dS' pieces per thread
+    constexpr int NS = K * V / 4 / NT;               // S / dS' pieces per thread
     constexpr int RQ = V / 4;                        // pieces per state row
-    static_assert(NS * 256 * 4 == K * V && 256 % RQ == 0, "state tiling");
+    static_assert(NS * NT * 4 == K * V && 64 % RQ == 0, "state tiling");
     constexpr int PRK = K * SZ / 16, PRV = V * SZ / 16;
-    constexpr int NPW = (C * PRK + 255) / 256, NPO = (C * PRV + 255) / 256;
-    constexpr int NDU = (C * V / 4 + 255) / 256;
+    constexpr int NPW = (C * PRK + NT - 1) / NT, NPO = (C * PRV + NT - 1) / NT;
+    constexpr int NDU = (C * V / 4 + NT - 1) / NT;
     f32x4 rS[NS], rD[NS], rU[NDU];
     uint4 rw[NPW], ro[NPO];
 #pragma unroll
     for (int m = 0; m < NS; ++m) {
-        const int i = tid + 256 * m, r = i / RQ, c4 = 4 * (i % RQ);
+        const int i = tid + NT * m, r = i / RQ, c4 = 4 * (i % RQ);
         rS[m] = S0 ? *reinterpret_cast<const f32x4*>(S0 + (size_t)r * V + c4) : f32x4{0.f, 0.f, 0.f, 0.f};
         rD[m] = dSp ? *reinterpret_cast<const f32x4*>(dSp + (size_t)r * V + c4) : f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    load_flat_pieces(rec + RL.oW, C * PRK, rw, tid);
-    load_tok_pieces<T, V>(p.d_o, p, b, h, t0, nt, ro, tid);
+    load_flat_pieces<NPW, NT>(rec + RL.oW, C * PRK, rw, tid);
+    load_tok_pieces<T, V, NPO, NT>(p.d_o, p, b, h, t0, nt, ro, tid);
     {
         const f32x4* du = reinterpret_cast<const f32x4*>(p.cdU + cs * C * V);
 #pragma unroll
         for (int m = 0; m < NDU; ++m) {
-            const int i = tid + 256 * m;
+            const int i = tid + NT * m;
             rU[m] = i < C * V / 4 ? du[i] : f32x4{0.f, 0.f, 0.f, 0.f};
         }
     }
@@ -186,59 +187,56 @@ __global__ __launch_bounds__(256) void kda_bwd_vside_kernel(BwdParams p) {
     // ---- phase 1: S^T and W; U = U~ - W S ----------------------------------------
 #pragma unroll
     for (int m = 0; m < NS; ++m) {
-        const int i = tid + 256 * m, r = i / RQ, c4 = 4 * (i % RQ);
+        const int i = tid + NT * m, r = i / RQ, c4 = 4 * (i % RQ);
 #pragma unroll
         for (int e = 0; e < 4; ++e) sR1[(c4 + e) * LDK + r] = from_f32<T>(rS[m][e]);
     }
-    store_pieces(sR2, LDK * SZ, PRK, C * PRK, rw, tid);
+    store_pieces<NPW, NT>(sR2, LDK * SZ, PRK, C * PRK, rw, tid);
     // rs[r] = e^{G_C}[r] sum_v S[r][v] dS'[r][v] (fp32): the RQ consecutive
     // threads of a row add their pieces
 #pragma unroll
     for (int m = 0; m < NS; ++m) {
-        const int i = tid + 256 * m, r = i / RQ;
+        const int i = tid + NT * m, r = i / RQ;
         float d = rS[m][0] * rD[m][0] + rS[m][1] * rD[m][1] + rS[m][2] * rD[m][2] + rS[m][3] * rD[m][3];
 #pragma unroll
         for (int x = 1; x < RQ; x <<= 1) d += __shfl_xor(d, x);
         if (i % RQ == 0) p.crs[cs * K + r] = reinterpret_cast<const float*>(rec + RL.oEgc)[r] * d;
     }
     __syncthreads();
-    for (int vt = w; vt < NVT; vt += 4) {
-        Frag bs[KS];
+    for (int u = w; u < 4 * NVT; u += NW) {
+        const int vt = u >> 2, ti = u & 3;
+        // U~[t][v] for t = 16 ti + 4 lg + e (the record holds U~^T [V][C])
+        const T* ut = reinterpret_cast<const T*>(rec + RL.oUtT) + (size_t)(16 * vt + lr) * C + 16 * ti + 4 * lg;
+        f32x4 acc = ld4_as_f32<T>(ut);
+        f32x4 m = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) bs[ks] = ld_frag_perm<T>(&sR1[(16 * vt + lr) * LDK + 32 * ks + 4 * lg]);
+        for (int ks = 0; ks < KS; ++ks)
+            m = mma(m, ld_frag_perm<T>(&sR2[(16 * ti + lr) * LDK + 32 * ks + 4 * lg]),
+                    ld_frag_perm<T>(&sR1[(16 * vt + lr) * LDK + 32 * ks + 4 * lg]));
+        acc = acc - m;
 #pragma unroll
-        for (int ti = 0; ti < 4; ++ti) {
-            // U~[t][v] for t = 16 ti + 4 lg + e (the record holds U~^T [V][C])
-            const T* ut = reinterpret_cast<const T*>(rec + RL.oUtT) + (size_t)(16 * vt + lr) * C + 16 * ti + 4 * lg;
-            f32x4 acc = ld4_as_f32<T>(ut);
-            f32x4 m = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) m = mma(m, ld_frag_perm<T>(&sR2[(16 * ti + lr) * LDK + 32 * ks + 4 * lg]), bs[ks]);
-            acc = acc - m;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sU[(16 * ti + 4 * lg + e) * LDV + 16 * vt + lr] = from_f32<T>(acc[e]);
-        }
+        for (int e = 0; e < 4; ++e) sU[(16 * ti + 4 * lg + e) * LDV + 16 * vt + lr] = from_f32<T>(acc[e]);
     }
     __syncthreads();
 
     // ---- phase 2: S, dS', dO, dU from the registers ---------------------------------
 #pragma unroll
     for (int m = 0; m < NS; ++m) {
-        const int i = tid + 256 * m, r = i / RQ, c4 = 4 * (i % RQ);
+        const int i = tid + NT * m, r = i / RQ, c4 = 4 * (i % RQ);
         st4<T>(&sR1[r * LDV + c4], rS[m]);
         st4<T>(&sDS[r * LDV + c4], rD[m]);
     }
-    store_pieces(sR2, LDV * SZ, PRV, C * PRV, ro, tid);
+    store_pieces<NPO, NT>(sR2, LDV * SZ, PRV, C * PRV, ro, tid);
 #pragma unroll
     for (int m = 0; m < NDU; ++m) {
-        const int i = tid + 256 * m, t = i / RQ, c4 = 4 * (i % RQ);
+        const int i = tid + NT * m, t = i / RQ, c4 = 4 * (i % RQ);
         if (i < C * V / 4) st4<T>(&sDU[t * LDV + c4], rU[m]);
     }
     __syncthreads();
 
     // D = tril(dO U^T): 16 tiles (zeros above the diagonal blocks)
     float* Dg = p.cD + cs * C * C;
-    for (int d = w; d < 16; d += 4) {
+    for (int d = w; d < 16; d += NW) {
         const int i = d >> 2, j = d & 3;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         if (j <= i) {
@@ -257,7 +255,7 @@ __global__ __launch_bounds__(256) void kda_bwd_vside_kernel(BwdParams p) {
     float* dQh = p.cdQh + cs * C * K;
     float* dKb = p.cdKb + cs * C * K;
     float* dW = p.cdW + cs * C * K;
-    for (int q = w; q < 4 * NKT; q += 4) {
+    for (int q = w; q < 4 * NKT; q += NW) {
         const int i = q / NKT, ct = q % NKT;
         f32x4 aq = {0.f, 0.f, 0.f, 0.f}, aw = aq, ak = aq;
 #pragma unroll
@@ -302,10 +300,11 @@ struct KsolveLayout {
 };
 
 template <typename T, int K, int V>
-__global__ __launch_bounds__(256) void kda_bwd_ksolve_kernel(BwdParams p) {
+__global__ __launch_bounds__(512) void kda_bwd_ksolve_kernel(BwdParams p) {
     using L = KsolveLayout<T, K, V>;
     using Frag = typename FragOf<T>::type;
     constexpr int LDK = L::LDK, LDV = L::LDV, LDC = L::LDC, LDG = L::LDG, LDA = L::LDA, SZ = L::SZ;
+    constexpr int NT = 512, NW = 8;
     constexpr int KS = K / 32, VS = V / 32;
     __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
     float* sG = reinterpret_cast<float*>(smem + L::oG);
@@ -331,19 +330,19 @@ __global__ __launch_bounds__(256) void kda_bwd_ksolve_kernel(BwdParams p) {
     // ---- staging (the raw gates pass through the Ak^T area) -------------------------
     {
         constexpr int PRK = K * SZ / 16, PRC = C * SZ / 16;
-        constexpr int NPK = (C * PRK + 255) / 256, NPU = (V * PRC + 255) / 256;
+        constexpr int NPK = (C * PRK + NT - 1) / NT, NPU = (V * PRC + NT - 1) / NT;
         uint4 rk[NPK], rg[NPK], rw[NPK], ru[NPU];
-        load_tok_pieces<T, K>(p.k, p, b, h, t0, nt, rk, tid);
-        load_tok_pieces<T, K>(p.g, p, b, h, t0, nt, rg, tid);
-        load_flat_pieces(rec + RL.oW, C * PRK, rw, tid);
-        load_flat_pieces(rec + RL.oUtT, V * PRC, ru, tid);
+        load_tok_pieces<T, K, NPK, NT>(p.k, p, b, h, t0, nt, rk, tid);
+        load_tok_pieces<T, K, NPK, NT>(p.g, p, b, h, t0, nt, rg, tid);
+        load_flat_pieces<NPK, NT>(rec + RL.oW, C * PRK, rw, tid);
+        load_flat_pieces<NPU, NT>(rec + RL.oUtT, V * PRC, ru, tid);
         const float bt = tid < nt ? to_f32(reinterpret_cast<const T*>(p.beta)[((size_t)b * p.T + t0 + tid) * p.H + h])
                                   : 0.f;
         if (tid < C) sB[tid] = bt;
-        store_pieces(sK, LDK * SZ, PRK, C * PRK, rk, tid);
-        store_pieces(sAkT, K * SZ, PRK, C * PRK, rg, tid);
-        store_pieces(sW, LDK * SZ, PRK, C * PRK, rw, tid);
-        store_pieces(sUt, LDC * SZ, PRC, V * PRC, ru, tid);
+        store_pieces<NPK, NT>(sK, LDK * SZ, PRK, C * PRK, rk, tid);
+        store_pieces<NPK, NT>(sAkT, K * SZ, PRK, C * PRK, rg, tid);
+        store_pieces<NPK, NT>(sW, LDK * SZ, PRK, C * PRK, rw, tid);
+        store_pieces<NPU, NT>(sUt, LDC * SZ, PRC, V * PRC, ru, tid);
     }
     __syncthreads();
     if (tid < K) gate_cumsum_lds<T, LDG, K>(reinterpret_cast<const T*>(sAkT), nt, tid, sG, sR, nullptr);
@@ -353,7 +352,7 @@ __global__ __launch_bounds__(256) void kda_bwd_ksolve_kernel(BwdParams p) {
     // ---- Ak = sum_c k_s k_r e^{G_s - G_r} (r < s), per sub-chunk block pair (i >= j) ----
     // operands: k_s e^{G_s - R_i} (<= 1) and k_r e^{R_i - G_r} (<= 1 off the diagonal,
     // <= e^80 on it)
-    for (int pr = w; pr < 10; pr += 4) {
+    for (int pr = w; pr < 10; pr += NW) {
         int i = 0, j = pr;
         while (j > i) { j -= i + 1; ++i; }
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -387,11 +386,13 @@ __global__ __launch_bounds__(256) void kda_bwd_ksolve_kernel(BwdParams p) {
         float x[C], y[C];
 #pragma unroll
         for (int s = 0; s < C; ++s) x[s] = rhs[(size_t)s * ld];
+        // four partial sums per token: the dependent chain is a quarter as long
 #pragma unroll
         for (int s = C - 1; s >= 0; --s) {
-            float acc = x[s];
+            float a4[4] = {x[s], 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int r = s + 1; r < C; ++r) acc -= sAkT[s * LDA + r] * y[r];
+            for (int r = s + 1; r < C; ++r) a4[r & 3] -= sAkT[s * LDA + r] * y[r];
+            const float acc = (a4[0] + a4[1]) + (a4[2] + a4[3]);
             x[s] = acc;
             y[s] = sB[s] * acc;
         }
@@ -415,9 +416,9 @@ __global__ __launch_bounds__(256) void kda_bwd_ksolve_kernel(BwdParams p) {
     __syncthreads();
 
     // ---- E = -(dBv U~^T + dBk W^T), strictly lower; Et = diag(beta) E ---------------
-    f32x4 eacc[3];
+    f32x4 eacc[(10 + NW - 1) / NW];
     int npr = 0;
-    for (int pr = w; pr < 10; pr += 4, ++npr) {
+    for (int pr = w; pr < 10; pr += NW, ++npr) {
         int i = 0, j = pr;
         while (j > i) { j -= i + 1; ++i; }
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -442,7 +443,7 @@ __global__ __launch_bounds__(256) void kda_bwd_ksolve_kernel(BwdParams p) {
     __syncthreads();                                // W, U~^T no longer read: E goes over them
     float* Et = p.cEt + cs * C * C;
     npr = 0;
-    for (int pr = w; pr < 10; pr += 4, ++npr) {
+    for (int pr = w; pr < 10; pr += NW, ++npr) {
         int i = 0, j = pr;
         while (j > i) { j -= i + 1; ++i; }
 #pragma unroll
@@ -454,7 +455,7 @@ __global__ __launch_bounds__(256) void kda_bwd_ksolve_kernel(BwdParams p) {
         }
     }
     // the six blocks above the diagonal of Et are zero
-    for (int pr = w; pr < 6; pr += 4) {
+    for (int pr = w; pr < 6; pr += NW) {
         const int i = pr < 3 ? 0 : (pr < 5 ? 1 : 2);
         const int j = pr < 3 ? pr + 1 : (pr < 5 ? pr - 1 : 3);
 #pragma unroll
@@ -462,19 +463,20 @@ __global__ __launch_bounds__(256) void kda_bwd_ksolve_kernel(BwdParams p) {
     }
     __syncthreads();
 
-    // ---- dbeta: four threads per token --------------------------------------------
+    // ---- dbeta: eight threads per token --------------------------------------------
     {
-        const int s = tid >> 2, part = tid & 3;
+        const int s = tid >> 3, part = tid & 7;
         float acc = 0.f;
         if (s < nt) {
             const T* vp = reinterpret_cast<const T*>(p.v) + (((size_t)b * p.T + t0 + s) * p.H + h) * V;
-            for (int v = part; v < V; v += 4) acc += to_f32(sBV[s * LDV + v]) * to_f32(vp[v]);
-            for (int c = part; c < K; c += 4)
+            for (int v = part; v < V; v += 8) acc += to_f32(sBV[s * LDV + v]) * to_f32(vp[v]);
+            for (int c = part; c < K; c += 8)
                 acc += to_f32(sBK[s * LDK + c]) * to_f32(sK[s * LDK + c]) * fast_exp2(sG[s * LDG + c]);
-            for (int r = part; r < s; r += 4) acc += sE[s * LDA + r] * sAkT[r * LDA + s];
+            for (int r = part; r < s; r += 8) acc += sE[s * LDA + r] * sAkT[r * LDA + s];
         }
         acc += __shfl_xor(acc, 1);
         acc += __shfl_xor(acc, 2);
+        acc += __shfl_xor(acc, 4);
         if (part == 0 && s < nt)
             reinterpret_cast<T*>(p.dbeta)[((size_t)b * p.T + t0 + s) * p.H + h] = from_f32<T>(acc);
     }
@@ -504,10 +506,12 @@ struct KgradLayout {
 };
 
 template <typename T, int K>
-__global__ __launch_bounds__(256) void kda_bwd_kgrad_kernel(BwdParams p) {
+__global__ __launch_bounds__(512) void kda_bwd_kgrad_kernel(BwdParams p) {
     using L = KgradLayout<T, K>;
     constexpr int LDK = L::LDK, LDC = L::LDC, LDG = L::LDG, SZ = L::SZ;
-    constexpr int NKT = K / 16;                  // channel tiles; each wave takes NKT of the 4 NKT tiles
+    constexpr int NT = 512, NW = 8;
+    constexpr int NKT = K / 16;                  // channel tiles (4 NKT tiles in all)
+    constexpr int TPW = 4 * NKT / NW;            // tiles per wave
     __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
     float* sG = reinterpret_cast<float*>(smem + L::oG);
     float* sR = reinterpret_cast<float*>(smem + L::oR);
@@ -529,18 +533,18 @@ __global__ __launch_bounds__(256) void kda_bwd_kgrad_kernel(BwdParams p) {
 
     {
         constexpr int PRK = K * SZ / 16, PRC = C * 4 / 16;
-        constexpr int NPK = (C * PRK + 255) / 256, NPC = (C * PRC + 255) / 256;
+        constexpr int NPK = (C * PRK + NT - 1) / NT, NPC = (C * PRC + NT - 1) / NT;
         uint4 rk[NPK], rq[NPK], rg[NPK], rd[NPC], re[NPC];
-        load_tok_pieces<T, K>(p.k, p, b, h, t0, nt, rk, tid);
-        load_tok_pieces<T, K>(p.q, p, b, h, t0, nt, rq, tid);
-        load_tok_pieces<T, K>(p.g, p, b, h, t0, nt, rg, tid);
-        load_flat_pieces(p.cD + cs * C * C, C * PRC, rd, tid);
-        load_flat_pieces(p.cEt + cs * C * C, C * PRC, re, tid);
-        store_pieces(sK, LDK * SZ, PRK, C * PRK, rk, tid);
-        store_pieces(sQ, LDK * SZ, PRK, C * PRK, rq, tid);
-        store_pieces(sGR, K * SZ, PRK, C * PRK, rg, tid);
-        store_pieces(sD, LDC * 4, PRC, C * PRC, rd, tid);
-        store_pieces(sE, LDC * 4, PRC, C * PRC, re, tid);
+        load_tok_pieces<T, K, NPK, NT>(p.k, p, b, h, t0, nt, rk, tid);
+        load_tok_pieces<T, K, NPK, NT>(p.q, p, b, h, t0, nt, rq, tid);
+        load_tok_pieces<T, K, NPK, NT>(p.g, p, b, h, t0, nt, rg, tid);
+        load_flat_pieces<NPC, NT>(p.cD + cs * C * C, C * PRC, rd, tid);
+        load_flat_pieces<NPC, NT>(p.cEt + cs * C * C, C * PRC, re, tid);
+        store_pieces<NPK, NT>(sK, LDK * SZ, PRK, C * PRK, rk, tid);
+        store_pieces<NPK, NT>(sQ, LDK * SZ, PRK, C * PRK, rq, tid);
+        store_pieces<NPK, NT>(sGR, K * SZ, PRK, C * PRK, rg, tid);
+        store_pieces<NPC, NT>(sD, LDC * 4, PRC, C * PRC, rd, tid);
+        store_pieces<NPC, NT>(sE, LDC * 4, PRC, C * PRC, re, tid);
     }
     __syncthreads();
     unsigned long long pass = 0;
@@ -553,10 +557,10 @@ __global__ __launch_bounds__(256) void kda_bwd_kgrad_kernel(BwdParams p) {
     T* dqo = reinterpret_cast<T*>(p.dq) + (((size_t)b * p.T + t0) * p.H + h) * K;
     T* dko = reinterpret_cast<T*>(p.dk) + (((size_t)b * p.T + t0) * p.H + h) * K;
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    f32x4 dgr[NKT];                              // dG of this wave's tiles until D, Et are done
+    f32x4 dgr[TPW];                              // dG of this wave's tiles until D, Et are done
 #pragma unroll
-    for (int it = 0; it < NKT; ++it) {
-        const int q = w + 4 * it;
+    for (int it = 0; it < TPW; ++it) {
+        const int q = w + NW * it;
         const int i = q / NKT, ct = q % NKT;
         const int c = 16 * ct + lr;
         const float Ri = sR[i * K + c];
@@ -639,8 +643,8 @@ __global__ __launch_bounds__(256) void kda_bwd_kgrad_kernel(BwdParams p) {
     }
     __syncthreads();                             // D and Et are no longer read: dG goes over them
 #pragma unroll
-    for (int it = 0; it < NKT; ++it) {
-        const int q = w + 4 * it;
+    for (int it = 0; it < TPW; ++it) {
+        const int q = w + NW * it;
         const int i = q / NKT, ct = q % NKT;
 #pragma unroll
         for (int e = 0; e < 4; ++e) sDG[(16 * i + 4 * lg + e) * LDG + 16 * ct + lr] = dgr[it][e];
@@ -666,11 +670,11 @@ static hipError_t launch_bwd_chunk_t(int stage, const BwdParams& p, hipStream_t 
     if (n <= 0) return hipSuccess;
     if (n > 2000000000L) return hipErrorInvalidValue;
     if (stage == 0)
-        hipLaunchKernelGGL((kda_bwd_vside_kernel<T, K, V>), dim3((unsigned)n), dim3(256), 0, stream, p);
+        hipLaunchKernelGGL((kda_bwd_vside_kernel<T, K, V>), dim3((unsigned)n), dim3(512), 0, stream, p);
     else if (stage == 1)
-        hipLaunchKernelGGL((kda_bwd_ksolve_kernel<T, K, V>), dim3((unsigned)n), dim3(256), 0, stream, p);
+        hipLaunchKernelGGL((kda_bwd_ksolve_kernel<T, K, V>), dim3((unsigned)n), dim3(512), 0, stream, p);
     else
-        hipLaunchKernelGGL((kda_bwd_kgrad_kernel<T, K>), dim3((unsigned)n), dim3(256), 0, stream, p);
+        hipLaunchKernelGGL((kda_bwd_kgrad_kernel<T, K>), dim3((unsigned)n), dim3(512), 0, stream, p);
     return hipGetLastError();
 }
 
