@@ -292,9 +292,8 @@ struct KsolveLayout {
     static constexpr int oBV = oAkT + C * LDA * 4;              // T [C][LDV] dBv
     static constexpr int oBK = oBV + C * LDV * SZ;              // T [C][LDK] dBk
     static constexpr int oW = oBK + C * LDK * SZ;               // T [C][LDK] W      } then E fp32 [C][LDA]
-    static constexpr int oUt = oW + C * LDK * SZ;               // T [V][LDC] U~^T   }
-    static constexpr int TOTAL = oUt + V * LDC * SZ;
-    static_assert(C * LDA * 4 <= C * LDK * SZ + V * LDC * SZ, "E must fit over W and U~^T");
+    static constexpr int oUt = oW + C * LDK * SZ;               // T [V][LDC] U~^T   } and v T [C][V]
+    static constexpr int TOTAL = oW + cmax2(C * LDK * SZ + V * LDC * SZ, C * LDA * 4 + C * V * SZ);
     static_assert(C * K * SZ <= C * LDA * 4, "the raw gates must fit over Ak^T");
     static_assert(TOTAL <= 160 * 1024, "LDS budget exceeded");
 };
@@ -327,6 +326,28 @@ __global__ __launch_bounds__(512) void kda_bwd_ksolve_kernel(BwdParams p) {
     const RecLayout RL = rec_layout(K, V, SZ);
     const unsigned char* rec = p.rec + cs * RL.bytes;
 
+    // right-hand sides [dU | dW] of this wave's 16-column tiles, accumulator layout
+    constexpr int NCT = (V + K) / 16, CPW = (NCT + NW - 1) / NW;
+    f32x4 R[CPW][4];
+    auto load_rhs = [&]() {
+#pragma unroll
+        for (int q = 0; q < CPW; ++q) {
+            const int ct = w + NW * q;
+            const bool vcol = ct < V / 16;
+            const int c = (vcol ? 16 * ct : 16 * ct - V) + lr;
+            const float* rhs = vcol ? p.cdU + cs * C * V : p.cdW + cs * C * K;
+            const int ld = vcol ? V : K;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    R[q][j][e] = ct < NCT ? rhs[(size_t)(16 * j + 4 * lg + e) * ld + c] : 0.f;
+        }
+    };
+    constexpr int NPV = (C * V * SZ / 16 + NT - 1) / NT;
+    uint4 rv[NPV];                                  // v rows, for dbeta
+    T* sV = reinterpret_cast<T*>(smem + L::oW + C * LDA * 4);   // after E, over U~^T
+
     // ---- staging (the raw gates pass through the Ak^T area) -------------------------
     {
         constexpr int PRK = K * SZ / 16, PRC = C * SZ / 16;
@@ -338,6 +359,9 @@ __global__ __launch_bounds__(512) void kda_bwd_ksolve_kernel(BwdParams p) {
         load_flat_pieces<NPU, NT>(rec + RL.oUtT, V * PRC, ru, tid);
         const float bt = tid < nt ? to_f32(reinterpret_cast<const T*>(p.beta)[((size_t)b * p.T + t0 + tid) * p.H + h])
                                   : 0.f;
+        // this wave's right-hand sides and v: loaded now, used after the Gram
+        load_rhs();
+        load_tok_pieces<T, V, NPV, NT>(p.v, p, b, h, t0, nt, rv, tid);
         if (tid < C) sB[tid] = bt;
         store_pieces<NPK, NT>(sK, LDK * SZ, PRK, C * PRK, rk, tid);
         store_pieces<NPK, NT>(sAkT, K * SZ, PRK, C * PRK, rg, tid);
@@ -377,40 +401,68 @@ __global__ __launch_bounds__(512) void kda_bwd_ksolve_kernel(BwdParams p) {
     }
     __syncthreads();
 
-    // ---- back substitution, one column of [dU | dW] per thread ---------------------
-    // x_s = rhs_s - sum_{r > s} A[r][s] x_r,  A[r][s] = beta_r Ak[r][s]
-    if (tid < V + K) {
-        const bool vcol = tid < V;
-        const float* rhs = vcol ? p.cdU + cs * C * V + tid : p.cdW + cs * C * K + (tid - V);
-        const int ld = vcol ? V : K;
-        float x[C], y[C];
+    // ---- back substitution (I + A)^T [dBv | dBk] = [dU | dW], A[r][s] = beta_r Ak[r][s] ----
+    // By 16-token blocks from the last: X_j = T_j^T (R_j - sum_{i > j} A_ij^T X_i), with
+    // T_j = (I + A_jj)^{-1}, on fp32 MFMA.  T_j^T lives in a block of Ak^T below the
+    // diagonal (entries never written or read there otherwise).
+    auto tblock = [&](int j) {
+        const int I = j < 3 ? j + 1 : 2, J = j < 3 ? 0 : 1;
+        return sAkT + 16 * I * LDA + 16 * J;
+    };
+    if (tid < 64) {
+        // column c of T_j by forward substitution; written as row c of T_j^T
+        const int j = tid >> 4, c = tid & 15;
+        float tc[16];
 #pragma unroll
-        for (int s = 0; s < C; ++s) x[s] = rhs[(size_t)s * ld];
-        // four partial sums per token: the dependent chain is a quarter as long
+        for (int r = 0; r < 16; ++r) {
+            float a = 0.f;
 #pragma unroll
-        for (int s = C - 1; s >= 0; --s) {
-            float a4[4] = {x[s], 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int r = s + 1; r < C; ++r) a4[r & 3] -= sAkT[s * LDA + r] * y[r];
-            const float acc = (a4[0] + a4[1]) + (a4[2] + a4[3]);
-            x[s] = acc;
-            y[s] = sB[s] * acc;
+            for (int m = 0; m < r; ++m)
+                if (m >= c) a += sAkT[(16 * j + m) * LDA + 16 * j + r] * tc[m];
+            tc[r] = r == c ? 1.f : (r > c ? -sB[16 * j + r] * a : 0.f);
         }
-        if (vcol) {
-            T* dvp = reinterpret_cast<T*>(p.dv) + (((size_t)b * p.T + t0) * p.H + h) * V + tid;
+        float* tt = tblock(j) + c * LDA;
 #pragma unroll
-            for (int s = 0; s < C; ++s) {
-                sBV[s * LDV + tid] = from_f32<T>(x[s]);
-                if (s < nt) dvp[(size_t)s * p.H * V] = from_f32<T>(y[s]);
+        for (int r = 0; r < 16; ++r) tt[r] = tc[r];
+    }
+    __syncthreads();
+    {
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q = 0; q < CPW; ++q) {
+            const int ct = w + NW * q;
+            if (ct >= NCT) break;
+            const bool vcol = ct < V / 16;
+            const int c = (vcol ? 16 * ct : 16 * ct - V) + lr;      // column within dU or dW
+            f32x4 X[4];
+#pragma unroll
+            for (int j = 3; j >= 0; --j) {
+                f32x4 acc = R[q][j];
+#pragma unroll
+                for (int i = j + 1; i < 4; ++i) {
+                    // -A_ij^T: row s = 16 j + lr, reduction r = 16 i + 4 lg + u
+                    const f32x4 ak = *reinterpret_cast<const f32x4*>(&sAkT[(16 * j + lr) * LDA + 16 * i + 4 * lg]);
+                    const f32x4 bt = *reinterpret_cast<const f32x4*>(&sB[16 * i + 4 * lg]);
+                    acc = mma16(acc, -(ak * bt), X[i]);
+                }
+                X[j] = mma16(z, *reinterpret_cast<const f32x4*>(tblock(j) + lr * LDA + 4 * lg), acc);
             }
-        } else {
-            const int c = tid - V;
+            T* dvp = reinterpret_cast<T*>(p.dv) + (((size_t)b * p.T + t0) * p.H + h) * V + c;
             float* dkh = p.cdKh + cs * C * K + c;
 #pragma unroll
-            for (int s = 0; s < C; ++s) {
-                sBK[s * LDK + c] = from_f32<T>(x[s]);
-                dkh[(size_t)s * K] = y[s];
-            }
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int s = 16 * j + 4 * lg + e;
+                    const float x = X[j][e], y = sB[s] * x;
+                    if (vcol) {
+                        sBV[s * LDV + c] = from_f32<T>(x);
+                        if (s < nt) dvp[(size_t)s * p.H * V] = from_f32<T>(y);
+                    } else {
+                        sBK[s * LDK + c] = from_f32<T>(x);
+                        dkh[(size_t)s * K] = y;
+                    }
+                }
         }
     }
     __syncthreads();
@@ -461,6 +513,7 @@ __global__ __launch_bounds__(512) void kda_bwd_ksolve_kernel(BwdParams p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) Et[(16 * i + 4 * lg + e) * C + 16 * j + lr] = 0.f;
     }
+    store_pieces<NPV, NT>(sV, V * SZ, V * SZ / 16, C * V * SZ / 16, rv, tid);
     __syncthreads();
 
     // ---- dbeta: eight threads per token --------------------------------------------
@@ -468,8 +521,7 @@ __global__ __launch_bounds__(512) void kda_bwd_ksolve_kernel(BwdParams p) {
         const int s = tid >> 3, part = tid & 7;
         float acc = 0.f;
         if (s < nt) {
-            const T* vp = reinterpret_cast<const T*>(p.v) + (((size_t)b * p.T + t0 + s) * p.H + h) * V;
-            for (int v = part; v < V; v += 8) acc += to_f32(sBV[s * LDV + v]) * to_f32(vp[v]);
+            for (int v = part; v < V; v += 8) acc += to_f32(sBV[s * LDV + v]) * to_f32(sV[s * V + v]);
             for (int c = part; c < K; c += 8)
                 acc += to_f32(sBK[s * LDK + c]) * to_f32(sK[s * LDK + c]) * fast_exp2(sG[s * LDG + c]);
             for (int r = part; r < s; r += 8) acc += sE[s * LDA + r] * sAkT[r * LDA + s];
