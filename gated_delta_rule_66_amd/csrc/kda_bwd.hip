@@ -319,30 +319,32 @@ __global__ __launch_bounds__(256) void kda_bwd_kernel(BwdParams p) {
 }
 
 // ---- reverse state pass ------------------------------------------------------------
-// Workgroup (b, h, block of VB = 16 NW value columns); wave w owns the block's
-// 16-column tile w.  Per chunk, from the last to the second: the chunk's W,
-// Qh, Mqk, KbT and e^{G_C} are staged in LDS as the record holds them
-// (row-major), and dO^T of the block's columns; the transposed operands
-// (Mqk^T, KbT^T, Qh^T, W^T) are gathered column-wise from those rows.  The
-// result dS is the adjoint of the state after the previous chunk.
+// Workgroup (b, h, segment, block of VB = 16 NW columns); wave w owns the
+// block's 16-column tile w.  Per chunk, from the segment's last: the chunk's
+// W, Qh, Mqk, KbT (staged transposed, so that each MFMA operand is read along
+// its reduction index), e^{G_C} and dO^T of the block's columns go to LDS;
+// dU and dS follow.  dS is the adjoint of the state after the previous chunk.
 template <typename T, int K, int NW>
 struct BwdStateLayout {
     static constexpr int SZ = (int)sizeof(T);
     static constexpr int PAD = 16 / SZ;
     static constexpr int VB = 16 * NW;
     static constexpr int NT = 64 * NW;
-    static constexpr int LDK = K + PAD;          // W, Qh: [C][LDK]
-    static constexpr int LDC = kChunk + PAD;     // Mqk [C][LDC], KbT [K][LDC], dO^T [VB][LDC]
-    static constexpr int oW = 0;
-    static constexpr int oQh = oW + kChunk * LDK * SZ;
-    static constexpr int oM = oQh + kChunk * LDK * SZ;
-    static constexpr int oKbT = oM + kChunk * LDC * SZ;
-    static constexpr int oDoT = oKbT + K * LDC * SZ;
+    // the record's matrices are staged transposed, so that every MFMA operand
+    // is read along its reduction index
+    static constexpr int LDK = K + PAD;          // Kb = KbT^T: [C][LDK]
+    static constexpr int LDC = kChunk + PAD;     // W^T, Qh^T [K][LDC]; Mqk^T [C][LDC]; dO^T [VB][LDC]
+    static constexpr int oWT = 0;
+    static constexpr int oQhT = oWT + K * LDC * SZ;
+    static constexpr int oMT = oQhT + K * LDC * SZ;
+    static constexpr int oKb = oMT + kChunk * LDC * SZ;
+    static constexpr int oDoT = oKb + kChunk * LDK * SZ;
     static constexpr int oEgc = oDoT + VB * LDC * SZ;
     static constexpr int TOTAL = oEgc + K * 4;
     static_assert(TOTAL <= 160 * 1024, "LDS budget exceeded");
-    // 16-byte pieces staged from a record: W | Qh | Mqk | KbT (contiguous in
-    // the record) | e^{G_C}
+    // 16-byte pieces staged from a record: W | Qh | Mqk | KbT | e^{G_C}.  In
+    // every matrix, consecutive pieces run down a column of the source (lanes
+    // then write consecutive LDS addresses of the transposed row).
     static constexpr int PRK = K * SZ / 16, PRC = kChunk * SZ / 16;
     static constexpr int E1 = kChunk * PRK, E2 = E1 + kChunk * PRK, E3 = E2 + kChunk * PRC, E4 = E3 + K * PRC;
     static constexpr int PTOT = E4 + K * 4 / 16;
@@ -361,10 +363,10 @@ __global__ __launch_bounds__(64 * NW) void kda_bwd_state_kernel(BwdParams p) {
     constexpr int SZ = L::SZ, EPP = 16 / SZ;
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
-    const T* sW = reinterpret_cast<const T*>(smem + L::oW);
-    const T* sQh = reinterpret_cast<const T*>(smem + L::oQh);
-    const T* sM = reinterpret_cast<const T*>(smem + L::oM);
-    const T* sKbT = reinterpret_cast<const T*>(smem + L::oKbT);
+    T* sWT = reinterpret_cast<T*>(smem + L::oWT);
+    T* sQhT = reinterpret_cast<T*>(smem + L::oQhT);
+    T* sMT = reinterpret_cast<T*>(smem + L::oMT);
+    T* sKb = reinterpret_cast<T*>(smem + L::oKb);
     T* sDoT = reinterpret_cast<T*>(smem + L::oDoT);
     const float* sEgc = reinterpret_cast<const float*>(smem + L::oEgc);
 
@@ -412,8 +414,19 @@ __global__ __launch_bounds__(64 * NW) void kda_bwd_state_kernel(BwdParams p) {
 #pragma unroll
         for (int m = 0; m < NPT; ++m) {
             const int pc = tid + NT * m;
-            const unsigned off = pc < L::E4 ? (unsigned)RL.oW + (unsigned)pc * 16u
-                                            : (unsigned)RL.oEgc + (unsigned)(pc - L::E4) * 16u;
+            unsigned off;
+            if (pc < L::E2) {                        // W, Qh [C][K]: piece (g, t) = row t, columns EPP g ..
+                const int q = pc < L::E1 ? pc : pc - L::E1;
+                off = (unsigned)(pc < L::E1 ? RL.oW : RL.oQh) + (unsigned)((q % C) * L::PRK + q / C) * 16u;
+            } else if (pc < L::E3) {                 // Mqk [C][C]
+                const int q = pc - L::E2;
+                off = (unsigned)RL.oMqk + (unsigned)((q % C) * L::PRC + q / C) * 16u;
+            } else if (pc < L::E4) {                 // KbT [K][C]: piece (tg, c) = row c, tokens EPP tg ..
+                const int q = pc - L::E3;
+                off = (unsigned)RL.oKbT + (unsigned)((q % K) * L::PRC + q / K) * 16u;
+            } else {
+                off = (unsigned)RL.oEgc + (unsigned)(pc - L::E4) * 16u;
+            }
             pre[m] = pc < L::PTOT ? buf_load16(rr, off) : make_uint4(0, 0, 0, 0);
         }
         const int t0 = ci * C, nt = min(C, T_ - t0);
@@ -423,7 +436,7 @@ __global__ __launch_bounds__(64 * NW) void kda_bwd_state_kernel(BwdParams p) {
         const unsigned rowV = (unsigned)H * V * SZ;
 #pragma unroll
         for (int m = 0; m < NPD; ++m) {
-            const int pc = tid + NT * m, t = pc / L::PDR, sg = pc % L::PDR;
+            const int pc = tid + NT * m, t = pc % C, sg = pc / C;
             dpre[m] = (dob && pc < C * L::PDR && t < nt) ? buf_load16(rd, (unsigned)t * rowV + (unsigned)sg * 16u)
                                                          : make_uint4(0, 0, 0, 0);
         }
@@ -432,48 +445,37 @@ __global__ __launch_bounds__(64 * NW) void kda_bwd_state_kernel(BwdParams p) {
 #pragma unroll
         for (int m = 0; m < NPT; ++m) {
             const int pc = tid + NT * m;
-            unsigned char* dst = nullptr;
-            if (pc < L::E1) {
-                dst = smem + L::oW + (pc / L::PRK) * LDK * SZ + (pc % L::PRK) * 16;
-            } else if (pc < L::E2) {
-                const int q = pc - L::E1;
-                dst = smem + L::oQh + (q / L::PRK) * LDK * SZ + (q % L::PRK) * 16;
-            } else if (pc < L::E3) {
-                const int q = pc - L::E2;
-                dst = smem + L::oM + (q / L::PRC) * LDC * SZ + (q % L::PRC) * 16;
-            } else if (pc < L::E4) {
-                const int q = pc - L::E3;
-                dst = smem + L::oKbT + (q / L::PRC) * LDC * SZ + (q % L::PRC) * 16;
+            T v[EPP];
+            __builtin_memcpy(v, &pre[m], 16);
+            if (pc < L::E2) {                        // W^T, Qh^T [K][LDC]
+                const int q = pc < L::E1 ? pc : pc - L::E1, t = q % C, g = q / C;
+                T* d = (pc < L::E1 ? sWT : sQhT) + (EPP * g) * LDC + t;
+#pragma unroll
+                for (int e = 0; e < EPP; ++e) d[e * LDC] = v[e];
+            } else if (pc < L::E3) {                 // Mqk^T [C][LDC]
+                const int q = pc - L::E2, t = q % C, g = q / C;
+#pragma unroll
+                for (int e = 0; e < EPP; ++e) sMT[(EPP * g + e) * LDC + t] = v[e];
+            } else if (pc < L::E4) {                 // Kb [C][LDK]
+                const int q = pc - L::E3, c = q % K, g = q / K;
+#pragma unroll
+                for (int e = 0; e < EPP; ++e) sKb[(EPP * g + e) * LDK + c] = v[e];
             } else if (pc < L::PTOT) {
-                dst = smem + L::oEgc + (pc - L::E4) * 16;
+                *reinterpret_cast<uint4*>(smem + L::oEgc + (pc - L::E4) * 16) = pre[m];
             }
-            if (dst) *reinterpret_cast<uint4*>(dst) = pre[m];
         }
-        // dO^T: element e of piece (t, sg) is column EPP sg + e of token t
+        // dO^T: element e of piece (sg, t) is column EPP sg + e of token t
 #pragma unroll
         for (int m = 0; m < NPD; ++m) {
             const int pc = tid + NT * m;
             if (pc < C * L::PDR) {
-                const int t = pc / L::PDR, sg = pc % L::PDR;
+                const int t = pc % C, sg = pc / C;
                 T v[EPP];
                 __builtin_memcpy(v, &dpre[m], 16);
 #pragma unroll
                 for (int e = 0; e < EPP; ++e) sDoT[(EPP * sg + e) * LDC + t] = v[e];
             }
         }
-    };
-    // A fragment of X^T for X row-major [reduction][row] in LDS: slot s of
-    // lane (lr, lg) holds X[32 ks + 4 lg + s][r0 + lr] (s < 4) and
-    // X[32 ks + 16 + 4 lg + s - 4][r0 + lr], the slot order of the B fragments
-    auto gather = [&](const T* X, int ld, int ks, int r0) {
-        Frag f;
-        const T* q0 = X + (32 * ks + 4 * lg) * ld + r0 + lr;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            f[i] = q0[i * ld];
-            f[4 + i] = q0[(16 + i) * ld];
-        }
-        return f;
     };
 
     // every chunk's dU goes to p.cdU (chunk-form gradients); the adjoint
@@ -493,40 +495,44 @@ __global__ __launch_bounds__(64 * NW) void kda_bwd_state_kernel(BwdParams p) {
         for (int ti = 0; ti < 4; ++ti) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) acc = mma(acc, gather(sM, LDC, ks, 16 * ti), bdo[ks]);
+            for (int ks = 0; ks < 2; ++ks) acc = mma(acc, ld_frag_perm<T>(&sMT[(16 * ti + lr) * LDC + 32 * ks + 4 * lg]), bdo[ks]);
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) acc = mma(acc, gather(sKbT, LDC, ks, 16 * ti), bds[ks]);
+            for (int ks = 0; ks < KS; ++ks) acc = mma(acc, ld_frag_perm<T>(&sKb[(16 * ti + lr) * LDK + 32 * ks + 4 * lg]), bds[ks]);
             ndU[ti] = -acc;
         }
         if (!SUMMARY) {
-            float* du = p.cdU + ((size_t)bh * NC + ci) * kChunk * V;
+            // per-chunk lane offsets (not hoisted out of the chunk loop: registers)
+            float* du = p.cdU + ((size_t)bh * NC + ci) * kChunk * V + (size_t)(4 * opaque(lg)) * V + opaque(col);
 #pragma unroll
             for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) du[(size_t)(16 * ti + 4 * lg + e) * V + col] = -ndU[ti][e];
+                for (int e = 0; e < 4; ++e) du[(size_t)(16 * ti + e) * V] = -ndU[ti][e];
             if (ci == 0 && !p.ds0) return false;
         }
         Frag bdu[2];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) bdu[ks] = frag_from_tiles<T>(ndU[2 * ks], ndU[2 * ks + 1]);
-        // dS = Diag(e^{G_C}) dS' + Qh^T dO - W^T dU
+        // dS = Diag(e^{G_C}) dS' + Qh^T dO - W^T dU (operands read per row tile:
+        // hoisting all of them would exceed the 8-wave register budget)
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
+            __builtin_amdgcn_sched_barrier(0);
             const f32x4 eg = *reinterpret_cast<const f32x4*>(&sEgc[16 * ct + 4 * lg]);
             f32x4 acc = dS[ct] * eg;
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) acc = mma(acc, gather(sQh, LDK, ks, 16 * ct), bdo[ks]);
+            for (int ks = 0; ks < 2; ++ks) acc = mma(acc, ld_frag_perm<T>(&sQhT[(16 * ct + lr) * LDC + 32 * ks + 4 * lg]), bdo[ks]);
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) acc = mma(acc, gather(sW, LDK, ks, 16 * ct), bdu[ks]);
+            for (int ks = 0; ks < 2; ++ks) acc = mma(acc, ld_frag_perm<T>(&sWT[(16 * ct + lr) * LDC + 32 * ks + 4 * lg]), bdu[ks]);
             dS[ct] = acc;
         }
         if (!SUMMARY) {
             // the adjoint before chunk ci: after chunk ci - 1, or dL/dS_0
-            float* dst = ci > 0 ? p.adj + ((size_t)bh * NC + ci - 1) * KV : p.ds0 + (size_t)bh * KV;
+            float* dst = (ci > 0 ? p.adj + ((size_t)bh * NC + ci - 1) * KV : p.ds0 + (size_t)bh * KV) +
+                         (size_t)(4 * opaque(lg)) * V + opaque(col);
 #pragma unroll
             for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) dst[(size_t)(16 * ct + 4 * lg + e) * V + col] = dS[ct][e];
+                for (int e = 0; e < 4; ++e) dst[(size_t)(16 * ct + e) * V] = dS[ct][e];
         }
         __syncthreads();
         return true;
