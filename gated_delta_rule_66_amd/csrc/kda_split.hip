@@ -700,8 +700,9 @@ struct StateLayout {
     static constexpr int NPT = (PTOT + NT - 1) / NT;     // pieces per thread
 };
 
-// OUT: the output pass computes and stores O (false: states and snapshots only)
-template <typename T, int K, int NW, int NTW, bool SUMMARY, bool OUT = !SUMMARY>
+// OUT: the output pass computes and stores O (false: states and snapshots only);
+// GATE: o is multiplied by sigmoid of the gate input
+template <typename T, int K, int NW, int NTW, bool SUMMARY, bool OUT = !SUMMARY, bool GATE = false>
 __global__ __launch_bounds__(64 * NW, (NW == 4 && NTW == 1 && sizeof(T) == 2 ? 2 : 1))
 void kda_state_kernel(StateParams p) {
     using L = StateLayout<T, K, NW, NTW, SUMMARY>;
@@ -857,6 +858,19 @@ void kda_state_kernel(StateParams p) {
     auto step = [&](int ci) {
         const size_t trow = row0 + (size_t)ci * C;                 // first token row of the chunk
         const int nt = (int)min((size_t)C, row_end - trow);
+        // the output gate's pieces of this wave's o rows, loaded before the
+        // products (the stores of o must not wait for them one by one)
+        constexpr int OWG = 16 * NTW, PPRG = OWG * (int)SZ / 16;
+        uint4 zr[GATE ? PPRG : 1];
+        if constexpr (GATE) {
+            const size_t obase = (trow * p.H + h) * V + vcol0 + OWG * w;
+            const __amdgpu_buffer_rsrc_t rz = make_rsrc(reinterpret_cast<const T*>(p.gate) + obase);
+#pragma unroll
+            for (int m = 0; m < PPRG; ++m) {
+                const int pc = l + 64 * m, row = pc / PPRG, sg = pc % PPRG;
+                zr[m] = row < nt ? buf_load16(rz, (unsigned)row * rowV + (unsigned)sg * 16u) : make_uint4(0, 0, 0, 0);
+            }
+        }
         // every phase first reads all of its LDS operands, then runs its MFMAs
         Frag Sb[NTW][KS];
 #pragma unroll
@@ -946,17 +960,16 @@ void kda_state_kernel(StateParams p) {
                     for (int e = 0; e < 4; ++e) sO[(16 * ti + 4 * lg + e) * OW + 16 * j + lr] = from_f32<T>(acco[j][ti][e]);
             wave_lds_sync();
             constexpr int PPR = OW * (int)SZ / 16;
+            static_assert(PPR == PPRG && C * PPR == 64 * PPR, "output pieces per lane");
             const __amdgpu_buffer_rsrc_t ro = make_rsrc(
                 reinterpret_cast<T*>(p.o) + (trow * p.H + h) * V + vcol0 + OW * w);
-            const size_t obase = (trow * p.H + h) * V + vcol0 + OW * w;
-            const __amdgpu_buffer_rsrc_t rz = make_rsrc(p.gate ? reinterpret_cast<const T*>(p.gate) + obase : nullptr);
 #pragma unroll
-            for (int pc = l; pc < C * PPR; pc += 64) {
-                const int row = pc / PPR, sg = pc % PPR;
+            for (int m = 0; m < PPR; ++m) {
+                const int pc = l + 64 * m, row = pc / PPR, sg = pc % PPR;
                 if (row < nt) {
                     const unsigned off = (unsigned)row * rowV + (unsigned)sg * 16u;
                     uint4 ov = *reinterpret_cast<const uint4*>(&sO[row * OW + sg * (16 / (int)SZ)]);
-                    if (p.gate) ov = gate_piece(ov, buf_load16(rz, off), (const T*)nullptr);
+                    if constexpr (GATE) ov = gate_piece(ov, zr[m], (const T*)nullptr);
                     buf_store16(ro, off, 0u, ov);
                 }
             }
@@ -1133,6 +1146,8 @@ template <typename T, int K, int NW, int NTW>
 static hipError_t launch_state_t(const StateParams& p, int grid, hipStream_t stream) {
     if (p.summary)
         hipLaunchKernelGGL((kda_state_kernel<T, K, NW, NTW, true>), dim3(grid), dim3(64 * NW), 0, stream, p);
+    else if (p.o && p.gate)
+        hipLaunchKernelGGL((kda_state_kernel<T, K, NW, NTW, false, true, true>), dim3(grid), dim3(64 * NW), 0, stream, p);
     else if (p.o)
         hipLaunchKernelGGL((kda_state_kernel<T, K, NW, NTW, false, true>), dim3(grid), dim3(64 * NW), 0, stream, p);
     else
