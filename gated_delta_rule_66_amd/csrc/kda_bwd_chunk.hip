@@ -32,10 +32,11 @@
 // exponent is either <= 0 or within a sub-chunk (at most 80 at the clamp
 // floor), as in the forward.
 //
-// Three kernels, one workgroup (4 waves) per (b, h, chunk):
+// Three kernels, one workgroup (8 waves) per (b, h, chunk):
 //   vside  : U, D, dQh, dKb, dW and the e^{G_C} rowsum term (value-side products)
-//   ksolve : Ak, the back substitution, dv, dKh, Et, dbeta
+//   ksolve : Ak, the back substitution (blocked, fp32 MFMA), dv, dKh, Et, dbeta
 //   kgrad  : the gated products and dq, dk, dg (fp32 throughout)
+// Each issues all of a phase's global loads before it waits on any of them.
 // Intermediates live in an fp32 workspace, one slot per chunk.
 #include "kda_device.h"
 #include "kda_internal.h"
