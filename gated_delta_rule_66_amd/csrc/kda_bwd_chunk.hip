@@ -541,30 +541,49 @@ __global__ __launch_bounds__(512) void kda_bwd_ksolve_kernel(BwdParams p) {
 // All in fp32 (operands and MFMA), whatever the input dtype: the terms of dG
 // are each far larger than their sum (they cancel), so bf16 operands here
 // would cost dg most of its precision.
-template <typename T, int K>
+// The products are independent per channel: a workgroup takes KH of the K
+// channels (two workgroups per chunk at K = 128), so that two fit on a CU.
+template <typename T, int KH>
 struct KgradLayout {
     static constexpr int SZ = (int)sizeof(T), PAD = 16 / SZ;
-    static constexpr int LDK = K + PAD, LDC = C + 4, LDG = K + 4;
+    static constexpr int LDK = KH + PAD, LDC = C + 4, LDG = KH + 4;
     static constexpr int oG = 0;                                // fp32 [C][LDG] cumsum (log2 units)
-    static constexpr int oR = oG + C * LDG * 4;                 // fp32 [5][K]
-    static constexpr int oK = oR + 5 * K * 4;                   // T [C][LDK] k (exact in fp32)
+    static constexpr int oR = oG + C * LDG * 4;                 // fp32 [5][KH]
+    static constexpr int oK = oR + 5 * KH * 4;                  // T [C][LDK] k (exact in fp32)
     static constexpr int oQ = oK + C * LDK * SZ;                // T [C][LDK] q
     static constexpr int oD = oQ + C * LDK * SZ;                // fp32 [C][LDC] D      } then dG [C][LDG]
     static constexpr int oE = oD + C * LDC * 4;                 // fp32 [C][LDC] Et     }
-    static constexpr int oCS = oE + C * LDC * 4;                // fp32 [4][K] column sums
-    static constexpr int oGR = oCS + 4 * K * 4;                 // T [C][K] raw gates
-    static constexpr int TOTAL = oGR + C * K * SZ;
+    static constexpr int oCS = oE + C * LDC * 4;                // fp32 [4][KH] column sums
+    static constexpr int oGR = oCS + 4 * KH * 4;                // T [C][KH] raw gates
+    static constexpr int TOTAL = oGR + C * KH * SZ;
     static_assert(C * LDG <= 2 * C * LDC, "dG must fit over D and Et");
-    static_assert(TOTAL <= 160 * 1024, "LDS budget exceeded");
+    static_assert(TOTAL <= (SZ == 2 ? 80 : 160) * 1024, "two bf16 workgroups per CU");
 };
 
-template <typename T, int K>
+// pieces of columns [c0, c0 + KH) of the [C][N] token tile of a [B, T, H, N]
+// tensor (head h, tokens t0 ..); rows from nt on are zero
+template <typename T, int N, int KH, int NP, int NT>
+__device__ __forceinline__ void load_tok_cols(const void* src, const BwdParams& p, int b, int h, int t0, int nt,
+                                              int c0, uint4 (&r)[NP], int tid) {
+    constexpr int PR = KH * (int)sizeof(T) / 16;
+    const T* base = reinterpret_cast<const T*>(src) + (((size_t)b * p.T + t0) * p.H + h) * N + c0;
+#pragma unroll
+    for (int m = 0; m < NP; ++m) {
+        const int i = tid + NT * m, t = i / PR, sg = i % PR;
+        r[m] = (i < C * PR && t < nt)
+                   ? *reinterpret_cast<const uint4*>(base + (size_t)t * p.H * N + sg * (16 / (int)sizeof(T)))
+                   : make_uint4(0, 0, 0, 0);
+    }
+}
+
+template <typename T, int K, int KH>
 __global__ __launch_bounds__(512) void kda_bwd_kgrad_kernel(BwdParams p) {
-    using L = KgradLayout<T, K>;
+    using L = KgradLayout<T, KH>;
     constexpr int LDK = L::LDK, LDC = L::LDC, LDG = L::LDG, SZ = L::SZ;
-    constexpr int NT = 512, NW = 8;
-    constexpr int NKT = K / 16;                  // channel tiles (4 NKT tiles in all)
+    constexpr int NT = 512, NW = 8, NH = K / KH;
+    constexpr int NKT = KH / 16;                 // channel tiles (4 NKT tiles in all)
     constexpr int TPW = 4 * NKT / NW;            // tiles per wave
+    static_assert(TPW * NW == 4 * NKT, "tiles per wave");
     __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
     float* sG = reinterpret_cast<float*>(smem + L::oG);
     float* sR = reinterpret_cast<float*>(smem + L::oR);
@@ -578,45 +597,48 @@ __global__ __launch_bounds__(512) void kda_bwd_kgrad_kernel(BwdParams p) {
 
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lg = l >> 4, lr = l & 15;
     const int NC = p.NC;
-    const int ci = blockIdx.x % NC, bh = blockIdx.x / NC;
+    // workgroup (b, h, chunk, channel block); the blocks of a chunk are adjacent
+    const int c0 = (blockIdx.x % NH) * KH;
+    const int item = blockIdx.x / NH;
+    const int ci = item % NC, bh = item / NC;
     const int b = bh / p.H, h = bh % p.H;
     const int t0 = ci * C, nt = min(C, p.T - t0);
     const size_t cs = (size_t)bh * NC + ci;
     const size_t rowK = (size_t)p.H * K;
 
     {
-        constexpr int PRK = K * SZ / 16, PRC = C * 4 / 16;
+        constexpr int PRK = KH * SZ / 16, PRC = C * 4 / 16;
         constexpr int NPK = (C * PRK + NT - 1) / NT, NPC = (C * PRC + NT - 1) / NT;
         uint4 rk[NPK], rq[NPK], rg[NPK], rd[NPC], re[NPC];
-        load_tok_pieces<T, K, NPK, NT>(p.k, p, b, h, t0, nt, rk, tid);
-        load_tok_pieces<T, K, NPK, NT>(p.q, p, b, h, t0, nt, rq, tid);
-        load_tok_pieces<T, K, NPK, NT>(p.g, p, b, h, t0, nt, rg, tid);
+        load_tok_cols<T, K, KH, NPK, NT>(p.k, p, b, h, t0, nt, c0, rk, tid);
+        load_tok_cols<T, K, KH, NPK, NT>(p.q, p, b, h, t0, nt, c0, rq, tid);
+        load_tok_cols<T, K, KH, NPK, NT>(p.g, p, b, h, t0, nt, c0, rg, tid);
         load_flat_pieces<NPC, NT>(p.cD + cs * C * C, C * PRC, rd, tid);
         load_flat_pieces<NPC, NT>(p.cEt + cs * C * C, C * PRC, re, tid);
         store_pieces<NPK, NT>(sK, LDK * SZ, PRK, C * PRK, rk, tid);
         store_pieces<NPK, NT>(sQ, LDK * SZ, PRK, C * PRK, rq, tid);
-        store_pieces<NPK, NT>(sGR, K * SZ, PRK, C * PRK, rg, tid);
+        store_pieces<NPK, NT>(sGR, KH * SZ, PRK, C * PRK, rg, tid);
         store_pieces<NPC, NT>(sD, LDC * 4, PRC, C * PRC, rd, tid);
         store_pieces<NPC, NT>(sE, LDC * 4, PRC, C * PRC, re, tid);
     }
     __syncthreads();
     unsigned long long pass = 0;
-    if (tid < K) gate_cumsum_lds<T, LDG, K>(sGR, nt, tid, sG, sR, &pass);
+    if (tid < KH) gate_cumsum_lds<T, LDG, KH>(sGR, nt, tid, sG, sR, &pass);
     __syncthreads();
 
-    const float* dQhg = p.cdQh + cs * C * K;
-    const float* dKbg = p.cdKb + cs * C * K;
-    const float* dKhg = p.cdKh + cs * C * K;
-    T* dqo = reinterpret_cast<T*>(p.dq) + (((size_t)b * p.T + t0) * p.H + h) * K;
-    T* dko = reinterpret_cast<T*>(p.dk) + (((size_t)b * p.T + t0) * p.H + h) * K;
+    const float* dQhg = p.cdQh + cs * C * K + c0;
+    const float* dKbg = p.cdKb + cs * C * K + c0;
+    const float* dKhg = p.cdKh + cs * C * K + c0;
+    T* dqo = reinterpret_cast<T*>(p.dq) + (((size_t)b * p.T + t0) * p.H + h) * K + c0;
+    T* dko = reinterpret_cast<T*>(p.dk) + (((size_t)b * p.T + t0) * p.H + h) * K + c0;
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
     f32x4 dgr[TPW];                              // dG of this wave's tiles until D, Et are done
 #pragma unroll
     for (int it = 0; it < TPW; ++it) {
         const int q = w + NW * it;
         const int i = q / NKT, ct = q % NKT;
-        const int c = 16 * ct + lr;
-        const float Ri = sR[i * K + c];
+        const int c = 16 * ct + lr;              // channel within the block
+        const float Ri = sR[i * KH + c];
         // the epilogue's fp32 operands, loaded ahead of the tile's products
         float eQh[4], eKb[4], eKh[4];
 #pragma unroll
@@ -629,7 +651,7 @@ __global__ __launch_bounds__(512) void kda_bwd_kgrad_kernel(BwdParams p) {
         // forward type on token block i: Y1 = D (k gated), X1 = Et (k gated)
         f32x4 y1 = z, x1 = z;
         for (int j = 0; j <= i; ++j) {
-            const float ref = j == i ? Ri : sR[(j + 1) * K + c];
+            const float ref = j == i ? Ri : sR[(j + 1) * KH + c];
             f32x4 bk;
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
@@ -644,9 +666,9 @@ __global__ __launch_bounds__(512) void kda_bwd_kgrad_kernel(BwdParams p) {
         }
         // transposed type on token block i: Y2 = D^T (q gated), X2 = Et^T (k gated)
         f32x4 y2d = z, x2d = z, y2o = z, x2o = z;
-        const float Rn = sR[(i + 1) * K + c];
+        const float Rn = sR[(i + 1) * KH + c];
         for (int i2 = i; i2 < 4; ++i2) {
-            const float R2 = sR[i2 * K + c];
+            const float R2 = sR[i2 * KH + c];
             f32x4 bq, bk, aD, aE;
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
@@ -669,7 +691,7 @@ __global__ __launch_bounds__(512) void kda_bwd_kgrad_kernel(BwdParams p) {
             }
         }
         // epilogue on rows t = 16 i + 4 lg + e, channel c
-        const float RC = sR[4 * K + c];
+        const float RC = sR[4 * KH + c];
         float colpart = 0.f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -692,7 +714,7 @@ __global__ __launch_bounds__(512) void kda_bwd_kgrad_kernel(BwdParams p) {
         }
         colpart += __shfl_xor(colpart, 16);
         colpart += __shfl_xor(colpart, 32);
-        if (lg == 0) sCS[i * K + c] = colpart;
+        if (lg == 0) sCS[i * KH + c] = colpart;
     }
     __syncthreads();                             // D and Et are no longer read: dG goes over them
 #pragma unroll
@@ -705,10 +727,10 @@ __global__ __launch_bounds__(512) void kda_bwd_kgrad_kernel(BwdParams p) {
     __syncthreads();
 
     // dg: reverse cumsum over the chunk plus the G_C terms, gate-derivative mask
-    if (tid < K) {
+    if (tid < KH) {
         const int c = tid;
-        float tot = p.crs[cs * K + c] + sCS[c] + sCS[K + c] + sCS[2 * K + c] + sCS[3 * K + c];
-        T* dgo = reinterpret_cast<T*>(p.dg) + (((size_t)b * p.T + t0) * p.H + h) * K + c;
+        float tot = p.crs[cs * K + c0 + c] + sCS[c] + sCS[KH + c] + sCS[2 * KH + c] + sCS[3 * KH + c];
+        T* dgo = reinterpret_cast<T*>(p.dg) + (((size_t)b * p.T + t0) * p.H + h) * K + c0 + c;
         for (int t = C - 1; t >= 0; --t) {
             tot += sDG[t * LDG + c];
             if (t < nt) dgo[(size_t)t * rowK] = from_f32<T>(((pass >> t) & 1ull) ? tot : 0.f);
@@ -727,7 +749,7 @@ static hipError_t launch_bwd_chunk_t(int stage, const BwdParams& p, hipStream_t 
     else if (stage == 1)
         hipLaunchKernelGGL((kda_bwd_ksolve_kernel<T, K, V>), dim3((unsigned)n), dim3(512), 0, stream, p);
     else
-        hipLaunchKernelGGL((kda_bwd_kgrad_kernel<T, K>), dim3((unsigned)n), dim3(512), 0, stream, p);
+        hipLaunchKernelGGL((kda_bwd_kgrad_kernel<T, K, 64>), dim3((unsigned)(n * (K / 64))), dim3(512), 0, stream, p);
     return hipGetLastError();
 }
 
