@@ -36,18 +36,31 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
+def _first_bool(kernel_name: str, after: str):
+    """The first bool template argument of a kernel symbol, mangled (Lb0E /
+    Lb1E) or demangled (false / true), after the name `after`."""
+    n = kernel_name[kernel_name.index(after) + len(after):]
+    cands = [(n.find(tok), val) for tok, val in (("Lb0E", False), ("Lb1E", True),
+                                                  ("false", False), ("true", True))]
+    cands = [c for c in cands if c[0] >= 0]
+    return min(cands)[1] if cands else False
+
+
 def launch_name(kernel_name: str):
     """Library launch name of a kernel symbol (None for other kernels)."""
     n = kernel_name
     if "kda_chunk_kernel" in n:
-        # template flag SUMMARY is the last template argument
-        return "chunk_summary" if ("true>" in n or "Lb1E" in n) else "chunk_output"
+        # template flag SUMMARY is the first bool template argument
+        return "chunk_summary" if _first_bool(n, "kda_chunk_kernel") else "chunk_output"
     if "kda_intra_kernel" in n:
         return "intra_chunk"
     if "kda_state_kernel" in n:
-        return "state_summary" if ("true>" in n or "Lb1E" in n) else "state_output"
+        # <T, K, waves, tiles, SUMMARY, OUT, GATE>
+        return "state_summary" if _first_bool(n, "kda_state_kernel") else "state_output"
     if "kda_scan_kernel" in n:
         return "segment_scan"
+    if "kda_decode_multi_kernel" in n:
+        return "decode_steps"
     if "kda_decode_kernel" in n:
         return "decode_step"
     if "kda_copy_state_kernel" in n:
