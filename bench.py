@@ -274,6 +274,13 @@ def main():
                "hbm_frac": dec_gbs / HBM_PEAK_GBS, "bytes_per_step": dec_bytes,
                "kernel_avg_ms": dk["avg_ms"],
                "kernel_gbs": dec_bytes / (dk["avg_ms"] * 1e-3) / 1e9}
+        # HBM bytes per decode launch from the same counter record as the
+        # prefill's (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None
+        dec_traffic, dec_note = recorded_traffic("decode_step", plan)
+        dec["traffic"] = dec_traffic
+        dec["traffic_gbs"] = None if dec_traffic is None else dec_traffic / (dk["avg_ms"] * 1e-3) / 1e9
+        if dec_traffic is None:
+            dec["traffic_note"] = dec_note
         # multi-token verification: the first 4 tokens of every sequence in one
         # call, state read and written once, against 4 single steps
         TV = 4
