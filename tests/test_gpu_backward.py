@@ -37,11 +37,13 @@ def _check(dq, dk, dv, dg, db, ds0, ref, dtype):
         assert max_rel_l2(ds0, rs, (0, 1)) < tol, "ds0"
 
 
-# the last two run the reverse state pass over several segments (10 and 4)
+# the last four run the reverse state pass over several segments (10, 4, 11
+# and 78 segments of the plan for a 256-CU device)
 CASES = [(2, 1, 2, 128, 128, torch.bfloat16), (1, 7, 2, 64, 64, torch.float32),
          (2, 9, 2, 128, 64, torch.bfloat16), (1, 100, 3, 64, 128, torch.bfloat16),
          (2, 300, 2, 128, 128, torch.bfloat16), (1, 257, 2, 128, 128, torch.float32),
-         (1, 2597, 2, 128, 128, torch.bfloat16), (1, 1100, 1, 64, 64, torch.float32)]
+         (1, 2597, 2, 128, 128, torch.bfloat16), (1, 1100, 1, 64, 64, torch.float32),
+         (1, 3000, 1, 64, 64, torch.bfloat16), (1, 20000, 1, 128, 128, torch.bfloat16)]
 
 
 @pytest.mark.parametrize("B,T,H,K,V,dtype", CASES)
