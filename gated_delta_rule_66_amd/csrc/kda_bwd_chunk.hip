@@ -61,27 +61,27 @@ __device__ __forceinline__ void st4(T* dst, f32x4 x) {
 // of them is waited on, then the pieces go to LDS
 // pieces of the [C][N] token tile (head h, tokens t0 ..) of a [B, T, H, N]
 // tensor; rows from nt on (and a null source) are zero
+// (buffer loads over exactly the valid rows: rows past nt read as zeros)
 template <typename T, int N, int NP, int NT = 256>
 __device__ __forceinline__ void load_tok_pieces(const void* src, const BwdParams& p, int b, int h, int t0, int nt,
                                                 uint4 (&r)[NP], int tid) {
     constexpr int PR = N * (int)sizeof(T) / 16;
+    const unsigned rowb = (unsigned)p.H * N * sizeof(T);
     const T* base = src ? reinterpret_cast<const T*>(src) + (((size_t)b * p.T + t0) * p.H + h) * N : nullptr;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc_n(base, base && nt > 0 ? (unsigned)(nt - 1) * rowb + N * sizeof(T) : 0u);
 #pragma unroll
     for (int m = 0; m < NP; ++m) {
         const int i = tid + NT * m, t = i / PR, sg = i % PR;
-        r[m] = (base && i < C * PR && t < nt)
-                   ? *reinterpret_cast<const uint4*>(base + (size_t)t * p.H * N + sg * (16 / (int)sizeof(T)))
-                   : make_uint4(0, 0, 0, 0);
+        const unsigned off = i < C * PR ? (unsigned)t * rowb + (unsigned)sg * 16u : 0xffffffffu - 15u;
+        r[m] = buf_load16(rs, off);
     }
 }
 // pieces [0, n) of a contiguous array
 template <int NP, int NT = 256>
 __device__ __forceinline__ void load_flat_pieces(const void* src, int n, uint4 (&r)[NP], int tid) {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc_n(src, (unsigned)n * 16u);
 #pragma unroll
-    for (int m = 0; m < NP; ++m) {
-        const int i = tid + NT * m;
-        r[m] = i < n ? reinterpret_cast<const uint4*>(src)[i] : make_uint4(0, 0, 0, 0);
-    }
+    for (int m = 0; m < NP; ++m) r[m] = buf_load16(rs, (unsigned)(tid + NT * m) * 16u);
 }
 // piece i to row i / PR, byte (i % PR) 16 of an LDS array with row stride ld_bytes
 template <int NP, int NT = 256>
@@ -168,20 +168,26 @@ __global__ __launch_bounds__(512) void kda_bwd_vside_kernel(BwdParams p) {
     constexpr int NDU = (C * V / 4 + NT - 1) / NT;
     f32x4 rS[NS], rD[NS], rU[NDU];
     uint4 rw[NPW], ro[NPO];
+    {
+        // a missing S0 or dL/dS_T reads as zeros
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc_n(S0, S0 ? (unsigned)(KV * 4) : 0u);
+        const __amdgpu_buffer_rsrc_t rd = make_rsrc_n(dSp, dSp ? (unsigned)(KV * 4) : 0u);
 #pragma unroll
-    for (int m = 0; m < NS; ++m) {
-        const int i = tid + NT * m, r = i / RQ, c4 = 4 * (i % RQ);
-        rS[m] = S0 ? *reinterpret_cast<const f32x4*>(S0 + (size_t)r * V + c4) : f32x4{0.f, 0.f, 0.f, 0.f};
-        rD[m] = dSp ? *reinterpret_cast<const f32x4*>(dSp + (size_t)r * V + c4) : f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int m = 0; m < NS; ++m) {
+            const unsigned off = (unsigned)(tid + NT * m) * 16u;
+            const uint4 a = buf_load16(rs, off), d = buf_load16(rd, off);
+            rS[m] = f32x4{__uint_as_float(a.x), __uint_as_float(a.y), __uint_as_float(a.z), __uint_as_float(a.w)};
+            rD[m] = f32x4{__uint_as_float(d.x), __uint_as_float(d.y), __uint_as_float(d.z), __uint_as_float(d.w)};
+        }
     }
     load_flat_pieces<NPW, NT>(rec + RL.oW, C * PRK, rw, tid);
     load_tok_pieces<T, V, NPO, NT>(p.d_o, p, b, h, t0, nt, ro, tid);
     {
-        const f32x4* du = reinterpret_cast<const f32x4*>(p.cdU + cs * C * V);
+        const __amdgpu_buffer_rsrc_t ru = make_rsrc_n(p.cdU + cs * C * V, (unsigned)(C * V * 4));
 #pragma unroll
         for (int m = 0; m < NDU; ++m) {
-            const int i = tid + NT * m;
-            rU[m] = i < C * V / 4 ? du[i] : f32x4{0.f, 0.f, 0.f, 0.f};
+            const uint4 a = buf_load16(ru, (unsigned)(tid + NT * m) * 16u);
+            rU[m] = f32x4{__uint_as_float(a.x), __uint_as_float(a.y), __uint_as_float(a.z), __uint_as_float(a.w)};
         }
     }
 
@@ -414,13 +420,17 @@ __global__ __launch_bounds__(512) void kda_bwd_ksolve_kernel(BwdParams p) {
         // column c of T_j by forward substitution; written as row c of T_j^T
         const int j = tid >> 4, c = tid & 15;
         float tc[16];
+        // branch-free: T[m][c] = 0 for m < c, so the sums need no mask; rows
+        // r <= c keep their start value
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
+        for (int r = 0; r < 16; ++r) tc[r] = (float)(r == c);
+#pragma unroll
+        for (int r = 1; r < 16; ++r) {
             float a = 0.f;
 #pragma unroll
-            for (int m = 0; m < r; ++m)
-                if (m >= c) a += sAkT[(16 * j + m) * LDA + 16 * j + r] * tc[m];
-            tc[r] = r == c ? 1.f : (r > c ? -sB[16 * j + r] * a : 0.f);
+            for (int m = 0; m < r; ++m) a += sAkT[(16 * j + m) * LDA + 16 * j + r] * tc[m];
+            const float v = -sB[16 * j + r] * a;
+            tc[r] = r > c ? v : tc[r];
         }
         float* tt = tblock(j) + c * LDA;
 #pragma unroll
@@ -566,13 +576,14 @@ template <typename T, int N, int KH, int NP, int NT>
 __device__ __forceinline__ void load_tok_cols(const void* src, const BwdParams& p, int b, int h, int t0, int nt,
                                               int c0, uint4 (&r)[NP], int tid) {
     constexpr int PR = KH * (int)sizeof(T) / 16;
+    const unsigned rowb = (unsigned)p.H * N * sizeof(T);
     const T* base = reinterpret_cast<const T*>(src) + (((size_t)b * p.T + t0) * p.H + h) * N + c0;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc_n(base, nt > 0 ? (unsigned)(nt - 1) * rowb + KH * sizeof(T) : 0u);
 #pragma unroll
     for (int m = 0; m < NP; ++m) {
         const int i = tid + NT * m, t = i / PR, sg = i % PR;
-        r[m] = (i < C * PR && t < nt)
-                   ? *reinterpret_cast<const uint4*>(base + (size_t)t * p.H * N + sg * (16 / (int)sizeof(T)))
-                   : make_uint4(0, 0, 0, 0);
+        const unsigned off = i < C * PR ? (unsigned)t * rowb + (unsigned)sg * 16u : 0xffffffffu - 15u;
+        r[m] = buf_load16(rs, off);
     }
 }
 

@@ -215,6 +215,12 @@ template <int N> __device__ __forceinline__ void st_run(float* p, const float* x
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)0xffffffff, 0x00020000);
 }
+// a resource over the first `bytes` bytes at base: loads at or past the end
+// return zeros (range checking of raw buffer accesses), so conditional reads
+// need no branch; bytes = 0 (e.g. a null source) reads zeros only
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_n(const void* base, unsigned bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
 template <typename T> __device__ __forceinline__ void buf_load2(Pack2<T>& x, __amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff);
 template <> __device__ __forceinline__ void buf_load2<bf16>(Pack2<bf16>& x, __amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
     x.d = __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
