@@ -17,7 +17,7 @@ states it must read or write) over its average duration, measured with HIP
 events that the library records on the launch stream (kda_profile_start).
 ``traffic`` is the HBM traffic per launch from rocprofv3 FETCH_SIZE and
 WRITE_SIZE counters, scaled by a plain-copy calibration; it is read from
-profiles/prefill_c1_traffic.json and reported only while the kernel
+profiles/prefill_8k_traffic.json and reported only while the kernel
 source still has the hash recorded there.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-ms MS] [--extra]
@@ -32,7 +32,7 @@ import sys
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_c1_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_8k_traffic.json")
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
@@ -96,8 +96,8 @@ def main():
                     help="run only a plain device copy of this size (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py: this build runs on one GPU only; --gpus %d is not supported "
-              "(heads and batch shard without communication; see DESIGN.md)" % args.gpus,
+        print("bench.py: measures one GPU only; --gpus %d is not supported "
+              "(heads and batch rows would shard across GPUs without communication)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
 
@@ -162,7 +162,7 @@ def main():
         return {n: {"avg_ms": sum(v) / len(v), "launches_per_call": len(v) / steps} for n, v in per.items()}
 
     # ------------------------------------------------------------ prefill, 8K workload
-    cfg = CONFIGS["c1"]
+    cfg = CONFIGS["prefill_8k"]
     x = make_prefill_config(cfg, dev)
     B, T, H, K, V = cfg.B, cfg.T, cfg.H, cfg.K, cfg.V
     plan = kda.chunk_plan(B, T, H, K, V, cfg.dtype)
@@ -252,7 +252,7 @@ def main():
     # ------------------------------------------------------------ decode workload
     dec = None
     if not args.no_decode:
-        dcfg = CONFIGS["c4"]
+        dcfg = CONFIGS["decode_256x32"]
         d = make_decode_config(dcfg, dev)
         pristine = d["state"]
         state = pristine.clone()
@@ -301,7 +301,7 @@ def main():
 
     extra = {}
     if args.extra:
-        for name in ("c2", "c3"):
+        for name in ("prefill_32k_x8", "prefill_1m"):
             c = CONFIGS[name]
             xe = make_prefill_config(c, dev)
             oe = torch.empty((c.B, c.T, c.H, c.V), dtype=c.dtype, device=dev)
@@ -332,7 +332,7 @@ def main():
         cu = torch.zeros(257, dtype=torch.int32)
         cu[1:] = torch.cumsum(lengths, 0).to(torch.int32)
         Tt, Hv = int(cu[-1]), 32
-        xv = make_prefill_config(CONFIGS["c1"], dev, T=Tt, B=1, H=Hv)
+        xv = make_prefill_config(CONFIGS["prefill_8k"], dev, T=Tt, B=1, H=Hv)
         sq = lambda t: t[0]
         s0v = torch.zeros((256, Hv, 128, 128), dtype=torch.float32, device=dev)
         ov = torch.empty((Tt, Hv, 128), dtype=torch.bfloat16, device=dev)

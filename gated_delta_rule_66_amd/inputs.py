@@ -59,12 +59,12 @@ class DecodeConfig:
 # gate floor, one 1M-token sequence on 16 heads, and 64 decode steps over
 # 256 sequences with a 512 MiB fp32 state.
 CONFIGS = {
-    "c0": PrefillConfig("c0", B=1, T=256, H=2, K=64, V=64, dtype=torch.float32, seed=0),
-    "c1": PrefillConfig("c1", B=1, T=8192, H=32, K=128, V=128, dtype=torch.bfloat16, seed=1),
-    "c2": PrefillConfig("c2", B=8, T=32768, H=32, K=128, V=128, dtype=torch.bfloat16, seed=2,
+    "prefill_small_fp32": PrefillConfig("prefill_small_fp32", B=1, T=256, H=2, K=64, V=64, dtype=torch.float32, seed=0),
+    "prefill_8k": PrefillConfig("prefill_8k", B=1, T=8192, H=32, K=128, V=128, dtype=torch.bfloat16, seed=1),
+    "prefill_32k_x8": PrefillConfig("prefill_32k_x8", B=8, T=32768, H=32, K=128, V=128, dtype=torch.bfloat16, seed=2,
                         s0_std=0.02, pinned_frac=0.2),
-    "c3": PrefillConfig("c3", B=1, T=1048576, H=16, K=128, V=128, dtype=torch.bfloat16, seed=3),
-    "c4": DecodeConfig("c4", N=256, H=32, K=128, V=128, steps=64, dtype=torch.bfloat16, seed=4),
+    "prefill_1m": PrefillConfig("prefill_1m", B=1, T=1048576, H=16, K=128, V=128, dtype=torch.bfloat16, seed=3),
+    "decode_256x32": DecodeConfig("decode_256x32", N=256, H=32, K=128, V=128, steps=64, dtype=torch.bfloat16, seed=4),
 }
 
 

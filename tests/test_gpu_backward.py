@@ -90,7 +90,7 @@ def test_backward_full_8k_workload_sampled():
     it: all gradients of sampled (b, h) chains against the oracle."""
     from gated_delta_rule_66_amd.inputs import CONFIGS, make_prefill_config
     say("bwd full 8K workload, sampled chains")
-    c = CONFIGS["c1"]
+    c = CONFIGS["prefill_8k"]
     x = make_prefill_config(c, "cpu")
     B, T, H, K, V = c.B, c.T, c.H, c.K, c.V
     gen = torch.Generator().manual_seed(12)

@@ -46,8 +46,8 @@ PATHS = [1, 2]
 # ------------------------------------------------------------------ small cases
 @pytest.mark.parametrize("split", PATHS)
 def test_config0_full_parity(split):
-    cfg = CONFIGS["c0"]
-    say("c0 full: B=1 H=2 T=256 K=V=64 fp32 split=%d" % split)
+    cfg = CONFIGS["prefill_small_fp32"]
+    say("small fp32 workload: B=1 H=2 T=256 K=V=64 split=%d" % split)
     d = make_prefill_config(cfg, "cpu")
     x = to_dev(d)
     o, sT = gpu_fwd(x, split=split)
@@ -562,10 +562,10 @@ def _sampled_oracle(x, chains):
     return outs
 
 
-@pytest.mark.parametrize("name,chains,split", [("c1", [(0, 0), (0, 7), (0, 19), (0, 31)], 0),
-                                               ("c1", [(0, 3), (0, 30)], 1),
-                                               ("c2", [(0, 3), (5, 17), (7, 31)], 0),
-                                               ("c3", [(0, 11)], 0)])
+@pytest.mark.parametrize("name,chains,split", [("prefill_8k", [(0, 0), (0, 7), (0, 19), (0, 31)], 0),
+                                               ("prefill_8k", [(0, 3), (0, 30)], 1),
+                                               ("prefill_32k_x8", [(0, 3), (5, 17), (7, 31)], 0),
+                                               ("prefill_1m", [(0, 11)], 0)])
 def test_full_size_prefill_sampled(name, chains, split):
     """Full-size workloads in the launch configuration bench.py times (the
     library's plan), checked against the oracle on sampled (b, h) chains."""
@@ -587,8 +587,8 @@ def test_full_size_prefill_sampled(name, chains, split):
 
 
 def test_full_size_decode_sampled():
-    cfg = CONFIGS["c4"]
-    say("full c4 decode N=%d H=%d steps=%d, oracle on 8 sequences" % (cfg.N, cfg.H, cfg.steps))
+    cfg = CONFIGS["decode_256x32"]
+    say("full decode workload N=%d H=%d steps=%d, oracle on 8 sequences" % (cfg.N, cfg.H, cfg.steps))
     x = make_decode_config(cfg, DEV)
     sel = torch.arange(0, cfg.N, cfg.N // 8)
     ref_state = x["state"][sel].double().cpu().numpy().copy()
