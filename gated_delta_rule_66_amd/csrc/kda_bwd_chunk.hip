@@ -93,25 +93,33 @@ __device__ __forceinline__ void store_pieces(void* dst, int ld_bytes, int PR, in
     }
 }
 
-// the in-chunk cumsum of the clamped log-gates (log2 units) for channel c
-// from the raw gates in LDS ([C][K], zero rows past nt), the sub-chunk
-// references R_j (j = 0..4; R_4 = G_C), and the tokens whose gate lies in
-// [-5, 0] (the clamp passes the gradient there)
-template <typename T, int LDG, int K>
-__device__ __forceinline__ void gate_cumsum_lds(const T* sgraw, int nt, int c, float* sG, float* sR,
-                                                unsigned long long* pass_mask) {
-    float acc = 0.f;
-    unsigned long long m = 0;
-    sR[c] = 0.f;
-#pragma unroll 8
-    for (int t = 0; t < C; ++t) {
-        const float gv = to_f32(sgraw[t * K + c]);
-        if (t < nt && gv >= -5.f && gv <= 0.f) m |= 1ull << t;
-        acc += fminf(fmaxf(gv, -5.f), 0.f) * kLog2e;
-        sG[t * LDG + c] = acc;
-        if ((t & 15) == 15) sR[((t >> 4) + 1) * K + c] = acc;
+// the in-chunk cumsum of the clamped log-gates (log2 units) from the raw gates
+// in LDS ([C][K], zero rows past nt), and the sub-chunk references R_j
+// (j = 0..4; R_4 = G_C).  All NT threads take part: the P = NT / K
+// consecutive lanes of a channel each scan C / P tokens in registers, and
+// their totals are combined by shuffles (no barrier, no LDS scratch).
+template <typename T, int LDG, int K, int NT>
+__device__ __forceinline__ void gate_cumsum_par(const T* sgraw, int tid, float* sG, float* sR) {
+    constexpr int P = NT / K, L = C / P;
+    static_assert(P * K == NT && L * P == C && 16 % L == 0 && (P & (P - 1)) == 0, "cumsum split");
+    const int c = tid / P, part = tid % P;
+    float x[L];
+#pragma unroll
+    for (int i = 0; i < L; ++i) x[i] = to_f32(sgraw[(part * L + i) * K + c]);
+#pragma unroll
+    for (int i = 0; i < L; ++i) x[i] = fminf(fmaxf(x[i], -5.f), 0.f) * kLog2e + (i ? x[i - 1] : 0.f);
+    const float tot = x[L - 1];
+    float incl = tot;
+#pragma unroll
+    for (int d = 1; d < P; d <<= 1) {
+        const float y = __shfl_up(incl, d, P);
+        if (part >= d) incl += y;
     }
-    if (pass_mask) *pass_mask = m;
+    const float off = incl - tot;
+#pragma unroll
+    for (int i = 0; i < L; ++i) sG[(part * L + i) * LDG + c] = off + x[i];
+    if (part == 0) sR[c] = 0.f;
+    if (((part + 1) * L) % 16 == 0) sR[((part + 1) * L / 16) * K + c] = incl;
 }
 
 }  // namespace
@@ -168,6 +176,23 @@ __global__ __launch_bounds__(512) void kda_bwd_vside_kernel(BwdParams p) {
     constexpr int NDU = (C * V / 4 + NT - 1) / NT;
     f32x4 rS[NS], rD[NS], rU[NDU];
     uint4 rw[NPW], ro[NPO];
+    // e^{G_C} of the state rows this thread sums for rs, and the U~ values of
+    // this wave's U tiles: loaded first, so that no phase below waits on a
+    // global load of its own
+    constexpr int NUT = 4 * NVT / NW;                // U tiles per wave
+    static_assert(NUT * NW == 4 * NVT, "U tiles per wave");
+    float egr[NS];
+    typename Frag4Of<T>::type utr[NUT];
+    {
+        const float* egc = reinterpret_cast<const float*>(rec + RL.oEgc);
+#pragma unroll
+        for (int m = 0; m < NS; ++m) egr[m] = egc[(tid + NT * m) / RQ];
+#pragma unroll
+        for (int it = 0; it < NUT; ++it) {
+            const int u = w + NW * it, vt = u >> 2, ti = u & 3;
+            utr[it] = ld_frag4<T>(reinterpret_cast<const T*>(rec + RL.oUtT) + (size_t)(16 * vt + lr) * C + 16 * ti + 4 * lg);
+        }
+    }
     {
         // a missing S0 or dL/dS_T reads as zeros
         const __amdgpu_buffer_rsrc_t rs = make_rsrc_n(S0, S0 ? (unsigned)(KV * 4) : 0u);
@@ -207,14 +232,16 @@ __global__ __launch_bounds__(512) void kda_bwd_vside_kernel(BwdParams p) {
         float d = rS[m][0] * rD[m][0] + rS[m][1] * rD[m][1] + rS[m][2] * rD[m][2] + rS[m][3] * rD[m][3];
 #pragma unroll
         for (int x = 1; x < RQ; x <<= 1) d += __shfl_xor(d, x);
-        if (i % RQ == 0) p.crs[cs * K + r] = reinterpret_cast<const float*>(rec + RL.oEgc)[r] * d;
+        if (i % RQ == 0) p.crs[cs * K + r] = egr[m] * d;
     }
     __syncthreads();
-    for (int u = w; u < 4 * NVT; u += NW) {
-        const int vt = u >> 2, ti = u & 3;
+#pragma unroll
+    for (int it = 0; it < NUT; ++it) {
+        const int u = w + NW * it, vt = u >> 2, ti = u & 3;
         // U~[t][v] for t = 16 ti + 4 lg + e (the record holds U~^T [V][C])
-        const T* ut = reinterpret_cast<const T*>(rec + RL.oUtT) + (size_t)(16 * vt + lr) * C + 16 * ti + 4 * lg;
-        f32x4 acc = ld4_as_f32<T>(ut);
+        f32x4 acc;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = to_f32(utr[it][e]);
         f32x4 m = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
@@ -376,7 +403,7 @@ __global__ __launch_bounds__(512) void kda_bwd_ksolve_kernel(BwdParams p) {
         store_pieces<NPU, NT>(sUt, LDC * SZ, PRC, V * PRC, ru, tid);
     }
     __syncthreads();
-    if (tid < K) gate_cumsum_lds<T, LDG, K>(reinterpret_cast<const T*>(sAkT), nt, tid, sG, sR, nullptr);
+    gate_cumsum_par<T, LDG, K, NT>(reinterpret_cast<const T*>(sAkT), tid, sG, sR);
     __syncthreads();
     // (Ak^T needs no clearing: every entry read below is written by the Gram)
 
@@ -633,8 +660,7 @@ __global__ __launch_bounds__(512) void kda_bwd_kgrad_kernel(BwdParams p) {
         store_pieces<NPC, NT>(sE, LDC * 4, PRC, C * PRC, re, tid);
     }
     __syncthreads();
-    unsigned long long pass = 0;
-    if (tid < KH) gate_cumsum_lds<T, LDG, KH>(sGR, nt, tid, sG, sR, &pass);
+    gate_cumsum_par<T, LDG, KH, NT>(sGR, tid, sG, sR);
     __syncthreads();
 
     const float* dQhg = p.cdQh + cs * C * K + c0;
@@ -744,7 +770,9 @@ __global__ __launch_bounds__(512) void kda_bwd_kgrad_kernel(BwdParams p) {
         T* dgo = reinterpret_cast<T*>(p.dg) + (((size_t)b * p.T + t0) * p.H + h) * K + c0 + c;
         for (int t = C - 1; t >= 0; --t) {
             tot += sDG[t * LDG + c];
-            if (t < nt) dgo[(size_t)t * rowK] = from_f32<T>(((pass >> t) & 1ull) ? tot : 0.f);
+            // the clamp passes the gradient where the raw gate lies in [-5, 0]
+            const float gv = to_f32(sGR[t * KH + c]);
+            if (t < nt) dgo[(size_t)t * rowK] = from_f32<T>(gv >= -5.f && gv <= 0.f ? tot : 0.f);
         }
     }
 }
