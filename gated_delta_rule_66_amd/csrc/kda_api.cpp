@@ -54,7 +54,6 @@ kda_status check_prefill_sizes(int B, int T, int H, int K, int V, kda_dtype dt) 
     if (B < 0 || T < 0 || H < 0 || K <= 0 || V <= 0) return KDA_ERR_INVALID_ARG;
     if (check_dtype(dt) != KDA_OK) return KDA_ERR_INVALID_ARG;
     if (!(K == 64 || K == 128) || !(V == 64 || V == 128)) return KDA_ERR_UNSUPPORTED;
-    if (dt == KDA_F32 && !(K == 64 && V == 64)) return KDA_ERR_UNSUPPORTED;
     // every index stays within size_t and every grid within int
     const double rows = (double)B * (double)T * (double)H;
     if (rows * (double)(K > V ? K : V) > 9.0e18) return KDA_ERR_UNSUPPORTED;
@@ -88,8 +87,19 @@ kda_status resolve_plan(int B, int T, int H, int K, int V, kda_dtype dt, const k
     int vb = req ? req->v_block : 0;
     int ns = req ? req->n_seg : 0;
     int split = req ? req->split : 0;
-    if (vb < 0 || ns < 0 || split < 0 || split > 2) return KDA_ERR_INVALID_ARG;
+    if (vb < 0 || ns < 0 || split < 0 || split > 3) return KDA_ERR_INVALID_ARG;
     if (vb != 0 && vb != 64 && vb != 128) return KDA_ERR_INVALID_ARG;
+    // the token-serial form: the only one for sizes without chunk kernels
+    // (fp32 with K or V = 128); one 64-column workgroup per (b, h, block)
+    if (split == 0 && !split_variant_exists((int)dt, K, V, 64) && !chunk_variant_exists((int)dt, K, 64)) split = 3;
+    if (split == 3) {
+        if ((vb != 0 && vb != 64) || ns > 1) return KDA_ERR_UNSUPPORTED;
+        out->n_seg = 1;
+        out->v_block = 64;
+        out->split = 3;
+        if (cps_out) *cps_out = n_chunks > 0 ? n_chunks : 1;
+        return KDA_OK;
+    }
     // requests no path can serve, rejected before any device query
     if (vb != 0 && vb > V) return KDA_ERR_UNSUPPORTED;
     if (vb != 0 && ns > 1 && K % vb != 0) {
@@ -263,6 +273,16 @@ static kda_status chunk_impl(int B, int T, int H, int K, int V, kda_dtype dt,
     const size_t need = workspace_bytes_for(B, T, H, K, V, dt, pl);
     if (need > 0 && (!workspace || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
 
+    if (pl.split == 3) {
+        TokenFwdParams tp{};
+        tp.q = q; tp.k = k; tp.v = v; tp.g = g; tp.beta = beta; tp.gate = gate;
+        tp.s0 = initial_state;
+        tp.sT = final_state;
+        tp.o = o;
+        tp.B = B; tp.T = T; tp.H = H;
+        return launch_timed("token_fwd", st, [&] { return launch_token_fwd((int)dt, K, V, tp, st); }) == hipSuccess
+                   ? KDA_OK : KDA_ERR_HIP;
+    }
     if (pl.split == 2) {
         // ---- intra-chunk pass: every (b, h, chunk) record at once ----------
         const int NC = (T + kChunk - 1) / kChunk;
@@ -444,7 +464,6 @@ static kda_status check_varlen_sizes(int N, int T_total, int H, int K, int V, kd
     if (N < 0) return KDA_ERR_INVALID_ARG;
     kda_status s = check_prefill_sizes(1, T_total, H, K, V, dt);
     if (s != KDA_OK) return s;
-    if (!split_variant_exists((int)dt, K, V, 64)) return KDA_ERR_UNSUPPORTED;
     if ((double)H * (double)varlen_chunk_bound(N, T_total) > 2.0e9 || (double)N * H * 2.0 > 2.0e9)
         return KDA_ERR_UNSUPPORTED;
     return KDA_OK;
@@ -456,6 +475,7 @@ static size_t varlen_offsets_bytes(int N) { return ((size_t)(N + 1) * sizeof(int
 
 size_t kda_chunk_fwd_varlen_workspace_size(int N, int T_total, int H, int K, int V, kda_dtype dt) {
     if (check_varlen_sizes(N, T_total, H, K, V, dt) != KDA_OK) return (size_t)-1;
+    if (!split_variant_exists((int)dt, K, V, 64)) return 0;    // token-serial form
     return 2 * varlen_offsets_bytes(N) + (size_t)H * varlen_chunk_bound(N, T_total) * record_bytes(K, V, dt);
 }
 
@@ -468,6 +488,8 @@ static kda_status varlen_impl(int N, const int* cu_seqlens, int T_total, int H, 
     kda_status s = check_varlen_sizes(N, T_total, H, K, V, dt);
     if (s != KDA_OK) return s;
     if (snap_interval < 0 || max_snapshots < 0 || snap_interval % kChunk != 0) return KDA_ERR_INVALID_ARG;
+    // snapshots come from the chunk state pass: none for the token-serial form
+    if (snap_interval > 0 && !split_variant_exists((int)dt, K, V, 64)) return KDA_ERR_UNSUPPORTED;
     if (snap_interval > 0 && max_snapshots > 0) {
         if (!snapshots || !aligned16(snapshots)) return KDA_ERR_INVALID_ARG;
         if ((double)max_snapshots * H * K * V > 9.0e15) return KDA_ERR_INVALID_ARG;
@@ -495,6 +517,18 @@ static kda_status varlen_impl(int N, const int* cu_seqlens, int T_total, int H, 
         return launch_timed("copy_state", st, [&] {
                    return launch_copy_state(initial_state, final_state, (size_t)nh * K * V, st);
                }) == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+    }
+    if (!split_variant_exists((int)dt, K, V, 64)) {
+        // sizes without chunk kernels: the token-serial form, per sequence
+        TokenFwdParams tp{};
+        tp.q = q; tp.k = k; tp.v = v; tp.g = g; tp.beta = beta; tp.gate = gate;
+        tp.s0 = initial_state;
+        tp.sT = final_state;
+        tp.o = o;
+        tp.cu_seqlens = cu_seqlens;
+        tp.B = N; tp.T = T_total; tp.H = H;
+        return launch_timed("token_fwd", st, [&] { return launch_token_fwd((int)dt, K, V, tp, st); }) == hipSuccess
+                   ? KDA_OK : KDA_ERR_HIP;
     }
     const size_t need = kda_chunk_fwd_varlen_workspace_size(N, T_total, H, K, V, dt);
     if (!workspace || workspace_bytes < need) return KDA_ERR_WORKSPACE;

@@ -63,6 +63,24 @@ struct MultiDecodeParams {
     int N, T, H;
 };
 
+// Token-serial prefill: one workgroup per (sequence, head, 64-column block)
+// walks the tokens of its chain.  Plain layout [B][T][H][*] (cu_seqlens null)
+// or a packed batch [T_total][H][*] with N = B sequences at cu_seqlens.
+struct TokenFwdParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* g;
+    const void* beta;
+    const void* gate;          // output gate input [.., H, V], or null
+    const float* s0;           // [B][H][K][V] or null (zeros)
+    float* sT;                 // [B][H][K][V] or null; may alias s0
+    void* o;
+    const int* cu_seqlens;     // null: plain layout
+    int B, T, H;               // T: tokens per sequence, or T_total when packed
+};
+hipError_t launch_token_fwd(int dtype, int K, int V, const TokenFwdParams& p, hipStream_t stream);
+
 // ---- split path: intra-chunk pass, then state pass ----------------------------
 // Per (b, h, chunk) the intra-chunk pass writes one record of the operands the
 // state pass needs; all arrays row-major without padding, in the input dtype

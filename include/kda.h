@@ -71,7 +71,13 @@ typedef enum kda_dtype {
  *            walks the chunks and does all chunk work in order;
  *            2 = two passes: an intra-chunk pass over every (b, h, chunk) at
  *            once writes per-chunk operands to the workspace, then a state
- *            pass walks the chunks (the workspace holds those records).
+ *            pass walks the chunks (the workspace holds those records);
+ *            3 = token-serial: one workgroup per (b, h, 64-column block)
+ *            applies the recurrence token by token (the defining equation of
+ *            the page's section "Как хранить миллион токенов в памяти"), the
+ *            state in registers; no workspace, n_seg 1, v_block 64.  The
+ *            library's choice only where no chunk kernel exists (fp32 with
+ *            K = 128); a chain's time grows with its length.
  *   n_seg:   number of sequence segments evaluated side by side on one card
  *            (1 = none; > 1 adds the segment summary and segment scan passes).
  *   v_block: value columns per workgroup of the state-carrying pass (64 or
@@ -86,8 +92,8 @@ typedef struct kda_plan {
 } kda_plan;
 
 /* Sizes supported by the kernels: K, V in {64, 128}; bf16 or fp32 inputs
- * (fp32 only with K = 64).  T >= 0 is arbitrary (the tail chunk is masked);
- * B, H >= 0. */
+ * (fp32 with K = 128 runs the token-serial form, split 3).  T >= 0 is
+ * arbitrary (the tail chunk is masked); B, H >= 0. */
 
 /*
  * The plan kda_chunk_fwd would use for these sizes on the current device.
@@ -183,8 +189,9 @@ kda_status kda_chunk_fwd_gated(int B, int T, int H, int K, int V, kda_dtype dt,
  * Runs the two-pass plan (intra-chunk pass over every chunk of every
  * sequence, then one state-carrying workgroup column block per (sequence,
  * head)); sequences of length 0 copy their state.  Same conventions, dtypes
- * and error codes as kda_chunk_fwd; sizes: K, V in {64, 128}, bf16 (fp32 with
- * K = V = 64).
+ * and error codes as kda_chunk_fwd; sizes: K, V in {64, 128}, bf16 or fp32.
+ * fp32 other than K = V = 64 runs the token-serial form per (sequence, head)
+ * and needs no workspace (the size function returns 0).
  */
 size_t kda_chunk_fwd_varlen_workspace_size(int N, int T_total, int H, int K, int V, kda_dtype dt);
 kda_status kda_chunk_fwd_varlen(int N, const int* cu_seqlens, int T_total, int H, int K, int V, kda_dtype dt,
@@ -223,6 +230,8 @@ kda_status kda_chunk_fwd_varlen_gated(int N, const int* cu_seqlens, int T_total,
  * snap_off_i = sum_{j < i} floor(len_j / snapshot_interval); nothing else in
  * `snapshots` is touched.  o and final_state are exactly those of
  * kda_chunk_fwd_varlen with the same arguments; the workspace is the same.
+ * Snapshots come from the chunk state pass: sizes that run the token-serial
+ * form (fp32 other than K = V = 64) return KDA_ERR_UNSUPPORTED.
  */
 kda_status kda_chunk_fwd_varlen_snapshots(int N, const int* cu_seqlens, int T_total, int H, int K, int V,
                                           kda_dtype dt, const void* q, const void* k, const void* v,

@@ -69,7 +69,28 @@ def test_prefill_rejects_bad_sizes_before_any_launch():
     assert _fwd(lib, dt=7) == INVALID
     assert _fwd(lib, K=96) == UNSUPPORTED
     assert _fwd(lib, V=256) == UNSUPPORTED
-    assert _fwd(lib, dt=F32, K=128, V=128) == UNSUPPORTED
+
+
+def test_fp32_at_128_takes_the_token_serial_form():
+    # no chunk kernels for fp32 with K = 128: the plan is the token-serial
+    # form (split 3, one segment, 64-column blocks), chosen without a device
+    # query and with no workspace (fp32 at K = 64, V = 128 runs the
+    # single-pass chunk kernel in 64-column blocks)
+    lib = _lib()
+    for K, V in ((128, 128), (128, 64)):
+        pl = K_.Plan()
+        assert lib.kda_chunk_fwd_plan(2, 1000, 3, K, V, F32, ctypes.byref(pl)) == OK
+        assert (pl.n_seg, pl.v_block, pl.split) == (1, 64, 3)
+        assert lib.kda_chunk_fwd_workspace_size(2, 1000, 3, K, V, F32, None) == 0
+        assert lib.kda_chunk_fwd_varlen_workspace_size(4, 1000, 3, K, V, F32) == 0
+    # the token-serial form has one segment and 64-column blocks only
+    for bad in (K_.Plan(2, 64, 3), K_.Plan(1, 128, 3)):
+        assert _fwd(lib, plan=bad) == UNSUPPORTED
+        assert lib.kda_chunk_fwd_workspace_size(1, 64, 1, 128, 128, BF16, ctypes.byref(bad)) == ctypes.c_size_t(-1).value
+    assert lib.kda_chunk_fwd_workspace_size(1, 64, 1, 128, 128, BF16, ctypes.byref(K_.Plan(1, 64, 3))) == 0
+    # state snapshots come from the chunk state pass: not with the token-serial form
+    assert _snap(lib, dt=F32) == UNSUPPORTED
+    assert _snap(lib, dt=F32, K=64, V=64, ws=None) == WORKSPACE  # supported: fails only on the workspace
 
 
 def test_prefill_rejects_null_and_misaligned_pointers():
@@ -113,7 +134,7 @@ def test_prefill_rejects_bad_plans():
     assert _fwd(lib, K=64, V=64, plan=K_.Plan(1, 128)) == UNSUPPORTED
     # a segmented plan needs value blocks that tile the K transition columns
     assert _fwd(lib, T=64 * 40, K=64, V=128, plan=K_.Plan(2, 128), ws=FAKE, ws_bytes=1 << 30) == UNSUPPORTED
-    assert _fwd(lib, plan=K_.Plan(1, 64, 3)) == INVALID
+    assert _fwd(lib, plan=K_.Plan(1, 64, 4)) == INVALID
     assert _fwd(lib, plan=K_.Plan(1, 64, -1)) == INVALID
     bad = K_.Plan(1, 96)
     assert lib.kda_chunk_fwd_workspace_size(1, 64, 1, 128, 128, BF16, ctypes.byref(bad)) == ctypes.c_size_t(-1).value
@@ -164,7 +185,6 @@ def test_varlen_validation_before_any_launch():
     assert _varlen(lib, cu=None) == INVALID
     assert _varlen(lib, cu=FAKE + 2) == INVALID                  # int32 alignment
     assert _varlen(lib, K=96) == UNSUPPORTED
-    assert _varlen(lib, K=128, V=128, dt=F32) == UNSUPPORTED    # fp32 only at K = V = 64
     assert _varlen(lib, q=None) == INVALID
     assert _varlen(lib, o=FAKE + 8) == INVALID
     assert _varlen(lib, s0=FAKE, sT=FAKE + 16) == INVALID        # partial state overlap
@@ -184,13 +204,14 @@ def test_varlen_workspace_formula():
     assert _varlen(lib, N=N, T=T, H=H, ws_bytes=2 * offs + H * bound * rec - 1) == WORKSPACE
 
 
-def _snap(lib, interval=128, snaps=FAKE, cap=4, N=3, T=300, H=2, K=128, V=128, ws=FAKE, ws_bytes=1 << 40):
+def _snap(lib, interval=128, snaps=FAKE, cap=4, N=3, T=300, H=2, K=128, V=128, ws=FAKE, ws_bytes=1 << 40,
+          dt=BF16):
     p = ctypes.c_void_p
     lib.kda_chunk_fwd_varlen_snapshots.argtypes = [ctypes.c_int, p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                                    ctypes.c_int, ctypes.c_int] + [p] * 8 + \
         [ctypes.c_int, p, ctypes.c_int, p, ctypes.c_size_t, p]
     lib.kda_chunk_fwd_varlen_snapshots.restype = ctypes.c_int
-    return lib.kda_chunk_fwd_varlen_snapshots(N, p(FAKE), T, H, K, V, BF16, *([p(FAKE)] * 5), None, p(FAKE), None,
+    return lib.kda_chunk_fwd_varlen_snapshots(N, p(FAKE), T, H, K, V, dt, *([p(FAKE)] * 5), None, p(FAKE), None,
                                               interval, p(snaps) if snaps else None, cap, p(ws) if ws else None,
                                               ws_bytes, None)
 
