@@ -671,7 +671,11 @@ static kda_status bwd_layout(int B, int T, int H, int K, int V, kda_dtype dt, Bw
     }
     const size_t bh = (size_t)B * H, kv = (size_t)K * V * sizeof(float);
     size_t o = 0;
-    L->seg = o;   o += align256(segment_bytes(B, H, K, V, L->plan));
+    // the forward plan's segment arrays with one more transition slot: the
+    // backward's summary pass keeps the last segment's transition too, whose
+    // transpose the reverse scan applies first
+    L->seg = o;   o += align256(segment_bytes(B, H, K, V, L->plan) +
+                                (L->plan.n_seg > 1 ? bh * K * K * sizeof(float) : 0));
     L->rec = o;   o += align256(bh * L->NC * record_bytes(K, V, dt));
     L->snaps = o; o += align256(bh * L->NC * kv);
     L->adj = o;   o += align256(bh * L->NC * kv);
@@ -754,17 +758,20 @@ kda_status kda_chunk_bwd(int B, int T, int H, int K, int V, kda_dtype dt,
         sp.n_seg = pl.n_seg;
         sp.cps = L.cps;
         sp.s0 = initial_state;
+        // transitions P (forward order) and loads L of every segment: the
+        // reverse scan applies the transposes of the same P
         float* wsP = reinterpret_cast<float*>(ws + L.seg);
-        float* wsL = wsP + (size_t)(pl.n_seg - 1) * bh * K * K;
+        float* wsL = wsP + (size_t)pl.n_seg * bh * K * K;
         if (pl.n_seg > 1) {
             const int vbs = ((int)dt == 1 && K == 128 && V == 128) ? K + V : vb;
             StateParams s1 = sp;
             s1.summary = 1;
+            s1.summary_all = 1;
             s1.n_vb = (K + V) / vbs;
             s1.wsP = wsP;
             s1.wsL = wsL;
             if (launch_timed("bwd_state_summary", st, [&] {
-                    return launch_state((int)dt, K, vbs, s1, (int)(bh * (pl.n_seg - 1) * s1.n_vb), st);
+                    return launch_state((int)dt, K, vbs, s1, (int)(bh * pl.n_seg * s1.n_vb), st);
                 }) != hipSuccess)
                 return KDA_ERR_HIP;
             ScanParams scp{};
@@ -810,6 +817,7 @@ kda_status kda_chunk_bwd(int B, int T, int H, int K, int V, kda_dtype dt,
         p.cps = L.cps;
         p.wsP = wsP;
         p.wsL = wsL;
+        p.load_only = 1;
         if (pl.n_seg > 1) {
             if (launch_timed("bwd_reverse_summary", st,
                              [&] { return launch_bwd_state(true, (int)dt, K, p, st); }) != hipSuccess)
@@ -821,6 +829,7 @@ kda_status kda_chunk_bwd(int B, int T, int H, int K, int V, kda_dtype dt,
             scp.BH = (int)bh;
             scp.V = V;
             scp.n_seg = pl.n_seg;
+            scp.p_reverse = 1;
             if (launch_timed("bwd_reverse_scan", st, [&] { return launch_scan(K, scp, st); }) != hipSuccess)
                 return KDA_ERR_HIP;
         }

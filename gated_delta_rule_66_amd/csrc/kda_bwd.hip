@@ -375,12 +375,16 @@ __global__ __launch_bounds__(64 * NW) void kda_bwd_state_kernel(BwdParams p) {
     // workgroup (b, h, segment, column block).  Summary: segments 1 .. n_seg - 1,
     // columns [0, K + V): the first K carry the segment's transposed transition
     // (identity start, dO taken as zero), the others its load (zero start).
-    const int nvb = (SUMMARY ? K + V : V) / VB;
+    const bool lonly = SUMMARY && p.load_only;
+    const int nvb = (SUMMARY && !lonly ? K + V : V) / VB;
     const int nseg_here = SUMMARY ? p.n_seg - 1 : p.n_seg;
     // the workgroups of one (b, h) read the same records: one XCD (L2)
     const int G = gridDim.x, x = blockIdx.x;
     const int lid = ((G & 7) == 0) ? (x & 7) * (G >> 3) + (x >> 3) : x;
-    const int vb = lid % nvb, rest = lid / nvb;
+    // block index over [0, K + V) columns in the summary (the load blocks
+    // only: shifted past the K transition columns)
+    const int vb = lid % nvb + (lonly ? K / VB : 0), rest = lid / nvb;
+    static_assert(K % VB == 0, "whole transition blocks");
     const int seg = (rest % nseg_here) + (SUMMARY ? 1 : 0), bh = rest / nseg_here;
     const int b = bh / p.H, h = bh % p.H;
     const int c_begin = seg * p.cps, c_end = min(c_begin + p.cps, NC);
@@ -610,7 +614,7 @@ hipError_t launch_bwd(int dtype, int K, const BwdParams& p, hipStream_t stream) 
 template <typename T, int K, int NW>
 static hipError_t launch_bwd_state_t(bool summary, const BwdParams& p, hipStream_t stream) {
     const long segs = summary ? p.n_seg - 1 : p.n_seg;
-    const long wgs = (long)p.B * p.H * segs * ((summary ? K + p.V : p.V) / (16 * NW));
+    const long wgs = (long)p.B * p.H * segs * ((summary && !p.load_only ? K + p.V : p.V) / (16 * NW));
     if (wgs <= 0) return hipSuccess;
     if (wgs > 2000000000L) return hipErrorInvalidValue;
     if (summary)

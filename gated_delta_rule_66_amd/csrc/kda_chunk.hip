@@ -639,7 +639,7 @@ __global__ __launch_bounds__(256) void kda_chunk_kernel(ChunkParams p) {
 // {(K/4) g + ks : g = 0..3} (lane group g supplies one of them), so every lane
 // reads K/4 consecutive elements of its P row.  The next segment's P rows and
 // L tiles are loaded while the current one is applied.
-template <int K>
+template <int K, bool REV>
 __global__ __launch_bounds__(256) void kda_scan_kernel(ScanParams p) {
     constexpr int RT = K / 16;          // row tiles
     constexpr int TPW = RT / 4;         // row tiles per wave
@@ -665,19 +665,28 @@ __global__ __launch_bounds__(256) void kda_scan_kernel(ScanParams p) {
     float aA[TPW][KQ], aB[TPW][KQ];
     f32x4 lA[TPW], lB[TPW];
     auto load_seg = [&](int j, float (&a)[TPW][KQ], f32x4 (&lt)[TPW]) {
-        const float* P = p.wsP + ((size_t)j * p.BH + bh) * K * K;
+        const int pj = REV ? p.n_seg - 1 - j : j;
+        const float* P = p.wsP + ((size_t)pj * p.BH + bh) * K * K;
         const float* Lj = p.wsL + ((size_t)j * p.BH + bh) * K * V;
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
             const int rt = TPW * w + t;
-            const float* prow = P + (size_t)(16 * rt + lr) * K + KQ * lg;
+            if constexpr (REV) {
+                // row 16 rt + lr of P^T: column 16 rt + lr of P (16 lanes read
+                // 64 consecutive bytes of each row)
+                const float* pcol = P + (size_t)(KQ * lg) * K + 16 * rt + lr;
 #pragma unroll
-            for (int q4 = 0; q4 < KQ / 4; ++q4) {
-                const float4 v4 = *reinterpret_cast<const float4*>(prow + 4 * q4);
-                a[t][4 * q4] = v4.x;
-                a[t][4 * q4 + 1] = v4.y;
-                a[t][4 * q4 + 2] = v4.z;
-                a[t][4 * q4 + 3] = v4.w;
+                for (int q = 0; q < KQ; ++q) a[t][q] = pcol[(size_t)q * K];
+            } else {
+                const float* prow = P + (size_t)(16 * rt + lr) * K + KQ * lg;
+#pragma unroll
+                for (int q4 = 0; q4 < KQ / 4; ++q4) {
+                    const float4 v4 = *reinterpret_cast<const float4*>(prow + 4 * q4);
+                    a[t][4 * q4] = v4.x;
+                    a[t][4 * q4 + 1] = v4.y;
+                    a[t][4 * q4 + 2] = v4.z;
+                    a[t][4 * q4 + 3] = v4.w;
+                }
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) lt[t][e] = Lj[(size_t)(16 * rt + 4 * lg + e) * V + col];
@@ -762,8 +771,10 @@ hipError_t launch_chunk(int dtype, int K, int VB, const ChunkParams& p, int grid
 hipError_t launch_scan(int K, const ScanParams& p, hipStream_t stream) {
     const int grid = p.BH * (p.V / 16);
     if (grid <= 0 || p.n_seg < 2) return hipSuccess;
-    if (K == 128) hipLaunchKernelGGL(kda_scan_kernel<128>, dim3(grid), dim3(256), 0, stream, p);
-    else if (K == 64) hipLaunchKernelGGL(kda_scan_kernel<64>, dim3(grid), dim3(256), 0, stream, p);
+    if (K == 128 && p.p_reverse) hipLaunchKernelGGL((kda_scan_kernel<128, true>), dim3(grid), dim3(256), 0, stream, p);
+    else if (K == 128) hipLaunchKernelGGL((kda_scan_kernel<128, false>), dim3(grid), dim3(256), 0, stream, p);
+    else if (K == 64 && p.p_reverse) hipLaunchKernelGGL((kda_scan_kernel<64, true>), dim3(grid), dim3(256), 0, stream, p);
+    else if (K == 64) hipLaunchKernelGGL((kda_scan_kernel<64, false>), dim3(grid), dim3(256), 0, stream, p);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }

@@ -36,6 +36,10 @@ struct ScanParams {
     const float* wsP;       // [n_seg-1][B*H][K][K]
     float* wsL;             // [n_seg-1][B*H][K][V], overwritten with start states
     int BH, V, n_seg;
+    // reverse scan: slot j applies the transpose of the forward transition of
+    // segment n_seg - 1 - j (wsP holds the forward transitions of all n_seg
+    // segments in forward order)
+    int p_reverse;
 };
 
 struct DecodeParams {
@@ -148,6 +152,8 @@ struct StateParams {
     float* snaps;
     const int* snap_off;
     int snap_every, max_snaps, snap_stride;
+    // summary pass over every segment, the last included (0: all but the last)
+    int summary_all;
 };
 
 bool split_variant_exists(int dtype, int K, int V, int VB);
@@ -206,12 +212,15 @@ struct BwdParams {
     float* cdKh;            // [C][K] diag(beta) dBk
     float* cEt;             // [C][C] diag(beta) E
     // reverse state pass over segments of cps chunks: the summary pass writes
-    // each segment's transposed transition (wsP [K][K]) and load (wsL [K][V])
-    // at scan slot n_seg - 1 - segment; the segment scan (from dL/dS_T) leaves
-    // dL/dS after segment j at wsL slot n_seg - 2 - j
+    // each segment's load (wsL [K][V]) at scan slot n_seg - 1 - segment, and
+    // with load_only == 0 also its transposed transition (wsP [K][K]); with
+    // load_only the scan takes the transposes of the forward transitions
+    // instead.  The segment scan (from dL/dS_T) leaves dL/dS after segment j
+    // at wsL slot n_seg - 2 - j
     int n_seg, cps;
     float* wsP;
     float* wsL;
+    int load_only;
 };
 hipError_t launch_bwd(int dtype, int K, const BwdParams& p, hipStream_t stream);
 // the reverse state pass.  summary: every segment's map (segments >= 1);

@@ -731,7 +731,7 @@ void kda_state_kernel(StateParams p) {
     const int lid = ((G & 7) == 0) ? (x & 7) * (G >> 3) + (x >> 3) : x;
     const int vb = lid % p.n_vb;
     const int rest = lid / p.n_vb;
-    const int nseg_here = SUMMARY ? p.n_seg - 1 : p.n_seg;
+    const int nseg_here = SUMMARY && !p.summary_all ? p.n_seg - 1 : p.n_seg;
     const int seg = rest % nseg_here;
     const int bh = rest / nseg_here;
     const int b = bh / p.H, h = bh % p.H;

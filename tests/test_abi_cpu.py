@@ -322,6 +322,12 @@ def test_backward_validation_before_any_launch():
     assert n == 4 * rec + 2 * (4 * 128 * 128 * 4) + 4 * inter * 4
     assert _bwd(lib, ws_bytes=n - 1) == WORKSPACE
     assert lib.kda_chunk_bwd_workspace_size(1, 0, 2, 128, 128, BF16) == 0
+    # several segments (40 chunks of 2 chains, planned for 256 CUs: 10
+    # segments of 4 chunks): the segment arrays hold the transitions of all
+    # 10 segments (the reverse scan applies their transposes) and the loads
+    n10 = lib.kda_chunk_bwd_workspace_size(1, 64 * 40, 2, 128, 128, BF16)
+    seg = -(-((10 * 2 * 128 * 128 + 10 * 2 * 128 * 128) * 4) // 256) * 256
+    assert n10 == seg + 2 * 40 * rec + 2 * (2 * 40 * 128 * 128 * 4) + 2 * 40 * inter * 4
 
 
 def test_package_raises_without_library(tmp_path):

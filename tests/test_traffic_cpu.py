@@ -17,7 +17,7 @@ def test_state_kernel_classified_by_its_summary_flag():
 
 def test_other_kernels():
     assert launch_name("_ZN3kda16kda_intra_kernelIDF16bLi128ELi128EEEvNS_11IntraParamsE") == "intra_chunk"
-    assert launch_name("void kda::kda_scan_kernel<128>(kda::ScanParams)") == "segment_scan"
+    assert launch_name("void kda::kda_scan_kernel<128, false>(kda::ScanParams)") == "segment_scan"
     assert launch_name("_ZN3kda16kda_chunk_kernelIDF16bLi128ELi4ELb1EEEvNS_11ChunkParamsE") == "chunk_summary"
     assert launch_name("_ZN3kda16kda_chunk_kernelIDF16bLi128ELi4ELb0EEEvNS_11ChunkParamsE") == "chunk_output"
     assert launch_name("_ZN3kda17kda_decode_kernelIDF16bLi128ELi128ELi64EEEvNS_12DecodeParamsE") == "decode_step"
