@@ -554,14 +554,30 @@ __global__ __launch_bounds__(512) void kda_bwd_ksolve_kernel(BwdParams p) {
     store_pieces<NPV, NT>(sV, V * SZ, V * SZ / 16, C * V * SZ / 16, rv, tid);
     __syncthreads();
 
-    // ---- dbeta: eight threads per token --------------------------------------------
+    // ---- dbeta: eight threads per token, each on a contiguous eighth of the
+    // value and key columns (16-byte LDS reads) -------------------------------------
     {
         const int s = tid >> 3, part = tid & 7;
+        constexpr int VP = V / 8, KP = K / 8;
+        static_assert(VP % 8 == 0 && KP % 8 == 0, "whole 8-element pieces per thread");
         float acc = 0.f;
         if (s < nt) {
-            for (int v = part; v < V; v += 8) acc += to_f32(sBV[s * LDV + v]) * to_f32(sV[s * V + v]);
-            for (int c = part; c < K; c += 8)
-                acc += to_f32(sBK[s * LDK + c]) * to_f32(sK[s * LDK + c]) * fast_exp2(sG[s * LDG + c]);
+#pragma unroll
+            for (int u = 0; u < VP / 8; ++u) {
+                const int v = VP * part + 8 * u;
+                const Frag a = ld_frag<T>(&sBV[s * LDV + v]), b = ld_frag<T>(&sV[s * V + v]);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc += to_f32(a[e]) * to_f32(b[e]);
+            }
+#pragma unroll
+            for (int u = 0; u < KP / 8; ++u) {
+                const int c = KP * part + 8 * u;
+                const Frag a = ld_frag<T>(&sBK[s * LDK + c]), b = ld_frag<T>(&sK[s * LDK + c]);
+                float gv[8];
+                ld8f(&sG[s * LDG + c], gv);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc += to_f32(a[e]) * to_f32(b[e]) * fast_exp2(gv[e]);
+            }
             for (int r = part; r < s; r += 8) acc += sE[s * LDA + r] * sAkT[r * LDA + s];
         }
         acc += __shfl_xor(acc, 1);
