@@ -818,6 +818,7 @@ kda_status kda_chunk_bwd(int B, int T, int H, int K, int V, kda_dtype dt,
         p.wsP = wsP;
         p.wsL = wsL;
         p.load_only = 1;
+        p.n_cus = cus;
         if (pl.n_seg > 1) {
             if (launch_timed("bwd_reverse_summary", st,
                              [&] { return launch_bwd_state(true, (int)dt, K, p, st); }) != hipSuccess)

@@ -156,45 +156,33 @@ __global__ __launch_bounds__(512) void kda_bwd_vside_kernel(BwdParams p) {
     T* sDU = reinterpret_cast<T*>(smem + L::oDU);
 
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lg = l >> 4, lr = l & 15;
+    // persistent: workgroup x takes items x, x + G, ... (item = bh * NC + ci);
+    // the next item's S and dS' are loaded while this item's products run
     const int NC = p.NC;
-    const int ci = blockIdx.x % NC, bh = blockIdx.x / NC;
-    const int b = bh / p.H, h = bh % p.H;
-    const int t0 = ci * C, nt = min(C, p.T - t0);
-    const size_t KV = (size_t)K * V, cs = (size_t)bh * NC + ci;
+    const long n_items = (long)p.B * p.H * NC;
+    const size_t KV = (size_t)K * V;
     const RecLayout RL = rec_layout(K, V, SZ);
-    const unsigned char* rec = p.rec + cs * RL.bytes;
-    const float* S0 = ci == 0 ? (p.s0 ? p.s0 + (size_t)bh * KV : nullptr)
-                              : p.snaps + (((size_t)b * NC + ci - 1) * p.H + h) * KV;
-    const float* dSp = ci == NC - 1 ? (p.dsT ? p.dsT + (size_t)bh * KV : nullptr) : p.adj + cs * KV;
-
-    // ---- every global load first: S, dS' (fp32, 4 columns per piece), W, dO, dU ------
     constexpr int NS = K * V / 4 / NT;               // S / dS' pieces per thread
     constexpr int RQ = V / 4;                        // pieces per state row
     static_assert(NS * NT * 4 == K * V && 64 % RQ == 0, "state tiling");
     constexpr int PRK = K * SZ / 16, PRV = V * SZ / 16;
     constexpr int NPW = (C * PRK + NT - 1) / NT, NPO = (C * PRV + NT - 1) / NT;
     constexpr int NDU = (C * V / 4 + NT - 1) / NT;
-    f32x4 rS[NS], rD[NS], rU[NDU];
-    uint4 rw[NPW], ro[NPO];
-    // e^{G_C} of the state rows this thread sums for rs, and the U~ values of
-    // this wave's U tiles: loaded first, so that no phase below waits on a
-    // global load of its own
     constexpr int NUT = 4 * NVT / NW;                // U tiles per wave
     static_assert(NUT * NW == 4 * NVT, "U tiles per wave");
+    f32x4 rS[NS], rD[NS], rU[NDU];
+    uint4 rw[NPW], ro[NPO];
     float egr[NS];
     typename Frag4Of<T>::type utr[NUT];
-    {
-        const float* egc = reinterpret_cast<const float*>(rec + RL.oEgc);
-#pragma unroll
-        for (int m = 0; m < NS; ++m) egr[m] = egc[(tid + NT * m) / RQ];
-#pragma unroll
-        for (int it = 0; it < NUT; ++it) {
-            const int u = w + NW * it, vt = u >> 2, ti = u & 3;
-            utr[it] = ld_frag4<T>(reinterpret_cast<const T*>(rec + RL.oUtT) + (size_t)(16 * vt + lr) * C + 16 * ti + 4 * lg);
-        }
-    }
-    {
-        // a missing S0 or dL/dS_T reads as zeros
+    // S (chunk start) and dS' (chunk end) of an item, fp32, 4 columns per
+    // piece; a missing S0 or dL/dS_T reads as zeros
+    auto load_states = [&](long it_) {
+        const int ci_ = (int)(it_ % NC);
+        const long bh_ = it_ / NC;
+        const int b_ = (int)(bh_ / p.H), h_ = (int)(bh_ % p.H);
+        const float* S0 = ci_ == 0 ? (p.s0 ? p.s0 + (size_t)bh_ * KV : nullptr)
+                                   : p.snaps + (((size_t)b_ * NC + ci_ - 1) * p.H + h_) * KV;
+        const float* dSp = ci_ == NC - 1 ? (p.dsT ? p.dsT + (size_t)bh_ * KV : nullptr) : p.adj + (size_t)it_ * KV;
         const __amdgpu_buffer_rsrc_t rs = make_rsrc_n(S0, S0 ? (unsigned)(KV * 4) : 0u);
         const __amdgpu_buffer_rsrc_t rd = make_rsrc_n(dSp, dSp ? (unsigned)(KV * 4) : 0u);
 #pragma unroll
@@ -203,6 +191,28 @@ __global__ __launch_bounds__(512) void kda_bwd_vside_kernel(BwdParams p) {
             const uint4 a = buf_load16(rs, off), d = buf_load16(rd, off);
             rS[m] = f32x4{__uint_as_float(a.x), __uint_as_float(a.y), __uint_as_float(a.z), __uint_as_float(a.w)};
             rD[m] = f32x4{__uint_as_float(d.x), __uint_as_float(d.y), __uint_as_float(d.z), __uint_as_float(d.w)};
+        }
+    };
+    const long G = gridDim.x;
+    if ((long)blockIdx.x < n_items) load_states(blockIdx.x);
+    for (long item = blockIdx.x; item < n_items; item += G) {
+    const int ci = (int)(item % NC), bh = (int)(item / NC);
+    const int b = bh / p.H, h = bh % p.H;
+    const int t0 = ci * C, nt = min(C, p.T - t0);
+    const size_t cs = (size_t)item;
+    const unsigned char* rec = p.rec + cs * RL.bytes;
+
+    // e^{G_C} of the state rows this thread sums for rs, and the U~ values of
+    // this wave's U tiles: loaded first, so that no phase below waits on a
+    // global load of its own
+    {
+        const float* egc = reinterpret_cast<const float*>(rec + RL.oEgc);
+#pragma unroll
+        for (int m = 0; m < NS; ++m) egr[m] = egc[(tid + NT * m) / RQ];
+#pragma unroll
+        for (int it = 0; it < NUT; ++it) {
+            const int u = w + NW * it, vt = u >> 2, ti = u & 3;
+            utr[it] = ld_frag4<T>(reinterpret_cast<const T*>(rec + RL.oUtT) + (size_t)(16 * vt + lr) * C + 16 * ti + 4 * lg);
         }
     }
     load_flat_pieces<NPW, NT>(rec + RL.oW, C * PRK, rw, tid);
@@ -266,6 +276,9 @@ __global__ __launch_bounds__(512) void kda_bwd_vside_kernel(BwdParams p) {
         const int i = tid + NT * m, t = i / RQ, c4 = 4 * (i % RQ);
         if (i < C * V / 4) st4<T>(&sDU[t * LDV + c4], rU[m]);
     }
+    // the registers of S and dS' are free: the next item's are loaded behind
+    // this item's products
+    if (item + G < n_items) load_states(item + G);
     __syncthreads();
 
     // D = tril(dO U^T): 16 tiles (zeros above the diagonal blocks)
@@ -307,6 +320,8 @@ __global__ __launch_bounds__(512) void kda_bwd_vside_kernel(BwdParams p) {
             dW[o] = -aw[e];
             dKb[o] = ak[e];
         }
+    }
+    __syncthreads();                                 // the next item overwrites the LDS operands
     }
 }
 
@@ -800,7 +815,9 @@ static hipError_t launch_bwd_chunk_t(int stage, const BwdParams& p, hipStream_t 
     if (n <= 0) return hipSuccess;
     if (n > 2000000000L) return hipErrorInvalidValue;
     if (stage == 0)
-        hipLaunchKernelGGL((kda_bwd_vside_kernel<T, K, V>), dim3((unsigned)n), dim3(512), 0, stream, p);
+        // persistent, one workgroup per CU (its LDS allows no second)
+        hipLaunchKernelGGL((kda_bwd_vside_kernel<T, K, V>), dim3((unsigned)(p.n_cus > 0 && p.n_cus < n ? p.n_cus : n)),
+                           dim3(512), 0, stream, p);
     else if (stage == 1)
         hipLaunchKernelGGL((kda_bwd_ksolve_kernel<T, K, V>), dim3((unsigned)n), dim3(512), 0, stream, p);
     else

@@ -221,6 +221,7 @@ struct BwdParams {
     float* wsP;
     float* wsL;
     int load_only;
+    int n_cus;              // compute units of the device (grid of persistent kernels)
 };
 hipError_t launch_bwd(int dtype, int K, const BwdParams& p, hipStream_t stream);
 // the reverse state pass.  summary: every segment's map (segments >= 1);
