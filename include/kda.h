@@ -292,7 +292,9 @@ kda_status kda_recurrent_steps(int N, int T, int H, int K, int V, kda_dtype dt,
  *   d_initial_state : [B, H, K, V] fp32 (written) or NULL
  *   workspace     : at least kda_chunk_bwd_workspace_size(...) bytes (the
  *                   size does not depend on the device).  Chunk form: the
- *                   forward plan's segment arrays, its chunk records, the
+ *                   forward plan's segment arrays (with n_seg > 1, the
+ *                   transitions of all n_seg segments: one K x K fp32 slot
+ *                   per (b, h) more than the forward's), its chunk records, the
  *                   state and dL/dS after every chunk (2 B*H*ceil(T/64)*K*V
  *                   fp32) and per-chunk fp32 intermediates.  Token-level
  *                   form: the state every 8 tokens (B*H*ceil(T/8)*K*V fp32)
