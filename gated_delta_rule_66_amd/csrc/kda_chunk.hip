@@ -639,10 +639,11 @@ __global__ __launch_bounds__(256) void kda_chunk_kernel(ChunkParams p) {
 // {(K/4) g + ks : g = 0..3} (lane group g supplies one of them), so every lane
 // reads K/4 consecutive elements of its P row.  The next segment's P rows and
 // L tiles are loaded while the current one is applied.
-template <int K, bool REV>
-__global__ __launch_bounds__(256) void kda_scan_kernel(ScanParams p) {
+template <int K, bool REV, int NWS>
+__global__ __launch_bounds__(64 * NWS) void kda_scan_kernel(ScanParams p) {
     constexpr int RT = K / 16;          // row tiles
-    constexpr int TPW = RT / 4;         // row tiles per wave
+    constexpr int TPW = RT / NWS;       // row tiles per wave
+    static_assert(TPW * NWS == RT, "whole row tiles per wave");
     constexpr int KQ = K / 4;           // reduction steps
     constexpr int LD = 17;
     __shared__ float sS[K * LD];
@@ -656,7 +657,7 @@ __global__ __launch_bounds__(256) void kda_scan_kernel(ScanParams p) {
     const int w = tid >> 6, l = tid & 63, lg = l >> 4, lr = l & 15;
     const int V = p.V;
     const size_t col = (size_t)cb * 16 + lr;
-    for (int i = tid; i < K * 16; i += 256) {
+    for (int i = tid; i < K * 16; i += 64 * NWS) {
         const int row = i / 16, c = i % 16;
         sS[row * LD + c] = p.s0 ? p.s0[((size_t)bh * K + row) * V + (size_t)cb * 16 + c] : 0.f;
     }
@@ -771,10 +772,12 @@ hipError_t launch_chunk(int dtype, int K, int VB, const ChunkParams& p, int grid
 hipError_t launch_scan(int K, const ScanParams& p, hipStream_t stream) {
     const int grid = p.BH * (p.V / 16);
     if (grid <= 0 || p.n_seg < 2) return hipSuccess;
-    if (K == 128 && p.p_reverse) hipLaunchKernelGGL((kda_scan_kernel<128, true>), dim3(grid), dim3(256), 0, stream, p);
-    else if (K == 128) hipLaunchKernelGGL((kda_scan_kernel<128, false>), dim3(grid), dim3(256), 0, stream, p);
-    else if (K == 64 && p.p_reverse) hipLaunchKernelGGL((kda_scan_kernel<64, true>), dim3(grid), dim3(256), 0, stream, p);
-    else if (K == 64) hipLaunchKernelGGL((kda_scan_kernel<64, false>), dim3(grid), dim3(256), 0, stream, p);
+    // K = 128: eight waves of one row tile each (two waves per SIMD fill the
+    // bubbles of the dependent MFMA chains); K = 64: four waves
+    if (K == 128 && p.p_reverse) hipLaunchKernelGGL((kda_scan_kernel<128, true, 8>), dim3(grid), dim3(512), 0, stream, p);
+    else if (K == 128) hipLaunchKernelGGL((kda_scan_kernel<128, false, 8>), dim3(grid), dim3(512), 0, stream, p);
+    else if (K == 64 && p.p_reverse) hipLaunchKernelGGL((kda_scan_kernel<64, true, 4>), dim3(grid), dim3(256), 0, stream, p);
+    else if (K == 64) hipLaunchKernelGGL((kda_scan_kernel<64, false, 4>), dim3(grid), dim3(256), 0, stream, p);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }
