@@ -701,14 +701,22 @@ __global__ __launch_bounds__(64 * NWS) void kda_scan_kernel(ScanParams p) {
 #pragma unroll
         for (int ks = 0; ks < KQ; ++ks) bS[ks] = sS[(KQ * lg + ks) * LD + lr];
         __builtin_amdgcn_sched_barrier(0);
-        f32x4 acc[TPW];
+        // two independent chains per tile (even and odd reduction steps)
+        f32x4 acc[TPW], acc2[TPW];
 #pragma unroll
-        for (int t = 0; t < TPW; ++t) acc[t] = lt[t];
+        for (int t = 0; t < TPW; ++t) {
+            acc[t] = lt[t];
+            acc2[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
 #pragma unroll
-        for (int ks = 0; ks < KQ; ++ks)
+        for (int ks = 0; ks < KQ; ks += 2)
 #pragma unroll
-            for (int t = 0; t < TPW; ++t)
+            for (int t = 0; t < TPW; ++t) {
                 acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t][ks], bS[ks], acc[t], 0, 0, 0);
+                acc2[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[t][ks + 1], bS[ks + 1], acc2[t], 0, 0, 0);
+            }
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) acc[t] += acc2[t];
         if (j + 3 < p.n_seg) load_seg(j + 2, a, lt);
         float* Lj = p.wsL + ((size_t)j * p.BH + bh) * K * V;
         __syncthreads();
