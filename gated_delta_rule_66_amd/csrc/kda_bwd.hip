@@ -375,6 +375,8 @@ __global__ __launch_bounds__(64 * NW) void kda_bwd_state_kernel(BwdParams p) {
     // workgroup (b, h, segment, column block).  Summary: segments 1 .. n_seg - 1,
     // columns [0, K + V): the first K carry the segment's transposed transition
     // (identity start, dO taken as zero), the others its load (zero start).
+    // With load_only (the chunk-form backward) only the load columns run: the
+    // reverse scan takes the transposes of the forward transitions instead.
     const bool lonly = SUMMARY && p.load_only;
     const int nvb = (SUMMARY && !lonly ? K + V : V) / VB;
     const int nseg_here = SUMMARY ? p.n_seg - 1 : p.n_seg;
@@ -627,7 +629,8 @@ static hipError_t launch_bwd_state_t(bool summary, const BwdParams& p, hipStream
 hipError_t launch_bwd_state(bool summary, int dtype, int K, const BwdParams& p, hipStream_t stream) {
     if (p.NC <= 0 || (long)p.B * p.H == 0) return hipSuccess;
     if (p.V % 64 != 0 || K % 64 != 0 || p.n_seg < 1 || p.cps < 1) return hipErrorInvalidValue;
-    // the 8-wave variant's blocks: (K + V) / 128 in the summary, V / 128 otherwise
+    // the 8-wave variant's blocks: (K + V) / 128 in a full summary, V / 128 in a
+    // load-only summary and in the per-segment pass
     if (dtype == 1) {
         if (K == 128 && p.V == 128) return launch_bwd_state_t<bf16, 128, 8>(summary, p, stream);
         if (K == 128) return launch_bwd_state_t<bf16, 128, 4>(summary, p, stream);
