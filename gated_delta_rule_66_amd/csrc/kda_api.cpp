@@ -7,24 +7,32 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
+
 using namespace kda;
 
 namespace {
 
 // ---- optional per-launch timing (kda_profile_start / kda_profile_stop) ------
 // While active, every kernel launch is bracketed by two HIP events recorded on
-// the launch stream.  Process-wide, not thread-safe; off unless started.
+// the launch stream.  The one piece of process-wide state of the library: off
+// unless started; a mutex guards the record, so launches from several threads
+// are each recorded whole (they serialise while profiling is on).
 struct LaunchProfiler {
-    bool on = false;
     int cap = 0, n = 0;
     hipEvent_t* ev = nullptr;          // 2 * cap events
     const char** names = nullptr;      // cap launch names
 };
 LaunchProfiler g_prof;
+std::mutex g_prof_mu;
+std::atomic<bool> g_prof_on{false};
 
 template <class F>
 hipError_t launch_timed(const char* name, hipStream_t st, F&& launch) {
-    if (!g_prof.on || g_prof.n >= g_prof.cap) return launch();
+    if (!g_prof_on.load(std::memory_order_acquire)) return launch();
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    if (!g_prof.ev || g_prof.n >= g_prof.cap) return launch();
     const int i = g_prof.n++;
     (void)hipEventRecord(g_prof.ev[2 * i], st);
     const hipError_t e = launch();
@@ -33,6 +41,7 @@ hipError_t launch_timed(const char* name, hipStream_t st, F&& launch) {
     return e;
 }
 
+// caller holds g_prof_mu
 void profiler_release() {
     if (g_prof.ev)
         for (int i = 0; i < 2 * g_prof.cap; ++i) (void)hipEventDestroy(g_prof.ev[i]);
@@ -59,6 +68,11 @@ kda_status check_prefill_sizes(int B, int T, int H, int K, int V, kda_dtype dt) 
     if (rows * (double)(K > V ? K : V) > 9.0e18) return KDA_ERR_UNSUPPORTED;
     if ((double)B * H * 2.0 * 1024 > 2.0e9) return KDA_ERR_UNSUPPORTED;
     return KDA_OK;
+}
+
+bool ranges_overlap(const void* a, const void* b, size_t n) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return n > 0 && ((x < y) ? (y < x + n) : (x < y + n));
 }
 
 bool ranges_partially_overlap(const void* a, const void* b, size_t n) {
@@ -224,8 +238,12 @@ kda_status kda_chunk_fwd_plan(int B, int T, int H, int K, int V, kda_dtype dt, k
     return resolve_plan(B, T, H, K, V, dt, nullptr, plan, nullptr);
 }
 
-size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int K, int V, kda_dtype dt,
-                                    const kda_plan* plan) {
+size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int K, int V, kda_dtype dt) {
+    return kda_chunk_fwd_planned_workspace_size(B, T, H, K, V, dt, nullptr);
+}
+
+size_t kda_chunk_fwd_planned_workspace_size(int B, int T, int H, int K, int V, kda_dtype dt,
+                                            const kda_plan* plan) {
     if (check_prefill_sizes(B, T, H, K, V, dt) != KDA_OK) return (size_t)-1;
     kda_plan pl;
     if (resolve_plan(B, T, H, K, V, dt, plan, &pl, nullptr) != KDA_OK) return (size_t)-1;
@@ -239,7 +257,7 @@ static kda_status chunk_impl(int B, int T, int H, int K, int V, kda_dtype dt,
                              void* o, float* final_state,
                              const kda_plan* plan,
                              void* workspace, size_t workspace_bytes,
-                             void* stream) {
+                             hipStream_t stream) {
     kda_status s = check_prefill_sizes(B, T, H, K, V, dt);
     if (s != KDA_OK) return s;
     const long bh = (long)B * H;
@@ -257,7 +275,7 @@ static kda_status chunk_impl(int B, int T, int H, int K, int V, kda_dtype dt,
     if (initial_state && final_state && ranges_partially_overlap(initial_state, final_state, state_bytes))
         return KDA_ERR_INVALID_ARG;
     if (bh == 0) return KDA_OK;
-    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    hipStream_t st = stream;
 
     if (T == 0) {
         if (!final_state || final_state == initial_state) return KDA_OK;
@@ -431,12 +449,25 @@ static kda_status chunk_impl(int B, int T, int H, int K, int V, kda_dtype dt,
 
 kda_status kda_chunk_fwd(int B, int T, int H, int K, int V, kda_dtype dt,
                          const void* q, const void* k, const void* v,
-                         const void* g, const void* beta,
+                         const void* g,
+                         const void* beta,
                          const float* initial_state,
-                         void* o, float* final_state,
-                         const kda_plan* plan,
+                         void* o,
+                         float* final_state,
                          void* workspace, size_t workspace_bytes,
-                         void* stream) {
+                         hipStream_t stream) {
+    return chunk_impl(B, T, H, K, V, dt, q, k, v, g, beta, nullptr, initial_state, o, final_state, nullptr,
+                      workspace, workspace_bytes, stream);
+}
+
+kda_status kda_chunk_fwd_planned(int B, int T, int H, int K, int V, kda_dtype dt,
+                                 const void* q, const void* k, const void* v,
+                                 const void* g, const void* beta,
+                                 const float* initial_state,
+                                 void* o, float* final_state,
+                                 const kda_plan* plan,
+                                 void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
     return chunk_impl(B, T, H, K, V, dt, q, k, v, g, beta, nullptr, initial_state, o, final_state, plan,
                       workspace, workspace_bytes, stream);
 }
@@ -448,7 +479,7 @@ kda_status kda_chunk_fwd_gated(int B, int T, int H, int K, int V, kda_dtype dt,
                                void* o, float* final_state,
                                const kda_plan* plan,
                                void* workspace, size_t workspace_bytes,
-                               void* stream) {
+                               hipStream_t stream) {
     if (!gate && (long)B * H > 0 && T > 0) return KDA_ERR_INVALID_ARG;
     return chunk_impl(B, T, H, K, V, dt, q, k, v, g, beta, gate, initial_state, o, final_state, plan,
                       workspace, workspace_bytes, stream);
@@ -484,7 +515,7 @@ static kda_status varlen_impl(int N, const int* cu_seqlens, int T_total, int H, 
                               const void* gate,
                               const float* initial_state, void* o, float* final_state, int snap_interval,
                               float* snapshots, int max_snapshots, void* workspace, size_t workspace_bytes,
-                              void* stream) {
+                              hipStream_t stream) {
     kda_status s = check_varlen_sizes(N, T_total, H, K, V, dt);
     if (s != KDA_OK) return s;
     if (snap_interval < 0 || max_snapshots < 0 || snap_interval % kChunk != 0) return KDA_ERR_INVALID_ARG;
@@ -511,7 +542,7 @@ static kda_status varlen_impl(int N, const int* cu_seqlens, int T_total, int H, 
     if (initial_state && final_state && ranges_partially_overlap(initial_state, final_state, state_bytes))
         return KDA_ERR_INVALID_ARG;
     if (nh == 0) return KDA_OK;
-    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    hipStream_t st = stream;
     if (T_total == 0) {
         if (!final_state || final_state == initial_state) return KDA_OK;
         return launch_timed("copy_state", st, [&] {
@@ -595,7 +626,7 @@ kda_status kda_chunk_fwd_varlen(int N, const int* cu_seqlens, int T_total, int H
                                 const float* initial_state,
                                 void* o, float* final_state,
                                 void* workspace, size_t workspace_bytes,
-                                void* stream) {
+                                hipStream_t stream) {
     return varlen_impl(N, cu_seqlens, T_total, H, K, V, dt, q, k, v, g, beta, nullptr, initial_state, o,
                        final_state, 0, nullptr, 0, workspace, workspace_bytes, stream);
 }
@@ -604,7 +635,7 @@ kda_status kda_chunk_fwd_varlen_gated(int N, const int* cu_seqlens, int T_total,
                                       kda_dtype dt, const void* q, const void* k, const void* v,
                                       const void* g, const void* beta, const void* gate,
                                       const float* initial_state, void* o, float* final_state,
-                                      void* workspace, size_t workspace_bytes, void* stream) {
+                                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
     if (!gate && (long)N * H > 0 && T_total > 0) return KDA_ERR_INVALID_ARG;
     return varlen_impl(N, cu_seqlens, T_total, H, K, V, dt, q, k, v, g, beta, gate, initial_state, o,
                        final_state, 0, nullptr, 0, workspace, workspace_bytes, stream);
@@ -615,7 +646,7 @@ kda_status kda_chunk_fwd_varlen_snapshots(int N, const int* cu_seqlens, int T_to
                                           const void* g, const void* beta, const float* initial_state,
                                           void* o, float* final_state, int snapshot_interval,
                                           float* snapshots, int max_snapshots,
-                                          void* workspace, size_t workspace_bytes, void* stream) {
+                                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
     if (snapshot_interval <= 0) return KDA_ERR_INVALID_ARG;
     return varlen_impl(N, cu_seqlens, T_total, H, K, V, dt, q, k, v, g, beta, nullptr, initial_state, o,
                        final_state, snapshot_interval, snapshots, max_snapshots, workspace, workspace_bytes,
@@ -696,7 +727,7 @@ kda_status kda_chunk_bwd(int B, int T, int H, int K, int V, kda_dtype dt,
                          const void* q, const void* k, const void* v, const void* g, const void* beta,
                          const float* initial_state, const void* d_o, const float* d_final_state,
                          void* dq, void* dk, void* dv, void* dg, void* dbeta, float* d_initial_state,
-                         void* workspace, size_t workspace_bytes, void* stream) {
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
     kda_status s = check_bwd_sizes(B, T, H, K, V, dt);
     if (s != KDA_OK) return s;
     const long bh = (long)B * H;
@@ -710,8 +741,13 @@ kda_status kda_chunk_bwd(int B, int T, int H, int K, int V, kda_dtype dt,
     if ((initial_state && !aligned16(initial_state)) || (d_final_state && !aligned16(d_final_state)) ||
         (d_initial_state && !aligned16(d_initial_state)) || (workspace && !aligned16(workspace)))
         return KDA_ERR_INVALID_ARG;
+    // the reverse state pass reads dL/dS_T in the same launch that writes
+    // dL/dS_0: the two may not share a byte (not even as an exact alias)
+    if (d_initial_state && d_final_state &&
+        ranges_overlap(d_initial_state, d_final_state, (size_t)bh * K * V * sizeof(float)))
+        return KDA_ERR_INVALID_ARG;
     if (bh == 0) return KDA_OK;
-    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    hipStream_t st = stream;
     if (T == 0) {
         // no tokens: dL/dS_0 = dL/dS_T
         if (!d_initial_state) return KDA_OK;
@@ -861,7 +897,7 @@ kda_status kda_chunk_bwd(int B, int T, int H, int K, int V, kda_dtype dt,
 kda_status kda_recurrent_steps(int N, int T, int H, int K, int V, kda_dtype dt,
                                const void* q, const void* k, const void* v,
                                const void* g, const void* beta,
-                               float* state, void* o, float* step_states, void* stream) {
+                               float* state, void* o, float* step_states, hipStream_t stream) {
     if (N < 0 || T < 0 || H < 0 || K <= 0 || V <= 0) return KDA_ERR_INVALID_ARG;
     if (check_dtype(dt) != KDA_OK) return KDA_ERR_INVALID_ARG;
     if (!(K == 64 || K == 128) || !(V == 64 || V == 128)) return KDA_ERR_UNSUPPORTED;
@@ -886,7 +922,7 @@ kda_status kda_recurrent_steps(int N, int T, int H, int K, int V, kda_dtype dt,
     p.o = o;
     p.step_states = step_states;
     p.N = N; p.T = T; p.H = H;
-    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    hipStream_t st = stream;
     return launch_timed("decode_steps", st, [&] { return launch_decode_multi((int)dt, K, V, p, st); }) ==
                    hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
@@ -894,7 +930,7 @@ kda_status kda_recurrent_steps(int N, int T, int H, int K, int V, kda_dtype dt,
 kda_status kda_recurrent_step(int N, int H, int K, int V, kda_dtype dt,
                               const void* q, const void* k, const void* v,
                               const void* g, const void* beta,
-                              float* state, void* o, void* stream) {
+                              float* state, void* o, hipStream_t stream) {
     if (N < 0 || H < 0 || K <= 0 || V <= 0) return KDA_ERR_INVALID_ARG;
     if (check_dtype(dt) != KDA_OK) return KDA_ERR_INVALID_ARG;
     if (!(K == 64 || K == 128) || !(V == 64 || V == 128)) return KDA_ERR_UNSUPPORTED;
@@ -911,31 +947,36 @@ kda_status kda_recurrent_step(int N, int H, int K, int V, kda_dtype dt,
     p.state = state;
     p.o = o;
     p.NH = (int)nh;
-    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    hipStream_t st = stream;
     return launch_timed("decode_step", st, [&] { return launch_decode((int)dt, K, V, p, st); }) ==
                    hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
 kda_status kda_profile_start(int max_launches) {
     if (max_launches <= 0 || max_launches > (1 << 20)) return KDA_ERR_INVALID_ARG;
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof_on.store(false, std::memory_order_release);
     profiler_release();
-    g_prof.ev = new hipEvent_t[2 * (size_t)max_launches]();
-    g_prof.names = new const char*[max_launches]();
+    LaunchProfiler p;
+    p.ev = new hipEvent_t[2 * (size_t)max_launches]();
+    p.names = new const char*[max_launches]();
     for (int i = 0; i < 2 * max_launches; ++i) {
-        if (hipEventCreate(&g_prof.ev[i]) != hipSuccess) {
-            for (int j = 0; j < i; ++j) (void)hipEventDestroy(g_prof.ev[j]);
-            delete[] g_prof.ev;
-            delete[] g_prof.names;
-            g_prof = LaunchProfiler{};
+        if (hipEventCreate(&p.ev[i]) != hipSuccess) {
+            for (int j = 0; j < i; ++j) (void)hipEventDestroy(p.ev[j]);
+            delete[] p.ev;
+            delete[] p.names;
             return KDA_ERR_HIP;
         }
     }
-    g_prof.cap = max_launches;
-    g_prof.on = true;
+    p.cap = max_launches;
+    g_prof = p;
+    g_prof_on.store(true, std::memory_order_release);
     return KDA_OK;
 }
 
 int kda_profile_stop(const char** names, float* ms, int cap) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof_on.store(false, std::memory_order_release);
     if (!g_prof.ev) return -1;
     const int n = g_prof.n;
     int ret = n;

@@ -26,6 +26,8 @@ EXPORTED_SYMBOLS = (
     "kda_chunk_fwd_plan",
     "kda_chunk_fwd_workspace_size",
     "kda_chunk_fwd",
+    "kda_chunk_fwd_planned_workspace_size",
+    "kda_chunk_fwd_planned",
     "kda_chunk_fwd_gated",
     "kda_chunk_fwd_varlen_workspace_size",
     "kda_chunk_fwd_varlen",
@@ -66,11 +68,15 @@ def load_library(path: str = LIB_PATH):
     i, p, sz = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
     lib.kda_chunk_fwd_plan.argtypes = [i, i, i, i, i, i, ctypes.POINTER(Plan)]
     lib.kda_chunk_fwd_plan.restype = i
-    lib.kda_chunk_fwd_workspace_size.argtypes = [i, i, i, i, i, i, ctypes.POINTER(Plan)]
+    lib.kda_chunk_fwd_workspace_size.argtypes = [i, i, i, i, i, i]
     lib.kda_chunk_fwd_workspace_size.restype = sz
-    lib.kda_chunk_fwd.argtypes = [i, i, i, i, i, i, p, p, p, p, p, p, p, p,
-                                  ctypes.POINTER(Plan), p, sz, p]
+    lib.kda_chunk_fwd.argtypes = [i, i, i, i, i, i, p, p, p, p, p, p, p, p, p, sz, p]
     lib.kda_chunk_fwd.restype = i
+    lib.kda_chunk_fwd_planned_workspace_size.argtypes = [i, i, i, i, i, i, ctypes.POINTER(Plan)]
+    lib.kda_chunk_fwd_planned_workspace_size.restype = sz
+    lib.kda_chunk_fwd_planned.argtypes = [i, i, i, i, i, i, p, p, p, p, p, p, p, p,
+                                          ctypes.POINTER(Plan), p, sz, p]
+    lib.kda_chunk_fwd_planned.restype = i
     lib.kda_chunk_fwd_gated.argtypes = [i, i, i, i, i, i, p, p, p, p, p, p, p, p, p,
                                         ctypes.POINTER(Plan), p, sz, p]
     lib.kda_chunk_fwd_gated.restype = i
@@ -176,9 +182,14 @@ def chunk_plan(B: int, T: int, H: int, K: int, V: int, dtype: torch.dtype) -> Tu
 
 
 def chunk_workspace_size(B: int, T: int, H: int, K: int, V: int, dtype: torch.dtype, plan=None) -> int:
+    """Workspace bytes of ``kda_chunk_fwd`` (plan None: the library's plan) or
+    of ``kda_chunk_fwd_planned`` in ``plan``."""
     pl = _plan_arg(plan)
-    n = load_library().kda_chunk_fwd_workspace_size(B, T, H, K, V, _dtype_code(dtype),
-                                                    None if pl is None else ctypes.byref(pl))
+    lib = load_library()
+    if pl is None:
+        n = lib.kda_chunk_fwd_workspace_size(B, T, H, K, V, _dtype_code(dtype))
+    else:
+        n = lib.kda_chunk_fwd_planned_workspace_size(B, T, H, K, V, _dtype_code(dtype), ctypes.byref(pl))
     if n == ctypes.c_size_t(-1).value:
         raise KDAError(KDA_ERR_INVALID_ARG, "kda_chunk_fwd_workspace_size")
     return int(n)
@@ -189,8 +200,8 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
               output_final_state: bool = True, plan=None, *,
               out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
               workspace: Optional[torch.Tensor] = None, gate: Optional[torch.Tensor] = None):
-    """KDA chunked prefill through ``kda_chunk_fwd`` (``kda_chunk_fwd_gated``
-    with ``gate``).
+    """KDA chunked prefill through ``kda_chunk_fwd`` (``kda_chunk_fwd_planned``
+    with a ``plan``, ``kda_chunk_fwd_gated`` with ``gate``).
 
     q, k, g: [B, T, H, K]; v: [B, T, H, V]; beta: [B, T, H] (one dtype, bf16
     or fp32, on one GPU); initial_state: [B, H, K, V] fp32 or None.
@@ -231,12 +242,19 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
         if st != KDA_OK:
             raise KDAError(st, "kda_chunk_fwd_gated")
         return out, final_state
-    st = load_library().kda_chunk_fwd(
+    if pl is None:
+        st = load_library().kda_chunk_fwd(
+            B, T, H, K, V, _dtype_code(dt), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+            _ptr(initial_state), _ptr(out), _ptr(final_state), _ptr(workspace), ws_len, _stream_ptr(dev))
+        if st != KDA_OK:
+            raise KDAError(st, "kda_chunk_fwd")
+        return out, final_state
+    st = load_library().kda_chunk_fwd_planned(
         B, T, H, K, V, _dtype_code(dt), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-        _ptr(initial_state), _ptr(out), _ptr(final_state),
-        None if pl is None else ctypes.byref(pl), _ptr(workspace), ws_len, _stream_ptr(dev))
+        _ptr(initial_state), _ptr(out), _ptr(final_state), ctypes.byref(pl), _ptr(workspace), ws_len,
+        _stream_ptr(dev))
     if st != KDA_OK:
-        raise KDAError(st, "kda_chunk_fwd")
+        raise KDAError(st, "kda_chunk_fwd_planned")
     return out, final_state
 
 

@@ -28,8 +28,8 @@
  *     and o 16 bytes and beta its element size; for decode every token
  *     tensor its element size.  The caller owns every buffer, the workspace
  *     included; the library allocates no device memory.
- *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is
- *     the default stream) of the current HIP device.  Nothing is synchronised.
+ *   - Work is enqueued asynchronously on `stream` (NULL is the default
+ *     stream) of the current HIP device.  Nothing is synchronised.
  *   - Arguments are validated on the host before anything is launched; on an
  *     error nothing is launched.  KDA_ERR_INVALID_ARG: a null pointer, a
  *     negative size, a misaligned pointer, a partially overlapping state
@@ -39,14 +39,17 @@
  *   - Token tensors (q, k, v, g, beta, o) share one dtype `dt`; states are
  *     always fp32.  o is rounded to `dt` (round to nearest even).
  *   - Results are deterministic: no floating-point atomics.
- *   - The library keeps no state between calls, except the opt-in launch
- *     timing of kda_profile_start / kda_profile_stop below.
+ *   - The library keeps no state between calls and every call is reentrant,
+ *     with one opt-in exception: the launch timing of kda_profile_start /
+ *     kda_profile_stop below keeps one process-wide record (guarded by a
+ *     mutex) while it is on.
  *   - Non-finite inputs propagate; they are not detected.
  */
 #ifndef KDA_H
 #define KDA_H
 
 #include <stddef.h>
+#include <hip/hip_runtime_api.h>   /* hipStream_t */
 
 #ifdef __cplusplus
 extern "C" {
@@ -96,7 +99,7 @@ typedef struct kda_plan {
  * arbitrary (the tail chunk is masked); B, H >= 0. */
 
 /*
- * The plan kda_chunk_fwd would use for these sizes on the current device.
+ * The plan kda_chunk_fwd uses for these sizes on the current device.
  * Fills *plan.  Returns KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED or
  * KDA_ERR_HIP (device query failed).
  */
@@ -104,20 +107,18 @@ kda_status kda_chunk_fwd_plan(int B, int T, int H, int K, int V, kda_dtype dt,
                               kda_plan* plan);
 
 /*
- * Bytes of device workspace kda_chunk_fwd needs for these sizes and plan
- * (plan NULL or fields 0: the library's choice on the current device):
- * with split = 2 one record per (b, h, chunk) (for K = V = 128 bf16, 72.5 KiB),
- * with n_seg > 1 the segment transitions and local states
- * ((n_seg - 1) * B * H * K * (K + V) fp32) plus B * H * K * V fp32.
- * 0 when none is needed; (size_t)-1 for invalid or unsupported arguments.
+ * Bytes of device workspace kda_chunk_fwd needs for these sizes in the plan
+ * the library picks on the current device (kda_chunk_fwd_plan).  0 when none
+ * is needed; (size_t)-1 for invalid or unsupported arguments or a failed
+ * device query.
  */
-size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int K, int V, kda_dtype dt,
-                                    const kda_plan* plan);
+size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int K, int V, kda_dtype dt);
 
 /*
  * Chunked prefill (the page's chunk-parallel form, section "Как
  * распараллелили последовательное обновление"), optionally resuming from an
- * initial state and returning the final state (the prefix-cache mechanism).
+ * initial state and returning the final state (the prefix-cache mechanism),
+ * in the plan the library picks for the current device.
  *
  *   q, k, g : [B, T, H, K]  dtype dt   (g = log alpha before the clamp)
  *   v       : [B, T, H, V]  dtype dt
@@ -127,26 +128,48 @@ size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int K, int V, kda_dtype
  *   final_state   : [B, H, K, V] fp32, or NULL (not written).  It may alias
  *                   initial_state exactly (in-place resume); a partial
  *                   overlap is KDA_ERR_INVALID_ARG.
- *   plan    : NULL or a kda_plan (fields 0 = library's choice).
  *   workspace / workspace_bytes : device scratch of at least
- *             kda_chunk_fwd_workspace_size(...) bytes for the same plan
- *             (may be NULL when that size is 0).
+ *             kda_chunk_fwd_workspace_size(...) bytes (may be NULL when that
+ *             size is 0); its contents on entry do not matter.
  * T == 0 writes final_state = initial_state (or zeros) and nothing else.
  */
 kda_status kda_chunk_fwd(int B, int T, int H, int K, int V, kda_dtype dt,
                          const void* q, const void* k, const void* v,
-                         const void* g, const void* beta,
+                         const void* g,
+                         const void* beta,
                          const float* initial_state,
-                         void* o, float* final_state,
-                         const kda_plan* plan,
+                         void* o,
+                         float* final_state,
                          void* workspace, size_t workspace_bytes,
-                         void* stream);
+                         hipStream_t stream);
 
 /*
- * kda_chunk_fwd with the output gate of the KDA block fused into the store
- * of o (habr.com article on the Kimi K3 technical report, the section on
- * gating after attention: a gate decides what fraction of the attention
- * output enters the residual stream, and KDA blocks use it too; the form is
+ * kda_chunk_fwd in a caller-chosen execution plan, and its workspace size.
+ *   plan : NULL or a kda_plan; fields 0 are the library's choice.  A plan the
+ *          kernels cannot run is KDA_ERR_INVALID_ARG (a field out of range) or
+ *          KDA_ERR_UNSUPPORTED (a valid field these sizes have no kernel for).
+ * The workspace size in a plan: with split = 2 one record per (b, h, chunk)
+ * (for K = V = 128 bf16, 72.5 KiB); with n_seg > 1 the segment transitions
+ * and local states ((n_seg - 1) * B * H * K * (K + V) fp32) plus
+ * B * H * K * V fp32 (a redirected final state).  Every other argument, and
+ * the result up to fp32/bf16 rounding, as kda_chunk_fwd.
+ */
+size_t kda_chunk_fwd_planned_workspace_size(int B, int T, int H, int K, int V, kda_dtype dt,
+                                            const kda_plan* plan);
+kda_status kda_chunk_fwd_planned(int B, int T, int H, int K, int V, kda_dtype dt,
+                                 const void* q, const void* k, const void* v,
+                                 const void* g, const void* beta,
+                                 const float* initial_state,
+                                 void* o, float* final_state,
+                                 const kda_plan* plan,
+                                 void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
+
+/*
+ * kda_chunk_fwd_planned with the output gate of the KDA block fused into the
+ * store of o (aiblin.ru page, section "KV‑кэш все‑таки не исчез полностью":
+ * after the attention a gate decides what share of its result passes on into
+ * the model's main stream, and the KDA blocks use the same gate; its form is
  * not given there, the plainest reading is taken):
  *
  *   o[b,t,h,:] = RNE_dt( RNE_dt(S_t^T q_t) * sigmoid(gate[b,t,h,:]) )
@@ -155,7 +178,8 @@ kda_status kda_chunk_fwd(int B, int T, int H, int K, int V, kda_dtype dt,
  *          NULL is KDA_ERR_INVALID_ARG when there is work.
  * The same result as kda_chunk_fwd followed by an elementwise o * sigmoid(gate)
  * in fp32 rounded to dt, up to the 1-ulp exp2 and reciprocal of the sigmoid;
- * it saves that pass over o.  Every other argument as kda_chunk_fwd.
+ * it saves that pass over o.  Every other argument as kda_chunk_fwd_planned
+ * (workspace size: kda_chunk_fwd_planned_workspace_size).
  */
 kda_status kda_chunk_fwd_gated(int B, int T, int H, int K, int V, kda_dtype dt,
                                const void* q, const void* k, const void* v,
@@ -164,7 +188,7 @@ kda_status kda_chunk_fwd_gated(int B, int T, int H, int K, int V, kda_dtype dt,
                                void* o, float* final_state,
                                const kda_plan* plan,
                                void* workspace, size_t workspace_bytes,
-                               void* stream);
+                               hipStream_t stream);
 
 /*
  * Prefill of a packed batch of N variable-length sequences (the
@@ -200,7 +224,7 @@ kda_status kda_chunk_fwd_varlen(int N, const int* cu_seqlens, int T_total, int H
                                 const float* initial_state,
                                 void* o, float* final_state,
                                 void* workspace, size_t workspace_bytes,
-                                void* stream);
+                                hipStream_t stream);
 
 /*
  * kda_chunk_fwd_varlen with the output gate fused as in kda_chunk_fwd_gated;
@@ -210,7 +234,7 @@ kda_status kda_chunk_fwd_varlen_gated(int N, const int* cu_seqlens, int T_total,
                                       kda_dtype dt, const void* q, const void* k, const void* v,
                                       const void* g, const void* beta, const void* gate,
                                       const float* initial_state, void* o, float* final_state,
-                                      void* workspace, size_t workspace_bytes, void* stream);
+                                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * kda_chunk_fwd_varlen that also returns state snapshots at fixed block
@@ -238,7 +262,7 @@ kda_status kda_chunk_fwd_varlen_snapshots(int N, const int* cu_seqlens, int T_to
                                           const void* g, const void* beta, const float* initial_state,
                                           void* o, float* final_state, int snapshot_interval,
                                           float* snapshots, int max_snapshots,
-                                          void* workspace, size_t workspace_bytes, void* stream);
+                                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * One decode step for N independent sequences (page section "Как хранить
@@ -252,7 +276,7 @@ kda_status kda_chunk_fwd_varlen_snapshots(int N, const int* cu_seqlens, int T_to
 kda_status kda_recurrent_step(int N, int H, int K, int V, kda_dtype dt,
                               const void* q, const void* k, const void* v,
                               const void* g, const void* beta,
-                              float* state, void* o, void* stream);
+                              float* state, void* o, hipStream_t stream);
 
 /*
  * T consecutive tokens of each of N sequences in one call (multi-token
@@ -270,7 +294,7 @@ kda_status kda_recurrent_step(int N, int H, int K, int V, kda_dtype dt,
 kda_status kda_recurrent_steps(int N, int T, int H, int K, int V, kda_dtype dt,
                                const void* q, const void* k, const void* v,
                                const void* g, const void* beta,
-                               float* state, void* o, float* step_states, void* stream);
+                               float* state, void* o, float* step_states, hipStream_t stream);
 
 /*
  * Backward of kda_chunk_fwd: the gradients of a loss L with respect to q, k,
@@ -289,7 +313,10 @@ kda_status kda_recurrent_steps(int N, int T, int H, int K, int V, kda_dtype dt,
  *   dq, dk, dg    : [B, T, H, K] dtype dt (written)
  *   dv            : [B, T, H, V] dtype dt (written)
  *   dbeta         : [B, T, H] dtype dt (written)
- *   d_initial_state : [B, H, K, V] fp32 (written) or NULL
+ *   d_initial_state : [B, H, K, V] fp32 (written) or NULL.  It must not
+ *                     overlap d_final_state (not even exactly: the reverse
+ *                     pass reads dL/dS_T while it writes dL/dS_0), else
+ *                     KDA_ERR_INVALID_ARG.
  *   workspace     : at least kda_chunk_bwd_workspace_size(...) bytes (the
  *                   size does not depend on the device).  Chunk form: the
  *                   forward plan's segment arrays (with n_seg > 1, the
@@ -308,7 +335,7 @@ kda_status kda_chunk_bwd(int B, int T, int H, int K, int V, kda_dtype dt,
                          const void* q, const void* k, const void* v, const void* g, const void* beta,
                          const float* initial_state, const void* d_o, const float* d_final_state,
                          void* dq, void* dk, void* dv, void* dg, void* dbeta, float* d_initial_state,
-                         void* workspace, size_t workspace_bytes, void* stream);
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Optional per-launch timing, for benchmarks and tracing.  After
@@ -323,8 +350,10 @@ kda_status kda_chunk_bwd(int B, int T, int H, int K, int V, kda_dtype dt,
  * "bwd_states", "bwd_reverse_summary", "bwd_reverse_scan", "bwd_state_reverse",
  * "bwd_value_side", "bwd_solve", "bwd_gated") and durations in milliseconds, releases the
  * events, and returns the number of timed launches (-1: profiling was not
- * started or a HIP event query failed).  The recording state is process-wide
- * and not thread-safe; profiling is off unless started.
+ * started or a HIP event query failed).  The record is process-wide (the one
+ * piece of state the library keeps, opt-in): launches from several threads
+ * while it is on are each recorded whole (a mutex guards it), in the order
+ * they took their slots.  Profiling is off unless started.
  * kda_profile_start returns KDA_ERR_INVALID_ARG for max_launches outside
  * [1, 2^20] and KDA_ERR_HIP if an event cannot be created.
  */

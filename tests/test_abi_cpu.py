@@ -55,9 +55,57 @@ def test_version_and_status_strings():
 
 def _fwd(lib, B=1, T=64, H=1, K=128, V=128, dt=BF16, q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE,
          s0=None, o=FAKE, sT=None, plan=None, ws=None, ws_bytes=0):
+    """kda_chunk_fwd (library plan), or kda_chunk_fwd_planned with `plan`."""
     p = lambda x: None if x is None else ctypes.c_void_p(x)
-    return lib.kda_chunk_fwd(B, T, H, K, V, dt, p(q), p(k), p(v), p(g), p(beta), p(s0), p(o), p(sT),
-                             None if plan is None else ctypes.byref(plan), p(ws), ws_bytes, None)
+    if plan is None:
+        return lib.kda_chunk_fwd(B, T, H, K, V, dt, p(q), p(k), p(v), p(g), p(beta), p(s0), p(o), p(sT),
+                                 p(ws), ws_bytes, None)
+    return lib.kda_chunk_fwd_planned(B, T, H, K, V, dt, p(q), p(k), p(v), p(g), p(beta), p(s0), p(o), p(sT),
+                                     ctypes.byref(plan), p(ws), ws_bytes, None)
+
+
+def _ws(lib, B, T, H, K, V, dt, plan=None):
+    if plan is None:
+        return lib.kda_chunk_fwd_workspace_size(B, T, H, K, V, dt)
+    return lib.kda_chunk_fwd_planned_workspace_size(B, T, H, K, V, dt, ctypes.byref(plan))
+
+
+# The prototypes of the hot-path boundary, as fixed for this library: the two
+# calls of the path (prefill with optional initial and final state, one decode
+# step), the workspace query, status strings and version.
+BOUNDARY_PROTOTYPES = {
+    "kda_chunk_fwd_workspace_size":
+        "size_t kda_chunk_fwd_workspace_size(int B, int T, int H, int K, int V, kda_dtype dt);",
+    "kda_chunk_fwd":
+        "kda_status kda_chunk_fwd(int B, int T, int H, int K, int V, kda_dtype dt, "
+        "const void* q, const void* k, const void* v, const void* g, const void* beta, "
+        "const float* initial_state, void* o, float* final_state, void* workspace, size_t workspace_bytes, "
+        "hipStream_t stream);",
+    "kda_recurrent_step":
+        "kda_status kda_recurrent_step(int N, int H, int K, int V, kda_dtype dt, "
+        "const void* q, const void* k, const void* v, const void* g, const void* beta, "
+        "float* state, void* o, hipStream_t stream);",
+    "kda_status_string": "const char* kda_status_string(kda_status s);",
+    "kda_version": "const char* kda_version(void);",
+}
+
+
+def _declaration(src, name):
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    m = re.search(r"^[^;{}#]*?\b%s\s*\([^;]*\);" % name, src, flags=re.M)
+    assert m, name
+    return " ".join(m.group(0).split()).replace("( ", "(").replace(" )", ")")
+
+
+def test_boundary_prototypes_verbatim():
+    src = open(HEADER).read()
+    for name, proto in BOUNDARY_PROTOTYPES.items():
+        assert _declaration(src, name) == proto, (name, _declaration(src, name))
+    # the status and dtype codes
+    body = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    for code, val in (("KDA_OK", 0), ("KDA_ERR_INVALID_ARG", 1), ("KDA_ERR_UNSUPPORTED", 2),
+                      ("KDA_ERR_WORKSPACE", 3), ("KDA_ERR_HIP", 4), ("KDA_F32", 0), ("KDA_BF16", 1)):
+        assert re.search(r"\b%s\s*=\s*%d\b" % (code, val), body), code
 
 
 def test_prefill_rejects_bad_sizes_before_any_launch():
@@ -81,13 +129,13 @@ def test_fp32_at_128_takes_the_token_serial_form():
         pl = K_.Plan()
         assert lib.kda_chunk_fwd_plan(2, 1000, 3, K, V, F32, ctypes.byref(pl)) == OK
         assert (pl.n_seg, pl.v_block, pl.split) == (1, 64, 3)
-        assert lib.kda_chunk_fwd_workspace_size(2, 1000, 3, K, V, F32, None) == 0
+        assert _ws(lib, 2, 1000, 3, K, V, F32) == 0
         assert lib.kda_chunk_fwd_varlen_workspace_size(4, 1000, 3, K, V, F32) == 0
     # the token-serial form has one segment and 64-column blocks only
     for bad in (K_.Plan(2, 64, 3), K_.Plan(1, 128, 3)):
         assert _fwd(lib, plan=bad) == UNSUPPORTED
-        assert lib.kda_chunk_fwd_workspace_size(1, 64, 1, 128, 128, BF16, ctypes.byref(bad)) == ctypes.c_size_t(-1).value
-    assert lib.kda_chunk_fwd_workspace_size(1, 64, 1, 128, 128, BF16, ctypes.byref(K_.Plan(1, 64, 3))) == 0
+        assert _ws(lib, 1, 64, 1, 128, 128, BF16, bad) == ctypes.c_size_t(-1).value
+    assert _ws(lib, 1, 64, 1, 128, 128, BF16, K_.Plan(1, 64, 3)) == 0
     # state snapshots come from the chunk state pass: not with the token-serial form
     assert _snap(lib, dt=F32) == UNSUPPORTED
     assert _snap(lib, dt=F32, K=64, V=64, ws=None) == WORKSPACE  # supported: fails only on the workspace
@@ -120,7 +168,7 @@ def test_prefill_workspace_check_with_explicit_plan():
     assert rec % 256 == 0
     for plan, need_expected in ((K_.Plan(4, 64, 1), seg), (K_.Plan(4, 64, 2), seg + H * 40 * rec),
                                 (K_.Plan(1, 64, 2), H * 40 * rec), (K_.Plan(1, 128, 1), 0)):
-        need = lib.kda_chunk_fwd_workspace_size(1, T, H, 128, 128, BF16, ctypes.byref(plan))
+        need = _ws(lib, 1, T, H, 128, 128, BF16, plan)
         assert need == need_expected, (plan.n_seg, plan.v_block, plan.split)
         if need:
             assert _fwd(lib, T=T, H=H, plan=plan, ws=None) == WORKSPACE
@@ -137,7 +185,7 @@ def test_prefill_rejects_bad_plans():
     assert _fwd(lib, plan=K_.Plan(1, 64, 4)) == INVALID
     assert _fwd(lib, plan=K_.Plan(1, 64, -1)) == INVALID
     bad = K_.Plan(1, 96)
-    assert lib.kda_chunk_fwd_workspace_size(1, 64, 1, 128, 128, BF16, ctypes.byref(bad)) == ctypes.c_size_t(-1).value
+    assert _ws(lib, 1, 64, 1, 128, 128, BF16, bad) == ctypes.c_size_t(-1).value
 
 
 def test_prefill_empty_batch_is_a_no_op():
@@ -285,13 +333,14 @@ def test_gated_entry_points_validate_the_gate():
     assert lib.kda_chunk_fwd_varlen_gated(*vargs(None, N=0)) == OK   # nothing to do
 
 
-def _bwd(lib, B=1, T=100, H=2, K=128, V=128, dt=BF16, ws=FAKE, ws_bytes=1 << 40, ds0=None, **kw):
+def _bwd(lib, B=1, T=100, H=2, K=128, V=128, dt=BF16, ws=FAKE, ws_bytes=1 << 40, ds0=None, dsT=None, **kw):
     p = ctypes.c_void_p
     lib.kda_chunk_bwd.argtypes = [ctypes.c_int] * 6 + [p] * 14 + [p, ctypes.c_size_t, p]
     lib.kda_chunk_bwd.restype = ctypes.c_int
     t = {n: kw.get(n, FAKE) for n in ("q", "k", "v", "g", "beta", "do", "dq", "dk", "dv", "dg", "dbeta")}
     pt = lambda n: p(t[n]) if t[n] else None
-    return lib.kda_chunk_bwd(B, T, H, K, V, dt, pt("q"), pt("k"), pt("v"), pt("g"), pt("beta"), None, pt("do"), None,
+    return lib.kda_chunk_bwd(B, T, H, K, V, dt, pt("q"), pt("k"), pt("v"), pt("g"), pt("beta"), None, pt("do"),
+                             p(dsT) if dsT else None,
                              pt("dq"), pt("dk"), pt("dv"), pt("dg"), pt("dbeta"), p(ds0) if ds0 else None,
                              p(ws) if ws else None, ws_bytes, None)
 
@@ -307,6 +356,13 @@ def test_backward_validation_before_any_launch():
     assert _bwd(lib, ds0=FAKE + 8) == INVALID                   # 16-byte alignment
     assert _bwd(lib, ws=None) == WORKSPACE
     assert _bwd(lib, B=0) == OK
+    # dL/dS_0 may not share a byte with dL/dS_T (read and written by the same
+    # reverse pass): exact alias and partial overlap are both rejected
+    nstate = 2 * 128 * 128 * 4
+    assert _bwd(lib, ds0=FAKE, dsT=FAKE) == INVALID
+    assert _bwd(lib, ds0=FAKE + nstate - 16, dsT=FAKE) == INVALID
+    assert _bwd(lib, ds0=FAKE, dsT=FAKE + nstate - 16) == INVALID
+    assert _bwd(lib, ds0=FAKE, dsT=FAKE + nstate, ws=None) == WORKSPACE   # disjoint: passes the check
     lib.kda_chunk_bwd_workspace_size.restype = ctypes.c_size_t
     ck = -(-(2 * 13 * 128 * 128 * 4) // 256) * 256              # the state every 8 tokens
     tok = ck + 8 * (100 * 2) * (3 * 128 + 1) * 4                # partial sums per 16-column block
