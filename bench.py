@@ -1,27 +1,39 @@
 #!/usr/bin/env python3
 """KDA prefill + decode throughput on one MI355X.
 
-A step is one ``kda_chunk_fwd`` over the 8K-token workload (B=1, H=32,
-T=8192, K=V=128, bf16 inputs, fp32 state, zero initial state, final state
-returned), with all inputs resident in HBM.  ``value`` is prefill tokens/s
-(B*T / step time).  Before its W warm-up steps the step runs untimed for
---settle-ms (50 ms): an idle GPU needs about 30 ms of work to reach its
-steady clocks, and the first calls run up to 10 % slower.  The same line carries the decode workload (256
-sequences x 32 heads, 512 MiB fp32 state, 64 successive one-token steps), the
-roofline of the dominant launch, and the fp64 CPU oracle timed on a bounded
-sample of the prefill workload.
+The headline step is one ``kda_chunk_fwd`` over the 1M-token workload: one
+sequence of T = 1,048,576 tokens on H = 16 heads (one GPU's head share),
+K = V = 128, bf16 inputs, fp32 state, zero initial state, final state
+returned, all inputs resident in HBM, in the plan the library picks.
+``value`` is prefill tokens/s (B*T / step time).  The same JSON line carries,
+each measured the same way in its own timed region:
 
-The roofline object describes the dominant kernel of the prefill step: its
-algorithmic bytes per launch (1,282 B per head-token it processes plus the
-states it must read or write) over its average duration, measured with HIP
-events that the library records on the launch stream (kda_profile_start).
-``traffic`` is the HBM traffic per launch from rocprofv3 FETCH_SIZE and
-WRITE_SIZE counters, scaled by a plain-copy calibration; it is read from
-profiles/prefill_8k_traffic.json and reported only while the kernel
-source still has the hash recorded there.
+* ``prefill_32k_x8``: 8 sequences of 32,768 tokens on 32 heads from a random
+  fp32 initial state, 20 % of the (head, channel) gates pinned at the clamp
+  floor, final state returned;
+* ``prefill_8k``: one 8,192-token sequence on 32 heads (with its fused output
+  gate and its backward beside it);
+* ``decode``: 256 sequences x 32 heads, 512 MiB fp32 state, 64 successive
+  one-token steps (and a 4-token verify).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-ms MS] [--extra]
-       [--no-cpu-baseline] [--no-decode] [--no-backward] [--cpu-seconds S]
+For every prefill workload: ``roofline`` is the dominant kernel of the call
+(its algorithmic bytes per launch over its average launch duration, measured
+with HIP events that the library records on the launch stream,
+kda_profile_start); ``roofline_call`` is the whole call against its
+algorithmic bytes (1,282 B per head-token plus the states), the binding
+roofline of the path; ``mfma`` is its algorithmic flops against the bf16 MFMA
+peak; ``traffic`` is the counter-measured HBM bytes per launch of the dominant
+kernel (rocprofv3 FETCH_SIZE / WRITE_SIZE scaled by a plain-copy calibration,
+read from profiles/<workload>_traffic.json while the kernel sources still have
+the hash recorded there); ``cpu_baseline`` is the fp64 oracle on the host
+cores on a bounded sample of the same workload.
+
+Before each workload's warm-up steps its step runs untimed for --settle-ms
+(an idle GPU needs about 30 ms of work to reach its steady clocks).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle-ms MS]
+       [--workloads prefill_1m,prefill_32k_x8,prefill_8k] [--extra]
+       [--no-cpu-baseline] [--no-decode] [--no-backward] [--no-gate] [--cpu-seconds S]
 """
 from __future__ import annotations
 
@@ -32,12 +44,19 @@ import sys
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_8k_traffic.json")
+PROFILES = os.path.join(ROOT, "profiles")
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
+MALL_BYTES = 256 << 20         # last-level (Infinity) cache
 
 METRIC = "KDA prefill tokens/s (MFMA % peak) + decode tokens/s (HBM GB/s %)"
+PREFILL_WORKLOADS = ("prefill_1m", "prefill_32k_x8", "prefill_8k")
+
+# launches that write o (and read S0 / write S_T): the path's algorithmic
+# bytes are attributed to them; the two-pass plan's intra-chunk pass gets the
+# input reads; summaries, scans and copies are plan overhead (zero)
+OUTPUT_LAUNCHES = ("chunk_output", "state_output", "fused_output", "token_fwd")
 
 
 def prefill_bytes(B, T, H, K, V, in_bytes=2, s0=False, final=True):
@@ -58,14 +77,28 @@ def decode_bytes(N, H, K, V, in_bytes=2):
     return N * H * (8 * K * V + in_bytes * (3 * K + V + 1) + in_bytes * V)
 
 
-def recorded_traffic(kernel, plan):
-    """Counter-derived HBM bytes per launch of `kernel`, if the committed
-    measurement was taken on the current kernel sources and plan."""
+def kernel_bytes(name, B, T, H, K, V, in_bytes, s0, final, two_pass):
+    """Algorithmic bytes of one launch named `name` (see OUTPUT_LAUNCHES)."""
+    ht = B * T * H
+    states = B * H * K * V * 4 * (int(s0) + int(final))
+    reads = ht * in_bytes * (3 * K + V + 1)
+    writes = ht * in_bytes * V
+    if name == "intra_chunk":
+        return reads
+    if name in OUTPUT_LAUNCHES:
+        return writes + states + (0 if two_pass else reads)
+    return 0
+
+
+def recorded_traffic(workload, kernel, plan):
+    """Counter-derived HBM bytes per launch of `kernel` in `workload`, if the
+    committed record was taken on the current kernel sources and plan."""
+    path = os.path.join(PROFILES, "%s_traffic.json" % workload)
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
-        return None, "no counter record"
+        return None, "no counter record for this workload"
     from gated_delta_rule_66_amd.traffic import kernel_source_hash
     if rec.get("source_sha256") != kernel_source_hash():
         return None, "kernel changed since the counters were taken"
@@ -77,21 +110,42 @@ def recorded_traffic(kernel, plan):
     return k["hbm_bytes_per_launch"], rec.get("note", "")
 
 
+def host_cpu():
+    """Model name and core counts of the host (the oracle's machine)."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = None
+    return {"model": model, "cpu_count": os.cpu_count(), "affinity_cpus": affinity}
+
+
 def main():
-    ap = argparse.ArgumentParser(description=__doc__)
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-passes", type=int, default=3)
     ap.add_argument("--settle-ms", type=float, default=50.0,
-                    help="untimed run of the prefill step before its warm-up steps, so that the GPU "
-                         "has left its idle clock state (the first ~30 ms of work run up to 10%% slower)")
-    ap.add_argument("--extra", action="store_true", help="also time the 32K x 256-chain and 1M-token workloads")
+                    help="untimed run of each step before its warm-up steps, so that the GPU has left its "
+                         "idle clock state (the first ~30 ms of work run up to 10%% slower)")
+    ap.add_argument("--workloads", default=",".join(PREFILL_WORKLOADS),
+                    help="prefill workloads to time, the first being the headline")
+    ap.add_argument("--extra", action="store_true", help="also time a packed variable-length batch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0,
-                    help="target duration of the oracle sample (heads of the 8K workload)")
+    ap.add_argument("--no-gate", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=8.0,
+                    help="target duration of each workload's oracle sample")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run only a plain device copy of this size (counter calibration) and exit")
     args = ap.parse_args()
@@ -100,6 +154,11 @@ def main():
               "(heads and batch rows would shard across GPUs without communication)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
+    workloads = [w for w in args.workloads.split(",") if w]
+    for w in workloads:
+        if w not in PREFILL_WORKLOADS:
+            print("bench.py: unknown workload %s" % w, file=sys.stderr)
+            sys.exit(2)
 
     import torch
     import gated_delta_rule_66_amd as kda
@@ -161,97 +220,174 @@ def main():
             per.setdefault(name, []).append(ms)
         return {n: {"avg_ms": sum(v) / len(v), "launches_per_call": len(v) / steps} for n, v in per.items()}
 
-    # ------------------------------------------------------------ prefill, 8K workload
-    cfg = CONFIGS["prefill_8k"]
-    x = make_prefill_config(cfg, dev)
-    B, T, H, K, V = cfg.B, cfg.T, cfg.H, cfg.K, cfg.V
-    plan = kda.chunk_plan(B, T, H, K, V, cfg.dtype)
-    o = torch.empty((B, T, H, V), dtype=cfg.dtype, device=dev)
-    sT = torch.empty((B, H, K, V), dtype=torch.float32, device=dev)
-    ws_n = kda.chunk_workspace_size(B, T, H, K, V, cfg.dtype)
-    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
+    def describe(c):
+        return "KDA prefill B=%d T=%d H=%d K=V=%d bf16 in, fp32 state, %s, final state out%s" % (
+            c.B, c.T, c.H, c.K, "S0~N(0,0.02)" if c.s0_std is not None else "S0=0",
+            ", %d%% of (head, channel) gates pinned at the floor" % round(100 * c.pinned_frac)
+            if c.pinned_frac else "")
 
-    def prefill_step():
-        kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], True, None,
-                      out=o, final_state=sT, workspace=ws)
+    # ------------------------------------------------------------ prefill workloads
+    def bench_prefill(name):
+        c = CONFIGS[name]
+        x = make_prefill_config(c, dev)
+        B, T, H, K, V = c.B, c.T, c.H, c.K, c.V
+        plan = kda.chunk_plan(B, T, H, K, V, c.dtype)
+        o = torch.empty((B, T, H, V), dtype=c.dtype, device=dev)
+        sT = torch.empty((B, H, K, V), dtype=torch.float32, device=dev)
+        ws_n = kda.chunk_workspace_size(B, T, H, K, V, c.dtype)
+        ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev)
 
-    settle(prefill_step, args.settle_ms)
-    ms = time_calls(prefill_step, args.warmup, args.steps)
-    kernels = time_launches(prefill_step, args.steps)
-    tok_s = B * T / (ms * 1e-3)
-    nbytes = prefill_bytes(B, T, H, K, V, 2, s0=False, final=True)
-    nflops = prefill_flops(B, T, H, K, V)
-    gbs = nbytes / (ms * 1e-3) / 1e9
-    tflops = nflops / (ms * 1e-3) / 1e12
+        def step():
+            kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], True, None,
+                          out=o, final_state=sT, workspace=ws)
 
-    # algorithmic bytes per launch of each kernel: the path's 1,282 B per
-    # head-token (q, k, g, v, beta in; o out) plus the states, attributed to
-    # the kernel that moves them; workspace traffic (segment summaries, the
-    # per-chunk records of the two-pass plan) is overhead and counts zero
-    in_bytes = B * T * H * 2 * (3 * K + V + 1)
-    out_bytes = B * T * H * 2 * V + B * H * K * V * 4
-    per_kernel_bytes = {
-        "chunk_output": nbytes, "chunk_summary": 0, "segment_scan": 0, "copy_state": 0,
-        "intra_chunk": in_bytes, "state_output": out_bytes, "state_summary": 0,
-    }
-    dom = max(kernels, key=lambda n: kernels[n]["avg_ms"] * kernels[n]["launches_per_call"])
-    dom_ms = kernels[dom]["avg_ms"]
-    dom_bytes = per_kernel_bytes.get(dom, 0)
-    dom_gbs = dom_bytes / (dom_ms * 1e-3) / 1e9
-    traffic, traffic_note = recorded_traffic(dom, plan)
+        settle(step, args.settle_ms)
+        ms = time_calls(step, args.warmup, args.steps)
+        kernels = time_launches(step, args.steps)
+        has_s0 = c.s0_std is not None
+        nbytes = prefill_bytes(B, T, H, K, V, 2, s0=has_s0, final=True)
+        nflops = prefill_flops(B, T, H, K, V)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        tflops = nflops / (ms * 1e-3) / 1e12
+        dom = max(kernels, key=lambda n: kernels[n]["avg_ms"] * kernels[n]["launches_per_call"])
+        dom_ms = kernels[dom]["avg_ms"]
+        dom_bytes = kernel_bytes(dom, B, T, H, K, V, 2, has_s0, True, plan[2] == 2)
+        dom_gbs = dom_bytes / (dom_ms * 1e-3) / 1e9
+        traffic, traffic_note = recorded_traffic(name, dom, plan)
+        working_set = nbytes + ws_n
+        res = {
+            "workload": describe(c),
+            "global_batch": B, "seq_len": T, "heads": H,
+            "plan": {"n_seg": plan[0], "v_block": plan[1], "split": plan[2]},
+            "ms": ms,
+            "tokens_per_s": B * T / (ms * 1e-3),
+            "head_tokens_per_s": B * T * H / (ms * 1e-3),
+            "roofline": {"bound": "hbm", "achieved": dom_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": dom_gbs / HBM_PEAK_GBS, "traffic": traffic,
+                         "kernel": dom, "kernel_avg_ms": dom_ms,
+                         "algorithmic_bytes_per_launch": dom_bytes, "traffic_note": traffic_note},
+            "roofline_call": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                              "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_call": nbytes},
+            "mfma": {"achieved_tflops": tflops, "peak_tflops": BF16_PEAK_TFLOPS,
+                     "frac": tflops / BF16_PEAK_TFLOPS, "algorithmic_flops_per_call": nflops},
+            "kernels": kernels,
+            "workspace_bytes": ws_n,
+            "cache_note": ("inputs, outputs and workspace (%.0f MB) partly fit the 256 MB last-level cache; "
+                           "it is not flushed between repetitions" % (working_set / 1e6))
+            if working_set < 2 * MALL_BYTES else
+            "working set %.1f GB, far above the 256 MB last-level cache" % (working_set / 1e9),
+        }
+        extras = {}
+        if name == "prefill_8k" and not args.no_gate:
+            # the same call with the output gate fused into the store of o, beside
+            # the ungated call followed by a separate elementwise o * sigmoid(gate)
+            gen = torch.Generator(device=dev)
+            gen.manual_seed(11)
+            z = torch.randn((B, T, H, V), generator=gen, device=dev).to(c.dtype)
 
-    # the same call with the output gate fused into the store of o, beside the
-    # ungated call followed by a separate elementwise o * sigmoid(gate)
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(11)
-    z = torch.randn((B, T, H, V), generator=gen, device=dev).to(cfg.dtype)
+            def gated_step():
+                kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], True, tuple(plan),
+                              out=o, final_state=sT, workspace=ws, gate=z)
 
-    def gated_step():
-        kda.chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], True, None,
-                      out=o, final_state=sT, workspace=ws, gate=z)
+            def unfused_step():
+                step()
+                o.mul_(torch.sigmoid(z))
 
-    def unfused_step():
-        prefill_step()
-        o.mul_(torch.sigmoid(z))
-
-    # the three variants back to back, after a settle run, in the same conditions
-    settle(gated_step, args.settle_ms)
-    ms_gated = time_calls(gated_step, 2, args.steps)
-    ms_plain = time_calls(prefill_step, 2, args.steps)
-    ms_unfused = time_calls(unfused_step, 2, args.steps)
-    gate = {"ms": ms_gated, "tokens_per_s": B * T / (ms_gated * 1e-3), "ms_ungated": ms_plain,
-            "ms_unfused": ms_unfused}
-    del x, o, sT, ws, z
-    torch.cuda.empty_cache()
-
-    # ------------------------------------------------------------ backward, 8K workload
-    bwd = None
-    if not args.no_backward:
-        x = make_prefill_config(cfg, dev)
-        gen = torch.Generator(device=dev)
-        gen.manual_seed(12)
-        d_o = torch.randn((B, T, H, V), generator=gen, device=dev).to(cfg.dtype)
-        ws_b = torch.empty(max(kda.chunk_bwd_workspace_size(B, T, H, K, V, cfg.dtype), 1), dtype=torch.uint8,
-                           device=dev)
-
-        def bwd_step():
-            kda.chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], d_o, None, workspace=ws_b)
-
-        settle(bwd_step, args.settle_ms)
-        ms_b = time_calls(bwd_step, 1, 3)
-        # algorithmic bytes: the forward's inputs and dL/do read, the five gradients written
-        b_bytes = B * T * H * 2 * (2 * (3 * K + V + 1) + V)
-        bwd = {"workload": "gradients of the 8K prefill (dq, dk, dv, dg, dbeta; zero S0, no dL/dS_T)",
-               "ms": ms_b, "tokens_per_s": B * T / (ms_b * 1e-3),
-               "achieved_gbs": b_bytes / (ms_b * 1e-3) / 1e9,
-               "hbm_frac": b_bytes / (ms_b * 1e-3) / 1e9 / HBM_PEAK_GBS,
-               "workspace_bytes": ws_b.numel()}
-        del x, d_o, ws_b
+            settle(gated_step, args.settle_ms)
+            ms_gated = time_calls(gated_step, 2, args.steps)
+            ms_plain = time_calls(step, 2, args.steps)
+            ms_unfused = time_calls(unfused_step, 2, args.steps)
+            extras["gate"] = {"ms": ms_gated, "tokens_per_s": B * T / (ms_gated * 1e-3), "ms_ungated": ms_plain,
+                              "ms_unfused": ms_unfused}
+            del z
+        del x, o, sT, ws
         torch.cuda.empty_cache()
+        if name == "prefill_8k" and not args.no_backward:
+            xb = make_prefill_config(c, dev)
+            gen = torch.Generator(device=dev)
+            gen.manual_seed(12)
+            d_o = torch.randn((B, T, H, V), generator=gen, device=dev).to(c.dtype)
+            ws_b = torch.empty(max(kda.chunk_bwd_workspace_size(B, T, H, K, V, c.dtype), 1), dtype=torch.uint8,
+                               device=dev)
+
+            def bwd_step():
+                kda.chunk_bwd(xb["q"], xb["k"], xb["v"], xb["g"], xb["beta"], xb["s0"], d_o, None, workspace=ws_b)
+
+            settle(bwd_step, args.settle_ms)
+            ms_b = time_calls(bwd_step, 1, 3)
+            # algorithmic bytes: the forward's inputs and dL/do read, the five gradients written
+            b_bytes = B * T * H * 2 * (2 * (3 * K + V + 1) + V)
+            extras["backward"] = {
+                "workload": "gradients of the 8K prefill (dq, dk, dv, dg, dbeta; zero S0, no dL/dS_T)",
+                "ms": ms_b, "tokens_per_s": B * T / (ms_b * 1e-3),
+                "achieved_gbs": b_bytes / (ms_b * 1e-3) / 1e9,
+                "hbm_frac": b_bytes / (ms_b * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                "kernels": time_launches(bwd_step, 2),
+                "workspace_bytes": ws_b.numel()}
+            del xb, d_o, ws_b
+            torch.cuda.empty_cache()
+        res.update(extras)
+        return res
+
+    # ------------------------------------------------------------ CPU oracle baseline
+    def cpu_baseline(name):
+        """The fp64 oracle on the host cores, on a bounded sample of the
+        workload: the first Ts tokens of batch row 0, all H heads, drawn by the
+        same recipe (its cost is linear in tokens x heads and independent of
+        the values), repeated to about --cpu-seconds; tokens/s of the whole
+        workload = Ts * reps / wall time."""
+        import oracle
+        c = CONFIGS[name]
+        nthreads = oracle.oracle_max_threads()
+
+        def sample(ts):
+            xs = make_prefill_config(c, dev, T=ts, B=1)
+            inp = [xs[n].cpu() for n in ("q", "k", "v", "g", "beta")]
+            return inp, (xs["s0"].cpu() if xs["s0"] is not None else None)
+
+        def run(inp, s0, reps):
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                oracle.oracle_fwd(*inp, s0, want_state=False, nthreads=nthreads)
+            return time.perf_counter() - t0
+
+        # at most about a million head-tokens per sample (host memory), at
+        # least enough for every thread to hold a (head, 16-column) chain
+        ts = min(c.T, max(64, (1 << 20) // c.H // 64 * 64))
+        inp, s0 = sample(min(ts, 1024))
+        t_small = run(inp, s0, 1) / min(ts, 1024)
+        reps = max(1, int(round(args.cpu_seconds / max(t_small * ts, 1e-9))))
+        inp, s0 = sample(ts)
+        dt = run(inp, s0, reps)
+        chains = c.H * (c.V // 16)
+        return {
+            "value": ts * reps / dt,
+            "unit": "tokens/s",
+            "cores": min(nthreads, chains),
+            "kind": "oracle",
+            "sample": "fp64 token-by-token oracle (C, OpenMP, %d threads over %d (head, 16-column) chains) on "
+                      "the first %d tokens of one sequence, all %d heads, drawn by the workload's recipe, run "
+                      "%d time(s): %.1f s wall; its cost is linear in tokens x heads, so tokens/s of the whole "
+                      "workload = %d x %d / wall" % (min(nthreads, chains), chains, ts, c.H, reps, dt, ts, reps),
+            "host": host_cpu(),
+        }
+
+    def progress(msg):
+        print("[bench] " + msg, file=sys.stderr, flush=True)
+
+    results = {}
+    for w in workloads:
+        progress("%s: timing" % w)
+        results[w] = bench_prefill(w)
+        progress("%s: %.4f ms per call, plan %s" % (w, results[w]["ms"], results[w]["plan"]))
+        if not args.no_cpu_baseline:
+            results[w]["cpu_baseline"] = cpu_baseline(w)
+            progress("%s: oracle %.0f tokens/s" % (w, results[w]["cpu_baseline"]["value"]))
 
     # ------------------------------------------------------------ decode workload
     dec = None
     if not args.no_decode:
+        progress("decode_256x32: timing")
         dcfg = CONFIGS["decode_256x32"]
         d = make_decode_config(dcfg, dev)
         pristine = d["state"]
@@ -274,9 +410,7 @@ def main():
                "hbm_frac": dec_gbs / HBM_PEAK_GBS, "bytes_per_step": dec_bytes,
                "kernel_avg_ms": dk["avg_ms"],
                "kernel_gbs": dec_bytes / (dk["avg_ms"] * 1e-3) / 1e9}
-        # HBM bytes per decode launch from the same counter record as the
-        # prefill's (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None
-        dec_traffic, dec_note = recorded_traffic("decode_step", plan)
+        dec_traffic, dec_note = recorded_traffic("decode_256x32", "decode_step", [0, 0, 0])
         dec["traffic"] = dec_traffic
         dec["traffic_gbs"] = None if dec_traffic is None else dec_traffic / (dk["avg_ms"] * 1e-3) / 1e9
         if dec_traffic is None:
@@ -301,30 +435,6 @@ def main():
 
     extra = {}
     if args.extra:
-        for name in ("prefill_32k_x8", "prefill_1m"):
-            c = CONFIGS[name]
-            xe = make_prefill_config(c, dev)
-            oe = torch.empty((c.B, c.T, c.H, c.V), dtype=c.dtype, device=dev)
-            se = torch.empty((c.B, c.H, c.K, c.V), dtype=torch.float32, device=dev)
-            n_ws = kda.chunk_workspace_size(c.B, c.T, c.H, c.K, c.V, c.dtype)
-            wse = torch.empty(max(n_ws, 1), dtype=torch.uint8, device=dev)
-            fn = lambda: kda.chunk_fwd(xe["q"], xe["k"], xe["v"], xe["g"], xe["beta"], xe["s0"], True,
-                                       None, out=oe, final_state=se, workspace=wse)
-            mse = time_calls(fn, 2, 5)
-            nb = prefill_bytes(c.B, c.T, c.H, c.K, c.V, 2, s0=c.s0_std is not None, final=True)
-            nf = prefill_flops(c.B, c.T, c.H, c.K, c.V)
-            extra[name] = {
-                "workload": "B=%d T=%d H=%d K=V=%d bf16%s" % (c.B, c.T, c.H, c.K,
-                                                             ", S0~N(0,0.02), 20%% channels at g=-5"
-                                                             if c.pinned_frac else ""),
-                "plan": list(kda.chunk_plan(c.B, c.T, c.H, c.K, c.V, c.dtype)),
-                "ms": round(mse, 4),
-                "tokens_per_s": c.B * c.T / (mse * 1e-3),
-                "hbm_frac": nb / (mse * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                "mfma_frac": nf / (mse * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-            }
-            del xe, oe, se, wse
-            torch.cuda.empty_cache()
         # packed variable-length batch: 256 sequences of lengths drawn
         # uniformly from [1, 2048], 32 heads, K = V = 128, per-sequence states
         gen = torch.Generator().manual_seed(7)
@@ -355,78 +465,32 @@ def main():
         del xv, s0v, ov, sv, wsv
         torch.cuda.empty_cache()
 
-    # ------------------------------------------------------------ CPU oracle baseline
-    cpu = None
-    if not args.no_cpu_baseline:
-        import oracle
-        nthreads = oracle.oracle_max_threads()
-
-        def oracle_inputs(nh):
-            xs = make_prefill_config(cfg, dev, H=nh)   # same recipe, first nh heads' draws
-            return [xs[n].cpu() for n in ("q", "k", "v", "g", "beta")]
-
-        def run_oracle(inp, reps):
-            t0 = time.perf_counter()
-            for _ in range(reps):
-                oracle.oracle_fwd(*inp, None, nthreads=nthreads)
-            return time.perf_counter() - t0
-
-        # the oracle parallelises over (b, h, 16-column block) chains: size the
-        # sample (heads, then repetitions of the whole workload) so that every
-        # thread has chains and the run lasts about cpu_seconds
-        chains1 = V // 16
-        t1 = run_oracle(oracle_inputs(1), 1)
-        per_chain = t1 / -(-chains1 // nthreads)
-        rounds = max(1, int(args.cpu_seconds / max(per_chain, 1e-9)))
-        nh = max(1, min(H, rounds * nthreads // chains1))
-        inp = oracle_inputs(nh)
-        t_one = run_oracle(inp, 1)
-        reps = max(1, int(round(args.cpu_seconds / max(t_one, 1e-9)))) if nh == H else 1
-        dt = run_oracle(inp, reps) if reps > 1 else t_one
-        chains = nh * chains1
-        cpu = {
-            "value": B * T * nh * reps / dt / H,       # tokens/s of all H heads
-            "unit": "tokens/s",
-            "cores": min(nthreads, chains),
-            "kind": "oracle",
-            "sample": "fp64 token-by-token oracle (C, OpenMP, %d threads) on %d of %d heads of the 8K "
-                      "workload (B=1, T=%d, K=V=128), run %d time(s): %.1f s wall; tokens/s scaled to "
-                      "all %d heads" % (min(nthreads, chains), nh, H, T, reps, dt, H),
-        }
-
+    head = results[workloads[0]]
     line = {
         "metric": METRIC,
-        "value": tok_s,
+        "value": head["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms,
+        "ms_per_step": head["ms"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "KDA prefill B=1 T=8192 H=32 K=V=128 bf16 in, fp32 state, S0=0, final state out",
-                   "global_batch": B, "seq_len": T, "heads": H,
-                   "plan": {"n_seg": plan[0], "v_block": plan[1], "split": plan[2]},
-                   "parallelism": "single GPU"},
-        "roofline": {"bound": "hbm", "achieved": dom_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": dom_gbs / HBM_PEAK_GBS,
-                     "traffic": traffic,
-                     "kernel": dom, "kernel_avg_ms": dom_ms,
-                     "algorithmic_bytes_per_launch": dom_bytes,
-                     "traffic_note": traffic_note},
-        "roofline_call": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                          "frac": gbs / HBM_PEAK_GBS, "algorithmic_bytes_per_call": nbytes},
-        "mfma": {"achieved_tflops": tflops, "peak_tflops": BF16_PEAK_TFLOPS, "frac": tflops / BF16_PEAK_TFLOPS,
-                 "algorithmic_flops_per_call": nflops},
-        "kernels": kernels,
-        "gate": gate,
-        "backward": bwd,
-        "decode": dec,
-        "cpu_baseline": cpu,
+        "config": {"workload": "%s: %s" % (workloads[0], head["workload"]),
+                   "global_batch": head["global_batch"], "seq_len": head["seq_len"], "heads": head["heads"],
+                   "plan": head["plan"], "parallelism": "single GPU"},
+        "roofline": head["roofline"],
+        "roofline_call": head["roofline_call"],
+        "mfma": head["mfma"],
+        "kernels": head["kernels"],
+        "cpu_baseline": head.get("cpu_baseline"),
     }
+    for w in workloads[1:]:
+        line[w] = results[w]
+    line["decode"] = dec
     if extra:
         line["extra"] = extra
     print(json.dumps(line))

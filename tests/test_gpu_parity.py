@@ -284,6 +284,56 @@ def test_deterministic_repeat():
         assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
+@pytest.mark.parametrize("dtype,K,V", [(torch.bfloat16, 64, 64), (torch.float32, 64, 64),
+                                       (torch.bfloat16, 64, 128)])
+def test_deterministic_repeat_k64(dtype, K, V):
+    """Bitwise repeatability of the K = 64 variants on both plans, segmented
+    and not: their diagonal-block inverses hand fp32 blocks between lanes of
+    one wave through LDS, which needs the wave-level fence."""
+    say("bitwise repeatability %s K=%d V=%d" % (dtype, K, V))
+    d = make_prefill(2, 64 * 20 + 9, 3, K, V, dtype, seed=29, s0_std=0.02)
+    x = to_dev(d)
+    for split in PATHS:
+        for n_seg in (1, 4):
+            plan = (n_seg, 64, split)
+            ref = gpu_fwd(x, plan)
+            for _ in range(3):
+                again = gpu_fwd(x, plan)
+                torch.cuda.synchronize()
+                assert torch.equal(ref[0], again[0]) and torch.equal(ref[1], again[1]), plan
+
+
+@pytest.mark.parametrize("split", PATHS)
+@pytest.mark.parametrize("n_seg", [1, 3])
+def test_p4_pure_decay_closed_form(split, n_seg):
+    """P4 on the device: with beta = 0 the state only decays, so
+    S_T = Diag(exp(sum_t clamp g_t)) S0 and o_t = (Diag(exp G_t) S0)^T q_t
+    with G_t the running sum of the clamped gates, across chunk and segment
+    boundaries (gates drawn past both clamp bounds)."""
+    say("P4 beta=0 pure decay, T=300, split=%d n_seg=%d" % (split, n_seg))
+    B, T, H, K, V = 1, 300, 2, 128, 128
+    d = make_prefill(B, T, H, K, V, torch.bfloat16, seed=31, s0_std=0.02)
+    gen = torch.Generator().manual_seed(32)
+    # gates uniform in [-0.05, 0.05] (a slow mean decay, so that the state
+    # stays alive over 300 tokens), channels 0-7 below the floor (-6 -> -5)
+    # and channels 8-15 above the ceiling (0.5 -> 0)
+    d["g"] = (torch.rand((B, T, H, K), generator=gen) * 0.1 - 0.05).to(torch.bfloat16)
+    d["g"][..., 0:8] = -6.0
+    d["g"][..., 8:16] = 0.5
+    d["beta"] = torch.zeros_like(d["beta"])
+    x = to_dev(d)
+    o, sT = gpu_fwd(x, (n_seg, 128, split))
+    torch.cuda.synchronize()
+    gc = d["g"].double().clamp(-5.0, 0.0)                       # [B, T, H, K]
+    G = torch.cumsum(gc, dim=1)                                 # running sums
+    s0 = d["s0"].double()                                       # [B, H, K, V]
+    s_ref = torch.exp(G[:, -1]).unsqueeze(-1) * s0              # [B, H, K, V]
+    # o_t[v] = sum_c q_t[c] e^{G_t[c]} S0[c][v]
+    o_ref = torch.einsum("bthc,bhcv->bthv", d["q"].double() * torch.exp(G), s0)
+    assert o_err(o, o_ref.numpy()) < TOL[torch.bfloat16]
+    assert s_err(sT, s_ref.numpy()) < TOL[torch.bfloat16]
+
+
 def test_launch_profiling_names_every_launch():
     say("per-launch event timing: plain and segmented plans")
     import gated_delta_rule_66_amd as kda
@@ -552,20 +602,28 @@ def max_rel(o, o_ref):
 
 # ------------------------------------------------------------------ full-size workloads
 def _sampled_oracle(x, chains):
-    """Oracle on selected (b, h) chains of device inputs; returns lists."""
-    outs = []
+    """Oracle on selected (b, h) chains of device inputs; returns a list of
+    (o_ref [1, T, 1, V], s_ref [1, 1, K, V]) in the order of `chains`.  The
+    chains of one batch row go to the oracle in one call (its threads run
+    over every (head, 16-column) chain of the call)."""
+    by_row = {}
     for b, h in chains:
-        sl = lambda t: t[b:b + 1, :, h:h + 1].contiguous().cpu()
-        s0 = None if x["s0"] is None else x["s0"][b:b + 1, h:h + 1].cpu()
+        by_row.setdefault(b, []).append(h)
+    refs = {}
+    for b, hs in by_row.items():
+        idx = torch.tensor(hs, device=x["q"].device)
+        sl = lambda t: t[b:b + 1].index_select(2, idx).contiguous().cpu()
+        s0 = None if x["s0"] is None else x["s0"][b:b + 1].index_select(1, idx).cpu()
         o_ref, s_ref = oracle.oracle_fwd(sl(x["q"]), sl(x["k"]), sl(x["v"]), sl(x["g"]), sl(x["beta"]), s0)
-        outs.append((o_ref, s_ref))
-    return outs
+        for i, h in enumerate(hs):
+            refs[(b, h)] = (o_ref[:, :, i:i + 1], s_ref[:, i:i + 1])
+    return [refs[c] for c in chains]
 
 
 @pytest.mark.parametrize("name,chains,split", [("prefill_8k", [(0, 0), (0, 7), (0, 19), (0, 31)], 0),
                                                ("prefill_8k", [(0, 3), (0, 30)], 1),
-                                               ("prefill_32k_x8", [(0, 3), (5, 17), (7, 31)], 0),
-                                               ("prefill_1m", [(0, 11)], 0)])
+                                               ("prefill_32k_x8", [(0, 3), (5, 17), (7, 31), (2, 9)], 0),
+                                               ("prefill_1m", [(0, 0), (0, 5), (0, 11), (0, 15)], 0)])
 def test_full_size_prefill_sampled(name, chains, split):
     """Full-size workloads in the launch configuration bench.py times (the
     library's plan), checked against the oracle on sampled (b, h) chains."""
@@ -575,6 +633,10 @@ def test_full_size_prefill_sampled(name, chains, split):
         (name, cfg.B, cfg.T, cfg.H, chunk_plan(cfg.B, cfg.T, cfg.H, cfg.K, cfg.V, cfg.dtype) if not split
          else plan, chains))
     x = make_prefill_config(cfg, DEV)
+    if cfg.pinned_frac:
+        # the sampled heads carry gates pinned at the clamp floor
+        for _, h in chains:
+            assert bool(x["pinned"][h].any()), h
     o, sT = chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], True, plan)
     torch.cuda.synchronize()
     assert torch.isfinite(sT).all()
