@@ -10,6 +10,7 @@ from .kda import (  # noqa: F401
     chunk_bwd,
     chunk_bwd_workspace_size,
     chunk_fwd,
+    chunk_fwd_noalloc,
     chunk_fwd_varlen,
     chunk_fwd_varlen_workspace_size,
     snapshot_count,
@@ -25,5 +26,5 @@ from .kda import (  # noqa: F401
 )
 from .build import LIB_PATH, build_library  # noqa: F401
 
-__all__ = ["chunk_fwd", "chunk_bwd", "chunk_bwd_workspace_size", "chunk_fwd_varlen", "chunk_fwd_varlen_workspace_size", "snapshot_count", "recurrent_step", "recurrent_steps", "chunk_plan", "chunk_workspace_size", "profile_start", "profile_stop",
+__all__ = ["chunk_fwd", "chunk_fwd_noalloc", "chunk_bwd", "chunk_bwd_workspace_size", "chunk_fwd_varlen", "chunk_fwd_varlen_workspace_size", "snapshot_count", "recurrent_step", "recurrent_steps", "chunk_plan", "chunk_workspace_size", "profile_start", "profile_stop",
            "load_library", "build_library", "version", "status_string", "KDAError", "Plan"]

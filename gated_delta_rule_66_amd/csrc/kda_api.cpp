@@ -250,6 +250,8 @@ size_t kda_chunk_fwd_planned_workspace_size(int B, int T, int H, int K, int V, k
     return workspace_bytes_for(B, T, H, K, V, dt, pl);
 }
 
+// dry_run: every host check (sizes, pointers, plan, workspace size with the
+// workspace pointer itself not yet known), then KDA_OK before any HIP call
 static kda_status chunk_impl(int B, int T, int H, int K, int V, kda_dtype dt,
                              const void* q, const void* k, const void* v,
                              const void* g, const void* beta, const void* gate,
@@ -257,7 +259,7 @@ static kda_status chunk_impl(int B, int T, int H, int K, int V, kda_dtype dt,
                              void* o, float* final_state,
                              const kda_plan* plan,
                              void* workspace, size_t workspace_bytes,
-                             hipStream_t stream) {
+                             hipStream_t stream, bool dry_run = false) {
     kda_status s = check_prefill_sizes(B, T, H, K, V, dt);
     if (s != KDA_OK) return s;
     const long bh = (long)B * H;
@@ -278,6 +280,7 @@ static kda_status chunk_impl(int B, int T, int H, int K, int V, kda_dtype dt,
     hipStream_t st = stream;
 
     if (T == 0) {
+        if (dry_run) return KDA_OK;
         if (!final_state || final_state == initial_state) return KDA_OK;
         return launch_timed("copy_state", st, [&] {
                    return launch_copy_state(initial_state, final_state, (size_t)bh * K * V, st);
@@ -289,7 +292,8 @@ static kda_status chunk_impl(int B, int T, int H, int K, int V, kda_dtype dt,
     s = resolve_plan(B, T, H, K, V, dt, plan, &pl, &cps);
     if (s != KDA_OK) return s;
     const size_t need = workspace_bytes_for(B, T, H, K, V, dt, pl);
-    if (need > 0 && (!workspace || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
+    if (need > 0 && ((!workspace && !dry_run) || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
+    if (dry_run) return KDA_OK;
 
     if (pl.split == 3) {
         TokenFwdParams tp{};
@@ -997,3 +1001,40 @@ int kda_profile_stop(const char** names, float* ms, int cap) {
 }
 
 }  // extern "C"
+
+namespace kda {
+
+// kda_chunk_fwd_planned with the workspace bounded to ws_cap bytes (see
+// kda_internal.h).  launch false: checks and plan choice only.
+kda_status chunk_fwd_bounded(int B, int T, int H, int K, int V, kda_dtype dt, const void* q, const void* k,
+                             const void* v, const void* g, const void* beta, const float* initial_state,
+                             void* o, float* final_state, const kda_plan* plan, void* ws, size_t ws_cap,
+                             bool launch, hipStream_t stream) {
+    // the pointer and size checks of the planned call come first
+    kda_status s = chunk_impl(B, T, H, K, V, dt, q, k, v, g, beta, nullptr, initial_state, o, final_state, plan,
+                              nullptr, ~(size_t)0, stream, true);
+    if (s != KDA_OK) return s;
+    kda_plan pl{0, 0, 0};
+    if ((long)B * H > 0 && T > 0) {
+        s = resolve_plan(B, T, H, K, V, dt, plan, &pl, nullptr);
+        if (s != KDA_OK) return s;
+        if (workspace_bytes_for(B, T, H, K, V, dt, pl) > ws_cap) {
+            if (plan) return KDA_ERR_WORKSPACE;
+            // the library's plan keeps records: the single pass instead, with
+            // as many of its segments as the bound holds (one always fits)
+            kda_plan req{0, 0, 1};
+            s = resolve_plan(B, T, H, K, V, dt, &req, &pl, nullptr);
+            if (s != KDA_OK) return s;
+            while (pl.n_seg > 1 && workspace_bytes_for(B, T, H, K, V, dt, pl) > ws_cap) {
+                req = kda_plan{pl.n_seg - 1, pl.v_block, 1};
+                s = resolve_plan(B, T, H, K, V, dt, &req, &pl, nullptr);
+                if (s != KDA_OK) return s;
+            }
+            if (workspace_bytes_for(B, T, H, K, V, dt, pl) > ws_cap) return KDA_ERR_WORKSPACE;
+        }
+    }
+    return chunk_impl(B, T, H, K, V, dt, q, k, v, g, beta, nullptr, initial_state, o, final_state,
+                      pl.split ? &pl : nullptr, ws, ws_cap, stream, !launch);
+}
+
+}  // namespace kda

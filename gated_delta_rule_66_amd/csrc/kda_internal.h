@@ -237,3 +237,21 @@ size_t bwd_workspace_bytes(int B, int T, int H, int K, int V);
 hipError_t launch_decode_multi(int dtype, int K, int V, const MultiDecodeParams& p, hipStream_t stream);
 
 }  // namespace kda
+
+#include "kda.h"
+
+namespace kda {
+
+// The prefill of kda_chunk_fwd_planned with at most ws_cap bytes of workspace
+// at ws.  plan NULL: the library's plan when its workspace fits, else the
+// single-pass plan with as many of the library's segments as fit (one segment
+// needs no workspace); an explicit plan that does not fit is
+// KDA_ERR_WORKSPACE.  launch false runs every host check and the plan choice
+// (ws may then be null) and returns before any HIP call other than the
+// device query of a plan left to the library.  Defined in kda_api.cpp.
+kda_status chunk_fwd_bounded(int B, int T, int H, int K, int V, kda_dtype dt, const void* q, const void* k,
+                             const void* v, const void* g, const void* beta, const float* initial_state,
+                             void* o, float* final_state, const kda_plan* plan, void* ws, size_t ws_cap,
+                             bool launch, hipStream_t stream);
+
+}  // namespace kda

@@ -28,6 +28,7 @@ EXPORTED_SYMBOLS = (
     "kda_chunk_fwd",
     "kda_chunk_fwd_planned_workspace_size",
     "kda_chunk_fwd_planned",
+    "kda_chunk_fwd_noalloc",
     "kda_chunk_fwd_gated",
     "kda_chunk_fwd_varlen_workspace_size",
     "kda_chunk_fwd_varlen",
@@ -77,6 +78,8 @@ def load_library(path: str = LIB_PATH):
     lib.kda_chunk_fwd_planned.argtypes = [i, i, i, i, i, i, p, p, p, p, p, p, p, p,
                                           ctypes.POINTER(Plan), p, sz, p]
     lib.kda_chunk_fwd_planned.restype = i
+    lib.kda_chunk_fwd_noalloc.argtypes = [i, i, i, i, i, i, p, p, p, p, p, p, p, p, ctypes.POINTER(Plan), p]
+    lib.kda_chunk_fwd_noalloc.restype = i
     lib.kda_chunk_fwd_gated.argtypes = [i, i, i, i, i, i, p, p, p, p, p, p, p, p, p,
                                         ctypes.POINTER(Plan), p, sz, p]
     lib.kda_chunk_fwd_gated.restype = i
@@ -255,6 +258,35 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
         _stream_ptr(dev))
     if st != KDA_OK:
         raise KDAError(st, "kda_chunk_fwd_planned")
+    return out, final_state
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def chunk_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                      beta: torch.Tensor, initial_state: Optional[torch.Tensor], *, out: torch.Tensor,
+                      final_state: Optional[torch.Tensor] = None, plan=None):
+    """Prefill through ``kda_chunk_fwd_noalloc``: no workspace argument and no
+    allocation here or in the library (the caller passes ``out`` and, if
+    wanted, ``final_state``; it may be ``initial_state``).  ``plan`` as in
+    ``chunk_fwd``.  Returns (out, final_state)."""
+    B, T, H, K = q.shape
+    V = v.shape[-1]
+    dev = q.device
+    dt = q.dtype
+    for name, t, shp in (("q", q, (B, T, H, K)), ("k", k, (B, T, H, K)), ("g", g, (B, T, H, K)),
+                         ("v", v, (B, T, H, V)), ("beta", beta, (B, T, H)), ("out", out, (B, T, H, V))):
+        _check(t, name, shp, dt, dev)
+    for name, t in (("initial_state", initial_state), ("final_state", final_state)):
+        if t is not None:
+            _check(t, name, (B, H, K, V), torch.float32, dev)
+    pl = _plan_arg(plan)
+    st = load_library().kda_chunk_fwd_noalloc(
+        B, T, H, K, V, _dtype_code(dt), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+        _ptr(out), _ptr(final_state), None if pl is None else ctypes.byref(pl), _stream_ptr(dev))
+    if st != KDA_OK:
+        raise KDAError(st, "kda_chunk_fwd_noalloc")
     return out, final_state
 
 

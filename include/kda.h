@@ -166,6 +166,33 @@ kda_status kda_chunk_fwd_planned(int B, int T, int H, int K, int V, kda_dtype dt
                                  hipStream_t stream);
 
 /*
+ * kda_chunk_fwd_planned for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  No workspace argument: the workspace comes from a device array
+ * of KDA_NOALLOC_SCRATCH_BYTES (64 MiB) that the library defines and that
+ * each GPU it runs on holds until the process ends; the call allocates
+ * nothing.
+ *   plan : NULL = the plan kda_chunk_fwd picks when its workspace
+ *          (kda_chunk_fwd_planned_workspace_size) fits the array, else the
+ *          single-pass plan (split 1) with as many of the library's segments
+ *          as fit (one segment needs none, so every size runs); an explicit
+ *          plan whose workspace exceeds the array is KDA_ERR_WORKSPACE.
+ * All calls on one GPU share that GPU's array: calls that overlap in time on
+ * one GPU (from several streams or host threads) race and give wrong
+ * results; calls ordered on one stream are safe (nothing in the array needs
+ * to start at zero).  Every other argument, and the result, as
+ * kda_chunk_fwd_planned in the same plan.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+kda_status kda_chunk_fwd_noalloc(int B, int T, int H, int K, int V, kda_dtype dt,
+                                 const void* q, const void* k, const void* v,
+                                 const void* g, const void* beta,
+                                 const float* initial_state,
+                                 void* o, float* final_state,
+                                 const kda_plan* plan,
+                                 hipStream_t stream);
+
+/*
  * kda_chunk_fwd_planned with the output gate of the KDA block fused into the
  * store of o (aiblin.ru page, section "KV‑кэш все‑таки не исчез полностью":
  * after the attention a gate decides what share of its result passes on into

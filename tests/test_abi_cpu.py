@@ -175,6 +175,31 @@ def test_prefill_workspace_check_with_explicit_plan():
             assert _fwd(lib, T=T, H=H, plan=plan, ws=FAKE, ws_bytes=need - 1) == WORKSPACE
 
 
+def test_noalloc_validates_before_taking_its_scratch():
+    # host checks and the plan choice come before any HIP call; an explicit
+    # plan whose workspace exceeds the 64 MiB scratch array is rejected
+    lib = _lib()
+    p = lambda x: None if x is None else ctypes.c_void_p(x)
+
+    def call(B=1, T=64, H=1, K=128, V=128, dt=BF16, q=FAKE, s0=None, sT=None, plan=None):
+        return lib.kda_chunk_fwd_noalloc(B, T, H, K, V, dt, p(q), p(FAKE), p(FAKE), p(FAKE), p(FAKE), p(s0),
+                                         p(FAKE), p(sT), None if plan is None else ctypes.byref(plan), None)
+    assert call(K=96) == UNSUPPORTED
+    assert call(T=-1) == INVALID
+    assert call(q=None) == INVALID
+    assert call(s0=FAKE, sT=FAKE + 16) == INVALID
+    # 16 segments of 64 (b, h) chains: 15 * 64 * 128 KiB of transitions and
+    # local states plus 4 MiB, above 64 MiB; records of the two-pass plan too
+    big = dict(B=1, T=64 * 160, H=64)
+    assert _ws(lib, 1, 64 * 160, 64, 128, 128, BF16, K_.Plan(16, 128, 1)) == (15 * 64 + 64) * 128 * 128 * 4 + \
+        15 * 64 * 128 * 128 * 4
+    assert _ws(lib, 1, 64 * 160, 64, 128, 128, BF16, K_.Plan(16, 128, 1)) > K_.NOALLOC_SCRATCH_BYTES
+    assert call(plan=K_.Plan(16, 128, 1), **big) == WORKSPACE
+    assert call(plan=K_.Plan(1, 128, 2), **big) == WORKSPACE
+    assert call(B=0, q=None) == OK                   # nothing to do, no scratch taken
+    assert call(H=0, q=None) == OK
+
+
 def test_prefill_rejects_bad_plans():
     lib = _lib()
     assert _fwd(lib, plan=K_.Plan(1, 96)) == INVALID
