@@ -55,7 +55,10 @@ PREFILL_WORKLOADS = ("prefill_1m", "prefill_32k_x8", "prefill_8k")
 
 # launches that write o (and read S0 / write S_T): the path's algorithmic
 # bytes are attributed to them; the two-pass plan's intra-chunk pass gets the
-# input reads; summaries, scans and copies are plan overhead (zero)
+# input reads; the fused plan's summary pass reads k, g, v and beta of every
+# segment but the last and writes two states per segment; the two-pass
+# summaries (which read the intra-chunk workspace), scans and copies are plan
+# overhead (zero)
 OUTPUT_LAUNCHES = ("chunk_output", "state_output", "fused_output", "token_fwd")
 
 
@@ -77,7 +80,7 @@ def decode_bytes(N, H, K, V, in_bytes=2):
     return N * H * (8 * K * V + in_bytes * (3 * K + V + 1) + in_bytes * V)
 
 
-def kernel_bytes(name, B, T, H, K, V, in_bytes, s0, final, two_pass):
+def kernel_bytes(name, B, T, H, K, V, in_bytes, s0, final, two_pass, n_seg=1):
     """Algorithmic bytes of one launch named `name` (see OUTPUT_LAUNCHES)."""
     ht = B * T * H
     states = B * H * K * V * 4 * (int(s0) + int(final))
@@ -87,6 +90,11 @@ def kernel_bytes(name, B, T, H, K, V, in_bytes, s0, final, two_pass):
         return reads
     if name in OUTPUT_LAUNCHES:
         return writes + states + (0 if two_pass else reads)
+    if name == "fused_summary" and n_seg > 1:
+        n_chunks = (T + 63) // 64
+        cps = (n_chunks + n_seg - 1) // n_seg
+        covered = min((n_seg - 1) * cps * 64, T)          # tokens of the summarised segments
+        return B * covered * H * in_bytes * (2 * K + V + 1) + 2 * B * H * (n_seg - 1) * K * V * 4
     return 0
 
 
@@ -251,7 +259,7 @@ def main():
         tflops = nflops / (ms * 1e-3) / 1e12
         dom = max(kernels, key=lambda n: kernels[n]["avg_ms"] * kernels[n]["launches_per_call"])
         dom_ms = kernels[dom]["avg_ms"]
-        dom_bytes = kernel_bytes(dom, B, T, H, K, V, 2, has_s0, True, plan[2] == 2)
+        dom_bytes = kernel_bytes(dom, B, T, H, K, V, 2, has_s0, True, plan[2] == 2, plan[0])
         dom_gbs = dom_bytes / (dom_ms * 1e-3) / 1e9
         traffic, traffic_note = recorded_traffic(name, dom, plan)
         working_set = nbytes + ws_n

@@ -11,7 +11,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libkda.so")
 SOURCES = ["kda_api.cpp", "kda_chunk.hip", "kda_split.hip", "kda_decode.hip", "kda_bwd.hip", "kda_bwd_chunk.hip",
-           "kda_noalloc.hip"]
+           "kda_noalloc.hip", "kda_fused.hip"]
 ARCH = "gfx950"
 
 

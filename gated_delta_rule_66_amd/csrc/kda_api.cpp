@@ -101,8 +101,39 @@ kda_status resolve_plan(int B, int T, int H, int K, int V, kda_dtype dt, const k
     int vb = req ? req->v_block : 0;
     int ns = req ? req->n_seg : 0;
     int split = req ? req->split : 0;
-    if (vb < 0 || ns < 0 || split < 0 || split > 3) return KDA_ERR_INVALID_ARG;
+    if (vb < 0 || ns < 0 || split < 0 || split > 4) return KDA_ERR_INVALID_ARG;
     if (vb != 0 && vb != 64 && vb != 128) return KDA_ERR_INVALID_ARG;
+    // the fused form wherever it exists (bf16 with K = V = 128): one
+    // workgroup per (b, h, segment) holds every value column; segments until
+    // the workgroups cover the CUs, each segment keeping at least 4 chunks
+    // (a request for narrower column blocks keeps the other forms)
+    if (split == 0 && fused_variant_exists((int)dt, K, V) && (vb == 0 || vb == V)) split = 4;
+    if (split == 4) {
+        if (!fused_variant_exists((int)dt, K, V) || (vb != 0 && vb != V)) return KDA_ERR_UNSUPPORTED;
+        if (ns == 0) {
+            int cus = cus_fixed;
+            if (cus <= 0) {
+                kda_status s = device_cus(&cus);
+                if (s != KDA_OK) return s;
+            }
+            ns = 1;
+            if (bh > 0 && bh < cus) {
+                const long want = (cus + bh - 1) / bh;
+                const long cap = n_chunks / 4;
+                ns = (int)(want < cap ? want : cap);
+                if (ns < 1) ns = 1;
+            }
+        }
+        if (n_chunks > 0 && ns > n_chunks) ns = n_chunks;
+        if (ns < 1) ns = 1;
+        const int cps4 = n_chunks > 0 ? (n_chunks + ns - 1) / ns : 1;
+        if (n_chunks > 0) ns = (n_chunks + cps4 - 1) / cps4;   // no empty segments
+        out->n_seg = ns;
+        out->v_block = V;
+        out->split = 4;
+        if (cps_out) *cps_out = cps4;
+        return KDA_OK;
+    }
     // the token-serial form: the only one for sizes without chunk kernels
     // (fp32 with K or V = 128); one 64-column workgroup per (b, h, block)
     if (split == 0 && !split_variant_exists((int)dt, K, V, 64) && !chunk_variant_exists((int)dt, K, 64)) split = 3;
@@ -295,6 +326,60 @@ static kda_status chunk_impl(int B, int T, int H, int K, int V, kda_dtype dt,
     if (need > 0 && ((!workspace && !dry_run) || workspace_bytes < need)) return KDA_ERR_WORKSPACE;
     if (dry_run) return KDA_OK;
 
+    if (pl.split == 4) {
+        FusedParams fp{};
+        fp.q = q; fp.k = k; fp.v = v; fp.g = g; fp.beta = beta;
+        fp.B = B; fp.T = T; fp.H = H;
+        fp.n_seg = pl.n_seg;
+        fp.cps = cps;
+        if (pl.n_seg == 1) {
+            fp.s0 = initial_state;
+            fp.o = o;
+            fp.gate = gate;
+            fp.sT = final_state;
+            return launch_timed("fused_output", st, [&] { return launch_fused(fp, false, (int)bh, st); }) ==
+                   hipSuccess ? KDA_OK : KDA_ERR_HIP;
+        }
+        float* ws = reinterpret_cast<float*>(workspace);
+        float* wsP = ws;
+        float* wsL = wsP + (size_t)(pl.n_seg - 1) * bh * K * K;
+        float* wsFinal = wsL + (size_t)(pl.n_seg - 1) * bh * K * V;
+        // pass 1: per segment (but the last), transition P and local state L
+        FusedParams f1 = fp;
+        f1.wsP = wsP;
+        f1.wsL = wsL;
+        if (launch_timed("fused_summary", st, [&] {
+                return launch_fused(f1, true, (int)(bh * (pl.n_seg - 1)), st);
+            }) != hipSuccess)
+            return KDA_ERR_HIP;
+        // pass 2: segment start states
+        ScanParams scp{};
+        scp.s0 = initial_state;
+        scp.wsP = wsP;
+        scp.wsL = wsL;
+        scp.BH = (int)bh;
+        scp.V = V;
+        scp.n_seg = pl.n_seg;
+        if (launch_timed("segment_scan", st, [&] { return launch_scan(K, scp, st); }) != hipSuccess)
+            return KDA_ERR_HIP;
+        // pass 3: every segment from its true start state, with output
+        const bool aliased = final_state && final_state == initial_state;
+        FusedParams f3 = fp;
+        f3.s0 = initial_state;
+        f3.seg_init = wsL;
+        f3.o = o;
+        f3.gate = gate;
+        f3.sT = aliased ? wsFinal : final_state;
+        if (launch_timed("fused_output", st, [&] {
+                return launch_fused(f3, false, (int)(bh * pl.n_seg), st);
+            }) != hipSuccess)
+            return KDA_ERR_HIP;
+        if (aliased && launch_timed("copy_state", st, [&] {
+                return launch_copy_state(wsFinal, final_state, (size_t)bh * K * V, st);
+            }) != hipSuccess)
+            return KDA_ERR_HIP;
+        return KDA_OK;
+    }
     if (pl.split == 3) {
         TokenFwdParams tp{};
         tp.q = q; tp.k = k; tp.v = v; tp.g = g; tp.beta = beta; tp.gate = gate;
@@ -694,7 +779,8 @@ static kda_status bwd_layout(int B, int T, int H, int K, int V, kda_dtype dt, Bw
     if (split_variant_exists((int)dt, K, V, 64) && bwd_chunk_variant_exists((int)dt, K, V) && V % 64 == 0) {
         // the forward inside the backward is planned for the 256 CUs of an
         // MI355X, so that the workspace size does not depend on the device
-        kda_status s = resolve_plan(B, T, H, K, V, dt, nullptr, &L->plan, &L->cps, 256);
+        const kda_plan two_pass{0, 0, 2};
+        kda_status s = resolve_plan(B, T, H, K, V, dt, &two_pass, &L->plan, &L->cps, 256);
         if (s != KDA_OK) return s;
         L->chunked = L->plan.split == 2;
     }

@@ -30,6 +30,27 @@ struct ChunkParams {
     int summary;            // 1: segment summary pass (no output, identity/zero start)
 };
 
+// Arguments of the fused chunk kernel (bf16, K = V = 128): one workgroup per
+// (b, h, segment); four waves prepare chunk c + 1 while four carry the state
+// through chunk c.  Fields as ChunkParams.
+struct FusedParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* g;
+    const void* beta;
+    const float* s0;        // [B,H,K,V] initial state of segment 0, or null (zeros)
+    const float* seg_init;  // [n_seg-1][B*H][K][V]: start state of segment s >= 1 at slot s-1
+    void* o;                // [B,T,H,V] (output pass)
+    const void* gate;       // [B,T,H,V] output gate pre-activation z (o <- o sigmoid(z)), or null
+    float* sT;              // [B,H,K,V] final state or null (output pass)
+    float* wsP;             // summary pass: [n_seg-1][B*H][K][K]
+    float* wsL;             // summary pass: [n_seg-1][B*H][K][V]
+    int B, T, H;
+    int n_seg;              // segments of the sequence
+    int cps;                // chunks per segment
+};
+
 // Arguments of the segment scan: S_{j+1} = P_j S_j + L_j, written over L_j.
 struct ScanParams {
     const float* s0;        // [B,H,K,V] or null
@@ -168,6 +189,8 @@ hipError_t launch_state(int dtype, int K, int VB, const StateParams& p, int grid
 
 // Kernel-variant selection: returns false if (dtype, K, VB) has no kernel.
 bool chunk_variant_exists(int dtype, int K, int VB);
+bool fused_variant_exists(int dtype, int K, int V);
+hipError_t launch_fused(const FusedParams& p, bool summary, int grid, hipStream_t stream);
 
 hipError_t launch_chunk(int dtype, int K, int VB, const ChunkParams& p, int grid,
                         hipStream_t stream);

@@ -11,7 +11,7 @@ uses for its launches, together with a hash of the kernel sources (so that a
 reader can tell when the record no longer describes the current kernels).
 
     python -m gated_delta_rule_66_amd.traffic --fetch DIR --write DIR \\
-        --copy-fetch DIR --copy-write DIR --copy-mib N --plan NSEG,VB --out FILE
+        --copy-fetch DIR --copy-write DIR --copy-mib N --plan NSEG,VB,SPLIT --out FILE
 """
 from __future__ import annotations
 
@@ -57,6 +57,9 @@ def launch_name(kernel_name: str):
     if "kda_state_kernel" in n:
         # <T, K, waves, tiles, SUMMARY, OUT, GATE>
         return "state_summary" if _first_bool(n, "kda_state_kernel") else "state_output"
+    if "kda_fused_kernel" in n:
+        # <SUMMARY, GATE>
+        return "fused_summary" if _first_bool(n, "kda_fused_kernel") else "fused_output"
     if "kda_scan_kernel" in n:
         return "segment_scan"
     if "kda_decode_multi_kernel" in n:
@@ -107,7 +110,7 @@ def main():
     ap.add_argument("--copy-fetch", required=True)
     ap.add_argument("--copy-write", required=True)
     ap.add_argument("--copy-mib", type=int, required=True)
-    ap.add_argument("--plan", required=True, help="n_seg,v_block of the profiled prefill call")
+    ap.add_argument("--plan", required=True, help="n_seg,v_block,split of the profiled prefill call")
     ap.add_argument("--workload", default="")
     ap.add_argument("--command", default="")
     ap.add_argument("--out", required=True)

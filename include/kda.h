@@ -80,7 +80,14 @@ typedef enum kda_dtype {
  *            the page's section "Как хранить миллион токенов в памяти"), the
  *            state in registers; no workspace, n_seg 1, v_block 64.  The
  *            library's choice only where no chunk kernel exists (fp32 with
- *            K = 128); a chain's time grows with its length.
+ *            K = 128); a chain's time grows with its length;
+ *            4 = fused: one workgroup per (b, h, segment) in which four waves
+ *            prepare chunk c + 1 (gate cumsum, in-chunk products, the
+ *            triangular solve) while four waves carry the state through
+ *            chunk c, the operands passed through LDS: the inputs are read
+ *            once and nothing per chunk touches HBM.  bf16 with K = V = 128
+ *            only, v_block 128 (0 or V); the library's choice for those
+ *            sizes.
  *   n_seg:   number of sequence segments evaluated side by side on one card
  *            (1 = none; > 1 adds the segment summary and segment scan passes).
  *   v_block: value columns per workgroup of the state-carrying pass (64 or
@@ -149,7 +156,8 @@ kda_status kda_chunk_fwd(int B, int T, int H, int K, int V, kda_dtype dt,
  *          kernels cannot run is KDA_ERR_INVALID_ARG (a field out of range) or
  *          KDA_ERR_UNSUPPORTED (a valid field these sizes have no kernel for).
  * The workspace size in a plan: with split = 2 one record per (b, h, chunk)
- * (for K = V = 128 bf16, 72.5 KiB); with n_seg > 1 the segment transitions
+ * (for K = V = 128 bf16, 72.5 KiB; splits 1, 3 and 4 keep none); with
+ * n_seg > 1 the segment transitions
  * and local states ((n_seg - 1) * B * H * K * (K + V) fp32) plus
  * B * H * K * V fp32 (a redirected final state).  Every other argument, and
  * the result up to fp32/bf16 rounding, as kda_chunk_fwd.

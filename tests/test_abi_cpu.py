@@ -207,7 +207,11 @@ def test_prefill_rejects_bad_plans():
     assert _fwd(lib, K=64, V=64, plan=K_.Plan(1, 128)) == UNSUPPORTED
     # a segmented plan needs value blocks that tile the K transition columns
     assert _fwd(lib, T=64 * 40, K=64, V=128, plan=K_.Plan(2, 128), ws=FAKE, ws_bytes=1 << 30) == UNSUPPORTED
-    assert _fwd(lib, plan=K_.Plan(1, 64, 4)) == INVALID
+    assert _fwd(lib, plan=K_.Plan(1, 64, 5)) == INVALID
+    # the fused plan holds every value column of bf16 K = V = 128 in one workgroup
+    assert _fwd(lib, plan=K_.Plan(1, 64, 4)) == UNSUPPORTED
+    assert _fwd(lib, K=64, V=64, plan=K_.Plan(1, 0, 4)) == UNSUPPORTED
+    assert _fwd(lib, dt=F32, plan=K_.Plan(1, 0, 4)) == UNSUPPORTED
     assert _fwd(lib, plan=K_.Plan(1, 64, -1)) == INVALID
     bad = K_.Plan(1, 96)
     assert _ws(lib, 1, 64, 1, 128, 128, BF16, bad) == ctypes.c_size_t(-1).value

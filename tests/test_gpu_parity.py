@@ -33,14 +33,21 @@ def run_oracle(d):
 
 def gpu_fwd(x, plan=None, s0="use", split=0, **kw):
     """Prefill through the C ABI; split 1 = single-pass kernel, 2 = intra-chunk
-    pass + state pass, 0 = the library's choice."""
+    pass + state pass, 4 = the fused producer/consumer kernel (bf16 with
+    K = V = 128 only: other shapes skip; it holds all value columns, so the
+    plan's column block is left to the library), 0 = the library's choice."""
     init = x["s0"] if s0 == "use" else s0
-    if split:
+    if split == 4:
+        K, V = x["q"].shape[-1], x["v"].shape[-1]
+        if x["q"].dtype != torch.bfloat16 or K != 128 or V != 128:
+            pytest.skip("the fused kernel covers bf16 with K = V = 128")
+        plan = (0, 0, 4) if plan is None else (plan[0], 0, 4)
+    elif split:
         plan = (0, 0, split) if plan is None else (plan[0], plan[1], split)
     return chunk_fwd(x["q"], x["k"], x["v"], x["g"], x["beta"], init, True, plan, **kw)
 
 
-PATHS = [1, 2]
+PATHS = [1, 2, 4]
 
 
 # ------------------------------------------------------------------ small cases
@@ -277,7 +284,7 @@ def test_deterministic_repeat():
     say("bitwise repeatability")
     d = make_prefill(1, 64 * 30, 4, 128, 128, torch.bfloat16, seed=19, s0_std=0.02)
     x = to_dev(d)
-    for plan in ((1, 64, 1), (3, 128, 1), (1, 64, 2), (3, 128, 2)):
+    for plan in ((1, 64, 1), (3, 128, 1), (1, 64, 2), (3, 128, 2), (1, 128, 4), (3, 128, 4)):
         a = gpu_fwd(x, plan)
         b = gpu_fwd(x, plan)
         torch.cuda.synchronize()
@@ -293,7 +300,7 @@ def test_deterministic_repeat_k64(dtype, K, V):
     say("bitwise repeatability %s K=%d V=%d" % (dtype, K, V))
     d = make_prefill(2, 64 * 20 + 9, 3, K, V, dtype, seed=29, s0_std=0.02)
     x = to_dev(d)
-    for split in PATHS:
+    for split in (1, 2):
         for n_seg in (1, 4):
             plan = (n_seg, 64, split)
             ref = gpu_fwd(x, plan)
@@ -346,10 +353,13 @@ def test_launch_profiling_names_every_launch():
     gpu_fwd(x, (3, 64, 1), workspace=ws)
     gpu_fwd(x, (1, 64, 2), workspace=ws)
     gpu_fwd(x, (3, 64, 2), workspace=ws)
+    gpu_fwd(x, (1, 0, 4))
+    gpu_fwd(x, (3, 0, 4), workspace=ws)
     rec = kda.profile_stop(16)
     assert [n for n, _ in rec] == ["chunk_output", "chunk_summary", "segment_scan", "chunk_output",
                                    "intra_chunk", "state_output",
-                                   "intra_chunk", "state_summary", "segment_scan", "state_output"]
+                                   "intra_chunk", "state_summary", "segment_scan", "state_output",
+                                   "fused_output", "fused_summary", "segment_scan", "fused_output"]
     assert all(ms > 0 for _, ms in rec)
     o, _ = gpu_fwd(x, (1, 64))                 # timing is off again: results unchanged
     ref, _ = run_oracle(d)
@@ -622,6 +632,7 @@ def _sampled_oracle(x, chains):
 
 @pytest.mark.parametrize("name,chains,split", [("prefill_8k", [(0, 0), (0, 7), (0, 19), (0, 31)], 0),
                                                ("prefill_8k", [(0, 3), (0, 30)], 1),
+                                               ("prefill_8k", [(0, 5), (0, 26)], 2),
                                                ("prefill_32k_x8", [(0, 3), (5, 17), (7, 31), (2, 9)], 0),
                                                ("prefill_1m", [(0, 0), (0, 5), (0, 11), (0, 15)], 0)])
 def test_full_size_prefill_sampled(name, chains, split):
