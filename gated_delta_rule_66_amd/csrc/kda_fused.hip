@@ -50,36 +50,16 @@ namespace {
 constexpr int FC = 64;     // tokens per chunk
 constexpr int FK = 128;    // key channels = value columns
 
-// LDS layout (bytes).  Per iteration, phase 1a: the producers do the
-// block-local work of chunk c + 1 while the consumers read K^ and Q^ of chunk
-// c and assemble its T diag(beta) from D and N'; phase 1b: the consumers read
-// the rest of chunk c while the producers write K^, Q^, K-^T, e^{G_C}, the
-// off-diagonal Mqk and N' of chunk c + 1.  What the producers write while the
-// consumers may still read the previous chunk's copy (K-^T, e^{G_C}, Mqk, D,
-// beta) is double-buffered by chunk parity.  Then producer scratch: the
-// block-scaled k and q fragments and k e^{Tot - Gin}, from phase 1a to 1b.
-template <bool SUMMARY>
-struct FusedLds {
-    static constexpr int NQ = SUMMARY ? 0 : 1;      // Q^ buffers
-    static constexpr int NM = SUMMARY ? 0 : 2;      // Mqk buffers
-    static constexpr int oK = 0;                    // K^ fragments [4 blk][4 slab][64 lanes] x 16 B
-    static constexpr int oQ = oK + 16384;           // Q^ fragments [NQ][4 blk][4 slab][64] x 16 B
-    static constexpr int oKb = oQ + NQ * 16384;     // K- tiles, transposed [2][4 blk][8 m][64] x 8 B
-    static constexpr int oT = oKb + 32768;          // T diag(beta), row layout [4 ti][4 j][64] x 8 B
-    static constexpr int oM = oT + 8192;            // Mqk, row layout [NM][4 ti][4 j][64] x 8 B
-    static constexpr int oG = oM + NM * 8192;       // e^{G_C} [2][128] fp32
-    static constexpr int oETot = oG + 1024;         // e^{Tot} of each block [4][128] fp32
-    static constexpr int oKend = oETot + 2048;      // k e^{Tot - Gin}, fragments [3 blk][4 slab][64] x 16 B
-    static constexpr int oBeta = oKend + 12288;     // beta [2][64] fp32
-    static constexpr int oD = oBeta + 512;          // D_i acc layout [2][4][64] x 8 B
-    static constexpr int oNa = oD + 4096;           // N'_ij acc layout, fp32 [6 pairs][64] x 16 B
-    static constexpr int oNr = oNa + 6144;          // N'_ij row layout [6 pairs][64] x 8 B
-    static constexpr int oFac = oNr + 3072;         // per producer wave: e^{G_b}, e^{G_C - G_b} [4][2][128] fp32
-    static constexpr int oKd = oFac + 4096;         // k e^{Gin} fragments [4 blk][4 slab][64] x 16 B
-    static constexpr int oQd = oKd + 16384;         // q e^{Gin} fragments [4 blk][4 slab][64] x 16 B (output pass)
-    static constexpr int TOTAL = oQd + (SUMMARY ? 0 : 16384);
-    static_assert(TOTAL <= 160 * 1024, "LDS budget");
-};
+// LDS.  Per iteration, phase 1a: the producers do the block-local work of
+// chunk c + 1 while the consumers read K^ and Q^ of chunk c and assemble its
+// T diag(beta) from D and N'; phase 1b: the consumers read the rest of chunk
+// c while the producers write K^, Q^, K-^T, e^{G_C}, the off-diagonal Mqk and
+// N' of chunk c + 1.  What the producers write while the consumers may still
+// read the previous chunk's copy (K-^T, e^{G_C}, Mqk, D, beta) is
+// double-buffered by chunk parity.  Producer scratch: the block-scaled k and
+// q fragments and k e^{Tot - Gin}, from phase 1a to 1b.  Each region is an
+// array of its own (declared in the kernel), so that the compiler knows a
+// store to one does not alias a load from another and can move loads ahead.
 
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
@@ -194,23 +174,23 @@ __device__ __forceinline__ int chan4(int m, int g) { return 32 * (m >> 1) + 8 * 
 
 template <bool SUMMARY, bool GATE>
 __global__ __launch_bounds__(512, 1) void kda_fused_kernel(FusedParams p) {
-    using L = FusedLds<SUMMARY>;
-    __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
-    bf16x8* hK = reinterpret_cast<bf16x8*>(smem + L::oK);
-    bf16x8* hQ = reinterpret_cast<bf16x8*>(smem + L::oQ);
-    bf16x4* hKb = reinterpret_cast<bf16x4*>(smem + L::oKb);
-    bf16x4* hT = reinterpret_cast<bf16x4*>(smem + L::oT);
-    bf16x4* hM = reinterpret_cast<bf16x4*>(smem + L::oM);
-    float* hG = reinterpret_cast<float*>(smem + L::oG);
-    float* sETot = reinterpret_cast<float*>(smem + L::oETot);
-    bf16x8* sKend = reinterpret_cast<bf16x8*>(smem + L::oKend);
-    float* sBeta = reinterpret_cast<float*>(smem + L::oBeta);
-    bf16x4* sD = reinterpret_cast<bf16x4*>(smem + L::oD);
-    f32x4* sNa = reinterpret_cast<f32x4*>(smem + L::oNa);
-    bf16x4* sNr = reinterpret_cast<bf16x4*>(smem + L::oNr);
-    bf16x8* sQd = reinterpret_cast<bf16x8*>(smem + L::oQd);
-    bf16x8* sKd = reinterpret_cast<bf16x8*>(smem + L::oKd);
-    float* sFac = reinterpret_cast<float*>(smem + L::oFac);
+    constexpr int NQ = SUMMARY ? 1 : 4 * 4 * 64;       // the summary pass has no q: 1-element stand-ins
+    constexpr int NM = SUMMARY ? 1 : 2 * 4 * 4 * 64;
+    __shared__ bf16x8 hK[4 * 4 * 64];                   // K^ fragments [4 blk][4 slab][64 lanes]
+    __shared__ bf16x8 hQ[NQ];                           // Q^ fragments [4 blk][4 slab][64]
+    __shared__ bf16x4 hKb[2 * 4 * 8 * 64];              // K- tiles, transposed [2][4 blk][8 m][64]
+    __shared__ bf16x4 hT[4 * 4 * 64];                   // T diag(beta), row layout [4 ti][4 j][64]
+    __shared__ bf16x4 hM[NM];                           // Mqk, row layout [2][4 ti][4 j][64]
+    __shared__ __attribute__((aligned(16))) float hG[2 * FK];        // e^{G_C} [2][128]
+    __shared__ __attribute__((aligned(16))) float sETot[4 * FK];     // e^{Tot} of each block [4][128]
+    __shared__ bf16x8 sKend[3 * 4 * 64];                // k e^{Tot - Gin} [3 blk][4 slab][64]
+    __shared__ float sBeta[2 * 64];                     // beta [2][64]
+    __shared__ bf16x4 sD[2 * 4 * 64];                   // D_i acc layout [2][4][64]
+    __shared__ f32x4 sNa[6 * 64];                       // N'_ij acc layout [6 pairs][64]
+    __shared__ bf16x4 sNr[6 * 64];                      // N'_ij row layout [6 pairs][64]
+    __shared__ __attribute__((aligned(16))) float sFac[4 * 2 * FK];  // per producer wave: e^{G_b}, e^{G_C - G_b}
+    __shared__ bf16x8 sKd[4 * 4 * 64];                  // k e^{Gin} fragments [4 blk][4 slab][64]
+    __shared__ bf16x8 sQd[NQ];                          // q e^{Gin} fragments [4 blk][4 slab][64]
 
     const int tid = threadIdx.x;
     // the wave index is uniform across the wave: in a scalar register, so
@@ -381,17 +361,18 @@ __global__ __launch_bounds__(512, 1) void kda_fused_kernel(FusedParams p) {
             // into the wave's table; wave 0's second factor is e^{G_C}
             float* fac = sFac + pw * 2 * FK;
             {
+                float2 t[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) t[j] = *reinterpret_cast<const float2*>(&sETot[j * FK + 2 * l]);
                 float2 eg = make_float2(1.f, 1.f), ec = make_float2(1.f, 1.f);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const float2 t = *reinterpret_cast<const float2*>(&sETot[j * FK + 2 * l]);
-                    if (j < pw) {
-                        eg.x *= t.x;
-                        eg.y *= t.y;
-                    } else {
-                        ec.x *= t.x;
-                        ec.y *= t.y;
-                    }
+                    // selects, not branches: the four loads are waited for once
+                    const bool pre = j < pw;
+                    eg.x *= pre ? t[j].x : 1.f;
+                    eg.y *= pre ? t[j].y : 1.f;
+                    ec.x *= pre ? 1.f : t[j].x;
+                    ec.y *= pre ? 1.f : t[j].y;
                 }
                 *reinterpret_cast<float2*>(&fac[2 * l]) = eg;
                 *reinterpret_cast<float2*>(&fac[FK + 2 * l]) = ec;
@@ -526,47 +507,56 @@ __global__ __launch_bounds__(512, 1) void kda_fused_kernel(FusedParams p) {
                 vq[ti][jt] = ld_b64(rv, (unsigned)(16 * ti + lr) * rowK + (unsigned)(2 * (32 * cw + 16 * jt + 4 * lg)));
     };
 
-    // Block row i = cw of T diag(beta), T = D (I + N')^{-1} assembled from
-    // D_i = (I + A_ii)^{-1} and N'_ij = A_ij D_j (both from the producers):
-    // T_ii = D_i, T_ij = D_i M'_ij with M' = (I + N')^{-1}, written in row
-    // layout.
-    auto t_rows = [&](int ci) {
+    // T diag(beta), T = D (I + N')^{-1} assembled from D_i = (I + A_ii)^{-1}
+    // and N'_ij = A_ij D_j (both from the producers): T_ii = D_i and
+    // T_ij = D_i M'_ij with M' = (I + N')^{-1}:
+    //   M'_{i,i-1} = -N'_{i,i-1},  M'_20 = N'_21 N'_10 - N'_20,
+    //   M'_31 = N'_32 N'_21 - N'_31,  M'_30 = N'_31 N'_10 - N'_30 - N'_32 M'_20,
+    // written in row layout.  The ten tiles are shared out so that each wave's
+    // chain of dependent products is at most seven long.
+    auto t_tiles = [&](int ci) {
         const int buf = ci & 1;
-        const int i = cw;
-        const float bt = sBeta[buf * 64 + 16 * i + lr];
-        const bf16x4 drow = to_bf4(mm16(sD[(buf * 4 + i) * 64 + l], ident));     // row layout of D_i
-        {
+        auto drow = [&](int i) { return to_bf4(mm16(sD[(buf * 4 + i) * 64 + l], ident)); };   // row layout of D_i
+        auto na = [&](int i, int j) { return sNa[pair_ix(i, j) * 64 + l]; };
+        auto nr = [&](int i, int j) { return sNr[pair_ix(i, j) * 64 + l]; };
+        auto diag = [&](int i, bf16x4 dr) {
+            const float bt = sBeta[buf * 64 + 16 * i + lr];
             bf16x4 dg;
 #pragma unroll
             for (int e = 0; e < 4; ++e) dg[e] = (bf16)((4 * lg + e == lr) ? bt : 0.f);
-            hT[(i * 4 + i) * 64 + l] = to_bf4(mm16(dg, drow));        // D_i diag(beta_i)
-        }
-        if (i == 0) return;
-        f32x4 mp[3];                         // M'_{ij} = ((I + N')^{-1})_{ij}, acc layout
-        if (i == 1) {
-            mp[0] = -sNa[pair_ix(1, 0) * 64 + l];
-        } else if (i == 2) {
-            mp[0] = mm16(sNr[pair_ix(2, 1) * 64 + l], to_bf4(sNa[pair_ix(1, 0) * 64 + l]), -sNa[pair_ix(2, 0) * 64 + l]);
-            mp[1] = -sNa[pair_ix(2, 1) * 64 + l];
+            hT[(i * 4 + i) * 64 + l] = to_bf4(mm16(dg, dr));             // D_i diag(beta_i)
+        };
+        auto off = [&](int i, int j, f32x4 mp, bf16x4 dr) {           // mp = M'_ij, acc layout
+            const float bj = sBeta[buf * 64 + 16 * j + lr];           // column lr of block j
+            hT[(i * 4 + j) * 64 + l] = to_bf4(mm16(to_bf4(mp * bj), dr));
+        };
+        auto m20 = [&]() { return mm16(nr(2, 1), to_bf4(na(1, 0)), -na(2, 0)); };
+        if (cw == 0) {
+            diag(0, drow(0));
+            const f32x4 m30 = mm16(nr(3, 1), to_bf4(na(1, 0)), -na(3, 0)) - mm16(nr(3, 2), to_bf4(m20()));
+            off(3, 0, m30, drow(3));
+        } else if (cw == 1) {
+            const bf16x4 d1 = drow(1);
+            diag(1, d1);
+            off(1, 0, -na(1, 0), d1);
+            off(2, 0, m20(), drow(2));
+        } else if (cw == 2) {
+            const bf16x4 d2 = drow(2);
+            diag(2, d2);
+            off(2, 1, -na(2, 1), d2);
+            off(3, 1, mm16(nr(3, 2), to_bf4(na(2, 1)), -na(3, 1)), drow(3));
         } else {
-            const bf16x4 na10 = to_bf4(sNa[pair_ix(1, 0) * 64 + l]);
-            const f32x4 m20 = mm16(sNr[pair_ix(2, 1) * 64 + l], na10, -sNa[pair_ix(2, 0) * 64 + l]);
-            mp[0] = mm16(sNr[pair_ix(3, 1) * 64 + l], na10, -sNa[pair_ix(3, 0) * 64 + l]) -
-                    mm16(sNr[pair_ix(3, 2) * 64 + l], to_bf4(m20));
-            mp[1] = mm16(sNr[pair_ix(3, 2) * 64 + l], to_bf4(sNa[pair_ix(2, 1) * 64 + l]), -sNa[pair_ix(3, 1) * 64 + l]);
-            mp[2] = -sNa[pair_ix(3, 2) * 64 + l];
-        }
-#pragma unroll
-        for (int j = 0; j < 3; ++j) {
-            if (j < i) {
-                const float bj = sBeta[buf * 64 + 16 * j + lr];         // column lr of block j
-                hT[(i * 4 + j) * 64 + l] = to_bf4(mm16(to_bf4(mp[j] * bj), drow));
-            }
+            const bf16x4 d3 = drow(3);
+            diag(3, d3);
+            off(3, 2, -na(3, 2), d3);
         }
     };
 
     // Y = V - K^ S, as 32-deep fragments (blocks 2 ks, 2 ks + 1); in the
-    // output pass also the inter-chunk part of the output, Q^ S
+    // output pass also the inter-chunk part of the output, Q^ S, computed
+    // transposed ((Q^ S)^T = S^T Q^^T: the state fragments as the A operand)
+    // so that its accumulator holds one token per lane and four consecutive
+    // value columns, the layout of the stores
     auto consume_a = [&](int ci, f32x4 (&St)[2][8], bool with_v, bf16x8 (&yb)[2][2], f32x4 (&accO)[4][2]) {
         const int buf = ci & 1;
         f32x4 accY[4][2];
@@ -590,7 +580,7 @@ __global__ __launch_bounds__(512, 1) void kda_fused_kernel(FusedParams p) {
                 if (!SUMMARY) {
                     const bf16x8 aq = hQ[(ti * 4 + s4) * 64 + l];
 #pragma unroll
-                    for (int jt = 0; jt < 2; ++jt) accO[ti][jt] = mma(accO[ti][jt], aq, sb[jt]);
+                    for (int jt = 0; jt < 2; ++jt) accO[ti][jt] = mma(accO[ti][jt], sb[jt], aq);
                 }
             }
         }
@@ -639,8 +629,9 @@ __global__ __launch_bounds__(512, 1) void kda_fused_kernel(FusedParams p) {
             const __amdgpu_buffer_rsrc_t ro = make_rsrc_n(reinterpret_cast<bf16*>(p.o) + row0 * FK, span);
             const __amdgpu_buffer_rsrc_t rz =
                 make_rsrc_n(GATE ? reinterpret_cast<const bf16*>(p.gate) + row0 * FK : nullptr, GATE ? span : 0u);
-            // O = Q^ S + Mqk U per 16-token tile, rounded to bf16 and turned to
-            // row layout for 8-byte stores (4 columns of one token per lane)
+            // O^T += U^T Mqk^T per 16-token tile (the U fragments as the A
+            // operand), rounded to bf16 and stored 8 bytes a lane (4 columns of
+            // one token)
 #pragma unroll
             for (int ti = 0; ti < 4; ++ti) {
                 f32x4 (&accO)[2] = accO4[ti];
@@ -650,12 +641,12 @@ __global__ __launch_bounds__(512, 1) void kda_fused_kernel(FusedParams p) {
                         const bf16x8 a = cat8(hM[((buf * 4 + ti) * 4 + 2 * ks) * 64 + l],
                                               (2 * ks + 1 <= ti) ? hM[((buf * 4 + ti) * 4 + 2 * ks + 1) * 64 + l] : z4);
 #pragma unroll
-                        for (int jt = 0; jt < 2; ++jt) accO[jt] = mma(accO[jt], a, ub[ks][jt]);
+                        for (int jt = 0; jt < 2; ++jt) accO[jt] = mma(accO[jt], ub[ks][jt], a);
                     }
                 }
 #pragma unroll
                 for (int jt = 0; jt < 2; ++jt) {
-                    bf16x4 o4 = to_bf4(mm16(to_bf4(accO[jt]), ident));
+                    bf16x4 o4 = to_bf4(accO[jt]);
                     const unsigned voff = (unsigned)(16 * ti + lr) * rowK + (unsigned)(2 * (32 * cw + 16 * jt + 4 * lg));
                     if (GATE) {
                         // output gate: o (rounded to bf16) * sigmoid(z), rounded once more
@@ -698,7 +689,7 @@ __global__ __launch_bounds__(512, 1) void kda_fused_kernel(FusedParams p) {
             // two states to carry: V is loaded in the phase that reads it
             bf16x8 yp[2][2];
             load_vq(ci);
-            t_rows(ci);
+            t_tiles(ci);
             __builtin_amdgcn_sched_barrier(0);
             consume_a(ci, S[0], true, yb, accO);
             __builtin_amdgcn_sched_barrier(0);     // one column group's temporaries at a time
@@ -709,7 +700,7 @@ __global__ __launch_bounds__(512, 1) void kda_fused_kernel(FusedParams p) {
             consume_b(ci, S[NG - 1], yp, false, accO);
             __syncthreads();
         } else {
-            t_rows(ci);
+            t_tiles(ci);
             consume_a(ci, S[0], true, yb, accO);
             __syncthreads();
             consume_b(ci, S[0], yb, true, accO);
