@@ -258,6 +258,7 @@ const char* kda_status_string(kda_status s) {
         case KDA_ERR_UNSUPPORTED: return "unsupported sizes or dtype";
         case KDA_ERR_WORKSPACE: return "workspace missing or too small";
         case KDA_ERR_HIP: return "HIP runtime error";
+        default: break;
     }
     return "unknown status";
 }

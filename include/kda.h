@@ -60,12 +60,22 @@ typedef enum kda_status {
     KDA_ERR_INVALID_ARG = 1,
     KDA_ERR_UNSUPPORTED = 2,
     KDA_ERR_WORKSPACE = 3,
-    KDA_ERR_HIP = 4
+    KDA_ERR_HIP = 4,
+    /* never returned: they stretch the enum's value range over all of int,
+     * so that any code a caller passes to kda_status_string is a valid
+     * kda_status (in C++ a value outside the range is undefined) */
+    KDA_STATUS_RANGE_MIN_ = -2147483647 - 1,
+    KDA_STATUS_RANGE_MAX_ = 2147483647
 } kda_status;
 
 typedef enum kda_dtype {
     KDA_F32 = 0,
-    KDA_BF16 = 1
+    KDA_BF16 = 1,
+    /* never valid: the same value range as kda_status, so that an unknown
+     * code reaches the argument checks (which reject it) with defined
+     * behaviour */
+    KDA_DTYPE_RANGE_MIN_ = -2147483647 - 1,
+    KDA_DTYPE_RANGE_MAX_ = 2147483647
 } kda_dtype;
 
 /*

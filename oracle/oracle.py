@@ -15,7 +15,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 ORACLE_SRC = os.path.join(_HERE, "kda_oracle.c")
-ORACLE_SO = os.path.join(_HERE, "libkda_oracle.so")
+# KDA_ORACLE_LIBRARY: another build of kda_oracle.c to load instead (the
+# sanitizer test's ASan/UBSan build); it is not rebuilt here
+ORACLE_SO = os.environ.get("KDA_ORACLE_LIBRARY") or os.path.join(_HERE, "libkda_oracle.so")
 
 _lib = None
 
@@ -30,6 +32,16 @@ def build_oracle(force: bool = True) -> str:
     subprocess.run(cmd, check=True)
     os.replace(tmp, ORACLE_SO)
     return ORACLE_SO
+
+
+def build_oracle_sanitized(path: str) -> str:
+    """Compile the oracle with gcc's AddressSanitizer and UndefinedBehavior-
+    Sanitizer (every report fatal) into `path`, for the host sanitizer test."""
+    cmd = ["gcc", "-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=all", "-fopenmp", "-fPIC", "-shared", "-std=c99",
+           "-o", path, ORACLE_SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    return path
 
 
 def _load():
