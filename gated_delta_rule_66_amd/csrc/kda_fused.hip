@@ -498,6 +498,20 @@ __global__ __launch_bounds__(512, 1) void kda_fused_kernel(FusedParams p) {
     // the wave's value columns of a chunk, row layout: lane (g, t) holds
     // V[16 ti + t][32 cw + 16 jt + 4 g + e]; loaded a chunk ahead
     u32x2 vq[4][2];
+    // the output gate of the chunk being finished, same layout as o (one token
+    // per lane, four consecutive columns), loaded in phase 1a
+    u32x2 zq[4][2];
+    auto load_zq = [&](int ci) {
+        const int nt = chunk_rows(ci);
+        const __amdgpu_buffer_rsrc_t rz = make_rsrc_n(
+            reinterpret_cast<const bf16*>(p.gate) + (((size_t)b * p.T + (size_t)ci * FC) * p.H + h) * FK,
+            nt > 0 ? (unsigned)(nt - 1) * rowK + FK * 2u : 0u);
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+            for (int jt = 0; jt < 2; ++jt)
+                zq[ti][jt] = ld_b64(rz, (unsigned)(16 * ti + lr) * rowK + (unsigned)(2 * (32 * cw + 16 * jt + 4 * lg)));
+    };
     auto load_vq = [&](int ci) {
         const __amdgpu_buffer_rsrc_t rv = chunk_rsrc(p.v, ci);
 #pragma unroll
@@ -627,8 +641,6 @@ __global__ __launch_bounds__(512, 1) void kda_fused_kernel(FusedParams p) {
             const size_t row0 = ((size_t)b * p.T + t0) * p.H + h;
             const unsigned span = (unsigned)(nt - 1) * rowK + FK * 2u;
             const __amdgpu_buffer_rsrc_t ro = make_rsrc_n(reinterpret_cast<bf16*>(p.o) + row0 * FK, span);
-            const __amdgpu_buffer_rsrc_t rz =
-                make_rsrc_n(GATE ? reinterpret_cast<const bf16*>(p.gate) + row0 * FK : nullptr, GATE ? span : 0u);
             // O^T += U^T Mqk^T per 16-token tile (the U fragments as the A
             // operand), rounded to bf16 and stored 8 bytes a lane (4 columns of
             // one token)
@@ -651,7 +663,7 @@ __global__ __launch_bounds__(512, 1) void kda_fused_kernel(FusedParams p) {
                     if (GATE) {
                         // output gate: o (rounded to bf16) * sigmoid(z), rounded once more
                         float z[4];
-                        unpack4(ld_b64(rz, voff), z);
+                        unpack4(zq[ti][jt], z);
 #pragma unroll
                         for (int e = 0; e < 4; ++e) o4[e] = (bf16)((float)o4[e] * sigmoidf_fast(z[e]));
                     }
@@ -702,6 +714,7 @@ __global__ __launch_bounds__(512, 1) void kda_fused_kernel(FusedParams p) {
         } else {
             t_tiles(ci);
             consume_a(ci, S[0], true, yb, accO);
+            if (GATE) load_zq(ci);
             __syncthreads();
             consume_b(ci, S[0], yb, true, accO);
             load_vq(ci + 1);
