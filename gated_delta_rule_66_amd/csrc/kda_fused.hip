@@ -70,6 +70,11 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_f(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, true));
 }
+// the gate clamp [-5, 0] as a [0, 1] clamp of g * kGateScale; kGateToLog2
+// turns sums of those back into log2 units
+constexpr float kGateScale = -0.2f;
+constexpr float kGateToLog2 = 1.4426950408889634f / -0.2f;
+
 // inclusive prefix sums over the 16 lanes of each DPP row (lanes r = 0..15),
 // of N independent values: each step over all of them before the next, so
 // that no DPP read waits on the add just before it (and no add is fused with
@@ -274,17 +279,20 @@ __global__ __launch_bounds__(512, 1) void kda_fused_kernel(FusedParams p) {
             f32x4 at = {0.f, 0.f, 0.f, 0.f}, mt = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int hv = 0; hv < 2; ++hv) {
-                // Gin (log2 units): the block's inclusive sums of the gate,
-                // clamped to [-5, 0]
+                // Gin: the block's inclusive sums of the gate clamped to [-5, 0],
+                // scanned as clamp(-g / 5) in [0, 1] (one multiply with the
+                // output clamp) and scaled to log2 units before the exponentials
                 float gin[16];
 #pragma unroll
                 for (int mm = 0; mm < 4; ++mm) {
                     float x[4];
                     unpack4(half_of(gr[2 * hv + (mm >> 1)], mm & 1), x);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) gin[4 * mm + e] = __builtin_amdgcn_fmed3f(x[e], -5.f, 0.f) * kLog2e;
+                    for (int e = 0; e < 4; ++e) gin[4 * mm + e] = __builtin_amdgcn_fmed3f(x[e] * kGateScale, 0.f, 1.f);
                 }
                 row_scan(gin);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) gin[i] *= kGateToLog2;
                 float kd[16], ki[16], qd[16], e1[16];
 #pragma unroll
                 for (int mm = 0; mm < 4; ++mm) {
@@ -436,7 +444,6 @@ __global__ __launch_bounds__(512, 1) void kda_fused_kernel(FusedParams p) {
             };
             if (pw == 0) {
                 pair(3, 0);
-                pair(1, 0);
             } else if (pw == 1) {
                 pair(2, 0);
             } else if (pw == 2) {
@@ -444,6 +451,7 @@ __global__ __launch_bounds__(512, 1) void kda_fused_kernel(FusedParams p) {
             } else {
                 pair(3, 2);
                 pair(2, 1);
+                pair(1, 0);
             }
         };
 
