@@ -55,10 +55,12 @@ PREFILL_WORKLOADS = ("prefill_1m", "prefill_32k_x8", "prefill_8k")
 
 # launches that write o (and read S0 / write S_T): the path's algorithmic
 # bytes are attributed to them; the two-pass plan's intra-chunk pass gets the
-# input reads; the fused plan's summary pass reads k, g, v and beta of every
-# segment but the last and writes two states per segment; the two-pass
-# summaries (which read the intra-chunk workspace), scans and copies are plan
-# overhead (zero)
+# input reads; a segmented fused call splits them: its first launch runs
+# segment 0 with output (all of that segment's bytes) beside the summaries of
+# segments 1 .. n_seg - 2 (k, g, v and beta read, two states written per
+# segment), its output launch the other segments; the two-pass summaries
+# (which read the intra-chunk workspace), scans and copies are plan overhead
+# (zero)
 OUTPUT_LAUNCHES = ("chunk_output", "state_output", "fused_output", "token_fwd")
 
 
@@ -88,13 +90,18 @@ def kernel_bytes(name, B, T, H, K, V, in_bytes, s0, final, two_pass, n_seg=1):
     writes = ht * in_bytes * V
     if name == "intra_chunk":
         return reads
+    n_chunks = (T + 63) // 64
+    cps = (n_chunks + n_seg - 1) // n_seg
+    t0 = min(cps * 64, T)                                 # tokens of segment 0
+    per_tok = in_bytes * (3 * K + V + 1) + in_bytes * V
+    if name == "fused_output" and n_seg > 1:
+        return B * (T - t0) * H * per_tok + B * H * K * V * 4 * int(final)
     if name in OUTPUT_LAUNCHES:
         return writes + states + (0 if two_pass else reads)
     if name == "fused_summary" and n_seg > 1:
-        n_chunks = (T + 63) // 64
-        cps = (n_chunks + n_seg - 1) // n_seg
-        covered = min((n_seg - 1) * cps * 64, T)          # tokens of the summarised segments
-        return B * covered * H * in_bytes * (2 * K + V + 1) + 2 * B * H * (n_seg - 1) * K * V * 4
+        covered = min((n_seg - 1) * cps * 64, T) - t0     # tokens of the summarised segments
+        return (B * t0 * H * per_tok + B * H * K * V * 4 * int(s0) +
+                B * covered * H * in_bytes * (2 * K + V + 1) + 2 * B * H * (n_seg - 1) * K * V * 4)
     return 0
 
 

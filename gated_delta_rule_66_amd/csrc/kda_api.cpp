@@ -116,9 +116,11 @@ kda_status resolve_plan(int B, int T, int H, int K, int V, kda_dtype dt, const k
                 kda_status s = device_cus(&cus);
                 if (s != KDA_OK) return s;
             }
+            // both passes of a segmented call run (n_seg - 1) workgroups per
+            // (b, h): n_seg - 1 = the (b, h) chains that fit the CUs once
             ns = 1;
-            if (bh > 0 && bh < cus) {
-                const long want = (cus + bh - 1) / bh;
+            if (bh > 0 && 2 * bh <= cus) {
+                const long want = cus / bh + 1;
                 const long cap = n_chunks / 4;
                 ns = (int)(want < cap ? want : cap);
                 if (ns < 1) ns = 1;
@@ -333,6 +335,8 @@ static kda_status chunk_impl(int B, int T, int H, int K, int V, kda_dtype dt,
         fp.B = B; fp.T = T; fp.H = H;
         fp.n_seg = pl.n_seg;
         fp.cps = cps;
+        fp.seg_first = 0;
+        fp.seg_count = pl.n_seg;
         if (pl.n_seg == 1) {
             fp.s0 = initial_state;
             fp.o = o;
@@ -345,17 +349,31 @@ static kda_status chunk_impl(int B, int T, int H, int K, int V, kda_dtype dt,
         float* wsP = ws;
         float* wsL = wsP + (size_t)(pl.n_seg - 1) * bh * K * K;
         float* wsFinal = wsL + (size_t)(pl.n_seg - 1) * bh * K * V;
-        // pass 1: per segment (but the last), transition P and local state L
+        // pass 1: segment 0 with its output (it needs no summary: its end
+        // state goes to the scan as L_0 with P_0 = 0) beside the transition P
+        // and local state L of segments 1 .. n_seg - 2; (n_seg - 1) workgroups
+        // per (b, h), as many as pass 3
+        FusedParams f0 = fp;
+        f0.s0 = initial_state;
+        f0.o = o;
+        f0.gate = gate;
+        f0.sT = nullptr;
+        f0.seg_first = 0;
+        f0.seg_count = 1;
+        f0.seg0_L = wsL;
+        f0.seg0_P = wsP;
         FusedParams f1 = fp;
         f1.wsP = wsP;
         f1.wsL = wsL;
+        f1.seg_first = 1;
+        f1.seg_count = pl.n_seg - 2;
         if (launch_timed("fused_summary", st, [&] {
-                return launch_fused(f1, true, (int)(bh * (pl.n_seg - 1)), st);
+                return launch_fused_first(f0, f1, (int)(bh * (pl.n_seg - 1)), st);
             }) != hipSuccess)
             return KDA_ERR_HIP;
-        // pass 2: segment start states
+        // pass 2: segment start states (S_1 = L_0)
         ScanParams scp{};
-        scp.s0 = initial_state;
+        scp.s0 = nullptr;
         scp.wsP = wsP;
         scp.wsL = wsL;
         scp.BH = (int)bh;
@@ -363,20 +381,18 @@ static kda_status chunk_impl(int B, int T, int H, int K, int V, kda_dtype dt,
         scp.n_seg = pl.n_seg;
         if (launch_timed("segment_scan", st, [&] { return launch_scan(K, scp, st); }) != hipSuccess)
             return KDA_ERR_HIP;
-        // pass 3: every segment from its true start state, with output
-        const bool aliased = final_state && final_state == initial_state;
+        // pass 3: segments 1 .. n_seg - 1 from their true start states, with
+        // output (S0 was read in pass 1, so the final state may overwrite it)
         FusedParams f3 = fp;
-        f3.s0 = initial_state;
         f3.seg_init = wsL;
         f3.o = o;
         f3.gate = gate;
-        f3.sT = aliased ? wsFinal : final_state;
+        f3.sT = final_state;
+        f3.seg_first = 1;
+        f3.seg_count = pl.n_seg - 1;
+        (void)wsFinal;
         if (launch_timed("fused_output", st, [&] {
-                return launch_fused(f3, false, (int)(bh * pl.n_seg), st);
-            }) != hipSuccess)
-            return KDA_ERR_HIP;
-        if (aliased && launch_timed("copy_state", st, [&] {
-                return launch_copy_state(wsFinal, final_state, (size_t)bh * K * V, st);
+                return launch_fused(f3, false, (int)(bh * (pl.n_seg - 1)), st);
             }) != hipSuccess)
             return KDA_ERR_HIP;
         return KDA_OK;

@@ -49,6 +49,10 @@ struct FusedParams {
     int B, T, H;
     int n_seg;              // segments of the sequence
     int cps;                // chunks per segment
+    int seg_first;          // this launch's segments of each (b, h): seg_first .. seg_first + seg_count - 1
+    int seg_count;
+    float* seg0_L;          // output pass: segment 0's end state (slot 0 of the summaries' L), or null
+    float* seg0_P;          // output pass: zeroed (slot 0 of the summaries' P), or null
 };
 
 // Arguments of the segment scan: S_{j+1} = P_j S_j + L_j, written over L_j.
@@ -191,6 +195,9 @@ hipError_t launch_state(int dtype, int K, int VB, const StateParams& p, int grid
 bool chunk_variant_exists(int dtype, int K, int VB);
 bool fused_variant_exists(int dtype, int K, int V);
 hipError_t launch_fused(const FusedParams& p, bool summary, int grid, hipStream_t stream);
+// segment 0 with output (po, the first po.B * po.H * po.seg_count workgroups)
+// beside the summaries ps, in one launch of `grid` workgroups
+hipError_t launch_fused_first(const FusedParams& po, const FusedParams& ps, int grid, hipStream_t stream);
 
 hipError_t launch_chunk(int dtype, int K, int VB, const ChunkParams& p, int grid,
                         hipStream_t stream);

@@ -30,7 +30,7 @@ def kernel_source_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(PKG, "csrc")
     for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h", ".cpp")):
+        if name.endswith((".hip", ".h", ".cpp", ".inc")):
             with open(os.path.join(csrc, name), "rb") as f:
                 h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
@@ -57,6 +57,9 @@ def launch_name(kernel_name: str):
     if "kda_state_kernel" in n:
         # <T, K, waves, tiles, SUMMARY, OUT, GATE>
         return "state_summary" if _first_bool(n, "kda_state_kernel") else "state_output"
+    if "kda_fused_first_kernel" in n:
+        # segment 0 with output beside the summaries: the summary launch
+        return "fused_summary"
     if "kda_fused_kernel" in n:
         # <SUMMARY, GATE>
         return "fused_summary" if _first_bool(n, "kda_fused_kernel") else "fused_output"

@@ -253,8 +253,11 @@ def test_p8_prefill_then_decode_equals_longer_prefill():
     assert s_err(s_p, st) < TOL[torch.bfloat16]
 
 
-@pytest.mark.parametrize("plan", [(1, 64, 1), (4, 64, 1), (1, 64, 2), (4, 64, 2)])
+@pytest.mark.parametrize("plan", [(1, 64, 1), (4, 64, 1), (1, 64, 2), (4, 64, 2), (1, 0, 4), (2, 0, 4), (4, 0, 4)])
 def test_in_place_state_resume(plan):
+    """The final state written over S0.  The fused plan with segments reads S0
+    in its first launch (segment 0 with output beside the summaries) and
+    writes the final state in its last; (2, 0, 4) has no summaries at all."""
     say("final_state aliasing initial_state plan=%s" % (plan,))
     d = make_prefill(1, 64 * 20 + 9, 2, 128, 128, torch.bfloat16, seed=17, s0_std=0.02)
     x = to_dev(d)

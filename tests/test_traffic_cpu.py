@@ -28,4 +28,6 @@ def test_other_kernels():
     assert launch_name("_ZN3kda16kda_fused_kernelILb0ELb0EEEvNS_11FusedParamsE") == "fused_output"
     assert launch_name("void kda::kda_fused_kernel<true, false>(kda::FusedParams)") == "fused_summary"
     assert launch_name("void kda::kda_fused_kernel<false, true>(kda::FusedParams)") == "fused_output"
+    assert launch_name("_ZN3kda22kda_fused_first_kernelILb0EEEvNS_11FusedParamsES1_") == "fused_summary"
+    assert launch_name("void kda::kda_fused_first_kernel<true>(kda::FusedParams, kda::FusedParams)") == "fused_summary"
     assert launch_name("void at::native::vectorized_elementwise_kernel<4>(...)") is None
