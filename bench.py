@@ -503,6 +503,9 @@ def main():
         "kernels": head["kernels"],
         "cpu_baseline": head.get("cpu_baseline"),
     }
+    for key in ("gate", "backward"):
+        if key in head:
+            line[key] = head[key]
     for w in workloads[1:]:
         line[w] = results[w]
     line["decode"] = dec

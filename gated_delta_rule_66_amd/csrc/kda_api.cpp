@@ -782,10 +782,11 @@ struct BwdLayout {
     size_t tok;                           // byte offset of the checkpoints and partial sums (token level)
     size_t total;                         // bytes
 };
-// fp32 values per chunk of the chunk-form intermediates: dU, D, dQh, dKb,
-// dW, rs, dKh, Et
-static size_t bwd_inter_floats(int K, int V) {
+// fp32 values per chunk of the chunk-form intermediates: dU, then (when the
+// three stages run as separate launches) D, dQh, dKb, dW, rs, dKh, Et
+static size_t bwd_inter_floats(int dt, int K, int V) {
     const size_t c = kChunk;
+    if (bwd_fused_variant_exists(dt, K, V)) return c * V;
     return c * V + c * c + 4 * c * K + K + c * c;
 }
 static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
@@ -817,7 +818,7 @@ static kda_status bwd_layout(int B, int T, int H, int K, int V, kda_dtype dt, Bw
     L->rec = o;   o += align256(bh * L->NC * record_bytes(K, V, dt));
     L->snaps = o; o += align256(bh * L->NC * kv);
     L->adj = o;   o += align256(bh * L->NC * kv);
-    L->inter = o; o += align256(bh * L->NC * bwd_inter_floats(K, V) * sizeof(float));
+    L->inter = o; o += align256(bh * L->NC * bwd_inter_floats((int)dt, K, V) * sizeof(float));
     L->total = o;
     return KDA_OK;
 }
@@ -946,7 +947,9 @@ kda_status kda_chunk_bwd(int B, int T, int H, int K, int V, kda_dtype dt,
         p.adj = reinterpret_cast<float*>(ws + L.adj);
         const size_t nch = (size_t)bh * NC, c = kChunk;
         float* f = reinterpret_cast<float*>(ws + L.inter);
+        const bool fused = bwd_fused_variant_exists((int)dt, K, V);
         p.cdU = f;  f += nch * c * V;
+        if (fused) f = nullptr;                 // no other intermediate
         p.cD = f;   f += nch * c * c;
         p.cdQh = f; f += nch * c * K;
         p.cdKb = f; f += nch * c * K;
@@ -980,6 +983,9 @@ kda_status kda_chunk_bwd(int B, int T, int H, int K, int V, kda_dtype dt,
         if (launch_timed("bwd_state_reverse", st, [&] { return launch_bwd_state(false, (int)dt, K, p, st); }) !=
             hipSuccess)
             return KDA_ERR_HIP;
+        if (fused)
+            return launch_timed("bwd_chunk_fused", st, [&] { return launch_bwd_fused(p, st); }) == hipSuccess
+                       ? KDA_OK : KDA_ERR_HIP;
         static const char* const stage_names[3] = {"bwd_value_side", "bwd_solve", "bwd_gated"};
         for (int stage = 0; stage < 3; ++stage)
             if (launch_timed(stage_names[stage], st, [&] { return launch_bwd_chunk(stage, (int)dt, K, V, p, st); }) !=

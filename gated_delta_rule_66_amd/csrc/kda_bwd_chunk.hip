@@ -46,7 +46,6 @@ namespace kda {
 namespace {
 
 constexpr int C = kChunk;
-constexpr float kLog2e = 1.4426950408889634f;
 
 constexpr int cmax2(int a, int b) { return a > b ? a : b; }
 
@@ -75,6 +74,54 @@ __device__ __forceinline__ void load_tok_pieces(const void* src, const BwdParams
         const unsigned off = i < C * PR ? (unsigned)t * rowb + (unsigned)sg * 16u : 0xffffffffu - 15u;
         r[m] = buf_load16(rs, off);
     }
+}
+// one bf16 element at byte offset off of a buffer (zero past its end)
+__device__ __forceinline__ float buf_bf16(__amdgpu_buffer_rsrc_t r, unsigned off) {
+    const unsigned short x = __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+    return __uint_as_float((unsigned)x << 16);
+}
+// a buffer over the rows [0, nt) of the token tile (tokens t0.., head h) of a
+// [B, T, H, N] bf16 tensor; row t starts at byte t * H * N * 2
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tok_rsrc(const void* src, const BwdParams& p, int b, int h, int t0,
+                                                          int nt, int N) {
+    const bf16* base = reinterpret_cast<const bf16*>(src) + (((size_t)b * p.T + t0) * p.H + h) * N;
+    return make_rsrc_n(base, nt > 0 ? (unsigned)(nt - 1) * (unsigned)(p.H * N * 2) + (unsigned)(N * 2) : 0u);
+}
+// fp32 products on bf16 MFMA: x = hi + lo with hi = bf16(x), lo = bf16(x - hi),
+// and a b = a.hi b.hi + a.hi b.lo + a.lo b.hi (the dropped a.lo b.lo and the
+// rounding of lo are below 2^-16 of |a b|)
+struct Split4 {
+    bf16x4 hi, lo;
+};
+__device__ __forceinline__ Split4 split4(f32x4 x) {
+    Split4 s;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        s.hi[i] = (bf16)x[i];
+        s.lo[i] = (bf16)(x[i] - (float)s.hi[i]);
+    }
+    return s;
+}
+// x as one word: bf16 hi in the upper half, bf16 lo in the lower
+__device__ __forceinline__ unsigned pack_hl(float x) {
+    const bf16 hi = (bf16)x;
+    const bf16 lo = (bf16)(x - (float)hi);
+    return ((unsigned)__builtin_bit_cast(unsigned short, hi) << 16) | (unsigned)__builtin_bit_cast(unsigned short, lo);
+}
+// four packed words (elements 0..3) as the hi and lo fragments
+__device__ __forceinline__ Split4 unpack_hl(unsigned w0, unsigned w1, unsigned w2, unsigned w3) {
+    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 h = {__builtin_amdgcn_perm(w1, w0, 0x07060302u), __builtin_amdgcn_perm(w3, w2, 0x07060302u)};
+    const u32x2 lo = {__builtin_amdgcn_perm(w1, w0, 0x05040100u), __builtin_amdgcn_perm(w3, w2, 0x05040100u)};
+    Split4 s;
+    s.hi = __builtin_bit_cast(bf16x4, h);
+    s.lo = __builtin_bit_cast(bf16x4, lo);
+    return s;
+}
+__device__ __forceinline__ f32x4 mma16x3(f32x4 acc, const Split4& a, const Split4& b) {
+    acc = mma16(acc, a.lo, b.hi);
+    acc = mma16(acc, a.hi, b.lo);
+    return mma16(acc, a.hi, b.hi);
 }
 // pieces [0, n) of a contiguous array
 template <int NP, int NT = 256>
@@ -808,6 +855,577 @@ __global__ __launch_bounds__(512) void kda_bwd_kgrad_kernel(BwdParams p) {
     }
 }
 
+// ============================================================================
+// fused: the three stages above in one workgroup per chunk (bf16, K = V = 128)
+// ============================================================================
+// Nothing between the stages leaves the workgroup: D, E and the Gram stay in
+// LDS, and dQh, dKb, dKh stay in the registers of the wave that uses them.
+// Wave w owns channel (and value) columns 16 w .. 16 w + 15 throughout:
+//   dQh = dO S^T, dKb = U dS'^T and dBk = -dBv S^T take their B operands
+//   from rows 16 w .. of S and dS', loaded straight into this wave's
+//   registers; the back substitution solves value column tile w; the gated
+//   products and the epilogue run on channel tile w.
+// dBk needs no solve of its own: W = (I + A)^{-1} diag(beta) K e^G enters
+// only through U = U~ - W S, so dW = -dU S^T and, the solve being linear,
+// (I + A)^{-T} dW = -((I + A)^{-T} dU) S^T = -dBv S^T.
+struct FusedBwdLayout {
+    static constexpr int K = 128, V = 128;
+    static constexpr int LDK = K + 8, LDV = V + 8, LDC = C + 8;     // bf16 row strides
+    static constexpr int LDA = C + 4, LDG = K + 4, LDDG = K + 1;     // fp32 row strides
+    static constexpr int oA = 0;                  // S^T [V][LDK] | Ak^T, D (hi|lo words) [C][LDA] | dG [C][LDDG]
+    static constexpr int oAkT = oA, oD = oA + C * LDA * 4;
+    static constexpr int oW = oA + V * LDK * 2;   // W [C][LDK] | diag(beta) E (hi|lo words) [C][LDA]
+    static constexpr int oUt = oW + C * LDK * 2;  // U~^T [V][LDC] | column sums fp32 [5][K], E.Ak partial sums [C][4]
+    static constexpr int oDO = oUt + V * LDC * 2; // dO [C][LDV] | dBv [C][LDV]
+    static constexpr int oK = oDO + C * LDV * 2;  // k [C][LDK]
+    static constexpr int oG = oK + C * LDK * 2;   // G fp32 [C][LDG] (log2 units)
+    static constexpr int oU = oG + C * LDG * 4;   // U [C][LDV] | dBk [C][LDK]
+    static constexpr int oR = oU + C * LDV * 2;   // R fp32 [5][K]
+    static constexpr int oM = oR + 5 * K * 4;     // clamp pass mask: [C][K / 64] bits
+    static constexpr int oB = oM + C * (K / 64) * 8;  // beta fp32 [C]
+    static constexpr int oTot = oB + C * 4;       // gate totals of the four token blocks fp32 [4][K]
+    static constexpr int TOTAL = oTot + 4 * K * 4;
+    static_assert(2 * C * LDA * 4 <= V * LDK * 2 && C * LDDG * 4 <= V * LDK * 2, "region A");
+    static_assert(C * LDA * 4 <= C * LDK * 2, "E over W");
+    static_assert(5 * K * 4 + C * 4 * 4 <= V * LDC * 2, "column sums and E.Ak sums over U~^T");
+    static_assert(C * LDK <= C * LDV, "dBk over U");
+    static_assert(TOTAL <= 160 * 1024, "LDS budget exceeded");
+};
+
+__global__ __launch_bounds__(512, 1) void kda_bwd_fused_kernel(BwdParams p) {
+    using L = FusedBwdLayout;
+    using T = bf16;
+    constexpr int K = L::K, V = L::V;
+    constexpr int LDK = L::LDK, LDV = L::LDV, LDC = L::LDC, LDA = L::LDA, LDG = L::LDG, LDDG = L::LDDG;
+    constexpr int NT = 512;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
+    T* sST = reinterpret_cast<T*>(smem + L::oA);
+    float* sAkT = reinterpret_cast<float*>(smem + L::oAkT);
+    unsigned* sD = reinterpret_cast<unsigned*>(smem + L::oD);
+    float* sDG = reinterpret_cast<float*>(smem + L::oA);
+    T* sW = reinterpret_cast<T*>(smem + L::oW);
+    unsigned* sE = reinterpret_cast<unsigned*>(smem + L::oW);
+    T* sUt = reinterpret_cast<T*>(smem + L::oUt);
+    float* sCS = reinterpret_cast<float*>(smem + L::oUt);
+    float* sPE = sCS + 5 * K;                      // [C][4]: sum_r E[s][r] Ak[s][r] over key block j
+    T* sDO = reinterpret_cast<T*>(smem + L::oDO);
+    T* sBV = reinterpret_cast<T*>(smem + L::oDO);
+    T* sK = reinterpret_cast<T*>(smem + L::oK);
+    float* sG = reinterpret_cast<float*>(smem + L::oG);
+    T* sU = reinterpret_cast<T*>(smem + L::oU);
+    T* sBK = reinterpret_cast<T*>(smem + L::oU);
+    float* sR = reinterpret_cast<float*>(smem + L::oR);
+    unsigned long long* sM = reinterpret_cast<unsigned long long*>(smem + L::oM);
+    float* sB = reinterpret_cast<float*>(smem + L::oB);
+    float* sTot = reinterpret_cast<float*>(smem + L::oTot);
+
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lg = l >> 4, lr = l & 15;
+    const int cw = 16 * w + lr;                   // this lane's channel / value column
+    const int NC = p.NC;
+    const int item = blockIdx.x;                  // (b * H + h) * NC + chunk
+    const int ci = item % NC, bh = item / NC;
+    const int b = bh / p.H, h = bh % p.H;
+    const int t0 = ci * C, nt = min(C, p.T - t0);
+    const size_t KV = (size_t)K * V;
+    const size_t rowK = (size_t)p.H * K;          // token stride of [B, T, H, K] (and V = K)
+    const RecLayout RL = rec_layout(K, V, 2);
+    const unsigned char* rec = p.rec + (size_t)item * RL.bytes;
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+
+    // ---- global loads, all issued before any is waited on ---------------------------
+    // rows cw of S (chunk start) and dS' (chunk end): lane group lg holds
+    // columns 32 ks + 4 lg + {0..3} and 32 ks + 16 + 4 lg + {0..3} (permuted slots)
+    uint4 rS[8], rDS[8];
+    {
+        const float* S0 = ci == 0 ? (p.s0 ? p.s0 + (size_t)bh * KV : nullptr)
+                                  : p.snaps + (((size_t)b * NC + ci - 1) * p.H + h) * KV;
+        const float* dSp = ci == NC - 1 ? (p.dsT ? p.dsT + (size_t)bh * KV : nullptr) : p.adj + (size_t)item * KV;
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc_n(S0, S0 ? (unsigned)(KV * 4) : 0u);
+        const __amdgpu_buffer_rsrc_t rd = make_rsrc_n(dSp, dSp ? (unsigned)(KV * 4) : 0u);
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const unsigned off = (unsigned)(cw * V + 32 * (m >> 1) + 16 * (m & 1) + 4 * lg) * 4u;
+            rS[m] = buf_load16(rs, off);
+            rDS[m] = buf_load16(rd, off);
+        }
+    }
+    uint4 rw[2], ru[2], ro[2], rk[2];
+    load_flat_pieces<2, NT>(rec + RL.oW, C * K * 2 / 16, rw, tid);
+    load_flat_pieces<2, NT>(rec + RL.oUtT, V * C * 2 / 16, ru, tid);
+    load_tok_pieces<T, V, 2, NT>(p.d_o, p, b, h, t0, nt, ro, tid);
+    load_tok_pieces<T, K, 2, NT>(p.k, p, b, h, t0, nt, rk, tid);
+    const float egc_c = reinterpret_cast<const float*>(rec + RL.oEgc)[cw];
+    // raw gates of channel gc, tokens 16 gp .. 16 gp + 15 (zeros past the end)
+    const int gc = tid & (K - 1), gp = tid >> 7;
+    float graw[16];
+    {
+        const __amdgpu_buffer_rsrc_t rg = tok_rsrc(p.g, p, b, h, t0, nt, K);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) graw[i] = buf_bf16(rg, (unsigned)((16 * gp + i) * rowK + gc) * 2u);
+    }
+    float beta_t;
+    {
+        const T* bb = reinterpret_cast<const T*>(p.beta) + ((size_t)b * p.T + t0) * p.H + h;
+        const __amdgpu_buffer_rsrc_t rb = make_rsrc_n(bb, nt > 0 ? (unsigned)((nt - 1) * p.H + 1) * 2u : 0u);
+        beta_t = buf_bf16(rb, (unsigned)(tid * p.H) * 2u);   // zero from token nt on
+    }
+    // ---- stage 0: operands to LDS; S, dS' fragments; rs; gate scan within blocks ----
+    typename FragOf<T>::type fS[4], fD[4];
+    float rsp = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        float s8[8], d8[8];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const uint4 a = rS[2 * ks + hh], d = rDS[2 * ks + hh];
+            s8[4 * hh + 0] = __uint_as_float(a.x); s8[4 * hh + 1] = __uint_as_float(a.y);
+            s8[4 * hh + 2] = __uint_as_float(a.z); s8[4 * hh + 3] = __uint_as_float(a.w);
+            d8[4 * hh + 0] = __uint_as_float(d.x); d8[4 * hh + 1] = __uint_as_float(d.y);
+            d8[4 * hh + 2] = __uint_as_float(d.z); d8[4 * hh + 3] = __uint_as_float(d.w);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) rsp += s8[e] * d8[e];
+        fS[ks] = frag_from<T>(s8);
+        fD[ks] = frag_from<T>(d8);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            sST[(32 * ks + 4 * lg + e) * LDK + cw] = fS[ks][e];
+            sST[(32 * ks + 16 + 4 * lg + e) * LDK + cw] = fS[ks][4 + e];
+        }
+    }
+    rsp += __shfl_xor(rsp, 16);
+    rsp += __shfl_xor(rsp, 32);
+    const float rs_c = egc_c * rsp;               // e^{G_C} sum_v S[cw][v] dS'[cw][v]
+    store_pieces<2, NT>(sW, LDK * 2, K * 2 / 16, C * K * 2 / 16, rw, tid);
+    store_pieces<2, NT>(sUt, LDC * 2, C * 2 / 16, V * C * 2 / 16, ru, tid);
+    store_pieces<2, NT>(sDO, LDV * 2, V * 2 / 16, C * V * 2 / 16, ro, tid);
+    store_pieces<2, NT>(sK, LDK * 2, K * 2 / 16, C * K * 2 / 16, rk, tid);
+    if (tid < C) sB[tid] = beta_t;
+    float gx[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        gx[i] = fminf(fmaxf(graw[i], -5.f), 0.f) * kLog2e + (i ? gx[i - 1] : 0.f);
+        // the clamp passes the gradient where the raw gate lies in [-5, 0]
+        const unsigned long long pass = __ballot(graw[i] >= -5.f && graw[i] <= 0.f);
+        if (l == 0) sM[(16 * gp + i) * 2 + (w & 1)] = pass;
+    }
+    sTot[gp * K + gc] = gx[15];
+    __syncthreads();
+
+    // ---- stage 1: G and the references R_j; U = U~ - W S ----------------------------
+    {
+        float off = 0.f;
+#pragma unroll
+        for (int q = 0; q < 3; ++q)
+            if (q < gp) off += sTot[q * K + gc];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sG[(16 * gp + i) * LDG + gc] = off + gx[i];
+        sR[gp * K + gc] = off;
+        if (gp == 3) sR[4 * K + gc] = off + gx[15];
+    }
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti) {
+        f32x4 acc = ld4_as_f32<T>(&sUt[cw * LDC + 16 * ti + 4 * lg]);      // U~[16 ti + 4 lg + e][cw]
+        f32x4 m = z;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            m = mma(m, ld_frag_perm<T>(&sW[(16 * ti + lr) * LDK + 32 * ks + 4 * lg]),
+                    ld_frag_perm<T>(&sST[cw * LDK + 32 * ks + 4 * lg]));
+        acc = acc - m;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sU[(16 * ti + 4 * lg + e) * LDV + cw] = from_f32<T>(acc[e]);
+    }
+    __syncthreads();
+
+    // ---- stage 2: the gated Gram Ak; D = tril(dO U^T); dQh = dO S^T; dKb = U dS'^T ----
+    // loads for the later stages, issued here so that they are not held
+    // through the first ones
+    // right-hand side of the solve: dU (fp32) of value column cw, accumulator layout
+    f32x4 R[4];
+    {
+        const float* dUg = p.cdU + (size_t)item * C * V + cw;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) R[j][e] = dUg[(size_t)(16 * j + 4 * lg + e) * V];
+    }
+    auto pair_ij = [](int pr, int& i, int& j) {
+        i = 0;
+        j = pr;
+        while (j > i) { j -= i + 1; ++i; }
+    };
+    for (int pr = w; pr < 10; pr += 8) {
+        int i, j;
+        pair_ij(pr, i, j);
+        f32x4 acc = z;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            typename FragOf<T>::type fa, fb;
+            const int s = 16 * i + lr, r = 16 * j + lr;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int c = 32 * ks + 4 * lg + (u & 3) + (u >> 2) * 16;
+                const float ri = sR[i * K + c];
+                fa[u] = from_f32<T>(to_f32(sK[s * LDK + c]) * fast_exp2(sG[s * LDG + c] - ri));
+                fb[u] = from_f32<T>(to_f32(sK[r * LDK + c]) * fast_exp2(ri - sG[r * LDG + c]));
+            }
+            acc = mma(acc, fa, fb);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int s = 16 * i + 4 * lg + e, r = 16 * j + lr;
+            if (r < s) sAkT[r * LDA + s] = acc[e];
+        }
+    }
+    auto d_block = [&](int dd) {
+        int i, j;
+        pair_ij(dd, i, j);
+        f32x4 acc = z;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            acc = mma(acc, ld_frag_perm<T>(&sDO[(16 * i + lr) * LDV + 32 * ks + 4 * lg]),
+                      ld_frag_perm<T>(&sU[(16 * j + lr) * LDV + 32 * ks + 4 * lg]));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int t = 16 * i + 4 * lg + e, s = 16 * j + lr;
+            sD[t * LDA + s] = s <= t ? pack_hl(acc[e]) : 0u;
+        }
+    };
+    d_block(w);
+    if (w >= 6) d_block(15 - w);
+    f32x4 qh[4], kb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        qh[i] = z;
+        kb[i] = z;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            qh[i] = mma(qh[i], ld_frag_perm<T>(&sDO[(16 * i + lr) * LDV + 32 * ks + 4 * lg]), fS[ks]);
+            kb[i] = mma(kb[i], ld_frag_perm<T>(&sU[(16 * i + lr) * LDV + 32 * ks + 4 * lg]), fD[ks]);
+        }
+    }
+    __syncthreads();
+
+    // ---- stage 3: T_j = (I + A_jj)^{-1}, A = diag(beta) Ak, by forward substitution --
+    // q of channel cw at tokens 16 i + 4 lg + e (gated products, epilogue)
+    float qv[4][4];
+    {
+        const __amdgpu_buffer_rsrc_t rq = tok_rsrc(p.q, p, b, h, t0, nt, K);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                qv[i][e] = buf_bf16(rq, (unsigned)((16 * i + 4 * lg + e) * rowK + cw) * 2u);
+    }
+    // v of token tid / 8, columns 16 (tid % 8) .. + 15 (dbeta)
+    uint4 rv[2];
+    {
+        const __amdgpu_buffer_rsrc_t rvs = tok_rsrc(p.v, p, b, h, t0, nt, V);
+        const unsigned off = (unsigned)((tid >> 3) * rowK + 16 * (tid & 7)) * 2u;
+        rv[0] = buf_load16(rvs, off);
+        rv[1] = buf_load16(rvs, off + 16u);
+    }
+    // T_j^T goes to a block of Ak^T below the diagonal (never written or read otherwise)
+    auto tblock = [&](int j) {
+        const int I = j < 3 ? j + 1 : 2, J = j < 3 ? 0 : 1;
+        return sAkT + 16 * I * LDA + 16 * J;
+    };
+    if (tid < 64) {
+        const int j = tid >> 4, c = tid & 15;
+        float tc[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) tc[r] = (float)(r == c);
+#pragma unroll
+        for (int r = 1; r < 16; ++r) {
+            float a = 0.f;
+#pragma unroll
+            for (int m = 0; m < r; ++m) a += sAkT[(16 * j + m) * LDA + 16 * j + r] * tc[m];
+            const float v = -sB[16 * j + r] * a;
+            tc[r] = r > c ? v : tc[r];
+        }
+        float* tt = tblock(j) + c * LDA;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) tt[r] = tc[r];
+    }
+    __syncthreads();
+
+    // ---- stage 4: (I + A)^T dBv = dU for value column tile w; dv -------------------
+    {
+        f32x4 X[4];
+#pragma unroll
+        for (int j = 3; j >= 0; --j) {
+            f32x4 acc = R[j];
+#pragma unroll
+            for (int i = j + 1; i < 4; ++i) {
+                const f32x4 ak = *reinterpret_cast<const f32x4*>(&sAkT[(16 * j + lr) * LDA + 16 * i + 4 * lg]);
+                const f32x4 bt = *reinterpret_cast<const f32x4*>(&sB[16 * i + 4 * lg]);
+                acc = mma16(acc, -(ak * bt), X[i]);
+            }
+            X[j] = mma16(z, *reinterpret_cast<const f32x4*>(tblock(j) + lr * LDA + 4 * lg), acc);
+        }
+        T* dvp = reinterpret_cast<T*>(p.dv) + (((size_t)b * p.T + t0) * p.H + h) * V + cw;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int s = 16 * j + 4 * lg + e;
+                const float x = X[j][e];
+                sBV[s * LDV + cw] = from_f32<T>(x);
+                if (s < nt) dvp[(size_t)s * rowK] = from_f32<T>(sB[s] * x);
+            }
+    }
+    __syncthreads();
+
+    // ---- stage 5: dBk = -dBv S^T for channel tile w; dKh = diag(beta) dBk -----------
+    f32x4 dkh[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f32x4 a = z;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) a = mma(a, ld_frag_perm<T>(&sBV[(16 * i + lr) * LDV + 32 * ks + 4 * lg]), fS[ks]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int s = 16 * i + 4 * lg + e;
+            sBK[s * LDK + cw] = from_f32<T>(-a[e]);
+            dkh[i][e] = -sB[s] * a[e];
+        }
+    }
+    __syncthreads();
+
+    // ---- stage 6: E = -(dBv U~^T + dBk W^T), strictly lower; diag(beta) E kept split --
+    {
+        f32x4 eacc[2];
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            const int pr = w + 8 * n;
+            if (pr >= 10) break;
+            int i, j;
+            pair_ij(pr, i, j);
+            f32x4 acc = z;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                typename FragOf<T>::type fb;
+                const T* u0 = sUt + (32 * ks + 4 * lg) * LDC + 16 * j + lr;
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    fb[u] = u0[u * LDC];
+                    fb[4 + u] = u0[(16 + u) * LDC];
+                }
+                acc = mma(acc, ld_frag_perm<T>(&sBV[(16 * i + lr) * LDV + 32 * ks + 4 * lg]), fb);
+            }
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                acc = mma(acc, ld_frag_perm<T>(&sBK[(16 * i + lr) * LDK + 32 * ks + 4 * lg]),
+                          ld_frag_perm<T>(&sW[(16 * j + lr) * LDK + 32 * ks + 4 * lg]));
+            eacc[n] = -acc;
+        }
+        __syncthreads();                          // W and U~^T are no longer read: E goes over W
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            const int pr = w + 8 * n;
+            if (pr >= 10) break;
+            int i, j;
+            pair_ij(pr, i, j);
+            // and dbeta's sum_r E[s][r] Ak[s][r] over this key block (16 lanes per row)
+            f32x4 pe;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int s = 16 * i + 4 * lg + e, r = 16 * j + lr;
+                const float ev = r < s ? eacc[n][e] : 0.f;
+                sE[s * LDA + r] = pack_hl(sB[s] * ev);
+                pe[e] = r < s ? ev * sAkT[r * LDA + s] : 0.f;
+            }
+#pragma unroll
+            for (int x = 1; x < 16; x <<= 1)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) pe[e] += __shfl_xor(pe[e], x);
+            if (lr == 0)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sPE[(16 * i + 4 * lg + e) * 4 + j] = pe[e];
+        }
+    }
+    __syncthreads();
+
+    // ---- stage 7: dbeta; the gated products and dq, dk, dG --------------------------
+    {
+        // eight threads per token, each on an eighth of the value and key columns
+        const int s = tid >> 3, part = tid & 7;
+        float acc = 0.f;
+        if (s < nt) {
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int v = 16 * part + 8 * u;
+                const typename FragOf<T>::type a = ld_frag<T>(&sBV[s * LDV + v]);
+                const uint4 pv = rv[u];
+                const unsigned pw[4] = {pv.x, pv.y, pv.z, pv.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    acc += to_f32(a[2 * e]) * __uint_as_float(pw[e] << 16);
+                    acc += to_f32(a[2 * e + 1]) * __uint_as_float(pw[e] & 0xffff0000u);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int c = 16 * part + 8 * u;
+                const typename FragOf<T>::type a = ld_frag<T>(&sBK[s * LDK + c]), kk = ld_frag<T>(&sK[s * LDK + c]);
+                float gv[8];
+                ld8f(&sG[s * LDG + c], gv);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc += to_f32(a[e]) * to_f32(kk[e]) * fast_exp2(gv[e]);
+            }
+            // the key blocks j <= s / 16 hold the E.Ak sums of token s
+            if (part <= (s >> 4)) acc += sPE[s * 4 + part];
+        }
+        acc += __shfl_xor(acc, 1);
+        acc += __shfl_xor(acc, 2);
+        acc += __shfl_xor(acc, 4);
+        if (part == 0 && s < nt)
+            reinterpret_cast<T*>(p.dbeta)[((size_t)b * p.T + t0 + s) * p.H + h] = from_f32<T>(acc);
+    }
+    f32x4 dgr[4];
+    {
+        // per token t = 16 i + 4 lg + e of channel cw (R_i the reference of its block):
+        //   ep = e^{G_t - R_i} <= 1,  em = e^{R_i - G_t} (>= 1, below e^80 at the clamp floor)
+        // and the key / query operands of the gated products, split once per block:
+        //   km_i = k em (forward type),  kp_i = k ep, qp_i = q ep (transposed type)
+        float kv[4][4], ep[4][4], em[4][4], gl[4][4];
+        float Rr[5];
+#pragma unroll
+        for (int j = 0; j < 5; ++j) Rr[j] = sR[j * K + cw];
+        Split4 km[4], kp[4], qp[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f32x4 a, b2, c2;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = 16 * i + 4 * lg + e;
+                kv[i][e] = to_f32(sK[t * LDK + cw]);
+                gl[i][e] = sG[t * LDG + cw];
+                ep[i][e] = fast_exp2(gl[i][e] - Rr[i]);
+                em[i][e] = fast_exp2(Rr[i] - gl[i][e]);
+                a[e] = kv[i][e] * em[i][e];
+                b2[e] = kv[i][e] * ep[i][e];
+                c2[e] = qv[i][e] * ep[i][e];
+            }
+            km[i] = split4(a);
+            kp[i] = split4(b2);
+            qp[i] = split4(c2);
+        }
+        // e^{R_a - R_b} (a > b, <= 1) between block references
+        float xr[5][5];
+#pragma unroll
+        for (int a2 = 1; a2 < 5; ++a2)
+#pragma unroll
+            for (int b3 = 0; b3 < a2; ++b3) xr[a2][b3] = fast_exp2(Rr[a2] - Rr[b3]);
+        T* dqo = reinterpret_cast<T*>(p.dq) + (((size_t)b * p.T + t0) * p.H + h) * K + cw;
+        T* dko = reinterpret_cast<T*>(p.dk) + (((size_t)b * p.T + t0) * p.H + h) * K + cw;
+        const float RC = Rr[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            // forward type on token block i: Y1 = D (k gated), X1 = Et (k gated).
+            // Key block j enters with k e^{R_j - G_s} and the factor e^{R_i - R_j}.
+            f32x4 y1, x1;
+            {
+                const uint4 dw = *reinterpret_cast<const uint4*>(&sD[(16 * i + lr) * LDA + 16 * i + 4 * lg]);
+                const uint4 ew = *reinterpret_cast<const uint4*>(&sE[(16 * i + lr) * LDA + 16 * i + 4 * lg]);
+                y1 = mma16x3(z, unpack_hl(dw.x, dw.y, dw.z, dw.w), km[i]);
+                x1 = mma16x3(z, unpack_hl(ew.x, ew.y, ew.z, ew.w), km[i]);
+            }
+#pragma unroll
+            for (int j = 0; j < i; ++j) {
+                const uint4 dw = *reinterpret_cast<const uint4*>(&sD[(16 * i + lr) * LDA + 16 * j + 4 * lg]);
+                const uint4 ew = *reinterpret_cast<const uint4*>(&sE[(16 * i + lr) * LDA + 16 * j + 4 * lg]);
+                const f32x4 tD = mma16x3(z, unpack_hl(dw.x, dw.y, dw.z, dw.w), km[j]);
+                const f32x4 tE = mma16x3(z, unpack_hl(ew.x, ew.y, ew.z, ew.w), km[j]);
+                y1 += xr[i][j] * tD;
+                x1 += xr[i][j] * tE;
+            }
+            // transposed type on token block i: Y2 = D^T (q gated), X2 = Et^T (k gated).
+            // Token block i2 enters with q e^{G_t - R_i2}; for i2 > i, the factor
+            // e^{R_i2 - R_{i+1}} brings it to the reference R_{i+1}.
+            f32x4 y2d, x2d, y2o = z, x2o = z;
+#pragma unroll
+            for (int i2 = i; i2 < 4; ++i2) {
+                unsigned dwv[4], ewv[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int t = 16 * i2 + 4 * lg + u;
+                    dwv[u] = sD[t * LDA + 16 * i + lr];
+                    ewv[u] = sE[t * LDA + 16 * i + lr];
+                }
+                const f32x4 tY = mma16x3(z, unpack_hl(dwv[0], dwv[1], dwv[2], dwv[3]), qp[i2]);
+                const f32x4 tX = mma16x3(z, unpack_hl(ewv[0], ewv[1], ewv[2], ewv[3]), kp[i2]);
+                if (i2 == i) {
+                    y2d = tY;
+                    x2d = tX;
+                } else {
+                    const float f = i2 == i + 1 ? 1.f : xr[i2][i + 1];
+                    y2o += f * tY;
+                    x2o += f * tX;
+                }
+            }
+            const float gi = i < 3 ? xr[i + 1][i] : 1.f;     // e^{R_{i+1} - R_i}
+            // epilogue on tokens t = 16 i + 4 lg + e, channel cw
+            float colpart = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = 16 * i + 4 * lg + e;
+                const float g = gl[i][e];
+                const float eg = fast_exp2(g), egc = fast_exp2(RC - g);
+                const float Y1 = ep[i][e] * y1[e], X1 = ep[i][e] * x1[e];
+                const float Y2 = em[i][e] * (y2d[e] + gi * y2o[e]);
+                const float X2 = em[i][e] * (x2d[e] + gi * x2o[e]);
+                const float kk = kv[i][e], qq = qv[i][e];
+                const float dQh = qh[i][e], dKb = kb[i][e], dKh = dkh[i][e];
+                const float kbar = kk * egc;
+                dgr[i][e] = dQh * qq * eg + dKh * kk * eg - dKb * kbar + kk * (X1 - X2 - Y2) + qq * Y1;
+                colpart += dKb * kbar;
+                if (t < nt) {
+                    dqo[(size_t)t * rowK] = from_f32<T>(dQh * eg + Y1);
+                    dko[(size_t)t * rowK] = from_f32<T>(dKh * eg + X1 + X2 + Y2 + dKb * egc);
+                }
+            }
+            colpart += __shfl_xor(colpart, 16);
+            colpart += __shfl_xor(colpart, 32);
+            if (lg == 0) sCS[i * K + cw] = colpart;
+        }
+        if (lg == 0) sCS[4 * K + cw] = rs_c;
+    }
+    __syncthreads();                              // Ak^T and D are no longer read: dG goes over them
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sDG[(16 * i + 4 * lg + e) * LDDG + cw] = dgr[i][e];
+    __syncthreads();
+
+    // ---- stage 8: dg = mask * (reverse cumsum of dG over the chunk + the G_C terms) ---
+    {
+        // four threads per channel, each on a 16-token block
+        const int c = tid >> 2, part = tid & 3;
+        float dv16[16], sum = 0.f;
+#pragma unroll
+        for (int i = 15; i >= 0; --i) {
+            dv16[i] = sDG[(16 * part + i) * LDDG + c];
+            sum += dv16[i];
+        }
+        const int base = l & ~3;
+        float tot = sCS[4 * K + c] + sCS[c] + sCS[K + c] + sCS[2 * K + c] + sCS[3 * K + c];
+#pragma unroll
+        for (int q = 3; q >= 1; --q) {
+            const float sq = __shfl(sum, base + q);
+            if (q > part) tot += sq;
+        }
+        T* dgo = reinterpret_cast<T*>(p.dg) + (((size_t)b * p.T + t0) * p.H + h) * K + c;
+#pragma unroll
+        for (int i = 15; i >= 0; --i) {
+            const int t = 16 * part + i;
+            tot += dv16[i];
+            const bool pass = (sM[t * 2 + (c >> 6)] >> (c & 63)) & 1ull;
+            if (t < nt) dgo[(size_t)t * rowK] = from_f32<T>(pass ? tot : 0.f);
+        }
+    }
+}
+
 // ---- launchers ---------------------------------------------------------------------
 template <typename T, int K, int V>
 static hipError_t launch_bwd_chunk_t(int stage, const BwdParams& p, hipStream_t stream) {
@@ -843,6 +1461,16 @@ hipError_t launch_bwd_chunk(int stage, int dtype, int K, int V, const BwdParams&
         if (K == 64 && V == 64) return launch_bwd_chunk_t<float, 64, 64>(stage, p, stream);
     }
     return hipErrorInvalidValue;
+}
+
+bool bwd_fused_variant_exists(int dtype, int K, int V) { return dtype == 1 && K == 128 && V == 128; }
+
+hipError_t launch_bwd_fused(const BwdParams& p, hipStream_t stream) {
+    const long n = (long)p.B * p.H * p.NC;
+    if (n <= 0) return hipSuccess;
+    if (n > 2000000000L) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(kda_bwd_fused_kernel, dim3((unsigned)n), dim3(512), 0, stream, p);
+    return hipGetLastError();
 }
 
 }  // namespace kda

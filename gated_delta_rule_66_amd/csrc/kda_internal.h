@@ -263,6 +263,10 @@ hipError_t launch_bwd_state(bool summary, int dtype, int K, const BwdParams& p, 
 // substitution (dv, dbeta), 2 gated products (dq, dk, dg)
 bool bwd_chunk_variant_exists(int dtype, int K, int V);
 hipError_t launch_bwd_chunk(int stage, int dtype, int K, int V, const BwdParams& p, hipStream_t stream);
+// the three stages in one launch, one workgroup per chunk (needs p.rec,
+// p.snaps, p.adj, p.cdU; no other intermediate): bf16 with K = V = 128
+bool bwd_fused_variant_exists(int dtype, int K, int V);
+hipError_t launch_bwd_fused(const BwdParams& p, hipStream_t stream);
 size_t bwd_workspace_bytes(int B, int T, int H, int K, int V);
 hipError_t launch_decode_multi(int dtype, int K, int V, const MultiDecodeParams& p, hipStream_t stream);
 
