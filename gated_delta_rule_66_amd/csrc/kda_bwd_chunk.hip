@@ -123,6 +123,11 @@ __device__ __forceinline__ f32x4 mma16x3(f32x4 acc, const Split4& a, const Split
     acc = mma16(acc, a.hi, b.lo);
     return mma16(acc, a.hi, b.hi);
 }
+// x of the lane N places further round its row of 16 lanes (DPP row_ror)
+template <int N>
+__device__ __forceinline__ float row_ror_f(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + N, 0xf, 0xf, false));
+}
 // pieces [0, n) of a contiguous array
 template <int NP, int NT = 256>
 __device__ __forceinline__ void load_flat_pieces(const void* src, int n, uint4 (&r)[NP], int tid) {
@@ -875,7 +880,7 @@ struct FusedBwdLayout {
     static constexpr int oA = 0;                  // S^T [V][LDK] | Ak^T, D (hi|lo words) [C][LDA] | dG [C][LDDG]
     static constexpr int oAkT = oA, oD = oA + C * LDA * 4;
     static constexpr int oW = oA + V * LDK * 2;   // W [C][LDK] | diag(beta) E (hi|lo words) [C][LDA]
-    static constexpr int oUt = oW + C * LDK * 2;  // U~^T [V][LDC] | column sums fp32 [5][K], E.Ak partial sums [C][4]
+    static constexpr int oUt = oW + C * LDK * 2;  // U~^T [V][LDC] | column sums fp32 [4][K], E.Ak partial sums [C][4]
     static constexpr int oDO = oUt + V * LDC * 2; // dO [C][LDV] | dBv [C][LDV]
     static constexpr int oK = oDO + C * LDV * 2;  // k [C][LDK]
     static constexpr int oG = oK + C * LDK * 2;   // G fp32 [C][LDG] (log2 units)
@@ -883,11 +888,11 @@ struct FusedBwdLayout {
     static constexpr int oR = oU + C * LDV * 2;   // R fp32 [5][K]
     static constexpr int oM = oR + 5 * K * 4;     // clamp pass mask: [C][K / 64] bits
     static constexpr int oB = oM + C * (K / 64) * 8;  // beta fp32 [C]
-    static constexpr int oTot = oB + C * 4;       // gate totals of the four token blocks fp32 [4][K]
+    static constexpr int oTot = oB + C * 4;       // gate totals of the four token blocks fp32 [4][K] | rs at [3][K]
     static constexpr int TOTAL = oTot + 4 * K * 4;
     static_assert(2 * C * LDA * 4 <= V * LDK * 2 && C * LDDG * 4 <= V * LDK * 2, "region A");
     static_assert(C * LDA * 4 <= C * LDK * 2, "E over W");
-    static_assert(5 * K * 4 + C * 4 * 4 <= V * LDC * 2, "column sums and E.Ak sums over U~^T");
+    static_assert(4 * K * 4 + C * 4 * 4 <= V * LDC * 2, "column sums and E.Ak sums over U~^T");
     static_assert(C * LDK <= C * LDV, "dBk over U");
     static_assert(TOTAL <= 160 * 1024, "LDS budget exceeded");
 };
@@ -907,7 +912,7 @@ __global__ __launch_bounds__(512, 1) void kda_bwd_fused_kernel(BwdParams p) {
     unsigned* sE = reinterpret_cast<unsigned*>(smem + L::oW);
     T* sUt = reinterpret_cast<T*>(smem + L::oUt);
     float* sCS = reinterpret_cast<float*>(smem + L::oUt);
-    float* sPE = sCS + 5 * K;                      // [C][4]: sum_r E[s][r] Ak[s][r] over key block j
+    float* sPE = sCS + 4 * K;                      // [C][4]: sum_r E[s][r] Ak[s][r] over key block j
     T* sDO = reinterpret_cast<T*>(smem + L::oDO);
     T* sBV = reinterpret_cast<T*>(smem + L::oDO);
     T* sK = reinterpret_cast<T*>(smem + L::oK);
@@ -933,28 +938,23 @@ __global__ __launch_bounds__(512, 1) void kda_bwd_fused_kernel(BwdParams p) {
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
 
     // ---- global loads, all issued before any is waited on ---------------------------
-    // rows cw of S (chunk start) and dS' (chunk end): lane group lg holds
-    // columns 32 ks + 4 lg + {0..3} and 32 ks + 16 + 4 lg + {0..3} (permuted slots)
+    // first what stages 0 and 1 use (S, W, U~^T, the gates), then dS', dO and k,
+    // which arrive while they run.  Rows cw of S (chunk start) and dS' (chunk
+    // end): lane group lg holds columns 32 ks + 4 lg + {0..3} and
+    // 32 ks + 16 + 4 lg + {0..3} (permuted slots)
+    const float* S0 = ci == 0 ? (p.s0 ? p.s0 + (size_t)bh * KV : nullptr)
+                              : p.snaps + (((size_t)b * NC + ci - 1) * p.H + h) * KV;
+    const float* dSp = ci == NC - 1 ? (p.dsT ? p.dsT + (size_t)bh * KV : nullptr) : p.adj + (size_t)item * KV;
     uint4 rS[8], rDS[8];
     {
-        const float* S0 = ci == 0 ? (p.s0 ? p.s0 + (size_t)bh * KV : nullptr)
-                                  : p.snaps + (((size_t)b * NC + ci - 1) * p.H + h) * KV;
-        const float* dSp = ci == NC - 1 ? (p.dsT ? p.dsT + (size_t)bh * KV : nullptr) : p.adj + (size_t)item * KV;
         const __amdgpu_buffer_rsrc_t rs = make_rsrc_n(S0, S0 ? (unsigned)(KV * 4) : 0u);
-        const __amdgpu_buffer_rsrc_t rd = make_rsrc_n(dSp, dSp ? (unsigned)(KV * 4) : 0u);
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            const unsigned off = (unsigned)(cw * V + 32 * (m >> 1) + 16 * (m & 1) + 4 * lg) * 4u;
-            rS[m] = buf_load16(rs, off);
-            rDS[m] = buf_load16(rd, off);
-        }
+        for (int m = 0; m < 8; ++m)
+            rS[m] = buf_load16(rs, (unsigned)(cw * V + 32 * (m >> 1) + 16 * (m & 1) + 4 * lg) * 4u);
     }
     uint4 rw[2], ru[2], ro[2], rk[2];
     load_flat_pieces<2, NT>(rec + RL.oW, C * K * 2 / 16, rw, tid);
     load_flat_pieces<2, NT>(rec + RL.oUtT, V * C * 2 / 16, ru, tid);
-    load_tok_pieces<T, V, 2, NT>(p.d_o, p, b, h, t0, nt, ro, tid);
-    load_tok_pieces<T, K, 2, NT>(p.k, p, b, h, t0, nt, rk, tid);
-    const float egc_c = reinterpret_cast<const float*>(rec + RL.oEgc)[cw];
     // raw gates of channel gc, tokens 16 gp .. 16 gp + 15 (zeros past the end)
     const int gc = tid & (K - 1), gp = tid >> 7;
     float graw[16];
@@ -969,37 +969,36 @@ __global__ __launch_bounds__(512, 1) void kda_bwd_fused_kernel(BwdParams p) {
         const __amdgpu_buffer_rsrc_t rb = make_rsrc_n(bb, nt > 0 ? (unsigned)((nt - 1) * p.H + 1) * 2u : 0u);
         beta_t = buf_bf16(rb, (unsigned)(tid * p.H) * 2u);   // zero from token nt on
     }
-    // ---- stage 0: operands to LDS; S, dS' fragments; rs; gate scan within blocks ----
+    {
+        const __amdgpu_buffer_rsrc_t rd = make_rsrc_n(dSp, dSp ? (unsigned)(KV * 4) : 0u);
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+            rDS[m] = buf_load16(rd, (unsigned)(cw * V + 32 * (m >> 1) + 16 * (m & 1) + 4 * lg) * 4u);
+    }
+    load_tok_pieces<T, V, 2, NT>(p.d_o, p, b, h, t0, nt, ro, tid);
+    load_tok_pieces<T, K, 2, NT>(p.k, p, b, h, t0, nt, rk, tid);
+    const float egc_c = reinterpret_cast<const float*>(rec + RL.oEgc)[cw];
+
+    // ---- stage 0: S^T, W, U~^T to LDS; S fragments; gate scan within blocks ----------
     typename FragOf<T>::type fS[4], fD[4];
-    float rsp = 0.f;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-        float s8[8], d8[8];
+        float s8[8];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-            const uint4 a = rS[2 * ks + hh], d = rDS[2 * ks + hh];
+            const uint4 a = rS[2 * ks + hh];
             s8[4 * hh + 0] = __uint_as_float(a.x); s8[4 * hh + 1] = __uint_as_float(a.y);
             s8[4 * hh + 2] = __uint_as_float(a.z); s8[4 * hh + 3] = __uint_as_float(a.w);
-            d8[4 * hh + 0] = __uint_as_float(d.x); d8[4 * hh + 1] = __uint_as_float(d.y);
-            d8[4 * hh + 2] = __uint_as_float(d.z); d8[4 * hh + 3] = __uint_as_float(d.w);
         }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) rsp += s8[e] * d8[e];
         fS[ks] = frag_from<T>(s8);
-        fD[ks] = frag_from<T>(d8);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             sST[(32 * ks + 4 * lg + e) * LDK + cw] = fS[ks][e];
             sST[(32 * ks + 16 + 4 * lg + e) * LDK + cw] = fS[ks][4 + e];
         }
     }
-    rsp += __shfl_xor(rsp, 16);
-    rsp += __shfl_xor(rsp, 32);
-    const float rs_c = egc_c * rsp;               // e^{G_C} sum_v S[cw][v] dS'[cw][v]
     store_pieces<2, NT>(sW, LDK * 2, K * 2 / 16, C * K * 2 / 16, rw, tid);
     store_pieces<2, NT>(sUt, LDC * 2, C * 2 / 16, V * C * 2 / 16, ru, tid);
-    store_pieces<2, NT>(sDO, LDV * 2, V * 2 / 16, C * V * 2 / 16, ro, tid);
-    store_pieces<2, NT>(sK, LDK * 2, K * 2 / 16, C * K * 2 / 16, rk, tid);
     if (tid < C) sB[tid] = beta_t;
     float gx[16];
 #pragma unroll
@@ -1012,7 +1011,8 @@ __global__ __launch_bounds__(512, 1) void kda_bwd_fused_kernel(BwdParams p) {
     sTot[gp * K + gc] = gx[15];
     __syncthreads();
 
-    // ---- stage 1: G and the references R_j; U = U~ - W S ----------------------------
+    // ---- stage 1: G and the references R_j; U = U~ - W S; dS' fragments and rs;
+    // dO and k to LDS ------------------------------------------------------------------
     {
         float off = 0.f;
 #pragma unroll
@@ -1035,6 +1035,27 @@ __global__ __launch_bounds__(512, 1) void kda_bwd_fused_kernel(BwdParams p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) sU[(16 * ti + 4 * lg + e) * LDV + cw] = from_f32<T>(acc[e]);
     }
+    float rsp = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        float d8[8];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const uint4 a = rS[2 * ks + hh], d = rDS[2 * ks + hh];
+            d8[4 * hh + 0] = __uint_as_float(d.x); d8[4 * hh + 1] = __uint_as_float(d.y);
+            d8[4 * hh + 2] = __uint_as_float(d.z); d8[4 * hh + 3] = __uint_as_float(d.w);
+            rsp += __uint_as_float(a.x) * d8[4 * hh + 0] + __uint_as_float(a.y) * d8[4 * hh + 1] +
+                   __uint_as_float(a.z) * d8[4 * hh + 2] + __uint_as_float(a.w) * d8[4 * hh + 3];
+        }
+        fD[ks] = frag_from<T>(d8);
+    }
+    rsp += __shfl_xor(rsp, 16);
+    rsp += __shfl_xor(rsp, 32);
+    // e^{G_C} sum_v S[cw][v] dS'[cw][v], kept in the fourth block total's slot
+    // (the offsets above read only the first three)
+    if (lg == 0) sTot[3 * K + cw] = egc_c * rsp;
+    store_pieces<2, NT>(sDO, LDV * 2, V * 2 / 16, C * V * 2 / 16, ro, tid);
+    store_pieces<2, NT>(sK, LDK * 2, K * 2 / 16, C * K * 2 / 16, rk, tid);
     __syncthreads();
 
     // ---- stage 2: the gated Gram Ak; D = tril(dO U^T); dQh = dO S^T; dKb = U dS'^T ----
@@ -1106,7 +1127,7 @@ __global__ __launch_bounds__(512, 1) void kda_bwd_fused_kernel(BwdParams p) {
     }
     __syncthreads();
 
-    // ---- stage 3: T_j = (I + A_jj)^{-1}, A = diag(beta) Ak, by forward substitution --
+    // ---- stage 3: T_j = (I + A_jj)^{-1}, A = diag(beta) Ak: (I - N)(I + N^2)(I + N^4)(I + N^8) --
     // q of channel cw at tokens 16 i + 4 lg + e (gated products, epilogue)
     float qv[4][4];
     {
@@ -1130,22 +1151,37 @@ __global__ __launch_bounds__(512, 1) void kda_bwd_fused_kernel(BwdParams p) {
         const int I = j < 3 ? j + 1 : 2, J = j < 3 ? 0 : 1;
         return sAkT + 16 * I * LDA + 16 * J;
     };
-    if (tid < 64) {
-        const int j = tid >> 4, c = tid & 15;
-        float tc[16];
+    if (w < 4) {
+        // wave j: N = A_jj (strictly lower, so N^16 = 0).  Every factor is a
+        // polynomial in N (they commute); a product P Q takes P's A operand from
+        // the accumulator of P^T and Q's B operand from the accumulator of Q,
+        // so both layouts are carried.
+        const int j = w;
+        const f32x4 bt4 = *reinterpret_cast<const f32x4*>(&sB[16 * j + 4 * lg]);
+        const float btr = sB[16 * j + lr];
+        f32x4 n, nt4;                              // acc(N), acc(N^T)
+        {
+            const f32x4 a = *reinterpret_cast<const f32x4*>(&sAkT[(16 * j + lr) * LDA + 16 * j + 4 * lg]);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) tc[r] = (float)(r == c);
-#pragma unroll
-        for (int r = 1; r < 16; ++r) {
-            float a = 0.f;
-#pragma unroll
-            for (int m = 0; m < r; ++m) a += sAkT[(16 * j + m) * LDA + 16 * j + r] * tc[m];
-            const float v = -sB[16 * j + r] * a;
-            tc[r] = r > c ? v : tc[r];
+            for (int e = 0; e < 4; ++e) {
+                const int rr = 4 * lg + e;         // N[rr][lr] = beta_rr Ak[rr][lr], rr > lr
+                n[e] = rr > lr ? bt4[e] * a[e] : 0.f;
+                const float at = sAkT[(16 * j + rr) * LDA + 16 * j + lr];
+                nt4[e] = lr > rr ? btr * at : 0.f;  // N^T[rr][lr] = N[lr][rr]
+            }
         }
-        float* tt = tblock(j) + c * LDA;
+        f32x4 id;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) tt[r] = tc[r];
+        for (int e = 0; e < 4; ++e) id[e] = (4 * lg + e == lr) ? 1.f : 0.f;
+        const f32x4 n2 = mma16(z, nt4, n), n2t = mma16(z, n, nt4);
+        const f32x4 n4 = mma16(z, n2t, n2), n4t = mma16(z, n2, n2t);
+        const f32x4 n8 = mma16(z, n4t, n4);
+        const f32x4 p1 = id - n, p1t = id - nt4;
+        const f32x4 p2 = p1 + mma16(z, n2t, p1), p2t = p1t + mma16(z, n2, p1t);
+        const f32x4 p3 = p2 + mma16(z, n4t, p2), p3t = p2t + mma16(z, n4, p2t);
+        const f32x4 tj = p3 + mma16(z, p3t, n8);  // acc(T_j)
+        // T_j^T as the solve reads it: row c holds column c of T_j
+        *reinterpret_cast<f32x4*>(tblock(j) + lr * LDA + 4 * lg) = tj;
     }
     __syncthreads();
 
@@ -1236,9 +1272,12 @@ __global__ __launch_bounds__(512, 1) void kda_bwd_fused_kernel(BwdParams p) {
                 pe[e] = r < s ? ev * sAkT[r * LDA + s] : 0.f;
             }
 #pragma unroll
-            for (int x = 1; x < 16; x <<= 1)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) pe[e] += __shfl_xor(pe[e], x);
+            for (int e = 0; e < 4; ++e) {
+                pe[e] += row_ror_f<8>(pe[e]);
+                pe[e] += row_ror_f<4>(pe[e]);
+                pe[e] += row_ror_f<2>(pe[e]);
+                pe[e] += row_ror_f<1>(pe[e]);
+            }
             if (lr == 0)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) sPE[(16 * i + 4 * lg + e) * 4 + j] = pe[e];
@@ -1389,7 +1428,6 @@ __global__ __launch_bounds__(512, 1) void kda_bwd_fused_kernel(BwdParams p) {
             colpart += __shfl_xor(colpart, 32);
             if (lg == 0) sCS[i * K + cw] = colpart;
         }
-        if (lg == 0) sCS[4 * K + cw] = rs_c;
     }
     __syncthreads();                              // Ak^T and D are no longer read: dG goes over them
 #pragma unroll
@@ -1409,7 +1447,7 @@ __global__ __launch_bounds__(512, 1) void kda_bwd_fused_kernel(BwdParams p) {
             sum += dv16[i];
         }
         const int base = l & ~3;
-        float tot = sCS[4 * K + c] + sCS[c] + sCS[K + c] + sCS[2 * K + c] + sCS[3 * K + c];
+        float tot = sTot[3 * K + c] + sCS[c] + sCS[K + c] + sCS[2 * K + c] + sCS[3 * K + c];
 #pragma unroll
         for (int q = 3; q >= 1; --q) {
             const float sq = __shfl(sum, base + q);
