@@ -57,6 +57,22 @@ def test_backward_matches_oracle(B, T, H, K, V, dtype):
     _check(*out, ref, dtype)
 
 
+def test_backward_with_floor_channels():
+    """A quarter of the (head, channel) pairs hold g = -5 (the clamp floor) at
+    every token: the largest in-block exponents (16 tokens at the floor) and
+    the gate derivative on the closed end of the clamp range."""
+    say("bwd: 25 % floor channels, B=2 T=300 H=2 K=V=128 bf16")
+    d = make_prefill(2, 300, 2, 128, 128, torch.bfloat16, seed=97, s0_std=0.02, pinned_frac=0.25)
+    gen = torch.Generator().manual_seed(1097)
+    d_o = torch.randn((2, 300, 2, 128), generator=gen).to(torch.bfloat16)
+    dsT = torch.randn((2, 2, 128, 128), generator=gen)
+    x = {n: (t.to(DEV) if isinstance(t, torch.Tensor) else t) for n, t in d.items()}
+    out = chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], d_o.to(DEV), dsT.to(DEV))
+    torch.cuda.synchronize()
+    ref = oracle.oracle_bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["s0"], d_o, dsT)
+    _check(*out, ref, torch.bfloat16)
+
+
 def test_backward_without_incoming_state_gradient_or_initial_state():
     say("bwd: no S0, no dS_T, no dS0 output")
     d, d_o, _ = _grads_in(2, 130, 2, 128, 128, torch.bfloat16, seed=95, with_s0=False, with_dst=False)
@@ -70,14 +86,15 @@ def test_backward_without_incoming_state_gradient_or_initial_state():
 
 
 def test_backward_deterministic_and_t0():
-    say("bwd: bitwise repeat; T = 0")
-    d, d_o, dsT = _grads_in(1, 70, 2, 64, 64, torch.bfloat16, seed=96)
-    x = {n: (t.to(DEV) if isinstance(t, torch.Tensor) else t) for n, t in d.items()}
-    a = chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], d_o.to(DEV), dsT.to(DEV))
-    b = chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], d_o.to(DEV), dsT.to(DEV))
-    torch.cuda.synchronize()
-    for u, w in zip(a, b):
-        assert torch.equal(u, w)
+    say("bwd: bitwise repeat (three chunk stages at K = V = 64, one fused kernel at 128); T = 0")
+    for K, T in ((64, 70), (128, 200)):
+        d, d_o, dsT = _grads_in(1, T, 2, K, K, torch.bfloat16, seed=96)
+        x = {n: (t.to(DEV) if isinstance(t, torch.Tensor) else t) for n, t in d.items()}
+        a = chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], d_o.to(DEV), dsT.to(DEV))
+        b = chunk_bwd(x["q"], x["k"], x["v"], x["g"], x["beta"], x["s0"], d_o.to(DEV), dsT.to(DEV))
+        torch.cuda.synchronize()
+        for u, w in zip(a, b):
+            assert torch.equal(u, w)
     z = {n: t[:, :0].contiguous() for n, t in x.items() if n != "s0"}
     dsT_d = dsT.to(DEV)
     out = chunk_bwd(z["q"], z["k"], z["v"], z["g"], z["beta"], x["s0"], None, dsT_d)
