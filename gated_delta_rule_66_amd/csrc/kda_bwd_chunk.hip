@@ -128,6 +128,10 @@ template <int N>
 __device__ __forceinline__ float row_ror_f(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x120 + N, 0xf, 0xf, false));
 }
+// one bf16 element to byte offset off of a buffer (dropped past its end)
+__device__ __forceinline__ void buf_st_bf16(__amdgpu_buffer_rsrc_t r, unsigned off, float v) {
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (bf16)v), r, (int)off, 0, 0);
+}
 // pieces [0, n) of a contiguous array
 template <int NP, int NT = 256>
 __device__ __forceinline__ void load_flat_pieces(const void* src, int n, uint4 (&r)[NP], int tid) {
@@ -886,8 +890,8 @@ struct FusedBwdLayout {
     static constexpr int oG = oK + C * LDK * 2;   // G fp32 [C][LDG] (log2 units)
     static constexpr int oU = oG + C * LDG * 4;   // U [C][LDV] | dBk [C][LDK]
     static constexpr int oR = oU + C * LDV * 2;   // R fp32 [5][K]
-    static constexpr int oM = oR + 5 * K * 4;     // clamp pass mask: [C][K / 64] bits
-    static constexpr int oB = oM + C * (K / 64) * 8;  // beta fp32 [C]
+    static constexpr int oM = oR + 5 * K * 4;     // clamp pass mask: [K][4] x 16 bits (channel, token block)
+    static constexpr int oB = oM + K * 4 * 2;     // beta fp32 [C]
     static constexpr int oTot = oB + C * 4;       // gate totals of the four token blocks fp32 [4][K] | rs at [3][K]
     static constexpr int TOTAL = oTot + 4 * K * 4;
     static_assert(2 * C * LDA * 4 <= V * LDK * 2 && C * LDDG * 4 <= V * LDK * 2, "region A");
@@ -920,7 +924,7 @@ __global__ __launch_bounds__(512, 1) void kda_bwd_fused_kernel(BwdParams p) {
     T* sU = reinterpret_cast<T*>(smem + L::oU);
     T* sBK = reinterpret_cast<T*>(smem + L::oU);
     float* sR = reinterpret_cast<float*>(smem + L::oR);
-    unsigned long long* sM = reinterpret_cast<unsigned long long*>(smem + L::oM);
+    unsigned short* sM = reinterpret_cast<unsigned short*>(smem + L::oM);
     float* sB = reinterpret_cast<float*>(smem + L::oB);
     float* sTot = reinterpret_cast<float*>(smem + L::oTot);
 
@@ -1004,9 +1008,13 @@ __global__ __launch_bounds__(512, 1) void kda_bwd_fused_kernel(BwdParams p) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         gx[i] = fminf(fmaxf(graw[i], -5.f), 0.f) * kLog2e + (i ? gx[i - 1] : 0.f);
+    }
+    {
         // the clamp passes the gradient where the raw gate lies in [-5, 0]
-        const unsigned long long pass = __ballot(graw[i] >= -5.f && graw[i] <= 0.f);
-        if (l == 0) sM[(16 * gp + i) * 2 + (w & 1)] = pass;
+        unsigned pass = 0u;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) pass |= (graw[i] >= -5.f && graw[i] <= 0.f) ? (1u << i) : 0u;
+        sM[gc * 4 + gp] = (unsigned short)pass;
     }
     sTot[gp * K + gc] = gx[15];
     __syncthreads();
@@ -1199,7 +1207,7 @@ __global__ __launch_bounds__(512, 1) void kda_bwd_fused_kernel(BwdParams p) {
             }
             X[j] = mma16(z, *reinterpret_cast<const f32x4*>(tblock(j) + lr * LDA + 4 * lg), acc);
         }
-        T* dvp = reinterpret_cast<T*>(p.dv) + (((size_t)b * p.T + t0) * p.H + h) * V + cw;
+        const __amdgpu_buffer_rsrc_t rdv = tok_rsrc(p.dv, p, b, h, t0, nt, V);   // rows past nt dropped
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -1207,7 +1215,7 @@ __global__ __launch_bounds__(512, 1) void kda_bwd_fused_kernel(BwdParams p) {
                 const int s = 16 * j + 4 * lg + e;
                 const float x = X[j][e];
                 sBV[s * LDV + cw] = from_f32<T>(x);
-                if (s < nt) dvp[(size_t)s * rowK] = from_f32<T>(sB[s] * x);
+                buf_st_bf16(rdv, (unsigned)(s * rowK + cw) * 2u, sB[s] * x);
             }
     }
     __syncthreads();
@@ -1356,8 +1364,8 @@ __global__ __launch_bounds__(512, 1) void kda_bwd_fused_kernel(BwdParams p) {
         for (int a2 = 1; a2 < 5; ++a2)
 #pragma unroll
             for (int b3 = 0; b3 < a2; ++b3) xr[a2][b3] = fast_exp2(Rr[a2] - Rr[b3]);
-        T* dqo = reinterpret_cast<T*>(p.dq) + (((size_t)b * p.T + t0) * p.H + h) * K + cw;
-        T* dko = reinterpret_cast<T*>(p.dk) + (((size_t)b * p.T + t0) * p.H + h) * K + cw;
+        const __amdgpu_buffer_rsrc_t rdq = tok_rsrc(p.dq, p, b, h, t0, nt, K);   // rows past nt dropped
+        const __amdgpu_buffer_rsrc_t rdk = tok_rsrc(p.dk, p, b, h, t0, nt, K);
         const float RC = Rr[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -1419,10 +1427,8 @@ __global__ __launch_bounds__(512, 1) void kda_bwd_fused_kernel(BwdParams p) {
                 const float kbar = kk * egc;
                 dgr[i][e] = dQh * qq * eg + dKh * kk * eg - dKb * kbar + kk * (X1 - X2 - Y2) + qq * Y1;
                 colpart += dKb * kbar;
-                if (t < nt) {
-                    dqo[(size_t)t * rowK] = from_f32<T>(dQh * eg + Y1);
-                    dko[(size_t)t * rowK] = from_f32<T>(dKh * eg + X1 + X2 + Y2 + dKb * egc);
-                }
+                buf_st_bf16(rdq, (unsigned)(t * rowK + cw) * 2u, dQh * eg + Y1);
+                buf_st_bf16(rdk, (unsigned)(t * rowK + cw) * 2u, dKh * eg + X1 + X2 + Y2 + dKb * egc);
             }
             colpart += __shfl_xor(colpart, 16);
             colpart += __shfl_xor(colpart, 32);
@@ -1453,13 +1459,12 @@ __global__ __launch_bounds__(512, 1) void kda_bwd_fused_kernel(BwdParams p) {
             const float sq = __shfl(sum, base + q);
             if (q > part) tot += sq;
         }
-        T* dgo = reinterpret_cast<T*>(p.dg) + (((size_t)b * p.T + t0) * p.H + h) * K + c;
+        const __amdgpu_buffer_rsrc_t rdg = tok_rsrc(p.dg, p, b, h, t0, nt, K);   // rows past nt dropped
+        const unsigned pass = sM[c * 4 + part];
 #pragma unroll
         for (int i = 15; i >= 0; --i) {
-            const int t = 16 * part + i;
             tot += dv16[i];
-            const bool pass = (sM[t * 2 + (c >> 6)] >> (c & 63)) & 1ull;
-            if (t < nt) dgo[(size_t)t * rowK] = from_f32<T>(pass ? tot : 0.f);
+            buf_st_bf16(rdg, (unsigned)((16 * part + i) * rowK + c) * 2u, ((pass >> i) & 1u) ? tot : 0.f);
         }
     }
 }
