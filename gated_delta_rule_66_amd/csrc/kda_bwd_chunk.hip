@@ -1423,12 +1423,15 @@ __global__ __launch_bounds__(512, 1) void kda_bwd_fused_kernel(BwdParams p) {
                 const float Y2 = em[i][e] * (y2d[e] + gi * y2o[e]);
                 const float X2 = em[i][e] * (x2d[e] + gi * x2o[e]);
                 const float kk = kv[i][e], qq = qv[i][e];
-                const float dQh = qh[i][e], dKb = kb[i][e], dKh = dkh[i][e];
-                const float kbar = kk * egc;
-                dgr[i][e] = dQh * qq * eg + dKh * kk * eg - dKb * kbar + kk * (X1 - X2 - Y2) + qq * Y1;
-                colpart += dKb * kbar;
-                buf_st_bf16(rdq, (unsigned)(t * rowK + cw) * 2u, dQh * eg + Y1);
-                buf_st_bf16(rdk, (unsigned)(t * rowK + cw) * 2u, dKh * eg + X1 + X2 + Y2 + dKb * egc);
+                // dq = dQh e^G + Y1,  dk = (dKh e^G + X1) + dKb e^{G_C - G} + (X2 + Y2), and
+                // dG = dQh q e^G + dKh k e^G - dKb k e^{G_C - G} + k (X1 - X2 - Y2) + q Y1
+                //    = q dq + k ((dKh e^G + X1) - dKb e^{G_C - G} - (X2 + Y2))
+                const float dq = qh[i][e] * eg + Y1;
+                const float a1 = dkh[i][e] * eg + X1, bv = kb[i][e] * egc, cv = X2 + Y2;
+                dgr[i][e] = qq * dq + kk * (a1 - bv - cv);
+                colpart += kk * bv;
+                buf_st_bf16(rdq, (unsigned)(t * rowK + cw) * 2u, dq);
+                buf_st_bf16(rdk, (unsigned)(t * rowK + cw) * 2u, a1 + bv + cv);
             }
             colpart += __shfl_xor(colpart, 16);
             colpart += __shfl_xor(colpart, 32);
