@@ -779,6 +779,7 @@ struct BwdLayout {
     kda_plan plan;
     int cps, NC;
     size_t seg, rec, snaps, adj, inter;   // byte offsets (chunk form)
+    size_t s0h, dsTh;                     // bf16 copies of S0 and dL/dS_T (fused chunk kernel)
     size_t tok;                           // byte offset of the checkpoints and partial sums (token level)
     size_t total;                         // bytes
 };
@@ -808,7 +809,11 @@ static kda_status bwd_layout(int B, int T, int H, int K, int V, kda_dtype dt, Bw
         L->total = bwd_workspace_bytes(B, T, H, K, V);
         return KDA_OK;
     }
-    const size_t bh = (size_t)B * H, kv = (size_t)K * V * sizeof(float);
+    const size_t bh = (size_t)B * H;
+    // the fused chunk kernel reads the states and adjoints as bf16 (its products
+    // take bf16 operands); the three-stage form reads fp32
+    const bool fused = bwd_fused_variant_exists((int)dt, K, V);
+    const size_t kv = (size_t)K * V * (fused ? 2 : sizeof(float));
     size_t o = 0;
     // the forward plan's segment arrays with one more transition slot: the
     // backward's summary pass keeps the last segment's transition too, whose
@@ -819,6 +824,10 @@ static kda_status bwd_layout(int B, int T, int H, int K, int V, kda_dtype dt, Bw
     L->snaps = o; o += align256(bh * L->NC * kv);
     L->adj = o;   o += align256(bh * L->NC * kv);
     L->inter = o; o += align256(bh * L->NC * bwd_inter_floats((int)dt, K, V) * sizeof(float));
+    if (fused) {
+        L->s0h = o;  o += align256(bh * kv);
+        L->dsTh = o; o += align256(bh * kv);
+    }
     L->total = o;
     return KDA_OK;
 }
@@ -931,7 +940,10 @@ kda_status kda_chunk_bwd(int B, int T, int H, int K, int V, kda_dtype dt,
         }
         sp.summary = 0;
         sp.n_vb = V / vb;
+        // the fused chunk kernel's states and adjoints are bf16 (see bwd_layout)
+        const bool fused = bwd_fused_variant_exists((int)dt, K, V);
         sp.snaps = snaps;
+        sp.snap_bf16 = fused ? 1 : 0;
         sp.snap_every = 1;
         sp.max_snaps = B * NC;
         sp.snap_stride = NC;
@@ -943,11 +955,30 @@ kda_status kda_chunk_bwd(int B, int T, int H, int K, int V, kda_dtype dt,
         // gradients of every chunk at once
         p.NC = NC;
         p.rec = recs;
-        p.snaps = snaps;
-        p.adj = reinterpret_cast<float*>(ws + L.adj);
+        if (fused) {
+            p.snaps16 = snaps;
+            p.adj16 = ws + L.adj;
+            // S0 and dL/dS_T as bf16, for the first and the last chunk
+            if (initial_state) {
+                p.s0h = ws + L.s0h;
+                if (launch_timed("bwd_s0_bf16", st, [&] {
+                        return launch_to_bf16(initial_state, ws + L.s0h, (size_t)bh * K * V, st);
+                    }) != hipSuccess)
+                    return KDA_ERR_HIP;
+            }
+            if (d_final_state) {
+                p.dsTh = ws + L.dsTh;
+                if (launch_timed("bwd_dsT_bf16", st, [&] {
+                        return launch_to_bf16(d_final_state, ws + L.dsTh, (size_t)bh * K * V, st);
+                    }) != hipSuccess)
+                    return KDA_ERR_HIP;
+            }
+        } else {
+            p.snaps = snaps;
+            p.adj = reinterpret_cast<float*>(ws + L.adj);
+        }
         const size_t nch = (size_t)bh * NC, c = kChunk;
         float* f = reinterpret_cast<float*>(ws + L.inter);
-        const bool fused = bwd_fused_variant_exists((int)dt, K, V);
         p.cdU = f;  f += nch * c * V;
         if (fused) f = nullptr;                 // no other intermediate
         p.cD = f;   f += nch * c * c;

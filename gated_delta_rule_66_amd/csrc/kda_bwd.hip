@@ -532,13 +532,22 @@ __global__ __launch_bounds__(64 * NW) void kda_bwd_state_kernel(BwdParams p) {
             dS[ct] = acc;
         }
         if (!SUMMARY) {
-            // the adjoint before chunk ci: after chunk ci - 1, or dL/dS_0
-            float* dst = (ci > 0 ? p.adj + ((size_t)bh * NC + ci - 1) * KV : p.ds0 + (size_t)bh * KV) +
-                         (size_t)(4 * opaque(lg)) * V + opaque(col);
+            // the adjoint before chunk ci: after chunk ci - 1 (bf16 where the fused
+            // chunk kernel reads it), or dL/dS_0 (fp32)
+            const size_t lo = (size_t)(4 * opaque(lg)) * V + opaque(col);
+            if (ci > 0 && p.adj16) {
+                bf16* dst = reinterpret_cast<bf16*>(p.adj16) + ((size_t)bh * NC + ci - 1) * KV + lo;
 #pragma unroll
-            for (int ct = 0; ct < CT; ++ct)
+                for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) dst[(size_t)(16 * ct + e) * V] = dS[ct][e];
+                    for (int e = 0; e < 4; ++e) dst[(size_t)(16 * ct + e) * V] = (bf16)dS[ct][e];
+            } else {
+                float* dst = (ci > 0 ? p.adj + ((size_t)bh * NC + ci - 1) * KV : p.ds0 + (size_t)bh * KV) + lo;
+#pragma unroll
+                for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) dst[(size_t)(16 * ct + e) * V] = dS[ct][e];
+            }
         }
         __syncthreads();
         return true;

@@ -132,6 +132,8 @@ __device__ __forceinline__ float row_ror_f(float x) {
 __device__ __forceinline__ void buf_st_bf16(__amdgpu_buffer_rsrc_t r, unsigned off, float v) {
     __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (bf16)v), r, (int)off, 0, 0);
 }
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 // pieces [0, n) of a contiguous array
 template <int NP, int NT = 256>
 __device__ __forceinline__ void load_flat_pieces(const void* src, int n, uint4 (&r)[NP], int tid) {
@@ -944,17 +946,18 @@ __global__ __launch_bounds__(512, 1) void kda_bwd_fused_kernel(BwdParams p) {
     // ---- global loads, all issued before any is waited on ---------------------------
     // first what stages 0 and 1 use (S, W, U~^T, the gates), then dS', dO and k,
     // which arrive while they run.  Rows cw of S (chunk start) and dS' (chunk
-    // end): lane group lg holds columns 32 ks + 4 lg + {0..3} and
+    // end), bf16: lane group lg holds columns 32 ks + 4 lg + {0..3} and
     // 32 ks + 16 + 4 lg + {0..3} (permuted slots)
-    const float* S0 = ci == 0 ? (p.s0 ? p.s0 + (size_t)bh * KV : nullptr)
-                              : p.snaps + (((size_t)b * NC + ci - 1) * p.H + h) * KV;
-    const float* dSp = ci == NC - 1 ? (p.dsT ? p.dsT + (size_t)bh * KV : nullptr) : p.adj + (size_t)item * KV;
-    uint4 rS[8], rDS[8];
+    const bf16* S0 = ci == 0 ? (p.s0h ? reinterpret_cast<const bf16*>(p.s0h) + (size_t)bh * KV : nullptr)
+                             : reinterpret_cast<const bf16*>(p.snaps16) + (((size_t)b * NC + ci - 1) * p.H + h) * KV;
+    const bf16* dSp = ci == NC - 1 ? (p.dsTh ? reinterpret_cast<const bf16*>(p.dsTh) + (size_t)bh * KV : nullptr)
+                                   : reinterpret_cast<const bf16*>(p.adj16) + (size_t)item * KV;
+    u32x2 rS[8], rDS[8];
     {
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc_n(S0, S0 ? (unsigned)(KV * 4) : 0u);
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc_n(S0, S0 ? (unsigned)(KV * 2) : 0u);
 #pragma unroll
         for (int m = 0; m < 8; ++m)
-            rS[m] = buf_load16(rs, (unsigned)(cw * V + 32 * (m >> 1) + 16 * (m & 1) + 4 * lg) * 4u);
+            rS[m] = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)((cw * V + 32 * (m >> 1) + 16 * (m & 1) + 4 * lg) * 2), 0, 0);
     }
     uint4 rw[2], ru[2], ro[2], rk[2];
     load_flat_pieces<2, NT>(rec + RL.oW, C * K * 2 / 16, rw, tid);
@@ -974,10 +977,10 @@ __global__ __launch_bounds__(512, 1) void kda_bwd_fused_kernel(BwdParams p) {
         beta_t = buf_bf16(rb, (unsigned)(tid * p.H) * 2u);   // zero from token nt on
     }
     {
-        const __amdgpu_buffer_rsrc_t rd = make_rsrc_n(dSp, dSp ? (unsigned)(KV * 4) : 0u);
+        const __amdgpu_buffer_rsrc_t rd = make_rsrc_n(dSp, dSp ? (unsigned)(KV * 2) : 0u);
 #pragma unroll
         for (int m = 0; m < 8; ++m)
-            rDS[m] = buf_load16(rd, (unsigned)(cw * V + 32 * (m >> 1) + 16 * (m & 1) + 4 * lg) * 4u);
+            rDS[m] = __builtin_amdgcn_raw_buffer_load_b64(rd, (int)((cw * V + 32 * (m >> 1) + 16 * (m & 1) + 4 * lg) * 2), 0, 0);
     }
     load_tok_pieces<T, V, 2, NT>(p.d_o, p, b, h, t0, nt, ro, tid);
     load_tok_pieces<T, K, 2, NT>(p.k, p, b, h, t0, nt, rk, tid);
@@ -987,14 +990,8 @@ __global__ __launch_bounds__(512, 1) void kda_bwd_fused_kernel(BwdParams p) {
     typename FragOf<T>::type fS[4], fD[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-        float s8[8];
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            const uint4 a = rS[2 * ks + hh];
-            s8[4 * hh + 0] = __uint_as_float(a.x); s8[4 * hh + 1] = __uint_as_float(a.y);
-            s8[4 * hh + 2] = __uint_as_float(a.z); s8[4 * hh + 3] = __uint_as_float(a.w);
-        }
-        fS[ks] = frag_from<T>(s8);
+        const u32x4 w4 = {rS[2 * ks][0], rS[2 * ks][1], rS[2 * ks + 1][0], rS[2 * ks + 1][1]};
+        fS[ks] = __builtin_bit_cast(bf16x8, w4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             sST[(32 * ks + 4 * lg + e) * LDK + cw] = fS[ks][e];
@@ -1046,16 +1043,10 @@ __global__ __launch_bounds__(512, 1) void kda_bwd_fused_kernel(BwdParams p) {
     float rsp = 0.f;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-        float d8[8];
+        const u32x4 w4 = {rDS[2 * ks][0], rDS[2 * ks][1], rDS[2 * ks + 1][0], rDS[2 * ks + 1][1]};
+        fD[ks] = __builtin_bit_cast(bf16x8, w4);
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            const uint4 a = rS[2 * ks + hh], d = rDS[2 * ks + hh];
-            d8[4 * hh + 0] = __uint_as_float(d.x); d8[4 * hh + 1] = __uint_as_float(d.y);
-            d8[4 * hh + 2] = __uint_as_float(d.z); d8[4 * hh + 3] = __uint_as_float(d.w);
-            rsp += __uint_as_float(a.x) * d8[4 * hh + 0] + __uint_as_float(a.y) * d8[4 * hh + 1] +
-                   __uint_as_float(a.z) * d8[4 * hh + 2] + __uint_as_float(a.w) * d8[4 * hh + 3];
-        }
-        fD[ks] = frag_from<T>(d8);
+        for (int e = 0; e < 8; ++e) rsp += to_f32(fS[ks][e]) * to_f32(fD[ks][e]);
     }
     rsp += __shfl_xor(rsp, 16);
     rsp += __shfl_xor(rsp, 32);
@@ -1510,6 +1501,18 @@ hipError_t launch_bwd_chunk(int stage, int dtype, int K, int V, const BwdParams&
 }
 
 bool bwd_fused_variant_exists(int dtype, int K, int V) { return dtype == 1 && K == 128 && V == 128; }
+
+__global__ __launch_bounds__(256) void kda_to_bf16_kernel(const float* src, bf16* dst, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) dst[i] = (bf16)src[i];
+}
+
+hipError_t launch_to_bf16(const float* src, void* dst, size_t n, hipStream_t stream) {
+    if (n == 0) return hipSuccess;
+    const size_t blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(kda_to_bf16_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0, stream, src,
+                       reinterpret_cast<bf16*>(dst), n);
+    return hipGetLastError();
+}
 
 hipError_t launch_bwd_fused(const BwdParams& p, hipStream_t stream) {
     const long n = (long)p.B * p.H * p.NC;

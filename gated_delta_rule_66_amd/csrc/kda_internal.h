@@ -177,6 +177,7 @@ struct StateParams {
     float* snaps;
     const int* snap_off;
     int snap_every, max_snaps, snap_stride;
+    int snap_bf16;          // the snapshots are stored as bf16 (the backward's own copy)
     // summary pass over every segment, the last included (0: all but the last)
     int summary_all;
 };
@@ -232,6 +233,12 @@ struct BwdParams {
     const unsigned char* rec;   // [B*H*NC] records of the forward's intra-chunk pass
     const float* snaps;     // [B*NC][H][K][V]: slot b NC + c = state after chunk c
     float* adj;             // [B*H][NC][K][V]: dL/dS after chunk c (c < NC - 1)
+    // bf16 copies for the fused chunk kernel (null: fp32 snaps and adj): snapshots
+    // and adjoints as snaps and adj; S0 and dL/dS_T [B*H][K][V] (null: zeros)
+    const void* snaps16;
+    void* adj16;
+    const void* s0h;
+    const void* dsTh;
     // chunk-form gradients: fp32 intermediates, one slot per (b*H + h)*NC + chunk
     float* cdU;             // [C][V] dU (reverse state pass)
     float* cD;              // [C][C] tril(dO U^T)
@@ -267,6 +274,8 @@ hipError_t launch_bwd_chunk(int stage, int dtype, int K, int V, const BwdParams&
 // p.snaps, p.adj, p.cdU; no other intermediate): bf16 with K = V = 128
 bool bwd_fused_variant_exists(int dtype, int K, int V);
 hipError_t launch_bwd_fused(const BwdParams& p, hipStream_t stream);
+// n fp32 values to bf16 (round to nearest even)
+hipError_t launch_to_bf16(const float* src, void* dst, size_t n, hipStream_t stream);
 size_t bwd_workspace_bytes(int B, int T, int H, int K, int V);
 hipError_t launch_decode_multi(int dtype, int K, int V, const MultiDecodeParams& p, hipStream_t stream);
 

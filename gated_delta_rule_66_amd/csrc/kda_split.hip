@@ -1022,14 +1022,28 @@ void kda_state_kernel(StateParams p) {
             if (p.snaps && (ci + 1) % p.snap_every == 0 && row0 + (size_t)(ci + 1) * C <= row_end) {
                 const int slot = (p.snap_off ? p.snap_off[b] : b * p.snap_stride) + (ci + 1) / p.snap_every - 1;
                 if (slot < p.max_snaps) {
-                    float* sd = p.snaps + ((size_t)slot * p.H + h) * K * V;
+                    const size_t so = ((size_t)slot * p.H + h) * K * V;
+                    if (p.snap_bf16) {
+                        bf16* sd = reinterpret_cast<bf16*>(p.snaps) + so;
 #pragma unroll
-                    for (int j = 0; j < NTW; ++j) {
-                        const int col = col0 + 16 * (tile0 + j) + lr;
+                        for (int j = 0; j < NTW; ++j) {
+                            const int col = col0 + 16 * (tile0 + j) + lr;
 #pragma unroll
-                        for (int ct = 0; ct < CT; ++ct)
+                            for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-                            for (int e = 0; e < 4; ++e) sd[(size_t)(16 * ct + 4 * lg + e) * V + col] = S[j][ct][e];
+                                for (int e = 0; e < 4; ++e)
+                                    sd[(size_t)(16 * ct + 4 * lg + e) * V + col] = (bf16)S[j][ct][e];
+                        }
+                    } else {
+                        float* sd = p.snaps + so;
+#pragma unroll
+                        for (int j = 0; j < NTW; ++j) {
+                            const int col = col0 + 16 * (tile0 + j) + lr;
+#pragma unroll
+                            for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+                                for (int e = 0; e < 4; ++e) sd[(size_t)(16 * ct + 4 * lg + e) * V + col] = S[j][ct][e];
+                        }
                     }
                 }
             }

@@ -368,10 +368,13 @@ kda_status kda_recurrent_steps(int N, int T, int H, int K, int V, kda_dtype dt,
  *                   transitions of all n_seg segments: one K x K fp32 slot
  *                   per (b, h) more than the forward's), its chunk records, the
  *                   state and dL/dS after every chunk (2 B*H*ceil(T/64)*K*V
- *                   fp32) and per-chunk fp32 intermediates (bf16 at
- *                   K = V = 128: dL/dU only, 64 x V per chunk, since one
- *                   workgroup computes every gradient of a chunk; otherwise
- *                   also the products the three chunk stages hand on).
+ *                   values) and per-chunk fp32 intermediates.  bf16 at
+ *                   K = V = 128: one workgroup computes every gradient of a
+ *                   chunk from bf16 states and adjoints, and the workspace
+ *                   holds those bf16, dL/dU (fp32, 64 x V per chunk) and bf16
+ *                   copies of S0 and dL/dS_T.  Otherwise the states and
+ *                   adjoints are fp32 and the products the three chunk stages
+ *                   hand on are kept too.
  *                   Token-level
  *                   form: the state every 8 tokens (B*H*ceil(T/8)*K*V fp32)
  *                   and the per-16-column partial sums

@@ -400,11 +400,12 @@ def test_backward_validation_before_any_launch():
     # chunk form: 2 chunks of 2 (b, h) chains, one segment: the chunk records
     # (W, Qh, Mqk, KbT, U~^T bf16; e^{G_C} fp32), the state after every chunk
     # and dL/dS after every chunk, then per chunk the fp32 dU of the reverse
-    # pass; bf16 at K = V = 128 computes every gradient of a chunk in one
-    # workgroup and keeps nothing else
+    # pass.  bf16 at K = V = 128 computes every gradient of a chunk in one
+    # workgroup and keeps nothing else; its states and adjoints are bf16, and
+    # it keeps bf16 copies of S0 and dL/dS_T
     n = lib.kda_chunk_bwd_workspace_size(1, 100, 2, 128, 128, BF16)
     rec = (64 * 128 * 2 * 4 + 64 * 64 * 2 + 128 * 4 + 255) // 256 * 256
-    assert n == 4 * rec + 2 * (4 * 128 * 128 * 4) + 4 * (64 * 128) * 4
+    assert n == 4 * rec + 2 * (4 * 128 * 128 * 2) + 4 * (64 * 128) * 4 + 2 * (2 * 128 * 128 * 2)
     # the three-stage form (here K = 128, V = 64) keeps per chunk dU, D, dQh,
     # dKb, dW, rs, dKh, Et
     n64 = lib.kda_chunk_bwd_workspace_size(1, 100, 2, 128, 64, BF16)
@@ -418,7 +419,8 @@ def test_backward_validation_before_any_launch():
     # 10 segments (the reverse scan applies their transposes) and the loads
     n10 = lib.kda_chunk_bwd_workspace_size(1, 64 * 40, 2, 128, 128, BF16)
     seg = -(-((10 * 2 * 128 * 128 + 10 * 2 * 128 * 128) * 4) // 256) * 256
-    assert n10 == seg + 2 * 40 * rec + 2 * (2 * 40 * 128 * 128 * 4) + 2 * 40 * (64 * 128) * 4
+    assert n10 == (seg + 2 * 40 * rec + 2 * (2 * 40 * 128 * 128 * 2) + 2 * 40 * (64 * 128) * 4
+                   + 2 * (2 * 128 * 128 * 2))
 
 
 def test_package_raises_without_library(tmp_path):
