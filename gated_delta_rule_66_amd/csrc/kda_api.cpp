@@ -342,7 +342,7 @@ static kda_status chunk_impl(int B, int T, int H, int K, int V, kda_dtype dt,
             fp.o = o;
             fp.gate = gate;
             fp.sT = final_state;
-            return launch_timed("fused_output", st, [&] { return launch_fused(fp, false, (int)bh, st); }) ==
+            return launch_timed("fused_output", st, [&] { return launch_fused(fp, (int)bh, st); }) ==
                    hipSuccess ? KDA_OK : KDA_ERR_HIP;
         }
         float* ws = reinterpret_cast<float*>(workspace);
@@ -392,7 +392,7 @@ static kda_status chunk_impl(int B, int T, int H, int K, int V, kda_dtype dt,
         f3.seg_count = pl.n_seg - 1;
         (void)wsFinal;
         if (launch_timed("fused_output", st, [&] {
-                return launch_fused(f3, false, (int)(bh * (pl.n_seg - 1)), st);
+                return launch_fused(f3, (int)(bh * (pl.n_seg - 1)), st);
             }) != hipSuccess)
             return KDA_ERR_HIP;
         return KDA_OK;

@@ -62,6 +62,7 @@ constexpr int FK = 128;    // key channels = value columns
 // store to one does not alias a load from another and can move loads ahead.
 
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 // pair index of block pair (i, j), j < i
 __host__ __device__ constexpr int pair_ix(int i, int j) { return i * (i - 1) / 2 + j; }
@@ -119,6 +120,15 @@ __device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
 }
 // 8 consecutive fp32 values of a lane's channel array as a fragment
 __device__ __forceinline__ bf16x8 frag8(const float* x) { return frag_from<bf16>(x); }
+// the packed fragment itself from here on: a fragment kept across a barrier
+// is then unpacked from its bf16 words (one shift or mask a value) instead of
+// its fp32 source being kept and rounded again (twice the registers, two
+// operations a value)
+__device__ __forceinline__ bf16x8 packed(bf16x8 x) {
+    u32x4 w = __builtin_bit_cast(u32x4, x);
+    asm volatile("" : "+v"(w));
+    return __builtin_bit_cast(bf16x8, w);
+}
 
 __device__ __forceinline__ f32x4 mm16(bf16x4 a, bf16x4 b) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
@@ -159,7 +169,6 @@ __device__ __forceinline__ f32x4 inv_unit_lower(f32x4 nr, f16x4 idh, f32x4 idt) 
 __device__ __forceinline__ u32x2 ld_b64(__amdgpu_buffer_rsrc_t r, unsigned voff) {
     return __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, 0, 0);
 }
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ u32x4 ld_b128(__amdgpu_buffer_rsrc_t r, unsigned voff) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0);
 }
@@ -201,10 +210,11 @@ __device__ __forceinline__ int chan4(int m, int g) { return 32 * (m >> 1) + 8 * 
 constexpr int kFusedNQ = 4 * 4 * 64;
 constexpr int kFusedNM = 2 * 4 * 4 * 64;
 
-template <bool SUMMARY, bool GATE>
+// The output pass: segments from their start states, with output.
+template <bool GATE>
 __global__ __launch_bounds__(512, 1) void kda_fused_kernel(FusedParams p) {
-    KDA_FUSED_LDS(SUMMARY ? 1 : kFusedNQ, SUMMARY ? 1 : kFusedNM)
-    constexpr bool FIRST = false;
+    KDA_FUSED_LDS(kFusedNQ, kFusedNM)
+    constexpr bool SUMMARY = false, FIRST = false;
     const int blk = (int)blockIdx.x;
 #include "kda_fused_body.inc"
 }
@@ -237,11 +247,10 @@ hipError_t launch_fused_first(const FusedParams& po, const FusedParams& ps, int 
     return hipGetLastError();
 }
 
-hipError_t launch_fused(const FusedParams& p, bool summary, int grid, hipStream_t stream) {
+hipError_t launch_fused(const FusedParams& p, int grid, hipStream_t stream) {
     if (grid <= 0) return hipSuccess;
-    if (summary) hipLaunchKernelGGL((kda_fused_kernel<true, false>), dim3(grid), dim3(512), 0, stream, p);
-    else if (p.gate) hipLaunchKernelGGL((kda_fused_kernel<false, true>), dim3(grid), dim3(512), 0, stream, p);
-    else hipLaunchKernelGGL((kda_fused_kernel<false, false>), dim3(grid), dim3(512), 0, stream, p);
+    if (p.gate) hipLaunchKernelGGL((kda_fused_kernel<true>), dim3(grid), dim3(512), 0, stream, p);
+    else hipLaunchKernelGGL((kda_fused_kernel<false>), dim3(grid), dim3(512), 0, stream, p);
     return hipGetLastError();
 }
 

@@ -195,7 +195,7 @@ hipError_t launch_state(int dtype, int K, int VB, const StateParams& p, int grid
 // Kernel-variant selection: returns false if (dtype, K, VB) has no kernel.
 bool chunk_variant_exists(int dtype, int K, int VB);
 bool fused_variant_exists(int dtype, int K, int V);
-hipError_t launch_fused(const FusedParams& p, bool summary, int grid, hipStream_t stream);
+hipError_t launch_fused(const FusedParams& p, int grid, hipStream_t stream);
 // segment 0 with output (po, the first po.B * po.H * po.seg_count workgroups)
 // beside the summaries ps, in one launch of `grid` workgroups
 hipError_t launch_fused_first(const FusedParams& po, const FusedParams& ps, int grid, hipStream_t stream);
