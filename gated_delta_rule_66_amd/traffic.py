@@ -61,8 +61,8 @@ def launch_name(kernel_name: str):
         # segment 0 with output beside the summaries: the summary launch
         return "fused_summary"
     if "kda_fused_kernel" in n:
-        # <SUMMARY, GATE>
-        return "fused_summary" if _first_bool(n, "kda_fused_kernel") else "fused_output"
+        # <GATE>: the output pass, gated or not
+        return "fused_output"
     if "kda_scan_kernel" in n:
         return "segment_scan"
     if "kda_decode_multi_kernel" in n:

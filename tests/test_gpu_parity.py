@@ -39,8 +39,8 @@ def gpu_fwd(x, plan=None, s0="use", split=0, **kw):
     init = x["s0"] if s0 == "use" else s0
     if split == 4:
         K, V = x["q"].shape[-1], x["v"].shape[-1]
-        if x["q"].dtype != torch.bfloat16 or K != 128 or V != 128:
-            pytest.skip("the fused kernel covers bf16 with K = V = 128")
+        if not fused_exists(x["q"].dtype, K, V):
+            raise ValueError("the fused kernel covers bf16 with K = V = 128 only")
         plan = (0, 0, 4) if plan is None else (plan[0], 0, 4)
     elif split:
         plan = (0, 0, split) if plan is None else (plan[0], plan[1], split)
@@ -48,10 +48,25 @@ def gpu_fwd(x, plan=None, s0="use", split=0, **kw):
 
 
 PATHS = [1, 2, 4]
+FUSED = 4
+
+
+def fused_exists(dtype, K, V):
+    return dtype == torch.bfloat16 and K == 128 and V == 128
+
+
+def with_paths(cases, key):
+    """Every case on every path, except the fused path (split 4) for the
+    sizes it has no kernel for; key(case) gives the case's (dtype, K, V)."""
+    out = []
+    for c in cases:
+        c = c if isinstance(c, tuple) else (c,)
+        out += [c + (s,) for s in PATHS if s != FUSED or fused_exists(*key(c))]
+    return out
 
 
 # ------------------------------------------------------------------ small cases
-@pytest.mark.parametrize("split", PATHS)
+@pytest.mark.parametrize("split", [s for s in PATHS if s != FUSED])    # fp32, K = V = 64
 def test_config0_full_parity(split):
     cfg = CONFIGS["prefill_small_fp32"]
     say("small fp32 workload: B=1 H=2 T=256 K=V=64 split=%d" % split)
@@ -85,8 +100,7 @@ SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("split", PATHS)
-@pytest.mark.parametrize("K,V,T,B,H,with_s0,plan", SHAPES)
+@pytest.mark.parametrize("K,V,T,B,H,with_s0,plan,split", with_paths(SHAPES, lambda c: (torch.bfloat16, c[0], c[1])))
 def test_prefill_bf16_shapes(K, V, T, B, H, with_s0, plan, split):
     say("bf16 prefill K=%d V=%d T=%d B=%d H=%d s0=%s plan=%s split=%d" % (K, V, T, B, H, with_s0, plan, split))
     d = make_prefill(B, T, H, K, V, torch.bfloat16, seed=100 + T, s0_std=0.02 if with_s0 else None)
@@ -98,10 +112,9 @@ def test_prefill_bf16_shapes(K, V, T, B, H, with_s0, plan, split):
     assert s_err(sT, s_ref) < TOL[torch.bfloat16]
 
 
-@pytest.mark.parametrize("dtype,K,V", [(torch.bfloat16, 128, 128), (torch.bfloat16, 64, 64),
-                                       (torch.float32, 64, 64)])
-@pytest.mark.parametrize("n_seg", [2, 3, 7])
-@pytest.mark.parametrize("split", PATHS)
+@pytest.mark.parametrize("dtype,K,V,n_seg,split", with_paths(
+    [(dt, K, V, n) for (dt, K, V) in [(torch.bfloat16, 128, 128), (torch.bfloat16, 64, 64), (torch.float32, 64, 64)]
+     for n in (2, 3, 7)], lambda c: c[:3]))
 def test_segment_planner_matches_oracle(dtype, K, V, n_seg, split):
     """Segment transitions computed side by side and recombined: the result
     must not depend on the number of segments (page section on the one-card
@@ -133,8 +146,8 @@ def test_p1_no_forget_no_write(plan):
     assert o_err(o, o_ref) < TOL[torch.bfloat16]
 
 
-@pytest.mark.parametrize("split", PATHS)
-@pytest.mark.parametrize("dtype,K", [(torch.bfloat16, 128), (torch.float32, 64)])
+@pytest.mark.parametrize("dtype,K,split", with_paths([(torch.bfloat16, 128), (torch.float32, 64)],
+                                                     lambda c: (c[0], c[1], c[1])))
 def test_p2_full_write_unit_key(dtype, K, split):
     say("P2 alpha=1 beta=1 basis keys dtype=%s split=%d" % (dtype, split))
     T, H = 200, 2
@@ -176,7 +189,7 @@ def test_p3_clamp_bitwise(split):
     assert s_err(sT, s_ref) < TOL[torch.bfloat16]
 
 
-@pytest.mark.parametrize("split", PATHS)
+@pytest.mark.parametrize("split", [s for s in PATHS if s != FUSED])    # fp32, K = V = 64
 @pytest.mark.parametrize("T", [1, 2, 3, 5, 8])
 def test_p5_dense_expansion_short(T, split):
     say("P5 dense transition expansion T=%d split=%d" % (T, split))
@@ -384,11 +397,11 @@ def _gate_close(fused, o_plain, z, dtype):
     return bool(((fused.float() - ref).abs() <= ulp * ref.abs() + 1e-30).all())
 
 
-@pytest.mark.parametrize("split", PATHS)
-@pytest.mark.parametrize("T,K,V,dtype,plan", [(300, 128, 128, torch.bfloat16, None),
-                                              (1000, 128, 128, torch.bfloat16, (3, 128)),
-                                              (130, 64, 128, torch.bfloat16, None),
-                                              (200, 64, 64, torch.float32, None)])
+@pytest.mark.parametrize("T,K,V,dtype,plan,split", with_paths([(300, 128, 128, torch.bfloat16, None),
+                                                             (1000, 128, 128, torch.bfloat16, (3, 128)),
+                                                             (130, 64, 128, torch.bfloat16, None),
+                                                             (200, 64, 64, torch.float32, None)],
+                                                            lambda c: (c[3], c[1], c[2])))
 def test_output_gate_fused(split, T, K, V, dtype, plan):
     """o * sigmoid(gate) fused into the store of o: against the oracle's
     o * sigmoid(gate) and against the unfused composition on the GPU; the
