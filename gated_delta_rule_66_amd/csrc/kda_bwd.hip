@@ -413,10 +413,15 @@ __global__ __launch_bounds__(64 * NW) void kda_bwd_state_kernel(BwdParams p) {
             dS[ct][e] = dinit ? dinit[(size_t)row * V + col] : (pmode && row == col ? 1.f : 0.f);
         }
 
-    // the loads of chunk ci - 1 are in flight during chunk ci
-    uint4 pre[NPT], dpre[NPD];
+    // two register sets: the loads of chunks ci - 1 and ci - 2 are in flight
+    // during chunk ci.  A chunk before the segment gets empty resources (its
+    // loads return zeros and touch no memory), so that every load is issued
+    // unconditionally and each wait counts only the older set's loads.
+    uint4 preA[NPT], dpreA[NPD], preB[NPT], dpreB[NPD];
     auto load_chunk = [&](int ci, uint4 (&pre)[NPT], uint4 (&dpre)[NPD]) {
-        const __amdgpu_buffer_rsrc_t rr = make_rsrc(rec0 + (size_t)ci * RL.bytes);
+        const bool live = ci >= c_begin;
+        const int cl = live ? ci : c_begin;
+        const __amdgpu_buffer_rsrc_t rr = make_rsrc_n(rec0 + (size_t)cl * RL.bytes, live ? (unsigned)RL.bytes : 0u);
 #pragma unroll
         for (int m = 0; m < NPT; ++m) {
             const int pc = tid + NT * m;
@@ -435,16 +440,17 @@ __global__ __launch_bounds__(64 * NW) void kda_bwd_state_kernel(BwdParams p) {
             }
             pre[m] = pc < L::PTOT ? buf_load16(rr, off) : make_uint4(0, 0, 0, 0);
         }
-        const int t0 = ci * C, nt = min(C, T_ - t0);
-        const T* dob = (p.d_o && !pmode) ? reinterpret_cast<const T*>(p.d_o) + (((size_t)b * T_ + t0) * H + h) * V + vcol0
-                                         : nullptr;
-        const __amdgpu_buffer_rsrc_t rd = make_rsrc(dob);
+        const int t0 = cl * C, nt = min(C, T_ - t0);
+        const T* dob = (p.d_o && !pmode && live) ? reinterpret_cast<const T*>(p.d_o) + (((size_t)b * T_ + t0) * H + h) * V + vcol0
+                                                 : nullptr;
         const unsigned rowV = (unsigned)H * V * SZ;
+        // the chunk's token rows of the block's columns: rows past the sequence
+        // end (and a null or empty source) read as zeros
+        const __amdgpu_buffer_rsrc_t rd = make_rsrc_n(dob, dob ? (unsigned)(nt - 1) * rowV + (unsigned)(VB * SZ) : 0u);
 #pragma unroll
         for (int m = 0; m < NPD; ++m) {
             const int pc = tid + NT * m, t = pc % C, sg = pc / C;
-            dpre[m] = (dob && pc < C * L::PDR && t < nt) ? buf_load16(rd, (unsigned)t * rowV + (unsigned)sg * 16u)
-                                                         : make_uint4(0, 0, 0, 0);
+            dpre[m] = pc < C * L::PDR ? buf_load16(rd, (unsigned)t * rowV + (unsigned)sg * 16u) : make_uint4(0, 0, 0, 0);
         }
     };
     auto store_chunk = [&](const uint4 (&pre)[NPT], const uint4 (&dpre)[NPD]) {
@@ -486,10 +492,10 @@ __global__ __launch_bounds__(64 * NW) void kda_bwd_state_kernel(BwdParams p) {
 
     // every chunk's dU goes to p.cdU (chunk-form gradients); the adjoint
     // before chunk ci to p.adj (ci >= 1) or p.ds0; false: nothing left to do
-    auto step = [&](int ci) -> bool {
+    auto step = [&](int ci, uint4 (&pre)[NPT], uint4 (&dpre)[NPD]) -> bool {
         store_chunk(pre, dpre);
         __syncthreads();
-        if (ci - 1 >= c_begin) load_chunk(ci - 1, pre, dpre);
+        load_chunk(ci - 2, pre, dpre);
         Frag bdo[2], bds[KS];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) bdo[ks] = ld_frag_perm<T>(&sDoT[(16 * w + lr) * LDC + 32 * ks + 4 * lg]);
@@ -552,9 +558,12 @@ __global__ __launch_bounds__(64 * NW) void kda_bwd_state_kernel(BwdParams p) {
         __syncthreads();
         return true;
     };
-    if (c_end > c_begin) load_chunk(c_end - 1, pre, dpre);
-    for (int ci = c_end - 1; ci >= c_begin; --ci)
-        if (!step(ci)) break;
+    load_chunk(c_end - 1, preA, dpreA);
+    load_chunk(c_end - 2, preB, dpreB);
+    for (int ci = c_end - 1; ci >= c_begin; ci -= 2) {
+        if (!step(ci, preA, dpreA)) break;
+        if (ci - 1 < c_begin || !step(ci - 1, preB, dpreB)) break;
+    }
     if (SUMMARY) {
         // the segment's map, at scan slot n_seg - 1 - seg: transition [K][K] or load [K][V]
         const int slot = p.n_seg - 1 - seg;
