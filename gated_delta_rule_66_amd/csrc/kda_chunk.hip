@@ -662,35 +662,44 @@ __global__ __launch_bounds__(64 * NWS) void kda_scan_kernel(ScanParams p) {
         sS[row * LD + c] = p.s0 ? p.s0[((size_t)bh * K + row) * V + (size_t)cb * 16 + c] : 0.f;
     }
     // two register sets: segment j + 1's P rows and L tile are in flight
-    // during step j (loads are issued as soon as a set's MFMAs have read it)
+    // during step j (loads are issued as soon as a set's MFMAs have read it).
+    // Past the last transition the resources are empty (the loads return zeros
+    // and touch no memory): every load is issued unconditionally, so that each
+    // wait counts only the older set's loads instead of draining all of them.
     float aA[TPW][KQ], aB[TPW][KQ];
     f32x4 lA[TPW], lB[TPW];
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
     auto load_seg = [&](int j, float (&a)[TPW][KQ], f32x4 (&lt)[TPW]) {
-        const int pj = REV ? p.n_seg - 1 - j : j;
-        const float* P = p.wsP + ((size_t)pj * p.BH + bh) * K * K;
-        const float* Lj = p.wsL + ((size_t)j * p.BH + bh) * K * V;
+        const bool live = j < p.n_seg - 1;
+        const int jj = live ? j : 0;
+        const int pj = REV ? p.n_seg - 1 - jj : jj;
+        const __amdgpu_buffer_rsrc_t rp =
+            make_rsrc_n(p.wsP + ((size_t)pj * p.BH + bh) * K * K, live ? (unsigned)(K * K * 4) : 0u);
+        const __amdgpu_buffer_rsrc_t rl =
+            make_rsrc_n(p.wsL + ((size_t)jj * p.BH + bh) * K * V, live ? (unsigned)(K * V * 4) : 0u);
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
             const int rt = TPW * w + t;
             if constexpr (REV) {
                 // row 16 rt + lr of P^T: column 16 rt + lr of P (16 lanes read
                 // 64 consecutive bytes of each row)
-                const float* pcol = P + (size_t)(KQ * lg) * K + 16 * rt + lr;
 #pragma unroll
-                for (int q = 0; q < KQ; ++q) a[t][q] = pcol[(size_t)q * K];
+                for (int q = 0; q < KQ; ++q)
+                    a[t][q] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                        rp, (int)((unsigned)((KQ * lg + q) * K + 16 * rt + lr) * 4u), 0, 0));
             } else {
-                const float* prow = P + (size_t)(16 * rt + lr) * K + KQ * lg;
+                const unsigned row = (unsigned)((16 * rt + lr) * K + KQ * lg) * 4u;
 #pragma unroll
                 for (int q4 = 0; q4 < KQ / 4; ++q4) {
-                    const float4 v4 = *reinterpret_cast<const float4*>(prow + 4 * q4);
-                    a[t][4 * q4] = v4.x;
-                    a[t][4 * q4 + 1] = v4.y;
-                    a[t][4 * q4 + 2] = v4.z;
-                    a[t][4 * q4 + 3] = v4.w;
+                    const u32x4 v4 = __builtin_amdgcn_raw_buffer_load_b128(rp, (int)(row + 16u * q4), 0, 0);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) a[t][4 * q4 + e] = __uint_as_float(v4[e]);
                 }
             }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) lt[t][e] = Lj[(size_t)(16 * rt + 4 * lg + e) * V + col];
+            for (int e = 0; e < 4; ++e)
+                lt[t][e] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                    rl, (int)((unsigned)((16 * rt + 4 * lg + e) * V) * 4u + (unsigned)col * 4u), 0, 0));
         }
     };
     // S_{j+1} = P_j S_j + L_j with set (a, lt); then the set takes segment j + 2
@@ -717,7 +726,7 @@ __global__ __launch_bounds__(64 * NWS) void kda_scan_kernel(ScanParams p) {
             }
 #pragma unroll
         for (int t = 0; t < TPW; ++t) acc[t] += acc2[t];
-        if (j + 3 < p.n_seg) load_seg(j + 2, a, lt);
+        load_seg(j + 2, a, lt);
         float* Lj = p.wsL + ((size_t)j * p.BH + bh) * K * V;
         __syncthreads();
 #pragma unroll
@@ -732,13 +741,17 @@ __global__ __launch_bounds__(64 * NWS) void kda_scan_kernel(ScanParams p) {
         }
         __syncthreads();
     };
-    if (p.n_seg > 1) load_seg(0, aA, lA);
-    if (p.n_seg > 2) load_seg(1, aB, lB);
+    load_seg(0, aA, lA);
+    load_seg(1, aB, lB);
     __syncthreads();
-    for (int j = 0; j + 1 < p.n_seg; j += 2) {
+    // steps 0 .. n_seg - 2, in pairs (no step skipped inside the loop), then
+    // the odd one left
+    int j = 0;
+    for (; j + 2 < p.n_seg; j += 2) {
         step(j, aA, lA);
-        if (j + 2 < p.n_seg) step(j + 1, aB, lB);
+        step(j + 1, aB, lB);
     }
+    if (j + 1 < p.n_seg) step(j, aA, lA);
 }
 
 __global__ __launch_bounds__(256) void kda_copy_state_kernel(const float* src, float* dst, size_t n) {
