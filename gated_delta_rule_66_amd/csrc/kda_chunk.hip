@@ -726,32 +726,41 @@ __global__ __launch_bounds__(64 * NWS) void kda_scan_kernel(ScanParams p) {
             }
 #pragma unroll
         for (int t = 0; t < TPW; ++t) acc[t] += acc2[t];
-        load_seg(j + 2, a, lt);
+        // S_{j+1} to slot j, before the loads of segment j + 2: a wait for the
+        // other set's loads then counts these stores as issued earlier and
+        // need not wait for them to complete
         float* Lj = p.wsL + ((size_t)j * p.BH + bh) * K * V;
+#pragma unroll
+        for (int t = 0; t < TPW; ++t) {
+            const int rt = TPW * w + t;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Lj[(size_t)(16 * rt + 4 * lg + e) * V + col] = acc[t][e];
+        }
+        load_seg(j + 2, a, lt);
         __syncthreads();
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
             const int rt = TPW * w + t;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int row = 16 * rt + 4 * lg + e;
-                sS[row * LD + lr] = acc[t][e];
-                Lj[(size_t)row * V + col] = acc[t][e];
-            }
+            for (int e = 0; e < 4; ++e) sS[(16 * rt + 4 * lg + e) * LD + lr] = acc[t][e];
         }
         __syncthreads();
     };
     load_seg(0, aA, lA);
     load_seg(1, aB, lB);
     __syncthreads();
-    // steps 0 .. n_seg - 2, in pairs (no step skipped inside the loop), then
-    // the odd one left
-    int j = 0;
+    // steps 0 .. n_seg - 2 (n_seg >= 2): step 0, then pairs (no step skipped
+    // inside the loop), then the odd one left.  With step 0 ahead of the loop
+    // the memory operations in flight at the loop top are the same on entry
+    // and on the back edge, so its wait leaves the previous step's stores in
+    // flight.
+    step(0, aA, lA);
+    int j = 1;
     for (; j + 2 < p.n_seg; j += 2) {
-        step(j, aA, lA);
-        step(j + 1, aB, lB);
+        step(j, aB, lB);
+        step(j + 1, aA, lA);
     }
-    if (j + 1 < p.n_seg) step(j, aA, lA);
+    if (j + 1 < p.n_seg) step(j, aB, lB);
 }
 
 __global__ __launch_bounds__(256) void kda_copy_state_kernel(const float* src, float* dst, size_t n) {
