@@ -60,6 +60,9 @@ constexpr int FK = 128;    // key channels = value columns
 // q fragments and k e^{Tot - Gin}, from phase 1a to 1b.  Each region is an
 // array of its own (declared in the kernel), so that the compiler knows a
 // store to one does not alias a load from another and can move loads ahead.
+// The summary role has no q side: its producers stage V of chunk c + 1 in the
+// Q^ and q e^{Gin} arrays instead (one per chunk parity), for consumers that
+// hold two states and have no registers to prefetch it.
 
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
