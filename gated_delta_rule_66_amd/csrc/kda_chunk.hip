@@ -645,8 +645,10 @@ __global__ __launch_bounds__(64 * NWS) void kda_scan_kernel(ScanParams p) {
     constexpr int TPW = RT / NWS;       // row tiles per wave
     static_assert(TPW * NWS == RT, "whole row tiles per wave");
     constexpr int KQ = K / 4;           // reduction steps
-    constexpr int LD = 17;
-    __shared__ float sS[K * LD];
+    // the state block's 16 columns, column-major (a lane reads its column's
+    // 32 reduction rows with 16-byte reads and writes its 4 rows with one)
+    constexpr int LDT = K + 4;
+    __shared__ __attribute__((aligned(16))) float sS[16 * LDT];
     // the column blocks of one (b, h) read the same P rows: place them on one
     // XCD (workgroups are dealt to the 8 XCDs round robin) so they share its L2
     const int G = gridDim.x, x = blockIdx.x;
@@ -659,7 +661,7 @@ __global__ __launch_bounds__(64 * NWS) void kda_scan_kernel(ScanParams p) {
     const size_t col = (size_t)cb * 16 + lr;
     for (int i = tid; i < K * 16; i += 64 * NWS) {
         const int row = i / 16, c = i % 16;
-        sS[row * LD + c] = p.s0 ? p.s0[((size_t)bh * K + row) * V + (size_t)cb * 16 + c] : 0.f;
+        sS[c * LDT + row] = p.s0 ? p.s0[((size_t)bh * K + row) * V + (size_t)cb * 16 + c] : 0.f;
     }
     // two register sets: segment j + 1's P rows and L tile are in flight
     // during step j (loads are issued as soon as a set's MFMAs have read it).
@@ -708,7 +710,11 @@ __global__ __launch_bounds__(64 * NWS) void kda_scan_kernel(ScanParams p) {
         // MFMA chains, so the chains do not wait on each read
         float bS[KQ];
 #pragma unroll
-        for (int ks = 0; ks < KQ; ++ks) bS[ks] = sS[(KQ * lg + ks) * LD + lr];
+        for (int k4 = 0; k4 < KQ / 4; ++k4) {
+            const f32x4 v4 = *reinterpret_cast<const f32x4*>(&sS[lr * LDT + KQ * lg + 4 * k4]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) bS[4 * k4 + e] = v4[e];
+        }
         __builtin_amdgcn_sched_barrier(0);
         // two independent chains per tile (even and odd reduction steps)
         f32x4 acc[TPW], acc2[TPW];
@@ -741,8 +747,7 @@ __global__ __launch_bounds__(64 * NWS) void kda_scan_kernel(ScanParams p) {
 #pragma unroll
         for (int t = 0; t < TPW; ++t) {
             const int rt = TPW * w + t;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sS[(16 * rt + 4 * lg + e) * LD + lr] = acc[t][e];
+            *reinterpret_cast<f32x4*>(&sS[lr * LDT + 16 * rt + 4 * lg]) = acc[t];
         }
         __syncthreads();
     };
