@@ -48,7 +48,8 @@ struct FusedParams {
     float* wsL;             // summary pass: [n_seg-1][B*H][K][V]
     int B, T, H;
     int n_seg;              // segments of the sequence
-    int cps;                // chunks per segment
+    int cps;                // chunks per segment (segments 1 ..)
+    int cps0;               // chunks of segment 0 (segment s >= 1 starts at cps0 + (s - 1) cps)
     int seg_first;          // this launch's segments of each (b, h): seg_first .. seg_first + seg_count - 1
     int seg_count;
     float* seg0_L;          // output pass: segment 0's end state (slot 0 of the summaries' L), or null
